@@ -1,0 +1,163 @@
+/*
+ * gconv.h -- C ABI of the grouped 2-D convolution library for AMD MI355X
+ * (gfx950). Channels-first (NCHW) float32.
+ *
+ * The operation ("[Feature request] Groups support for SpatialConvolutionMM",
+ * the opening definition of groups): the C input planes and the K output
+ * planes are each split into `groups` contiguous blocks, and output block g
+ * is computed from input block g only. With Cg = C/groups and Kg = K/groups:
+ *
+ *   y[n,k,ho,wo] = bias[k] + sum_{c<Cg, i<kh, j<kw}
+ *                  w[k,c,i,j] * x[n, g*Cg + c, ho*stride_h - pad_h + i*dil_h,
+ *                                               wo*stride_w - pad_w + j*dil_w]
+ *
+ * with g = k / Kg, x read as 0 outside [0,H) x [0,W) (zero padding), and no
+ * kernel flip (cross-correlation: a kernel-sized input gives exactly the
+ * Linear layer on the flattened input, as "SpatialConvolution running in
+ * fully-connected mode is very slow, even with R4" relies on).
+ *
+ * Tensor layouts (all dense, row-major, float32, device memory):
+ *   x, dx  [N, C, H, W]
+ *   w, dw  [K, C/groups, kh, kw]    (K * C/groups filter planes)
+ *   bias, db [K]
+ *   y, dy  [N, K, Ho, Wo],  Ho = floor((H + 2*pad_h - dil_h*(kh-1) - 1)/stride_h) + 1
+ *                           (likewise Wo)
+ *
+ * Ownership and execution. The caller owns every buffer; the library never
+ * allocates device memory. Every op is enqueued on the caller's HIP stream
+ * (`stream` is a hipStream_t; NULL means the default stream) and returns once
+ * its kernels are enqueued. Inputs are read only. Outputs are overwritten in
+ * full (gradWeight and gradBias are not accumulated into); outputs must not
+ * overlap any input. Results are deterministic: the same inputs on the same
+ * device give bit-identical outputs (no floating-point atomics).
+ *
+ * Errors. Every function returns a gconv_status. Descriptor and argument
+ * errors are detected on the host before anything is enqueued, and nothing
+ * is written. GCONV_ERR_HIP reports a failed launch. gconv_last_error()
+ * gives a readable detail of the calling thread's last failure (e.g. which
+ * dimension does not divide by groups).
+ */
+#ifndef GCONV_H
+#define GCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Convolution descriptor. K is the total number of output planes, not the
+ * per-group count. The fields follow the constructor the clnn issue quotes
+ * (nInputPlane, nOutputPlane, kW, kH, dW, dH, padW, padH, groups), plus
+ * batch, input extent and dilation. Valid when N,C,H,W,K,kh,kw >= 1,
+ * stride >= 1, dil >= 1, pad >= 0, groups >= 1, C % groups == 0,
+ * K % groups == 0 and Ho, Wo >= 1 ("Support groups in DenseConvDims": the
+ * channel counts must agree with the tensors and with the group split).
+ */
+typedef struct gconv_desc {
+    int64_t N, C, H, W;
+    int64_t K;
+    int64_t kh, kw;
+    int64_t stride_h, stride_w;
+    int64_t pad_h, pad_w;
+    int64_t dil_h, dil_w;
+    int64_t groups;
+} gconv_desc;
+
+typedef enum gconv_status {
+    GCONV_OK = 0,
+    GCONV_ERR_NULL = 1,        /* a required pointer is NULL */
+    GCONV_ERR_SHAPE = 2,       /* a dimension < 1, a bad stride/pad/dilation, or Ho/Wo < 1 */
+    GCONV_ERR_GROUPS = 3,      /* C or K not divisible by groups */
+    GCONV_ERR_WORKSPACE = 4,   /* workspace smaller than gconv_workspace_size() */
+    GCONV_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
+    GCONV_ERR_UNSUPPORTED = 6, /* valid descriptor the forced path cannot run */
+    GCONV_ERR_ARG = 7          /* other bad argument, e.g. an output overlapping an input */
+} gconv_status;
+
+typedef enum gconv_op {
+    GCONV_OP_FWD = 0,
+    GCONV_OP_BWD_DATA = 1,
+    GCONV_OP_BWD_FILTER = 2,
+    GCONV_OP_BWD_BIAS = 3
+} gconv_op;
+
+/* Kernel families the dispatcher routes between. */
+typedef enum gconv_path {
+    GCONV_PATH_AUTO = 0,       /* the dispatcher's own choice (default) */
+    GCONV_PATH_DIRECT = 1,     /* general direct kernels: any valid descriptor */
+    GCONV_PATH_SMALLGROUP = 2, /* VALU/LDS kernels for few channels per group */
+    GCONV_PATH_IGEMM = 3,      /* fp32-MFMA implicit GEMM, groups in the grid */
+    GCONV_PATH_FC = 4          /* kernel == input: plain fp32-MFMA GEMM */
+} gconv_path;
+
+/* Output extent of the descriptor (the floor rule above). */
+int gconv_output_dims(const gconv_desc* d, int64_t* Ho, int64_t* Wo);
+
+/*
+ * Bytes of device workspace `op` needs for this descriptor (0 when none).
+ * Pass at least this much to the op; the workspace may be NULL when 0.
+ * The contents need no initialisation and are scratch after the call.
+ */
+int gconv_workspace_size(const gconv_desc* d, int op, size_t* bytes);
+
+/*
+ * Forward pass (updateOutput in the clnn issue): y = conv(x, w) + bias.
+ * `bias` may be NULL (no bias); otherwise bias[k] is added to every element
+ * of output plane k (DLPrimitives Blog, "Pointwise Broadcast Reduce": the
+ * [C] bias broadcast over [B,C,H,W]). One launch covers every group.
+ */
+int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* bias, float* y,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gradInput (updateGradInput in the clnn issue): dx = d<y,dy>/dx, the exact
+ * adjoint of the forward map. dx[n, g*Cg+c, h, w] sums w[k,c,i,j] *
+ * dy[n,k,ho,wo] over the k of group g and the taps (i, j) whose window
+ * position (ho, wo) reads (h, w); input pixels no window reads get 0.
+ */
+int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* dx,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gradWeight (the weight half of accGradParameters in the clnn issue):
+ * dw[k,c,i,j] = sum_{n,ho,wo} dy[n,k,ho,wo] * x[n, g*Cg+c, h(ho,i), w(wo,j)].
+ * Overwrites dw. Uses the workspace for split reductions.
+ */
+int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float* dw,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gradBias: db[k] = sum_{n,ho,wo} dy[n,k,ho,wo] (DLPrimitives Blog,
+ * "Pointwise Broadcast Reduce": the sum of dy over dims 0, 2 and 3).
+ * Only N, K, Ho and Wo of the descriptor matter. Overwrites db.
+ */
+int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Kernel family the dispatcher would run `op` on for this descriptor. */
+int gconv_select_path(const gconv_desc* d, int op, int* path);
+
+/*
+ * Force every later call in this process onto one kernel family (for
+ * cross-checking each family against the others); GCONV_PATH_AUTO restores
+ * the dispatcher's choice. A forced family that cannot run a descriptor
+ * makes that call return GCONV_ERR_UNSUPPORTED. Not meant for concurrent use.
+ */
+int gconv_set_path_override(int path);
+
+const char* gconv_status_string(int status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* gconv_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int gconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GCONV_H */

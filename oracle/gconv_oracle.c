@@ -54,10 +54,12 @@ static int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d
     return num / s + 1;
 }
 
-/* Returns 0 when the descriptor is valid, and fills Ho/Wo; nonzero otherwise. */
+/* Returns 0 when the descriptor is valid, and fills Ho/Wo; nonzero otherwise.
+ * An empty batch (N == 0) is valid: the outputs are empty, and the weight and
+ * bias gradients are sums over no terms, i.e. 0. */
 int oracle_output_dims(const oracle_desc* d, int64_t* Ho, int64_t* Wo)
 {
-    if (d->N < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->K < 1 || d->kh < 1 || d->kw < 1)
+    if (d->N < 0 || d->C < 1 || d->H < 1 || d->W < 1 || d->K < 1 || d->kh < 1 || d->kw < 1)
         return 1;
     if (d->stride_h < 1 || d->stride_w < 1 || d->dil_h < 1 || d->dil_w < 1) return 1;
     if (d->pad_h < 0 || d->pad_w < 0 || d->groups < 1) return 1;

@@ -163,7 +163,7 @@ def test_golden_output_dims_more():
     assert oracle.output_dims(1, 1, 7, 7, 1, 3, 3, 1, 0, 2) == (3, 3)
     assert oracle.output_dims(1, 1, 8, 5, 1, 2, 3, (3, 2), (1, 0), (1, 2)) == (3, 1)
     for bad in [dict(kh=8), dict(stride=0), dict(dilation=0), dict(padding=-1),
-                dict(groups=3), dict(N=0)]:
+                dict(groups=3), dict(N=-1)]:
         args = dict(N=1, C=4, H=7, W=7, K=4, kh=3, kw=3, stride=1, padding=0, dilation=1,
                     groups=2)
         args.update(bad)
@@ -380,3 +380,18 @@ def test_abs_sum_is_sum_of_abs_products():
     # and flips sign-insensitively
     y2, ya2 = oracle.fwd(-x, w, b, **kw)
     np.testing.assert_allclose(ya2, ya, rtol=1e-14)
+
+
+def test_empty_batch():
+    """N = 0 is a valid descriptor: empty y and gradInput, zero gradWeight and
+    gradBias (sums over no terms), as torch's float64 conv gives."""
+    d = dict(N=0, C=6, H=5, W=4, K=4, kh=3, kw=2, sh=1, sw=1, ph=1, pw=0, dh=1, dw=1, G=2)
+    kw = conv_kwargs(d)
+    x, w, b = tensors(d, 1400)
+    y_t, _, _, _ = torch_all(x, w, b, None, kw)
+    dy = np.zeros(y_t.shape, np.float32)
+    _, dx_t, dw_t, db_t = torch_all(x, w, b, dy, kw)
+    (y, _), (dx, _), (dw, _), (db, _) = run_oracle_all(x, w, b, dy, kw)
+    assert y.shape == y_t.shape and dx.shape == dx_t.shape == x.shape
+    assert np.array_equal(dw, dw_t) and np.all(dw == 0)
+    assert np.array_equal(db, db_t) and np.all(db == 0)
