@@ -1,0 +1,259 @@
+// direct.hip -- general direct kernels for grouped 2-D convolution (NCHW fp32).
+//
+// These run any valid descriptor (stride, padding, dilation, any group
+// split) and are the fallback every specialised family is checked against.
+// One launch covers all groups: the group of an output plane is derived from
+// its channel index, and each group's planes are reached by offsets into the
+// caller's tensors, never by copies ("[Feature request] Groups support for
+// SpatialConvolutionMM": narrow() as a zero-copy offset, and the request for a
+// single kernel over all groups).
+#include "gconv_internal.h"
+
+namespace gconv {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+// Sum of `v` over the 256 threads of a block, in a fixed order (wave64
+// butterfly, then the four wave totals in index order). Valid in thread 0.
+__device__ __forceinline__ float block_sum_256(float v, float* lds4)
+{
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) lds4[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    if (threadIdx.x == 0) t = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+    return t;
+}
+
+// y[n,k,ho,wo]: one thread per output element, grid-stride.
+__global__ void __launch_bounds__(kBlock)
+direct_fwd_kernel(Shape s, const float* __restrict__ x, const float* __restrict__ w,
+                  const float* __restrict__ bias, float* __restrict__ y)
+{
+    const int64_t total = s.y_elems;
+    const int64_t HW = (int64_t)s.H * s.W;
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * kBlock) {
+        const int wo = (int)(e % s.Wo);
+        int64_t t = e / s.Wo;
+        const int ho = (int)(t % s.Ho);
+        t /= s.Ho;
+        const int k = (int)(t % s.K);
+        const int64_t n = t / s.K;
+        const int g = k / s.Kg;
+        const float* xg = x + (n * s.C + (int64_t)g * s.Cg) * HW;
+        const float* wk = w + (int64_t)k * s.Cg * s.kh * s.kw;
+        float acc = 0.f;
+        for (int c = 0; c < s.Cg; ++c) {
+            for (int i = 0; i < s.kh; ++i) {
+                const int h = ho * s.sh - s.ph + i * s.dh;
+                if (h < 0 || h >= s.H) continue;
+                for (int j = 0; j < s.kw; ++j) {
+                    const int ww = wo * s.sw - s.pw + j * s.dw;
+                    if (ww < 0 || ww >= s.W) continue;
+                    acc = fmaf(wk[(c * s.kh + i) * s.kw + j], xg[c * HW + (int64_t)h * s.W + ww],
+                               acc);
+                }
+            }
+        }
+        if (bias) acc += bias[k];
+        y[e] = acc;
+    }
+}
+
+// dx[n, g*Cg+c, h, w]: one thread per input element; gathers the taps whose
+// window reads (h, w): ho = (h + ph - i*dh) / sh when exact and in range.
+__global__ void __launch_bounds__(kBlock)
+direct_bwd_data_kernel(Shape s, const float* __restrict__ dy, const float* __restrict__ w,
+                       float* __restrict__ dx)
+{
+    const int64_t total = s.x_elems;
+    const int64_t P = (int64_t)s.Ho * s.Wo;
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * kBlock) {
+        const int ww = (int)(e % s.W);
+        int64_t t = e / s.W;
+        const int h = (int)(t % s.H);
+        t /= s.H;
+        const int ca = (int)(t % s.C);
+        const int64_t n = t / s.C;
+        const int g = ca / s.Cg, c = ca % s.Cg;
+        float acc = 0.f;
+        for (int k = g * s.Kg; k < (g + 1) * s.Kg; ++k) {
+            const float* dyk = dy + (n * s.K + k) * P;
+            const float* wkc = w + ((int64_t)k * s.Cg + c) * s.kh * s.kw;
+            for (int i = 0; i < s.kh; ++i) {
+                const int th = h + s.ph - i * s.dh;
+                if (th < 0 || th % s.sh != 0) continue;
+                const int ho = th / s.sh;
+                if (ho >= s.Ho) continue;
+                for (int j = 0; j < s.kw; ++j) {
+                    const int tw = ww + s.pw - j * s.dw;
+                    if (tw < 0 || tw % s.sw != 0) continue;
+                    const int wo = tw / s.sw;
+                    if (wo >= s.Wo) continue;
+                    acc = fmaf(wkc[i * s.kw + j], dyk[(int64_t)ho * s.Wo + wo], acc);
+                }
+            }
+        }
+        dx[e] = acc;
+    }
+}
+
+// dw[k,c,i,j]: one block per weight element (grid-stride over elements); the
+// block's threads stride over the N*Ho*Wo reduction, then a fixed-order block sum.
+__global__ void __launch_bounds__(kBlock)
+direct_bwd_filter_kernel(Shape s, const float* __restrict__ x, const float* __restrict__ dy,
+                         float* __restrict__ dw)
+{
+    __shared__ float lds4[4];
+    const int64_t P = (int64_t)s.Ho * s.Wo, HW = (int64_t)s.H * s.W;
+    const int64_t total = (int64_t)s.N * P;
+    for (int64_t e = blockIdx.x; e < s.w_elems; e += gridDim.x) {
+        const int j = (int)(e % s.kw);
+        const int i = (int)((e / s.kw) % s.kh);
+        const int c = (int)((e / ((int64_t)s.kw * s.kh)) % s.Cg);
+        const int k = (int)(e / ((int64_t)s.kw * s.kh * s.Cg));
+        const int g = k / s.Kg;
+        float acc = 0.f;
+        for (int64_t t = threadIdx.x; t < total; t += kBlock) {
+            const int64_t n = t / P;
+            const int p = (int)(t % P);
+            const int ho = p / s.Wo, wo = p % s.Wo;
+            const int h = ho * s.sh - s.ph + i * s.dh;
+            const int ww = wo * s.sw - s.pw + j * s.dw;
+            if (h < 0 || h >= s.H || ww < 0 || ww >= s.W) continue;
+            acc = fmaf(dy[(n * s.K + k) * P + p],
+                       x[(n * s.C + (int64_t)g * s.Cg + c) * HW + (int64_t)h * s.W + ww], acc);
+        }
+        const float tot = block_sum_256(acc, lds4);
+        if (threadIdx.x == 0) dw[e] = tot;
+        __syncthreads();  // lds4 is reused by the next element
+    }
+}
+
+// Partial bias sums, plane layout (Ho*Wo > 1): block (s, k) sums images
+// [s*chunk, (s+1)*chunk) of plane k into ws[k*S + s].
+__global__ void __launch_bounds__(kBlock)
+bias_planes_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, int K, int P,
+                    int chunk)
+{
+    __shared__ float lds4[4];
+    const int sidx = blockIdx.x, k = blockIdx.y, S = gridDim.x;
+    const int n0 = sidx * chunk, n1 = min(N, n0 + chunk);
+    float acc = 0.f;
+    for (int n = n0; n < n1; ++n) {
+        const float* plane = dy + ((int64_t)n * K + k) * P;
+        for (int p = threadIdx.x; p < P; p += kBlock) acc += plane[p];
+    }
+    const float tot = block_sum_256(acc, lds4);
+    if (threadIdx.x == 0) ws[(int64_t)k * S + sidx] = tot;
+}
+
+// Partial bias sums, column layout (Ho*Wo == 1, dy is [N, K]): thread k of
+// block (kt, s) sums rows [s*chunk, (s+1)*chunk) of column k into ws[k*S + s].
+__global__ void __launch_bounds__(kBlock)
+bias_cols_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, int K, int chunk)
+{
+    const int k = blockIdx.x * kBlock + threadIdx.x, sidx = blockIdx.y, S = gridDim.y;
+    if (k >= K) return;
+    const int n0 = sidx * chunk, n1 = min(N, n0 + chunk);
+    float acc = 0.f;
+    for (int n = n0; n < n1; ++n) acc += dy[(int64_t)n * K + k];
+    ws[(int64_t)k * S + sidx] = acc;
+}
+
+// db[k] = sum_s ws[k*S + s], in index order.
+__global__ void __launch_bounds__(kBlock)
+bias_finalize(const float* __restrict__ ws, float* __restrict__ db, int K, int S)
+{
+    const int k = blockIdx.x * kBlock + threadIdx.x;
+    if (k >= K) return;
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) acc += ws[(int64_t)k * S + s];
+    db[k] = acc;
+}
+
+__global__ void __launch_bounds__(kBlock) fill_zero_kernel(float* p, int64_t count)
+{
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < count;
+         e += (int64_t)gridDim.x * kBlock)
+        p[e] = 0.f;
+}
+
+unsigned grid_for(int64_t total)
+{
+    const int64_t blocks = (total + kBlock - 1) / kBlock;
+    return (unsigned)(blocks < 65536 ? (blocks < 1 ? 1 : blocks) : 65536);
+}
+
+// Split count for the bias reduction: about 2048 partial sums in flight.
+int bias_splits(const Shape& s)
+{
+    const int P = s.Ho * s.Wo;
+    int S;
+    if (P == 1)
+        S = (int)((2048 + (s.K + kBlock - 1) / kBlock - 1) / ((s.K + kBlock - 1) / kBlock));
+    else
+        S = (2048 + s.K - 1) / s.K;
+    if (S > s.N) S = s.N;
+    if (S < 1) S = 1;
+    return S;
+}
+
+}  // namespace
+
+void direct_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                hipStream_t st)
+{
+    if (s.y_elems == 0) return;
+    hipLaunchKernelGGL(direct_fwd_kernel, dim3(grid_for(s.y_elems)), dim3(kBlock), 0, st, s, x,
+                       w, bias, y);
+}
+
+void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    if (s.x_elems == 0) return;
+    hipLaunchKernelGGL(direct_bwd_data_kernel, dim3(grid_for(s.x_elems)), dim3(kBlock), 0, st, s,
+                       dy, w, dx);
+}
+
+void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st)
+{
+    const int64_t blocks = s.w_elems < (1 << 20) ? s.w_elems : (1 << 20);
+    hipLaunchKernelGGL(direct_bwd_filter_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, s,
+                       x, dy, dw);
+}
+
+size_t bias_workspace_bytes(const Shape& s)
+{
+    if (s.N == 0) return 0;
+    return (size_t)s.K * (size_t)bias_splits(s) * sizeof(float);
+}
+
+void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStream_t st)
+{
+    const int P = s.Ho * s.Wo;
+    const int S = bias_splits(s);
+    const int chunk = (s.N + S - 1) / S;
+    if (P == 1) {
+        hipLaunchKernelGGL(bias_cols_partial, dim3((s.K + kBlock - 1) / kBlock, S), dim3(kBlock),
+                           0, st, dy, ws, s.N, s.K, chunk);
+    } else {
+        hipLaunchKernelGGL(bias_planes_partial, dim3(S, s.K), dim3(kBlock), 0, st, dy, ws, s.N,
+                           s.K, P, chunk);
+    }
+    hipLaunchKernelGGL(bias_finalize, dim3((s.K + kBlock - 1) / kBlock), dim3(kBlock), 0, st, ws,
+                       db, s.K, S);
+}
+
+void fill_zero(float* p, int64_t count, hipStream_t st)
+{
+    if (count == 0) return;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(count)), dim3(kBlock), 0, st, p, count);
+}
+
+}  // namespace gconv

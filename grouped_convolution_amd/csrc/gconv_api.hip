@@ -1,0 +1,299 @@
+// gconv_api.hip -- the C ABI (include/gconv.h): descriptor validation, output
+// extents, routing between kernel families, workspace sizing and error
+// reporting. Everything here runs on the host; kernels live in the other
+// translation units.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gconv.h"
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_path_override{GCONV_PATH_AUTO};
+
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
+{
+    const int64_t num = in + 2 * p - d * (k - 1) - 1;
+    return num < 0 ? 0 : num / s + 1;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Check the descriptor ("Support groups in DenseConvDims": channel counts
+// must agree with the group split, with a clear message when they do not)
+// and derive the shape every kernel uses.
+int make_shape(const gconv_desc* d, Shape* s)
+{
+    if (!d) return fail(GCONV_ERR_NULL, "descriptor is NULL");
+    if (d->N < 0 || d->C < 1 || d->H < 1 || d->W < 1 || d->K < 1 || d->kh < 1 || d->kw < 1)
+        return fail(GCONV_ERR_SHAPE,
+                    "need N>=0 and C,H,W,K,kh,kw>=1 (got N=%lld C=%lld H=%lld W=%lld K=%lld "
+                    "kh=%lld kw=%lld)",
+                    (long long)d->N, (long long)d->C, (long long)d->H, (long long)d->W,
+                    (long long)d->K, (long long)d->kh, (long long)d->kw);
+    if (d->stride_h < 1 || d->stride_w < 1 || d->dil_h < 1 || d->dil_w < 1 || d->pad_h < 0 ||
+        d->pad_w < 0)
+        return fail(GCONV_ERR_SHAPE, "need stride>=1, dilation>=1, pad>=0");
+    if (d->groups < 1) return fail(GCONV_ERR_GROUPS, "groups=%lld must be >= 1",
+                                   (long long)d->groups);
+    if (d->C % d->groups != 0)
+        return fail(GCONV_ERR_GROUPS, "input channels C=%lld not divisible by groups=%lld",
+                    (long long)d->C, (long long)d->groups);
+    if (d->K % d->groups != 0)
+        return fail(GCONV_ERR_GROUPS, "output channels K=%lld not divisible by groups=%lld",
+                    (long long)d->K, (long long)d->groups);
+    const int64_t dims[] = {d->N, d->C, d->H, d->W, d->K, d->kh, d->kw, d->stride_h,
+                            d->stride_w, d->pad_h, d->pad_w, d->dil_h, d->dil_w};
+    for (int64_t v : dims)
+        if (v > kMaxDim) return fail(GCONV_ERR_UNSUPPORTED, "a dimension exceeds 2^30");
+    const int64_t Ho = out_extent(d->H, d->kh, d->stride_h, d->pad_h, d->dil_h);
+    const int64_t Wo = out_extent(d->W, d->kw, d->stride_w, d->pad_w, d->dil_w);
+    if (Ho < 1 || Wo < 1)
+        return fail(GCONV_ERR_SHAPE,
+                    "empty output: the dilated kernel (%lldx%lld) exceeds the padded input",
+                    (long long)(d->dil_h * (d->kh - 1) + 1), (long long)(d->dil_w * (d->kw - 1) + 1));
+    s->N = (int)d->N; s->C = (int)d->C; s->H = (int)d->H; s->W = (int)d->W; s->K = (int)d->K;
+    s->kh = (int)d->kh; s->kw = (int)d->kw;
+    s->sh = (int)d->stride_h; s->sw = (int)d->stride_w;
+    s->ph = (int)d->pad_h; s->pw = (int)d->pad_w;
+    s->dh = (int)d->dil_h; s->dw = (int)d->dil_w;
+    s->G = (int)d->groups; s->Cg = (int)(d->C / d->groups); s->Kg = (int)(d->K / d->groups);
+    s->Ho = (int)Ho; s->Wo = (int)Wo;
+    s->x_elems = d->N * d->C * d->H * d->W;
+    s->w_elems = d->K * (d->C / d->groups) * d->kh * d->kw;
+    s->y_elems = d->N * d->K * Ho * Wo;
+    // Keep every per-image and per-filter extent in 32 bits for the kernels.
+    if ((int64_t)s->C * s->H * s->W > INT32_MAX || (int64_t)s->K * s->Ho * s->Wo > INT32_MAX ||
+        (int64_t)s->Cg * s->kh * s->kw > INT32_MAX || s->w_elems > INT32_MAX)
+        return fail(GCONV_ERR_UNSUPPORTED, "per-image or weight extent exceeds 2^31 elements");
+    return GCONV_OK;
+}
+
+bool overlap(const void* a, int64_t a_elems, const void* b, int64_t b_elems)
+{
+    if (!a || !b || a_elems == 0 || b_elems == 0) return false;
+    const char* pa = (const char*)a;
+    const char* pb = (const char*)b;
+    return pa < pb + b_elems * 4 && pb < pa + a_elems * 4;
+}
+
+// ---- routing ----------------------------------------------------------------
+
+bool path_supports(int path, const Shape& s, int op)
+{
+    (void)s;
+    if (op == GCONV_OP_BWD_BIAS) return true;  // one reduction serves every path
+    switch (path) {
+        case GCONV_PATH_DIRECT: return true;
+        default: return false;
+    }
+}
+
+int choose_path(const Shape& s, int op)
+{
+    const int forced = g_path_override.load();
+    if (forced != GCONV_PATH_AUTO) return forced;
+    (void)s;
+    (void)op;
+    return GCONV_PATH_DIRECT;
+}
+
+size_t workspace_for(const Shape& s, int op, int path)
+{
+    (void)path;
+    if (op == GCONV_OP_BWD_BIAS) return bias_workspace_bytes(s);
+    return 0;
+}
+
+// Common prologue of the four ops: shape, path, workspace checks.
+int prologue(const gconv_desc* d, int op, Shape* s, int* path, void* ws, size_t ws_bytes)
+{
+    int st = make_shape(d, s);
+    if (st != GCONV_OK) return st;
+    *path = choose_path(*s, op);
+    if (!path_supports(*path, *s, op))
+        return fail(GCONV_ERR_UNSUPPORTED, "forced path %d cannot run this descriptor for op %d",
+                    *path, op);
+    const size_t need = workspace_for(*s, op, *path);
+    if (ws_bytes < need || (need > 0 && ws == nullptr))
+        return fail(GCONV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes,
+                    need);
+    return GCONV_OK;
+}
+
+int epilogue()
+{
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(GCONV_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    g_last_error.clear();
+    return GCONV_OK;
+}
+
+}  // namespace
+}  // namespace gconv
+
+using namespace gconv;
+
+extern "C" {
+
+int gconv_output_dims(const gconv_desc* d, int64_t* Ho, int64_t* Wo)
+{
+    Shape s;
+    const int st = make_shape(d, &s);
+    if (st != GCONV_OK) return st;
+    if (!Ho || !Wo) return fail(GCONV_ERR_NULL, "output pointer is NULL");
+    *Ho = s.Ho;
+    *Wo = s.Wo;
+    return GCONV_OK;
+}
+
+int gconv_workspace_size(const gconv_desc* d, int op, size_t* bytes)
+{
+    Shape s;
+    const int st = make_shape(d, &s);
+    if (st != GCONV_OK) return st;
+    if (!bytes) return fail(GCONV_ERR_NULL, "bytes pointer is NULL");
+    if (op < GCONV_OP_FWD || op > GCONV_OP_BWD_BIAS) return fail(GCONV_ERR_ARG, "bad op %d", op);
+    *bytes = workspace_for(s, op, choose_path(s, op));
+    return GCONV_OK;
+}
+
+int gconv_select_path(const gconv_desc* d, int op, int* path)
+{
+    Shape s;
+    const int st = make_shape(d, &s);
+    if (st != GCONV_OK) return st;
+    if (!path) return fail(GCONV_ERR_NULL, "path pointer is NULL");
+    if (op < GCONV_OP_FWD || op > GCONV_OP_BWD_BIAS) return fail(GCONV_ERR_ARG, "bad op %d", op);
+    *path = choose_path(s, op);
+    return GCONV_OK;
+}
+
+int gconv_set_path_override(int path)
+{
+    if (path < GCONV_PATH_AUTO || path > GCONV_PATH_FC)
+        return fail(GCONV_ERR_ARG, "unknown path %d", path);
+    g_path_override.store(path);
+    return GCONV_OK;
+}
+
+int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* bias, float* y,
+              void* workspace, size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    int path;
+    int st = prologue(d, GCONV_OP_FWD, &s, &path, workspace, workspace_bytes);
+    if (st != GCONV_OK) return st;
+    if (!x || !w || !y) return fail(GCONV_ERR_NULL, "x, w and y must be non-NULL");
+    if (overlap(y, s.y_elems, x, s.x_elems) || overlap(y, s.y_elems, w, s.w_elems) ||
+        overlap(y, s.y_elems, bias, bias ? s.K : 0))
+        return fail(GCONV_ERR_ARG, "y overlaps an input");
+    hipStream_t hs = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (s.N == 0) return epilogue();
+    switch (path) {
+        case GCONV_PATH_DIRECT: direct_fwd(s, x, w, bias, y, hs); break;
+        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    }
+    return epilogue();
+}
+
+int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* dx,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    int path;
+    int st = prologue(d, GCONV_OP_BWD_DATA, &s, &path, workspace, workspace_bytes);
+    if (st != GCONV_OK) return st;
+    if (!dy || !w || !dx) return fail(GCONV_ERR_NULL, "dy, w and dx must be non-NULL");
+    if (overlap(dx, s.x_elems, dy, s.y_elems) || overlap(dx, s.x_elems, w, s.w_elems))
+        return fail(GCONV_ERR_ARG, "dx overlaps an input");
+    hipStream_t hs = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (s.N == 0) return epilogue();
+    switch (path) {
+        case GCONV_PATH_DIRECT: direct_bwd_data(s, dy, w, dx, hs); break;
+        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    }
+    return epilogue();
+}
+
+int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float* dw,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    int path;
+    int st = prologue(d, GCONV_OP_BWD_FILTER, &s, &path, workspace, workspace_bytes);
+    if (st != GCONV_OK) return st;
+    if (!x || !dy || !dw) return fail(GCONV_ERR_NULL, "x, dy and dw must be non-NULL");
+    if (overlap(dw, s.w_elems, x, s.x_elems) || overlap(dw, s.w_elems, dy, s.y_elems))
+        return fail(GCONV_ERR_ARG, "dw overlaps an input");
+    hipStream_t hs = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (s.N == 0) {
+        fill_zero(dw, s.w_elems, hs);  // a sum over no images
+        return epilogue();
+    }
+    switch (path) {
+        case GCONV_PATH_DIRECT: direct_bwd_filter(s, x, dy, dw, hs); break;
+        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    }
+    return epilogue();
+}
+
+int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* workspace,
+                   size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    int path;
+    int st = prologue(d, GCONV_OP_BWD_BIAS, &s, &path, workspace, workspace_bytes);
+    if (st != GCONV_OK) return st;
+    if (!dy || !db) return fail(GCONV_ERR_NULL, "dy and db must be non-NULL");
+    if (overlap(db, s.K, dy, s.y_elems)) return fail(GCONV_ERR_ARG, "db overlaps dy");
+    hipStream_t hs = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (s.N == 0) {
+        fill_zero(db, s.K, hs);
+        return epilogue();
+    }
+    bias_reduce(s, dy, db, (float*)workspace, hs);
+    return epilogue();
+}
+
+const char* gconv_status_string(int status)
+{
+    switch (status) {
+        case GCONV_OK: return "ok";
+        case GCONV_ERR_NULL: return "null pointer";
+        case GCONV_ERR_SHAPE: return "invalid shape";
+        case GCONV_ERR_GROUPS: return "channels not divisible by groups";
+        case GCONV_ERR_WORKSPACE: return "workspace too small";
+        case GCONV_ERR_HIP: return "HIP error";
+        case GCONV_ERR_UNSUPPORTED: return "unsupported";
+        case GCONV_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+const char* gconv_last_error(void) { return g_last_error.c_str(); }
+
+int gconv_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// gconv_internal.h -- shapes and launcher declarations shared by the host
+// dispatcher and the kernel translation units of the grouped-convolution
+// library. Not part of the public ABI (that is include/gconv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gconv {
+
+// A validated descriptor with the derived quantities every kernel needs.
+// 32-bit fields: the dispatcher refuses extents that do not fit.
+struct Shape {
+    int N, C, H, W, K, kh, kw;
+    int sh, sw, ph, pw, dh, dw;
+    int G, Cg, Kg;  // groups, input and output planes per group
+    int Ho, Wo;
+    // element counts (64-bit) of x, w, y
+    int64_t x_elems, w_elems, y_elems;
+};
+
+inline bool is_fc_mode(const Shape& s)
+{
+    // Kernel covers the whole (unpadded) input: the conv is one dense layer
+    // on the flattened image ("SpatialConvolution running in fully-connected
+    // mode is very slow, even with R4", the View + Linear replacement).
+    return s.kh == s.H && s.kw == s.W && s.ph == 0 && s.pw == 0 && s.Ho == 1 && s.Wo == 1;
+}
+
+// ---- general direct kernels (any valid descriptor) -------------------------
+void direct_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                hipStream_t st);
+void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
+                       hipStream_t st);
+
+// ---- reductions -------------------------------------------------------------
+// db[k] = sum over (n, p < P) of dy[(n*K + k)*P + p], P = Ho*Wo.
+size_t bias_workspace_bytes(const Shape& s);
+void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStream_t st);
+// Fill `count` floats with zero (outputs of empty-batch reductions).
+void fill_zero(float* p, int64_t count, hipStream_t st);
+
+}  // namespace gconv

@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path (through the C-ABI binding) against the CPU oracle.
+
+Bar: per element |gpu - oracle| <= 1e-5 * A_e + 1e-6, where A_e is the sum of
+|products| over that element's reduction (from the oracle); exact equality
+for integer-valued data (all partial sums exact in fp32) and for output
+shapes. Every kernel family is cross-checked by forcing it in turn.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from cases import conv_kwargs, random_descs, tensors
+from gpu_util import check, dev, gather, gpu_all_ops, sample_indices, say
+from grouped_convolution_amd.workloads import WORKLOAD_ORDER, WORKLOADS, draw, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import grouped_convolution_amd as G  # noqa: E402
+
+ALL_PATHS = [G.PATH_DIRECT, G.PATH_SMALLGROUP, G.PATH_IGEMM, G.PATH_FC]
+
+
+@pytest.fixture(autouse=True)
+def _auto_path():
+    G.gconv_set_path_override(G.PATH_AUTO)
+    yield
+    G.gconv_set_path_override(G.PATH_AUTO)
+
+
+def oracle_all(x, w, b, dy, kw):
+    return (oracle.fwd(x, w, b, **kw), oracle.bwd_data(dy, w, x.shape, **kw),
+            oracle.bwd_filter(x, dy, w.shape, **kw), oracle.bwd_bias(dy))
+
+
+def run_path(path, x, w, b, dy, kw):
+    """All four ops on one forced path; None if that path cannot run the descriptor."""
+    G.gconv_set_path_override(path)
+    try:
+        return gpu_all_ops(x, w, b, dy, **kw)
+    except G.GconvError as e:
+        if e.status == 6:          # GCONV_ERR_UNSUPPORTED: the family does not cover it
+            return None
+        raise
+    finally:
+        G.gconv_set_path_override(G.PATH_AUTO)
+
+
+def compare_full(tag, gpu, ref):
+    names = ("fwd", "bwd_data", "bwd_filter", "bwd_bias")
+    for name, g, (val, mag) in zip(names, gpu, ref):
+        assert tuple(g.shape) == val.shape, (tag, name, tuple(g.shape), val.shape)
+        check("%s %s" % (tag, name), g.cpu().numpy(), val, mag)
+
+
+# ----------------------------------------------------------------- random descriptors
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_descriptors_every_path(seed):
+    descs = random_descs(40 + seed, 24, max_hw=12, max_k=5, max_cg=6, max_kg=6, max_g=4)
+    for d in descs:
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 500 + seed)
+        y_ref, _ = oracle.fwd(x, w, b, **kw)
+        dy = draw(("normal", 1.0), y_ref.shape, 600 + seed)
+        ref = oracle_all(x, w, b, dy, kw)
+        ran = 0
+        for path in ALL_PATHS:
+            say("desc %s path %s" % (d, G.PATH_NAMES[path]))
+            out = run_path(path, x, w, b, dy, kw)
+            if out is None:
+                continue
+            ran += 1
+            compare_full("%s %s" % (G.PATH_NAMES[path], d), out, ref)
+        assert ran >= 1
+
+
+def test_ragged_shapes_span_several_tiles():
+    """Shapes whose extents are not multiples of any tile (tails in every dim)."""
+    cases = [
+        dict(N=3, C=70, H=19, W=23, K=66, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1),
+        dict(N=2, C=96, H=13, W=29, K=132, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=2),
+        dict(N=5, C=36, H=17, W=11, K=36, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=9),
+        dict(N=33, C=20, H=5, W=7, K=70, kh=5, kw=7, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+        dict(N=4, C=48, H=15, W=15, K=64, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=4),
+        dict(N=2, C=32, H=21, W=20, K=32, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=2, dw=2, G=32),
+    ]
+    for i, d in enumerate(cases):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 800 + i)
+        y, _ = oracle.fwd(x, w, b, **kw)
+        dy = draw(("normal", 1.0), y.shape, 900 + i)
+        ref = oracle_all(x, w, b, dy, kw)
+        for path in [G.PATH_AUTO] + ALL_PATHS:
+            say("ragged %s path %s" % (d, G.PATH_NAMES[path]))
+            out = run_path(path, x, w, b, dy, kw)
+            if out is not None:
+                compare_full("ragged%d %s" % (i, G.PATH_NAMES[path]), out, ref)
+
+
+# ----------------------------------------------------------------- the five workloads
+
+REDUCED_BATCH = {"tiny_grouped": 2, "dense3x3": 2, "alexnet_conv2": 2, "resnext_32x4d": 3,
+                 "fc_mode": 24}
+
+
+def wl_kwargs(wl):
+    return dict(stride=wl.stride, padding=wl.padding, dilation=wl.dilation, groups=wl.groups)
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_workload_reduced_batch_full_tensors(name):
+    """Every element, on the workload's own values cut to a few images."""
+    wl = WORKLOADS[name]
+    inp = make_inputs(name, batch=REDUCED_BATCH[name])
+    kw = wl_kwargs(wl)
+    say("workload %s reduced batch %d" % (name, REDUCED_BATCH[name]))
+    ref = oracle_all(inp["x"], inp["w"], inp["b"], inp["dy"], kw)
+    gpu = gpu_all_ops(inp["x"], inp["w"], inp["b"], inp["dy"], **kw)
+    compare_full(name, gpu, ref)
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_workload_full_size_sampled(name):
+    """Full size, the dispatcher's own path (what the benchmark times); sampled
+    elements computed one by one by the oracle."""
+    wl = WORKLOADS[name]
+    inp = make_inputs(name)
+    kw = wl_kwargs(wl)
+    x, w, b, dy = inp["x"], inp["w"], inp["b"], inp["dy"]
+    say("workload %s full size" % name)
+    y, dx, dw, db = gpu_all_ops(x, w, b, dy, **kw)
+    assert tuple(y.shape) == wl.dy_shape and tuple(dx.shape) == wl.x_shape
+    assert tuple(dw.shape) == wl.w_shape and tuple(db.shape) == (wl.w_shape[0],)
+    n = 384
+    iy = sample_indices(y.numel(), n, 1)
+    check(name + " fwd", gather(y, iy), *oracle.fwd(x, w, b, idx=iy, **kw))
+    ix = sample_indices(dx.numel(), n, 2)
+    check(name + " bwd_data", gather(dx, ix), *oracle.bwd_data(dy, w, x.shape, idx=ix, **kw))
+    iw = sample_indices(dw.numel(), 128, 3)
+    check(name + " bwd_filter", gather(dw, iw), *oracle.bwd_filter(x, dy, w.shape, idx=iw, **kw))
+    check(name + " bwd_bias", db.cpu().numpy(), *oracle.bwd_bias(dy))
+    # Smoke criteria of the clnn issue: right size, not all zeros, no NaN, no
+    # 1e-38-scale values where data is dense.
+    for t in (y, dx, dw):
+        assert torch.isfinite(t).all() and (t != 0).any()
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_workload_integer_probes_exact(name):
+    """Integer data in [-3, 3] at the workload's full shape: every partial sum is
+    an exact fp32 integer, so GPU == oracle bit for bit (index mapping, group
+    offsets, padding and shapes, whatever the summation order)."""
+    wl = WORKLOADS[name]
+    kw = wl_kwargs(wl)
+    x = draw(("int", -3, 3), wl.x_shape, 11)
+    w = draw(("int", -3, 3), wl.w_shape, 12)
+    b = draw(("int", -3, 3), (wl.w_shape[0],), 13)
+    dy = draw(("int", -3, 3), wl.dy_shape, 14)
+    say("integer probes %s" % name)
+    y, dx, dw, db = gpu_all_ops(x, w, b, dy, **kw)
+    iy = sample_indices(y.numel(), 256, 4)
+    ix = sample_indices(dx.numel(), 256, 5)
+    iw = sample_indices(dw.numel(), 96, 6)
+    assert np.array_equal(gather(y, iy), oracle.fwd(x, w, b, idx=iy, **kw)[0]), name
+    assert np.array_equal(gather(dx, ix), oracle.bwd_data(dy, w, x.shape, idx=ix, **kw)[0]), name
+    assert np.array_equal(gather(dw, iw), oracle.bwd_filter(x, dy, w.shape, idx=iw, **kw)[0]), name
+    assert np.array_equal(db.cpu().numpy().astype(np.float64), oracle.bwd_bias(dy)[0])
+
+
+def test_fc_all_ones_bit_exact():
+    """The all-ones fully-connected problem of the cudnn.torch issue: every
+    element of all four results equals its integer closed form."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fc_all_ones.json")))
+    x = torch.ones(g["x_shape"], device="cuda")
+    w = torch.ones(g["w_shape"], device="cuda")
+    b = torch.ones(g["w_shape"][0], device="cuda")
+    dy = torch.ones(g["dy_shape"], device="cuda")
+    say("fc all ones")
+    y = G.gconv_fwd(x, w, b)
+    dx = G.gconv_bwd_data(dy, w, x.shape)
+    dw = G.gconv_bwd_filter(x, dy, w.shape)
+    db = G.gconv_bwd_bias(dy)
+    torch.cuda.synchronize()
+    ex = g["expected"]
+    assert tuple(y.shape) == tuple(g["dy_shape"])
+    assert bool((y == ex["output"]).all()) and bool((dx == ex["gradInput"]).all())
+    assert bool((dw == ex["gradWeight"]).all()) and bool((db == ex["gradBias"]).all())
+
+
+# ----------------------------------------------------------------- robustness
+
+def test_deterministic_bitwise():
+    d = dict(N=4, C=64, H=20, W=20, K=64, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2)
+    kw = conv_kwargs(d)
+    x, w, b = tensors(d, 1)
+    dy = draw(("normal", 1.0), (4, 64, 20, 20), 2)
+    a = gpu_all_ops(x, w, b, dy, **kw)
+    c = gpu_all_ops(x, w, b, dy, **kw)
+    for u, v in zip(a, c):
+        assert torch.equal(u, v)
+
+
+def test_guard_bands_untouched():
+    """Outputs written into the middle of sentinel-filled buffers: no store
+    lands outside the result (tile edges)."""
+    d = dict(N=3, C=30, H=13, W=17, K=45, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=3)
+    kw = conv_kwargs(d)
+    x, w, b = tensors(d, 3)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    y_ref = G.gconv_fwd(xd, wd, bd, **kw)
+    dyd = dev(draw(("normal", 1.0), tuple(y_ref.shape), 4))
+    pad = 4096
+    for path in [G.PATH_AUTO] + ALL_PATHS:
+        G.gconv_set_path_override(path)
+        try:
+            for shape, fn in (
+                    (tuple(y_ref.shape), lambda o: G.gconv_fwd(xd, wd, bd, out=o, **kw)),
+                    (x.shape, lambda o: G.gconv_bwd_data(dyd, wd, x.shape, out=o, **kw)),
+                    (w.shape, lambda o: G.gconv_bwd_filter(xd, dyd, w.shape, out=o, **kw)),
+                    ((d["K"],), lambda o: G.gconv_bwd_bias(dyd, out=o))):
+                n = int(np.prod(shape))
+                buf = torch.full((n + 2 * pad,), 12345.0, device="cuda")
+                try:
+                    fn(buf[pad:pad + n].view(shape))
+                except G.GconvError as e:
+                    if e.status == 6:
+                        continue
+                    raise
+                torch.cuda.synchronize()
+                assert bool((buf[:pad] == 12345.0).all()) and bool((buf[pad + n:] == 12345.0).all())
+        finally:
+            G.gconv_set_path_override(G.PATH_AUTO)
+
+
+def test_empty_batch_on_gpu():
+    d = dict(N=0, C=8, H=6, W=6, K=4, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2)
+    kw = conv_kwargs(d)
+    x = torch.zeros((0, 8, 6, 6), device="cuda")
+    w = dev(tensors(d, 5)[1])
+    dy = torch.zeros((0, 4, 6, 6), device="cuda")
+    y = G.gconv_fwd(x, w, **kw)
+    dx = G.gconv_bwd_data(dy, w, x.shape, **kw)
+    dw = G.gconv_bwd_filter(x, dy, w.shape, out=torch.full(w.shape, 7.0, device="cuda"), **kw)
+    db = G.gconv_bwd_bias(dy, out=torch.full((4,), 7.0, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.shape == (0, 4, 6, 6) and dx.shape == (0, 8, 6, 6)
+    assert bool((dw == 0).all()) and bool((db == 0).all())
+
+
+def test_binding_rejects_bad_tensors():
+    x = torch.zeros((2, 8, 5, 5), device="cuda")
+    w = torch.zeros((4, 4, 3, 3), device="cuda")
+    with pytest.raises(ValueError):
+        G.gconv_fwd(x.double(), w, groups=2)
+    with pytest.raises(ValueError):
+        G.gconv_fwd(x.cpu(), w, groups=2)
+    with pytest.raises(ValueError):
+        G.gconv_fwd(x.transpose(2, 3), w, groups=2)
+    with pytest.raises(ValueError):
+        G.gconv_fwd(x, w, groups=3)
+    with pytest.raises(ValueError):
+        G.gconv_bwd_data(torch.zeros((2, 4, 4, 4), device="cuda"), w, x.shape, groups=2)
