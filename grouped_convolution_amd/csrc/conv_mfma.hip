@@ -1,0 +1,447 @@
+// conv_mfma.hip -- fp32-MFMA implicit-GEMM kernel for the forward pass and,
+// at stride 1, for gradInput. Grouped 2-D convolution, NCHW.
+//
+// Per group g the forward pass is a GEMM
+//     out[o, p] = sum_{r < Cin_g, t < kh*kw} W[o, r, t] * in[r, p shifted by tap t]
+// over output pixels p (the im2col matrix is never built). gradInput at
+// stride 1 is the same computation on dy with the filter transposed
+// (W[k, c, t] read as W'[c, k, T-1-t]) and padding (k-1)*d - p: the
+// adjoint of a stride-1 correlation is the correlation with the reversed
+// kernel. One launch covers every group: the group is a grid coordinate
+// and each group's planes are reached through offsets
+// ("[Feature request] Groups support for SpatialConvolutionMM": offsets per
+// group instead of narrowed copies, one kernel over all groups).
+//
+// Tiling (gfx950, wave64, v_mfma_f32_16x16x4f32):
+//   block  = 256 threads = 4 waves; one image, BP = 64*MP consecutive output
+//            pixels of that image, BO = 16*MO output channels of one group.
+//   wave   = 16*MP pixels x BO channels: MP x MO accumulators of 16x16.
+//   MFMA   = A: 16 pixels x 4 reduction channels (one tap), read from the
+//            LDS input tile at a per-lane pixel base plus a per-tap offset;
+//            B: 4 reduction channels x 16 output channels from the LDS
+//            weight tile; D: lane l holds pixels 4*(l/16)+v of channel l%16.
+//   LDS    = input rows covering the tile's pixels plus the kernel halo, all
+//            padded columns, CC channels; weights [tap][CC][BO] of the chunk.
+//            Zero padding is materialised in LDS, so the MFMA loop has no
+//            masks. Reduction channels advance CC at a time; the next chunk
+//            is fetched into registers while the current one is multiplied.
+#include <algorithm>
+
+#include "fastdiv.h"
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the MI355X (block b
+// runs on XCD b % 8). Renumber so that each XCD gets a contiguous range of
+// logical tiles: neighbouring tiles then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int nb)
+{
+    const int per = nb >> 3, rem = nb & 7, x = b & 7, i = b >> 3;
+    return x * per + min(x, rem) + i;
+}
+
+// Raw buffer resource over [p, p + bytes): a load whose byte offset is at or
+// past `bytes` returns 0 without touching memory, so zero padding and ragged
+// tails need no branch. `bytes` stays below 2^31, and kOOB is past it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;
+
+// 32-bit raw buffer load of a float (the builtin returns the bits as an integer).
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+struct ConvMfmaArgs {
+    const float* in;
+    const float* wgt;
+    const float* bias;
+    float* out;
+    int N, G;
+    int Cin_tot, Cin_g, Hin, Win;
+    int Cout_tot, Cout_g, Hout, Wout;
+    int sh, sw, dh, dw, ph, pw;
+    int w_so, w_sr, w_gstride;  // weight strides: output channel, reduction channel, group
+    int tiles_per_image, n_otiles;
+    int LW, LR, plane;          // LDS input tile: row width, rows, channel plane stride
+    FastDiv div_RW, div_LW, div_Wout;
+};
+
+template <int KH, int KW, int MP, int MO, int CC, int XPF, bool FLIP>
+__global__ void __launch_bounds__(256, 2) conv_mfma_kernel(ConvMfmaArgs a)
+{
+    constexpr int T = KH * KW;
+    constexpr int BO = 16 * MO;
+    constexpr int BOP = (BO % 64 == 16) ? BO : ((BO + 47) / 64) * 64 + 16;  // == 16 mod 64
+    constexpr int WP = 16 * MP;
+    constexpr int BP = 4 * WP;
+    constexpr int PARTS = 256 / BO;                   // weight loader: threads per channel
+    constexpr int WLEN = (CC * T + PARTS - 1) / PARTS;
+
+    extern __shared__ float lds[];
+    float* xs = lds;                     // [CC][plane]
+    float* ws = lds + CC * a.plane;      // [T][CC][BOP]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q = lane >> 4;
+
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int ot = bid % a.n_otiles;
+    bid /= a.n_otiles;
+    const int g = bid % a.G;
+    bid /= a.G;
+    const int pt = bid % a.tiles_per_image;
+    const int n = bid / a.tiles_per_image;
+
+    const int P = a.Hout * a.Wout;
+    const int p0 = pt * BP;
+    const int p1 = min(P, p0 + BP);
+    const int ho_first = (int)fastdiv((uint32_t)p0, a.div_Wout);
+    const int hbase = ho_first * a.sh - a.ph;
+    const int o0 = ot * BO;
+
+    // Per-lane LDS offset of each of its MP pixels (tap (0,0), channel 0).
+    // Pixels past the tile end are clamped to the last one (never stored).
+    int base[MP];
+#pragma unroll
+    for (int f = 0; f < MP; ++f) {
+        const int p = min(p0 + wave * WP + f * 16 + l16, p1 - 1);
+        const int ho = (int)fastdiv((uint32_t)p, a.div_Wout);
+        const int wo = p - ho * a.Wout;
+        base[f] = (ho - ho_first) * a.sh * a.LW + wo * a.sw;
+    }
+
+    const float* in_g = a.in + ((size_t)n * a.Cin_tot + (size_t)g * a.Cin_g) * a.Hin * a.Win;
+    const float* w_g = a.wgt + (size_t)g * a.w_gstride;
+    const int RW = a.LR * a.LW;
+    const int xtotal = CC * RW;
+
+    float xr[XPF];
+    float wr[WLEN];
+    // This block's input planes (group g of image n) and group weights.
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_g, (uint32_t)a.Cin_g * a.Hin * a.Win * 4u);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_g, (uint32_t)a.w_gstride * 4u);
+    const int dummy = CC * a.plane + T * CC * BOP;  // LDS slot that absorbs unused stores
+    const int wo_ = tid % BO, wpart = tid / BO;
+
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int k = 0; k < XPF; ++k) {
+            const int e = tid + 256 * k;
+            const int c = (int)fastdiv((uint32_t)e, a.div_RW);
+            const int rem = e - c * RW;
+            const int r = (int)fastdiv((uint32_t)rem, a.div_LW);
+            const int col = rem - r * a.LW;
+            const int h = hbase + r, w = col - a.pw;
+            // Channels past the group end fall outside the resource and read 0.
+            const bool ok = e < xtotal && (unsigned)h < (unsigned)a.Hin &&
+                            (unsigned)w < (unsigned)a.Win;
+            const uint32_t off = ok ? (uint32_t)(((c0 + c) * a.Hin + h) * a.Win + w) * 4u : kOOB;
+            xr[k] = load_f32(rx, off);
+        }
+#pragma unroll
+        for (int k = 0; k < WLEN; ++k) {
+            const int rt = wpart * WLEN + k;
+            const int r = rt / T, t = rt % T;
+            const int oo = o0 + wo_, rr = c0 + r;
+            const bool ok = wpart < PARTS && rt < CC * T && oo < a.Cout_g && rr < a.Cin_g;
+            const uint32_t off =
+                ok ? (uint32_t)(oo * a.w_so + rr * a.w_sr + (FLIP ? T - 1 - t : t)) * 4u : kOOB;
+            wr[k] = load_f32(rw, off);
+        }
+    };
+    auto store_chunk = [&]() {
+#pragma unroll
+        for (int k = 0; k < XPF; ++k) {
+            const int e = tid + 256 * k;
+            const int c = (int)fastdiv((uint32_t)e, a.div_RW);
+            xs[e < xtotal ? c * a.plane + (e - c * RW) : dummy] = xr[k];
+        }
+#pragma unroll
+        for (int k = 0; k < WLEN; ++k) {
+            const int rt = wpart * WLEN + k;
+            const int r = rt / T, t = rt % T;
+            // ws starts CC*plane floats into LDS; the dummy slot follows the weight tile.
+            ws[(wpart < PARTS && rt < CC * T) ? (t * CC + r) * BOP + wo_ : T * CC * BOP] = wr[k];
+        }
+    };
+
+    f4 acc[MP][MO];
+#pragma unroll
+    for (int f = 0; f < MP; ++f)
+#pragma unroll
+        for (int m = 0; m < MO; ++m) acc[f][m] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nchunks = (a.Cin_g + CC - 1) / CC;
+    load_chunk(0);
+    store_chunk();
+    __syncthreads();
+    const float* xq = xs + q * a.plane;
+    const float* wq = ws + q * BOP + l16;
+    for (int chunk = 0; chunk < nchunks; ++chunk) {
+        const bool more = chunk + 1 < nchunks;
+        if (more) load_chunk((chunk + 1) * CC);
+#pragma unroll 1
+        for (int cq = 0; cq < CC / 4; ++cq) {
+            // Operands of tap t+1 are read from LDS while the MFMAs of tap t
+            // run; the scheduling barrier keeps the compiler from hoisting
+            // every tap's loads (which would exhaust the register file).
+            const float* xc = xq + cq * 4 * a.plane;
+            const float* wc = wq + cq * 4 * BOP;
+            float av[2][MP], bv[2][MO];
+#pragma unroll
+            for (int f = 0; f < MP; ++f) av[0][f] = xc[base[f]];
+#pragma unroll
+            for (int m = 0; m < MO; ++m) bv[0][m] = wc[m * 16];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int cur = t & 1, nxt = cur ^ 1;
+                if (t + 1 < T) {
+                    const int i = (t + 1) / KW, j = (t + 1) % KW;
+                    const int toff = i * a.dh * a.LW + j * a.dw;
+#pragma unroll
+                    for (int f = 0; f < MP; ++f) av[nxt][f] = xc[base[f] + toff];
+#pragma unroll
+                    for (int m = 0; m < MO; ++m) bv[nxt][m] = wc[(t + 1) * CC * BOP + m * 16];
+                }
+#pragma unroll
+                for (int f = 0; f < MP; ++f)
+#pragma unroll
+                    for (int m = 0; m < MO; ++m)
+                        acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cur][f], bv[cur][m],
+                                                                         acc[f][m], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (more) {
+            __syncthreads();  // every wave is done reading this chunk
+            store_chunk();
+            __syncthreads();  // the next chunk is in LDS
+        }
+    }
+
+    // Epilogue: bias, then stores. Lane l holds pixels 4*(l/16)+v of channel l%16.
+    float* out_g = a.out + ((size_t)n * a.Cout_tot + (size_t)g * a.Cout_g) * P;
+    const bool vec4 = (P & 3) == 0;
+#pragma unroll
+    for (int m = 0; m < MO; ++m) {
+        const int o = o0 + m * 16 + l16;
+        if (o >= a.Cout_g) continue;
+        const float bv = a.bias ? a.bias[g * a.Cout_g + o] : 0.f;
+        float* orow = out_g + (size_t)o * P;
+#pragma unroll
+        for (int f = 0; f < MP; ++f) {
+            const int pb = p0 + wave * WP + f * 16 + 4 * q;
+            f4 v = acc[f][m];
+            v.x += bv;
+            v.y += bv;
+            v.z += bv;
+            v.w += bv;
+            if (vec4) {
+                if (pb < p1) *(f4*)(orow + pb) = v;
+            } else {
+                if (pb + 0 < p1) orow[pb + 0] = v.x;
+                if (pb + 1 < p1) orow[pb + 1] = v.y;
+                if (pb + 2 < p1) orow[pb + 2] = v.z;
+                if (pb + 3 < p1) orow[pb + 3] = v.w;
+            }
+        }
+    }
+}
+
+// ---- host side ------------------------------------------------------------
+
+constexpr int kMP = 4;
+constexpr int kBP = 64 * kMP;
+
+int bop_of(int BO) { return (BO % 64 == 16) ? BO : ((BO + 47) / 64) * 64 + 16; }
+
+struct Geometry {
+    int LW, LR, plane, xpf_needed;
+};
+
+Geometry tile_geometry(int Hout, int Wout, int sh, int sw, int dh, int dw, int kh, int kw, int CC)
+{
+    Geometry g;
+    g.LW = (Wout - 1) * sw + (kw - 1) * dw + 1;
+    const int rows_out = std::min(Hout, (kBP - 1) / Wout + 2);
+    g.LR = (rows_out - 1) * sh + (kh - 1) * dh + 1;
+    int plane = g.LR * g.LW;
+    plane = ((plane + 47) / 64) * 64 + 16;  // == 16 (mod 64): the 4 lane groups hit distinct banks
+    g.plane = plane;
+    g.xpf_needed = (CC * g.LR * g.LW + 255) / 256;
+    return g;
+}
+
+template <int KH, int KW, int MO, int CC, int XPF, bool FLIP>
+void launch(const ConvMfmaArgs& a, int blocks, size_t lds, hipStream_t st)
+{
+    hipLaunchKernelGGL((conv_mfma_kernel<KH, KW, kMP, MO, CC, XPF, FLIP>), dim3(blocks), dim3(256),
+                       lds, st, a);
+}
+
+template <int KH, int KW, int CC, bool FLIP>
+bool dispatch_mo_xpf(int MO, int xpf, const ConvMfmaArgs& a, int blocks, size_t lds,
+                     hipStream_t st)
+{
+#define GCONV_CASE(mo, x)                                             \
+    if (MO == mo && xpf <= x) {                                       \
+        launch<KH, KW, mo, CC, x, FLIP>(a, blocks, lds, st);          \
+        return true;                                                  \
+    }
+    if constexpr (KH * KW <= 9) {
+        GCONV_CASE(4, 16) GCONV_CASE(3, 16) GCONV_CASE(3, 24)
+        GCONV_CASE(2, 16) GCONV_CASE(2, 24) GCONV_CASE(1, 16) GCONV_CASE(1, 24)
+    } else {
+        GCONV_CASE(2, 16) GCONV_CASE(1, 16) GCONV_CASE(1, 24)
+    }
+#undef GCONV_CASE
+    return false;
+}
+
+// Problem in "forward" terms: input planes `in`, output planes `out`.
+struct Problem {
+    const float *in, *wgt, *bias;
+    float* out;
+    int N, G, Cin_tot, Cin_g, Hin, Win, Cout_tot, Cout_g, Hout, Wout;
+    int kh, kw, sh, sw, dh, dw, ph, pw;
+    int w_so, w_sr, w_gstride;
+    bool flip;
+};
+
+int choose_cc(const Problem& p) { return (p.kh * p.kw >= 16) ? 4 : 8; }
+
+// Output-channel fragments per wave: as many as the group has (up to 4), but
+// at most 2 for 25-tap filters, whose weight staging needs more registers.
+int choose_mo(const Problem& p)
+{
+    const int cap = p.kh * p.kw <= 9 ? 4 : 2;
+    return std::min(cap, (p.Cout_g + 15) / 16);
+}
+
+// The (MO, prefetch depth) instances compiled below.
+bool instance_exists(int T, int MO, int xpf)
+{
+    if (T <= 9) return (MO == 4 && xpf <= 16) || (MO <= 3 && xpf <= 24);
+    return (MO == 2 && xpf <= 16) || (MO == 1 && xpf <= 24);
+}
+
+bool problem_supported(const Problem& p)
+{
+    const bool k3 = p.kh == 3 && p.kw == 3, k5 = p.kh == 5 && p.kw == 5;
+    if (!k3 && !k5) return false;
+    if (p.Cout_g < 1 || p.Cin_g < 1) return false;
+    const int CC = choose_cc(p);
+    const Geometry geo = tile_geometry(p.Hout, p.Wout, p.sh, p.sw, p.dh, p.dw, p.kh, p.kw, CC);
+    if (geo.xpf_needed > 24) return false;
+    const int MO = choose_mo(p);
+    if (!instance_exists(p.kh * p.kw, MO, geo.xpf_needed)) return false;
+    const size_t lds =
+        ((size_t)CC * geo.plane + (size_t)p.kh * p.kw * CC * bop_of(16 * MO) + 1) * 4;
+    if (lds > 64 * 1024) return false;
+    // Buffer resources address each group's input planes and weights in bytes below 2^31.
+    // (the CC channels a chunk may read past the group end included)
+    if ((int64_t)(p.Cin_g + CC) * p.Hin * p.Win * 4 >= (int64_t(1) << 31)) return false;
+    if ((int64_t)p.w_gstride * 4 >= (int64_t(1) << 31)) return false;
+    // Per-image extents stay far below 2^31 (FastDiv and 32-bit pixel indices).
+    if ((int64_t)p.Hout * p.Wout >= (1 << 30) || (int64_t)CC * geo.LR * geo.LW >= (1 << 30))
+        return false;
+    return true;
+}
+
+bool run_problem(const Problem& p, hipStream_t st)
+{
+    const int CC = choose_cc(p);
+    const Geometry geo = tile_geometry(p.Hout, p.Wout, p.sh, p.sw, p.dh, p.dw, p.kh, p.kw, CC);
+    const int MO = choose_mo(p);
+    const int BO = 16 * MO;
+    ConvMfmaArgs a;
+    a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.N = p.N; a.G = p.G;
+    a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
+    a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
+    a.sh = p.sh; a.sw = p.sw; a.dh = p.dh; a.dw = p.dw; a.ph = p.ph; a.pw = p.pw;
+    a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
+    a.tiles_per_image = (p.Hout * p.Wout + kBP - 1) / kBP;
+    a.n_otiles = (p.Cout_g + BO - 1) / BO;
+    a.LW = geo.LW; a.LR = geo.LR; a.plane = geo.plane;
+    a.div_RW = make_fastdiv((uint32_t)(geo.LR * geo.LW));
+    a.div_LW = make_fastdiv((uint32_t)geo.LW);
+    a.div_Wout = make_fastdiv((uint32_t)p.Wout);
+    const int64_t blocks64 = (int64_t)p.N * p.G * a.tiles_per_image * a.n_otiles;
+    const int blocks = (int)blocks64;
+    const size_t lds = ((size_t)CC * geo.plane + (size_t)p.kh * p.kw * CC * bop_of(BO) + 1) * 4;
+    bool ok = false;
+    if (p.kh == 3 && CC == 8 && !p.flip) ok = dispatch_mo_xpf<3, 3, 8, false>(MO, geo.xpf_needed, a, blocks, lds, st);
+    else if (p.kh == 3 && CC == 8 && p.flip) ok = dispatch_mo_xpf<3, 3, 8, true>(MO, geo.xpf_needed, a, blocks, lds, st);
+    else if (p.kh == 5 && CC == 4 && !p.flip) ok = dispatch_mo_xpf<5, 5, 4, false>(MO, geo.xpf_needed, a, blocks, lds, st);
+    else if (p.kh == 5 && CC == 4 && p.flip) ok = dispatch_mo_xpf<5, 5, 4, true>(MO, geo.xpf_needed, a, blocks, lds, st);
+    return ok;
+}
+
+Problem fwd_problem(const Shape& s, const float* x, const float* w, const float* bias, float* y)
+{
+    Problem p;
+    p.in = x; p.wgt = w; p.bias = bias; p.out = y;
+    p.N = s.N; p.G = s.G;
+    p.Cin_tot = s.C; p.Cin_g = s.Cg; p.Hin = s.H; p.Win = s.W;
+    p.Cout_tot = s.K; p.Cout_g = s.Kg; p.Hout = s.Ho; p.Wout = s.Wo;
+    p.kh = s.kh; p.kw = s.kw; p.sh = s.sh; p.sw = s.sw; p.dh = s.dh; p.dw = s.dw;
+    p.ph = s.ph; p.pw = s.pw;
+    const int T = s.kh * s.kw;
+    p.w_so = s.Cg * T; p.w_sr = T; p.w_gstride = s.Kg * s.Cg * T;
+    p.flip = false;
+    return p;
+}
+
+// gradInput at stride 1: a forward correlation of dy with the transposed,
+// tap-reversed filter and padding (k-1)*d - p, whose output extent is H x W.
+Problem bwd_data_problem(const Shape& s, const float* dy, const float* w, float* dx)
+{
+    Problem p;
+    p.in = dy; p.wgt = w; p.bias = nullptr; p.out = dx;
+    p.N = s.N; p.G = s.G;
+    p.Cin_tot = s.K; p.Cin_g = s.Kg; p.Hin = s.Ho; p.Win = s.Wo;
+    p.Cout_tot = s.C; p.Cout_g = s.Cg; p.Hout = s.H; p.Wout = s.W;
+    p.kh = s.kh; p.kw = s.kw; p.sh = 1; p.sw = 1; p.dh = s.dh; p.dw = s.dw;
+    p.ph = (s.kh - 1) * s.dh - s.ph;
+    p.pw = (s.kw - 1) * s.dw - s.pw;
+    const int T = s.kh * s.kw;
+    p.w_so = T; p.w_sr = s.Cg * T; p.w_gstride = s.Kg * s.Cg * T;
+    p.flip = true;
+    return p;
+}
+
+}  // namespace
+
+bool igemm_fwd_supported(const Shape& s)
+{
+    return problem_supported(fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
+}
+
+bool igemm_bwd_data_supported(const Shape& s)
+{
+    if (s.sh != 1 || s.sw != 1) return false;
+    return problem_supported(bwd_data_problem(s, nullptr, nullptr, nullptr));
+}
+
+bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+               hipStream_t st)
+{
+    return run_problem(fwd_problem(s, x, w, bias, y), st);
+}
+
+bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    return run_problem(bwd_data_problem(s, dy, w, dx), st);
+}
+
+}  // namespace gconv

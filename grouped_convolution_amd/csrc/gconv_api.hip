@@ -98,20 +98,31 @@ bool overlap(const void* a, int64_t a_elems, const void* b, int64_t b_elems)
 
 bool path_supports(int path, const Shape& s, int op)
 {
-    (void)s;
     if (op == GCONV_OP_BWD_BIAS) return true;  // one reduction serves every path
     switch (path) {
         case GCONV_PATH_DIRECT: return true;
+        case GCONV_PATH_IGEMM:
+            if (op == GCONV_OP_FWD) return igemm_fwd_supported(s);
+            if (op == GCONV_OP_BWD_DATA) return igemm_bwd_data_supported(s);
+            return false;
         default: return false;
     }
 }
 
+// Static routing by shape. MFMA implicit GEMM when the per-group contraction
+// is a real dense GEMM (at least 16 output channels per group and a reduction
+// of at least 64); direct kernels otherwise.
 int choose_path(const Shape& s, int op)
 {
     const int forced = g_path_override.load();
     if (forced != GCONV_PATH_AUTO) return forced;
-    (void)s;
-    (void)op;
+    const int T = s.kh * s.kw;
+    if (op == GCONV_OP_FWD && s.Kg >= 16 && s.Cg * T >= 64 &&
+        path_supports(GCONV_PATH_IGEMM, s, op))
+        return GCONV_PATH_IGEMM;
+    if (op == GCONV_OP_BWD_DATA && s.Cg >= 16 && s.Kg * T >= 64 &&
+        path_supports(GCONV_PATH_IGEMM, s, op))
+        return GCONV_PATH_IGEMM;
     return GCONV_PATH_DIRECT;
 }
 
@@ -201,7 +212,8 @@ int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* 
     int path;
     int st = prologue(d, GCONV_OP_FWD, &s, &path, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
-    if (!x || !w || !y) return fail(GCONV_ERR_NULL, "x, w and y must be non-NULL");
+    if (!w || (s.N > 0 && (!x || !y)))
+        return fail(GCONV_ERR_NULL, "x, w and y must be non-NULL");
     if (overlap(y, s.y_elems, x, s.x_elems) || overlap(y, s.y_elems, w, s.w_elems) ||
         overlap(y, s.y_elems, bias, bias ? s.K : 0))
         return fail(GCONV_ERR_ARG, "y overlaps an input");
@@ -210,6 +222,10 @@ int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* 
     if (s.N == 0) return epilogue();
     switch (path) {
         case GCONV_PATH_DIRECT: direct_fwd(s, x, w, bias, y, hs); break;
+        case GCONV_PATH_IGEMM:
+            if (!igemm_fwd(s, x, w, bias, y, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();
@@ -222,7 +238,8 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
     int path;
     int st = prologue(d, GCONV_OP_BWD_DATA, &s, &path, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
-    if (!dy || !w || !dx) return fail(GCONV_ERR_NULL, "dy, w and dx must be non-NULL");
+    if (!w || (s.N > 0 && (!dy || !dx)))
+        return fail(GCONV_ERR_NULL, "dy, w and dx must be non-NULL");
     if (overlap(dx, s.x_elems, dy, s.y_elems) || overlap(dx, s.x_elems, w, s.w_elems))
         return fail(GCONV_ERR_ARG, "dx overlaps an input");
     hipStream_t hs = (hipStream_t)stream;
@@ -230,6 +247,10 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
     if (s.N == 0) return epilogue();
     switch (path) {
         case GCONV_PATH_DIRECT: direct_bwd_data(s, dy, w, dx, hs); break;
+        case GCONV_PATH_IGEMM:
+            if (!igemm_bwd_data(s, dy, w, dx, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();
@@ -242,7 +263,8 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
     int path;
     int st = prologue(d, GCONV_OP_BWD_FILTER, &s, &path, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
-    if (!x || !dy || !dw) return fail(GCONV_ERR_NULL, "x, dy and dw must be non-NULL");
+    if (!dw || (s.N > 0 && (!x || !dy)))
+        return fail(GCONV_ERR_NULL, "x, dy and dw must be non-NULL");
     if (overlap(dw, s.w_elems, x, s.x_elems) || overlap(dw, s.w_elems, dy, s.y_elems))
         return fail(GCONV_ERR_ARG, "dw overlaps an input");
     hipStream_t hs = (hipStream_t)stream;
@@ -265,7 +287,7 @@ int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* worksp
     int path;
     int st = prologue(d, GCONV_OP_BWD_BIAS, &s, &path, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
-    if (!dy || !db) return fail(GCONV_ERR_NULL, "dy and db must be non-NULL");
+    if (!db || (s.N > 0 && !dy)) return fail(GCONV_ERR_NULL, "dy and db must be non-NULL");
     if (overlap(db, s.K, dy, s.y_elems)) return fail(GCONV_ERR_ARG, "db overlaps dy");
     hipStream_t hs = (hipStream_t)stream;
     (void)hipGetLastError();

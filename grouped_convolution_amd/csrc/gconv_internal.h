@@ -35,6 +35,15 @@ void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
 void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
                        hipStream_t st);
 
+// ---- fp32-MFMA implicit GEMM (forward; gradInput at stride 1) ---------------
+// *_supported() tell whether the family covers a shape; the launchers return
+// false if no kernel instance matches (the dispatcher checks support first).
+bool igemm_fwd_supported(const Shape& s);
+bool igemm_bwd_data_supported(const Shape& s);
+bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+               hipStream_t st);
+bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+
 // ---- reductions -------------------------------------------------------------
 // db[k] = sum over (n, p < P) of dy[(n*K + k)*P + p], P = Ho*Wo.
 size_t bias_workspace_bytes(const Shape& s);

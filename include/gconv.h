@@ -31,6 +31,10 @@
  * overlap any input. Results are deterministic: the same inputs on the same
  * device give bit-identical outputs (no floating-point atomics).
  *
+ * Empty batch. N == 0 is valid: forward and gradInput write nothing, and
+ * gradWeight and gradBias are set to 0 (sums over no images). Pointers to
+ * tensors with no elements may be NULL.
+ *
  * Errors. Every function returns a gconv_status. Descriptor and argument
  * errors are detected on the host before anything is enqueued, and nothing
  * is written. GCONV_ERR_HIP reports a failed launch. gconv_last_error()
@@ -51,7 +55,7 @@ extern "C" {
  * Convolution descriptor. K is the total number of output planes, not the
  * per-group count. The fields follow the constructor the clnn issue quotes
  * (nInputPlane, nOutputPlane, kW, kH, dW, dH, padW, padH, groups), plus
- * batch, input extent and dilation. Valid when N,C,H,W,K,kh,kw >= 1,
+ * batch, input extent and dilation. Valid when N >= 0, C,H,W,K,kh,kw >= 1,
  * stride >= 1, dil >= 1, pad >= 0, groups >= 1, C % groups == 0,
  * K % groups == 0 and Ho, Wo >= 1 ("Support groups in DenseConvDims": the
  * channel counts must agree with the tensors and with the group split).

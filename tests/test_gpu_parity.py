@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from cases import conv_kwargs, random_descs, tensors
+from cases import conv_kwargs, fits, random_descs, tensors
 from gpu_util import check, dev, gather, gpu_all_ops, sample_indices, say
 from grouped_convolution_amd.workloads import WORKLOAD_ORDER, WORKLOADS, draw, make_inputs
 
@@ -38,24 +38,49 @@ def oracle_all(x, w, b, dy, kw):
             oracle.bwd_filter(x, dy, w.shape, **kw), oracle.bwd_bias(dy))
 
 
+OPS = ("fwd", "bwd_data", "bwd_filter", "bwd_bias")
+
+
 def run_path(path, x, w, b, dy, kw):
-    """All four ops on one forced path; None if that path cannot run the descriptor."""
+    """Each op on one forced path: a dict op -> result tensor, or None for the
+    ops that path does not cover (GCONV_ERR_UNSUPPORTED)."""
+    xd, wd, dyd = dev(x), dev(w), dev(dy)
+    bd = None if b is None else dev(b)
+    calls = {
+        "fwd": lambda: G.gconv_fwd(xd, wd, bd, **kw),
+        "bwd_data": lambda: G.gconv_bwd_data(dyd, wd, x.shape, **kw),
+        "bwd_filter": lambda: G.gconv_bwd_filter(xd, dyd, w.shape, **kw),
+        "bwd_bias": lambda: G.gconv_bwd_bias(dyd),
+    }
+    out = {}
     G.gconv_set_path_override(path)
     try:
-        return gpu_all_ops(x, w, b, dy, **kw)
-    except G.GconvError as e:
-        if e.status == 6:          # GCONV_ERR_UNSUPPORTED: the family does not cover it
-            return None
-        raise
+        for op in OPS:
+            try:
+                out[op] = calls[op]()
+            except G.GconvError as e:
+                if e.status != 6:  # GCONV_ERR_UNSUPPORTED: the family does not cover it
+                    raise
+                out[op] = None
+        torch.cuda.synchronize()
     finally:
         G.gconv_set_path_override(G.PATH_AUTO)
+    return out
 
 
 def compare_full(tag, gpu, ref):
-    names = ("fwd", "bwd_data", "bwd_filter", "bwd_bias")
-    for name, g, (val, mag) in zip(names, gpu, ref):
+    """gpu: tuple of 4 tensors, or dict op -> tensor/None. Returns ops compared."""
+    if not isinstance(gpu, dict):
+        gpu = dict(zip(OPS, gpu))
+    done = []
+    for name, (val, mag) in zip(OPS, ref):
+        g = gpu[name]
+        if g is None:
+            continue
         assert tuple(g.shape) == val.shape, (tag, name, tuple(g.shape), val.shape)
         check("%s %s" % (tag, name), g.cpu().numpy(), val, mag)
+        done.append(name)
+    return done
 
 
 # ----------------------------------------------------------------- random descriptors
@@ -69,15 +94,52 @@ def test_random_descriptors_every_path(seed):
         y_ref, _ = oracle.fwd(x, w, b, **kw)
         dy = draw(("normal", 1.0), y_ref.shape, 600 + seed)
         ref = oracle_all(x, w, b, dy, kw)
-        ran = 0
+        covered = set()
         for path in ALL_PATHS:
             say("desc %s path %s" % (d, G.PATH_NAMES[path]))
-            out = run_path(path, x, w, b, dy, kw)
-            if out is None:
-                continue
-            ran += 1
-            compare_full("%s %s" % (G.PATH_NAMES[path], d), out, ref)
-        assert ran >= 1
+            covered |= set(compare_full("%s %s" % (G.PATH_NAMES[path], d),
+                                        run_path(path, x, w, b, dy, kw), ref))
+        assert covered == set(OPS)
+
+
+def mfma_family_descs(seed, count):
+    """Random descriptors inside the MFMA family's reach: 3x3 / 5x5 filters,
+    channel counts that span several reduction chunks and output tiles (with
+    ragged tails), stride on the forward pass, dilation, groups."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        k = int(rng.choice([3, 5]))
+        G_ = int(rng.choice([1, 2, 3]))
+        d = dict(N=int(rng.integers(1, 4)), C=G_ * int(rng.integers(1, 40)),
+                 K=G_ * int(rng.integers(1, 80)), H=int(rng.integers(k, 30)),
+                 W=int(rng.integers(k, 30)), kh=k, kw=k,
+                 sh=int(rng.choice([1, 1, 2])), sw=int(rng.choice([1, 1, 2])),
+                 ph=int(rng.integers(0, k)), pw=int(rng.integers(0, k)),
+                 dh=int(rng.choice([1, 1, 2])), dw=int(rng.choice([1, 1, 2])), G=G_)
+        if fits(d["H"], d["W"], d["kh"], d["kw"], d["sh"], d["sw"], d["ph"], d["pw"], d["dh"],
+                d["dw"]):
+            out.append(d)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_descriptors_mfma_family(seed):
+    covered = {op: 0 for op in OPS}
+    for d in mfma_family_descs(70 + seed, 16):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 700 + seed)
+        y_ref, _ = oracle.fwd(x, w, b, **kw)
+        dy = draw(("normal", 1.0), y_ref.shape, 710 + seed)
+        ref = oracle_all(x, w, b, dy, kw)
+        for path in [G.PATH_AUTO] + ALL_PATHS:
+            say("mfma-family desc %s path %s" % (d, G.PATH_NAMES[path]))
+            for op in compare_full("%s %s" % (G.PATH_NAMES[path], d),
+                                   run_path(path, x, w, b, dy, kw), ref):
+                if path == G.PATH_IGEMM:
+                    covered[op] += 1
+    # the MFMA family must actually have run forward and gradInput here
+    assert covered["fwd"] >= 8 and covered["bwd_data"] >= 4, covered
 
 
 def test_ragged_shapes_span_several_tiles():
@@ -98,9 +160,8 @@ def test_ragged_shapes_span_several_tiles():
         ref = oracle_all(x, w, b, dy, kw)
         for path in [G.PATH_AUTO] + ALL_PATHS:
             say("ragged %s path %s" % (d, G.PATH_NAMES[path]))
-            out = run_path(path, x, w, b, dy, kw)
-            if out is not None:
-                compare_full("ragged%d %s" % (i, G.PATH_NAMES[path]), out, ref)
+            compare_full("ragged%d %s" % (i, G.PATH_NAMES[path]),
+                         run_path(path, x, w, b, dy, kw), ref)
 
 
 # ----------------------------------------------------------------- the five workloads
