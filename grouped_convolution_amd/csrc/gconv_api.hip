@@ -104,6 +104,7 @@ bool path_supports(int path, const Shape& s, int op)
         case GCONV_PATH_IGEMM:
             if (op == GCONV_OP_FWD) return igemm_fwd_supported(s);
             if (op == GCONV_OP_BWD_DATA) return igemm_bwd_data_supported(s);
+            if (op == GCONV_OP_BWD_FILTER) return igemm_bwd_filter_supported(s);
             return false;
         default: return false;
     }
@@ -123,13 +124,17 @@ int choose_path(const Shape& s, int op)
     if (op == GCONV_OP_BWD_DATA && s.Cg >= 16 && s.Kg * T >= 64 &&
         path_supports(GCONV_PATH_IGEMM, s, op))
         return GCONV_PATH_IGEMM;
+    if (op == GCONV_OP_BWD_FILTER && s.Cg >= 16 && s.Kg >= 16 &&
+        path_supports(GCONV_PATH_IGEMM, s, op))
+        return GCONV_PATH_IGEMM;
     return GCONV_PATH_DIRECT;
 }
 
 size_t workspace_for(const Shape& s, int op, int path)
 {
-    (void)path;
     if (op == GCONV_OP_BWD_BIAS) return bias_workspace_bytes(s);
+    if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_IGEMM && s.N > 0)
+        return igemm_bwd_filter_workspace(s);
     return 0;
 }
 
@@ -275,6 +280,10 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
     }
     switch (path) {
         case GCONV_PATH_DIRECT: direct_bwd_filter(s, x, dy, dw, hs); break;
+        case GCONV_PATH_IGEMM:
+            if (!igemm_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();

@@ -44,6 +44,12 @@ bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias
                hipStream_t st);
 bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
 
+// ---- fp32-MFMA gradWeight (split pixel reduction + deterministic reduce) -----
+bool igemm_bwd_filter_supported(const Shape& s);
+size_t igemm_bwd_filter_workspace(const Shape& s);
+bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+                      hipStream_t st);
+
 // ---- reductions -------------------------------------------------------------
 // db[k] = sum over (n, p < P) of dy[(n*K + k)*P + p], P = Ho*Wo.
 size_t bias_workspace_bytes(const Shape& s);
