@@ -215,7 +215,22 @@ def main():
                     help="also time every workload and print one line each to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (for scaling the HBM "
+                         "byte counters of a profiler run) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = 64 * 1024 * 1024                      # 64 Mi floats = 256 MiB read + 256 MiB written
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written":
+                          4 * n, "launches": 5}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "

@@ -6,20 +6,23 @@
 // For every tap (i, j) this is a GEMM over output pixels: rows = the Cg input
 // channels, columns = the Kg output channels, reduction = N*Ho*Wo pixels.
 // Each wave keeps one 16x16 accumulator per tap and per output-channel
-// fragment, so an input value read once from LDS feeds all taps' MFMAs.
+// fragment, so an input value read once from LDS feeds every tap's MFMAs and
+// a dy value feeds every tap.
 //
 //   v_mfma_f32_16x16x4f32: A = 16 input channels x 4 pixels (x at the tap's
 //   shifted position), B = 4 pixels x 16 output channels (dy), D: lane l holds
 //   dw[c = 4*(l/16)+v][k = l%16].
 //
-// The pixel reduction is split: the N*Ho output rows are cut into chunks of R
-// rows of one image, and each block reduces a contiguous run of chunks for one
-// (group, input-channel tile, output-channel tile). Blocks write partial tiles
-// to the workspace in the accumulator's own order; a second kernel sums the
-// splits in a fixed order and scatters into dw, so results are deterministic
-// (no atomics). Tiles are staged global -> LDS directly (buffer loads with an
-// LDS destination; out-of-range offsets write 0, which is the zero padding),
-// double-buffered so the next chunk streams in while this one is multiplied.
+// Block = 4 waves arranged WC (input-channel fragments) x 4/WC, each wave
+// 16 input channels x 16*WK output channels x all taps. The pixel reduction
+// is split: the N*Ho output rows are cut into chunks of R rows of one image,
+// and each block reduces a contiguous run of chunks for one (group, input tile,
+// output tile). Blocks write partial tiles to the workspace in accumulator
+// order; a second kernel sums the splits in a fixed order and scatters into
+// dw, so results are deterministic (no atomics). Tiles are staged global ->
+// LDS directly (buffer loads with an LDS destination; out-of-range offsets
+// write 0, which is the zero padding), double-buffered so the next chunk
+// streams in while this one is multiplied.
 #include <algorithm>
 
 #include "fastdiv.h"
@@ -32,6 +35,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kMaxSegX = 8;   // 64-float segments of one input-channel plane
+constexpr int kMaxSegD = 4;   // ... of one dy plane
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
 {
@@ -65,7 +70,7 @@ struct WgradArgs {
 };
 
 template <int KH, int KW, int WC, int WK, int R>
-__global__ void __launch_bounds__(256, 2) wgrad_mfma_kernel(WgradArgs a)
+__global__ void __launch_bounds__(256) wgrad_mfma_kernel(WgradArgs a)
 {
     constexpr int T = KH * KW;
     constexpr int CT = 16 * WC;
@@ -91,7 +96,34 @@ __global__ void __launch_bounds__(256, 2) wgrad_mfma_kernel(WgradArgs a)
     const int ch_begin = s * a.chunks_per_split;
     const int ch_end = min(a.chunks_total, ch_begin + a.chunks_per_split);
 
-    // Issue the loads of chunk `ch` into LDS buffer `b` (all four waves share the work).
+    // Per-lane parts of the tile loads, fixed for the whole kernel: for the
+    // segment sg of a plane, this lane's (row, column) inside the tile.
+    int xrow[kMaxSegX], xoff[kMaxSegX];
+    bool xok[kMaxSegX];
+#pragma unroll
+    for (int sg = 0; sg < kMaxSegX; ++sg) {
+        const int e = sg * 64 + lane;
+        const int r = (int)fastdiv((uint32_t)e, a.div_LW);
+        const int w = e - r * a.LW - a.pw;
+        xrow[sg] = r;
+        xoff[sg] = r * a.W + w;
+        xok[sg] = sg < a.nsx && e < a.LR * a.LW && (unsigned)w < (unsigned)a.W;
+    }
+    int drow[kMaxSegD], doff[kMaxSegD];
+    bool dok[kMaxSegD];
+#pragma unroll
+    for (int sg = 0; sg < kMaxSegD; ++sg) {
+        const int e = sg * 64 + lane;
+        const int r = (int)fastdiv((uint32_t)e, a.div_WoP);
+        const int col = e - r * a.WoP;
+        drow[sg] = r;
+        doff[sg] = r * a.Wo + col;
+        dok[sg] = sg < a.nsd && e < R * a.WoP && col < a.Wo;
+    }
+    const uint32_t xplane = (uint32_t)a.H * a.W * 4u, dplane = (uint32_t)a.Ho * a.Wo * 4u;
+
+    // Issue the loads of chunk `ch` into LDS buffer `b`: plane p of the tile is
+    // loaded by wave p % 4, one 64-float segment per instruction.
     auto issue = [&](int ch, int b) {
         float* xs = lds + b * buf_floats;
         float* ds = xs + CT * a.XS;
@@ -100,32 +132,28 @@ __global__ void __launch_bounds__(256, 2) wgrad_mfma_kernel(WgradArgs a)
         const float* xg = a.x + ((size_t)n * a.C + (size_t)g * a.Cg + c0) * a.H * a.W;
         const float* dyg = a.dy + ((size_t)n * a.K + (size_t)g * a.Kg + k0) * a.Ho * a.Wo;
         // Channels past the group end fall outside these resources and read 0.
-        const __amdgpu_buffer_rsrc_t rx =
-            make_rsrc(xg, (uint32_t)max(0, min(CT, a.Cg - c0)) * a.H * a.W * 4u);
-        const __amdgpu_buffer_rsrc_t rd =
-            make_rsrc(dyg, (uint32_t)max(0, min(KT, a.Kg - k0)) * a.Ho * a.Wo * 4u);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, (uint32_t)max(0, min(CT, a.Cg - c0)) * xplane);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, (uint32_t)max(0, min(KT, a.Kg - k0)) * dplane);
         const int hb = ho0 * a.sh - a.ph;
-        const int xlen = a.LR * a.LW;
-        for (int i = wave; i < CT * a.nsx; i += 4) {
-            const int c = i / a.nsx, sg = i - c * a.nsx;
-            const int e = sg * 64 + lane;
-            const int r = (int)fastdiv((uint32_t)e, a.div_LW);
-            const int col = e - r * a.LW;
-            const int h = hb + r, w = col - a.pw;
-            const bool ok = e < xlen && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
-            load_lds64(rx, xs + c * a.XS + sg * 64,
-                       ok ? (uint32_t)((c * a.H + h) * a.W + w) * 4u : kOOB);
+        const int row_lo = -hb, row_hi = a.H - hb;     // tile rows r with 0 <= hb + r < H
+        const int drow_hi = a.Ho - ho0;                // dy rows r with ho0 + r < Ho
+        const int xbase = hb * a.W * 4;
+#pragma unroll
+        for (int sg = 0; sg < kMaxSegX; ++sg) {
+            if (sg >= a.nsx) break;
+            const bool ok = xok[sg] && xrow[sg] >= row_lo && xrow[sg] < row_hi;
+            const uint32_t lo = (uint32_t)(xbase + xoff[sg] * 4);
+            for (int c = wave; c < CT; c += 4)
+                load_lds64(rx, xs + c * a.XS + sg * 64, ok ? lo + (uint32_t)c * xplane : kOOB);
         }
-        const int dlen = R * a.WoP;
-        for (int i = wave; i < KT * a.nsd; i += 4) {
-            const int k = i / a.nsd, sg = i - k * a.nsd;
-            const int e = sg * 64 + lane;
-            const int r = (int)fastdiv((uint32_t)e, a.div_WoP);
-            const int col = e - r * a.WoP;
-            const int ho = ho0 + r;
-            const bool ok = e < dlen && ho < a.Ho && col < a.Wo;
-            load_lds64(rd, ds + k * a.DS + sg * 64,
-                       ok ? (uint32_t)((k * a.Ho + ho) * a.Wo + col) * 4u : kOOB);
+        const int dbase = ho0 * a.Wo * 4;
+#pragma unroll
+        for (int sg = 0; sg < kMaxSegD; ++sg) {
+            if (sg >= a.nsd) break;
+            const bool ok = dok[sg] && drow[sg] < drow_hi;
+            const uint32_t lo = (uint32_t)(dbase + doff[sg] * 4);
+            for (int k = wave; k < KT; k += 4)
+                load_lds64(rd, ds + k * a.DS + sg * 64, ok ? lo + (uint32_t)k * dplane : kOOB);
         }
     };
 
@@ -146,28 +174,40 @@ __global__ void __launch_bounds__(256, 2) wgrad_mfma_kernel(WgradArgs a)
         const float* ds = xs + CT * a.XS;
         const int n = (int)fastdiv((uint32_t)ch, a.div_cpi);
         const int ho0 = (ch - n * a.chunks_per_image) * R;
-        const int rows = min(R, a.Ho - ho0);
+        const int total = min(R, a.Ho - ho0) * nsteps;  // (row, 4-pixel step) pairs
         const float* xl = xs + (wc * 16 + l16) * a.XS + q * a.sw;
         const float* dl = ds + (wk * 16 * WK + l16) * a.DS + q;
-        for (int r = 0; r < rows; ++r) {
-            const float* xr = xl + r * a.sh * a.LW;
-            const float* dr = dl + r * a.WoP;
-            for (int st = 0; st < nsteps; ++st) {
-                const int xo = st * 4 * a.sw;
-                float av[T], bv[WK];
+        // Operands of step u+1 are fetched while the MFMAs of step u run.
+        float av[2][T], bv[2][WK];
+        int r = 0, st = 0;
+        auto fetch = [&](int slot, int rr, int ss) {
+            const float* xr = xl + rr * a.sh * a.LW + ss * 4 * a.sw;
+            const float* dr = dl + rr * a.WoP + ss * 4;
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const int i = t / KW, j = t % KW;
-                    av[t] = xr[xo + i * a.dh * a.LW + j * a.dw];
+            for (int t = 0; t < T; ++t) {
+                const int i = t / KW, j = t % KW;
+                av[slot][t] = xr[i * a.dh * a.LW + j * a.dw];
+            }
+#pragma unroll
+            for (int m = 0; m < WK; ++m) bv[slot][m] = dr[m * 16 * a.DS];
+        };
+        fetch(0, 0, 0);
+        for (int u = 0; u < total; u += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                if (u + half >= total) break;
+                const int cur = half;
+                if (++st == nsteps) {
+                    st = 0;
+                    ++r;
                 }
-#pragma unroll
-                for (int m = 0; m < WK; ++m) bv[m] = dr[m * 16 * a.DS + st * 4];
+                if (u + half + 1 < total) fetch(cur ^ 1, r, st);
 #pragma unroll
                 for (int t = 0; t < T; ++t)
 #pragma unroll
                     for (int m = 0; m < WK; ++m)
-                        acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[m], acc[t][m],
-                                                                         0, 0, 0);
+                        acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cur][t], bv[cur][m],
+                                                                         acc[t][m], 0, 0, 0);
             }
         }
         __syncthreads();  // every wave is done with buffer b before it is refilled
@@ -185,7 +225,9 @@ __global__ void __launch_bounds__(256, 2) wgrad_mfma_kernel(WgradArgs a)
             for (int v = 0; v < 4; ++v) out[(t * WK + m) * 256 + v * 64 + lane] = acc[t][m][v];
 }
 
-// dw from the partial tiles: sum over splits in index order, then scatter.
+// dw from the partial tiles. Block = 32 elements x 8 split groups: thread
+// (e, sg) sums splits sg, sg+8, ... in order; the 8 group sums are then added
+// in order, so the result does not depend on scheduling.
 template <int T, int WC, int WK>
 __global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float* __restrict__ ws,
                                                            float* __restrict__ dw, int splits,
@@ -194,10 +236,18 @@ __global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float* __restri
 {
     constexpr int CT = 16 * WC;
     constexpr int KT = 16 * WK * (4 / WC);
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= per_split) return;
+    __shared__ float part[8][33];
+    const int el = threadIdx.x & 31, sg = threadIdx.x >> 5;
+    const int j = blockIdx.x * 32 + el;
     float sum = 0.f;
-    for (int s = 0; s < splits; ++s) sum += ws[(size_t)s * per_split + j];
+    if (j < per_split)
+        for (int s = sg; s < splits; s += 8) sum += ws[(size_t)s * per_split + j];
+    part[sg][el] = sum;
+    __syncthreads();
+    if (sg != 0 || j >= per_split) return;
+    sum = part[0][el];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) sum += part[i][el];
     // j = ((tile*4 + wave)*T + t)*WK*256 + m*256 + v*64 + lane
     const int lane = j & 63, v = (j >> 6) & 3;
     int rest = j >> 8;
@@ -221,17 +271,9 @@ struct Config {
     int WC, WK, R;
 };
 
-Config choose_config(const Shape& s)
-{
-    // One 16-channel input tile per wave column; four waves along output
-    // channels. Rows per chunk keep a step loop of >= ~10 quads.
-    Config c;
-    c.WC = 1;
-    c.WK = 1;
-    c.R = std::max(1, std::min(4, 64 / std::max(1, s.Wo)));
-    if (c.R > s.Ho) c.R = s.Ho;
-    return c;
-}
+// Plane stride: a multiple of 64 plus 2, so that the 16 channels x 2 pixels a
+// half-wave reads in one instruction fall in 32 distinct banks.
+int plane_stride(int nseg) { return nseg * 64 + 2; }
 
 struct Plan {
     bool ok;
@@ -242,19 +284,44 @@ struct Plan {
     int per_split;
 };
 
-int ceil64(int v) { return (v + 63) / 64 * 64; }
-
-Plan make_plan(const Shape& s, int max_splits_override = 0)
+Plan make_plan(const Shape& s)
 {
     Plan p{};
     p.ok = false;
     const bool k3 = s.kh == 3 && s.kw == 3, k5 = s.kh == 5 && s.kw == 5;
     if (!k3 && !k5) return p;
     if (s.N < 1) return p;
-    const Config cfg = choose_config(s);
-    const int CT = 16 * cfg.WC, KT = 16 * cfg.WK * (4 / cfg.WC), R = cfg.R;
     const int T = s.kh * s.kw;
+    Config cfg;
+    // Wide tiles (2x2 waves of 16 channels x 32 outputs) where the group has
+    // >= 32 input and >= 64 output channels; otherwise one input tile of 16
+    // with four waves along the outputs. 25-tap filters keep one input tile
+    // per block (their per-wave accumulators already fill 200 registers).
+    if (T <= 9 && s.Cg >= 32 && s.Kg >= 64) cfg = {2, 2, 0};
+    else if (T > 9 && s.Kg >= 128) cfg = {1, 2, 0};
+    else cfg = {1, 1, 0};
+    const int CT = 16 * cfg.WC, KT = 16 * cfg.WK * (4 / cfg.WC);
     WgradArgs& a = p.a;
+    a.WoP = (s.Wo + 3) / 4 * 4;
+    a.LW = (s.Wo - 1) * s.sw + (s.kw - 1) * s.dw + 1;
+    // Rows per chunk: about 64-112 output pixels, as many as the double-buffered
+    // tiles allow in LDS.
+    int R = std::max(1, std::min(4, 112 / std::max(1, s.Wo)));
+    if (R > s.Ho) R = s.Ho;
+    for (;; --R) {
+        if (R < 1) return p;
+        a.LR = (R - 1) * s.sh + (s.kh - 1) * s.dh + 1;
+        // The last quad of a row may reach up to 3 columns (times the stride)
+        // past the row end: keep those reads inside the loaded (zero-filled) span.
+        const int xspan = a.LR * a.LW + 4 * s.sw;
+        a.nsx = (xspan + 63) / 64;
+        a.nsd = (R * a.WoP + 63) / 64;
+        a.XS = plane_stride(a.nsx);
+        a.DS = plane_stride(a.nsd);
+        p.lds_bytes = 2 * ((size_t)CT * a.XS + (size_t)KT * a.DS) * 4;
+        if (a.nsx <= kMaxSegX && a.nsd <= kMaxSegD && p.lds_bytes <= 160 * 1024) break;
+    }
+    cfg.R = R;
     a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
     a.G = s.G; a.Cg = s.Cg; a.Kg = s.Kg;
     a.sh = s.sh; a.sw = s.sw; a.dh = s.dh; a.dw = s.dw; a.ph = s.ph; a.pw = s.pw;
@@ -264,27 +331,14 @@ Plan make_plan(const Shape& s, int max_splits_override = 0)
     const int64_t chunks_total = (int64_t)s.N * a.chunks_per_image;
     if (chunks_total >= (1 << 30)) return p;
     a.chunks_total = (int)chunks_total;
-    a.WoP = (s.Wo + 3) / 4 * 4;
-    a.LW = (s.Wo - 1) * s.sw + (s.kw - 1) * s.dw + 1;
-    a.LR = (R - 1) * s.sh + (s.kh - 1) * s.dh + 1;
-    // The last quad of a row may reach up to 3 columns (times the stride)
-    // past the row end: keep those reads inside the loaded (zero-filled) span.
-    const int xspan = a.LR * a.LW + 4 * s.sw;
-    a.nsx = (xspan + 63) / 64;
-    a.XS = a.nsx * 64 + 4;  // == 4 (mod 64): the 4 pixel lanes of a channel hit distinct banks
-    a.nsd = (R * a.WoP + 63) / 64;
-    a.DS = a.nsd * 64 + 4;
-    const size_t buf = (size_t)CT * a.XS + (size_t)KT * a.DS;
-    p.lds_bytes = 2 * buf * 4;
-    if (p.lds_bytes > 64 * 1024) return p;
-    // Tiles are addressed with 32-bit byte offsets, including the channels a
-    // tile may reach past the end of its group.
-    if ((int64_t)(s.Cg + CT) * s.H * s.W * 4 >= (int64_t(1) << 31)) return p;
-    if ((int64_t)(s.Kg + KT) * s.Ho * s.Wo * 4 >= (int64_t(1) << 31)) return p;
+    // Tiles are addressed with 32-bit byte offsets below 2^30, including the
+    // channels a tile may reach past the end of its group.
+    if ((int64_t)(s.Cg + CT) * s.H * s.W * 4 >= (int64_t(1) << 30)) return p;
+    if ((int64_t)(s.Kg + KT) * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return p;
     const int n_tiles = s.G * a.n_ctiles * a.n_ktiles;
-    // Splits: about two blocks per CU in total, at most one chunk run each.
-    int splits = std::max(1, 512 / n_tiles);
-    if (max_splits_override > 0) splits = max_splits_override;
+    // Blocks per CU that fit in LDS, and about that many blocks per CU in total.
+    const int per_cu = std::max(1, (int)((160 * 1024) / p.lds_bytes));
+    int splits = std::max(1, (256 * std::min(per_cu, 2)) / n_tiles);
     splits = std::min(splits, a.chunks_total);
     a.chunks_per_split = (a.chunks_total + splits - 1) / splits;
     splits = (a.chunks_total + a.chunks_per_split - 1) / a.chunks_per_split;
@@ -305,20 +359,33 @@ Plan make_plan(const Shape& s, int max_splits_override = 0)
 template <int KH, int KW, int WC, int WK, int R>
 void launch_main(const Plan& p, hipStream_t st)
 {
-    hipLaunchKernelGGL((wgrad_mfma_kernel<KH, KW, WC, WK, R>), dim3(p.blocks), dim3(256),
-                       p.lds_bytes, st, p.a);
+    auto kern = wgrad_mfma_kernel<KH, KW, WC, WK, R>;
+    // Allow dynamic LDS up to the CU's 160 KiB (once per kernel instance).
+    static const bool attr_set = hipFuncSetAttribute((const void*)kern,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     160 * 1024) == hipSuccess;
+    (void)attr_set;
+    hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(256), p.lds_bytes, st, p.a);
 }
 
-template <int KH, int KW>
+template <int KH, int KW, int WC, int WK>
 bool launch_r(const Plan& p, hipStream_t st)
 {
     switch (p.cfg.R) {
-        case 1: launch_main<KH, KW, 1, 1, 1>(p, st); return true;
-        case 2: launch_main<KH, KW, 1, 1, 2>(p, st); return true;
-        case 3: launch_main<KH, KW, 1, 1, 3>(p, st); return true;
-        case 4: launch_main<KH, KW, 1, 1, 4>(p, st); return true;
+        case 1: launch_main<KH, KW, WC, WK, 1>(p, st); return true;
+        case 2: launch_main<KH, KW, WC, WK, 2>(p, st); return true;
+        case 3: launch_main<KH, KW, WC, WK, 3>(p, st); return true;
+        case 4: launch_main<KH, KW, WC, WK, 4>(p, st); return true;
         default: return false;
     }
+}
+
+template <int T, int WC, int WK>
+void launch_reduce(const Plan& p, const Shape& s, float* ws, float* dw, hipStream_t st)
+{
+    const int blocks = (p.per_split + 31) / 32;
+    hipLaunchKernelGGL((wgrad_reduce_kernel<T, WC, WK>), dim3(blocks), dim3(256), 0, st, ws, dw,
+                       p.a.splits, p.a.n_ctiles, p.a.n_ktiles, s.Cg, s.Kg, p.per_split);
 }
 
 }  // namespace
@@ -335,22 +402,26 @@ bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw
                       hipStream_t st)
 {
     Plan p = make_plan(s);
-    if (!p.ok || p.cfg.WC != 1 || p.cfg.WK != 1) return false;
+    if (!p.ok) return false;
     p.a.x = x;
     p.a.dy = dy;
     p.a.ws = ws;
-    bool ok = false;
-    if (s.kh == 3) ok = launch_r<3, 3>(p, st);
-    else if (s.kh == 5) ok = launch_r<5, 5>(p, st);
-    if (!ok) return false;
-    const int T = s.kh * s.kw;
-    const int blocks = (p.per_split + 255) / 256;
-    if (T == 9)
-        hipLaunchKernelGGL((wgrad_reduce_kernel<9, 1, 1>), dim3(blocks), dim3(256), 0, st, ws, dw,
-                           p.a.splits, p.a.n_ctiles, p.a.n_ktiles, s.Cg, s.Kg, p.per_split);
-    else
-        hipLaunchKernelGGL((wgrad_reduce_kernel<25, 1, 1>), dim3(blocks), dim3(256), 0, st, ws, dw,
-                           p.a.splits, p.a.n_ctiles, p.a.n_ktiles, s.Cg, s.Kg, p.per_split);
+    const Config c = p.cfg;
+    if (s.kh == 3 && c.WC == 2 && c.WK == 2) {
+        if (!launch_r<3, 3, 2, 2>(p, st)) return false;
+        launch_reduce<9, 2, 2>(p, s, ws, dw, st);
+    } else if (s.kh == 3 && c.WC == 1 && c.WK == 1) {
+        if (!launch_r<3, 3, 1, 1>(p, st)) return false;
+        launch_reduce<9, 1, 1>(p, s, ws, dw, st);
+    } else if (s.kh == 5 && c.WC == 1 && c.WK == 2) {
+        if (!launch_r<5, 5, 1, 2>(p, st)) return false;
+        launch_reduce<25, 1, 2>(p, s, ws, dw, st);
+    } else if (s.kh == 5 && c.WC == 1 && c.WK == 1) {
+        if (!launch_r<5, 5, 1, 1>(p, st)) return false;
+        launch_reduce<25, 1, 1>(p, s, ws, dw, st);
+    } else {
+        return false;
+    }
     return true;
 }
 
