@@ -106,6 +106,7 @@ bool path_supports(int path, const Shape& s, int op)
             if (op == GCONV_OP_BWD_DATA) return igemm_bwd_data_supported(s);
             if (op == GCONV_OP_BWD_FILTER) return igemm_bwd_filter_supported(s);
             return false;
+        case GCONV_PATH_FC: return fc_supported(s);
         default: return false;
     }
 }
@@ -118,6 +119,8 @@ int choose_path(const Shape& s, int op)
     const int forced = g_path_override.load();
     if (forced != GCONV_PATH_AUTO) return forced;
     const int T = s.kh * s.kw;
+    // Kernel == input: one dense layer per group on the flattened image.
+    if (is_fc_mode(s) && path_supports(GCONV_PATH_FC, s, op)) return GCONV_PATH_FC;
     if (op == GCONV_OP_FWD && s.Kg >= 16 && s.Cg * T >= 64 &&
         path_supports(GCONV_PATH_IGEMM, s, op))
         return GCONV_PATH_IGEMM;
@@ -231,6 +234,7 @@ int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* 
             if (!igemm_fwd(s, x, w, bias, y, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
+        case GCONV_PATH_FC: fc_fwd(s, x, w, bias, y, hs); break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();
@@ -256,6 +260,7 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
             if (!igemm_bwd_data(s, dy, w, dx, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
+        case GCONV_PATH_FC: fc_bwd_data(s, dy, w, dx, hs); break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();
@@ -284,6 +289,7 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
             if (!igemm_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
+        case GCONV_PATH_FC: fc_bwd_filter(s, x, dy, dw, hs); break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();

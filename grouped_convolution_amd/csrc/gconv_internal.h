@@ -50,6 +50,13 @@ size_t igemm_bwd_filter_workspace(const Shape& s);
 bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                       hipStream_t st);
 
+// ---- fully-connected mode (kernel == input): fp32-MFMA GEMMs ----------------
+bool fc_supported(const Shape& s);
+void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+            hipStream_t st);
+void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+void fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st);
+
 // ---- reductions -------------------------------------------------------------
 // db[k] = sum over (n, p < P) of dy[(n*K + k)*P + p], P = Ho*Wo.
 size_t bias_workspace_bytes(const Shape& s);

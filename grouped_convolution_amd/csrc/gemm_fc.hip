@@ -1,0 +1,294 @@
+// gemm_fc.hip -- fully-connected mode: a convolution whose kernel covers the
+// whole unpadded input (kh == H, kw == W, no padding, so Ho = Wo = 1) is one
+// dense layer on the flattened image ("SpatialConvolution running in
+// fully-connected mode is very slow, even with R4": MatConvNet switches to a
+// fully-connected layer there, and the View + Linear replacement gives the same
+// result). With X = x.view(N, C*H*W) and Wm = w.view(K, C*kh*kw), per group:
+//     forward     Y  = X  * Wm^T + b     (M = N, cols = K,   reduction = D)
+//     gradInput   dX = dY * Wm           (M = N, cols = D,   reduction = K)
+//     gradWeight  dW = dY^T * X          (M = K, cols = D,   reduction = N)
+// All three run on one fp32-MFMA GEMM kernel, C[M x Nc] = A[M x R] * B[R x Nc],
+// templated on which index of A and of B is contiguous in memory.
+//
+// Block tile 128 x 128, reduction stages of 32, four waves of 64 x 64 each
+// (4 x 4 accumulators of v_mfma_f32_16x16x4f32). Stages are copied global ->
+// LDS directly (buffer loads with an LDS destination; out-of-range offsets
+// write 0), double-buffered. An operand whose reduction index is contiguous is
+// kept as [row][32] with its 16-byte chunks XOR-swizzled by row, and each lane
+// reads 4 consecutive reduction values with one 128-bit LDS read; the MFMA
+// steps consume them in a permuted order (any bijection of the reduction index
+// applied to both operands leaves the sum unchanged). An operand whose row
+// index is contiguous is kept as [32][row + 4]. The MFMA's A/B roles are
+// swapped so that each lane ends up holding 4 consecutive output columns,
+// stored as one 16-byte write.
+#include <algorithm>
+
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int BM = 128, BN = 128, BR = 32;
+constexpr int SROW = BM + 4;          // row stride of a [32][row] tile (== 4 mod 8)
+constexpr int TILE_R = BM * BR;       // floats of a swizzled [row][32] tile
+constexpr int TILE_N = BR * SROW;     // floats of a [32][row + 4] tile
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
+}
+
+__device__ __forceinline__ int xcd_remap(int b, int nb)
+{
+    const int per = nb >> 3, rem = nb & 7, x = b & 7, i = b >> 3;
+    return x * per + min(x, rem) + i;
+}
+
+struct GemmArgs {
+    const float* A;
+    const float* B;
+    const float* bias;
+    float* C;
+    int M, N, R, G;
+    int a_ld, b_ld, c_ld;          // leading dimension of A, B, C (their non-unit stride)
+    int64_t a_gs, b_gs, c_gs, bias_gs;  // group offsets (floats)
+    uint32_t a_bytes, b_bytes;     // extent each group's A / B resource may address
+    int m_tiles, n_tiles;
+};
+
+// Load one 32-deep stage of an operand into LDS.
+//   RCONTIG: element (row, r) at P[row*ld + r]; LDS [row][32], chunk c of row
+//            `row` stored at chunk position c ^ (row & 7).
+//   else:    element (row, r) at P[r*ld + row]; LDS [r][SROW].
+template <bool RCONTIG>
+__device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, float* dst, int row0, int rows,
+                                           int r0, int R, int ld, int wave, int lane)
+{
+    if constexpr (RCONTIG) {
+        // 64 instructions of 64 floats = 2 rows of 32 each.
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = wave + 4 * k;
+            const int row = 2 * i + (lane >> 5);
+            const int chunk = ((lane & 31) >> 2) ^ (row & 7);
+            const int r = 4 * chunk + (lane & 3);
+            const bool ok = row0 + row < rows && r0 + r < R;
+            load_lds64(rs, dst + i * 64,
+                       ok ? (uint32_t)((row0 + row) * ld + r0 + r) * 4u : kOOB);
+        }
+    } else {
+        // 32 rows of 128 floats = 2 instructions per row.
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = wave + 4 * k;
+            const int r = i >> 1, h = i & 1;
+            const int row = h * 64 + lane;
+            const bool ok = r0 + r < R && row0 + row < rows;
+            load_lds64(rs, dst + r * SROW + h * 64,
+                       ok ? (uint32_t)((r0 + r) * ld + row0 + row) * 4u : kOOB);
+        }
+    }
+}
+
+// Operand values of one 16-deep reduction group (4 MFMA steps) for fragment
+// rows row0..row0+15 of an LDS stage: v[s] feeds MFMA step s.
+template <bool RCONTIG>
+__device__ __forceinline__ f4 frag(const float* t, int row, int kg, int q)
+{
+    if constexpr (RCONTIG) {
+        const int chunk = (kg * 4 + q) ^ (row & 7);
+        return *(const f4*)(t + row * BR + chunk * 4);
+    } else {
+        const int r = kg * 16 + q * 4;
+        return f4{t[(r + 0) * SROW + row], t[(r + 1) * SROW + row], t[(r + 2) * SROW + row],
+                  t[(r + 3) * SROW + row]};
+    }
+}
+
+template <bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
+{
+    constexpr int TA = A_RC ? TILE_R : TILE_N;
+    constexpr int TB = B_RC ? TILE_R : TILE_N;
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;  // wave's 64x64 quadrant
+
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int mt = bid % a.m_tiles;
+    bid /= a.m_tiles;
+    const int nt = bid % a.n_tiles;
+    const int g = bid / a.n_tiles;
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A + g * a.a_gs, a.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B + g * a.b_gs, a.b_bytes);
+
+    f4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int stage, int b) {
+        float* ta = lds + b * (TA + TB);
+        float* tb = ta + TA;
+        load_stage<A_RC>(ra, ta, m0, a.M, stage * BR, a.R, a.a_ld, wave, lane);
+        load_stage<B_RC>(rb, tb, n0, a.N, stage * BR, a.R, a.b_ld, wave, lane);
+    };
+
+    const int nst = (a.R + BR - 1) / BR;
+    issue(0, 0);
+    for (int st = 0; st < nst; ++st) {
+        const int b = st & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (st + 1 < nst) issue(st + 1, b ^ 1);
+        const float* ta = lds + b * (TA + TB);
+        const float* tb = ta + TA;
+#pragma unroll
+        for (int kg = 0; kg < BR / 16; ++kg) {
+            f4 av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[i] = frag<A_RC>(ta, wm * 64 + i * 16 + l16, kg, q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = frag<B_RC>(tb, wn * 64 + j * 16 + l16, kg, q);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        // A role <- B operand, B role <- A operand: lane l then
+                        // holds C[m = l%16][n = 4*(l/16) + v].
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[j][s], av[i][s],
+                                                                         acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    float* Cg = a.C + g * a.c_gs;
+    const float* bias = a.bias ? a.bias + g * a.bias_gs : nullptr;
+    const bool vec = (a.N & 3) == 0 && (a.c_ld & 3) == 0 && ((uintptr_t)Cg & 15) == 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 64 + j * 16 + 4 * q;
+        f4 bv = f4{0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+            bv.x = n + 0 < a.N ? bias[n + 0] : 0.f;
+            bv.y = n + 1 < a.N ? bias[n + 1] : 0.f;
+            bv.z = n + 2 < a.N ? bias[n + 2] : 0.f;
+            bv.w = n + 3 < a.N ? bias[n + 3] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wm * 64 + i * 16 + l16;
+            if (m >= a.M) continue;
+            const f4 v = acc[i][j] + bv;
+            float* row = Cg + (size_t)m * a.c_ld;
+            if (vec && n + 3 < a.N) {
+                *(f4*)(row + n) = v;
+            } else {
+                if (n + 0 < a.N) row[n + 0] = v.x;
+                if (n + 1 < a.N) row[n + 1] = v.y;
+                if (n + 2 < a.N) row[n + 2] = v.z;
+                if (n + 3 < a.N) row[n + 3] = v.w;
+            }
+        }
+    }
+}
+
+template <bool A_RC, bool B_RC>
+void launch(GemmArgs& a, hipStream_t st)
+{
+    constexpr int TA = A_RC ? TILE_R : TILE_N;
+    constexpr int TB = B_RC ? TILE_R : TILE_N;
+    const size_t lds = 2 * (size_t)(TA + TB) * 4;
+    a.m_tiles = (a.M + BM - 1) / BM;
+    a.n_tiles = (a.N + BN - 1) / BN;
+    const int blocks = a.m_tiles * a.n_tiles * a.G;
+    auto kern = gemm_fc_kernel<A_RC, B_RC>;
+    static const bool attr = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 160 * 1024) == hipSuccess;
+    (void)attr;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, st, a);
+}
+
+// Byte extent of one group's operand: rows x leading dimension (the last row
+// only as far as it is used), which must stay below 2^30.
+bool extent_ok(int64_t rows, int64_t ld, int64_t used_last)
+{
+    const int64_t e = ((rows - 1) * ld + used_last) * 4;
+    return e > 0 && e < (int64_t(1) << 30);
+}
+
+}  // namespace
+
+bool fc_supported(const Shape& s)
+{
+    if (!is_fc_mode(s)) return false;
+    const int64_t D = (int64_t)s.Cg * s.kh * s.kw;     // per-group flattened extent
+    const int64_t Dt = (int64_t)s.C * s.H * s.W;        // full row of x
+    if (s.N < 1) return false;
+    // A and B resources of every op (see the launchers below).
+    return extent_ok(s.N, Dt, D) && extent_ok(s.N, s.K, s.Kg) && extent_ok(s.Kg, D, D) &&
+           D < (1 << 30) && s.w_elems < (int64_t(1) << 28);
+}
+
+// y[n, g*Kg + k] = sum_d x[n, g*D + d] * w[g*Kg + k, d] + b
+void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+            hipStream_t st)
+{
+    const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
+    GemmArgs a{};
+    a.A = x; a.B = w; a.bias = bias; a.C = y;
+    a.M = s.N; a.N = s.Kg; a.R = D; a.G = s.G;
+    a.a_ld = Dt; a.b_ld = D; a.c_ld = s.K;
+    a.a_gs = D; a.b_gs = (int64_t)s.Kg * D; a.c_gs = s.Kg; a.bias_gs = s.Kg;
+    a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * Dt + D) * 4);
+    a.b_bytes = (uint32_t)((int64_t)s.Kg * D * 4);
+    launch<true, true>(a, st);
+}
+
+// dx[n, g*D + d] = sum_k dy[n, g*Kg + k] * w[g*Kg + k, d]
+void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
+    GemmArgs a{};
+    a.A = dy; a.B = w; a.bias = nullptr; a.C = dx;
+    a.M = s.N; a.N = D; a.R = s.Kg; a.G = s.G;
+    a.a_ld = s.K; a.b_ld = D; a.c_ld = Dt;
+    a.a_gs = s.Kg; a.b_gs = (int64_t)s.Kg * D; a.c_gs = D; a.bias_gs = 0;
+    a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.K + s.Kg) * 4);
+    a.b_bytes = (uint32_t)((int64_t)s.Kg * D * 4);
+    launch<true, false>(a, st);
+}
+
+// dw[g*Kg + k, d] = sum_n dy[n, g*Kg + k] * x[n, g*D + d]
+void fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st)
+{
+    const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
+    GemmArgs a{};
+    a.A = dy; a.B = x; a.bias = nullptr; a.C = dw;
+    a.M = s.Kg; a.N = D; a.R = s.N; a.G = s.G;
+    a.a_ld = s.K; a.b_ld = Dt; a.c_ld = D;
+    a.a_gs = s.Kg; a.b_gs = D; a.c_gs = (int64_t)s.Kg * D; a.bias_gs = 0;
+    a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.K + s.Kg) * 4);
+    a.b_bytes = (uint32_t)(((int64_t)(s.N - 1) * Dt + D) * 4);
+    launch<false, false>(a, st);
+}
+
+}  // namespace gconv

@@ -142,6 +142,43 @@ def test_random_descriptors_mfma_family(seed):
     assert covered["fwd"] >= 8 and covered["bwd_data"] >= 4, covered
 
 
+@pytest.mark.parametrize("seed", range(2))
+def test_fc_mode_random(seed):
+    """Kernel == input (fully-connected mode), with groups and ragged M / N / R,
+    through the GEMM path and every other path that covers it."""
+    rng = np.random.default_rng(90 + seed)
+    fc_ran = 0
+    for _ in range(8):
+        G_ = int(rng.choice([1, 1, 2, 3]))
+        H, W = int(rng.integers(1, 7)), int(rng.integers(1, 7))
+        d = dict(N=int(rng.integers(1, 300)), C=G_ * int(rng.integers(1, 40)),
+                 K=G_ * int(rng.integers(1, 150)), H=H, W=W, kh=H, kw=W, sh=1, sw=1,
+                 ph=0, pw=0, dh=1, dw=1, G=G_)
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 900 + seed)
+        dy = draw(("normal", 1.0), (d["N"], d["K"], 1, 1), 910 + seed)
+        ref = oracle_all(x, w, b, dy, kw)
+        for path in [G.PATH_AUTO, G.PATH_FC, G.PATH_DIRECT]:
+            say("fc desc %s path %s" % (d, G.PATH_NAMES[path]))
+            done = compare_full("%s %s" % (G.PATH_NAMES[path], d), run_path(path, x, w, b, dy, kw),
+                                ref)
+            if path == G.PATH_FC:
+                fc_ran += len(done) >= 3
+    assert fc_ran == 8
+
+
+def test_fc_1x1_on_1x1_is_linear():
+    """A 1x1 convolution of a 1x1 input (the Linear(128, 32) case of the
+    cudnn.torch issue) runs the GEMM path and matches the oracle."""
+    d = dict(N=16, C=128, H=1, W=1, K=32, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1)
+    kw = conv_kwargs(d)
+    x, w, b = tensors(d, 950)
+    dy = draw(("normal", 1.0), (16, 32, 1, 1), 951)
+    desc = G.make_desc(16, 128, 1, 1, 32, 1, 1)
+    assert G.gconv_select_path(desc, G.OP_FWD) == G.PATH_FC
+    compare_full("linear", run_path(G.PATH_AUTO, x, w, b, dy, kw), oracle_all(x, w, b, dy, kw))
+
+
 def test_ragged_shapes_span_several_tiles():
     """Shapes whose extents are not multiples of any tile (tails in every dim)."""
     cases = [
