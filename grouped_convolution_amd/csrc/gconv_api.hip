@@ -107,6 +107,11 @@ bool path_supports(int path, const Shape& s, int op)
             if (op == GCONV_OP_BWD_FILTER) return igemm_bwd_filter_supported(s);
             return false;
         case GCONV_PATH_FC: return fc_supported(s);
+        case GCONV_PATH_SMALLGROUP:
+            if (op == GCONV_OP_FWD) return smallgroup_fwd_supported(s);
+            if (op == GCONV_OP_BWD_DATA) return smallgroup_bwd_data_supported(s);
+            if (op == GCONV_OP_BWD_FILTER) return smallgroup_bwd_filter_supported(s);
+            return false;
         default: return false;
     }
 }
@@ -121,6 +126,9 @@ int choose_path(const Shape& s, int op)
     const int T = s.kh * s.kw;
     // Kernel == input: one dense layer per group on the flattened image.
     if (is_fc_mode(s) && path_supports(GCONV_PATH_FC, s, op)) return GCONV_PATH_FC;
+    // A handful of channels per group (ResNeXt-style, depthwise-like): the
+    // HBM-bound 4x4x1-MFMA kernels.
+    if (path_supports(GCONV_PATH_SMALLGROUP, s, op)) return GCONV_PATH_SMALLGROUP;
     if (op == GCONV_OP_FWD && s.Kg >= 16 && s.Cg * T >= 64 &&
         path_supports(GCONV_PATH_IGEMM, s, op))
         return GCONV_PATH_IGEMM;
@@ -138,6 +146,8 @@ size_t workspace_for(const Shape& s, int op, int path)
     if (op == GCONV_OP_BWD_BIAS) return bias_workspace_bytes(s);
     if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_IGEMM && s.N > 0)
         return igemm_bwd_filter_workspace(s);
+    if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_SMALLGROUP && s.N > 0)
+        return smallgroup_bwd_filter_workspace(s);
     return 0;
 }
 
@@ -235,6 +245,10 @@ int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* 
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
         case GCONV_PATH_FC: fc_fwd(s, x, w, bias, y, hs); break;
+        case GCONV_PATH_SMALLGROUP:
+            if (!smallgroup_fwd(s, x, w, bias, y, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
+            break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();
@@ -261,6 +275,10 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
         case GCONV_PATH_FC: fc_bwd_data(s, dy, w, dx, hs); break;
+        case GCONV_PATH_SMALLGROUP:
+            if (!smallgroup_bwd_data(s, dy, w, dx, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
+            break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();
@@ -290,6 +308,10 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
         case GCONV_PATH_FC: fc_bwd_filter(s, x, dy, dw, hs); break;
+        case GCONV_PATH_SMALLGROUP:
+            if (!smallgroup_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
+            break;
         default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
     }
     return epilogue();

@@ -50,6 +50,18 @@ size_t igemm_bwd_filter_workspace(const Shape& s);
 bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                       hipStream_t st);
 
+// ---- few channels per group: v_mfma_f32_4x4x1 kernels (HBM-bound shapes) ------
+bool smallgroup_fwd_supported(const Shape& s);
+bool smallgroup_bwd_data_supported(const Shape& s);
+bool smallgroup_bwd_filter_supported(const Shape& s);
+size_t smallgroup_bwd_filter_workspace(const Shape& s);
+bool smallgroup_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                    hipStream_t st);
+bool smallgroup_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
+                         hipStream_t st);
+bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+                           hipStream_t st);
+
 // ---- fully-connected mode (kernel == input): fp32-MFMA GEMMs ----------------
 bool fc_supported(const Shape& s);
 void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,

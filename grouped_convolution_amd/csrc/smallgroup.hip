@@ -1,0 +1,521 @@
+// smallgroup.hip -- grouped 2-D convolution (NCHW fp32) when each group has only
+// a few channels (ResNeXt-style 4-in / 4-out groups, depthwise-like shapes).
+// Such a layer moves ~9 FLOP per byte, so it is HBM-bound; the point is to read
+// x (or dy) once and write y (or dx) once with full-width coalesced accesses,
+// while the arithmetic runs on v_mfma_f32_4x4x1f32 (sixteen independent 4x4
+// outer products per instruction, the full fp32 matrix rate).
+//
+// Forward / gradInput (stride 1; gradInput is the forward correlation of dy
+// with the transposed, tap-reversed filter):
+//   lane l of a wave owns output pixel p0 + l; MFMA block b = l/4 holds pixels
+//   4b..4b+3. Per (input channel, tap): A = the filter value of output channel
+//   4*oq + l%4 (kept in registers for the whole kernel), B = the input value at
+//   the lane's pixel shifted by the tap (LDS), and lane l ends up holding its
+//   pixel's four output channels (acc[v] = channel 4*oq + v). One block = 256
+//   consecutive output pixels of one (image, group); the input rows they touch
+//   (with halo and zero padding) are staged in LDS.
+//
+// gradWeight: dw[k, c, tap] = sum_pixels dy[k, p] * x[c, p + tap]. MFMA block b
+//   takes pixel P + b of a 16-pixel step: A = dy of channel l%4 at that pixel
+//   (read straight from memory, reused by all taps), B = x of channel l%4 at the
+//   pixel shifted by the tap (LDS). Each block accumulates its own pixels; at
+//   the end the 16 blocks are summed across lanes, then the 4 waves through LDS,
+//   in a fixed order. One workgroup per (image, group) writes a partial to the
+//   workspace and a second kernel sums the images in order.
+#include <algorithm>
+
+#include "fastdiv.h"
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ int xcd_remap(int b, int nb)
+{
+    const int per = nb >> 3, rem = nb & 7, x = b & 7, i = b >> 3;
+    return x * per + min(x, rem) + i;
+}
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// forward / gradInput
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 64 lanes load one dword each into 64 consecutive LDS floats at `dst`
+// (out-of-range offsets write 0).
+__device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
+}
+
+struct SgArgs {
+    const float* in;
+    const float* wgt;
+    const float* bias;
+    float* out;
+    int N, G;
+    int Cin_tot, Cin_g, Hin, Win;
+    int Cout_tot, Cout_g, Hout, Wout;
+    int sh, sw, dh, dw, ph, pw;
+    int w_so, w_sr, w_gstride;
+    int R, nbands;              // output rows per workgroup, bands per plane
+    int LW, LR, plane;          // LDS input tile: row width, rows, plane floats
+    FastDiv div_plane, div_LW, div_Wout;
+};
+
+// One workgroup = R output rows of one (image, group) plane. Its input rows
+// (with halo; zero padding from out-of-range loads) are copied global -> LDS
+// directly, so no registers hold staged data and many workgroups per CU keep
+// their loads in flight; the filters of this group sit in registers.
+template <int KH, int KW, int CIN, int OQ, bool FLIP>
+__global__ void __launch_bounds__(256) sg_conv_kernel(SgArgs a)
+{
+    constexpr int T = KH * KW;
+    constexpr int NW = CIN * T * 4 * OQ;     // staged filter values
+    extern __shared__ float lds[];           // [CIN][plane] (64-float aligned end), filters
+    const int xfloats = (CIN * a.plane + 63) / 64 * 64;
+    float* wl = lds + xfloats;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int band = bid % a.nbands;
+    bid /= a.nbands;
+    const int g = bid % a.G;
+    const int n = bid / a.G;
+    const int ho0 = band * a.R;
+    const int rows = min(a.R, a.Hout - ho0);
+    const int hbase = ho0 * a.sh - a.ph;
+
+    const float* in_g = a.in + ((size_t)n * a.Cin_tot + (size_t)g * a.Cin_g) * a.Hin * a.Win;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_g, (uint32_t)a.Cin_g * a.Hin * a.Win * 4u);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(a.wgt + (size_t)g * a.w_gstride, (uint32_t)a.w_gstride * 4u);
+
+    // Input tile: element e = c*plane + r*LW + col, 64 per instruction.
+    for (int i = wave; i < xfloats / 64; i += 4) {
+        const int e = i * 64 + lane;
+        const int c = (int)fastdiv((uint32_t)e, a.div_plane);
+        const int rem = e - c * a.plane;
+        const int r = (int)fastdiv((uint32_t)rem, a.div_LW);
+        const int w = rem - r * a.LW - a.pw;
+        const int h = hbase + r;
+        const bool ok = c < CIN && (unsigned)h < (unsigned)a.Hin && (unsigned)w < (unsigned)a.Win;
+        load_lds64(rx, lds + i * 64, ok ? (uint32_t)((c * a.Hin + h) * a.Win + w) * 4u : kOOB);
+    }
+    // Filters -> LDS as [(c*T + t)][o] (zeros past the group's channels).
+    for (int e = tid; e < NW; e += 256) {
+        const int o = e % (4 * OQ), ct = e / (4 * OQ), c = ct / T, t = ct % T;
+        const bool ok = o < a.Cout_g && c < a.Cin_g;
+        wl[e] = load_f32(rw, ok ? (uint32_t)(o * a.w_so + c * a.w_sr + (FLIP ? T - 1 - t : t)) * 4u : kOOB);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    float wv[CIN][T][OQ];
+#pragma unroll
+    for (int c = 0; c < CIN; ++c)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int oq = 0; oq < OQ; ++oq) wv[c][t][oq] = wl[(c * T + t) * 4 * OQ + oq * 4 + (lane & 3)];
+    float bv[OQ][4];
+#pragma unroll
+    for (int oq = 0; oq < OQ; ++oq)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int o = oq * 4 + v;
+            bv[oq][v] = (a.bias && o < a.Cout_g) ? a.bias[g * a.Cout_g + o] : 0.f;
+        }
+
+    const int P = a.Hout * a.Wout;
+    float* out_g = a.out + ((size_t)n * a.Cout_tot + (size_t)g * a.Cout_g) * P + (size_t)ho0 * a.Wout;
+    const int npix = rows * a.Wout;
+    for (int s = wave * 64; s < npix; s += 256) {
+        const int pl = s + lane;
+        const int pc = min(pl, npix - 1);
+        const int r = (int)fastdiv((uint32_t)pc, a.div_Wout);
+        const int base = r * a.sh * a.LW + (pc - r * a.Wout) * a.sw;
+        f4 acc[OQ];
+#pragma unroll
+        for (int oq = 0; oq < OQ; ++oq) acc[oq] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CIN; ++c)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int i = t / KW, j = t % KW;
+                const float xv = lds[c * a.plane + base + i * a.dh * a.LW + j * a.dw];
+#pragma unroll
+                for (int oq = 0; oq < OQ; ++oq) acc[oq] = mfma4(wv[c][t][oq], xv, acc[oq]);
+            }
+        if (pl < npix) {
+#pragma unroll
+            for (int oq = 0; oq < OQ; ++oq)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int o = oq * 4 + v;
+                    if (o < a.Cout_g) out_g[(size_t)o * P + pl] = acc[oq][v] + bv[oq][v];
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gradWeight
+// ---------------------------------------------------------------------------
+
+struct SgWArgs {
+    const float* x;
+    const float* dy;
+    float* ws;
+    int N, C, H, W, K, Ho, Wo, G, Cg, Kg;
+    int sh, sw, dh, dw, ph, pw;
+    int R, nbands, LW, LR, plane;   // input band
+    int dplane;                     // dy band plane stride (== 8 mod 32)
+    FastDiv div_plane, div_LW, div_Wo, div_dband;
+};
+
+// One workgroup per (image, group, band of R output rows): the band's input
+// rows and dy rows are copied global -> LDS directly; 16-pixel MFMA steps are
+// spread over the four waves. Partial sums go to the workspace per band.
+template <int KH, int KW>
+__global__ void __launch_bounds__(256) sg_wgrad_kernel(SgWArgs a)
+{
+    constexpr int T = KH * KW;
+    extern __shared__ float lds[];  // [4][plane] input, [4][dplane] dy; later [4][T*16] sums
+    const int xfloats = (4 * a.plane + 63) / 64 * 64;
+    float* ds = lds + xfloats;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c4 = lane & 3, blk = lane >> 2;  // this lane's channel (c and k), MFMA block
+
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int band = bid % a.nbands;
+    bid /= a.nbands;
+    const int g = bid % a.G;
+    const int n = bid / a.G;
+    const int ho0 = band * a.R;
+    const int rows = min(a.R, a.Ho - ho0);
+    const int hb = ho0 * a.sh - a.ph;
+    const int npix = rows * a.Wo;
+
+    const float* xg = a.x + ((size_t)n * a.C + (size_t)g * a.Cg) * a.H * a.W;
+    const float* dyg = a.dy + ((size_t)n * a.K + (size_t)g * a.Kg) * a.Ho * a.Wo + (size_t)ho0 * a.Wo;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, (uint32_t)a.Cg * a.H * a.W * 4u);
+    // dy rows of this band, channel stride Ho*Wo; the resource ends after the
+    // group's last channel so channels past Kg read 0.
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(dyg, (uint32_t)(((a.Kg - 1) * a.Ho + (a.Ho - ho0)) * a.Wo) * 4u);
+
+    for (int i = wave; i < xfloats / 64; i += 4) {
+        const int e = i * 64 + lane;
+        const int c = (int)fastdiv((uint32_t)e, a.div_plane);
+        const int rem = e - c * a.plane;
+        const int r = (int)fastdiv((uint32_t)rem, a.div_LW);
+        const int w = rem - r * a.LW - a.pw;
+        const int h = hb + r;
+        const bool ok = c < 4 && (unsigned)h < (unsigned)a.H && (unsigned)w < (unsigned)a.W;
+        load_lds64(rx, lds + i * 64, ok ? (uint32_t)((c * a.H + h) * a.W + w) * 4u : kOOB);
+    }
+    // dy band: per channel, R*Wo contiguous floats into a plane of dplane.
+    const int nseg = (a.dplane - 8) / 64;  // dplane = 64*nseg + 8: segments stay in the plane
+    for (int i = wave; i < 4 * nseg; i += 4) {
+        const int k = i / nseg, sg = i - k * nseg;
+        const int e = sg * 64 + lane;
+        const bool ok = k < a.Kg && e < npix;
+        load_lds64(rd, ds + k * a.dplane + sg * 64,
+                   ok ? (uint32_t)(k * a.Ho * a.Wo + e) * 4u : kOOB);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    f4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int s = wave * 16; s < npix; s += 64) {
+        const int pl = min(s + blk, npix - 1);
+        const float dv = (s + blk < npix) ? ds[c4 * a.dplane + pl] : 0.f;
+        const int r = (int)fastdiv((uint32_t)pl, a.div_Wo);
+        const int base = c4 * a.plane + r * a.sh * a.LW + (pl - r * a.Wo) * a.sw;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int ii = t / KW, jj = t % KW;
+            acc[t] = mfma4(dv, lds[base + ii * a.dh * a.LW + jj * a.dw], acc[t]);
+        }
+    }
+
+    // acc[t][v] of lane l = sum over its block's pixels of dy[k = v] * x[c = l%4].
+    // Sum the 16 blocks (lanes with equal l%4), in a fixed butterfly order.
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sum = acc[t][v];
+            sum += __shfl_xor(sum, 4, 64);
+            sum += __shfl_xor(sum, 8, 64);
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            acc[t][v] = sum;
+        }
+    __syncthreads();  // LDS reuse for the cross-wave sum
+    float* red = lds;  // [wave][t][k(4)][c(4)]
+    if (lane < 4) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[(wave * T + t) * 16 + v * 4 + lane] = acc[t][v];
+    }
+    __syncthreads();
+    // Partial of this (image, band, group): [(n*nbands + band)][g][k][c][t].
+    float* out = a.ws + (((size_t)n * a.nbands + band) * a.G + g) * (16 * T);
+    for (int e = tid; e < 16 * T; e += 256) {
+        const int t = e % T, kc = e / T;  // kc = k*4 + c
+        const float sum = ((red[(0 * T + t) * 16 + kc] + red[(1 * T + t) * 16 + kc]) +
+                           red[(2 * T + t) * 16 + kc]) +
+                          red[(3 * T + t) * 16 + kc];
+        out[kc * T + t] = sum;
+    }
+}
+
+// dw[g*Kg + k, c, t] = sum over the (image, band) partial sets. Block = 16
+// outputs x 16 set groups: thread (e, sg) sums sets sg, sg+16, ... in order,
+// then the 16 group sums are added in order.
+__global__ void __launch_bounds__(256) sg_wgrad_reduce(const float* __restrict__ ws,
+                                                       float* __restrict__ dw, int nsets, int G,
+                                                       int Kg, int Cg, int T)
+{
+    __shared__ float part[16][17];
+    const int el = threadIdx.x & 15, sg = threadIdx.x >> 4;
+    const int e = blockIdx.x * 16 + el;  // over G * 16 * T
+    const int per_set = G * 16 * T;
+    float sum = 0.f;
+    if (e < per_set)
+        for (int s = sg; s < nsets; s += 16) sum += ws[(size_t)s * per_set + e];
+    part[sg][el] = sum;
+    __syncthreads();
+    if (sg != 0 || e >= per_set) return;
+    sum = part[0][el];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) sum += part[i][el];
+    const int t = e % T, kc = (e / T) % 16, g = e / (16 * T);
+    const int k = kc >> 2, c = kc & 3;
+    if (k >= Kg || c >= Cg) return;
+    dw[(((size_t)g * Kg + k) * Cg + c) * T + t] = sum;
+}
+
+// ---- host side --------------------------------------------------------------
+
+struct SgProblem {
+    const float *in, *wgt, *bias;
+    float* out;
+    int N, G, Cin_tot, Cin_g, Hin, Win, Cout_tot, Cout_g, Hout, Wout;
+    int kh, kw, sh, sw, dh, dw, ph, pw;
+    int w_so, w_sr, w_gstride;
+    bool flip;
+};
+
+// LDS tile budget per workgroup (28 KiB): five workgroups share a CU, so the
+// loads of some overlap the arithmetic of others.
+constexpr int kSgTileFloats = 7168;
+
+int sg_cinq(int cin) { return cin <= 1 ? 1 : cin <= 2 ? 2 : 4; }
+int ceil64(int v) { return (v + 63) / 64 * 64; }
+
+// Rows per workgroup: the most whose input tile fits the budget.
+int sg_rows(const SgProblem& p, int cinq, int* LW, int* LR)
+{
+    *LW = (p.Wout - 1) * p.sw + (p.kw - 1) * p.dw + 1;
+    int R = p.Hout;
+    for (; R >= 1; --R) {
+        *LR = (R - 1) * p.sh + (p.kh - 1) * p.dh + 1;
+        if ((int64_t)cinq * *LR * *LW <= kSgTileFloats) break;
+    }
+    return R;
+}
+
+bool sg_problem_ok(const SgProblem& p)
+{
+    if (!(p.kh == 3 && p.kw == 3)) return false;
+    if (p.Cin_g > 4 || p.Cout_g > 8 || p.N < 1) return false;
+    int LW, LR;
+    if (sg_rows(p, sg_cinq(p.Cin_g), &LW, &LR) < 1) return false;
+    if ((int64_t)(p.Cin_g + 4) * p.Hin * p.Win * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)p.Hout * p.Wout >= (1 << 30)) return false;
+    return true;
+}
+
+template <int CIN, int OQ, bool FLIP>
+void sg_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
+{
+    hipLaunchKernelGGL((sg_conv_kernel<3, 3, CIN, OQ, FLIP>), dim3(blocks), dim3(256), lds, st, a);
+}
+
+bool sg_run(const SgProblem& p, hipStream_t st)
+{
+    if (!sg_problem_ok(p)) return false;
+    const int CINq = sg_cinq(p.Cin_g);
+    const int OQ = p.Cout_g <= 4 ? 1 : 2;
+    SgArgs a;
+    a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.N = p.N; a.G = p.G;
+    a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
+    a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
+    a.sh = p.sh; a.sw = p.sw; a.dh = p.dh; a.dw = p.dw; a.ph = p.ph; a.pw = p.pw;
+    a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
+    a.R = sg_rows(p, CINq, &a.LW, &a.LR);
+    a.nbands = (p.Hout + a.R - 1) / a.R;
+    a.plane = a.LR * a.LW;
+    a.div_plane = make_fastdiv((uint32_t)a.plane);
+    a.div_LW = make_fastdiv((uint32_t)a.LW);
+    a.div_Wout = make_fastdiv((uint32_t)p.Wout);
+    const int64_t blocks = (int64_t)p.N * p.G * a.nbands;
+    if (blocks >= (1 << 30)) return false;
+    const size_t lds = ((size_t)ceil64(CINq * a.plane) + (size_t)CINq * 9 * 4 * OQ) * 4;
+#define SG_CASE(cin, oq)                                                       \
+    if (CINq == cin && OQ == oq) {                                             \
+        if (p.flip) sg_launch<cin, oq, true>(a, (int)blocks, lds, st);         \
+        else sg_launch<cin, oq, false>(a, (int)blocks, lds, st);               \
+        return true;                                                           \
+    }
+    SG_CASE(1, 1) SG_CASE(2, 1) SG_CASE(4, 1) SG_CASE(1, 2) SG_CASE(2, 2) SG_CASE(4, 2)
+#undef SG_CASE
+    return false;
+}
+
+SgProblem sg_fwd_problem(const Shape& s, const float* x, const float* w, const float* bias, float* y)
+{
+    SgProblem p;
+    p.in = x; p.wgt = w; p.bias = bias; p.out = y;
+    p.N = s.N; p.G = s.G; p.Cin_tot = s.C; p.Cin_g = s.Cg; p.Hin = s.H; p.Win = s.W;
+    p.Cout_tot = s.K; p.Cout_g = s.Kg; p.Hout = s.Ho; p.Wout = s.Wo;
+    p.kh = s.kh; p.kw = s.kw; p.sh = s.sh; p.sw = s.sw; p.dh = s.dh; p.dw = s.dw;
+    p.ph = s.ph; p.pw = s.pw;
+    const int T = s.kh * s.kw;
+    p.w_so = s.Cg * T; p.w_sr = T; p.w_gstride = s.Kg * s.Cg * T;
+    p.flip = false;
+    return p;
+}
+
+SgProblem sg_bwd_data_problem(const Shape& s, const float* dy, const float* w, float* dx)
+{
+    SgProblem p;
+    p.in = dy; p.wgt = w; p.bias = nullptr; p.out = dx;
+    p.N = s.N; p.G = s.G; p.Cin_tot = s.K; p.Cin_g = s.Kg; p.Hin = s.Ho; p.Win = s.Wo;
+    p.Cout_tot = s.C; p.Cout_g = s.Cg; p.Hout = s.H; p.Wout = s.W;
+    p.kh = s.kh; p.kw = s.kw; p.sh = 1; p.sw = 1; p.dh = s.dh; p.dw = s.dw;
+    p.ph = (s.kh - 1) * s.dh - s.ph;
+    p.pw = (s.kw - 1) * s.dw - s.pw;
+    const int T = s.kh * s.kw;
+    p.w_so = T; p.w_sr = s.Cg * T; p.w_gstride = s.Kg * s.Cg * T;
+    p.flip = true;
+    return p;
+}
+
+// Plane stride == 8 (mod 32): the 4 channels x 8 pixels of a half-wave read
+// fall in distinct banks.
+int pad8(int v) { return (v + 23) / 32 * 32 + 8; }
+
+bool sgw_plan(const Shape& s, SgWArgs* out)
+{
+    if (!(s.kh == 3 && s.kw == 3)) return false;
+    if (s.Cg > 4 || s.Kg > 4 || s.N < 1) return false;
+    SgWArgs a{};
+    a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
+    a.G = s.G; a.Cg = s.Cg; a.Kg = s.Kg;
+    a.sh = s.sh; a.sw = s.sw; a.dh = s.dh; a.dw = s.dw; a.ph = s.ph; a.pw = s.pw;
+    a.LW = (s.Wo - 1) * s.sw + (s.kw - 1) * s.dw + 1;
+    // Rows per band: the most whose input and dy bands fit the LDS budget.
+    int R = s.Ho;
+    for (; R >= 1; --R) {
+        a.LR = (R - 1) * s.sh + (s.kh - 1) * s.dh + 1;
+        a.plane = pad8(a.LR * a.LW);
+        a.dplane = ceil64(R * s.Wo) + 8;
+        if (ceil64(4 * a.plane) + 4 * a.dplane <= kSgTileFloats) break;
+    }
+    if (R < 1) return false;
+    a.R = R;
+    a.nbands = (s.Ho + R - 1) / R;
+    if ((int64_t)(s.Cg + 4) * s.H * s.W * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)(s.Kg + 4) * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)s.N * a.nbands * s.G >= (1 << 30)) return false;
+    a.div_plane = make_fastdiv((uint32_t)a.plane);
+    a.div_LW = make_fastdiv((uint32_t)a.LW);
+    a.div_Wo = make_fastdiv((uint32_t)a.Wo);
+    if (out) *out = a;
+    return true;
+}
+
+}  // namespace
+
+bool smallgroup_fwd_supported(const Shape& s)
+{
+    return sg_problem_ok(sg_fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
+}
+
+bool smallgroup_bwd_data_supported(const Shape& s)
+{
+    if (s.sh != 1 || s.sw != 1) return false;
+    return sg_problem_ok(sg_bwd_data_problem(s, nullptr, nullptr, nullptr));
+}
+
+bool smallgroup_bwd_filter_supported(const Shape& s) { return sgw_plan(s, nullptr); }
+
+size_t smallgroup_bwd_filter_workspace(const Shape& s)
+{
+    SgWArgs a;
+    if (!sgw_plan(s, &a)) return 0;
+    return (size_t)s.N * a.nbands * s.G * 16 * s.kh * s.kw * sizeof(float);
+}
+
+bool smallgroup_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                    hipStream_t st)
+{
+    return sg_run(sg_fwd_problem(s, x, w, bias, y), st);
+}
+
+bool smallgroup_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
+                         hipStream_t st)
+{
+    return sg_run(sg_bwd_data_problem(s, dy, w, dx), st);
+}
+
+bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+                           hipStream_t st)
+{
+    SgWArgs a;
+    if (!sgw_plan(s, &a)) return false;
+    a.x = x;
+    a.dy = dy;
+    a.ws = ws;
+    const int T = s.kh * s.kw;
+    const size_t lds =
+        std::max((size_t)ceil64(4 * a.plane) + (size_t)4 * a.dplane, (size_t)4 * T * 16) * 4;
+    const int blocks = s.N * a.nbands * s.G;
+    hipLaunchKernelGGL((sg_wgrad_kernel<3, 3>), dim3(blocks), dim3(256), lds, st, a);
+    const int total = s.G * 16 * T;
+    hipLaunchKernelGGL(sg_wgrad_reduce, dim3((total + 15) / 16), dim3(256), 0, st, ws, dw,
+                       s.N * a.nbands, s.G, s.Kg, s.Cg, T);
+    return true;
+}
+
+}  // namespace gconv

@@ -143,6 +143,39 @@ def test_random_descriptors_mfma_family(seed):
 
 
 @pytest.mark.parametrize("seed", range(2))
+def test_random_descriptors_smallgroup_family(seed):
+    """3x3 filters with a few channels per group (up to 4 in, 8 out), the reach
+    of the small-group kernels: strides, dilation, padding, ragged widths."""
+    rng = np.random.default_rng(120 + seed)
+    covered = {op: 0 for op in OPS}
+    n_done = 0
+    while n_done < 12:
+        G_ = int(rng.integers(1, 9))
+        d = dict(N=int(rng.integers(1, 4)), C=G_ * int(rng.integers(1, 5)),
+                 K=G_ * int(rng.integers(1, 9)), H=int(rng.integers(3, 40)),
+                 W=int(rng.integers(3, 70)), kh=3, kw=3,
+                 sh=int(rng.choice([1, 1, 2])), sw=int(rng.choice([1, 1, 2])),
+                 ph=int(rng.integers(0, 3)), pw=int(rng.integers(0, 3)),
+                 dh=int(rng.choice([1, 1, 2])), dw=int(rng.choice([1, 1, 2])), G=G_)
+        if not fits(d["H"], d["W"], 3, 3, d["sh"], d["sw"], d["ph"], d["pw"], d["dh"], d["dw"]):
+            continue
+        n_done += 1
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 1200 + seed)
+        y_ref, _ = oracle.fwd(x, w, b, **kw)
+        dy = draw(("normal", 1.0), y_ref.shape, 1210 + seed)
+        ref = oracle_all(x, w, b, dy, kw)
+        for path in [G.PATH_AUTO, G.PATH_SMALLGROUP]:
+            say("small-group desc %s path %s" % (d, G.PATH_NAMES[path]))
+            for op in compare_full("%s %s" % (G.PATH_NAMES[path], d),
+                                   run_path(path, x, w, b, dy, kw), ref):
+                if path == G.PATH_SMALLGROUP:
+                    covered[op] += 1
+    assert covered["fwd"] >= 10 and covered["bwd_data"] >= 3 and covered["bwd_filter"] >= 3, \
+        covered
+
+
+@pytest.mark.parametrize("seed", range(2))
 def test_fc_mode_random(seed):
     """Kernel == input (fully-connected mode), with groups and ragged M / N / R,
     through the GEMM path and every other path that covers it."""
