@@ -257,6 +257,250 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_kernel(ConvMfmaArgs a)
     }
 }
 
+// ---- flattened-pixel variant ------------------------------------------------
+//
+// Same GEMM, tiled differently: a block owns BPX = 16*MP*WPX consecutive
+// output pixels of the flattened (image, row, column) index, so the tile count
+// no longer rounds up per image and the last tile of an image is not mostly
+// empty. Such a run of pixels touches at most two images (BPX <= Hout*Wout);
+// the LDS input tile holds the needed input rows of the first image followed
+// by those of the second ("virtual rows"). The block's WO*WPX waves split it
+// as WPX pixel groups x WO output-channel groups; a wave owns MP pixel
+// fragments of 16 and MO output fragments of 16 (three waves of one fragment
+// cover 48 channels exactly).
+//   - input planes go global -> LDS with buffer_load ... lds (no register
+//     staging), double-buffered over chunks of 4 reduction channels;
+//   - each wave keeps its own filter column (4 channels x T taps x MO) in
+//     registers, prefetched one chunk ahead, so LDS holds only the input tile;
+//   - per tap the LDS reads of the next tap are issued ahead of this tap's
+//     MFMAs.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
+}
+
+struct ConvFlatArgs {
+    const float* in;
+    const float* wgt;
+    const float* bias;
+    float* out;
+    int N, G;
+    int Cin_tot, Cin_g, Hin, Win;
+    int Cout_tot, Cout_g, Hout, Wout;
+    int sh, sw, dh, dw, ph, pw;
+    int w_so, w_sr, w_gstride;
+    int P, NP;                  // Hout*Wout, N*P
+    int n_otiles;
+    int LW, plane, nseg, bufsz; // LDS row width, channel plane, DMA segments per wave, floats per buffer
+    int halo;                   // (kh-1)*dh + 1 input rows under one output row
+    FastDiv div_P, div_Wout, div_plane, div_LW;
+};
+
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, int MINW>
+__global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlatArgs a)
+{
+    constexpr int T = KH * KW;
+    constexpr int CC = 4;
+    constexpr int NW = WO * WPX;
+    constexpr int BPX = WPX * MP * 16;
+    constexpr int BO = WO * MO * 16;
+
+    extern __shared__ float lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q = lane >> 4;
+    const int wo_i = wave % WO, wp_i = wave / WO;
+
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int ot = bid % a.n_otiles;
+    bid /= a.n_otiles;
+    const int g = bid % a.G;
+    const int pt = bid / a.G;
+
+    const int q0 = pt * BPX;
+    const int q1 = min(a.NP, q0 + BPX);
+    const int n0 = (int)fastdiv((uint32_t)q0, a.div_P);
+    const int ho0 = (int)fastdiv((uint32_t)(q0 - n0 * a.P), a.div_Wout);
+    const int nl = (int)fastdiv((uint32_t)(q1 - 1), a.div_P);
+    const int hol = (int)fastdiv((uint32_t)(q1 - 1 - nl * a.P), a.div_Wout);
+    int rows0, rows1;
+    if (nl == n0) {
+        rows0 = (hol - ho0) * a.sh + a.halo;
+        rows1 = 0;
+    } else {
+        rows0 = (a.Hout - 1 - ho0) * a.sh + a.halo;
+        rows1 = hol * a.sh + a.halo;
+    }
+    const int hA = ho0 * a.sh - a.ph;  // input row of virtual row 0
+    const int HWin = a.Hin * a.Win;
+
+    // Per-lane global byte offset of each DMA segment element (chunk-relative:
+    // the buffer resource moves with the chunk). Out-of-image taps, rows past
+    // the tile and the plane padding read 0.
+    uint32_t xoff[NSX];
+#pragma unroll
+    for (int k = 0; k < NSX; ++k) {
+        const int e = (wave + NW * k) * 64 + lane;
+        const int c = (int)fastdiv((uint32_t)e, a.div_plane);
+        const int rem = e - c * a.plane;
+        const int v = (int)fastdiv((uint32_t)rem, a.div_LW);
+        const int col = rem - v * a.LW;
+        const bool second = v >= rows0;
+        const int h = second ? v - rows0 - a.ph : hA + v;
+        const int w = col - a.pw;
+        const bool ok = k < a.nseg && c < CC && v < rows0 + rows1 && (unsigned)h < (unsigned)a.Hin &&
+                        (unsigned)w < (unsigned)a.Win;
+        xoff[k] = ok ? (uint32_t)(((second ? a.Cin_tot : 0) + c) * HWin + h * a.Win + w) * 4u : kOOB;
+    }
+
+    // LDS address (floats, buffer-relative) of each pixel fragment at tap 0,
+    // reduction channel q of the chunk. Pixels past the tile end are clamped
+    // to the last one (computed, never stored).
+    int la[MP];
+#pragma unroll
+    for (int f = 0; f < MP; ++f) {
+        const int qq = min(q0 + (wp_i * MP + f) * 16 + l16, q1 - 1);
+        const int n = (int)fastdiv((uint32_t)qq, a.div_P);
+        const int p = qq - n * a.P;
+        const int ho = (int)fastdiv((uint32_t)p, a.div_Wout);
+        const int wo = p - ho * a.Wout;
+        const int v = (n == n0) ? (ho - ho0) * a.sh : rows0 + ho * a.sh;
+        la[f] = q * a.plane + v * a.LW + wo * a.sw;
+    }
+
+    // Filter operands: lane (l16, q) holds W[o = l16 of fragment m][r = c0 + q][tap].
+    const int o0 = ot * BO;
+    const float* w_g = a.wgt + (size_t)g * a.w_gstride;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_g, (uint32_t)a.w_gstride * 4u);
+    int wbase[MO];  // -1: output channel past the group end
+#pragma unroll
+    for (int m = 0; m < MO; ++m) {
+        const int o = o0 + (wo_i * MO + m) * 16 + l16;
+        wbase[m] = o < a.Cout_g ? o * a.w_so : -1;
+    }
+    auto load_b = [&](int c0, float (&b)[MO][T]) {
+        const int r = c0 + q;
+#pragma unroll
+        for (int m = 0; m < MO; ++m) {
+            // One select per fragment; the tap offsets then ride on the
+            // instruction's immediate offset (out-of-range stays out of range).
+            const uint32_t base =
+                (r < a.Cin_g && wbase[m] >= 0) ? (uint32_t)(wbase[m] + r * a.w_sr) * 4u : kOOB;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                b[m][t] = load_f32(rw, base + (uint32_t)(FLIP ? T - 1 - t : t) * 4u);
+        }
+    };
+
+    const float* in_n0 = a.in + ((size_t)n0 * a.Cin_tot + (size_t)g * a.Cin_g) * HWin;
+    const uint32_t second_recs = rows1 > 0 ? (uint32_t)a.Cin_tot * HWin : 0u;
+    auto issue_x = [&](int c0, int buf) {
+        const __amdgpu_buffer_rsrc_t rx =
+            make_rsrc(in_n0 + (size_t)c0 * HWin, (second_recs + (uint32_t)(a.Cin_g - c0) * HWin) * 4u);
+        // Channels past the group end: the second image's fall outside the
+        // resource; the first image's would alias the next group, so mask them.
+        const int lim = min(CC, a.Cin_g - c0) * a.plane;
+        float* dst = lds + buf * a.bufsz + wave * 64;
+#pragma unroll
+        for (int k = 0; k < NSX; ++k) {
+            if (k < a.nseg) {
+                uint32_t off = xoff[k];
+                if (lim < CC * a.plane) off = ((wave + NW * k) * 64 + lane < lim) ? off : kOOB;
+                load_lds64(rx, dst + k * (NW * 64), off);
+            }
+        }
+    };
+
+    f4 acc[MP][MO];
+#pragma unroll
+    for (int f = 0; f < MP; ++f)
+#pragma unroll
+        for (int m = 0; m < MO; ++m) acc[f][m] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nchunks = (a.Cin_g + CC - 1) / CC;
+    float bn[MO][T];
+    load_b(0, bn);
+    issue_x(0, 0);
+    for (int ch = 0; ch < nchunks; ++ch) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of chunk ch landed
+        __syncthreads();  // every wave's DMA landed; every wave is done with chunk ch-1
+        float bc[MO][T];
+#pragma unroll
+        for (int m = 0; m < MO; ++m)
+#pragma unroll
+            for (int t = 0; t < T; ++t) bc[m][t] = bn[m][t];
+        if (ch + 1 < nchunks) {
+            issue_x((ch + 1) * CC, (ch + 1) & 1);
+            load_b((ch + 1) * CC, bn);
+        }
+        const float* xb = lds + (ch & 1) * a.bufsz;
+        float av[2][MP];
+#pragma unroll
+        for (int f = 0; f < MP; ++f) av[0][f] = xb[la[f]];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int cur = t & 1, nxt = cur ^ 1;
+            if (t + 1 < T) {
+                const int i = (t + 1) / KW, j = (t + 1) % KW;
+                const int toff = i * a.dh * a.LW + j * a.dw;
+#pragma unroll
+                for (int f = 0; f < MP; ++f) av[nxt][f] = xb[la[f] + toff];
+            }
+#pragma unroll
+            for (int f = 0; f < MP; ++f)
+#pragma unroll
+                for (int m = 0; m < MO; ++m)
+                    acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cur][f], bc[m][t], acc[f][m],
+                                                                     0, 0, 0);
+            if (t + 1 < T) __builtin_amdgcn_sched_group_barrier(0x100, MP, 0);  // LDS reads first
+            __builtin_amdgcn_sched_group_barrier(0x008, MP * MO, 0);          // then the MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Epilogue: lane (l16, q) holds output channel l16 of each fragment,
+    // pixels 4q..4q+3 of each pixel fragment.
+    const bool vec4 = (a.P & 3) == 0;
+#pragma unroll
+    for (int m = 0; m < MO; ++m) {
+        const int o = o0 + (wo_i * MO + m) * 16 + l16;
+        if (o >= a.Cout_g) continue;
+        const float bv = a.bias ? a.bias[g * a.Cout_g + o] : 0.f;
+        const size_t ch_off = (size_t)g * a.Cout_g + o;
+#pragma unroll
+        for (int f = 0; f < MP; ++f) {
+            const int qb = q0 + (wp_i * MP + f) * 16 + 4 * q;
+            f4 v = acc[f][m];
+            v.x += bv;
+            v.y += bv;
+            v.z += bv;
+            v.w += bv;
+            if (vec4) {
+                // P % 4 == 0 and q0 % 16 == 0: the four pixels share an image.
+                if (qb < q1) {
+                    const int n = (int)fastdiv((uint32_t)qb, a.div_P);
+                    const int p = qb - n * a.P;
+                    *(f4*)(a.out + ((size_t)n * a.Cout_tot + ch_off) * a.P + p) = v;
+                }
+            } else {
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int qq = qb + u;
+                    if (qq < q1) {
+                        const int n = (int)fastdiv((uint32_t)qq, a.div_P);
+                        const int p = qq - n * a.P;
+                        a.out[((size_t)n * a.Cout_tot + ch_off) * a.P + p] = vv[u];
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ---- host side ------------------------------------------------------------
 
 constexpr int kMP = 4;
@@ -420,28 +664,160 @@ Problem bwd_data_problem(const Shape& s, const float* dy, const float* w, float*
     return p;
 }
 
+// ---- flattened-pixel variant: host side --------------------------------------
+
+struct FlatInst {
+    int T, MO, WO, WPX, MP;
+};
+#ifndef GCONV_FLAT_MP3
+#define GCONV_FLAT_MP3 5
+#endif
+// Compiled instances: output fragments per wave (MO), waves across output
+// channels (WO) and across pixels (WPX), pixel fragments per wave (MP). With
+// 64 channels per group, 5 fragments give 1255 tiles of 80 pixels for 32
+// images of 56 x 56, which spread evenly over the 256 CUs.
+#define GCONV_FLAT_INSTS(X)                                                          \
+    X(9, 3, 1, 4, 1, GCONV_FLAT_MP3) X(9, 3, 2, 4, 1, 4) X(9, 3, 1, 3, 1, 5)         \
+    X(9, 3, 1, 2, 2, 4) X(9, 3, 1, 1, 4, 4)                                          \
+    X(25, 5, 1, 4, 1, 4) X(25, 5, 2, 4, 1, 4) X(25, 5, 1, 3, 1, 4)                   \
+    X(25, 5, 1, 2, 2, 4) X(25, 5, 1, 1, 4, 4)
+#define GCONV_FLAT_ENTRY(t, k, mo, wo, wpx, mp) {t, mo, wo, wpx, mp},
+constexpr FlatInst kFlatInsts[] = {GCONV_FLAT_INSTS(GCONV_FLAT_ENTRY)};
+#undef GCONV_FLAT_ENTRY
+constexpr int kFlatNSX = 8;  // DMA segments (of 64 floats) per wave and buffer, at most
+
+struct FlatPlan {
+    FlatInst inst;
+    int LW, plane, nseg, bufsz;
+    size_t lds_bytes;
+    int blocks;
+};
+
+bool flat_plan(const Problem& p, FlatPlan& fp)
+{
+    const int T = p.kh * p.kw;
+    if (!((p.kh == 3 && p.kw == 3) || (p.kh == 5 && p.kw == 5))) return false;
+    const int nfrag = (p.Cout_g + 15) / 16;
+    const int mo = nfrag > 4 ? 2 : 1;
+    const int wo = nfrag > 4 ? 4 : nfrag;  // waves across output channels
+    const FlatInst* inst = nullptr;
+    for (const FlatInst& fi : kFlatInsts)
+        if (fi.T == T && fi.MO == mo && fi.WO == wo) inst = &fi;
+    if (!inst) return false;
+    fp.inst = *inst;
+    const int NW = inst->WO * inst->WPX;
+    const int BPX = inst->WPX * inst->MP * 16;
+    const int64_t P = (int64_t)p.Hout * p.Wout;
+    if (P < BPX) return false;  // a tile must span at most two images
+    const int64_t NP = (int64_t)p.N * P;
+    if (NP + BPX >= (int64_t(1) << 31)) return false;
+    const int halo = (p.kh - 1) * p.dh + 1;
+    const int R = (int)std::min<int64_t>(p.Hout, (BPX - 1) / p.Wout + 2);  // output rows per tile
+    const int LR = std::max((R - 1) * p.sh + halo, (R - 2) * p.sh + 2 * halo);
+    const int64_t LW = (int64_t)(p.Wout - 1) * p.sw + (p.kw - 1) * p.dw + 1;
+    int64_t plane = LR * LW;
+    plane = ((plane + 47) / 64) * 64 + 16;  // == 16 (mod 64): the 4 lane groups hit distinct banks
+    const int64_t nseg = (4 * plane + 64 * NW - 1) / (64 * NW);
+    if (nseg > kFlatNSX) return false;
+    fp.LW = (int)LW;
+    fp.plane = (int)plane;
+    fp.nseg = (int)nseg;
+    fp.bufsz = (int)(nseg * 64 * NW);
+    fp.lds_bytes = (size_t)2 * fp.bufsz * 4;
+    // Buffer resources: two images' worth of one group's planes, and one
+    // group's weights, addressed in bytes below 2^31.
+    if ((int64_t)(p.Cin_tot + p.Cin_g) * p.Hin * p.Win * 4 >= (int64_t(1) << 31)) return false;
+    if ((int64_t)p.w_gstride * 4 >= (int64_t(1) << 31)) return false;
+    const int BO = inst->WO * inst->MO * 16;
+    const int64_t blocks = ((NP + BPX - 1) / BPX) * p.G * ((p.Cout_g + BO - 1) / BO);
+    if (blocks >= (int64_t(1) << 31)) return false;
+    fp.blocks = (int)blocks;
+    return true;
+}
+
+template <int KH, int KW, int MP, int MO, int WO, int WPX, bool FLIP>
+void launch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
+{
+    constexpr int MINW = (KH * KW <= 9) ? 4 : 2;
+    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, kFlatNSX, FLIP, MINW>;
+    hipLaunchKernelGGL(kern, dim3(fp.blocks), dim3(64 * WO * WPX), fp.lds_bytes, st, a);
+}
+
+template <bool FLIP>
+bool dispatch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
+{
+    const FlatInst& i = fp.inst;
+#define GCONV_FLAT_CASE(t, k, mo, wo, wpx, mp)                                          \
+    if (i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp) {          \
+        launch_flat<k, k, mp, mo, wo, wpx, FLIP>(a, fp, st);                            \
+        return true;                                                                   \
+    }
+    GCONV_FLAT_INSTS(GCONV_FLAT_CASE)
+#undef GCONV_FLAT_CASE
+    return false;
+}
+
+bool run_flat(const Problem& p, hipStream_t st)
+{
+    FlatPlan fp;
+    if (!flat_plan(p, fp)) return false;
+    ConvFlatArgs a;
+    a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.N = p.N; a.G = p.G;
+    a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
+    a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
+    a.sh = p.sh; a.sw = p.sw; a.dh = p.dh; a.dw = p.dw; a.ph = p.ph; a.pw = p.pw;
+    a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
+    a.P = p.Hout * p.Wout;
+    a.NP = p.N * a.P;
+    const int BO = fp.inst.WO * fp.inst.MO * 16;
+    a.n_otiles = (p.Cout_g + BO - 1) / BO;
+    a.LW = fp.LW; a.plane = fp.plane; a.nseg = fp.nseg; a.bufsz = fp.bufsz;
+    a.halo = (p.kh - 1) * p.dh + 1;
+    a.div_P = make_fastdiv((uint32_t)a.P);
+    a.div_Wout = make_fastdiv((uint32_t)p.Wout);
+    a.div_plane = make_fastdiv((uint32_t)fp.plane);
+    a.div_LW = make_fastdiv((uint32_t)fp.LW);
+    return p.flip ? dispatch_flat<true>(a, fp, st) : dispatch_flat<false>(a, fp, st);
+}
+
+bool use_flat(const Problem& p)
+{
+#ifdef GCONV_NO_FLAT
+    (void)p;
+    return false;
+#else
+    FlatPlan fp;
+    return flat_plan(p, fp);
+#endif
+}
+
 }  // namespace
 
 bool igemm_fwd_supported(const Shape& s)
 {
-    return problem_supported(fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
+    const Problem p = fwd_problem(s, nullptr, nullptr, nullptr, nullptr);
+    return use_flat(p) || problem_supported(p);
 }
 
 bool igemm_bwd_data_supported(const Shape& s)
 {
     if (s.sh != 1 || s.sw != 1) return false;
-    return problem_supported(bwd_data_problem(s, nullptr, nullptr, nullptr));
+    const Problem p = bwd_data_problem(s, nullptr, nullptr, nullptr);
+    return use_flat(p) || problem_supported(p);
 }
 
 bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
                hipStream_t st)
 {
-    return run_problem(fwd_problem(s, x, w, bias, y), st);
+    const Problem p = fwd_problem(s, x, w, bias, y);
+    return use_flat(p) ? run_flat(p, st) : run_problem(p, st);
 }
 
 bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
-    return run_problem(bwd_data_problem(s, dy, w, dx), st);
+    const Problem p = bwd_data_problem(s, dy, w, dx);
+    return use_flat(p) ? run_flat(p, st) : run_problem(p, st);
 }
 
 }  // namespace gconv
