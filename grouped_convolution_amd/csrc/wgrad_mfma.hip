@@ -14,7 +14,9 @@
 //   dw[c = 4*(l/16)+v][k = l%16].
 //
 // Block = 4 waves arranged WC (input-channel fragments) x 4/WC, each wave
-// 16 input channels x 16*WK output channels x all taps. The pixel reduction
+// 16 input channels x 16*WK output channels x all taps (for the wide 9-tap
+// tile, two such sets of 4 waves split each chunk's pixels and add their sums
+// at the end, in a fixed order). The pixel reduction
 // is split: the N*Ho output rows are cut into chunks of R rows of one image,
 // and each block reduces a contiguous run of chunks for one (group, input tile,
 // output tile). Blocks write partial tiles to the workspace in accumulator
@@ -69,8 +71,8 @@ struct WgradArgs {
     FastDiv div_LW, div_WoP, div_cpi;
 };
 
-template <int KH, int KW, int WC, int WK, int R>
-__global__ void __launch_bounds__(256) wgrad_mfma_kernel(WgradArgs a)
+template <int KH, int KW, int WC, int WK, int R, int NH>
+__global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
 {
     constexpr int T = KH * KW;
     constexpr int CT = 16 * WC;
@@ -82,7 +84,11 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(WgradArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l16 = lane & 15, q = lane >> 4;
-    const int wc = wave % WC, wk = wave / WC;
+    // Waves wq = wave % 4 own the output sub-tiles; with NH = 2 a second set
+    // of four (h = 1) shares them and takes the second half of every chunk's
+    // pixels, so two waves per SIMD hide each other's stalls.
+    const int wq = wave & 3, h = wave >> 2;
+    const int wc = wq % WC, wk = wq / WC;
 
     int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int kt = bid % a.n_ktiles;
@@ -143,7 +149,7 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(WgradArgs a)
             if (sg >= a.nsx) break;
             const bool ok = xok[sg] && xrow[sg] >= row_lo && xrow[sg] < row_hi;
             const uint32_t lo = (uint32_t)(xbase + xoff[sg] * 4);
-            for (int c = wave; c < CT; c += 4)
+            for (int c = wave; c < CT; c += 4 * NH)
                 load_lds64(rx, xs + c * a.XS + sg * 64, ok ? lo + (uint32_t)c * xplane : kOOB);
         }
         const int dbase = ho0 * a.Wo * 4;
@@ -152,7 +158,7 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(WgradArgs a)
             if (sg >= a.nsd) break;
             const bool ok = dok[sg] && drow[sg] < drow_hi;
             const uint32_t lo = (uint32_t)(dbase + doff[sg] * 4);
-            for (int k = wave; k < KT; k += 4)
+            for (int k = wave; k < KT; k += 4 * NH)
                 load_lds64(rd, ds + k * a.DS + sg * 64, ok ? lo + (uint32_t)k * dplane : kOOB);
         }
     };
@@ -177,9 +183,10 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(WgradArgs a)
         const int total = min(R, a.Ho - ho0) * nsteps;  // (row, 4-pixel step) pairs
         const float* xl = xs + (wc * 16 + l16) * a.XS + q * a.sw;
         const float* dl = ds + (wk * 16 * WK + l16) * a.DS + q;
-        // Operands of step u+1 are fetched while the MFMAs of step u run.
+        // Operands of step u+1 are fetched while the MFMAs of step u run. The
+        // fetches are unconditional (the last one re-reads the final step), so
+        // the LDS wait before each step covers only that step's operands.
         float av[2][T], bv[2][WK];
-        int r = 0, st = 0;
         auto fetch = [&](int slot, int rr, int ss) {
             const float* xr = xl + rr * a.sh * a.LW + ss * 4 * a.sw;
             const float* dr = dl + rr * a.WoP + ss * 4;
@@ -191,32 +198,78 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(WgradArgs a)
 #pragma unroll
             for (int m = 0; m < WK; ++m) bv[slot][m] = dr[m * 16 * a.DS];
         };
-        fetch(0, 0, 0);
-        for (int u = 0; u < total; u += 2) {
+        auto mfmas = [&](int slot) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                if (u + half >= total) break;
-                const int cur = half;
-                if (++st == nsteps) {
-                    st = 0;
-                    ++r;
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int m = 0; m < WK; ++m)
+                    acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[slot][t], bv[slot][m],
+                                                                     acc[t][m], 0, 0, 0);
+        };
+        // This wave's steps of the chunk: [u0, u1).
+        const int u0 = h * total / NH, u1 = (h + 1) * total / NH;
+        if (u0 < u1) {
+            // (row, step) of the next fetch, advanced one step at a time.
+            int fr = u0 / nsteps, fs = u0 - (u0 / nsteps) * nsteps;
+            auto advance = [&]() {
+                if (++fs == nsteps) {
+                    fs = 0;
+                    ++fr;
                 }
-                if (u + half + 1 < total) fetch(cur ^ 1, r, st);
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-#pragma unroll
-                    for (int m = 0; m < WK; ++m)
-                        acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cur][t], bv[cur][m],
-                                                                         acc[t][m], 0, 0, 0);
+            };
+            const int last_r = (u1 - 1) / nsteps, last_s = (u1 - 1) - last_r * nsteps;
+            // Scheduling groups pin the order: the next step's LDS reads, then
+            // this step's MFMAs (the compiler would otherwise interleave them and
+            // wait on freshly issued reads).
+            constexpr int NRD = T + WK, NMF = T * WK;
+            fetch(0, fr, fs);
+            int u = u0;
+            for (; u + 1 < u1; u += 2) {
+                advance();
+                fetch(1, fr, fs);  // step u+1 (exists)
+                mfmas(0);          // step u
+                __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                advance();
+                const bool more = u + 2 < u1;
+                fetch(0, more ? fr : last_r, more ? fs : last_s);
+                mfmas(1);          // step u+1
+                __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            if (u < u1) mfmas(0);
         }
         __syncthreads();  // every wave is done with buffer b before it is refilled
+    }
+
+    if constexpr (NH == 2) {
+        // The second wave set hands its sums to the first through LDS (the
+        // tile buffers are free after the last barrier of the chunk loop).
+        float* xch = lds + (size_t)wq * (T * WK * 256) + lane;
+        if (h == 1) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int m = 0; m < WK; ++m)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) xch[(t * WK + m) * 256 + v * 64] = acc[t][m][v];
+        }
+        __syncthreads();
+        if (h == 1) return;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int m = 0; m < WK; ++m)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][m][v] += xch[(t * WK + m) * 256 + v * 64];
     }
 
     // Partial tile in accumulator order: [split][tile][wave][t][m][v][lane].
     const int tile = (g * a.n_ctiles + ct) * a.n_ktiles + kt;
     const int n_tiles = a.G * a.n_ctiles * a.n_ktiles;
-    float* out = a.ws + (((size_t)s * n_tiles + tile) * 4 + wave) * (size_t)(T * WK * 256);
+    float* out = a.ws + (((size_t)s * n_tiles + tile) * 4 + wq) * (size_t)(T * WK * 256);
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -268,7 +321,7 @@ __global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float* __restri
 // ---- host side ----------------------------------------------------------------
 
 struct Config {
-    int WC, WK, R;
+    int WC, WK, R, NH;
 };
 
 // Plane stride: a multiple of 64 plus 2, so that the 16 channels x 2 pixels a
@@ -297,9 +350,20 @@ Plan make_plan(const Shape& s)
     // >= 32 input and >= 64 output channels; otherwise one input tile of 16
     // with four waves along the outputs. 25-tap filters keep one input tile
     // per block (their per-wave accumulators already fill 200 registers).
-    if (T <= 9 && s.Cg >= 32 && s.Kg >= 64) cfg = {2, 2, 0};
-    else if (T > 9 && s.Kg >= 128) cfg = {1, 2, 0};
-    else cfg = {1, 1, 0};
+#ifndef GCONV_WGRAD_WIDE
+#define GCONV_WGRAD_WIDE 0
+#endif
+    // 9-tap tiles with >= 32 input and output channels per group: two wave
+    // sets per block (8 waves) on a 32 x 32 tile whose LDS stays under 80 KiB,
+    // so two blocks share a CU and one block's barriers and loads overlap the
+    // other's MFMAs.
+    int lds_cap = 160 * 1024;
+    if (GCONV_WGRAD_WIDE == 1 && T <= 9 && s.Cg >= 32 && s.Kg >= 32) {
+        cfg = {2, 1, 0, 2};
+        lds_cap = 80 * 1024;
+    } else if (T <= 9 && s.Cg >= 32 && s.Kg >= 64) cfg = {2, 2, 0, 2};
+    else if (T > 9 && s.Kg >= 128) cfg = {1, 2, 0, 1};
+    else cfg = {1, 1, 0, 1};
     const int CT = 16 * cfg.WC, KT = 16 * cfg.WK * (4 / cfg.WC);
     WgradArgs& a = p.a;
     a.WoP = (s.Wo + 3) / 4 * 4;
@@ -319,7 +383,9 @@ Plan make_plan(const Shape& s)
         a.XS = plane_stride(a.nsx);
         a.DS = plane_stride(a.nsd);
         p.lds_bytes = 2 * ((size_t)CT * a.XS + (size_t)KT * a.DS) * 4;
-        if (a.nsx <= kMaxSegX && a.nsd <= kMaxSegD && p.lds_bytes <= 160 * 1024) break;
+        // The second wave set's sums pass through LDS at the end.
+        if (cfg.NH == 2) p.lds_bytes = std::max(p.lds_bytes, (size_t)4 * T * cfg.WK * 256 * 4);
+        if (a.nsx <= kMaxSegX && a.nsd <= kMaxSegD && p.lds_bytes <= (size_t)lds_cap) break;
     }
     cfg.R = R;
     a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
@@ -356,26 +422,26 @@ Plan make_plan(const Shape& s)
     return p;
 }
 
-template <int KH, int KW, int WC, int WK, int R>
+template <int KH, int KW, int WC, int WK, int R, int NH>
 void launch_main(const Plan& p, hipStream_t st)
 {
-    auto kern = wgrad_mfma_kernel<KH, KW, WC, WK, R>;
+    auto kern = wgrad_mfma_kernel<KH, KW, WC, WK, R, NH>;
     // Allow dynamic LDS up to the CU's 160 KiB (once per kernel instance).
     static const bool attr_set = hipFuncSetAttribute((const void*)kern,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      160 * 1024) == hipSuccess;
     (void)attr_set;
-    hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(256), p.lds_bytes, st, p.a);
+    hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(256 * NH), p.lds_bytes, st, p.a);
 }
 
-template <int KH, int KW, int WC, int WK>
+template <int KH, int KW, int WC, int WK, int NH>
 bool launch_r(const Plan& p, hipStream_t st)
 {
     switch (p.cfg.R) {
-        case 1: launch_main<KH, KW, WC, WK, 1>(p, st); return true;
-        case 2: launch_main<KH, KW, WC, WK, 2>(p, st); return true;
-        case 3: launch_main<KH, KW, WC, WK, 3>(p, st); return true;
-        case 4: launch_main<KH, KW, WC, WK, 4>(p, st); return true;
+        case 1: launch_main<KH, KW, WC, WK, 1, NH>(p, st); return true;
+        case 2: launch_main<KH, KW, WC, WK, 2, NH>(p, st); return true;
+        case 3: launch_main<KH, KW, WC, WK, 3, NH>(p, st); return true;
+        case 4: launch_main<KH, KW, WC, WK, 4, NH>(p, st); return true;
         default: return false;
     }
 }
@@ -408,16 +474,19 @@ bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw
     p.a.ws = ws;
     const Config c = p.cfg;
     if (s.kh == 3 && c.WC == 2 && c.WK == 2) {
-        if (!launch_r<3, 3, 2, 2>(p, st)) return false;
+        if (!launch_r<3, 3, 2, 2, 2>(p, st)) return false;
         launch_reduce<9, 2, 2>(p, s, ws, dw, st);
+    } else if (s.kh == 3 && c.WC == 2 && c.WK == 1) {
+        if (!launch_r<3, 3, 2, 1, 2>(p, st)) return false;
+        launch_reduce<9, 2, 1>(p, s, ws, dw, st);
     } else if (s.kh == 3 && c.WC == 1 && c.WK == 1) {
-        if (!launch_r<3, 3, 1, 1>(p, st)) return false;
+        if (!launch_r<3, 3, 1, 1, 1>(p, st)) return false;
         launch_reduce<9, 1, 1>(p, s, ws, dw, st);
     } else if (s.kh == 5 && c.WC == 1 && c.WK == 2) {
-        if (!launch_r<5, 5, 1, 2>(p, st)) return false;
+        if (!launch_r<5, 5, 1, 2, 1>(p, st)) return false;
         launch_reduce<25, 1, 2>(p, s, ws, dw, st);
     } else if (s.kh == 5 && c.WC == 1 && c.WK == 1) {
-        if (!launch_r<5, 5, 1, 1>(p, st)) return false;
+        if (!launch_r<5, 5, 1, 1, 1>(p, st)) return false;
         launch_reduce<25, 1, 1>(p, s, ws, dw, st);
     } else {
         return false;
