@@ -27,38 +27,12 @@
 //            is fetched into registers while the current one is multiplied.
 #include <algorithm>
 
+#include "device_util.h"
 #include "fastdiv.h"
 #include "gconv_internal.h"
 
 namespace gconv {
 namespace {
-
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-// Workgroups are dispatched round-robin over the 8 XCDs of the MI355X (block b
-// runs on XCD b % 8). Renumber so that each XCD gets a contiguous range of
-// logical tiles: neighbouring tiles then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int b, int nb)
-{
-    const int per = nb >> 3, rem = nb & 7, x = b & 7, i = b >> 3;
-    return x * per + min(x, rem) + i;
-}
-
-// Raw buffer resource over [p, p + bytes): a load whose byte offset is at or
-// past `bytes` returns 0 without touching memory, so zero padding and ragged
-// tails need no branch. `bytes` stays below 2^31, and kOOB is past it.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-constexpr uint32_t kOOB = 0x80000000u;
-
-// 32-bit raw buffer load of a float (the builtin returns the bits as an integer).
-__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
-}
 
 struct ConvMfmaArgs {
     const float* in;
@@ -274,13 +248,6 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_kernel(ConvMfmaArgs a)
 //     registers, prefetched one chunk ahead, so LDS holds only the input tile;
 //   - per tap the LDS reads of the next tap are issued ahead of this tap's
 //     MFMAs.
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
-}
-
 struct ConvFlatArgs {
     const float* in;
     const float* wgt;

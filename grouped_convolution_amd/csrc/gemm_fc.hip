@@ -23,36 +23,16 @@
 // stored as one 16-byte write.
 #include <algorithm>
 
+#include "device_util.h"
 #include "gconv_internal.h"
 
 namespace gconv {
 namespace {
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr uint32_t kOOB = 0x80000000u;
 constexpr int BM = 128, BN = 128, BR = 32;
 constexpr int SROW = BM + 4;          // row stride of a [32][row] tile (== 4 mod 8)
 constexpr int TILE_R = BM * BR;       // floats of a swizzled [row][32] tile
 constexpr int TILE_N = BR * SROW;     // floats of a [32][row + 4] tile
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-__device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
-}
-
-__device__ __forceinline__ int xcd_remap(int b, int nb)
-{
-    const int per = nb >> 3, rem = nb & 7, x = b & 7, i = b >> 3;
-    return x * per + min(x, rem) + i;
-}
 
 struct GemmArgs {
     const float* A;

@@ -25,31 +25,11 @@
 #include <algorithm>
 
 #include "fastdiv.h"
+#include "device_util.h"
 #include "gconv_internal.h"
 
 namespace gconv {
 namespace {
-
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-constexpr uint32_t kOOB = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
-}
-
-__device__ __forceinline__ int xcd_remap(int b, int nb)
-{
-    const int per = nb >> 3, rem = nb & 7, x = b & 7, i = b >> 3;
-    return x * per + min(x, rem) + i;
-}
 
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 c)
 {
@@ -59,15 +39,6 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c)
 // ---------------------------------------------------------------------------
 // forward / gradInput
 // ---------------------------------------------------------------------------
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 64 lanes load one dword each into 64 consecutive LDS floats at `dst`
-// (out-of-range offsets write 0).
-__device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
-}
 
 struct SgArgs {
     const float* in;

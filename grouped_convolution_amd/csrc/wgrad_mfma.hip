@@ -27,36 +27,15 @@
 // streams in while this one is multiplied.
 #include <algorithm>
 
+#include "device_util.h"
 #include "fastdiv.h"
 #include "gconv_internal.h"
 
 namespace gconv {
 namespace {
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kMaxSegX = 8;   // 64-float segments of one input-channel plane
 constexpr int kMaxSegD = 4;   // ... of one dy plane
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-// 64 lanes load one dword each into 64 consecutive LDS floats at `dst`.
-__device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
-}
-
-__device__ __forceinline__ int xcd_remap(int b, int nb)
-{
-    const int per = nb >> 3, rem = nb & 7, x = b & 7, i = b >> 3;
-    return x * per + min(x, rem) + i;
-}
 
 struct WgradArgs {
     const float* x;
@@ -130,6 +109,8 @@ __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
 
     // Issue the loads of chunk `ch` into LDS buffer `b`: plane p of the tile is
     // loaded by wave p % 4, one 64-float segment per instruction.
+    // Channels (of x) and output channels (of dy) this wave loads per segment.
+    constexpr int CPW = CT / (4 * NH), KPW = KT / (4 * NH);
     auto issue = [&](int ch, int b) {
         float* xs = lds + b * buf_floats;
         float* ds = xs + CT * a.XS;
@@ -144,22 +125,29 @@ __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
         const int row_lo = -hb, row_hi = a.H - hb;     // tile rows r with 0 <= hb + r < H
         const int drow_hi = a.Ho - ho0;                // dy rows r with ho0 + r < Ho
         const int xbase = hb * a.W * 4;
+        // One select per segment; each of the wave's planes then adds a uniform
+        // plane offset (an out-of-range offset stays out of range: the planes
+        // a tile spans stay far below 2^31 bytes).
 #pragma unroll
         for (int sg = 0; sg < kMaxSegX; ++sg) {
             if (sg >= a.nsx) break;
             const bool ok = xok[sg] && xrow[sg] >= row_lo && xrow[sg] < row_hi;
-            const uint32_t lo = (uint32_t)(xbase + xoff[sg] * 4);
-            for (int c = wave; c < CT; c += 4 * NH)
-                load_lds64(rx, xs + c * a.XS + sg * 64, ok ? lo + (uint32_t)c * xplane : kOOB);
+            const uint32_t v = ok ? (uint32_t)(xbase + xoff[sg] * 4) + (uint32_t)wave * xplane : kOOB;
+            float* dst = xs + wave * a.XS + sg * 64;
+#pragma unroll
+            for (int ci = 0; ci < CPW; ++ci)
+                load_lds64(rx, dst + ci * (4 * NH) * a.XS, v + (uint32_t)(ci * 4 * NH) * xplane);
         }
         const int dbase = ho0 * a.Wo * 4;
 #pragma unroll
         for (int sg = 0; sg < kMaxSegD; ++sg) {
             if (sg >= a.nsd) break;
             const bool ok = dok[sg] && drow[sg] < drow_hi;
-            const uint32_t lo = (uint32_t)(dbase + doff[sg] * 4);
-            for (int k = wave; k < KT; k += 4 * NH)
-                load_lds64(rd, ds + k * a.DS + sg * 64, ok ? lo + (uint32_t)k * dplane : kOOB);
+            const uint32_t v = ok ? (uint32_t)(dbase + doff[sg] * 4) + (uint32_t)wave * dplane : kOOB;
+            float* dst = ds + wave * a.DS + sg * 64;
+#pragma unroll
+            for (int ki = 0; ki < KPW; ++ki)
+                load_lds64(rd, dst + ki * (4 * NH) * a.DS, v + (uint32_t)(ki * 4 * NH) * dplane);
         }
     };
 
