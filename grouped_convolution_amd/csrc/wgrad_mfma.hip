@@ -346,9 +346,9 @@ Plan make_plan(const Shape& s)
     // so two blocks share a CU and one block's barriers and loads overlap the
     // other's MFMAs.
     int lds_cap = 160 * 1024;
-    if (GCONV_WGRAD_WIDE == 1 && T <= 9 && s.Cg >= 32 && s.Kg >= 32) {
+    if (GCONV_WGRAD_WIDE >= 1 && T <= 9 && s.Cg >= 32 && s.Kg >= 32) {
         cfg = {2, 1, 0, 2};
-        lds_cap = 80 * 1024;
+        if (GCONV_WGRAD_WIDE == 1) lds_cap = 80 * 1024;
     } else if (T <= 9 && s.Cg >= 32 && s.Kg >= 64) cfg = {2, 2, 0, 2};
     else if (T > 9 && s.Kg >= 128) cfg = {1, 2, 0, 1};
     else cfg = {1, 1, 0, 1};
