@@ -151,6 +151,105 @@ __global__ void __launch_bounds__(256) sg_conv_kernel(SgArgs a)
     }
 }
 
+// Unit stride and dilation, padded rows of at most 64 floats (the common 3x3
+// case): the LDS tile keeps one 64-float row per input row, so one DMA
+// instruction copies one row (lane = column, a uniform row offset plus the
+// lane's column) and every tap read is an LDS load at an immediate offset from
+// the pixel's address. The address arithmetic of the general kernel above is
+// what limits it at these shapes, not the memory system.
+template <int CIN, int OQ, bool FLIP>
+__global__ void __launch_bounds__(256) sg_conv_row64_kernel(SgArgs a)
+{
+    constexpr int T = 9;
+    constexpr int NW = CIN * T * 4 * OQ;     // staged filter values
+    extern __shared__ float lds[];           // [CIN][LR][64] input rows, then filters
+    const int plane = a.LR * 64;
+    float* wl = lds + CIN * plane;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int band = bid % a.nbands;
+    bid /= a.nbands;
+    const int g = bid % a.G;
+    const int n = bid / a.G;
+    const int ho0 = band * a.R;
+    const int rows = min(a.R, a.Hout - ho0);
+    const int hbase = ho0 - a.ph;
+
+    const float* in_g = a.in + ((size_t)n * a.Cin_tot + (size_t)g * a.Cin_g) * a.Hin * a.Win;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_g, (uint32_t)a.Cin_g * a.Hin * a.Win * 4u);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(a.wgt + (size_t)g * a.w_gstride, (uint32_t)a.w_gstride * 4u);
+
+    // Tile column `lane` holds input column lane - pw (zero outside the image).
+    const int wcol = lane - a.pw;
+    const bool colok = (unsigned)wcol < (unsigned)a.Win;
+#pragma unroll
+    for (int c = 0; c < CIN; ++c)
+        for (int r = wave; r < a.LR; r += 4) {
+            const int h = hbase + r;
+            const bool ok = colok && c < a.Cin_g && (unsigned)h < (unsigned)a.Hin;
+            load_lds64(rx, lds + c * plane + r * 64,
+                       ok ? (uint32_t)((c * a.Hin + h) * a.Win + wcol) * 4u : kOOB);
+        }
+    // Filters -> LDS as [(c*T + t)][o] (zeros past the group's channels).
+    for (int e = tid; e < NW; e += 256) {
+        const int o = e % (4 * OQ), ct = e / (4 * OQ), c = ct / T, t = ct % T;
+        const bool ok = o < a.Cout_g && c < a.Cin_g;
+        wl[e] = load_f32(rw, ok ? (uint32_t)(o * a.w_so + c * a.w_sr + (FLIP ? T - 1 - t : t)) * 4u : kOOB);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    float wv[CIN][T][OQ];
+#pragma unroll
+    for (int c = 0; c < CIN; ++c)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int oq = 0; oq < OQ; ++oq) wv[c][t][oq] = wl[(c * T + t) * 4 * OQ + oq * 4 + (lane & 3)];
+    float bv[OQ][4];
+#pragma unroll
+    for (int oq = 0; oq < OQ; ++oq)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int o = oq * 4 + v;
+            bv[oq][v] = (a.bias && o < a.Cout_g) ? a.bias[g * a.Cout_g + o] : 0.f;
+        }
+
+    const int P = a.Hout * a.Wout;
+    float* out_g = a.out + ((size_t)n * a.Cout_tot + (size_t)g * a.Cout_g) * P + (size_t)ho0 * a.Wout;
+    const int npix = rows * a.Wout;
+    for (int s = wave * 64; s < npix; s += 256) {
+        const int pl = s + lane;
+        const int pc = min(pl, npix - 1);
+        const int r = (int)fastdiv((uint32_t)pc, a.div_Wout);
+        const float* xb = lds + r * 64 + (pc - r * a.Wout);
+        f4 acc[OQ];
+#pragma unroll
+        for (int oq = 0; oq < OQ; ++oq) acc[oq] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CIN; ++c) {
+            const float* xc = xb + c * plane;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float xv = xc[(t / 3) * 64 + t % 3];
+#pragma unroll
+                for (int oq = 0; oq < OQ; ++oq) acc[oq] = mfma4(wv[c][t][oq], xv, acc[oq]);
+            }
+        }
+        if (pl < npix) {
+#pragma unroll
+            for (int oq = 0; oq < OQ; ++oq)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int o = oq * 4 + v;
+                    if (o < a.Cout_g) out_g[(size_t)o * P + pl] = acc[oq][v] + bv[oq][v];
+                }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gradWeight
 // ---------------------------------------------------------------------------
@@ -341,9 +440,61 @@ void sg_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
     hipLaunchKernelGGL((sg_conv_kernel<3, 3, CIN, OQ, FLIP>), dim3(blocks), dim3(256), lds, st, a);
 }
 
+// The row-per-DMA fast path: 3x3 at unit stride and dilation, padded rows of
+// at most 64 floats. Bands of about 16 rows keep the tile near 17 KiB, so
+// eight workgroups share a CU.
+bool sg_row64_ok(const SgProblem& p)
+{
+    return p.kh == 3 && p.kw == 3 && p.sh == 1 && p.sw == 1 && p.dh == 1 && p.dw == 1 &&
+           p.Wout + 2 <= 64 && p.ph >= 0 && p.pw >= 0 && p.pw <= 2;
+}
+
+template <int CIN, int OQ, bool FLIP>
+void sg_row64_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
+{
+    hipLaunchKernelGGL((sg_conv_row64_kernel<CIN, OQ, FLIP>), dim3(blocks), dim3(256), lds, st, a);
+}
+
+bool sg_run_row64(const SgProblem& p, hipStream_t st)
+{
+    const int CINq = sg_cinq(p.Cin_g);
+    const int OQ = p.Cout_g <= 4 ? 1 : 2;
+    SgArgs a;
+    a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.N = p.N; a.G = p.G;
+    a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
+    a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
+    a.sh = 1; a.sw = 1; a.dh = 1; a.dw = 1; a.ph = p.ph; a.pw = p.pw;
+    a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
+    const int nb = (p.Hout + 15) / 16;
+    a.R = (p.Hout + nb - 1) / nb;
+    a.nbands = (p.Hout + a.R - 1) / a.R;
+    a.LR = a.R + 2;
+    a.LW = 64;
+    a.plane = a.LR * 64;
+    a.div_plane = make_fastdiv((uint32_t)a.plane);
+    a.div_LW = make_fastdiv(64u);
+    a.div_Wout = make_fastdiv((uint32_t)p.Wout);
+    const int64_t blocks = (int64_t)p.N * p.G * a.nbands;
+    if (blocks >= (1 << 30)) return false;
+    const size_t lds = ((size_t)CINq * a.plane + (size_t)CINq * 9 * 4 * OQ) * 4;
+#define SG_CASE(cin, oq)                                                          \
+    if (CINq == cin && OQ == oq) {                                                \
+        if (p.flip) sg_row64_launch<cin, oq, true>(a, (int)blocks, lds, st);      \
+        else sg_row64_launch<cin, oq, false>(a, (int)blocks, lds, st);            \
+        return true;                                                              \
+    }
+    SG_CASE(1, 1) SG_CASE(2, 1) SG_CASE(4, 1) SG_CASE(1, 2) SG_CASE(2, 2) SG_CASE(4, 2)
+#undef SG_CASE
+    return false;
+}
+
 bool sg_run(const SgProblem& p, hipStream_t st)
 {
     if (!sg_problem_ok(p)) return false;
+#ifndef GCONV_SG_NO_ROW64
+    if (sg_row64_ok(p)) return sg_run_row64(p, st);
+#endif
     const int CINq = sg_cinq(p.Cin_g);
     const int OQ = p.Cout_g <= 4 ? 1 : 2;
     SgArgs a;
