@@ -262,6 +262,7 @@ struct SgWArgs {
     int sh, sw, dh, dw, ph, pw;
     int R, nbands, LW, LR, plane;   // input band
     int dplane;                     // dy band plane stride (== 8 mod 32)
+    int run, nruns;                 // row-per-DMA kernel: images per workgroup, workgroups per group
     FastDiv div_plane, div_LW, div_Wo, div_dband;
 };
 
@@ -364,6 +365,116 @@ __global__ void __launch_bounds__(256) sg_wgrad_kernel(SgWArgs a)
                            red[(2 * T + t) * 16 + kc]) +
                           red[(3 * T + t) * 16 + kc];
         out[kc * T + t] = sum;
+    }
+}
+
+// Unit stride and dilation, padded rows of at most 64 floats. A workgroup owns
+// one group and a run of images (a.R images from image n0), loops over their
+// bands and keeps its sums in registers, so the cross-lane reduction runs
+// once per workgroup. Bands of x and dy are staged one row per DMA
+// instruction ([4][rows][64] planes, padded to 8 mod 32 so the 4 channels x 8
+// pixels of a half-wave hit distinct banks). Each wave walks whole output
+// rows in 16-pixel steps (MFMA block b = pixel b of the step; columns past the
+// image width hold dy = 0), so a step costs one dy read, nine x reads at
+// immediate offsets and nine MFMAs.
+template <int NSTEP>
+__global__ void __launch_bounds__(256) sg_wgrad_row64_kernel(SgWArgs a)
+{
+    constexpr int T = 9;
+    extern __shared__ float lds[];  // [4][plane] x rows, [4][dplane] dy rows; later [4][T*16] sums
+    float* ds = lds + 4 * a.plane;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c4 = lane & 3, blk = lane >> 2;  // this lane's channel (c and k), MFMA block
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int g = bid % a.G;
+    const int chunk = bid / a.G;               // image run
+    const int n_begin = chunk * a.run;
+    const int n_end = min(a.N, n_begin + a.run);
+
+    const int wcol = lane - a.pw;
+    const bool colok = (unsigned)wcol < (unsigned)a.W;
+    // Lanes past the image width may read up to two floats beyond the last x
+    // row of a plane (times dy = 0): keep the pad after each plane zero.
+    if (tid < 32) lds[(tid >> 3) * a.plane + (a.R + 2) * 64 + (tid & 7)] = 0.f;
+
+    f4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+    const float* xl = lds + c4 * a.plane + blk;
+    const float* dl = ds + c4 * a.dplane + blk;
+
+    for (int n = n_begin; n < n_end; ++n) {
+        const float* xg = a.x + ((size_t)n * a.C + (size_t)g * a.Cg) * a.H * a.W;
+        const float* dyg = a.dy + ((size_t)n * a.K + (size_t)g * a.Kg) * a.Ho * a.Wo;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, (uint32_t)a.Cg * a.H * a.W * 4u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, (uint32_t)a.Kg * a.Ho * a.Wo * 4u);
+        for (int ho0 = 0; ho0 < a.Ho; ho0 += a.R) {
+            const int rows = min(a.R, a.Ho - ho0);
+            const int hb = ho0 - a.ph;
+            const int LR = rows + 2;
+            __syncthreads();  // every wave is done with the previous band
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                for (int r = wave; r < LR; r += 4) {
+                    const int h = hb + r;
+                    const bool ok = colok && c < a.Cg && (unsigned)h < (unsigned)a.H;
+                    load_lds64(rx, lds + c * a.plane + r * 64,
+                               ok ? (uint32_t)((c * a.H + h) * a.W + wcol) * 4u : kOOB);
+                }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                for (int r = wave; r < rows; r += 4) {
+                    // Rows of the band only; channels past Kg fall outside the resource.
+                    load_lds64(rd, ds + k * a.dplane + r * 64,
+                               lane < a.Wo ? (uint32_t)((k * a.Ho + ho0 + r) * a.Wo + lane) * 4u : kOOB);
+                }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            for (int r = wave; r < rows; r += 4) {
+                const float* xr = xl + r * 64;
+                const float* dr = dl + r * 64;
+#pragma unroll
+                for (int st = 0; st < NSTEP; ++st) {
+                    const float dv = dr[st * 16];
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        acc[t] = mfma4(dv, xr[st * 16 + (t / 3) * 64 + t % 3], acc[t]);
+                }
+            }
+        }
+    }
+
+    // acc[t][v] of lane l = sum over its block's pixels of dy[k = v] * x[c = l%4].
+    // Sum the 16 blocks (lanes with equal l%4), in a fixed butterfly order.
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sum = acc[t][v];
+            sum += __shfl_xor(sum, 4, 64);
+            sum += __shfl_xor(sum, 8, 64);
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            acc[t][v] = sum;
+        }
+    __syncthreads();  // LDS reuse for the cross-wave sum
+    float* red = lds;  // [wave][t][k(4)][c(4)]
+    if (lane < 4) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[(wave * T + t) * 16 + v * 4 + lane] = acc[t][v];
+    }
+    __syncthreads();
+    // Partial of this (image run, group): [chunk][g][k][c][t].
+    float* out = a.ws + ((size_t)chunk * a.G + g) * (16 * T);
+    for (int e = tid; e < 16 * T; e += 256) {
+        const int t = e % T, kc = e / T;  // kc = k*4 + c
+        out[e] = ((red[(0 * T + t) * 16 + kc] + red[(1 * T + t) * 16 + kc]) +
+                  red[(2 * T + t) * 16 + kc]) +
+                 red[(3 * T + t) * 16 + kc];
     }
 }
 
@@ -557,7 +668,14 @@ SgProblem sg_bwd_data_problem(const Shape& s, const float* dy, const float* w, f
 // fall in distinct banks.
 int pad8(int v) { return (v + 23) / 32 * 32 + 8; }
 
-bool sgw_plan(const Shape& s, SgWArgs* out)
+// The row-per-DMA gradWeight kernel: unit stride and dilation, padded rows of
+// at most 64 floats; bands of about 16 rows.
+bool sgw_row64_ok(const Shape& s)
+{
+    return s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1 && s.Wo + 2 <= 64;
+}
+
+bool sgw_plan(const Shape& s, SgWArgs* out, bool* row64 = nullptr)
 {
     if (!(s.kh == 3 && s.kw == 3)) return false;
     if (s.Cg > 4 || s.Kg > 4 || s.N < 1) return false;
@@ -565,6 +683,29 @@ bool sgw_plan(const Shape& s, SgWArgs* out)
     a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
     a.G = s.G; a.Cg = s.Cg; a.Kg = s.Kg;
     a.sh = s.sh; a.sw = s.sw; a.dh = s.dh; a.dw = s.dw; a.ph = s.ph; a.pw = s.pw;
+    if ((int64_t)(s.Cg + 4) * s.H * s.W * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)(s.Kg + 4) * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
+#ifndef GCONV_SG_NO_ROW64
+    if (sgw_row64_ok(s)) {
+        // Bands of about 16 rows; runs of images such that about 1024
+        // workgroups (four per CU) cover all groups.
+        const int nb = (s.Ho + 15) / 16;
+        a.R = (s.Ho + nb - 1) / nb;
+        const int runs = std::max(1, std::min(s.N, 1024 / std::max(1, s.G)));
+        a.run = (s.N + runs - 1) / runs;
+        a.nruns = (s.N + a.run - 1) / a.run;
+        a.nbands = (s.Ho + a.R - 1) / a.R;
+        a.LW = 64;
+        a.LR = a.R + 2;
+        a.plane = a.LR * 64 + 8;  // == 8 (mod 32)
+        a.dplane = a.R * 64 + 8;
+        if ((int64_t)a.nruns * s.G >= (1 << 30)) return false;
+        if (out) *out = a;
+        if (row64) *row64 = true;
+        return true;
+    }
+#endif
+    if (row64) *row64 = false;
     a.LW = (s.Wo - 1) * s.sw + (s.kw - 1) * s.dw + 1;
     // Rows per band: the most whose input and dy bands fit the LDS budget.
     int R = s.Ho;
@@ -605,8 +746,10 @@ bool smallgroup_bwd_filter_supported(const Shape& s) { return sgw_plan(s, nullpt
 size_t smallgroup_bwd_filter_workspace(const Shape& s)
 {
     SgWArgs a;
-    if (!sgw_plan(s, &a)) return 0;
-    return (size_t)s.N * a.nbands * s.G * 16 * s.kh * s.kw * sizeof(float);
+    bool row64 = false;
+    if (!sgw_plan(s, &a, &row64)) return 0;
+    const size_t sets = row64 ? (size_t)a.nruns : (size_t)s.N * a.nbands;
+    return sets * s.G * 16 * s.kh * s.kw * sizeof(float);
 }
 
 bool smallgroup_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
@@ -625,15 +768,30 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
                            hipStream_t st)
 {
     SgWArgs a;
-    if (!sgw_plan(s, &a)) return false;
+    bool row64 = false;
+    if (!sgw_plan(s, &a, &row64)) return false;
     a.x = x;
     a.dy = dy;
     a.ws = ws;
     const int T = s.kh * s.kw;
-    const size_t lds =
-        std::max((size_t)ceil64(4 * a.plane) + (size_t)4 * a.dplane, (size_t)4 * T * 16) * 4;
     const int blocks = s.N * a.nbands * s.G;
-    hipLaunchKernelGGL((sg_wgrad_kernel<3, 3>), dim3(blocks), dim3(256), lds, st, a);
+    if (row64) {
+        const size_t lds = std::max((size_t)4 * a.plane + (size_t)4 * a.dplane, (size_t)4 * T * 16) * 4;
+        const int nstep = (s.Wo + 15) / 16;
+        const int rblocks = a.nruns * s.G;
+        if (nstep == 1) hipLaunchKernelGGL(sg_wgrad_row64_kernel<1>, dim3(rblocks), dim3(256), lds, st, a);
+        else if (nstep == 2) hipLaunchKernelGGL(sg_wgrad_row64_kernel<2>, dim3(rblocks), dim3(256), lds, st, a);
+        else if (nstep == 3) hipLaunchKernelGGL(sg_wgrad_row64_kernel<3>, dim3(rblocks), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL(sg_wgrad_row64_kernel<4>, dim3(rblocks), dim3(256), lds, st, a);
+        const int total = s.G * 16 * T;
+        hipLaunchKernelGGL(sg_wgrad_reduce, dim3((total + 15) / 16), dim3(256), 0, st, ws, dw,
+                           a.nruns, s.G, s.Kg, s.Cg, T);
+        return true;
+    } else {
+        const size_t lds =
+            std::max((size_t)ceil64(4 * a.plane) + (size_t)4 * a.dplane, (size_t)4 * T * 16) * 4;
+        hipLaunchKernelGGL((sg_wgrad_kernel<3, 3>), dim3(blocks), dim3(256), lds, st, a);
+    }
     const int total = s.G * 16 * T;
     hipLaunchKernelGGL(sg_wgrad_reduce, dim3((total + 15) / 16), dim3(256), 0, st, ws, dw,
                        s.N * a.nbands, s.G, s.Kg, s.Cg, T);
