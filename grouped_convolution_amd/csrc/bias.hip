@@ -1,0 +1,149 @@
+// bias.hip -- gradBias for grouped 2-D convolution, NCHW fp32:
+//   db[k] = sum over n, ho, wo of dy[n, k, ho, wo]
+// (a plain reduction of dy over everything but the channel: "Pointwise
+// Broadcast/Reduce" on the dlprimitives blog, the bias-gradient formula).
+// Two passes, deterministic: split blocks write partial sums laid out
+// [split][channel], then one thread per channel adds its splits in order
+// (consecutive channels read consecutive partials).
+//   plane layout (Ho*Wo > 1): block (s, k) sums images [s*chunk, (s+1)*chunk)
+//     of plane k, with 16-byte loads when the plane length is a multiple of 4;
+//   column layout (Ho*Wo == 1, dy is [N, K], fully-connected mode): block
+//     (kb, s) sums rows [s*chunk, (s+1)*chunk) of 1024 columns (4 per thread).
+#include "device_util.h"
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace {
+
+constexpr int kB = 256;
+
+// Sum of v over the 256 threads; the total is returned to thread 0.
+__device__ __forceinline__ float block_sum(float v, float* lds4)
+{
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) lds4[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    if (threadIdx.x == 0) t = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+    return t;
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kB)
+bias_planes_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, int K, int P,
+                    int chunk)
+{
+    __shared__ float lds4[4];
+    const int sidx = blockIdx.x, k = blockIdx.y;
+    const int n0 = sidx * chunk, n1 = min(N, n0 + chunk);
+    float acc = 0.f;
+    if constexpr (VEC) {
+        const int P4 = P >> 2;
+        f4 a4 = f4{0.f, 0.f, 0.f, 0.f};
+        for (int n = n0; n < n1; ++n) {
+            const f4* plane = reinterpret_cast<const f4*>(dy + ((int64_t)n * K + k) * P);
+#pragma unroll 4
+            for (int p = threadIdx.x; p < P4; p += kB) a4 += plane[p];
+        }
+        acc = (a4.x + a4.y) + (a4.z + a4.w);
+    } else {
+        for (int n = n0; n < n1; ++n) {
+            const float* plane = dy + ((int64_t)n * K + k) * P;
+#pragma unroll 4
+            for (int p = threadIdx.x; p < P; p += kB) acc += plane[p];
+        }
+    }
+    const float tot = block_sum(acc, lds4);
+    if (threadIdx.x == 0) ws[(int64_t)sidx * K + k] = tot;
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kB)
+bias_cols_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, int K, int chunk)
+{
+    const int sidx = blockIdx.y;
+    const int n0 = sidx * chunk, n1 = min(N, n0 + chunk);
+    if constexpr (VEC) {
+        const int k4 = blockIdx.x * kB + threadIdx.x;  // 4 columns per thread
+        if (k4 * 4 >= K) return;
+        f4 a = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int n = n0; n < n1; ++n) a += reinterpret_cast<const f4*>(dy + (int64_t)n * K)[k4];
+        reinterpret_cast<f4*>(ws + (int64_t)sidx * K)[k4] = a;
+    } else {
+        const int k = blockIdx.x * kB + threadIdx.x;
+        if (k >= K) return;
+        float a = 0.f;
+#pragma unroll 4
+        for (int n = n0; n < n1; ++n) a += dy[(int64_t)n * K + k];
+        ws[(int64_t)sidx * K + k] = a;
+    }
+}
+
+// db[k] = sum over s of ws[s*K + k], in split order.
+__global__ void __launch_bounds__(kB)
+bias_finalize(const float* __restrict__ ws, float* __restrict__ db, int K, int S)
+{
+    const int k = blockIdx.x * kB + threadIdx.x;
+    if (k >= K) return;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) acc += ws[(int64_t)s * K + k];
+    db[k] = acc;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool cols_vec(const Shape& s) { return (s.K & 3) == 0; }
+
+// Splits: about 2048 partial blocks for the plane layout (whole images per
+// block); about 1024 blocks of 1024 columns for the column layout.
+int bias_splits(const Shape& s)
+{
+    const int P = s.Ho * s.Wo;
+    int S;
+    if (P == 1) {
+        const int cpb = cols_vec(s) ? 4 * kB : kB;  // columns per block
+        const int kb = (s.K + cpb - 1) / cpb;
+        S = (1024 + kb - 1) / kb;
+    } else {
+        S = (2048 + s.K - 1) / s.K;
+    }
+    if (S > s.N) S = s.N;
+    if (S < 1) S = 1;
+    return S;
+}
+
+}  // namespace
+
+size_t bias_workspace_bytes(const Shape& s)
+{
+    if (s.N == 0) return 0;
+    return (size_t)s.K * (size_t)bias_splits(s) * sizeof(float);
+}
+
+void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStream_t st)
+{
+    const int P = s.Ho * s.Wo;
+    const int S = bias_splits(s);
+    const int chunk = (s.N + S - 1) / S;
+    if (P == 1) {
+        // (the split count, hence the workspace size, does not depend on the
+        // pointers: only the load width does)
+        if (cols_vec(s) && aligned16(dy) && aligned16(ws))
+            hipLaunchKernelGGL(bias_cols_partial<true>, dim3((s.K / 4 + kB - 1) / kB, S), dim3(kB),
+                               0, st, dy, ws, s.N, s.K, chunk);
+        else
+            hipLaunchKernelGGL(bias_cols_partial<false>, dim3((s.K + kB - 1) / kB, S), dim3(kB), 0,
+                               st, dy, ws, s.N, s.K, chunk);
+    } else if ((P & 3) == 0 && aligned16(dy)) {
+        hipLaunchKernelGGL(bias_planes_partial<true>, dim3(S, s.K), dim3(kB), 0, st, dy, ws, s.N,
+                           s.K, P, chunk);
+    } else {
+        hipLaunchKernelGGL(bias_planes_partial<false>, dim3(S, s.K), dim3(kB), 0, st, dy, ws, s.N,
+                           s.K, P, chunk);
+    }
+    hipLaunchKernelGGL(bias_finalize, dim3((s.K + kB - 1) / kB), dim3(kB), 0, st, ws, db, s.K, S);
+}
+
+}  // namespace gconv

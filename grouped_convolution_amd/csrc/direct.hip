@@ -135,48 +135,6 @@ direct_bwd_filter_kernel(Shape s, const float* __restrict__ x, const float* __re
     }
 }
 
-// Partial bias sums, plane layout (Ho*Wo > 1): block (s, k) sums images
-// [s*chunk, (s+1)*chunk) of plane k into ws[k*S + s].
-__global__ void __launch_bounds__(kBlock)
-bias_planes_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, int K, int P,
-                    int chunk)
-{
-    __shared__ float lds4[4];
-    const int sidx = blockIdx.x, k = blockIdx.y, S = gridDim.x;
-    const int n0 = sidx * chunk, n1 = min(N, n0 + chunk);
-    float acc = 0.f;
-    for (int n = n0; n < n1; ++n) {
-        const float* plane = dy + ((int64_t)n * K + k) * P;
-        for (int p = threadIdx.x; p < P; p += kBlock) acc += plane[p];
-    }
-    const float tot = block_sum_256(acc, lds4);
-    if (threadIdx.x == 0) ws[(int64_t)k * S + sidx] = tot;
-}
-
-// Partial bias sums, column layout (Ho*Wo == 1, dy is [N, K]): thread k of
-// block (kt, s) sums rows [s*chunk, (s+1)*chunk) of column k into ws[k*S + s].
-__global__ void __launch_bounds__(kBlock)
-bias_cols_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, int K, int chunk)
-{
-    const int k = blockIdx.x * kBlock + threadIdx.x, sidx = blockIdx.y, S = gridDim.y;
-    if (k >= K) return;
-    const int n0 = sidx * chunk, n1 = min(N, n0 + chunk);
-    float acc = 0.f;
-    for (int n = n0; n < n1; ++n) acc += dy[(int64_t)n * K + k];
-    ws[(int64_t)k * S + sidx] = acc;
-}
-
-// db[k] = sum_s ws[k*S + s], in index order.
-__global__ void __launch_bounds__(kBlock)
-bias_finalize(const float* __restrict__ ws, float* __restrict__ db, int K, int S)
-{
-    const int k = blockIdx.x * kBlock + threadIdx.x;
-    if (k >= K) return;
-    float acc = 0.f;
-    for (int s = 0; s < S; ++s) acc += ws[(int64_t)k * S + s];
-    db[k] = acc;
-}
-
 __global__ void __launch_bounds__(kBlock) fill_zero_kernel(float* p, int64_t count)
 {
     for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < count;
@@ -188,20 +146,6 @@ unsigned grid_for(int64_t total)
 {
     const int64_t blocks = (total + kBlock - 1) / kBlock;
     return (unsigned)(blocks < 65536 ? (blocks < 1 ? 1 : blocks) : 65536);
-}
-
-// Split count for the bias reduction: about 2048 partial sums in flight.
-int bias_splits(const Shape& s)
-{
-    const int P = s.Ho * s.Wo;
-    int S;
-    if (P == 1)
-        S = (int)((2048 + (s.K + kBlock - 1) / kBlock - 1) / ((s.K + kBlock - 1) / kBlock));
-    else
-        S = (2048 + s.K - 1) / s.K;
-    if (S > s.N) S = s.N;
-    if (S < 1) S = 1;
-    return S;
 }
 
 }  // namespace
@@ -226,28 +170,6 @@ void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* d
     const int64_t blocks = s.w_elems < (1 << 20) ? s.w_elems : (1 << 20);
     hipLaunchKernelGGL(direct_bwd_filter_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, s,
                        x, dy, dw);
-}
-
-size_t bias_workspace_bytes(const Shape& s)
-{
-    if (s.N == 0) return 0;
-    return (size_t)s.K * (size_t)bias_splits(s) * sizeof(float);
-}
-
-void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStream_t st)
-{
-    const int P = s.Ho * s.Wo;
-    const int S = bias_splits(s);
-    const int chunk = (s.N + S - 1) / S;
-    if (P == 1) {
-        hipLaunchKernelGGL(bias_cols_partial, dim3((s.K + kBlock - 1) / kBlock, S), dim3(kBlock),
-                           0, st, dy, ws, s.N, s.K, chunk);
-    } else {
-        hipLaunchKernelGGL(bias_planes_partial, dim3(S, s.K), dim3(kBlock), 0, st, dy, ws, s.N,
-                           s.K, P, chunk);
-    }
-    hipLaunchKernelGGL(bias_finalize, dim3((s.K + kBlock - 1) / kBlock), dim3(kBlock), 0, st, ws,
-                       db, s.K, S);
 }
 
 void fill_zero(float* p, int64_t count, hipStream_t st)
