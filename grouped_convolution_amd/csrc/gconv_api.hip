@@ -123,6 +123,9 @@ int choose_path(const Shape& s, int op)
 {
     const int forced = g_path_override.load();
     if (forced != GCONV_PATH_AUTO) return forced;
+    // gradBias is one reduction kernel pair whatever the shape; it reports
+    // the direct path.
+    if (op == GCONV_OP_BWD_BIAS) return GCONV_PATH_DIRECT;
     const int T = s.kh * s.kw;
     // Kernel == input: one dense layer per group on the flattened image.
     if (is_fc_mode(s) && path_supports(GCONV_PATH_FC, s, op)) return GCONV_PATH_FC;

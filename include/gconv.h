@@ -92,7 +92,7 @@ typedef enum gconv_op {
 typedef enum gconv_path {
     GCONV_PATH_AUTO = 0,       /* the dispatcher's own choice (default) */
     GCONV_PATH_DIRECT = 1,     /* general direct kernels: any valid descriptor */
-    GCONV_PATH_SMALLGROUP = 2, /* VALU/LDS kernels for few channels per group */
+    GCONV_PATH_SMALLGROUP = 2, /* few channels per group: HBM-bound 4x4x1-MFMA kernels */
     GCONV_PATH_IGEMM = 3,      /* fp32-MFMA implicit GEMM, groups in the grid */
     GCONV_PATH_FC = 4          /* kernel == input: plain fp32-MFMA GEMM */
 } gconv_path;
@@ -141,7 +141,10 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
 int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* Kernel family the dispatcher would run `op` on for this descriptor. */
+/*
+ * Kernel family the dispatcher would run `op` on for this descriptor
+ * (gradBias is one reduction for every shape and reports GCONV_PATH_DIRECT).
+ */
 int gconv_select_path(const gconv_desc* d, int op, int* path);
 
 /*
