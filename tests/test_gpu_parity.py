@@ -304,6 +304,47 @@ def test_workload_integer_probes_exact(name):
     assert np.array_equal(db.cpu().numpy().astype(np.float64), oracle.bwd_bias(dy)[0])
 
 
+EDGE_CASES = [
+    # flat-pixel MFMA conv: 48 outputs per group (three waves) with a partial
+    # 2-channel reduction chunk on the forward pass, 18 outputs (two waves
+    # across pixels) on gradInput; tiles spanning image boundaries
+    (dict(N=3, C=18, K=48, H=12, W=12, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1),
+     {"fwd": "igemm", "bwd_data": "igemm"}),
+    # two groups, 5x5, outputs past one 64-channel tile, ragged last tile
+    (dict(N=2, C=2 * 20, K=2 * 70, H=11, W=13, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1,
+          G=2), {"fwd": "igemm", "bwd_data": "igemm"}),
+    # small-group gradWeight over image runs: 37 images, 32 groups -> runs of
+    # two images, the last run holding one
+    (dict(N=37, C=128, K=128, H=12, W=14, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=32),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # row-per-DMA small-group kernels at the widest row (62 + 2 = 64 floats)
+    (dict(N=2, C=8, K=8, H=5, W=62, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # ... without padding (tile columns start at the image edge) and with pad 2
+    (dict(N=2, C=3, K=4, H=7, W=40, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    (dict(N=1, C=4, K=4, H=6, W=30, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=1),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE_CASES)))
+def test_kernel_edge_cases(case):
+    """Shapes at the edges of the tiled kernels' layouts, on the dispatcher's
+    own choice (asserted), every element against the oracle."""
+    d, paths = EDGE_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
+    for op, name in paths.items():
+        chosen = G.gconv_select_path(desc, getattr(G, "OP_" + op.upper()))
+        assert G.PATH_NAMES[chosen] == name, (d, op, G.PATH_NAMES[chosen])
+    x, w, b = tensors(d, 1500 + case)
+    y_ref, _ = oracle.fwd(x, w, b, **kw)
+    dy = draw(("normal", 1.0), y_ref.shape, 1510 + case)
+    say("edge case %s" % d)
+    compare_full("edge %s" % d, gpu_all_ops(x, w, b, dy, **kw), oracle_all(x, w, b, dy, kw))
+
+
 def test_fc_all_ones_bit_exact():
     """The all-ones fully-connected problem of the cudnn.torch issue: every
     element of all four results equals its integer closed form."""
