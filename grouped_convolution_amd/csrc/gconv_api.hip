@@ -167,6 +167,9 @@ int prologue(const gconv_desc* d, int op, Shape* s, int* path, void* ws, size_t 
     if (ws_bytes < need || (need > 0 && ws == nullptr))
         return fail(GCONV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes,
                     need);
+    // Partial sums are read back with 16-byte loads.
+    if (need > 0 && ((uintptr_t)ws & 15) != 0)
+        return fail(GCONV_ERR_WORKSPACE, "workspace pointer %p is not 16-byte aligned", ws);
     return GCONV_OK;
 }
 
@@ -346,7 +349,7 @@ const char* gconv_status_string(int status)
         case GCONV_ERR_NULL: return "null pointer";
         case GCONV_ERR_SHAPE: return "invalid shape";
         case GCONV_ERR_GROUPS: return "channels not divisible by groups";
-        case GCONV_ERR_WORKSPACE: return "workspace too small";
+        case GCONV_ERR_WORKSPACE: return "workspace too small or misaligned";
         case GCONV_ERR_HIP: return "HIP error";
         case GCONV_ERR_UNSUPPORTED: return "unsupported";
         case GCONV_ERR_ARG: return "invalid argument";

@@ -266,9 +266,10 @@ __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
             for (int v = 0; v < 4; ++v) out[(t * WK + m) * 256 + v * 64 + lane] = acc[t][m][v];
 }
 
-// dw from the partial tiles. Block = 32 elements x 8 split groups: thread
-// (e, sg) sums splits sg, sg+8, ... in order; the 8 group sums are then added
-// in order, so the result does not depend on scheduling.
+// dw from the partial tiles. Block = 16 quads of consecutive elements x 16
+// split groups: thread (quad, sg) sums splits sg, sg+16, ... in order with
+// 16-byte loads; the 16 group sums are then added in order, so the result
+// does not depend on scheduling. (per_split is a multiple of 256.)
 template <int T, int WC, int WK>
 __global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float* __restrict__ ws,
                                                            float* __restrict__ dw, int splits,
@@ -277,18 +278,26 @@ __global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float* __restri
 {
     constexpr int CT = 16 * WC;
     constexpr int KT = 16 * WK * (4 / WC);
-    __shared__ float part[8][33];
-    const int el = threadIdx.x & 31, sg = threadIdx.x >> 5;
-    const int j = blockIdx.x * 32 + el;
-    float sum = 0.f;
-    if (j < per_split)
-        for (int s = sg; s < splits; s += 8) sum += ws[(size_t)s * per_split + j];
-    part[sg][el] = sum;
+    __shared__ f4 part[16][17];
+    const int qd = threadIdx.x & 15, sg = threadIdx.x >> 4;
+    const int j4 = blockIdx.x * 16 + qd;  // quad index
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    if (j4 * 4 < per_split) {
+        const f4* src = reinterpret_cast<const f4*>(ws) + j4;
+        const size_t stride4 = (size_t)per_split / 4;
+#pragma unroll 8
+        for (int s = sg; s < splits; s += 16) acc += src[(size_t)s * stride4];
+    }
+    part[sg][qd] = acc;
     __syncthreads();
-    if (sg != 0 || j >= per_split) return;
-    sum = part[0][el];
+    if (threadIdx.x >= 64) return;
+    // Thread e of the first 64 finishes element 4*qd + e%4 of the block's quads.
+    const int q2 = threadIdx.x >> 2, comp = threadIdx.x & 3;
+    const int j = (blockIdx.x * 16 + q2) * 4 + comp;
+    if (j >= per_split) return;
+    float sum = part[0][q2][comp];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) sum += part[i][el];
+    for (int i = 1; i < 16; ++i) sum += part[i][q2][comp];
     // j = ((tile*4 + wave)*T + t)*WK*256 + m*256 + v*64 + lane
     const int lane = j & 63, v = (j >> 6) & 3;
     int rest = j >> 8;
@@ -437,7 +446,7 @@ bool launch_r(const Plan& p, hipStream_t st)
 template <int T, int WC, int WK>
 void launch_reduce(const Plan& p, const Shape& s, float* ws, float* dw, hipStream_t st)
 {
-    const int blocks = (p.per_split + 31) / 32;
+    const int blocks = (p.per_split + 63) / 64;
     hipLaunchKernelGGL((wgrad_reduce_kernel<T, WC, WK>), dim3(blocks), dim3(256), 0, st, ws, dw,
                        p.a.splits, p.a.n_ctiles, p.a.n_ktiles, s.Cg, s.Kg, p.per_split);
 }

@@ -75,7 +75,7 @@ typedef enum gconv_status {
     GCONV_ERR_NULL = 1,        /* a required pointer is NULL */
     GCONV_ERR_SHAPE = 2,       /* a dimension < 1, a bad stride/pad/dilation, or Ho/Wo < 1 */
     GCONV_ERR_GROUPS = 3,      /* C or K not divisible by groups */
-    GCONV_ERR_WORKSPACE = 4,   /* workspace smaller than gconv_workspace_size() */
+    GCONV_ERR_WORKSPACE = 4,   /* workspace smaller than gconv_workspace_size(), or misaligned */
     GCONV_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
     GCONV_ERR_UNSUPPORTED = 6, /* valid descriptor the forced path cannot run */
     GCONV_ERR_ARG = 7          /* other bad argument, e.g. an output overlapping an input */
@@ -102,8 +102,9 @@ int gconv_output_dims(const gconv_desc* d, int64_t* Ho, int64_t* Wo);
 
 /*
  * Bytes of device workspace `op` needs for this descriptor (0 when none).
- * Pass at least this much to the op; the workspace may be NULL when 0.
- * The contents need no initialisation and are scratch after the call.
+ * Pass at least this much to the op, 16-byte aligned (GCONV_ERR_WORKSPACE
+ * otherwise); the workspace may be NULL when 0. The contents need no
+ * initialisation and are scratch after the call.
  */
 int gconv_workspace_size(const gconv_desc* d, int op, size_t* bytes);
 

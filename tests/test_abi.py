@@ -106,6 +106,10 @@ def test_null_and_workspace_errors():
     assert n > 0
     assert lib.gconv_bwd_bias(ctypes.byref(desc), fake, fake, None, 0, None) == 4
     assert lib.gconv_bwd_bias(ctypes.byref(desc), fake, fake, fake, n - 1, None) == 4
+    # a large enough workspace that is not 16-byte aligned is refused before any launch
+    dy, db, ws = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30004)
+    assert lib.gconv_bwd_bias(ctypes.byref(desc), dy, db, ws, n, None) == 4
+    assert b"aligned" in lib.gconv_last_error()
 
 
 def test_overlapping_output_rejected():
