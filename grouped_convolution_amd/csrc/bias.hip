@@ -3,8 +3,8 @@
 // (a plain reduction of dy over everything but the channel: "Pointwise
 // Broadcast/Reduce" on the dlprimitives blog, the bias-gradient formula).
 // Two passes, deterministic: split blocks write partial sums laid out
-// [split][channel], then one thread per channel adds its splits in order
-// (consecutive channels read consecutive partials).
+// [split][channel], then a second kernel adds each channel's splits in a
+// fixed order (consecutive channels read consecutive partials).
 //   plane layout (Ho*Wo > 1): block (s, k) sums images [s*chunk, (s+1)*chunk)
 //     of plane k, with 16-byte loads when the plane length is a multiple of 4;
 //   column layout (Ho*Wo == 1, dy is [N, K], fully-connected mode): block
@@ -81,16 +81,28 @@ bias_cols_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, i
     }
 }
 
-// db[k] = sum over s of ws[s*K + k], in split order.
+// db[k] = sum over s of ws[s*K + k]. Block = 16 channels x 16 split groups:
+// thread (kk, sg) adds splits sg, sg+16, ... in order, then the 16 group sums
+// are added in order (deterministic; many partials per channel spread over
+// the whole block instead of one thread).
 __global__ void __launch_bounds__(kB)
 bias_finalize(const float* __restrict__ ws, float* __restrict__ db, int K, int S)
 {
-    const int k = blockIdx.x * kB + threadIdx.x;
-    if (k >= K) return;
+    __shared__ float part[16][17];
+    const int kk = threadIdx.x & 15, sg = threadIdx.x >> 4;
+    const int k = blockIdx.x * 16 + kk;
     float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) acc += ws[(int64_t)s * K + k];
-    db[k] = acc;
+    if (k < K) {
+#pragma unroll 4
+        for (int s = sg; s < S; s += 16) acc += ws[(int64_t)s * K + k];
+    }
+    part[sg][kk] = acc;
+    __syncthreads();
+    if (sg != 0 || k >= K) return;
+    float sum = part[0][kk];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) sum += part[i][kk];
+    db[k] = sum;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -143,7 +155,7 @@ void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStrea
         hipLaunchKernelGGL(bias_planes_partial<false>, dim3(S, s.K), dim3(kB), 0, st, dy, ws, s.N,
                            s.K, P, chunk);
     }
-    hipLaunchKernelGGL(bias_finalize, dim3((s.K + kB - 1) / kB), dim3(kB), 0, st, ws, db, s.K, S);
+    hipLaunchKernelGGL(bias_finalize, dim3((s.K + 15) / 16), dim3(kB), 0, st, ws, db, s.K, S);
 }
 
 }  // namespace gconv
