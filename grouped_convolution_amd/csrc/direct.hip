@@ -154,6 +154,7 @@ void direct_fwd(const Shape& s, const float* x, const float* w, const float* bia
                 hipStream_t st)
 {
     if (s.y_elems == 0) return;
+    if (direct_tile_fwd(s, x, w, bias, y, st)) return;
     hipLaunchKernelGGL(direct_fwd_kernel, dim3(grid_for(s.y_elems)), dim3(kBlock), 0, st, s, x,
                        w, bias, y);
 }
@@ -161,12 +162,14 @@ void direct_fwd(const Shape& s, const float* x, const float* w, const float* bia
 void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
     if (s.x_elems == 0) return;
+    if (direct_tile_bwd_data(s, dy, w, dx, st)) return;
     hipLaunchKernelGGL(direct_bwd_data_kernel, dim3(grid_for(s.x_elems)), dim3(kBlock), 0, st, s,
                        dy, w, dx);
 }
 
 void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st)
 {
+    if (direct_tile_bwd_filter(s, x, dy, dw, st)) return;
     const int64_t blocks = s.w_elems < (1 << 20) ? s.w_elems : (1 << 20);
     hipLaunchKernelGGL(direct_bwd_filter_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, s,
                        x, dy, dw);

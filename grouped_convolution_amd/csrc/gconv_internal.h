@@ -35,6 +35,15 @@ void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
 void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
                        hipStream_t st);
 
+// LDS-tiled direct kernels for up to 32 output channels per group; return
+// false (nothing launched) where they do not apply.
+bool direct_tile_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                     hipStream_t st);
+bool direct_tile_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
+                          hipStream_t st);
+bool direct_tile_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
+                            hipStream_t st);
+
 // ---- fp32-MFMA implicit GEMM (forward; gradInput at stride 1) ---------------
 // *_supported() tell whether the family covers a shape; the launchers return
 // false if no kernel instance matches (the dispatcher checks support first).
