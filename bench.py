@@ -7,13 +7,19 @@ through the C-ABI library on torch's current HIP stream.
   value  = 3 * FLOP_conv * steps / (time of the timed steps)       [TFLOP/s]
   FLOP_conv = 2*N*K*Ho*Wo*(C/G)*kh*kw (the standard count, padded taps included)
 The default workload is the dense 3x3 64->64 56x56 batch-32 convolution.
-Per op, HIP events bracket every launch inside the timed region; the op with
-the largest total time is the "dominant kernel" of the roofline object. The
-CPU baseline times the fp64 oracle on a bounded sample (the first images of
-the same batch) on this host's cores.
+Per op, HIP events bracket every launch in a second timed region of eager
+steps; the op with the largest total time is the "dominant kernel" of the
+roofline object. The CPU baseline times the fp64 oracle on a bounded sample
+(the first images of the same batch) on this host's cores.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dense3x3]
-                    [--all-workloads] [--no-cpu-baseline]
+                    [--all-workloads] [--no-cpu-baseline] [--launch graph|eager]
+
+Each timed step issues the four C-ABI calls; --launch graph replays one HIP
+graph holding the step's four launches instead (captured once from prepared
+plans), which takes the host's launch cost out of small workloads. Per-op
+times come from a second timed region of eager steps with events around each
+launch.
 """
 from __future__ import annotations
 
@@ -114,22 +120,61 @@ def run_gpu(args, wl_name):
     torch.cuda.synchronize()
 
     K_steps = args.steps
-    ev = {op: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(K_steps)] for op in OPS}
+
+    # Timed region 1 -> `value`: K whole steps, bracketed by synchronisations.
+    # By default each step is the four C-ABI calls; with --launch graph it is
+    # one replay of a HIP graph holding the four launches (captured once from
+    # the prepared plans; every replay recomputes all four results). If the
+    # capture fails the calls are issued directly.
+    launch = args.launch
+    graph = None
+    if launch == "graph":
+        try:
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cs):
+                gplans = [G.Plan.fwd(x, w, b, y, **kw), G.Plan.bwd_data(dy, w, dx, **kw),
+                          G.Plan.bwd_filter(x, dy, dw, **kw), G.Plan.bwd_bias(dy, db)]
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=cs):
+                    for p in gplans:
+                        p()
+            torch.cuda.current_stream().wait_stream(cs)
+            for _ in range(args.warmup):
+                graph.replay()
+        except Exception as e:  # launch mode only: the same kernels run eagerly
+            log("HIP graph capture failed (%s); timing eager launches" % e)
+            graph, launch = None, "eager"
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
+    for s in range(K_steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            for op in OPS:
+                plans[op]()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+
+    # Timed region 2 -> per-op times (the roofline object): K more eager steps
+    # with HIP events around every launch on its stream (an event between two
+    # launches costs a small pipeline bubble, so these are not summed into
+    # `value`).
+    ev = {op: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K_steps)] for op in OPS}
+    torch.cuda.synchronize()
     for s in range(K_steps):
         for op in OPS:
             e0, e1 = ev[op][s]
             e0.record()
             plans[op]()
             e1.record()
-    stop.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(stop)
     per_op_ms = {op: sum(a.elapsed_time(b_) for a, b_ in ev[op]) / K_steps for op in OPS}
 
     flop = conv_flop(wl, Ho, Wo)
@@ -167,9 +212,10 @@ def run_gpu(args, wl_name):
 
     ms_per_step = total_ms / K_steps
     value = 3.0 * flop / (ms_per_step * 1e-3) / 1e12
+
     return {
         "value": value, "ms_per_step": ms_per_step, "wall_s": wall, "ops": ops,
-        "roofline": roof, "Ho": Ho, "Wo": Wo, "flop_conv": flop,
+        "roofline": roof, "Ho": Ho, "Wo": Wo, "flop_conv": flop, "launch": launch,
         "device": torch.cuda.get_device_name(dev),
     }
 
@@ -214,6 +260,9 @@ def main():
     ap.add_argument("--all-workloads", action="store_true",
                     help="also time every workload and print one line each to stderr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="how the timed steps are issued: the four C-ABI calls directly "
+                         "(default), or replays of one HIP graph holding the four launches")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (for scaling the HBM "
@@ -250,7 +299,8 @@ def main():
             else:
                 r = run_gpu(args, name)
             log(json.dumps({"workload": name, "tflops": round(r["value"], 3),
-                            "ms_per_step": round(r["ms_per_step"], 4), "ops": r["ops"]}))
+                            "ms_per_step": round(r["ms_per_step"], 4), "launch": r["launch"],
+                            "ops": r["ops"]}))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -276,7 +326,8 @@ def main():
         "config": {"workload": wl.name, "x": list(wl.x_shape), "w": list(wl.w_shape),
                    "groups": wl.groups, "stride": wl.stride, "padding": wl.padding,
                    "dilation": wl.dilation, "bias": wl.b_dist is not None,
-                   "ops": list(OPS), "flop_per_step": 3 * res["flop_conv"]},
+                   "ops": list(OPS), "flop_per_step": 3 * res["flop_conv"],
+                   "launch": res["launch"]},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "ops": res["ops"],
