@@ -244,7 +244,10 @@ __global__ void __launch_bounds__(256) sg_conv_row64_kernel(SgArgs a)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int o = oq * 4 + v;
-                    if (o < a.Cout_g) out_g[(size_t)o * P + pl] = acc[oq][v] + bv[oq][v];
+                    // Streaming stores: the output is not read again here, so it
+                    // should not displace the input rows neighbouring bands reuse.
+                    if (o < a.Cout_g)
+                        __builtin_nontemporal_store(acc[oq][v] + bv[oq][v], out_g + (size_t)o * P + pl);
                 }
         }
     }
