@@ -23,9 +23,9 @@ STATUS = {0: "GCONV_OK", 1: "GCONV_ERR_NULL", 2: "GCONV_ERR_SHAPE", 3: "GCONV_ER
           4: "GCONV_ERR_WORKSPACE", 5: "GCONV_ERR_HIP", 6: "GCONV_ERR_UNSUPPORTED",
           7: "GCONV_ERR_ARG"}
 OP_FWD, OP_BWD_DATA, OP_BWD_FILTER, OP_BWD_BIAS = 0, 1, 2, 3
-PATH_AUTO, PATH_DIRECT, PATH_SMALLGROUP, PATH_IGEMM, PATH_FC = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_DIRECT, PATH_SMALLGROUP, PATH_IGEMM, PATH_FC, PATH_POINTWISE = 0, 1, 2, 3, 4, 5
 PATH_NAMES = {PATH_AUTO: "auto", PATH_DIRECT: "direct", PATH_SMALLGROUP: "smallgroup",
-              PATH_IGEMM: "igemm", PATH_FC: "fc"}
+              PATH_IGEMM: "igemm", PATH_FC: "fc", PATH_POINTWISE: "pointwise"}
 
 # Every symbol include/gconv.h declares.
 EXPORTS = ("gconv_output_dims", "gconv_workspace_size", "gconv_fwd", "gconv_bwd_data",

@@ -107,6 +107,7 @@ bool path_supports(int path, const Shape& s, int op)
             if (op == GCONV_OP_BWD_FILTER) return igemm_bwd_filter_supported(s);
             return false;
         case GCONV_PATH_FC: return fc_supported(s);
+        case GCONV_PATH_POINTWISE: return pointwise_supported(s);
         case GCONV_PATH_SMALLGROUP:
             if (op == GCONV_OP_FWD) return smallgroup_fwd_supported(s);
             if (op == GCONV_OP_BWD_DATA) return smallgroup_bwd_data_supported(s);
@@ -129,6 +130,9 @@ int choose_path(const Shape& s, int op)
     const int T = s.kh * s.kw;
     // Kernel == input: one dense layer per group on the flattened image.
     if (is_fc_mode(s) && path_supports(GCONV_PATH_FC, s, op)) return GCONV_PATH_FC;
+    // 1x1 at stride 1 without padding: the plane of each (image, group) is a
+    // matrix, and the convolution is a GEMM with the group's weight block.
+    if (s.kh == 1 && s.kw == 1 && path_supports(GCONV_PATH_POINTWISE, s, op)) return GCONV_PATH_POINTWISE;
     // A handful of channels per group (ResNeXt-style, depthwise-like): the
     // HBM-bound 4x4x1-MFMA kernels.
     if (path_supports(GCONV_PATH_SMALLGROUP, s, op)) return GCONV_PATH_SMALLGROUP;
@@ -151,6 +155,8 @@ size_t workspace_for(const Shape& s, int op, int path)
         return igemm_bwd_filter_workspace(s);
     if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_SMALLGROUP && s.N > 0)
         return smallgroup_bwd_filter_workspace(s);
+    if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_POINTWISE && s.N > 0)
+        return pointwise_bwd_filter_workspace(s);
     return 0;
 }
 
@@ -223,7 +229,7 @@ int gconv_select_path(const gconv_desc* d, int op, int* path)
 
 int gconv_set_path_override(int path)
 {
-    if (path < GCONV_PATH_AUTO || path > GCONV_PATH_FC)
+    if (path < GCONV_PATH_AUTO || path > GCONV_PATH_POINTWISE)
         return fail(GCONV_ERR_ARG, "unknown path %d", path);
     g_path_override.store(path);
     return GCONV_OK;
@@ -251,6 +257,7 @@ int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* 
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
         case GCONV_PATH_FC: fc_fwd(s, x, w, bias, y, hs); break;
+        case GCONV_PATH_POINTWISE: pointwise_fwd(s, x, w, bias, y, hs); break;
         case GCONV_PATH_SMALLGROUP:
             if (!smallgroup_fwd(s, x, w, bias, y, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
@@ -281,6 +288,7 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
         case GCONV_PATH_FC: fc_bwd_data(s, dy, w, dx, hs); break;
+        case GCONV_PATH_POINTWISE: pointwise_bwd_data(s, dy, w, dx, hs); break;
         case GCONV_PATH_SMALLGROUP:
             if (!smallgroup_bwd_data(s, dy, w, dx, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
@@ -314,6 +322,10 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             break;
         case GCONV_PATH_FC: fc_bwd_filter(s, x, dy, dw, hs); break;
+        case GCONV_PATH_POINTWISE:
+            if (!pointwise_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "pointwise gradWeight needs its workspace");
+            break;
         case GCONV_PATH_SMALLGROUP:
             if (!smallgroup_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");

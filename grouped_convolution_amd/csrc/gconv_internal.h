@@ -78,6 +78,15 @@ void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, f
 void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
 void fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st);
 
+// ---- pointwise (1x1, stride 1, no padding): batched fp32-MFMA GEMMs --------------
+bool pointwise_supported(const Shape& s);
+size_t pointwise_bwd_filter_workspace(const Shape& s);
+void pointwise_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                   hipStream_t st);
+void pointwise_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+bool pointwise_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+                          hipStream_t st);
+
 // ---- reductions -------------------------------------------------------------
 // db[k] = sum over (n, p < P) of dy[(n*K + k)*P + p], P = Ho*Wo.
 size_t bias_workspace_bytes(const Shape& s);

@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "device_util.h"
+#include "fastdiv.h"
 #include "gconv_internal.h"
 
 namespace gconv {
@@ -34,15 +35,30 @@ constexpr int SROW = BM + 4;          // row stride of a [32][row] tile (== 4 mo
 constexpr int TILE_R = BM * BR;       // floats of a swizzled [row][32] tile
 constexpr int TILE_N = BR * SROW;     // floats of a [32][row + 4] tile
 
+// C[M x N] = A[M x R] * B[R x N] for Z batch entries. Entry z uses block
+// z % a_mod of A (a_gs floats apart), z % b_mod of B, z % c_mod of C and
+// z % bias_mod of the bias: the groups of a layer, or (image, group) pairs
+// that share one weight block.
 struct GemmArgs {
     const float* A;
     const float* B;
     const float* bias;
     float* C;
-    int M, N, R, G;
+    int M, N, R, Z;
     int a_ld, b_ld, c_ld;          // leading dimension of A, B, C (their non-unit stride)
-    int64_t a_gs, b_gs, c_gs, bias_gs;  // group offsets (floats)
-    uint32_t a_bytes, b_bytes;     // extent each group's A / B resource may address
+    int a_mod, b_mod, c_mod, bias_mod;
+    int64_t a_gs, b_gs, c_gs, bias_gs;  // batch-entry offsets (floats)
+    int bias_rows;                 // bias indexed by the row (1) or by the column (0)
+    uint32_t a_bytes, b_bytes;     // extent each entry's A / B resource may address
+    // Reduction over several images (RIMG kernels): reduction index r is
+    // position r % r_img of image r / r_img, images a_is / b_is floats apart.
+    int r_img;
+    FastDiv div_rimg;
+    int64_t a_is, b_is;
+    // Split reduction: workgroup slice ks covers [ks*r_split, (ks+1)*r_split)
+    // and writes its partial C c_split floats after slice ks - 1.
+    int nsplit, r_split;
+    int64_t c_split;
     int m_tiles, n_tiles;
 };
 
@@ -50,9 +66,10 @@ struct GemmArgs {
 //   RCONTIG: element (row, r) at P[row*ld + r]; LDS [row][32], chunk c of row
 //            `row` stored at chunk position c ^ (row & 7).
 //   else:    element (row, r) at P[r*ld + row]; LDS [r][SROW].
-template <bool RCONTIG>
+template <bool RCONTIG, bool RIMG = false>
 __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, float* dst, int row0, int rows,
-                                           int r0, int R, int ld, int wave, int lane)
+                                           int r0, int R, int ld, int wave, int lane,
+                                           const GemmArgs* ga = nullptr, int64_t img_stride = 0)
 {
     if constexpr (RCONTIG) {
         // 64 instructions of 64 floats = 2 rows of 32 each.
@@ -63,8 +80,16 @@ __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, float* dst
             const int chunk = ((lane & 31) >> 2) ^ (row & 7);
             const int r = 4 * chunk + (lane & 3);
             const bool ok = row0 + row < rows && r0 + r < R;
-            load_lds64(rs, dst + i * 64,
-                       ok ? (uint32_t)((row0 + row) * ld + r0 + r) * 4u : kOOB);
+            uint32_t off;
+            if constexpr (RIMG) {
+                const uint32_t ra = (uint32_t)(r0 + r);
+                const uint32_t img = fastdiv(ra, ga->div_rimg);
+                off = (uint32_t)((int64_t)(row0 + row) * ld + (int64_t)img * img_stride +
+                                 (ra - img * (uint32_t)ga->r_img)) * 4u;
+            } else {
+                off = (uint32_t)((row0 + row) * ld + r0 + r) * 4u;
+            }
+            load_lds64(rs, dst + i * 64, ok ? off : kOOB);
         }
     } else {
         // 32 rows of 128 floats = 2 instructions per row.
@@ -95,9 +120,10 @@ __device__ __forceinline__ f4 frag(const float* t, int row, int kg, int q)
     }
 }
 
-template <bool A_RC, bool B_RC>
+template <bool A_RC, bool B_RC, bool RIMG>
 __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
 {
+    static_assert(!RIMG || (A_RC && B_RC), "the image-split reduction needs contiguous reductions");
     constexpr int TA = A_RC ? TILE_R : TILE_N;
     constexpr int TB = B_RC ? TILE_R : TILE_N;
     extern __shared__ float lds[];
@@ -110,11 +136,15 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
     const int mt = bid % a.m_tiles;
     bid /= a.m_tiles;
     const int nt = bid % a.n_tiles;
-    const int g = bid / a.n_tiles;
+    bid /= a.n_tiles;
+    const int z = bid % a.Z;
+    const int ks = bid / a.Z;
     const int m0 = mt * BM, n0 = nt * BN;
+    const int r_begin = ks * a.r_split;
+    const int r_end = min(a.R, r_begin + a.r_split);
 
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A + g * a.a_gs, a.a_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B + g * a.b_gs, a.b_bytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A + (z % a.a_mod) * a.a_gs, a.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B + (z % a.b_mod) * a.b_gs, a.b_bytes);
 
     f4 acc[4][4];
 #pragma unroll
@@ -125,11 +155,11 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
     auto issue = [&](int stage, int b) {
         float* ta = lds + b * (TA + TB);
         float* tb = ta + TA;
-        load_stage<A_RC>(ra, ta, m0, a.M, stage * BR, a.R, a.a_ld, wave, lane);
-        load_stage<B_RC>(rb, tb, n0, a.N, stage * BR, a.R, a.b_ld, wave, lane);
+        load_stage<A_RC, RIMG>(ra, ta, m0, a.M, r_begin + stage * BR, r_end, a.a_ld, wave, lane, &a, a.a_is);
+        load_stage<B_RC, RIMG>(rb, tb, n0, a.N, r_begin + stage * BR, r_end, a.b_ld, wave, lane, &a, a.b_is);
     };
 
-    const int nst = (a.R + BR - 1) / BR;
+    const int nst = (r_end - r_begin + BR - 1) / BR;
     issue(0, 0);
     for (int st = 0; st < nst; ++st) {
         const int b = st & 1;
@@ -159,14 +189,14 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
         __syncthreads();
     }
 
-    float* Cg = a.C + g * a.c_gs;
-    const float* bias = a.bias ? a.bias + g * a.bias_gs : nullptr;
+    float* Cg = a.C + (z % a.c_mod) * a.c_gs + ks * a.c_split;
+    const float* bias = a.bias ? a.bias + (z % a.bias_mod) * a.bias_gs : nullptr;
     const bool vec = (a.N & 3) == 0 && (a.c_ld & 3) == 0 && ((uintptr_t)Cg & 15) == 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = n0 + wn * 64 + j * 16 + 4 * q;
         f4 bv = f4{0.f, 0.f, 0.f, 0.f};
-        if (bias) {
+        if (bias && !a.bias_rows) {
             bv.x = n + 0 < a.N ? bias[n + 0] : 0.f;
             bv.y = n + 1 < a.N ? bias[n + 1] : 0.f;
             bv.z = n + 2 < a.N ? bias[n + 2] : 0.f;
@@ -176,7 +206,8 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
         for (int i = 0; i < 4; ++i) {
             const int m = m0 + wm * 64 + i * 16 + l16;
             if (m >= a.M) continue;
-            const f4 v = acc[i][j] + bv;
+            f4 v = acc[i][j] + bv;
+            if (bias && a.bias_rows) v += bias[m];
             float* row = Cg + (size_t)m * a.c_ld;
             if (vec && n + 3 < a.N) {
                 *(f4*)(row + n) = v;
@@ -190,7 +221,43 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
     }
 }
 
-template <bool A_RC, bool B_RC>
+// Sum of the split partials in slice order: out[e] = sum_s ws[s*E + e].
+__global__ void __launch_bounds__(256) gemm_split_reduce(const float* __restrict__ ws, float* __restrict__ out,
+                                                         int64_t E, int nsplit)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    if ((E & 3) == 0) {
+        const f4* w4 = (const f4*)ws;
+        f4* o4 = (f4*)out;
+        const int64_t E4 = E >> 2;
+        for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < E4; e += stride) {
+            f4 sum = w4[e];
+            for (int sl = 1; sl < nsplit; ++sl) sum += w4[sl * E4 + e];
+            o4[e] = sum;
+        }
+    } else {
+        for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < E; e += stride) {
+            float sum = ws[e];
+            for (int sl = 1; sl < nsplit; ++sl) sum += ws[sl * E + e];
+            out[e] = sum;
+        }
+    }
+}
+
+// Defaults that make the batch entries plain groups with one reduction slice.
+void plain(GemmArgs& a)
+{
+    a.a_mod = a.b_mod = a.c_mod = a.bias_mod = a.Z;
+    a.bias_rows = 0;
+    a.r_img = 0;
+    a.div_rimg = make_fastdiv(1);
+    a.a_is = a.b_is = 0;
+    a.nsplit = 1;
+    a.r_split = a.R;
+    a.c_split = 0;
+}
+
+template <bool A_RC, bool B_RC, bool RIMG = false>
 void launch(GemmArgs& a, hipStream_t st)
 {
     constexpr int TA = A_RC ? TILE_R : TILE_N;
@@ -198,8 +265,8 @@ void launch(GemmArgs& a, hipStream_t st)
     const size_t lds = 2 * (size_t)(TA + TB) * 4;
     a.m_tiles = (a.M + BM - 1) / BM;
     a.n_tiles = (a.N + BN - 1) / BN;
-    const int blocks = a.m_tiles * a.n_tiles * a.G;
-    auto kern = gemm_fc_kernel<A_RC, B_RC>;
+    const int blocks = a.m_tiles * a.n_tiles * a.Z * a.nsplit;
+    auto kern = gemm_fc_kernel<A_RC, B_RC, RIMG>;
     static const bool attr = hipFuncSetAttribute((const void*)kern,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  160 * 1024) == hipSuccess;
@@ -235,7 +302,8 @@ void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, f
     const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
     GemmArgs a{};
     a.A = x; a.B = w; a.bias = bias; a.C = y;
-    a.M = s.N; a.N = s.Kg; a.R = D; a.G = s.G;
+    a.M = s.N; a.N = s.Kg; a.R = D; a.Z = s.G;
+    plain(a);
     a.a_ld = Dt; a.b_ld = D; a.c_ld = s.K;
     a.a_gs = D; a.b_gs = (int64_t)s.Kg * D; a.c_gs = s.Kg; a.bias_gs = s.Kg;
     a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * Dt + D) * 4);
@@ -249,7 +317,8 @@ void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hip
     const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
     GemmArgs a{};
     a.A = dy; a.B = w; a.bias = nullptr; a.C = dx;
-    a.M = s.N; a.N = D; a.R = s.Kg; a.G = s.G;
+    a.M = s.N; a.N = D; a.R = s.Kg; a.Z = s.G;
+    plain(a);
     a.a_ld = s.K; a.b_ld = D; a.c_ld = Dt;
     a.a_gs = s.Kg; a.b_gs = (int64_t)s.Kg * D; a.c_gs = D; a.bias_gs = 0;
     a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.K + s.Kg) * 4);
@@ -263,12 +332,122 @@ void fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, h
     const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
     GemmArgs a{};
     a.A = dy; a.B = x; a.bias = nullptr; a.C = dw;
-    a.M = s.Kg; a.N = D; a.R = s.N; a.G = s.G;
+    a.M = s.Kg; a.N = D; a.R = s.N; a.Z = s.G;
+    plain(a);
     a.a_ld = s.K; a.b_ld = Dt; a.c_ld = D;
     a.a_gs = s.Kg; a.b_gs = D; a.c_gs = (int64_t)s.Kg * D; a.bias_gs = 0;
     a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.K + s.Kg) * 4);
     a.b_bytes = (uint32_t)(((int64_t)(s.N - 1) * Dt + D) * 4);
     launch<false, false>(a, st);
+}
+
+// ---- pointwise (1x1, stride 1, no padding) ------------------------------------
+// Per image n and group g, with P = H*W and the planes as matrices:
+//     forward     Y[n,g]  (Kg x P) = W[g] (Kg x Cg) * X[n,g] (Cg x P) + b
+//     gradInput   dX[n,g] (Cg x P) = W[g]^T * dY[n,g] (Kg x P)
+//     gradWeight  dW[g]   (Kg x Cg) = sum_n dY[n,g] * X[n,g]^T
+// The first two are N*G GEMMs that share the weight block of their group; the
+// third reduces over every image and pixel, split over workgroup slices whose
+// partials are added in slice order.
+
+bool pointwise_supported(const Shape& s)
+{
+    if (!(s.kh == 1 && s.kw == 1 && s.sh == 1 && s.sw == 1 && s.ph == 0 && s.pw == 0)) return false;
+    if (s.N < 1) return false;
+    const int64_t P = (int64_t)s.H * s.W;
+    if (P * s.N >= (int64_t(1) << 31) || s.x_elems >= (int64_t(1) << 31) || s.y_elems >= (int64_t(1) << 31))
+        return false;
+    // gradWeight addresses a group's planes across all images from one resource.
+    return extent_ok(s.N, (int64_t)s.C * P, (int64_t)s.Cg * P) &&
+           extent_ok(s.N, (int64_t)s.K * P, (int64_t)s.Kg * P) && extent_ok(s.Kg, s.Cg, s.Cg);
+}
+
+// Reduction slices of the gradWeight GEMM: about 512 workgroups, each slice at
+// least 8 stages deep, a multiple of the stage depth.
+static void pointwise_split(const Shape& s, int* nsplit, int* r_split)
+{
+    const int64_t R = (int64_t)s.N * s.H * s.W;
+    const int64_t tiles = (int64_t)((s.Kg + BM - 1) / BM) * ((s.Cg + BN - 1) / BN) * s.G;
+    int64_t want = std::max<int64_t>(1, (512 + tiles - 1) / tiles);
+    want = std::min<int64_t>(want, std::max<int64_t>(1, R / (8 * BR)));
+    int64_t rs = (R + want - 1) / want;
+    rs = (rs + BR - 1) / BR * BR;
+    *r_split = (int)rs;
+    *nsplit = (int)((R + rs - 1) / rs);
+}
+
+size_t pointwise_bwd_filter_workspace(const Shape& s)
+{
+    int nsplit, r_split;
+    pointwise_split(s, &nsplit, &r_split);
+    return nsplit > 1 ? (size_t)nsplit * (size_t)s.w_elems * 4 : 0;
+}
+
+// y[n, g*Kg + k, p] = sum_c w[g*Kg + k, c] * x[n, g*Cg + c, p] + b[g*Kg + k]
+void pointwise_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                   hipStream_t st)
+{
+    const int P = s.H * s.W;
+    GemmArgs a{};
+    a.A = w; a.B = x; a.bias = bias; a.C = y;
+    a.M = s.Kg; a.N = P; a.R = s.Cg; a.Z = s.N * s.G;
+    plain(a);
+    a.a_mod = s.G; a.bias_mod = s.G;
+    a.a_ld = s.Cg; a.b_ld = P; a.c_ld = P;
+    a.a_gs = (int64_t)s.Kg * s.Cg; a.b_gs = (int64_t)s.Cg * P; a.c_gs = (int64_t)s.Kg * P;
+    a.bias_gs = s.Kg; a.bias_rows = 1;
+    a.a_bytes = (uint32_t)((int64_t)s.Kg * s.Cg * 4);
+    a.b_bytes = (uint32_t)((int64_t)s.Cg * P * 4);
+    launch<true, false>(a, st);
+}
+
+// dx[n, g*Cg + c, p] = sum_k w[g*Kg + k, c] * dy[n, g*Kg + k, p]
+void pointwise_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    const int P = s.H * s.W;
+    GemmArgs a{};
+    a.A = w; a.B = dy; a.bias = nullptr; a.C = dx;
+    a.M = s.Cg; a.N = P; a.R = s.Kg; a.Z = s.N * s.G;
+    plain(a);
+    a.a_mod = s.G;
+    a.a_ld = s.Cg; a.b_ld = P; a.c_ld = P;
+    a.a_gs = (int64_t)s.Kg * s.Cg; a.b_gs = (int64_t)s.Kg * P; a.c_gs = (int64_t)s.Cg * P;
+    a.a_bytes = (uint32_t)((int64_t)s.Kg * s.Cg * 4);
+    a.b_bytes = (uint32_t)((int64_t)s.Kg * P * 4);
+    launch<false, false>(a, st);
+}
+
+// dw[g*Kg + k, c] = sum_{n, p} dy[n, g*Kg + k, p] * x[n, g*Cg + c, p]
+bool pointwise_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+                          hipStream_t st)
+{
+    const int P = s.H * s.W;
+    int nsplit, r_split;
+    pointwise_split(s, &nsplit, &r_split);
+    if (nsplit > 1 && !ws) return false;
+    GemmArgs a{};
+    a.A = dy; a.B = x; a.bias = nullptr; a.C = nsplit > 1 ? ws : dw;
+    a.M = s.Kg; a.N = s.Cg; a.R = s.N * P; a.Z = s.G;
+    plain(a);
+    a.a_ld = P; a.b_ld = P; a.c_ld = s.Cg;
+    a.a_gs = (int64_t)s.Kg * P; a.b_gs = (int64_t)s.Cg * P; a.c_gs = (int64_t)s.Kg * s.Cg;
+    a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.K * P + (int64_t)s.Kg * P) * 4);
+    a.b_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.C * P + (int64_t)s.Cg * P) * 4);
+    a.r_img = P;
+    a.div_rimg = make_fastdiv((uint32_t)P);
+    a.a_is = (int64_t)s.K * P;
+    a.b_is = (int64_t)s.C * P;
+    a.nsplit = nsplit;
+    a.r_split = r_split;
+    a.c_split = s.w_elems;
+    launch<true, true, true>(a, st);
+    if (nsplit > 1) {
+        const int64_t E = s.w_elems;
+        const int64_t per = (E & 3) == 0 ? E / 4 : E;
+        const int blocks = (int)std::min<int64_t>(2048, std::max<int64_t>(1, (per + 255) / 256));
+        hipLaunchKernelGGL(gemm_split_reduce, dim3(blocks), dim3(256), 0, st, ws, dw, E, nsplit);
+    }
+    return true;
 }
 
 }  // namespace gconv

@@ -94,7 +94,9 @@ typedef enum gconv_path {
     GCONV_PATH_DIRECT = 1,     /* general direct kernels: any valid descriptor */
     GCONV_PATH_SMALLGROUP = 2, /* few channels per group: HBM-bound 4x4x1-MFMA kernels */
     GCONV_PATH_IGEMM = 3,      /* fp32-MFMA implicit GEMM, groups in the grid */
-    GCONV_PATH_FC = 4          /* kernel == input: plain fp32-MFMA GEMM */
+    GCONV_PATH_FC = 4,         /* kernel == input: plain fp32-MFMA GEMM */
+    GCONV_PATH_POINTWISE = 5   /* 1x1, stride 1, no padding: one fp32-MFMA GEMM per
+                                  (image, group), gradWeight split over images */
 } gconv_path;
 
 /* Output extent of the descriptor (the floor rule above). */

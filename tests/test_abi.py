@@ -138,3 +138,23 @@ def test_status_strings():
     for s in range(8):
         assert lib.gconv_status_string(s).decode()
     assert B.version() >= 100
+
+
+def test_pointwise_routing():
+    """1x1 filters at stride 1 without padding go to the pointwise GEMM path
+    (all three conv ops; a 1x1 input stays on the fully-connected path), and
+    its gradWeight reports the workspace of its split reduction."""
+    for groups in (1, 4):
+        desc = B.make_desc(8, 64, 14, 14, 32, 1, 1, groups=groups)
+        for op in (B.OP_FWD, B.OP_BWD_DATA, B.OP_BWD_FILTER):
+            assert B.gconv_select_path(desc, op) == B.PATH_POINTWISE
+        assert B.gconv_workspace_size(desc, B.OP_BWD_FILTER) % (32 * 64 // groups * 4) == 0
+    assert B.gconv_select_path(B.make_desc(8, 64, 1, 1, 32, 1, 1), B.OP_FWD) == B.PATH_FC
+    # stride 2 or padding leave the pointwise path
+    assert B.gconv_select_path(B.make_desc(8, 64, 14, 14, 32, 1, 1, stride=2), B.OP_FWD) != B.PATH_POINTWISE
+    assert B.gconv_select_path(B.make_desc(8, 64, 14, 14, 32, 1, 1, padding=1), B.OP_FWD) != B.PATH_POINTWISE
+    try:
+        B.gconv_set_path_override(B.PATH_POINTWISE)
+        assert B.gconv_select_path(desc, B.OP_FWD) == B.PATH_POINTWISE
+    finally:
+        B.gconv_set_path_override(B.PATH_AUTO)

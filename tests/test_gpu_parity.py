@@ -23,7 +23,7 @@ if not torch.cuda.is_available():
 
 import grouped_convolution_amd as G  # noqa: E402
 
-ALL_PATHS = [G.PATH_DIRECT, G.PATH_SMALLGROUP, G.PATH_IGEMM, G.PATH_FC]
+ALL_PATHS = [G.PATH_DIRECT, G.PATH_SMALLGROUP, G.PATH_IGEMM, G.PATH_FC, G.PATH_POINTWISE]
 
 
 @pytest.fixture(autouse=True)
@@ -200,6 +200,60 @@ def test_fc_mode_random(seed):
     assert fc_ran == 8
 
 
+@pytest.mark.parametrize("seed", range(2))
+def test_random_descriptors_pointwise_family(seed):
+    """1x1 filters at stride 1 without padding, the pointwise GEMM path: planes
+    of any size (not a multiple of 4 or of the 128-wide tile), channel counts
+    on both sides of the tile edges, groups, and gradWeight reductions split
+    over several slices or not at all."""
+    rng = np.random.default_rng(160 + seed)
+    pw_ran = 0
+    for _ in range(6):
+        G_ = int(rng.choice([1, 1, 2, 3]))
+        d = dict(N=int(rng.integers(1, 5)), C=G_ * int(rng.integers(1, 150)),
+                 K=G_ * int(rng.integers(1, 150)), H=int(rng.integers(2, 24)),
+                 W=int(rng.integers(1, 24)), kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1,
+                 G=G_)
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 1600 + seed)
+        dy = draw(("normal", 1.0), (d["N"], d["K"], d["H"], d["W"]), 1610 + seed)
+        ref = oracle_all(x, w, b, dy, kw)
+        desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], 1, 1, groups=G_)
+        assert G.gconv_select_path(desc, G.OP_FWD) == G.PATH_POINTWISE, d
+        for path in [G.PATH_AUTO, G.PATH_POINTWISE]:
+            say("pointwise desc %s path %s" % (d, G.PATH_NAMES[path]))
+            done = compare_full("%s %s" % (G.PATH_NAMES[path], d), run_path(path, x, w, b, dy, kw),
+                                ref)
+            pw_ran += path == G.PATH_POINTWISE and len(done) == 4
+    assert pw_ran == 6
+
+
+@pytest.mark.parametrize("groups", [1, 2])
+def test_pointwise_integer_probe_exact(groups):
+    """Integer data in [-3, 3] on a ResNeXt-sized 1x1 layer (256 -> 128 channels,
+    56x56, 4 images): every partial sum is an exact fp32 integer, so the
+    pointwise path equals the oracle bit for bit, split reduction included."""
+    d = dict(N=4, C=256, K=128, H=56, W=56, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1,
+             G=groups)
+    kw = conv_kwargs(d)
+    x = draw(("int", -3, 3), (4, 256, 56, 56), 21)
+    w = draw(("int", -3, 3), (128, 256 // groups, 1, 1), 22)
+    b = draw(("int", -3, 3), (128,), 23)
+    dy = draw(("int", -3, 3), (4, 128, 56, 56), 24)
+    desc = G.make_desc(4, 256, 56, 56, 128, 1, 1, groups=groups)
+    for op in (G.OP_FWD, G.OP_BWD_DATA, G.OP_BWD_FILTER):
+        assert G.gconv_select_path(desc, op) == G.PATH_POINTWISE
+    assert G.gconv_workspace_size(desc, G.OP_BWD_FILTER) > 0   # split reduction
+    say("pointwise integer probe groups %d" % groups)
+    y, dx, dw, db = gpu_all_ops(x, w, b, dy, **kw)
+    iy = sample_indices(y.numel(), 256, 31)
+    ix = sample_indices(dx.numel(), 256, 32)
+    assert np.array_equal(gather(y, iy), oracle.fwd(x, w, b, idx=iy, **kw)[0])
+    assert np.array_equal(gather(dx, ix), oracle.bwd_data(dy, w, x.shape, idx=ix, **kw)[0])
+    assert np.array_equal(dw.cpu().numpy().astype(np.float64),
+                          oracle.bwd_filter(x, dy, w.shape, **kw)[0])
+
+
 def test_fc_1x1_on_1x1_is_linear():
     """A 1x1 convolution of a 1x1 input (the Linear(128, 32) case of the
     cudnn.torch issue) runs the GEMM path and matches the oracle."""
@@ -325,6 +379,20 @@ EDGE_CASES = [
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     (dict(N=1, C=4, K=4, H=6, W=30, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=1),
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # row-per-DMA small-group kernels over many (image, group) planes: 13 rows
+    # make one band of each plane ragged, and gradWeight runs hold two images
+    (dict(N=37, C=128, K=128, H=13, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=32),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # ... the widest tile with pad 2 (60 + 2 columns), 3 in / 7 out channels
+    # per group (two output quads, the second partial)
+    (dict(N=3, C=2 * 3, K=2 * 7, H=9, W=60, kh=3, kw=3, sh=1, sw=1, ph=1, pw=2, dh=1, dw=1, G=2),
+     {"fwd": "smallgroup", "bwd_data": "direct", "bwd_filter": "direct"}),
+    # ... gradInput with 3 in / 6 out channels per group
+    (dict(N=2, C=2 * 6, K=2 * 3, H=7, W=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2),
+     {"bwd_data": "smallgroup"}),
+    # ... one input channel, three outputs, no padding
+    (dict(N=2, C=1, K=3, H=6, W=8, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+     {"fwd": "smallgroup"}),
 ]
 
 
