@@ -221,26 +221,28 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
     }
 }
 
-// Sum of the split partials in slice order: out[e] = sum_s ws[s*E + e].
-__global__ void __launch_bounds__(256) gemm_split_reduce(const float* __restrict__ ws, float* __restrict__ out,
+// Sum of the split partials: out[e] = sum_s ws[s*E + e]. A workgroup owns 16
+// consecutive elements (16 float4 when E % 4 == 0); its 16 thread rows take
+// every 16th slice, and their 16 partial sums are added in a fixed order.
+template <typename V>
+__global__ void __launch_bounds__(256) gemm_split_reduce(const V* __restrict__ ws, V* __restrict__ out,
                                                          int64_t E, int nsplit)
 {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    if ((E & 3) == 0) {
-        const f4* w4 = (const f4*)ws;
-        f4* o4 = (f4*)out;
-        const int64_t E4 = E >> 2;
-        for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < E4; e += stride) {
-            f4 sum = w4[e];
-            for (int sl = 1; sl < nsplit; ++sl) sum += w4[sl * E4 + e];
-            o4[e] = sum;
-        }
-    } else {
-        for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < E; e += stride) {
-            float sum = ws[e];
-            for (int sl = 1; sl < nsplit; ++sl) sum += ws[sl * E + e];
-            out[e] = sum;
-        }
+    __shared__ V part[16][17];
+    const int q = threadIdx.x & 15, sg = threadIdx.x >> 4;
+    const int64_t e = (int64_t)blockIdx.x * 16 + q;
+    V sum{};
+    if (e < E) {
+#pragma unroll 4
+        for (int sl = sg; sl < nsplit; sl += 16) sum += ws[(int64_t)sl * E + e];
+    }
+    part[sg][q] = sum;
+    __syncthreads();
+    if (sg == 0 && e < E) {
+        V t = part[0][q];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) t += part[i][q];
+        out[e] = t;
     }
 }
 
@@ -443,9 +445,13 @@ bool pointwise_bwd_filter(const Shape& s, const float* x, const float* dy, float
     launch<true, true, true>(a, st);
     if (nsplit > 1) {
         const int64_t E = s.w_elems;
-        const int64_t per = (E & 3) == 0 ? E / 4 : E;
-        const int blocks = (int)std::min<int64_t>(2048, std::max<int64_t>(1, (per + 255) / 256));
-        hipLaunchKernelGGL(gemm_split_reduce, dim3(blocks), dim3(256), 0, st, ws, dw, E, nsplit);
+        if ((E & 3) == 0 && ((uintptr_t)dw & 15) == 0) {
+            hipLaunchKernelGGL(gemm_split_reduce<f4>, dim3((unsigned)((E / 4 + 15) / 16)), dim3(256), 0, st,
+                               (const f4*)ws, (f4*)dw, E / 4, nsplit);
+        } else {
+            hipLaunchKernelGGL(gemm_split_reduce<float>, dim3((unsigned)((E + 15) / 16)), dim3(256), 0, st,
+                               (const float*)ws, dw, E, nsplit);
+        }
     }
     return true;
 }

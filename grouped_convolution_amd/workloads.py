@@ -6,7 +6,7 @@ part of the method. Every tensor comes from ``numpy.random.default_rng``
 (PCG64) with seed ``1000*config_index + t``, where t is 0 for x, 1 for w, 2
 for bias and 3 for dy.
 
-The five workloads below carry the shapes and value distributions the pages
+The workloads below carry the shapes and value distributions the pages
 measure or motivate:
   tiny_grouped   the NNlib grouped-conv benchmark shape ("Support groups in
                  DenseConvDims": Float32 input 28x28x100x2, filter 3x3x20x15,
@@ -20,6 +20,11 @@ measure or motivate:
   fc_mode        the kernel==input problem of "SpatialConvolution running in
                  fully-connected mode is very slow, even with R4": 1600 images
                  of 256x6x6 into 4096 planes with a 6x6 kernel.
+  resnext_1x1    the 1x1 (pointwise) 256->128 reduction that precedes the
+                 grouped 3x3 in a resnext50_32x4d block, at the same 56x56
+                 size and batch; post-ReLU input, no bias (the pages treat a
+                 1x1 conv as a per-image GEMM unless its input is 1x1, in the
+                 cudnn.torch fully-connected-mode issue).
 No dataset or trained weight is involved; normals use the second parameter
 as the standard deviation (He/LeCun scales sqrt(2/fan_in), sqrt(1/fan_in)).
 """
@@ -67,8 +72,11 @@ WORKLOADS = {
     "fc_mode": Workload(
         "fc_mode", 5, (1600, 256, 6, 6), (4096, 256, 6, 6), (1600, 4096, 1, 1), 1, 1, 0, 1,
         ("normal", 1.0), ("normal", float(np.sqrt(1.0 / 9216.0))), ("normal", 0.01)),
+    "resnext_1x1": Workload(
+        "resnext_1x1", 6, (64, 256, 56, 56), (128, 256, 1, 1), (64, 128, 56, 56), 1, 1, 0, 1,
+        ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 256.0))), None),
 }
-WORKLOAD_ORDER = ["tiny_grouped", "dense3x3", "alexnet_conv2", "resnext_32x4d", "fc_mode"]
+WORKLOAD_ORDER = ["tiny_grouped", "dense3x3", "alexnet_conv2", "resnext_32x4d", "fc_mode", "resnext_1x1"]
 
 
 def draw(dist, shape, seed) -> np.ndarray:
