@@ -81,22 +81,26 @@ direct_bwd_data_kernel(Shape s, const float* __restrict__ dy, const float* __res
         const int ca = (int)(t % s.C);
         const int64_t n = t / s.C;
         const int g = ca / s.Cg, c = ca % s.Cg;
+        // Taps first: whether window (ho, wo) reads (h, ww) through tap (i, j)
+        // does not depend on the output channel, so the stride tests run once
+        // per tap and the channels of the group are the inner loop.
+        const float* dyn = dy + (n * s.K + (int64_t)g * s.Kg) * P;
+        const float* wgc = w + ((int64_t)g * s.Kg * s.Cg + c) * s.kh * s.kw;
+        const int64_t wk = (int64_t)s.Cg * s.kh * s.kw;  // w stride between output channels
         float acc = 0.f;
-        for (int k = g * s.Kg; k < (g + 1) * s.Kg; ++k) {
-            const float* dyk = dy + (n * s.K + k) * P;
-            const float* wkc = w + ((int64_t)k * s.Cg + c) * s.kh * s.kw;
-            for (int i = 0; i < s.kh; ++i) {
-                const int th = h + s.ph - i * s.dh;
-                if (th < 0 || th % s.sh != 0) continue;
-                const int ho = th / s.sh;
-                if (ho >= s.Ho) continue;
-                for (int j = 0; j < s.kw; ++j) {
-                    const int tw = ww + s.pw - j * s.dw;
-                    if (tw < 0 || tw % s.sw != 0) continue;
-                    const int wo = tw / s.sw;
-                    if (wo >= s.Wo) continue;
-                    acc = fmaf(wkc[i * s.kw + j], dyk[(int64_t)ho * s.Wo + wo], acc);
-                }
+        for (int i = 0; i < s.kh; ++i) {
+            const int th = h + s.ph - i * s.dh;
+            if (th < 0 || th % s.sh != 0) continue;
+            const int ho = th / s.sh;
+            if (ho >= s.Ho) continue;
+            for (int j = 0; j < s.kw; ++j) {
+                const int tw = ww + s.pw - j * s.dw;
+                if (tw < 0 || tw % s.sw != 0) continue;
+                const int wo = tw / s.sw;
+                if (wo >= s.Wo) continue;
+                const float* dp = dyn + (int64_t)ho * s.Wo + wo;
+                const float* wp = wgc + i * s.kw + j;
+                for (int k = 0; k < s.Kg; ++k) acc = fmaf(wp[k * wk], dp[k * P], acc);
             }
         }
         dx[e] = acc;

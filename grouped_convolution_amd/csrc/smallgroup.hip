@@ -539,7 +539,9 @@ int sg_rows(const SgProblem& p, int cinq, int* LW, int* LR)
 
 bool sg_problem_ok(const SgProblem& p)
 {
-    if (!(p.kh == 3 && p.kw == 3)) return false;
+    // 3x3, or 5x5 with at most two input channels per group (depthwise with a
+    // channel multiplier up to 8): the filters of a group sit in registers.
+    if (!((p.kh == 3 && p.kw == 3) || (p.kh == 5 && p.kw == 5 && p.Cin_g <= 2))) return false;
     if (p.Cin_g > 4 || p.Cout_g > 8 || p.N < 1) return false;
     int LW, LR;
     if (sg_rows(p, sg_cinq(p.Cin_g), &LW, &LR) < 1) return false;
@@ -548,10 +550,10 @@ bool sg_problem_ok(const SgProblem& p)
     return true;
 }
 
-template <int CIN, int OQ, bool FLIP>
+template <int KS, int CIN, int OQ, bool FLIP>
 void sg_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
 {
-    hipLaunchKernelGGL((sg_conv_kernel<3, 3, CIN, OQ, FLIP>), dim3(blocks), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((sg_conv_kernel<KS, KS, CIN, OQ, FLIP>), dim3(blocks), dim3(256), lds, st, a);
 }
 
 // The row-per-DMA fast path: 3x3 at unit stride and dilation, padded rows of
@@ -626,14 +628,15 @@ bool sg_run(const SgProblem& p, hipStream_t st)
     a.div_Wout = make_fastdiv((uint32_t)p.Wout);
     const int64_t blocks = (int64_t)p.N * p.G * a.nbands;
     if (blocks >= (1 << 30)) return false;
-    const size_t lds = ((size_t)ceil64(CINq * a.plane) + (size_t)CINq * 9 * 4 * OQ) * 4;
-#define SG_CASE(cin, oq)                                                       \
-    if (CINq == cin && OQ == oq) {                                             \
-        if (p.flip) sg_launch<cin, oq, true>(a, (int)blocks, lds, st);         \
-        else sg_launch<cin, oq, false>(a, (int)blocks, lds, st);               \
-        return true;                                                           \
+    const size_t lds = ((size_t)ceil64(CINq * a.plane) + (size_t)CINq * p.kh * p.kw * 4 * OQ) * 4;
+#define SG_CASE(ks, cin, oq)                                                       \
+    if (p.kh == ks && CINq == cin && OQ == oq) {                                   \
+        if (p.flip) sg_launch<ks, cin, oq, true>(a, (int)blocks, lds, st);         \
+        else sg_launch<ks, cin, oq, false>(a, (int)blocks, lds, st);               \
+        return true;                                                               \
     }
-    SG_CASE(1, 1) SG_CASE(2, 1) SG_CASE(4, 1) SG_CASE(1, 2) SG_CASE(2, 2) SG_CASE(4, 2)
+    SG_CASE(3, 1, 1) SG_CASE(3, 2, 1) SG_CASE(3, 4, 1) SG_CASE(3, 1, 2) SG_CASE(3, 2, 2) SG_CASE(3, 4, 2)
+    SG_CASE(5, 1, 1) SG_CASE(5, 2, 1) SG_CASE(5, 1, 2) SG_CASE(5, 2, 2)
 #undef SG_CASE
     return false;
 }
@@ -675,11 +678,13 @@ int pad8(int v) { return (v + 23) / 32 * 32 + 8; }
 // at most 64 floats; bands of about 16 rows.
 bool sgw_row64_ok(const Shape& s)
 {
-    return s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1 && s.Wo + 2 <= 64;
+    return s.kh == 3 && s.kw == 3 && s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1 && s.Wo + 2 <= 64;
 }
 
 bool sgw_plan(const Shape& s, SgWArgs* out, bool* row64 = nullptr)
 {
+    // 3x3 only: a 5x5 workgroup would hold 25 accumulators per lane and run
+    // at one wave per SIMD, slower than the direct kernel.
     if (!(s.kh == 3 && s.kw == 3)) return false;
     if (s.Cg > 4 || s.Kg > 4 || s.N < 1) return false;
     SgWArgs a{};

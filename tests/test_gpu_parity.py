@@ -393,6 +393,18 @@ EDGE_CASES = [
     # ... one input channel, three outputs, no padding
     (dict(N=2, C=1, K=3, H=6, W=8, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
      {"fwd": "smallgroup"}),
+    # 5x5 small-group forward / gradInput: depthwise with channel multiplier 2 ...
+    (dict(N=2, C=6, K=12, H=13, W=17, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=6),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "direct"}),
+    # ... and two input channels per group at stride 2, unequal padding
+    (dict(N=3, C=4, K=6, H=15, W=11, kh=5, kw=5, sh=2, sw=2, ph=1, pw=2, dh=1, dw=1, G=2),
+     {"fwd": "smallgroup", "bwd_data": "direct", "bwd_filter": "direct"}),
+    # strided gradInput on the direct kernel (taps filtered once per element,
+    # channels of the group innermost): 8 channels per group, stride 2 and 3
+    (dict(N=2, C=16, K=16, H=14, W=13, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
+     {"bwd_data": "direct"}),
+    (dict(N=2, C=6, K=9, H=16, W=17, kh=5, kw=3, sh=3, sw=2, ph=2, pw=0, dh=2, dw=1, G=3),
+     {"bwd_data": "direct"}),
 ]
 
 
