@@ -118,8 +118,12 @@ bool path_supports(int path, const Shape& s, int op)
 }
 
 // Static routing by shape. MFMA implicit GEMM when the per-group contraction
-// is a real dense GEMM (at least 16 output channels per group and a reduction
-// of at least 64); direct kernels otherwise.
+// is a real dense GEMM (at least 8 output channels per group for forward and
+// gradInput, 16 for gradWeight, and a reduction of at least 64); direct
+// kernels otherwise. At 8 channels per group half of each 16-wide MFMA
+// fragment is idle, and the forward and gradInput passes still run at twice
+// the LDS-tiled direct kernels' rate (ResNeXt's 8-per-group stage); the
+// gradWeight kernel there runs at half the direct kernel's rate.
 int choose_path(const Shape& s, int op)
 {
     const int forced = g_path_override.load();
@@ -136,10 +140,10 @@ int choose_path(const Shape& s, int op)
     // A handful of channels per group (ResNeXt-style, depthwise-like): the
     // HBM-bound 4x4x1-MFMA kernels.
     if (path_supports(GCONV_PATH_SMALLGROUP, s, op)) return GCONV_PATH_SMALLGROUP;
-    if (op == GCONV_OP_FWD && s.Kg >= 16 && s.Cg * T >= 64 &&
+    if (op == GCONV_OP_FWD && s.Kg >= 8 && s.Cg * T >= 64 &&
         path_supports(GCONV_PATH_IGEMM, s, op))
         return GCONV_PATH_IGEMM;
-    if (op == GCONV_OP_BWD_DATA && s.Cg >= 16 && s.Kg * T >= 64 &&
+    if (op == GCONV_OP_BWD_DATA && s.Cg >= 8 && s.Kg * T >= 64 &&
         path_supports(GCONV_PATH_IGEMM, s, op))
         return GCONV_PATH_IGEMM;
     if (op == GCONV_OP_BWD_FILTER && s.Cg >= 16 && s.Kg >= 16 &&

@@ -399,6 +399,10 @@ EDGE_CASES = [
     # ... and two input channels per group at stride 2, unequal padding
     (dict(N=3, C=4, K=6, H=15, W=11, kh=5, kw=5, sh=2, sw=2, ph=1, pw=2, dh=1, dw=1, G=2),
      {"fwd": "smallgroup", "bwd_data": "direct", "bwd_filter": "direct"}),
+    # 8 in / 8 out channels per group (ResNeXt's second stage): one 16-wide MFMA
+    # fragment half used on forward and gradInput; gradWeight stays direct
+    (dict(N=2, C=64, K=64, H=20, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8),
+     {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "direct"}),
     # strided gradInput on the direct kernel (taps filtered once per element,
     # channels of the group innermost): 8 channels per group, stride 2 and 3
     (dict(N=2, C=16, K=16, H=14, W=13, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
