@@ -262,6 +262,10 @@ struct ConvFlatArgs {
     int n_otiles;
     int LW, plane, nseg, bufsz; // LDS row width, channel plane, DMA segments per wave, floats per buffer
     int halo;                   // (kh-1)*dh + 1 input rows under one output row
+    // Input upsampling (strided gradInput): Hin x Win is the virtual input, in
+    // which only rows and columns divisible by uh, uw hold values, row h/uh and
+    // column w/uw of the stored Hr x Wr planes; 1, 1 otherwise.
+    int uh, uw, Hr, Wr;
     FastDiv div_P, div_Wout, div_plane, div_LW;
 };
 
@@ -302,7 +306,7 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
         rows1 = hol * a.sh + a.halo;
     }
     const int hA = ho0 * a.sh - a.ph;  // input row of virtual row 0
-    const int HWin = a.Hin * a.Win;
+    const int HWin = a.Hr * a.Wr;
 
     // Per-lane global byte offset of each DMA segment element (chunk-relative:
     // the buffer resource moves with the chunk). Out-of-image taps, rows past
@@ -318,9 +322,15 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
         const bool second = v >= rows0;
         const int h = second ? v - rows0 - a.ph : hA + v;
         const int w = col - a.pw;
-        const bool ok = k < a.nseg && c < CC && v < rows0 + rows1 && (unsigned)h < (unsigned)a.Hin &&
-                        (unsigned)w < (unsigned)a.Win;
-        xoff[k] = ok ? (uint32_t)(((second ? a.Cin_tot : 0) + c) * HWin + h * a.Win + w) * 4u : kOOB;
+        bool ok = k < a.nseg && c < CC && v < rows0 + rows1 && (unsigned)h < (unsigned)a.Hin &&
+                  (unsigned)w < (unsigned)a.Win;
+        int hr = h, wr = w;
+        if (a.uh != 1 || a.uw != 1) {   // upsampled input: the other positions are 0
+            hr = h / a.uh;
+            wr = w / a.uw;
+            ok = ok && hr * a.uh == h && wr * a.uw == w;
+        }
+        xoff[k] = ok ? (uint32_t)(((second ? a.Cin_tot : 0) + c) * HWin + hr * a.Wr + wr) * 4u : kOOB;
     }
 
     // LDS address (floats, buffer-relative) of each pixel fragment at tap 0,
@@ -526,6 +536,7 @@ struct Problem {
     int kh, kw, sh, sw, dh, dw, ph, pw;
     int w_so, w_sr, w_gstride;
     bool flip;
+    int uh = 1, uw = 1, Hr = 0, Wr = 0;  // input upsampling (flat kernel only), stored plane size
 };
 
 int choose_cc(const Problem& p) { return (p.kh * p.kw >= 16) ? 4 : 8; }
@@ -610,17 +621,23 @@ Problem fwd_problem(const Shape& s, const float* x, const float* w, const float*
     const int T = s.kh * s.kw;
     p.w_so = s.Cg * T; p.w_sr = T; p.w_gstride = s.Kg * s.Cg * T;
     p.flip = false;
+    p.Hr = s.H; p.Wr = s.W;
     return p;
 }
 
-// gradInput at stride 1: a forward correlation of dy with the transposed,
-// tap-reversed filter and padding (k-1)*d - p, whose output extent is H x W.
+// gradInput: a forward correlation of dy with the transposed, tap-reversed
+// filter and padding (k-1)*d - p, whose output extent is H x W. At stride s,
+// dy is read as if upsampled by s (its values at multiples of s, zeros
+// between): the adjoint of a strided correlation is the unit-stride
+// correlation of the upsampled dy with the reversed filter.
 Problem bwd_data_problem(const Shape& s, const float* dy, const float* w, float* dx)
 {
     Problem p;
     p.in = dy; p.wgt = w; p.bias = nullptr; p.out = dx;
     p.N = s.N; p.G = s.G;
-    p.Cin_tot = s.K; p.Cin_g = s.Kg; p.Hin = s.Ho; p.Win = s.Wo;
+    p.Cin_tot = s.K; p.Cin_g = s.Kg;
+    p.Hin = (s.Ho - 1) * s.sh + 1; p.Win = (s.Wo - 1) * s.sw + 1;
+    p.uh = s.sh; p.uw = s.sw; p.Hr = s.Ho; p.Wr = s.Wo;
     p.Cout_tot = s.C; p.Cout_g = s.Cg; p.Hout = s.H; p.Wout = s.W;
     p.kh = s.kh; p.kw = s.kw; p.sh = 1; p.sw = 1; p.dh = s.dh; p.dw = s.dw;
     p.ph = (s.kh - 1) * s.dh - s.ph;
@@ -634,7 +651,7 @@ Problem bwd_data_problem(const Shape& s, const float* dy, const float* w, float*
 // ---- flattened-pixel variant: host side --------------------------------------
 
 struct FlatInst {
-    int T, MO, WO, WPX, MP;
+    int T, MO, WO, WPX, MP, NSX;
 };
 #ifndef GCONV_FLAT_MP3
 #define GCONV_FLAT_MP3 5
@@ -643,15 +660,19 @@ struct FlatInst {
 // channels (WO) and across pixels (WPX), pixel fragments per wave (MP). With
 // 64 channels per group, 5 fragments give 1255 tiles of 80 pixels for 32
 // images of 56 x 56, which spread evenly over the 256 CUs.
-#define GCONV_FLAT_INSTS(X)                                                          \
-    X(9, 3, 1, 4, 1, GCONV_FLAT_MP3) X(9, 3, 2, 4, 1, 4) X(9, 3, 1, 3, 1, 5)         \
-    X(9, 3, 1, 2, 2, 4) X(9, 3, 1, 1, 4, 4)                                          \
-    X(25, 5, 1, 4, 1, 4) X(25, 5, 2, 4, 1, 4) X(25, 5, 1, 3, 1, 4)                   \
-    X(25, 5, 1, 2, 2, 4) X(25, 5, 1, 1, 4, 4)
-#define GCONV_FLAT_ENTRY(t, k, mo, wo, wpx, mp) {t, mo, wo, wpx, mp},
+// NSX: DMA segments (of 64 floats) per wave and buffer, at most (one
+// register each). The plan takes the first instance of its shape whose tile
+// fits: the larger-NSX copies serve strided layers, whose tiles span twice
+// the input rows, and wide images.
+#define GCONV_FLAT_INSTS(X)                                                                \
+    X(9, 3, 1, 4, 1, GCONV_FLAT_MP3, 8) X(9, 3, 2, 4, 1, 4, 12) X(9, 3, 1, 3, 1, 5, 8)     \
+    X(9, 3, 1, 2, 2, 4, 8) X(9, 3, 1, 1, 4, 4, 12)                                         \
+    X(25, 5, 1, 4, 1, 4, 8) X(25, 5, 2, 4, 1, 4, 8) X(25, 5, 1, 3, 1, 4, 8)                \
+    X(25, 5, 1, 2, 2, 4, 8) X(25, 5, 1, 1, 4, 4, 12)                                       \
+    X(9, 3, 2, 4, 1, 4, 16) X(9, 3, 1, 1, 4, 4, 24)
+#define GCONV_FLAT_ENTRY(t, k, mo, wo, wpx, mp, nsx) {t, mo, wo, wpx, mp, nsx},
 constexpr FlatInst kFlatInsts[] = {GCONV_FLAT_INSTS(GCONV_FLAT_ENTRY)};
 #undef GCONV_FLAT_ENTRY
-constexpr int kFlatNSX = 8;  // DMA segments (of 64 floats) per wave and buffer, at most
 
 struct FlatPlan {
     FlatInst inst;
@@ -668,24 +689,30 @@ bool flat_plan(const Problem& p, FlatPlan& fp)
     const int mo = nfrag > 4 ? 2 : 1;
     const int wo = nfrag > 4 ? 4 : nfrag;  // waves across output channels
     const FlatInst* inst = nullptr;
-    for (const FlatInst& fi : kFlatInsts)
-        if (fi.T == T && fi.MO == mo && fi.WO == wo) inst = &fi;
+    int64_t plane = 0, nseg = 0, LW = 0, P = (int64_t)p.Hout * p.Wout;
+    for (const FlatInst& fi : kFlatInsts) {
+        if (!(fi.T == T && fi.MO == mo && fi.WO == wo)) continue;
+        const int NWi = fi.WO * fi.WPX;
+        const int BPXi = fi.WPX * fi.MP * 16;
+        if (P < BPXi) continue;  // a tile must span at most two images
+        const int halo = (p.kh - 1) * p.dh + 1;
+        const int R = (int)std::min<int64_t>(p.Hout, (BPXi - 1) / p.Wout + 2);  // output rows per tile
+        const int LR = std::max((R - 1) * p.sh + halo, (R - 2) * p.sh + 2 * halo);
+        LW = (int64_t)(p.Wout - 1) * p.sw + (p.kw - 1) * p.dw + 1;
+        plane = LR * LW;
+        plane = ((plane + 47) / 64) * 64 + 16;  // == 16 (mod 64): the 4 lane groups hit distinct banks
+        nseg = (4 * plane + 64 * NWi - 1) / (64 * NWi);
+        if (nseg <= fi.NSX) {
+            inst = &fi;
+            break;
+        }
+    }
     if (!inst) return false;
     fp.inst = *inst;
     const int NW = inst->WO * inst->WPX;
     const int BPX = inst->WPX * inst->MP * 16;
-    const int64_t P = (int64_t)p.Hout * p.Wout;
-    if (P < BPX) return false;  // a tile must span at most two images
     const int64_t NP = (int64_t)p.N * P;
     if (NP + BPX >= (int64_t(1) << 31)) return false;
-    const int halo = (p.kh - 1) * p.dh + 1;
-    const int R = (int)std::min<int64_t>(p.Hout, (BPX - 1) / p.Wout + 2);  // output rows per tile
-    const int LR = std::max((R - 1) * p.sh + halo, (R - 2) * p.sh + 2 * halo);
-    const int64_t LW = (int64_t)(p.Wout - 1) * p.sw + (p.kw - 1) * p.dw + 1;
-    int64_t plane = LR * LW;
-    plane = ((plane + 47) / 64) * 64 + 16;  // == 16 (mod 64): the 4 lane groups hit distinct banks
-    const int64_t nseg = (4 * plane + 64 * NW - 1) / (64 * NW);
-    if (nseg > kFlatNSX) return false;
     fp.LW = (int)LW;
     fp.plane = (int)plane;
     fp.nseg = (int)nseg;
@@ -693,7 +720,7 @@ bool flat_plan(const Problem& p, FlatPlan& fp)
     fp.lds_bytes = (size_t)2 * fp.bufsz * 4;
     // Buffer resources: two images' worth of one group's planes, and one
     // group's weights, addressed in bytes below 2^31.
-    if ((int64_t)(p.Cin_tot + p.Cin_g) * p.Hin * p.Win * 4 >= (int64_t(1) << 31)) return false;
+    if ((int64_t)(p.Cin_tot + p.Cin_g) * p.Hr * p.Wr * 4 >= (int64_t(1) << 31)) return false;
     if ((int64_t)p.w_gstride * 4 >= (int64_t(1) << 31)) return false;
     const int BO = inst->WO * inst->MO * 16;
     const int64_t blocks = ((NP + BPX - 1) / BPX) * p.G * ((p.Cout_g + BO - 1) / BO);
@@ -702,11 +729,11 @@ bool flat_plan(const Problem& p, FlatPlan& fp)
     return true;
 }
 
-template <int KH, int KW, int MP, int MO, int WO, int WPX, bool FLIP>
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP>
 void launch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     constexpr int MINW = (KH * KW <= 9) ? 4 : 2;
-    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, kFlatNSX, FLIP, MINW>;
+    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW>;
     hipLaunchKernelGGL(kern, dim3(fp.blocks), dim3(64 * WO * WPX), fp.lds_bytes, st, a);
 }
 
@@ -714,9 +741,9 @@ template <bool FLIP>
 bool dispatch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     const FlatInst& i = fp.inst;
-#define GCONV_FLAT_CASE(t, k, mo, wo, wpx, mp)                                          \
-    if (i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp) {          \
-        launch_flat<k, k, mp, mo, wo, wpx, FLIP>(a, fp, st);                            \
+#define GCONV_FLAT_CASE(t, k, mo, wo, wpx, mp, nsx)                                     \
+    if (i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
+        launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP>(a, fp, st);                       \
         return true;                                                                   \
     }
     GCONV_FLAT_INSTS(GCONV_FLAT_CASE)
@@ -741,6 +768,7 @@ bool run_flat(const Problem& p, hipStream_t st)
     a.n_otiles = (p.Cout_g + BO - 1) / BO;
     a.LW = fp.LW; a.plane = fp.plane; a.nseg = fp.nseg; a.bufsz = fp.bufsz;
     a.halo = (p.kh - 1) * p.dh + 1;
+    a.uh = p.uh; a.uw = p.uw; a.Hr = p.Hr; a.Wr = p.Wr;
     a.div_P = make_fastdiv((uint32_t)a.P);
     a.div_Wout = make_fastdiv((uint32_t)p.Wout);
     a.div_plane = make_fastdiv((uint32_t)fp.plane);
@@ -769,8 +797,8 @@ bool igemm_fwd_supported(const Shape& s)
 
 bool igemm_bwd_data_supported(const Shape& s)
 {
-    if (s.sh != 1 || s.sw != 1) return false;
     const Problem p = bwd_data_problem(s, nullptr, nullptr, nullptr);
+    if (p.uh != 1 || p.uw != 1) return use_flat(p);  // only the flat kernel upsamples
     return use_flat(p) || problem_supported(p);
 }
 
@@ -784,7 +812,9 @@ bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias
 bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
     const Problem p = bwd_data_problem(s, dy, w, dx);
-    return use_flat(p) ? run_flat(p, st) : run_problem(p, st);
+    if (use_flat(p)) return run_flat(p, st);
+    if (p.uh != 1 || p.uw != 1) return false;
+    return run_problem(p, st);
 }
 
 }  // namespace gconv

@@ -404,11 +404,29 @@ EDGE_CASES = [
     (dict(N=2, C=64, K=64, H=20, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8),
      {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "direct"}),
     # strided gradInput on the direct kernel (taps filtered once per element,
-    # channels of the group innermost): 8 channels per group, stride 2 and 3
-    (dict(N=2, C=16, K=16, H=14, W=13, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
+    # channels of the group innermost): 6 channels per group, stride 2; 2 per
+    # group, strides 3 and 2 with dilation
+    (dict(N=2, C=12, K=16, H=14, W=13, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
      {"bwd_data": "direct"}),
     (dict(N=2, C=6, K=9, H=16, W=17, kh=5, kw=3, sh=3, sw=2, ph=2, pw=0, dh=2, dw=1, G=3),
      {"bwd_data": "direct"}),
+    # strided gradInput on the MFMA flat kernel, reading dy as if upsampled by
+    # the stride: 8 channels per group at stride 2 (odd and even sizes) ...
+    (dict(N=2, C=16, K=16, H=18, W=17, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
+     {"bwd_data": "igemm"}),
+    # ... 16 per group at strides 3 x 2 with unequal padding, 18 x 19 outputs ...
+    (dict(N=3, C=2 * 16, K=2 * 24, H=18, W=19, kh=3, kw=3, sh=3, sw=2, ph=1, pw=0, dh=1, dw=1,
+          G=2), {"bwd_data": "igemm"}),
+    # ... and 5x5 at stride 2
+    (dict(N=2, C=32, K=32, H=21, W=20, kh=5, kw=5, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=1),
+     {"bwd_data": "igemm"}),
+    # strided forward on the flat kernel: 8 per group at stride 2 (a tile spans
+    # 30 input rows: the 24-segment instance) ...
+    (dict(N=2, C=16, K=16, H=40, W=40, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
+     {"fwd": "igemm", "bwd_data": "igemm"}),
+    # ... and 80 outputs (two fragments) on 100-wide rows (the 16-segment one)
+    (dict(N=1, C=80, K=80, H=12, W=100, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),
+     {"fwd": "igemm", "bwd_data": "igemm"}),
 ]
 
 
