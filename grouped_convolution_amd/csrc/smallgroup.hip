@@ -52,6 +52,10 @@ struct SgArgs {
     int w_so, w_sr, w_gstride;
     int R, nbands;              // output rows per workgroup, bands per plane
     int LW, LR, plane;          // LDS input tile: row width, rows, plane floats
+    // Input upsampling (strided gradInput): Hin x Win is the virtual input, in
+    // which only rows and columns divisible by uh, uw hold values, row h/uh and
+    // column w/uw of the stored Hr x Wr planes; 1, 1 otherwise.
+    int uh, uw, Hr, Wr;
     FastDiv div_plane, div_LW, div_Wout;
 };
 
@@ -79,12 +83,13 @@ __global__ void __launch_bounds__(256) sg_conv_kernel(SgArgs a)
     const int rows = min(a.R, a.Hout - ho0);
     const int hbase = ho0 * a.sh - a.ph;
 
-    const float* in_g = a.in + ((size_t)n * a.Cin_tot + (size_t)g * a.Cin_g) * a.Hin * a.Win;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_g, (uint32_t)a.Cin_g * a.Hin * a.Win * 4u);
+    const float* in_g = a.in + ((size_t)n * a.Cin_tot + (size_t)g * a.Cin_g) * a.Hr * a.Wr;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_g, (uint32_t)a.Cin_g * a.Hr * a.Wr * 4u);
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(a.wgt + (size_t)g * a.w_gstride, (uint32_t)a.w_gstride * 4u);
 
     // Input tile: element e = c*plane + r*LW + col, 64 per instruction.
+    const bool up = a.uh != 1 || a.uw != 1;
     for (int i = wave; i < xfloats / 64; i += 4) {
         const int e = i * 64 + lane;
         const int c = (int)fastdiv((uint32_t)e, a.div_plane);
@@ -92,8 +97,14 @@ __global__ void __launch_bounds__(256) sg_conv_kernel(SgArgs a)
         const int r = (int)fastdiv((uint32_t)rem, a.div_LW);
         const int w = rem - r * a.LW - a.pw;
         const int h = hbase + r;
-        const bool ok = c < CIN && (unsigned)h < (unsigned)a.Hin && (unsigned)w < (unsigned)a.Win;
-        load_lds64(rx, lds + i * 64, ok ? (uint32_t)((c * a.Hin + h) * a.Win + w) * 4u : kOOB);
+        bool ok = c < CIN && (unsigned)h < (unsigned)a.Hin && (unsigned)w < (unsigned)a.Win;
+        int hr = h, wr = w;
+        if (up) {   // upsampled input: the other positions are 0
+            hr = h / a.uh;
+            wr = w / a.uw;
+            ok = ok && hr * a.uh == h && wr * a.uw == w;
+        }
+        load_lds64(rx, lds + i * 64, ok ? (uint32_t)((c * a.Hr + hr) * a.Wr + wr) * 4u : kOOB);
     }
     // Filters -> LDS as [(c*T + t)][o] (zeros past the group's channels).
     for (int e = tid; e < NW; e += 256) {
@@ -516,6 +527,7 @@ struct SgProblem {
     int kh, kw, sh, sw, dh, dw, ph, pw;
     int w_so, w_sr, w_gstride;
     bool flip;
+    int uh = 1, uw = 1, Hr = 0, Wr = 0;  // input upsampling (general kernel only), stored plane size
 };
 
 // LDS tile budget per workgroup (28 KiB): five workgroups share a CU, so the
@@ -545,8 +557,8 @@ bool sg_problem_ok(const SgProblem& p)
     if (p.Cin_g > 4 || p.Cout_g > 8 || p.N < 1) return false;
     int LW, LR;
     if (sg_rows(p, sg_cinq(p.Cin_g), &LW, &LR) < 1) return false;
-    if ((int64_t)(p.Cin_g + 4) * p.Hin * p.Win * 4 >= (int64_t(1) << 30)) return false;
-    if ((int64_t)p.Hout * p.Wout >= (1 << 30)) return false;
+    if ((int64_t)(p.Cin_g + 4) * p.Hr * p.Wr * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)p.Hin * p.Win >= (1 << 30) || (int64_t)p.Hout * p.Wout >= (1 << 30)) return false;
     return true;
 }
 
@@ -562,6 +574,7 @@ void sg_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
 bool sg_row64_ok(const SgProblem& p)
 {
     return p.kh == 3 && p.kw == 3 && p.sh == 1 && p.sw == 1 && p.dh == 1 && p.dw == 1 &&
+           p.uh == 1 && p.uw == 1 &&
            p.Wout + 2 <= 64 && p.ph >= 0 && p.pw >= 0 && p.pw <= 2;
 }
 
@@ -582,6 +595,7 @@ bool sg_run_row64(const SgProblem& p, hipStream_t st)
     a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
     a.sh = 1; a.sw = 1; a.dh = 1; a.dw = 1; a.ph = p.ph; a.pw = p.pw;
     a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
+    a.uh = 1; a.uw = 1; a.Hr = p.Hin; a.Wr = p.Win;
     const int nb = (p.Hout + 15) / 16;
     a.R = (p.Hout + nb - 1) / nb;
     a.nbands = (p.Hout + a.R - 1) / a.R;
@@ -620,6 +634,7 @@ bool sg_run(const SgProblem& p, hipStream_t st)
     a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
     a.sh = p.sh; a.sw = p.sw; a.dh = p.dh; a.dw = p.dw; a.ph = p.ph; a.pw = p.pw;
     a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
+    a.uh = p.uh; a.uw = p.uw; a.Hr = p.Hr; a.Wr = p.Wr;
     a.R = sg_rows(p, CINq, &a.LW, &a.LR);
     a.nbands = (p.Hout + a.R - 1) / a.R;
     a.plane = a.LR * a.LW;
@@ -652,6 +667,7 @@ SgProblem sg_fwd_problem(const Shape& s, const float* x, const float* w, const f
     const int T = s.kh * s.kw;
     p.w_so = s.Cg * T; p.w_sr = T; p.w_gstride = s.Kg * s.Cg * T;
     p.flip = false;
+    p.Hr = s.H; p.Wr = s.W;
     return p;
 }
 
@@ -659,7 +675,12 @@ SgProblem sg_bwd_data_problem(const Shape& s, const float* dy, const float* w, f
 {
     SgProblem p;
     p.in = dy; p.wgt = w; p.bias = nullptr; p.out = dx;
-    p.N = s.N; p.G = s.G; p.Cin_tot = s.K; p.Cin_g = s.Kg; p.Hin = s.Ho; p.Win = s.Wo;
+    p.N = s.N; p.G = s.G; p.Cin_tot = s.K; p.Cin_g = s.Kg;
+    // At stride s, dy is read as if upsampled by s (zeros between its values):
+    // the adjoint of a strided correlation is the unit-stride correlation of
+    // the upsampled dy with the tap-reversed filter.
+    p.Hin = (s.Ho - 1) * s.sh + 1; p.Win = (s.Wo - 1) * s.sw + 1;
+    p.uh = s.sh; p.uw = s.sw; p.Hr = s.Ho; p.Wr = s.Wo;
     p.Cout_tot = s.C; p.Cout_g = s.Cg; p.Hout = s.H; p.Wout = s.W;
     p.kh = s.kh; p.kw = s.kw; p.sh = 1; p.sw = 1; p.dh = s.dh; p.dw = s.dw;
     p.ph = (s.kh - 1) * s.dh - s.ph;
@@ -745,7 +766,6 @@ bool smallgroup_fwd_supported(const Shape& s)
 
 bool smallgroup_bwd_data_supported(const Shape& s)
 {
-    if (s.sh != 1 || s.sw != 1) return false;
     return sg_problem_ok(sg_bwd_data_problem(s, nullptr, nullptr, nullptr));
 }
 

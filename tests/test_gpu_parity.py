@@ -420,6 +420,13 @@ EDGE_CASES = [
     # ... and 5x5 at stride 2
     (dict(N=2, C=32, K=32, H=21, W=20, kh=5, kw=5, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=1),
      {"bwd_data": "igemm"}),
+    # strided gradInput on the small-group kernels (dy read as if upsampled):
+    # depthwise 3x3 at stride 2, odd and even sizes ...
+    (dict(N=2, C=8, K=8, H=15, W=14, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup"}),
+    # ... and 4 in / 2 out channels (gradInput's view) at stride 2, dilation 2
+    (dict(N=2, C=4, K=8, H=17, W=19, kh=3, kw=3, sh=2, sw=2, ph=2, pw=2, dh=2, dw=2, G=2),
+     {"bwd_data": "smallgroup"}),
     # strided forward on the flat kernel: 8 per group at stride 2 (a tile spans
     # 30 input rows: the 24-segment instance) ...
     (dict(N=2, C=16, K=16, H=40, W=40, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
