@@ -187,18 +187,21 @@ TileArgs bwd_data_args(const Shape& s, const float* dy, const float* w, float* d
     return a;
 }
 
-// gradWeight for 3x3 filters with at most KG output channels per group: one
-// block per (group, input channel) computes dw[g*Kg + k][c][tap] for all k and
-// taps. Threads stride over the N*Ho*Wo pixels, each keeping KG x 9 sums;
-// the block then adds them in a fixed order (a butterfly within each wave,
-// then the four waves in index order). One kernel, no workspace.
-template <int KG>
-__global__ void __launch_bounds__(256) direct_wgrad3x3_kernel(Shape s, const float* __restrict__ x,
-                                                              const float* __restrict__ dy,
-                                                              float* __restrict__ dw)
+// gradWeight for 3x3 and 5x5 filters with at most KG output channels per group:
+// one block per (group, input channel) computes dw[g*Kg + k][c][tap] for all k
+// and taps. Threads stride over the N*Ho*Wo pixels, each keeping KG x KS*KS
+// sums; the block then adds them in a fixed order (a butterfly within each
+// wave, then the waves in index order). One kernel, no workspace. Large
+// reductions take 1024-thread blocks, so each CU keeps enough loads in flight
+// although there is one block per (group, input channel).
+template <int KG, int KS, int NT>
+__global__ void __launch_bounds__(NT) direct_wgrad_kernel(Shape s, const float* __restrict__ x,
+                                                          const float* __restrict__ dy,
+                                                          float* __restrict__ dw)
 {
-    constexpr int T = 9;
-    __shared__ float red[4][KG * T];
+    constexpr int T = KS * KS;
+    constexpr int NWV = NT / 64;
+    __shared__ float red[NWV][KG * T];
     const int g = blockIdx.x / s.Cg, c = blockIdx.x - (blockIdx.x / s.Cg) * s.Cg;
     const int P = s.Ho * s.Wo;
     const int total = s.N * P;
@@ -206,7 +209,7 @@ __global__ void __launch_bounds__(256) direct_wgrad3x3_kernel(Shape s, const flo
     float acc[KG * T];
 #pragma unroll
     for (int e = 0; e < KG * T; ++e) acc[e] = 0.f;
-    for (int e = threadIdx.x; e < total; e += 256) {
+    for (int e = threadIdx.x; e < total; e += NT) {
         const int n = e / P, p = e - (e / P) * P;
         const int ho = p / s.Wo, wo = p - (p / s.Wo) * s.Wo;
         const float* dyp = dy + ((size_t)n * s.K + (size_t)g * s.Kg) * P + p;
@@ -215,15 +218,16 @@ __global__ void __launch_bounds__(256) direct_wgrad3x3_kernel(Shape s, const flo
         for (int k = 0; k < KG; ++k) dv[k] = k < s.Kg ? dyp[(size_t)k * P] : 0.f;
         const float* xc = x + ((size_t)n * s.C + (size_t)g * s.Cg + c) * HW;
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
+        for (int i = 0; i < KS; ++i) {
             const int h = ho * s.sh - s.ph + i * s.dh;
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
+            for (int j = 0; j < KS; ++j) {
                 const int w = wo * s.sw - s.pw + j * s.dw;
                 const bool ok = (unsigned)h < (unsigned)s.H && (unsigned)w < (unsigned)s.W;
                 const float xv = ok ? xc[(size_t)h * s.W + w] : 0.f;
 #pragma unroll
-                for (int k = 0; k < KG; ++k) acc[k * T + i * 3 + j] = fmaf(dv[k], xv, acc[k * T + i * 3 + j]);
+                for (int k = 0; k < KG; ++k)
+                    acc[k * T + i * KS + j] = fmaf(dv[k], xv, acc[k * T + i * KS + j]);
             }
         }
     }
@@ -235,11 +239,20 @@ __global__ void __launch_bounds__(256) direct_wgrad3x3_kernel(Shape s, const flo
         if (lane == 0) red[wave][e] = v;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < s.Kg * T; e += 256) {
+    for (int e = threadIdx.x; e < s.Kg * T; e += NT) {
         const int k = e / T, t = e - (e / T) * T;
-        dw[(((size_t)g * s.Kg + k) * s.Cg + c) * T + t] =
-            ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+        float sum = red[0][e];
+        for (int wv = 1; wv < NWV; ++wv) sum += red[wv][e];
+        dw[(((size_t)g * s.Kg + k) * s.Cg + c) * T + t] = sum;
     }
+}
+
+template <int KG, int KS>
+void launch_wgrad(const Shape& s, const float* x, const float* dy, float* dw, int blocks, bool big,
+                  hipStream_t st)
+{
+    if (big) hipLaunchKernelGGL((direct_wgrad_kernel<KG, KS, 1024>), dim3(blocks), dim3(1024), 0, st, s, x, dy, dw);
+    else hipLaunchKernelGGL((direct_wgrad_kernel<KG, KS, 256>), dim3(blocks), dim3(256), 0, st, s, x, dy, dw);
 }
 
 }  // namespace
@@ -263,14 +276,24 @@ bool direct_tile_bwd_data(const Shape& s, const float* dy, const float* w, float
 bool direct_tile_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
                             hipStream_t st)
 {
-    if (s.kh != 3 || s.kw != 3 || s.Kg > 8 || s.N < 1) return false;
+    const bool k3 = s.kh == 3 && s.kw == 3, k5 = s.kh == 5 && s.kw == 5;
+    if (!(k3 || k5) || s.Kg > (k3 ? 8 : 4) || s.N < 1) return false;
     if ((int64_t)s.N * s.Ho * s.Wo >= (int64_t(1) << 31) || (int64_t)s.G * s.Cg >= (1 << 30))
         return false;
     const int blocks = s.G * s.Cg;
-    if (s.Kg <= 4)
-        hipLaunchKernelGGL(direct_wgrad3x3_kernel<4>, dim3(blocks), dim3(256), 0, st, s, x, dy, dw);
-    else
-        hipLaunchKernelGGL(direct_wgrad3x3_kernel<8>, dim3(blocks), dim3(256), 0, st, s, x, dy, dw);
+    const int kg = s.Kg <= 1 ? 1 : s.Kg <= 2 ? 2 : s.Kg <= 4 ? 4 : 8;
+    // 1024 threads cap a lane at 128 registers: 5x5 with 4 outputs keeps 256.
+    const bool big = (int64_t)s.N * s.Ho * s.Wo >= 16384 && !(k5 && kg == 4);
+    if (k3) {
+        if (kg == 1) launch_wgrad<1, 3>(s, x, dy, dw, blocks, big, st);
+        else if (kg == 2) launch_wgrad<2, 3>(s, x, dy, dw, blocks, big, st);
+        else if (kg == 4) launch_wgrad<4, 3>(s, x, dy, dw, blocks, big, st);
+        else launch_wgrad<8, 3>(s, x, dy, dw, blocks, big, st);
+    } else {
+        if (kg == 1) launch_wgrad<1, 5>(s, x, dy, dw, blocks, big, st);
+        else if (kg == 2) launch_wgrad<2, 5>(s, x, dy, dw, blocks, big, st);
+        else launch_wgrad<4, 5>(s, x, dy, dw, blocks, big, st);
+    }
     return true;
 }
 

@@ -427,6 +427,12 @@ EDGE_CASES = [
     # ... and 4 in / 2 out channels (gradInput's view) at stride 2, dilation 2
     (dict(N=2, C=4, K=8, H=17, W=19, kh=3, kw=3, sh=2, sw=2, ph=2, pw=2, dh=2, dw=2, G=2),
      {"bwd_data": "smallgroup"}),
+    # direct gradWeight with 1024-thread blocks (at least 16K pixels): depthwise
+    # 5x5, and 8 per group at stride 2
+    (dict(N=4, C=8, K=8, H=64, W=64, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=8),
+     {"bwd_filter": "direct"}),
+    (dict(N=8, C=16, K=16, H=96, W=96, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
+     {"bwd_filter": "direct"}),
     # strided forward on the flat kernel: 8 per group at stride 2 (a tile spans
     # 30 input rows: the 24-segment instance) ...
     (dict(N=2, C=16, K=16, H=40, W=40, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
