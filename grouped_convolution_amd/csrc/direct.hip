@@ -171,9 +171,12 @@ void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
                        dy, w, dx);
 }
 
-void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st)
+size_t direct_bwd_filter_workspace(const Shape& s) { return direct_tile_bwd_filter_workspace(s); }
+
+void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+                       hipStream_t st)
 {
-    if (direct_tile_bwd_filter(s, x, dy, dw, st)) return;
+    if (direct_tile_bwd_filter(s, x, dy, dw, ws, st)) return;
     const int64_t blocks = s.w_elems < (1 << 20) ? s.w_elems : (1 << 20);
     hipLaunchKernelGGL(direct_bwd_filter_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, s,
                        x, dy, dw);

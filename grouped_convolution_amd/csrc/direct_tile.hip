@@ -188,35 +188,46 @@ TileArgs bwd_data_args(const Shape& s, const float* dy, const float* w, float* d
 }
 
 // gradWeight for 3x3 and 5x5 filters with at most KG output channels per group:
-// one block per (group, input channel) computes dw[g*Kg + k][c][tap] for all k
-// and taps. Threads stride over the N*Ho*Wo pixels, each keeping KG x KS*KS
-// sums; the block then adds them in a fixed order (a butterfly within each
-// wave, then the waves in index order). One kernel, no workspace. Large
-// reductions take 1024-thread blocks, so each CU keeps enough loads in flight
-// although there is one block per (group, input channel).
-template <int KG, int KS, int NT>
-__global__ void __launch_bounds__(NT) direct_wgrad_kernel(Shape s, const float* __restrict__ x,
-                                                          const float* __restrict__ dy,
-                                                          float* __restrict__ dw)
+// a block owns one (group, input channel) and one slice of the N*Ho*Wo pixels
+// and computes its share of dw[g*Kg + k][c][tap] for all k and taps. Threads
+// stride over the slice, each keeping KG x KS*KS sums; the block then adds
+// them in a fixed order (a butterfly within each wave, then the four waves in
+// index order). With one slice the block writes dw; with several, each writes
+// its partial to the workspace and direct_wgrad_reduce adds the slices in
+// order (depthwise layers have few (group, channel) pairs and long pixel
+// reductions: the slices keep every CU busy).
+struct WgradArgs {
+    Shape s;
+    const float* x;
+    const float* dy;
+    float* out;       // dw, or the workspace [nslice][w_elems]
+    int nslice, slice;  // slices per (group, channel) and pixels per slice
+};
+
+template <int KG, int KS>
+__global__ void __launch_bounds__(256) direct_wgrad_kernel(WgradArgs wa)
 {
     constexpr int T = KS * KS;
-    constexpr int NWV = NT / 64;
-    __shared__ float red[NWV][KG * T];
-    const int g = blockIdx.x / s.Cg, c = blockIdx.x - (blockIdx.x / s.Cg) * s.Cg;
+    __shared__ float red[4][KG * T];
+    const Shape& s = wa.s;
+    const int pairs = s.G * s.Cg;
+    const int gc = blockIdx.x % pairs, ks = blockIdx.x / pairs;
+    const int g = gc / s.Cg, c = gc - (gc / s.Cg) * s.Cg;
     const int P = s.Ho * s.Wo;
     const int total = s.N * P;
+    const int e0 = ks * wa.slice, e1 = min(total, e0 + wa.slice);
     const size_t HW = (size_t)s.H * s.W;
     float acc[KG * T];
 #pragma unroll
     for (int e = 0; e < KG * T; ++e) acc[e] = 0.f;
-    for (int e = threadIdx.x; e < total; e += NT) {
+    for (int e = e0 + threadIdx.x; e < e1; e += 256) {
         const int n = e / P, p = e - (e / P) * P;
         const int ho = p / s.Wo, wo = p - (p / s.Wo) * s.Wo;
-        const float* dyp = dy + ((size_t)n * s.K + (size_t)g * s.Kg) * P + p;
+        const float* dyp = wa.dy + ((size_t)n * s.K + (size_t)g * s.Kg) * P + p;
         float dv[KG];
 #pragma unroll
         for (int k = 0; k < KG; ++k) dv[k] = k < s.Kg ? dyp[(size_t)k * P] : 0.f;
-        const float* xc = x + ((size_t)n * s.C + (size_t)g * s.Cg + c) * HW;
+        const float* xc = wa.x + ((size_t)n * s.C + (size_t)g * s.Cg + c) * HW;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
             const int h = ho * s.sh - s.ph + i * s.dh;
@@ -239,20 +250,48 @@ __global__ void __launch_bounds__(NT) direct_wgrad_kernel(Shape s, const float* 
         if (lane == 0) red[wave][e] = v;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < s.Kg * T; e += NT) {
+    float* out = wa.out + (size_t)ks * s.w_elems;
+    for (int e = threadIdx.x; e < s.Kg * T; e += 256) {
         const int k = e / T, t = e - (e / T) * T;
-        float sum = red[0][e];
-        for (int wv = 1; wv < NWV; ++wv) sum += red[wv][e];
-        dw[(((size_t)g * s.Kg + k) * s.Cg + c) * T + t] = sum;
+        out[(((size_t)g * s.Kg + k) * s.Cg + c) * T + t] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+    }
+}
+
+// dw[e] = sum of the slices' partials, in slice order.
+__global__ void __launch_bounds__(256) direct_wgrad_reduce(const float* __restrict__ ws, float* __restrict__ dw,
+                                                           int64_t E, int nslice)
+{
+    for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < E; e += (int64_t)gridDim.x * 256) {
+        float sum = ws[e];
+        for (int k = 1; k < nslice; ++k) sum += ws[k * E + e];
+        dw[e] = sum;
     }
 }
 
 template <int KG, int KS>
-void launch_wgrad(const Shape& s, const float* x, const float* dy, float* dw, int blocks, bool big,
-                  hipStream_t st)
+void launch_wgrad(const WgradArgs& wa, int blocks, hipStream_t st)
 {
-    if (big) hipLaunchKernelGGL((direct_wgrad_kernel<KG, KS, 1024>), dim3(blocks), dim3(1024), 0, st, s, x, dy, dw);
-    else hipLaunchKernelGGL((direct_wgrad_kernel<KG, KS, 256>), dim3(blocks), dim3(256), 0, st, s, x, dy, dw);
+    hipLaunchKernelGGL((direct_wgrad_kernel<KG, KS>), dim3(blocks), dim3(256), 0, st, wa);
+}
+
+// Slices per (group, input channel): about 2048 blocks in all, each slice at
+// least 2048 pixels long.
+void wgrad_slices(const Shape& s, int* nslice, int* slice)
+{
+    const int64_t total = (int64_t)s.N * s.Ho * s.Wo;
+    const int64_t pairs = (int64_t)s.G * s.Cg;
+    int64_t n = std::min<int64_t>((2048 + pairs - 1) / pairs, std::max<int64_t>(1, total / 2048));
+    n = std::max<int64_t>(1, n);
+    const int64_t len = (total + n - 1) / n;
+    *slice = (int)len;
+    *nslice = (int)((total + len - 1) / len);
+}
+
+bool wgrad_shape_ok(const Shape& s)
+{
+    const bool k3 = s.kh == 3 && s.kw == 3, k5 = s.kh == 5 && s.kw == 5;
+    if (!(k3 || k5) || s.Kg > (k3 ? 8 : 4) || s.N < 1) return false;
+    return (int64_t)s.N * s.Ho * s.Wo < (int64_t(1) << 31) && (int64_t)s.G * s.Cg < (1 << 24);
 }
 
 }  // namespace
@@ -273,26 +312,39 @@ bool direct_tile_bwd_data(const Shape& s, const float* dy, const float* w, float
     return run(a, st);
 }
 
-bool direct_tile_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
+size_t direct_tile_bwd_filter_workspace(const Shape& s)
+{
+    if (!wgrad_shape_ok(s)) return 0;
+    int nslice, slice;
+    wgrad_slices(s, &nslice, &slice);
+    return nslice > 1 ? (size_t)nslice * (size_t)s.w_elems * 4 : 0;
+}
+
+bool direct_tile_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                             hipStream_t st)
 {
-    const bool k3 = s.kh == 3 && s.kw == 3, k5 = s.kh == 5 && s.kw == 5;
-    if (!(k3 || k5) || s.Kg > (k3 ? 8 : 4) || s.N < 1) return false;
-    if ((int64_t)s.N * s.Ho * s.Wo >= (int64_t(1) << 31) || (int64_t)s.G * s.Cg >= (1 << 30))
-        return false;
-    const int blocks = s.G * s.Cg;
+    if (!wgrad_shape_ok(s)) return false;
+    WgradArgs wa;
+    wa.s = s; wa.x = x; wa.dy = dy;
+    wgrad_slices(s, &wa.nslice, &wa.slice);
+    if (wa.nslice > 1 && !ws) return false;
+    wa.out = wa.nslice > 1 ? ws : dw;
+    const int blocks = s.G * s.Cg * wa.nslice;
     const int kg = s.Kg <= 1 ? 1 : s.Kg <= 2 ? 2 : s.Kg <= 4 ? 4 : 8;
-    // 1024 threads cap a lane at 128 registers: 5x5 with 4 outputs keeps 256.
-    const bool big = (int64_t)s.N * s.Ho * s.Wo >= 16384 && !(k5 && kg == 4);
-    if (k3) {
-        if (kg == 1) launch_wgrad<1, 3>(s, x, dy, dw, blocks, big, st);
-        else if (kg == 2) launch_wgrad<2, 3>(s, x, dy, dw, blocks, big, st);
-        else if (kg == 4) launch_wgrad<4, 3>(s, x, dy, dw, blocks, big, st);
-        else launch_wgrad<8, 3>(s, x, dy, dw, blocks, big, st);
+    if (s.kh == 3) {
+        if (kg == 1) launch_wgrad<1, 3>(wa, blocks, st);
+        else if (kg == 2) launch_wgrad<2, 3>(wa, blocks, st);
+        else if (kg == 4) launch_wgrad<4, 3>(wa, blocks, st);
+        else launch_wgrad<8, 3>(wa, blocks, st);
     } else {
-        if (kg == 1) launch_wgrad<1, 5>(s, x, dy, dw, blocks, big, st);
-        else if (kg == 2) launch_wgrad<2, 5>(s, x, dy, dw, blocks, big, st);
-        else launch_wgrad<4, 5>(s, x, dy, dw, blocks, big, st);
+        if (kg == 1) launch_wgrad<1, 5>(wa, blocks, st);
+        else if (kg == 2) launch_wgrad<2, 5>(wa, blocks, st);
+        else launch_wgrad<4, 5>(wa, blocks, st);
+    }
+    if (wa.nslice > 1) {
+        const int64_t E = s.w_elems;
+        const int rb = (int)std::min<int64_t>(1024, (E + 255) / 256);
+        hipLaunchKernelGGL(direct_wgrad_reduce, dim3(rb), dim3(256), 0, st, ws, dw, E, wa.nslice);
     }
     return true;
 }

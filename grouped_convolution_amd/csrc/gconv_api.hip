@@ -137,6 +137,11 @@ int choose_path(const Shape& s, int op)
     // 1x1 at stride 1 without padding: the plane of each (image, group) is a
     // matrix, and the convolution is a GEMM with the group's weight block.
     if (s.kh == 1 && s.kw == 1 && path_supports(GCONV_PATH_POINTWISE, s, op)) return GCONV_PATH_POINTWISE;
+    // Depthwise gradWeight (one input channel per group): the sliced direct
+    // gradWeight kernel, which spends no arithmetic on absent channels.
+    if (op == GCONV_OP_BWD_FILTER && s.Cg == 1 && s.Kg <= 8 && (s.kh == 3 || s.kh == 5) &&
+        s.kh == s.kw)
+        return GCONV_PATH_DIRECT;
     // A handful of channels per group (ResNeXt-style, depthwise-like): the
     // HBM-bound 4x4x1-MFMA kernels.
     if (path_supports(GCONV_PATH_SMALLGROUP, s, op)) return GCONV_PATH_SMALLGROUP;
@@ -161,6 +166,8 @@ size_t workspace_for(const Shape& s, int op, int path)
         return smallgroup_bwd_filter_workspace(s);
     if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_POINTWISE && s.N > 0)
         return pointwise_bwd_filter_workspace(s);
+    if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_DIRECT && s.N > 0)
+        return direct_bwd_filter_workspace(s);
     return 0;
 }
 
@@ -320,7 +327,7 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
         return epilogue();
     }
     switch (path) {
-        case GCONV_PATH_DIRECT: direct_bwd_filter(s, x, dy, dw, hs); break;
+        case GCONV_PATH_DIRECT: direct_bwd_filter(s, x, dy, dw, (float*)workspace, hs); break;
         case GCONV_PATH_IGEMM:
             if (!igemm_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");

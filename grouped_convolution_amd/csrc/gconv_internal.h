@@ -32,8 +32,9 @@ inline bool is_fc_mode(const Shape& s)
 void direct_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
                 hipStream_t st);
 void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
-void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
+void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                        hipStream_t st);
+size_t direct_bwd_filter_workspace(const Shape& s);
 
 // LDS-tiled direct kernels for up to 32 output channels per group; return
 // false (nothing launched) where they do not apply.
@@ -41,8 +42,9 @@ bool direct_tile_fwd(const Shape& s, const float* x, const float* w, const float
                      hipStream_t st);
 bool direct_tile_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
                           hipStream_t st);
-bool direct_tile_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw,
+bool direct_tile_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                             hipStream_t st);
+size_t direct_tile_bwd_filter_workspace(const Shape& s);
 
 // ---- fp32-MFMA implicit GEMM (forward; gradInput at stride 1) ---------------
 // *_supported() tell whether the family covers a shape; the launchers return

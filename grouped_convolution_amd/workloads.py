@@ -20,6 +20,10 @@ measure or motivate:
   fc_mode        the kernel==input problem of "SpatialConvolution running in
                  fully-connected mode is very slow, even with R4": 1600 images
                  of 256x6x6 into 4096 planes with a 6x6 kernel.
+  mobilenet_dw   a depthwise 3x3 layer (groups = channels = 144, one filter
+                 per channel) of the mobilenet family the DLPrimitives Blog
+                 validates, at 56x56 with the batch of the ResNeXt shapes;
+                 post-ReLU input, no bias.
   resnext_1x1    the 1x1 (pointwise) 256->128 reduction that precedes the
                  grouped 3x3 in a resnext50_32x4d block, at the same 56x56
                  size and batch; post-ReLU input, no bias (the pages treat a
@@ -75,8 +79,12 @@ WORKLOADS = {
     "resnext_1x1": Workload(
         "resnext_1x1", 6, (64, 256, 56, 56), (128, 256, 1, 1), (64, 128, 56, 56), 1, 1, 0, 1,
         ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 256.0))), None),
+    "mobilenet_dw": Workload(
+        "mobilenet_dw", 7, (64, 144, 56, 56), (144, 1, 3, 3), (64, 144, 56, 56), 144, 1, 1, 1,
+        ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 9.0))), None),
 }
-WORKLOAD_ORDER = ["tiny_grouped", "dense3x3", "alexnet_conv2", "resnext_32x4d", "fc_mode", "resnext_1x1"]
+WORKLOAD_ORDER = ["tiny_grouped", "dense3x3", "alexnet_conv2", "resnext_32x4d", "fc_mode", "resnext_1x1",
+                  "mobilenet_dw"]
 
 
 def draw(dist, shape, seed) -> np.ndarray:
