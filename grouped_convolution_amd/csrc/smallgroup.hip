@@ -264,6 +264,91 @@ __global__ void __launch_bounds__(256) sg_conv_row64_kernel(SgArgs a)
     }
 }
 
+// Depthwise form (one input channel per group, up to 8 outputs): a workgroup
+// takes kDwGroups consecutive groups of one band, so that the tiles stay large
+// although each group has a single input plane, and every output is a plain
+// 9-tap FMA chain on the vector ALUs (the 4x4 MFMA blocks would be at most a
+// quarter used here). Same tile as above: one 64-float LDS row per input row,
+// lane = pixel, taps at immediate offsets.
+constexpr int kDwGroups = 4;
+
+template <int MQ, bool FLIP>
+__global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
+{
+    constexpr int T = 9, GB = kDwGroups;
+    extern __shared__ float lds[];           // [GB][LR][64] input rows, then [GB][MQ][T] filters
+    const int plane = a.LR * 64;
+    float* wl = lds + GB * plane;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int band = bid % a.nbands;
+    bid /= a.nbands;
+    const int ngb = (a.G + GB - 1) / GB;
+    const int gb = bid % ngb;
+    const int n = bid / ngb;
+    const int g0 = gb * GB, ng = min(GB, a.G - g0);
+    const int ho0 = band * a.R;
+    const int rows = min(a.R, a.Hout - ho0);
+    const int hbase = ho0 - a.ph;
+
+    // The groups' input planes are consecutive channels of image n.
+    const float* in_n = a.in + ((size_t)n * a.Cin_tot + g0) * a.Hin * a.Win;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_n, (uint32_t)ng * a.Hin * a.Win * 4u);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(a.wgt + (size_t)g0 * a.w_gstride, (uint32_t)ng * a.w_gstride * 4u);
+    const int wcol = lane - a.pw;
+    const bool colok = (unsigned)wcol < (unsigned)a.Win;
+#pragma unroll
+    for (int gi = 0; gi < GB; ++gi)
+        for (int r = wave; r < a.LR; r += 4) {
+            const int h = hbase + r;
+            const bool ok = colok && gi < ng && (unsigned)h < (unsigned)a.Hin;
+            load_lds64(rx, lds + gi * plane + r * 64,
+                       ok ? (uint32_t)((gi * a.Hin + h) * a.Win + wcol) * 4u : kOOB);
+        }
+    for (int e = tid; e < GB * MQ * T; e += 256) {
+        const int gi = e / (MQ * T), o = (e / T) % MQ, t = e % T;
+        const bool ok = gi < ng && o < a.Cout_g;
+        wl[e] = load_f32(rw, ok ? (uint32_t)(gi * a.w_gstride + o * a.w_so + (FLIP ? T - 1 - t : t)) * 4u : kOOB);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    const size_t P = (size_t)a.Hout * a.Wout;
+    const int npix = rows * a.Wout;
+    for (int gi = 0; gi < ng; ++gi) {
+        float wv[MQ][T], bv[MQ];
+#pragma unroll
+        for (int o = 0; o < MQ; ++o) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) wv[o][t] = wl[(gi * MQ + o) * T + t];
+            bv[o] = (a.bias && o < a.Cout_g) ? a.bias[(g0 + gi) * a.Cout_g + o] : 0.f;
+        }
+        float* out_g = a.out + ((size_t)n * a.Cout_tot + (size_t)(g0 + gi) * a.Cout_g) * P + (size_t)ho0 * a.Wout;
+        for (int s0 = wave * 64; s0 < npix; s0 += 256) {
+            const int pl = s0 + lane;
+            const int pc = min(pl, npix - 1);
+            const int r = (int)fastdiv((uint32_t)pc, a.div_Wout);
+            const float* xb = lds + gi * plane + r * 64 + (pc - r * a.Wout);
+            float xv[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) xv[t] = xb[(t / 3) * 64 + t % 3];
+            if (pl < npix) {
+#pragma unroll
+                for (int o = 0; o < MQ; ++o) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int t = 0; t < T; ++t) acc = fmaf(wv[o][t], xv[t], acc);
+                    // Streaming stores: the output is not read again here.
+                    if (o < a.Cout_g) __builtin_nontemporal_store(acc + bv[o], out_g + (size_t)o * P + pl);
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gradWeight
 // ---------------------------------------------------------------------------
@@ -619,9 +704,55 @@ bool sg_run_row64(const SgProblem& p, hipStream_t st)
     return false;
 }
 
+template <int MQ, bool FLIP>
+void sg_dw_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
+{
+    hipLaunchKernelGGL((sg_dw_row64_kernel<MQ, FLIP>), dim3(blocks), dim3(256), lds, st, a);
+}
+
+// One input channel per group (depthwise forward; depthwise gradInput with a
+// multiplier of 1) on the row-per-DMA tile, kDwGroups groups per workgroup.
+bool sg_run_dw(const SgProblem& p, hipStream_t st)
+{
+    const int MQ = p.Cout_g <= 1 ? 1 : p.Cout_g <= 2 ? 2 : p.Cout_g <= 4 ? 4 : 8;
+    SgArgs a;
+    a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.N = p.N; a.G = p.G;
+    a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
+    a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
+    a.sh = 1; a.sw = 1; a.dh = 1; a.dw = 1; a.ph = p.ph; a.pw = p.pw;
+    a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
+    a.uh = 1; a.uw = 1; a.Hr = p.Hin; a.Wr = p.Win;
+    const int nb = (p.Hout + 15) / 16;
+    a.R = (p.Hout + nb - 1) / nb;
+    a.nbands = (p.Hout + a.R - 1) / a.R;
+    a.LR = a.R + 2;
+    a.LW = 64;
+    a.plane = a.LR * 64;
+    a.div_plane = make_fastdiv((uint32_t)a.plane);
+    a.div_LW = make_fastdiv(64u);
+    a.div_Wout = make_fastdiv((uint32_t)p.Wout);
+    const int64_t blocks = (int64_t)p.N * ((p.G + kDwGroups - 1) / kDwGroups) * a.nbands;
+    if (blocks >= (1 << 30)) return false;
+    if ((int64_t)kDwGroups * p.w_gstride * 4 >= (int64_t(1) << 30)) return false;
+    const size_t lds = ((size_t)kDwGroups * a.plane + (size_t)kDwGroups * MQ * 9) * 4;
+#define SG_CASE(mq)                                                             \
+    if (MQ == mq) {                                                             \
+        if (p.flip) sg_dw_launch<mq, true>(a, (int)blocks, lds, st);            \
+        else sg_dw_launch<mq, false>(a, (int)blocks, lds, st);                  \
+        return true;                                                            \
+    }
+    SG_CASE(1) SG_CASE(2) SG_CASE(4) SG_CASE(8)
+#undef SG_CASE
+    return false;
+}
+
 bool sg_run(const SgProblem& p, hipStream_t st)
 {
     if (!sg_problem_ok(p)) return false;
+#ifndef GCONV_SG_NO_DW
+    if (p.Cin_g == 1 && sg_row64_ok(p)) return sg_run_dw(p, st);
+#endif
 #ifndef GCONV_SG_NO_ROW64
     if (sg_row64_ok(p)) return sg_run_row64(p, st);
 #endif

@@ -420,6 +420,13 @@ EDGE_CASES = [
     # ... and 5x5 at stride 2
     (dict(N=2, C=32, K=32, H=21, W=20, kh=5, kw=5, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=1),
      {"bwd_data": "igemm"}),
+    # depthwise VALU kernel, four groups per workgroup: multiplier 3 over 6
+    # groups (the last workgroup holds two), and multiplier 1 over 5 groups
+    # (gradInput takes it too)
+    (dict(N=2, C=6, K=18, H=21, W=30, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=6),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup"}),
+    (dict(N=3, C=5, K=5, H=17, W=40, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=5),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "direct"}),
     # strided gradInput on the small-group kernels (dy read as if upsampled):
     # depthwise 3x3 at stride 2, odd and even sizes ...
     (dict(N=2, C=8, K=8, H=15, W=14, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),
