@@ -137,8 +137,10 @@ int choose_path(const Shape& s, int op)
     // 1x1 at stride 1 without padding: the plane of each (image, group) is a
     // matrix, and the convolution is a GEMM with the group's weight block.
     if (s.kh == 1 && s.kw == 1 && path_supports(GCONV_PATH_POINTWISE, s, op)) return GCONV_PATH_POINTWISE;
-    // Depthwise gradWeight (one input channel per group): the sliced direct
-    // gradWeight kernel, which spends no arithmetic on absent channels.
+    // Depthwise gradWeight (one input channel per group): the depthwise row
+    // kernel of the small-group family where it applies, else the sliced
+    // direct gradWeight kernel; neither spends arithmetic on absent channels.
+    if (op == GCONV_OP_BWD_FILTER && s.Cg == 1 && smallgroup_dw_wgrad_ok(s)) return GCONV_PATH_SMALLGROUP;
     if (op == GCONV_OP_BWD_FILTER && s.Cg == 1 && s.Kg <= 8 && (s.kh == 3 || s.kh == 5) &&
         s.kh == s.kw)
         return GCONV_PATH_DIRECT;

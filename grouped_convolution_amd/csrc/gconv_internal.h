@@ -65,6 +65,7 @@ bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw
 bool smallgroup_fwd_supported(const Shape& s);
 bool smallgroup_bwd_data_supported(const Shape& s);
 bool smallgroup_bwd_filter_supported(const Shape& s);
+bool smallgroup_dw_wgrad_ok(const Shape& s);
 size_t smallgroup_bwd_filter_workspace(const Shape& s);
 bool smallgroup_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
                     hipStream_t st);

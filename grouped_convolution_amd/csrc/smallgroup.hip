@@ -580,6 +580,135 @@ __global__ void __launch_bounds__(256) sg_wgrad_row64_kernel(SgWArgs a)
 // dw[g*Kg + k, c, t] = sum over the (image, band) partial sets. Block = 16
 // outputs x 16 set groups: thread (e, sg) sums sets sg, sg+16, ... in order,
 // then the 16 group sums are added in order.
+// Depthwise gradWeight (one input channel per group, up to 2 outputs): the
+// row tile of the kernel above for kDwwGroups consecutive groups at a time,
+// accumulated on the vector ALUs (lane = output column, 9 taps x MQ sums per
+// group and lane), so no arithmetic goes to absent channels. A workgroup owns
+// a group block and a run of images, walks their bands, and writes one
+// partial [o][tap] per group; sg_dw_wgrad_reduce adds the runs in order.
+constexpr int kDwwGroups = 4;
+
+struct SgDwWArgs {
+    const float* x;
+    const float* dy;
+    float* ws;
+    int N, C, H, W, K, Ho, Wo, G, Kg, ph, pw;
+    int R, run, nruns;      // band rows, images per workgroup, workgroups per group block
+    int plane, dplane;      // x plane ((R+2)*64 + 8) and dy plane (R*64 + 8), floats
+};
+
+template <int MQ>
+__global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
+{
+    constexpr int T = 9, GB = kDwwGroups;
+    extern __shared__ float lds[];  // [GB][plane] x rows, [GB*MQ][dplane] dy rows; later sums
+    float* ds = lds + GB * a.plane;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int ngb = (a.G + GB - 1) / GB;
+    const int gb = bid % ngb, chunk = bid / ngb;
+    const int g0 = gb * GB, ng = min(GB, a.G - g0);
+    const int n_begin = chunk * a.run, n_end = min(a.N, n_begin + a.run);
+
+    const int wcol = lane - a.pw;
+    const bool colok = (unsigned)wcol < (unsigned)a.W;
+    // Lanes past the image width read up to two floats beyond the last x row of
+    // a plane (times dy = 0): keep the pad after each plane zero.
+    if (tid < GB * 8) lds[(tid >> 3) * a.plane + (a.R + 2) * 64 + (tid & 7)] = 0.f;
+
+    float acc[GB][MQ][T];
+#pragma unroll
+    for (int gi = 0; gi < GB; ++gi)
+#pragma unroll
+        for (int o = 0; o < MQ; ++o)
+#pragma unroll
+            for (int t = 0; t < T; ++t) acc[gi][o][t] = 0.f;
+
+    for (int n = n_begin; n < n_end; ++n) {
+        const float* xg = a.x + ((size_t)n * a.C + g0) * a.H * a.W;
+        const float* dyg = a.dy + ((size_t)n * a.K + (size_t)g0 * a.Kg) * a.Ho * a.Wo;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, (uint32_t)ng * a.H * a.W * 4u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, (uint32_t)ng * a.Kg * a.Ho * a.Wo * 4u);
+        for (int ho0 = 0; ho0 < a.Ho; ho0 += a.R) {
+            const int rows = min(a.R, a.Ho - ho0);
+            const int hb = ho0 - a.ph;
+            __syncthreads();  // every wave is done with the previous band
+#pragma unroll
+            for (int gi = 0; gi < GB; ++gi)
+                for (int r = wave; r < rows + 2; r += 4) {
+                    const int h = hb + r;
+                    const bool ok = colok && gi < ng && (unsigned)h < (unsigned)a.H;
+                    load_lds64(rx, lds + gi * a.plane + r * 64,
+                               ok ? (uint32_t)((gi * a.H + h) * a.W + wcol) * 4u : kOOB);
+                }
+#pragma unroll
+            for (int j = 0; j < GB * MQ; ++j)
+                for (int r = wave; r < rows; r += 4) {
+                    const int gi = j / MQ, o = j % MQ;
+                    const bool ok = lane < a.Wo && gi < ng && o < a.Kg;
+                    load_lds64(rd, ds + j * a.dplane + r * 64,
+                               ok ? (uint32_t)(((gi * a.Kg + o) * a.Ho + ho0 + r) * a.Wo + lane) * 4u : kOOB);
+                }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            for (int r = wave; r < rows; r += 4) {
+#pragma unroll
+                for (int gi = 0; gi < GB; ++gi) {
+                    const float* xr = lds + gi * a.plane + r * 64 + lane;
+                    float xv[T];
+#pragma unroll
+                    for (int t = 0; t < T; ++t) xv[t] = xr[(t / 3) * 64 + t % 3];
+#pragma unroll
+                    for (int o = 0; o < MQ; ++o) {
+                        const float dv = ds[(gi * MQ + o) * a.dplane + r * 64 + lane];
+#pragma unroll
+                        for (int t = 0; t < T; ++t) acc[gi][o][t] = fmaf(dv, xv[t], acc[gi][o][t]);
+                    }
+                }
+            }
+        }
+    }
+
+    // Sum the 64 lanes (a fixed butterfly), then the four waves in order.
+    __syncthreads();  // LDS reuse
+    float* red = lds;  // [wave][GB*MQ*T]
+#pragma unroll
+    for (int gi = 0; gi < GB; ++gi)
+#pragma unroll
+        for (int o = 0; o < MQ; ++o)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                float v = acc[gi][o][t];
+                for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+                if (lane == 0) red[wave * (GB * MQ * T) + (gi * MQ + o) * T + t] = v;
+            }
+    __syncthreads();
+    // Partial of this (image run, group block): ws[chunk][g][o][t].
+    for (int e = tid; e < GB * MQ * T; e += 256) {
+        const int gi = e / (MQ * T);
+        if (gi >= ng) continue;
+        constexpr int S = GB * MQ * T;
+        const float v = ((red[e] + red[S + e]) + red[2 * S + e]) + red[3 * S + e];
+        a.ws[((size_t)chunk * a.G + g0) * (MQ * T) + e] = v;
+    }
+}
+
+// dw[g*Kg + o][0][t] = sum over image runs (in order) of ws[run][g][o][t].
+__global__ void __launch_bounds__(256) sg_dw_wgrad_reduce(const float* __restrict__ ws, float* __restrict__ dw,
+                                                          int nruns, int G, int Kg, int MQ)
+{
+    const int e = blockIdx.x * 256 + threadIdx.x;  // over G * Kg * 9
+    if (e >= G * Kg * 9) return;
+    const int t = e % 9, go = e / 9, g = go / Kg, o = go - (go / Kg) * Kg;
+    const size_t per = (size_t)G * MQ * 9;
+    const size_t idx = ((size_t)g * MQ + o) * 9 + t;
+    float sum = ws[idx];
+    for (int r = 1; r < nruns; ++r) sum += ws[(size_t)r * per + idx];
+    dw[e] = sum;
+}
+
 __global__ void __launch_bounds__(256) sg_wgrad_reduce(const float* __restrict__ ws,
                                                        float* __restrict__ dw, int nsets, int G,
                                                        int Kg, int Cg, int T)
@@ -890,6 +1019,33 @@ bool sgw_plan(const Shape& s, SgWArgs* out, bool* row64 = nullptr)
 
 }  // namespace
 
+// Depthwise gradWeight on the row tile: 3x3, stride and dilation 1, one input
+// and at most 2 output channels per group, rows of at most 62 outputs.
+bool sg_dw_wgrad_plan(const Shape& s, SgDwWArgs* out, int* mq)
+{
+    if (!(s.kh == 3 && s.kw == 3 && s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1)) return false;
+    if (s.Cg != 1 || s.Kg > 2 || s.N < 1 || s.Wo + 2 > 64 || s.ph < 0 || s.pw < 0 || s.pw > 2) return false;
+    if ((int64_t)kDwwGroups * s.H * s.W * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)kDwwGroups * s.Kg * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
+    SgDwWArgs a{};
+    a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
+    a.G = s.G; a.Kg = s.Kg; a.ph = s.ph; a.pw = s.pw;
+    const int nb = (s.Ho + 15) / 16;
+    a.R = (s.Ho + nb - 1) / nb;
+    const int ngb = (s.G + kDwwGroups - 1) / kDwwGroups;
+    const int runs = std::max(1, std::min(s.N, 1024 / std::max(1, ngb)));
+    a.run = (s.N + runs - 1) / runs;
+    a.nruns = (s.N + a.run - 1) / a.run;
+    a.plane = (a.R + 2) * 64 + 8;
+    a.dplane = a.R * 64 + 8;
+    if ((int64_t)a.nruns * ngb >= (1 << 30)) return false;
+    if (out) *out = a;
+    if (mq) *mq = s.Kg <= 1 ? 1 : 2;
+    return true;
+}
+
+bool smallgroup_dw_wgrad_ok(const Shape& s) { return sg_dw_wgrad_plan(s, nullptr, nullptr); }
+
 bool smallgroup_fwd_supported(const Shape& s)
 {
     return sg_problem_ok(sg_fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
@@ -904,6 +1060,9 @@ bool smallgroup_bwd_filter_supported(const Shape& s) { return sgw_plan(s, nullpt
 
 size_t smallgroup_bwd_filter_workspace(const Shape& s)
 {
+    SgDwWArgs da;
+    int mq;
+    if (sg_dw_wgrad_plan(s, &da, &mq)) return (size_t)da.nruns * s.G * mq * 9 * sizeof(float);
     SgWArgs a;
     bool row64 = false;
     if (!sgw_plan(s, &a, &row64)) return 0;
@@ -926,6 +1085,21 @@ bool smallgroup_bwd_data(const Shape& s, const float* dy, const float* w, float*
 bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                            hipStream_t st)
 {
+    SgDwWArgs da;
+    int mq;
+    if (sg_dw_wgrad_plan(s, &da, &mq)) {
+        da.x = x; da.dy = dy; da.ws = ws;
+        const int ngb = (s.G + kDwwGroups - 1) / kDwwGroups;
+        const int blocks = ngb * da.nruns;
+        const size_t lds = std::max((size_t)kDwwGroups * da.plane + (size_t)kDwwGroups * mq * da.dplane,
+                                    (size_t)4 * kDwwGroups * mq * 9) * 4;
+        if (mq == 1) hipLaunchKernelGGL(sg_dw_wgrad_kernel<1>, dim3(blocks), dim3(256), lds, st, da);
+        else hipLaunchKernelGGL(sg_dw_wgrad_kernel<2>, dim3(blocks), dim3(256), lds, st, da);
+        const int E = s.G * s.Kg * 9;
+        hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 255) / 256), dim3(256), 0, st, ws, dw, da.nruns, s.G,
+                           s.Kg, mq);
+        return true;
+    }
     SgWArgs a;
     bool row64 = false;
     if (!sgw_plan(s, &a, &row64)) return false;

@@ -426,7 +426,11 @@ EDGE_CASES = [
     (dict(N=2, C=6, K=18, H=21, W=30, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=6),
      {"fwd": "smallgroup", "bwd_data": "smallgroup"}),
     (dict(N=3, C=5, K=5, H=17, W=40, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=5),
-     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "direct"}),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # depthwise gradWeight on the row tile: multiplier 2 over 6 groups (the
+    # last group block holds two) and 37 images (one per workgroup run)
+    (dict(N=37, C=6, K=12, H=19, W=33, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=6),
+     {"fwd": "smallgroup", "bwd_filter": "smallgroup"}),
     # strided gradInput on the small-group kernels (dy read as if upsampled):
     # depthwise 3x3 at stride 2, odd and even sizes ...
     (dict(N=2, C=8, K=8, H=15, W=14, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),
