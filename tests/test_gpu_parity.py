@@ -201,6 +201,39 @@ def test_fc_mode_random(seed):
 
 
 @pytest.mark.parametrize("seed", range(2))
+def test_random_descriptors_depthwise_family(seed):
+    """Depthwise layers (groups = input channels, channel multiplier 1-3): 3x3
+    and 5x5 filters, strides 1 and 2, dilation, padding, ragged sizes, on the
+    dispatcher's choice and on the small-group and direct families."""
+    rng = np.random.default_rng(170 + seed)
+    covered = {op: 0 for op in OPS}
+    n_done = 0
+    while n_done < 8:
+        k = int(rng.choice([3, 3, 5]))
+        C = int(rng.integers(1, 10))
+        d = dict(N=int(rng.integers(1, 4)), C=C, K=C * int(rng.integers(1, 4)),
+                 H=int(rng.integers(k, 40)), W=int(rng.integers(k, 62)), kh=k, kw=k,
+                 sh=int(rng.choice([1, 1, 2])), sw=int(rng.choice([1, 1, 2])),
+                 ph=int(rng.integers(0, k)), pw=int(rng.integers(0, k // 2 + 1)),
+                 dh=int(rng.choice([1, 1, 2])), dw=int(rng.choice([1, 1, 2])), G=C)
+        if not fits(d["H"], d["W"], k, k, d["sh"], d["sw"], d["ph"], d["pw"], d["dh"], d["dw"]):
+            continue
+        n_done += 1
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 1700 + 10 * seed + n_done)
+        y_ref, _ = oracle.fwd(x, w, b, **kw)
+        dy = draw(("normal", 1.0), y_ref.shape, 1750 + 10 * seed + n_done)
+        ref = oracle_all(x, w, b, dy, kw)
+        for path in [G.PATH_AUTO, G.PATH_SMALLGROUP, G.PATH_DIRECT]:
+            say("depthwise desc %s path %s" % (d, G.PATH_NAMES[path]))
+            for op in compare_full("%s %s" % (G.PATH_NAMES[path], d),
+                                   run_path(path, x, w, b, dy, kw), ref):
+                if path == G.PATH_SMALLGROUP:
+                    covered[op] += 1
+    assert covered["fwd"] >= 6, covered
+
+
+@pytest.mark.parametrize("seed", range(2))
 def test_random_descriptors_pointwise_family(seed):
     """1x1 filters at stride 1 without padding, the pointwise GEMM path: planes
     of any size (not a multiple of 4 or of the 128-wide tile), channel counts
