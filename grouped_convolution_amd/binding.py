@@ -24,11 +24,12 @@ STATUS = {0: "GCONV_OK", 1: "GCONV_ERR_NULL", 2: "GCONV_ERR_SHAPE", 3: "GCONV_ER
           7: "GCONV_ERR_ARG"}
 OP_FWD, OP_BWD_DATA, OP_BWD_FILTER, OP_BWD_BIAS = 0, 1, 2, 3
 PATH_AUTO, PATH_DIRECT, PATH_SMALLGROUP, PATH_IGEMM, PATH_FC, PATH_POINTWISE = 0, 1, 2, 3, 4, 5
+EPILOGUE_NONE, EPILOGUE_RELU = 0, 1
 PATH_NAMES = {PATH_AUTO: "auto", PATH_DIRECT: "direct", PATH_SMALLGROUP: "smallgroup",
               PATH_IGEMM: "igemm", PATH_FC: "fc", PATH_POINTWISE: "pointwise"}
 
 # Every symbol include/gconv.h declares.
-EXPORTS = ("gconv_output_dims", "gconv_workspace_size", "gconv_fwd", "gconv_bwd_data",
+EXPORTS = ("gconv_output_dims", "gconv_workspace_size", "gconv_fwd", "gconv_fwd_ex", "gconv_bwd_data",
            "gconv_bwd_filter", "gconv_bwd_bias", "gconv_select_path", "gconv_set_path_override",
            "gconv_status_string", "gconv_last_error", "gconv_version")
 
@@ -65,6 +66,7 @@ def load(path: str = LIB_PATH):
         "gconv_output_dims": [D, i64p, i64p],
         "gconv_workspace_size": [D, I, ctypes.POINTER(ctypes.c_size_t)],
         "gconv_fwd": [D, P, P, P, P, P, S, P],
+        "gconv_fwd_ex": [D, P, P, P, I, P, P, S, P],
         "gconv_bwd_data": [D, P, P, P, P, S, P],
         "gconv_bwd_filter": [D, P, P, P, P, S, P],
         "gconv_bwd_bias": [D, P, P, P, S, P],
@@ -191,8 +193,9 @@ def _out(out, shape, like, name):
 
 
 def gconv_fwd(x, w, bias=None, *, stride=1, padding=0, dilation=1, groups=1, out=None,
-              workspace=None):
-    """y = conv(x, w) + bias; x [N,C,H,W], w [K,C/groups,kh,kw], bias [K] or None."""
+              workspace=None, relu=False):
+    """y = conv(x, w) + bias; x [N,C,H,W], w [K,C/groups,kh,kw], bias [K] or None.
+    With relu=True the kernels store max(y, 0) (gconv_fwd_ex, GCONV_EPILOGUE_RELU)."""
     _dev_f32(x, "x")
     _dev_f32(w, "w")
     if x.dim() != 4 or w.dim() != 4:
@@ -210,8 +213,9 @@ def gconv_fwd(x, w, bias=None, *, stride=1, padding=0, dilation=1, groups=1, out
     Ho, Wo = gconv_output_dims(desc)
     y = _out(out, (N, K, Ho, Wo), x, "out")
     ws, nws = _workspace(desc, OP_FWD, x.device, workspace)
-    _check(load().gconv_fwd(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(ws),
-                            nws, _stream(x.device)), "gconv_fwd")
+    _check(load().gconv_fwd_ex(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias),
+                               EPILOGUE_RELU if relu else EPILOGUE_NONE, _ptr(y), _ptr(ws), nws,
+                               _stream(x.device)), "gconv_fwd_ex")
     return y
 
 
@@ -297,15 +301,17 @@ class Plan:
         return ws, nws, _stream(device)
 
     @classmethod
-    def fwd(cls, x, w, bias, y, *, stride=1, padding=0, dilation=1, groups=1, workspace=None):
+    def fwd(cls, x, w, bias, y, *, stride=1, padding=0, dilation=1, groups=1, workspace=None,
+            relu=False):
         gconv_fwd(x, w, bias, stride=stride, padding=padding, dilation=dilation, groups=groups,
-                  out=y, workspace=workspace)            # validates once (and runs once)
+                  out=y, workspace=workspace, relu=relu)  # validates once (and runs once)
         N, C, H, W = x.shape
         K, _, kh, kw = w.shape
         desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
         ws, nws, st = cls._prep(desc, OP_FWD, x.device, workspace)
-        return cls("gconv_fwd", (ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias), _ptr(y),
-                                 _ptr(ws), nws, st), (desc, x, w, bias, y, ws))
+        act = EPILOGUE_RELU if relu else EPILOGUE_NONE
+        return cls("gconv_fwd_ex", (ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias), act, _ptr(y),
+                                    _ptr(ws), nws, st), (desc, x, w, bias, y, ws))
 
     @classmethod
     def bwd_data(cls, dy, w, dx, *, stride=1, padding=0, dilation=1, groups=1, workspace=None):

@@ -46,6 +46,7 @@ struct ConvMfmaArgs {
     int w_so, w_sr, w_gstride;  // weight strides: output channel, reduction channel, group
     int tiles_per_image, n_otiles;
     int LW, LR, plane;          // LDS input tile: row width, rows, channel plane stride
+    int relu;                   // forward epilogue: max(v, 0)
     FastDiv div_RW, div_LW, div_Wout;
 };
 
@@ -219,6 +220,12 @@ __global__ void __launch_bounds__(256, 2) conv_mfma_kernel(ConvMfmaArgs a)
             v.y += bv;
             v.z += bv;
             v.w += bv;
+            if (a.relu) {
+                v.x = relu_if(v.x, 1);
+                v.y = relu_if(v.y, 1);
+                v.z = relu_if(v.z, 1);
+                v.w = relu_if(v.w, 1);
+            }
             if (vec4) {
                 if (pb < p1) *(f4*)(orow + pb) = v;
             } else {
@@ -266,6 +273,7 @@ struct ConvFlatArgs {
     // which only rows and columns divisible by uh, uw hold values, row h/uh and
     // column w/uw of the stored Hr x Wr planes; 1, 1 otherwise.
     int uh, uw, Hr, Wr;
+    int relu;                   // forward epilogue: max(v, 0)
     FastDiv div_P, div_Wout, div_plane, div_LW;
 };
 
@@ -455,6 +463,12 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             v.y += bv;
             v.z += bv;
             v.w += bv;
+            if (a.relu) {
+                v.x = relu_if(v.x, 1);
+                v.y = relu_if(v.y, 1);
+                v.z = relu_if(v.z, 1);
+                v.w = relu_if(v.w, 1);
+            }
             if (vec4) {
                 // P % 4 == 0 and q0 % 16 == 0: the four pixels share an image.
                 if (qb < q1) {
@@ -537,6 +551,7 @@ struct Problem {
     int w_so, w_sr, w_gstride;
     bool flip;
     int uh = 1, uw = 1, Hr = 0, Wr = 0;  // input upsampling (flat kernel only), stored plane size
+    int relu = 0;                        // forward epilogue
 };
 
 int choose_cc(const Problem& p) { return (p.kh * p.kw >= 16) ? 4 : 8; }
@@ -587,6 +602,7 @@ bool run_problem(const Problem& p, hipStream_t st)
     const int BO = 16 * MO;
     ConvMfmaArgs a;
     a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.relu = p.relu;
     a.N = p.N; a.G = p.G;
     a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
     a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
@@ -622,6 +638,7 @@ Problem fwd_problem(const Shape& s, const float* x, const float* w, const float*
     p.w_so = s.Cg * T; p.w_sr = T; p.w_gstride = s.Kg * s.Cg * T;
     p.flip = false;
     p.Hr = s.H; p.Wr = s.W;
+    p.relu = s.relu;
     return p;
 }
 
@@ -769,6 +786,7 @@ bool run_flat(const Problem& p, hipStream_t st)
     a.LW = fp.LW; a.plane = fp.plane; a.nseg = fp.nseg; a.bufsz = fp.bufsz;
     a.halo = (p.kh - 1) * p.dh + 1;
     a.uh = p.uh; a.uw = p.uw; a.Hr = p.Hr; a.Wr = p.Wr;
+    a.relu = p.relu;
     a.div_P = make_fastdiv((uint32_t)a.P);
     a.div_Wout = make_fastdiv((uint32_t)p.Wout);
     a.div_plane = make_fastdiv((uint32_t)fp.plane);

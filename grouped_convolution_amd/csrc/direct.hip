@@ -60,7 +60,7 @@ direct_fwd_kernel(Shape s, const float* __restrict__ x, const float* __restrict_
             }
         }
         if (bias) acc += bias[k];
-        y[e] = acc;
+        y[e] = relu_if(acc, s.relu);
     }
 }
 

@@ -32,6 +32,7 @@ struct TileArgs {
     int kh, kw, sh, sw, dh, dw, ph, pw;
     int w_so, w_sr, w_gstride;
     int tiles;          // tiles of 256 output pixels per plane
+    int relu;           // forward epilogue: max(v, 0)
     int LW, LR, CC;     // LDS tile: row width, rows, input channels per chunk
     bool flip;
 };
@@ -117,7 +118,7 @@ __global__ void __launch_bounds__(256) direct_tile_kernel(TileArgs a)
         if (k < a.Cout_g) {
             const float v = ((red[k * 64 + px] + red[(KG + k) * 64 + px]) + red[(2 * KG + k) * 64 + px]) +
                             red[(3 * KG + k) * 64 + px];
-            out[(size_t)k * P] = v + (a.bias ? a.bias[g * a.Cout_g + k] : 0.f);
+            out[(size_t)k * P] = relu_if(v + (a.bias ? a.bias[g * a.Cout_g + k] : 0.f), a.relu);
         }
 }
 
@@ -160,6 +161,7 @@ TileArgs fwd_args(const Shape& s, const float* x, const float* w, const float* b
 {
     TileArgs a{};
     a.in = x; a.wgt = w; a.bias = bias; a.out = y;
+    a.relu = s.relu;
     a.N = s.N; a.G = s.G; a.Cin_tot = s.C; a.Cin_g = s.Cg; a.Hin = s.H; a.Win = s.W;
     a.Cout_tot = s.K; a.Cout_g = s.Kg; a.Hout = s.Ho; a.Wout = s.Wo;
     a.kh = s.kh; a.kw = s.kw; a.sh = s.sh; a.sw = s.sw; a.dh = s.dh; a.dw = s.dw;
@@ -176,6 +178,7 @@ TileArgs bwd_data_args(const Shape& s, const float* dy, const float* w, float* d
 {
     TileArgs a{};
     a.in = dy; a.wgt = w; a.bias = nullptr; a.out = dx;
+    a.relu = 0;
     a.N = s.N; a.G = s.G; a.Cin_tot = s.K; a.Cin_g = s.Kg; a.Hin = s.Ho; a.Win = s.Wo;
     a.Cout_tot = s.C; a.Cout_g = s.Cg; a.Hout = s.H; a.Wout = s.W;
     a.kh = s.kh; a.kw = s.kw; a.sh = 1; a.sw = 1; a.dh = s.dh; a.dw = s.dw;

@@ -251,10 +251,19 @@ int gconv_set_path_override(int path)
 int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* bias, float* y,
               void* workspace, size_t workspace_bytes, void* stream)
 {
+    return gconv_fwd_ex(d, x, w, bias, GCONV_EPILOGUE_NONE, y, workspace, workspace_bytes, stream);
+}
+
+int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const float* bias, int act,
+                 float* y, void* workspace, size_t workspace_bytes, void* stream)
+{
     Shape s;
     int path;
+    if (act != GCONV_EPILOGUE_NONE && act != GCONV_EPILOGUE_RELU)
+        return fail(GCONV_ERR_ARG, "unknown epilogue %d", act);
     int st = prologue(d, GCONV_OP_FWD, &s, &path, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
+    s.relu = act == GCONV_EPILOGUE_RELU;
     if (!w || (s.N > 0 && (!x || !y)))
         return fail(GCONV_ERR_NULL, "x, w and y must be non-NULL");
     if (overlap(y, s.y_elems, x, s.x_elems) || overlap(y, s.y_elems, w, s.w_elems) ||

@@ -18,7 +18,11 @@ struct Shape {
     int Ho, Wo;
     // element counts (64-bit) of x, w, y
     int64_t x_elems, w_elems, y_elems;
+    int relu = 0;   // forward only: y = max(conv + bias, 0)
 };
+
+// The forward epilogue's activation: max(v, 0), with 0 (not NaN) for NaN.
+__host__ __device__ inline float relu_if(float v, int relu) { return (relu && !(v > 0.f)) ? 0.f : v; }
 
 inline bool is_fc_mode(const Shape& s)
 {

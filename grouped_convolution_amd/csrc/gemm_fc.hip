@@ -49,6 +49,7 @@ struct GemmArgs {
     int a_mod, b_mod, c_mod, bias_mod;
     int64_t a_gs, b_gs, c_gs, bias_gs;  // batch-entry offsets (floats)
     int bias_rows;                 // bias indexed by the row (1) or by the column (0)
+    int relu;                      // epilogue: max(v, 0) after the bias
     uint32_t a_bytes, b_bytes;     // extent each entry's A / B resource may address
     // Reduction over several images (RIMG kernels): reduction index r is
     // position r % r_img of image r / r_img, images a_is / b_is floats apart.
@@ -208,6 +209,12 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
             if (m >= a.M) continue;
             f4 v = acc[i][j] + bv;
             if (bias && a.bias_rows) v += bias[m];
+            if (a.relu) {
+                v.x = relu_if(v.x, 1);
+                v.y = relu_if(v.y, 1);
+                v.z = relu_if(v.z, 1);
+                v.w = relu_if(v.w, 1);
+            }
             float* row = Cg + (size_t)m * a.c_ld;
             if (vec && n + 3 < a.N) {
                 *(f4*)(row + n) = v;
@@ -251,6 +258,7 @@ void plain(GemmArgs& a)
 {
     a.a_mod = a.b_mod = a.c_mod = a.bias_mod = a.Z;
     a.bias_rows = 0;
+    a.relu = 0;
     a.r_img = 0;
     a.div_rimg = make_fastdiv(1);
     a.a_is = a.b_is = 0;
@@ -308,6 +316,7 @@ void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, f
     plain(a);
     a.a_ld = Dt; a.b_ld = D; a.c_ld = s.K;
     a.a_gs = D; a.b_gs = (int64_t)s.Kg * D; a.c_gs = s.Kg; a.bias_gs = s.Kg;
+    a.relu = s.relu;
     a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * Dt + D) * 4);
     a.b_bytes = (uint32_t)((int64_t)s.Kg * D * 4);
     launch<true, true>(a, st);
@@ -398,6 +407,7 @@ void pointwise_fwd(const Shape& s, const float* x, const float* w, const float* 
     a.a_ld = s.Cg; a.b_ld = P; a.c_ld = P;
     a.a_gs = (int64_t)s.Kg * s.Cg; a.b_gs = (int64_t)s.Cg * P; a.c_gs = (int64_t)s.Kg * P;
     a.bias_gs = s.Kg; a.bias_rows = 1;
+    a.relu = s.relu;
     a.a_bytes = (uint32_t)((int64_t)s.Kg * s.Cg * 4);
     a.b_bytes = (uint32_t)((int64_t)s.Cg * P * 4);
     launch<true, false>(a, st);

@@ -56,6 +56,7 @@ struct SgArgs {
     // which only rows and columns divisible by uh, uw hold values, row h/uh and
     // column w/uw of the stored Hr x Wr planes; 1, 1 otherwise.
     int uh, uw, Hr, Wr;
+    int relu;                   // forward epilogue: max(v, 0)
     FastDiv div_plane, div_LW, div_Wout;
 };
 
@@ -156,7 +157,7 @@ __global__ void __launch_bounds__(256) sg_conv_kernel(SgArgs a)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int o = oq * 4 + v;
-                    if (o < a.Cout_g) out_g[(size_t)o * P + pl] = acc[oq][v] + bv[oq][v];
+                    if (o < a.Cout_g) out_g[(size_t)o * P + pl] = relu_if(acc[oq][v] + bv[oq][v], a.relu);
                 }
         }
     }
@@ -258,7 +259,8 @@ __global__ void __launch_bounds__(256) sg_conv_row64_kernel(SgArgs a)
                     // Streaming stores: the output is not read again here, so it
                     // should not displace the input rows neighbouring bands reuse.
                     if (o < a.Cout_g)
-                        __builtin_nontemporal_store(acc[oq][v] + bv[oq][v], out_g + (size_t)o * P + pl);
+                        __builtin_nontemporal_store(relu_if(acc[oq][v] + bv[oq][v], a.relu),
+                                                    out_g + (size_t)o * P + pl);
                 }
         }
     }
@@ -342,7 +344,8 @@ __global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
 #pragma unroll
                     for (int t = 0; t < T; ++t) acc = fmaf(wv[o][t], xv[t], acc);
                     // Streaming stores: the output is not read again here.
-                    if (o < a.Cout_g) __builtin_nontemporal_store(acc + bv[o], out_g + (size_t)o * P + pl);
+                    if (o < a.Cout_g)
+                        __builtin_nontemporal_store(relu_if(acc + bv[o], a.relu), out_g + (size_t)o * P + pl);
                 }
             }
         }
@@ -742,6 +745,7 @@ struct SgProblem {
     int w_so, w_sr, w_gstride;
     bool flip;
     int uh = 1, uw = 1, Hr = 0, Wr = 0;  // input upsampling (general kernel only), stored plane size
+    int relu = 0;                        // forward epilogue
 };
 
 // LDS tile budget per workgroup (28 KiB): five workgroups share a CU, so the
@@ -804,6 +808,7 @@ bool sg_run_row64(const SgProblem& p, hipStream_t st)
     const int OQ = p.Cout_g <= 4 ? 1 : 2;
     SgArgs a;
     a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.relu = p.relu;
     a.N = p.N; a.G = p.G;
     a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
     a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
@@ -846,6 +851,7 @@ bool sg_run_dw(const SgProblem& p, hipStream_t st)
     const int MQ = p.Cout_g <= 1 ? 1 : p.Cout_g <= 2 ? 2 : p.Cout_g <= 4 ? 4 : 8;
     SgArgs a;
     a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.relu = p.relu;
     a.N = p.N; a.G = p.G;
     a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
     a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
@@ -889,6 +895,7 @@ bool sg_run(const SgProblem& p, hipStream_t st)
     const int OQ = p.Cout_g <= 4 ? 1 : 2;
     SgArgs a;
     a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.relu = p.relu;
     a.N = p.N; a.G = p.G;
     a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
     a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
@@ -928,6 +935,7 @@ SgProblem sg_fwd_problem(const Shape& s, const float* x, const float* w, const f
     p.w_so = s.Cg * T; p.w_sr = T; p.w_gstride = s.Kg * s.Cg * T;
     p.flip = false;
     p.Hr = s.H; p.Wr = s.W;
+    p.relu = s.relu;
     return p;
 }
 

@@ -119,6 +119,23 @@ int gconv_workspace_size(const gconv_desc* d, int op, size_t* bytes);
 int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* bias, float* y,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Element-wise activations the forward pass can apply in its epilogue. */
+typedef enum gconv_epilogue {
+    GCONV_EPILOGUE_NONE = 0,   /* y = conv(x, w) + bias */
+    GCONV_EPILOGUE_RELU = 1    /* y = max(conv(x, w) + bias, 0); NaN becomes 0 */
+} gconv_epilogue;
+
+/*
+ * Forward pass with an element-wise activation applied to each output as it
+ * is stored, after the bias (DLPrimitives Blog, "Pointwise Broadcast Reduce":
+ * element-wise operations over the conv's output, broadcast over [B,C,H,W]),
+ * so the activation costs no extra pass over y. Same arguments as gconv_fwd
+ * plus `epilogue`, a gconv_epilogue; any other value is GCONV_ERR_ARG.
+ * gconv_fwd is gconv_fwd_ex with GCONV_EPILOGUE_NONE.
+ */
+int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const float* bias, int epilogue,
+                 float* y, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * gradInput (updateGradInput in the clnn issue): dx = d<y,dy>/dx, the exact
  * adjoint of the forward map. dx[n, g*Cg+c, h, w] sums w[k,c,i,j] *

@@ -17,6 +17,8 @@ Ops (names follow the Torch module passes the pages discuss):
   bwd_filter(x, dy, ...)  -> gradWeight  (accGradParameters, weight part)
   bwd_bias(dy)            -> gradBias    (DLPrimitives Blog, "Pointwise
                                           Broadcast Reduce": sum over 0,2,3)
+  fwd(..., relu=True)     -> max(y, 0)   (an element-wise operation on the
+                                          forward output, the same section)
 """
 from __future__ import annotations
 
@@ -141,10 +143,12 @@ def _run(fn, d, arrays, shape, idx):
     return val, mag
 
 
-def fwd(x, w, b=None, *, stride=1, padding=0, dilation=1, groups=1, idx=None):
+def fwd(x, w, b=None, *, stride=1, padding=0, dilation=1, groups=1, idx=None, relu=False):
     """y = conv(x, w) + b. x [N,C,H,W], w [K,C/G,kh,kw], b [K] or None.
 
-    With ``idx`` (flat indices into y), only those elements are computed."""
+    With ``idx`` (flat indices into y), only those elements are computed. With
+    ``relu``, y is replaced by max(y, 0) after the bias (NaN gives 0); A is
+    unchanged (the activation adds no rounding)."""
     x, w = _f64(x), _f64(w)
     b = None if b is None else _f64(b)
     N, C, H, W = x.shape
@@ -155,7 +159,10 @@ def fwd(x, w, b=None, *, stride=1, padding=0, dilation=1, groups=1, idx=None):
         raise OracleError("bias must have shape [K]")
     d = _desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
     Ho, Wo = output_dims(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
-    return _run(_load().oracle_fwd, d, [x, w, b], (N, K, Ho, Wo), idx)
+    y, a = _run(_load().oracle_fwd, d, [x, w, b], (N, K, Ho, Wo), idx)
+    if relu:
+        y = np.where(y > 0.0, y, 0.0)
+    return y, a
 
 
 def bwd_data(dy, w, x_shape, *, stride=1, padding=0, dilation=1, groups=1, idx=None):

@@ -287,6 +287,45 @@ def test_pointwise_integer_probe_exact(groups):
                           oracle.bwd_filter(x, dy, w.shape, **kw)[0])
 
 
+RELU_CASES = [
+    # (descriptor, path the dispatcher takes for the forward pass)
+    (dict(N=2, C=32, K=32, H=20, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1), "igemm"),
+    (dict(N=2, C=32, K=32, H=8, W=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1), "igemm"),
+    (dict(N=2, C=16, K=16, H=14, W=14, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=4),
+     "smallgroup"),
+    (dict(N=2, C=8, K=8, H=15, W=13, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
+     "smallgroup"),
+    (dict(N=2, C=8, K=16, H=12, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8),
+     "smallgroup"),
+    (dict(N=2, C=20, K=6, H=10, W=10, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=2), "direct"),
+    (dict(N=1, C=4, K=4, H=12, W=12, kh=7, kw=7, sh=1, sw=1, ph=3, pw=3, dh=1, dw=1, G=1), "direct"),
+    (dict(N=5, C=8, K=6, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), "fc"),
+    (dict(N=2, C=16, K=24, H=10, W=9, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+     "pointwise"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RELU_CASES)))
+def test_relu_epilogue(case):
+    """gconv_fwd_ex with the ReLU epilogue on every forward kernel family: max(y, 0)
+    after the bias, element by element against the oracle; the plain forward
+    pass of the same call sequence is unaffected."""
+    d, path = RELU_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
+    assert G.PATH_NAMES[G.gconv_select_path(desc, G.OP_FWD)] == path, d
+    x, w, b = tensors(d, 1900 + case)
+    say("relu epilogue %s" % d)
+    xd, wd, bd = dev(x), dev(w), dev(b)
+    y_relu = G.gconv_fwd(xd, wd, bd, relu=True, **kw)
+    y_plain = G.gconv_fwd(xd, wd, bd, **kw)
+    val, mag = oracle.fwd(x, w, b, relu=True, **kw)
+    check("relu %s" % d, y_relu.cpu().numpy(), val, mag)
+    val0, mag0 = oracle.fwd(x, w, b, **kw)
+    check("plain %s" % d, y_plain.cpu().numpy(), val0, mag0)
+    assert (y_relu >= 0).all()
+
+
 def test_fc_1x1_on_1x1_is_linear():
     """A 1x1 convolution of a 1x1 input (the Linear(128, 32) case of the
     cudnn.torch issue) runs the GEMM path and matches the oracle."""

@@ -395,3 +395,33 @@ def test_empty_batch():
     assert y.shape == y_t.shape and dx.shape == dx_t.shape == x.shape
     assert np.array_equal(dw, dw_t) and np.all(dw == 0)
     assert np.array_equal(db, db_t) and np.all(db == 0)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_relu_epilogue_matches_torch(seed):
+    """The forward pass with the ReLU epilogue equals torch's relu(conv2d(x, w, b))
+    in float64 on random descriptors (bias added before the activation)."""
+    for d in random_descs(40 + seed, 6):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 4000 + seed)
+        want = torch.relu(F.conv2d(torch.tensor(x, dtype=torch.float64),
+                                   torch.tensor(w, dtype=torch.float64),
+                                   torch.tensor(b, dtype=torch.float64), **kw)).numpy()
+        got, _ = oracle.fwd(x, w, b, relu=True, **kw)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), d
+
+
+def test_relu_epilogue_invariants():
+    """relu(y) - relu(-y) = y exactly (the negated output comes from negating w
+    and b, the forward pass being linear in them); nonnegative inputs leave the
+    output unchanged; nonnegative x with nonpositive w and b gives exact zeros."""
+    for d in random_descs(50, 6):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 4100)
+        y, _ = oracle.fwd(x, w, b, **kw)
+        pos, _ = oracle.fwd(x, w, b, relu=True, **kw)
+        neg, _ = oracle.fwd(x, -w, -b, relu=True, **kw)
+        assert np.array_equal(pos - neg, y), d
+        ax, aw, ab = np.abs(x), np.abs(w), np.abs(b)
+        assert np.array_equal(oracle.fwd(ax, aw, ab, relu=True, **kw)[0], oracle.fwd(ax, aw, ab, **kw)[0])
+        assert not np.any(oracle.fwd(ax, -aw, -ab, relu=True, **kw)[0])
