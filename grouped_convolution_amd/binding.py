@@ -44,7 +44,7 @@ class GconvError(RuntimeError):
 class gconv_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "N", "C", "H", "W", "K", "kh", "kw", "stride_h", "stride_w", "pad_h", "pad_w",
-        "dil_h", "dil_w", "groups")]
+        "dil_h", "dil_w", "groups", "pad_h_extra", "pad_w_extra")]
 
 
 _lib = None
@@ -103,12 +103,32 @@ def _pair(v, name):
     return int(v), int(v)
 
 
+def _padding(v):
+    """int, (pad_h, pad_w) or (top, bottom, left, right) -> (top, left, bottom - top, right - left)."""
+    if isinstance(v, (tuple, list)) and len(v) == 4:
+        t, b, l, r = (int(e) for e in v)
+        return t, l, b - t, r - l
+    ph, pw = _pair(v, "padding")
+    return ph, pw, 0, 0
+
+
+def same_padding(H, W, kh, kw, stride=1, dilation=1):
+    """TensorFlow's "same" padding as (top, bottom, left, right): Ho = ceil(H / stride), the
+    total padding split with the odd row or column at the end."""
+    out = []
+    for n, k, s, d in zip((H, W), (kh, kw), _pair(stride, "stride"), _pair(dilation, "dilation")):
+        total = max((-(-n // s) - 1) * s + (k - 1) * d + 1 - n, 0)
+        out += [total // 2, total - total // 2]
+    return tuple(out)
+
+
 def make_desc(N, C, H, W, K, kh, kw, stride=1, padding=0, dilation=1, groups=1) -> gconv_desc:
+    """`padding` is an int, a pair (pad_h, pad_w) or a 4-tuple (top, bottom, left, right)."""
     sh, sw = _pair(stride, "stride")
-    ph, pw = _pair(padding, "padding")
+    ph, pw, eh, ew = _padding(padding)
     dh, dw = _pair(dilation, "dilation")
     return gconv_desc(int(N), int(C), int(H), int(W), int(K), int(kh), int(kw), sh, sw, ph, pw,
-                      dh, dw, int(groups))
+                      dh, dw, int(groups), eh, ew)
 
 
 def gconv_output_dims(desc: gconv_desc):

@@ -28,9 +28,10 @@ int fail(int status, const char* fmt, ...)
     return status;
 }
 
-int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
+// Output extent with p0 zero rows before the input and p1 after it.
+int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p0, int64_t p1, int64_t d)
 {
-    const int64_t num = in + 2 * p - d * (k - 1) - 1;
+    const int64_t num = in + p0 + p1 - d * (k - 1) - 1;
     return num < 0 ? 0 : num / s + 1;
 }
 
@@ -51,6 +52,13 @@ int make_shape(const gconv_desc* d, Shape* s)
     if (d->stride_h < 1 || d->stride_w < 1 || d->dil_h < 1 || d->dil_w < 1 || d->pad_h < 0 ||
         d->pad_w < 0)
         return fail(GCONV_ERR_SHAPE, "need stride>=1, dilation>=1, pad>=0");
+    if (d->pad_h_extra < -kMaxDim || d->pad_h_extra > kMaxDim || d->pad_w_extra < -kMaxDim ||
+        d->pad_w_extra > kMaxDim)
+        return fail(GCONV_ERR_UNSUPPORTED, "a padding exceeds 2^30");
+    const int64_t pad_h_end = d->pad_h + d->pad_h_extra, pad_w_end = d->pad_w + d->pad_w_extra;
+    if (pad_h_end < 0 || pad_w_end < 0)
+        return fail(GCONV_ERR_SHAPE, "end padding pad+pad_extra must be >= 0 (got %lld, %lld)",
+                    (long long)pad_h_end, (long long)pad_w_end);
     if (d->groups < 1) return fail(GCONV_ERR_GROUPS, "groups=%lld must be >= 1",
                                    (long long)d->groups);
     if (d->C % d->groups != 0)
@@ -60,11 +68,12 @@ int make_shape(const gconv_desc* d, Shape* s)
         return fail(GCONV_ERR_GROUPS, "output channels K=%lld not divisible by groups=%lld",
                     (long long)d->K, (long long)d->groups);
     const int64_t dims[] = {d->N, d->C, d->H, d->W, d->K, d->kh, d->kw, d->stride_h,
-                            d->stride_w, d->pad_h, d->pad_w, d->dil_h, d->dil_w};
+                            d->stride_w, d->pad_h, d->pad_w, d->dil_h, d->dil_w,
+                            pad_h_end, pad_w_end};
     for (int64_t v : dims)
         if (v > kMaxDim) return fail(GCONV_ERR_UNSUPPORTED, "a dimension exceeds 2^30");
-    const int64_t Ho = out_extent(d->H, d->kh, d->stride_h, d->pad_h, d->dil_h);
-    const int64_t Wo = out_extent(d->W, d->kw, d->stride_w, d->pad_w, d->dil_w);
+    const int64_t Ho = out_extent(d->H, d->kh, d->stride_h, d->pad_h, pad_h_end, d->dil_h);
+    const int64_t Wo = out_extent(d->W, d->kw, d->stride_w, d->pad_w, pad_w_end, d->dil_w);
     if (Ho < 1 || Wo < 1)
         return fail(GCONV_ERR_SHAPE,
                     "empty output: the dilated kernel (%lldx%lld) exceeds the padded input",
@@ -73,6 +82,7 @@ int make_shape(const gconv_desc* d, Shape* s)
     s->kh = (int)d->kh; s->kw = (int)d->kw;
     s->sh = (int)d->stride_h; s->sw = (int)d->stride_w;
     s->ph = (int)d->pad_h; s->pw = (int)d->pad_w;
+    s->ph_end = (int)pad_h_end; s->pw_end = (int)pad_w_end;
     s->dh = (int)d->dil_h; s->dw = (int)d->dil_w;
     s->G = (int)d->groups; s->Cg = (int)(d->C / d->groups); s->Kg = (int)(d->K / d->groups);
     s->Ho = (int)Ho; s->Wo = (int)Wo;

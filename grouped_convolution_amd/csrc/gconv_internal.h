@@ -14,6 +14,10 @@ namespace gconv {
 struct Shape {
     int N, C, H, W, K, kh, kw;
     int sh, sw, ph, pw, dh, dw;
+    // Zero rows after the input and columns right of it. The kernels index
+    // with the leading pads (ph, pw) and take the extent from Ho, Wo, so the
+    // end pads matter only to shape checks.
+    int ph_end, pw_end;
     int G, Cg, Kg;  // groups, input and output planes per group
     int Ho, Wo;
     // element counts (64-bit) of x, w, y

@@ -364,6 +364,7 @@ void fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, h
 bool pointwise_supported(const Shape& s)
 {
     if (!(s.kh == 1 && s.kw == 1 && s.sh == 1 && s.sw == 1 && s.ph == 0 && s.pw == 0)) return false;
+    if (s.Ho != s.H || s.Wo != s.W) return false;  // no end padding: y planes are H x W
     if (s.N < 1) return false;
     const int64_t P = (int64_t)s.H * s.W;
     if (P * s.N >= (int64_t(1) << 31) || s.x_elems >= (int64_t(1) << 31) || s.y_elems >= (int64_t(1) << 31))

@@ -29,6 +29,12 @@ measure or motivate:
                  size and batch; post-ReLU input, no bias (the pages treat a
                  1x1 conv as a per-image GEMM unless its input is 1x1, in the
                  cudnn.torch fully-connected-mode issue).
+  mobilenet_dw_s2_same
+                 the stride-2 depthwise 3x3 of the same mobilenet family
+                 (144 channels, 56x56 -> 28x28) with TensorFlow's "same"
+                 padding, which puts the one padding row and column at the
+                 end only (DLPrimitives Blog, "TensorFlow"): padding given as
+                 (top, bottom, left, right) = (0, 1, 0, 1).
 No dataset or trained weight is involved; normals use the second parameter
 as the standard deviation (He/LeCun scales sqrt(2/fan_in), sqrt(1/fan_in)).
 """
@@ -50,7 +56,7 @@ class Workload:
     dy_shape: tuple                 # [N, K, Ho, Wo] as the workload states it
     groups: int
     stride: int
-    padding: int
+    padding: int | tuple            # int, or (top, bottom, left, right)
     dilation: int
     x_dist: tuple                   # ("uniform",) | ("normal", std) | ("relu_normal", std)
     w_dist: tuple
@@ -82,9 +88,12 @@ WORKLOADS = {
     "mobilenet_dw": Workload(
         "mobilenet_dw", 7, (64, 144, 56, 56), (144, 1, 3, 3), (64, 144, 56, 56), 144, 1, 1, 1,
         ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 9.0))), None),
+    "mobilenet_dw_s2_same": Workload(
+        "mobilenet_dw_s2_same", 8, (64, 144, 56, 56), (144, 1, 3, 3), (64, 144, 28, 28), 144, 2,
+        (0, 1, 0, 1), 1, ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 9.0))), None),
 }
 WORKLOAD_ORDER = ["tiny_grouped", "dense3x3", "alexnet_conv2", "resnext_32x4d", "fc_mode", "resnext_1x1",
-                  "mobilenet_dw"]
+                  "mobilenet_dw", "mobilenet_dw_s2_same"]
 
 
 def draw(dist, shape, seed) -> np.ndarray:

@@ -20,8 +20,8 @@
  *   x, dx  [N, C, H, W]
  *   w, dw  [K, C/groups, kh, kw]    (K * C/groups filter planes)
  *   bias, db [K]
- *   y, dy  [N, K, Ho, Wo],  Ho = floor((H + 2*pad_h - dil_h*(kh-1) - 1)/stride_h) + 1
- *                           (likewise Wo)
+ *   y, dy  [N, K, Ho, Wo],  Ho = floor((H + pad_h + pad_h_end - dil_h*(kh-1) - 1)/stride_h) + 1
+ *                           (likewise Wo), pad_h_end = pad_h + pad_h_extra
  *
  * Ownership and execution. The caller owns every buffer; the library never
  * allocates device memory. Every op is enqueued on the caller's HIP stream
@@ -56,9 +56,18 @@ extern "C" {
  * per-group count. The fields follow the constructor the clnn issue quotes
  * (nInputPlane, nOutputPlane, kW, kH, dW, dH, padW, padH, groups), plus
  * batch, input extent and dilation. Valid when N >= 0, C,H,W,K,kh,kw >= 1,
- * stride >= 1, dil >= 1, pad >= 0, groups >= 1, C % groups == 0,
- * K % groups == 0 and Ho, Wo >= 1 ("Support groups in DenseConvDims": the
- * channel counts must agree with the tensors and with the group split).
+ * stride >= 1, dil >= 1, pad >= 0, pad + pad_extra >= 0, groups >= 1,
+ * C % groups == 0, K % groups == 0 and Ho, Wo >= 1 ("Support groups in
+ * DenseConvDims": the channel counts must agree with the tensors and with the
+ * group split).
+ *
+ * Asymmetric padding (DLPrimitives Blog, "TensorFlow": TensorFlow's "same"
+ * padding can put one more zero row or column at the end of an axis than at
+ * its start, which cuDNN cannot express). pad_h / pad_w are the zero rows at
+ * the top and columns at the left; the bottom and right get pad_h +
+ * pad_h_extra and pad_w + pad_w_extra. The end padding only sets Ho and Wo;
+ * no padded copy of x is made. A zero-initialised pad_*_extra gives the
+ * symmetric padding of the formula above.
  */
 typedef struct gconv_desc {
     int64_t N, C, H, W;
@@ -68,6 +77,7 @@ typedef struct gconv_desc {
     int64_t pad_h, pad_w;
     int64_t dil_h, dil_w;
     int64_t groups;
+    int64_t pad_h_extra, pad_w_extra;  /* end padding minus start padding (0: symmetric) */
 } gconv_desc;
 
 typedef enum gconv_status {

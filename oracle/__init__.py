@@ -19,6 +19,9 @@ Ops (names follow the Torch module passes the pages discuss):
                                           Broadcast Reduce": sum over 0,2,3)
   fwd(..., relu=True)     -> max(y, 0)   (an element-wise operation on the
                                           forward output, the same section)
+
+``padding`` is an int, a pair (pad_h, pad_w), or (top, bottom, left, right):
+the end padding may differ from the start (DLPrimitives Blog, "TensorFlow").
 """
 from __future__ import annotations
 
@@ -43,7 +46,8 @@ class OracleError(ValueError):
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "N", "C", "H", "W", "K", "kh", "kw",
-        "stride_h", "stride_w", "pad_h", "pad_w", "dil_h", "dil_w", "groups")]
+        "stride_h", "stride_w", "pad_h", "pad_w", "dil_h", "dil_w", "groups",
+        "pad_h_end", "pad_w_end")]
 
 
 def build(force: bool = True) -> str:
@@ -100,11 +104,20 @@ def _pair(v):
     return int(v), int(v)
 
 
+def _pads(padding):
+    """int, (pad_h, pad_w), or (top, bottom, left, right) -> (top, left, bottom, right)."""
+    if isinstance(padding, (tuple, list)) and len(padding) == 4:
+        t, b, l, r = (int(v) for v in padding)
+        return t, l, b, r
+    ph, pw = _pair(padding)
+    return ph, pw, ph, pw
+
+
 def _desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups) -> _Desc:
     sh, sw = _pair(stride)
-    ph, pw = _pair(padding)
+    ph, pw, pb, pr = _pads(padding)
     dh, dw = _pair(dilation)
-    return _Desc(N, C, H, W, K, kh, kw, sh, sw, ph, pw, dh, dw, int(groups))
+    return _Desc(N, C, H, W, K, kh, kw, sh, sw, ph, pw, dh, dw, int(groups), pb, pr)
 
 
 def _f64(a):

@@ -43,13 +43,19 @@
 typedef struct {
     int64_t N, C, H, W, K, kh, kw;
     int64_t stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, groups;
+    /* Zero rows below the input and columns right of it. pad_h / pad_w are
+     * the rows above and columns left of it, the only ones that shift the tap
+     * coordinates below; the end padding only lengthens the output (the
+     * DLPrimitives Blog, "TensorFlow": TensorFlow's "same" padding may differ
+     * at the start and the end of an axis). */
+    int64_t pad_h_end, pad_w_end;
 } oracle_desc;
 
-/* Output extent along one axis: floor((in + 2p - d(k-1) - 1) / s) + 1, or 0
- * when the dilated kernel does not fit (a negative numerator). */
-static int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d)
+/* Output extent along one axis: floor((in + p0 + p1 - d(k-1) - 1) / s) + 1,
+ * or 0 when the dilated kernel does not fit (a negative numerator). */
+static int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p0, int64_t p1, int64_t d)
 {
-    int64_t num = in + 2 * p - d * (k - 1) - 1;
+    int64_t num = in + p0 + p1 - d * (k - 1) - 1;
     if (num < 0) return 0;
     return num / s + 1;
 }
@@ -63,9 +69,10 @@ int oracle_output_dims(const oracle_desc* d, int64_t* Ho, int64_t* Wo)
         return 1;
     if (d->stride_h < 1 || d->stride_w < 1 || d->dil_h < 1 || d->dil_w < 1) return 1;
     if (d->pad_h < 0 || d->pad_w < 0 || d->groups < 1) return 1;
+    if (d->pad_h_end < 0 || d->pad_w_end < 0) return 1;
     if (d->C % d->groups != 0 || d->K % d->groups != 0) return 2;
-    *Ho = out_extent(d->H, d->kh, d->stride_h, d->pad_h, d->dil_h);
-    *Wo = out_extent(d->W, d->kw, d->stride_w, d->pad_w, d->dil_w);
+    *Ho = out_extent(d->H, d->kh, d->stride_h, d->pad_h, d->pad_h_end, d->dil_h);
+    *Wo = out_extent(d->W, d->kw, d->stride_w, d->pad_w, d->pad_w_end, d->dil_w);
     if (*Ho < 1 || *Wo < 1) return 1;
     return 0;
 }

@@ -35,8 +35,28 @@ def random_descs(seed, count, max_hw=9, max_k=4, max_cg=3, max_kg=3, max_g=3, ma
     return out
 
 
+def asym_descs(seed, count, max_pad=3, **kw):
+    """Random descriptors whose end padding (keys pb, pr: rows below, columns right)
+    differs from the start padding (ph, pw) on at least one axis."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for d in random_descs(seed, 4 * count, **kw):
+        d["pb"], d["pr"] = int(rng.integers(0, max_pad + 1)), int(rng.integers(0, max_pad + 1))
+        if (d["pb"], d["pr"]) == (d["ph"], d["pw"]):
+            continue
+        if (d["H"] + d["ph"] + d["pb"] >= d["dh"] * (d["kh"] - 1) + 1 and
+                d["W"] + d["pw"] + d["pr"] >= d["dw"] * (d["kw"] - 1) + 1):
+            out.append(d)
+        if len(out) == count:
+            break
+    return out
+
+
 def conv_kwargs(d):
-    return dict(stride=(d["sh"], d["sw"]), padding=(d["ph"], d["pw"]),
+    """stride/padding/dilation/groups keywords; padding is (top, bottom, left, right)
+    when the descriptor carries end padding."""
+    pad = (d["ph"], d["pb"], d["pw"], d["pr"]) if "pb" in d else (d["ph"], d["pw"])
+    return dict(stride=(d["sh"], d["sw"]), padding=pad,
                 dilation=(d["dh"], d["dw"]), groups=d["G"])
 
 

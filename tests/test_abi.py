@@ -43,7 +43,7 @@ def test_desc_layout_matches_header():
     body = re.search(r"typedef struct gconv_desc \{(.*?)\} gconv_desc;", text, re.S).group(1)
     fields = re.findall(r"(\w+)(?=[,;])", re.sub(r"int64_t", "", body))
     assert fields == [f for f, _ in B.gconv_desc._fields_]
-    assert ctypes.sizeof(B.gconv_desc) == 14 * 8
+    assert ctypes.sizeof(B.gconv_desc) == 16 * 8
 
 
 def test_output_dims_match_oracle_random():
@@ -54,6 +54,35 @@ def test_output_dims_match_oracle_random():
         assert B.gconv_output_dims(desc) == oracle.output_dims(
             d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], (d["sh"], d["sw"]),
             (d["ph"], d["pw"]), (d["dh"], d["dw"]), d["G"])
+
+
+def test_output_dims_asymmetric_match_oracle():
+    from cases import asym_descs
+    for d in asym_descs(2100, 200, max_hw=40, max_k=7, strides=(1, 2, 3, 4), pads=(0, 1, 2, 3),
+                        dils=(1, 2, 3)):
+        pad = (d["ph"], d["pb"], d["pw"], d["pr"])
+        desc = B.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"],
+                           (d["sh"], d["sw"]), pad, (d["dh"], d["dw"]), d["G"])
+        assert (desc.pad_h_extra, desc.pad_w_extra) == (d["pb"] - d["ph"], d["pr"] - d["pw"])
+        assert B.gconv_output_dims(desc) == oracle.output_dims(
+            d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], (d["sh"], d["sw"]),
+            pad, (d["dh"], d["dw"]), d["G"])
+
+
+def test_same_padding_gives_ceil_extent():
+    """TensorFlow's "same" padding (DLPrimitives Blog, "TensorFlow"): the output
+    extent is ceil(H / stride), the end gets the odd padding row or column, and the
+    library and the oracle agree on the resulting extents."""
+    for H in range(1, 30):
+        for k in range(1, 8):
+            for s_ in (1, 2, 3, 4):
+                for dil in (1, 2, 3):
+                    t, b, l, r = B.same_padding(H, H + 1, k, k, s_, dil)
+                    assert 0 <= b - t <= 1 and 0 <= r - l <= 1
+                    desc = B.make_desc(1, 2, H, H + 1, 2, k, k, s_, (t, b, l, r), dil, 1)
+                    want = (-(-H // s_), -(-(H + 1) // s_))
+                    assert B.gconv_output_dims(desc) == want
+                    assert oracle.output_dims(1, 2, H, H + 1, 2, k, k, s_, (t, b, l, r), dil, 1) == want
 
 
 def test_output_dims_golden_configs():
@@ -72,6 +101,8 @@ def test_output_dims_golden_configs():
     (dict(N=-1), 2),
     (dict(H=0), 2),
     (dict(groups=0), 3),
+    (dict(padding=(0, -1, 0, 0)), 2),
+    (dict(padding=(1, 1, 2, -1)), 2),
 ])
 def test_invalid_descriptors_rejected_before_launch(bad, status):
     args = dict(N=2, C=8, H=7, W=7, K=8, kh=3, kw=3, stride=1, padding=0, dilation=1, groups=2)
@@ -158,3 +189,17 @@ def test_pointwise_routing():
         assert B.gconv_select_path(desc, B.OP_FWD) == B.PATH_POINTWISE
     finally:
         B.gconv_set_path_override(B.PATH_AUTO)
+
+
+def test_workload_output_shapes():
+    """Every workload's stated dy shape is the output extent of its descriptor,
+    by the library and by the oracle (the asymmetric "same" padding included)."""
+    from grouped_convolution_amd.workloads import WORKLOADS
+    for wl in WORKLOADS.values():
+        N, C, H, W = wl.x_shape
+        K, _, kh, kw = wl.w_shape
+        desc = B.make_desc(N, C, H, W, K, kh, kw, wl.stride, wl.padding, wl.dilation, wl.groups)
+        assert B.gconv_output_dims(desc) == tuple(wl.dy_shape[2:]), wl.name
+        assert oracle.output_dims(N, C, H, W, K, kh, kw, wl.stride, wl.padding, wl.dilation,
+                                  wl.groups) == tuple(wl.dy_shape[2:]), wl.name
+        assert wl.dy_shape[:2] == (N, K), wl.name

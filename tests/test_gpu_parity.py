@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from cases import conv_kwargs, fits, random_descs, tensors
+from cases import asym_descs, conv_kwargs, fits, random_descs, tensors
 from gpu_util import check, dev, gather, gpu_all_ops, sample_indices, say
 from grouped_convolution_amd.workloads import WORKLOAD_ORDER, WORKLOADS, draw, make_inputs
 
@@ -326,6 +326,93 @@ def test_relu_epilogue(case):
     assert (y_relu >= 0).all()
 
 
+# ----------------------------------------------------------------- asymmetric padding
+
+@pytest.mark.parametrize("seed", range(2))
+def test_asymmetric_padding_every_path(seed):
+    """End padding that differs from the start padding (DLPrimitives Blog,
+    "TensorFlow"), random descriptors, every kernel family that takes them."""
+    descs = asym_descs(70 + seed, 16, max_hw=12, max_k=5, max_cg=6, max_kg=6, max_g=4)
+    for d in descs:
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 700 + seed)
+        y_ref, _ = oracle.fwd(x, w, b, **kw)
+        dy = draw(("normal", 1.0), y_ref.shape, 710 + seed)
+        ref = oracle_all(x, w, b, dy, kw)
+        covered = set()
+        for path in ALL_PATHS:
+            say("asym desc %s path %s" % (d, G.PATH_NAMES[path]))
+            covered |= set(compare_full("%s %s" % (G.PATH_NAMES[path], d),
+                                        run_path(path, x, w, b, dy, kw), ref))
+        assert covered == set(OPS)
+
+
+def _same(H, W, k, s):
+    t, b, l, r = G.same_padding(H, W, k, k, s)
+    return dict(ph=t, pb=b, pw=l, pr=r)
+
+
+ASYM_CASES = [
+    # TensorFlow "same" padding at stride 2 (one more zero row and column at the end) on the
+    # MFMA kernels, 3x3 and 5x5 ...
+    (dict(N=2, C=32, K=32, H=20, W=20, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=1, **_same(20, 20, 3, 2)),
+     {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "igemm"}),
+    (dict(N=2, C=32, K=32, H=21, W=20, kh=5, kw=5, sh=2, sw=2, dh=1, dw=1, G=1, **_same(21, 20, 5, 2)),
+     {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "igemm"}),
+    # ... unequal start and end pads at stride 1, two groups
+    (dict(N=2, C=32, K=48, H=13, W=17, kh=3, kw=3, sh=1, sw=1, ph=0, pb=2, pw=1, pr=0, dh=1, dw=1,
+          G=2), {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "igemm"}),
+    # small-group row tile: no top pad, two right; and the widest row (62 + 0 + 2 columns)
+    (dict(N=3, C=16, K=16, H=14, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pb=0, pw=0, pr=2, dh=1, dw=1,
+          G=4), {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    (dict(N=2, C=8, K=8, H=5, W=62, kh=3, kw=3, sh=1, sw=1, ph=0, pb=1, pw=0, pr=2, dh=1, dw=1,
+          G=2), {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # small-group general kernels at stride 2 with "same" padding
+    (dict(N=2, C=32, K=32, H=15, W=14, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=8, **_same(15, 14, 3, 2)),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # depthwise row kernels (forward, gradInput, gradWeight) and depthwise "same" at stride 2
+    (dict(N=3, C=8, K=8, H=17, W=30, kh=3, kw=3, sh=1, sw=1, ph=0, pb=1, pw=2, pr=0, dh=1, dw=1,
+          G=8), {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    (dict(N=2, C=8, K=16, H=16, W=18, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=8, **_same(16, 18, 3, 2)),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "direct"}),
+    # LDS-tiled direct kernels (20 in / 3 out per group)
+    (dict(N=2, C=20, K=6, H=10, W=11, kh=3, kw=3, sh=1, sw=1, ph=2, pb=0, pw=0, pr=1, dh=1, dw=1,
+          G=2), {"fwd": "direct", "bwd_data": "direct", "bwd_filter": "direct"}),
+    # an even kernel, whose "same" padding is always asymmetric
+    (dict(N=2, C=8, K=8, H=9, W=10, kh=4, kw=4, sh=1, sw=1, dh=1, dw=1, G=1, **_same(9, 10, 4, 1)),
+     {"fwd": "direct", "bwd_data": "direct", "bwd_filter": "direct"}),
+    # 1x1 with end padding: the extra output rows and columns hold the bias only, so it
+    # leaves the pointwise GEMM (whose output planes are H x W)
+    (dict(N=2, C=16, K=24, H=10, W=9, kh=1, kw=1, sh=1, sw=1, ph=0, pb=1, pw=0, pr=2, dh=1, dw=1,
+          G=1), {"fwd": "direct", "bwd_data": "direct", "bwd_filter": "direct"}),
+    # kernel == input with end padding below the stride: still one output, FC mode
+    (dict(N=5, C=8, K=6, H=3, W=3, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1,
+          G=1), {"fwd": "fc", "bwd_data": "fc", "bwd_filter": "fc"}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ASYM_CASES)))
+def test_asymmetric_padding_cases(case):
+    """Asymmetric padding on the dispatcher's own choice of family (asserted):
+    normal data to the tolerance, then integer data bit for bit."""
+    d, paths = ASYM_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
+    for op, name in paths.items():
+        chosen = G.gconv_select_path(desc, getattr(G, "OP_" + op.upper()))
+        assert G.PATH_NAMES[chosen] == name, (d, op, G.PATH_NAMES[chosen])
+    say("asym case %s" % d)
+    x, w, b = tensors(d, 2100 + case)
+    y_ref, _ = oracle.fwd(x, w, b, **kw)
+    dy = draw(("normal", 1.0), y_ref.shape, 2110 + case)
+    compare_full("asym %s" % d, gpu_all_ops(x, w, b, dy, **kw), oracle_all(x, w, b, dy, kw))
+    xi, wi, bi = tensors(d, 2200 + case, dist=("int", -3, 3))
+    dyi = draw(("int", -3, 3), y_ref.shape, 2210 + case)
+    got = gpu_all_ops(xi, wi, bi, dyi, **kw)
+    for g, (val, _) in zip(got, oracle_all(xi, wi, bi, dyi, kw)):
+        assert np.array_equal(g.cpu().numpy().astype(np.float64), val), d
+
+
 def test_fc_1x1_on_1x1_is_linear():
     """A 1x1 convolution of a 1x1 input (the Linear(128, 32) case of the
     cudnn.torch issue) runs the GEMM path and matches the oracle."""
@@ -363,7 +450,7 @@ def test_ragged_shapes_span_several_tiles():
 # ----------------------------------------------------------------- the five workloads
 
 REDUCED_BATCH = {"tiny_grouped": 2, "dense3x3": 2, "alexnet_conv2": 2, "resnext_32x4d": 3,
-                 "fc_mode": 24, "resnext_1x1": 2, "mobilenet_dw": 2}
+                 "fc_mode": 24, "resnext_1x1": 2, "mobilenet_dw": 2, "mobilenet_dw_s2_same": 2}
 
 
 def wl_kwargs(wl):

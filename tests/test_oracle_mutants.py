@@ -49,8 +49,12 @@ MUTANTS = [
     ("bwd_bias_drops_column", "const double v = dy[((n * d->K + k) * Ho + ho) * Wo + wo];",
      "const double v = wo ? dy[((n * d->K + k) * Ho + ho) * Wo + wo] : 0.0;", 0),
     ("extent_ceil", "return num / s + 1;", "return (num + s - 1) / s + 1;", 0),
-    ("extent_off_by_one", "int64_t num = in + 2 * p - d * (k - 1) - 1;",
-     "int64_t num = in + 2 * p - d * (k - 1);", 0),
+    ("extent_off_by_one", "int64_t num = in + p0 + p1 - d * (k - 1) - 1;",
+     "int64_t num = in + p0 + p1 - d * (k - 1);", 0),
+    ("extent_end_pad_ignored", "int64_t num = in + p0 + p1 - d * (k - 1) - 1;",
+     "int64_t num = in + 2 * p0 - d * (k - 1) - 1;", 0),
+    ("extent_end_pads_swapped", "d->pad_h, d->pad_h_end, d->dil_h);",
+     "d->pad_h, d->pad_w_end, d->dil_h);", 0),
 ]
 
 
@@ -86,6 +90,7 @@ def _battery():
     run("bias", pins.test_bias_closed_forms)
     run("abs_sum", pins.test_abs_sum_is_sum_of_abs_products)
     run("closed_forms", closed_forms)
+    run("asym_explicit_pad", lambda: pins.test_asymmetric_padding_equals_explicit_zero_pad(0))
     return failed
 
 

@@ -21,7 +21,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from cases import conv_kwargs, random_descs, tensors
+from cases import asym_descs, conv_kwargs, random_descs, tensors
 from grouped_convolution_amd.workloads import draw
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -425,3 +425,74 @@ def test_relu_epilogue_invariants():
         ax, aw, ab = np.abs(x), np.abs(w), np.abs(b)
         assert np.array_equal(oracle.fwd(ax, aw, ab, relu=True, **kw)[0], oracle.fwd(ax, aw, ab, **kw)[0])
         assert not np.any(oracle.fwd(ax, -aw, -ab, relu=True, **kw)[0])
+
+
+# --------------------------------------------------------------------------- asymmetric padding
+
+def _pad_input(x, d):
+    return np.pad(x, ((0, 0), (0, 0), (d["ph"], d["pb"]), (d["pw"], d["pr"])))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_asymmetric_padding_equals_explicit_zero_pad(seed):
+    """Start and end padding that differ (DLPrimitives Blog, "TensorFlow": what
+    TensorFlow does by padding the input by hand) equal the unpadded convolution of
+    the input padded with those zero rows and columns: same forward output (and
+    magnitudes), same gradWeight, and gradInput is the padded input's gradInput
+    with the padding cut away. Skipped taps and added zeros leave every fp64 sum
+    unchanged, so the equality is exact."""
+    for d in asym_descs(300 + seed, 12):
+        kw = conv_kwargs(d)
+        kw0 = dict(kw, padding=0)
+        x, w, b = tensors(d, 5000 + seed)
+        xp = _pad_input(x, d)
+        y, ya = oracle.fwd(x, w, b, **kw)
+        y0, y0a = oracle.fwd(xp, w, b, **kw0)
+        assert np.array_equal(y, y0) and np.array_equal(ya, y0a), d
+        dy = draw(("normal", 1.0), y.shape, 5003 + seed)
+        dx, _ = oracle.bwd_data(dy, w, x.shape, **kw)
+        dx0, _ = oracle.bwd_data(dy, w, xp.shape, **kw0)
+        assert np.array_equal(dx, dx0[:, :, d["ph"]:d["ph"] + d["H"], d["pw"]:d["pw"] + d["W"]]), d
+        dw, _ = oracle.bwd_filter(x, dy, w.shape, **kw)
+        dw0, _ = oracle.bwd_filter(xp, dy, w.shape, **kw0)
+        assert np.array_equal(dw, dw0), d
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_asymmetric_padding_matches_torch(seed):
+    """torch CPU float64: conv2d of F.pad(x, (left, right, top, bottom)) and its
+    autograd gradients (through the pad) against the oracle with end padding."""
+    for d in asym_descs(400 + seed, 10):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 6000 + seed)
+        xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+        wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+        bt = torch.tensor(b, dtype=torch.float64, requires_grad=True)
+        yt = F.conv2d(F.pad(xt, (d["pw"], d["pr"], d["ph"], d["pb"])), wt, bt, stride=kw["stride"],
+                      dilation=kw["dilation"], groups=d["G"])
+        dy = draw(("normal", 1.0), tuple(yt.shape), 6003 + seed)
+        gx, gw, gb = torch.autograd.grad(yt, [xt, wt, bt], torch.tensor(dy, dtype=torch.float64))
+        (y, ya), (dx, dxa), (dw, dwa), (db, dba) = run_oracle_all(x, w, b, dy, kw)
+        assert y.shape == tuple(yt.shape), d
+        assert close(y, yt.detach().numpy(), ya) and close(dx, gx.numpy(), dxa), d
+        assert close(dw, gw.numpy(), dwa) and close(db, gb.numpy(), dba), d
+
+
+def test_asymmetric_padding_output_extents():
+    """Ho = floor((H + top + bottom - d(k-1) - 1)/s) + 1 by counting, for every
+    start and end padding up to 3: the number of window origins h0 = ho*s - top
+    whose last tap h0 + d(k-1) stays below H + bottom."""
+    for H in range(1, 12):
+        for k in range(1, 5):
+            for s_ in (1, 2, 3):
+                for dil in (1, 2):
+                    for top in range(4):
+                        for bot in range(4):
+                            count = sum(1 for ho in range(64)
+                                        if ho * s_ - top + dil * (k - 1) < H + bot)
+                            try:
+                                got = oracle.output_dims(1, 1, H, 1, 1, k, 1, (s_, 1),
+                                                         (top, bot, 0, 0), (dil, 1), 1)[0]
+                            except oracle.OracleError:
+                                got = 0
+                            assert got == count, (H, k, s_, dil, top, bot)
