@@ -271,10 +271,14 @@ __global__ void __launch_bounds__(256) sg_conv_row64_kernel(SgArgs a)
 // although each group has a single input plane, and every output is a plain
 // 9-tap FMA chain on the vector ALUs (the 4x4 MFMA blocks would be at most a
 // quarter used here). Same tile as above: one 64-float LDS row per input row,
-// lane = pixel, taps at immediate offsets.
+// lane = pixel, taps at immediate offsets from the pixel's address.
+//   S = 2: forward stride 2; output (r, wo) reads LDS rows 2r.., columns 2wo..
+//   a.uh, a.uw > 1 (unit stride only): the input is the virtually upsampled
+//     dy of a strided gradInput; its rows and columns that are not multiples
+//     of the factor are loaded as zeros (out-of-range DMA, no memory traffic).
 constexpr int kDwGroups = 4;
 
-template <int MQ, bool FLIP>
+template <int MQ, bool FLIP, int S>
 __global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
 {
     constexpr int T = 9, GB = kDwGroups;
@@ -293,22 +297,37 @@ __global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
     const int g0 = gb * GB, ng = min(GB, a.G - g0);
     const int ho0 = band * a.R;
     const int rows = min(a.R, a.Hout - ho0);
-    const int hbase = ho0 - a.ph;
+    const int hbase = ho0 * S - a.ph;
 
-    // The groups' input planes are consecutive channels of image n.
-    const float* in_n = a.in + ((size_t)n * a.Cin_tot + g0) * a.Hin * a.Win;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_n, (uint32_t)ng * a.Hin * a.Win * 4u);
+    // The groups' input planes are consecutive channels of image n (stored
+    // planes of Hr x Wr; equal to Hin x Win unless upsampled).
+    const int HWr = a.Hr * a.Wr;
+    const float* in_n = a.in + ((size_t)n * a.Cin_tot + g0) * HWr;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(in_n, (uint32_t)ng * HWr * 4u);
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(a.wgt + (size_t)g0 * a.w_gstride, (uint32_t)ng * a.w_gstride * 4u);
+    // Only gradInput reads an upsampled input.
+    const bool up = FLIP && (a.uh != 1 || a.uw != 1);
     const int wcol = lane - a.pw;
-    const bool colok = (unsigned)wcol < (unsigned)a.Win;
+    bool colok = (unsigned)wcol < (unsigned)a.Win;
+    int wsrc = wcol;
+    if (up) {
+        wsrc = colok ? wcol / a.uw : 0;
+        colok = colok && wsrc * a.uw == wcol;
+    }
+    const int lrows = (rows - 1) * S + 3;
 #pragma unroll
     for (int gi = 0; gi < GB; ++gi)
-        for (int r = wave; r < a.LR; r += 4) {
+        for (int r = wave; r < lrows; r += 4) {
             const int h = hbase + r;
-            const bool ok = colok && gi < ng && (unsigned)h < (unsigned)a.Hin;
+            bool ok = colok && gi < ng && (unsigned)h < (unsigned)a.Hin;
+            int hs = h;
+            if (up) {
+                hs = ok ? h / a.uh : 0;
+                ok = ok && hs * a.uh == h;
+            }
             load_lds64(rx, lds + gi * plane + r * 64,
-                       ok ? (uint32_t)((gi * a.Hin + h) * a.Win + wcol) * 4u : kOOB);
+                       ok ? (uint32_t)((gi * a.Hr + hs) * a.Wr + wsrc) * 4u : kOOB);
         }
     for (int e = tid; e < GB * MQ * T; e += 256) {
         const int gi = e / (MQ * T), o = (e / T) % MQ, t = e % T;
@@ -333,7 +352,7 @@ __global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
             const int pl = s0 + lane;
             const int pc = min(pl, npix - 1);
             const int r = (int)fastdiv((uint32_t)pc, a.div_Wout);
-            const float* xb = lds + gi * plane + r * 64 + (pc - r * a.Wout);
+            const float* xb = lds + gi * plane + r * (S * 64) + (pc - r * a.Wout) * S;
             float xv[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) xv[t] = xb[(t / 3) * 64 + t % 3];
@@ -589,6 +608,8 @@ __global__ void __launch_bounds__(256) sg_wgrad_row64_kernel(SgWArgs a)
 // group and lane), so no arithmetic goes to absent channels. A workgroup owns
 // a group block and a run of images, walks their bands, and writes one
 // partial [o][tap] per group; sg_dw_wgrad_reduce adds the runs in order.
+// S = 2 (stride 2): output (r, wo) pairs with LDS x rows 2r.., columns 2wo..;
+// lanes past the output width read the last output's x (their dy is 0).
 constexpr int kDwwGroups = 4;
 
 struct SgDwWArgs {
@@ -596,11 +617,12 @@ struct SgDwWArgs {
     const float* dy;
     float* ws;
     int N, C, H, W, K, Ho, Wo, G, Kg, ph, pw;
+    int S;                  // stride (both axes)
     int R, run, nruns;      // band rows, images per workgroup, workgroups per group block
-    int plane, dplane;      // x plane ((R+2)*64 + 8) and dy plane (R*64 + 8), floats
+    int plane, dplane;      // x plane (((R-1)*S+3)*64 + 8) and dy plane (R*64 + 8), floats
 };
 
-template <int MQ>
+template <int MQ, int S>
 __global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
 {
     constexpr int T = 9, GB = kDwwGroups;
@@ -619,7 +641,8 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
     const bool colok = (unsigned)wcol < (unsigned)a.W;
     // Lanes past the image width read up to two floats beyond the last x row of
     // a plane (times dy = 0): keep the pad after each plane zero.
-    if (tid < GB * 8) lds[(tid >> 3) * a.plane + (a.R + 2) * 64 + (tid & 7)] = 0.f;
+    if (S == 1 && tid < GB * 8) lds[(tid >> 3) * a.plane + (a.R + 2) * 64 + (tid & 7)] = 0.f;
+    const int xcol = S == 1 ? lane : min(lane, a.Wo - 1) * S;
 
     float acc[GB][MQ][T];
 #pragma unroll
@@ -636,11 +659,12 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, (uint32_t)ng * a.Kg * a.Ho * a.Wo * 4u);
         for (int ho0 = 0; ho0 < a.Ho; ho0 += a.R) {
             const int rows = min(a.R, a.Ho - ho0);
-            const int hb = ho0 - a.ph;
+            const int hb = ho0 * S - a.ph;
+            const int lrows = (rows - 1) * S + 3;
             __syncthreads();  // every wave is done with the previous band
 #pragma unroll
             for (int gi = 0; gi < GB; ++gi)
-                for (int r = wave; r < rows + 2; r += 4) {
+                for (int r = wave; r < lrows; r += 4) {
                     const int h = hb + r;
                     const bool ok = colok && gi < ng && (unsigned)h < (unsigned)a.H;
                     load_lds64(rx, lds + gi * a.plane + r * 64,
@@ -659,7 +683,7 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
             for (int r = wave; r < rows; r += 4) {
 #pragma unroll
                 for (int gi = 0; gi < GB; ++gi) {
-                    const float* xr = lds + gi * a.plane + r * 64 + lane;
+                    const float* xr = lds + gi * a.plane + r * (S * 64) + xcol;
                     float xv[T];
 #pragma unroll
                     for (int t = 0; t < T; ++t) xv[t] = xr[(t / 3) * 64 + t % 3];
@@ -692,8 +716,8 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
     for (int e = tid; e < GB * MQ * T; e += 256) {
         const int gi = e / (MQ * T);
         if (gi >= ng) continue;
-        constexpr int S = GB * MQ * T;
-        const float v = ((red[e] + red[S + e]) + red[2 * S + e]) + red[3 * S + e];
+        constexpr int NS = GB * MQ * T;
+        const float v = ((red[e] + red[NS + e]) + red[2 * NS + e]) + red[3 * NS + e];
         a.ws[((size_t)chunk * a.G + g0) * (MQ * T) + e] = v;
     }
 }
@@ -838,10 +862,22 @@ bool sg_run_row64(const SgProblem& p, hipStream_t st)
     return false;
 }
 
-template <int MQ, bool FLIP>
+template <int MQ, bool FLIP, int S>
 void sg_dw_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
 {
-    hipLaunchKernelGGL((sg_dw_row64_kernel<MQ, FLIP>), dim3(blocks), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((sg_dw_row64_kernel<MQ, FLIP, S>), dim3(blocks), dim3(256), lds, st, a);
+}
+
+// The depthwise row tile: 3x3, dilation 1, one input channel per group;
+// stride 1 (also over a virtually upsampled input: strided gradInput) or a
+// forward stride of 2; every column the outputs read lies in the 64-float
+// LDS row that starts pw columns left of the input.
+bool sg_dw_ok(const SgProblem& p)
+{
+    if (!(p.kh == 3 && p.kw == 3 && p.dh == 1 && p.dw == 1 && p.Cin_g == 1)) return false;
+    if (!(p.sh == p.sw && (p.sh == 1 || (p.sh == 2 && p.uh == 1 && p.uw == 1)))) return false;
+    if (p.uh < 1 || p.uw < 1) return false;
+    return (p.Wout - 1) * p.sw + 2 <= 63 && p.ph >= 0 && p.pw >= 0 && p.pw <= 2;
 }
 
 // One input channel per group (depthwise forward; depthwise gradInput with a
@@ -849,19 +885,25 @@ void sg_dw_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
 bool sg_run_dw(const SgProblem& p, hipStream_t st)
 {
     const int MQ = p.Cout_g <= 1 ? 1 : p.Cout_g <= 2 ? 2 : p.Cout_g <= 4 ? 4 : 8;
+    const int S = p.sh;
     SgArgs a;
     a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
     a.relu = p.relu;
     a.N = p.N; a.G = p.G;
     a.Cin_tot = p.Cin_tot; a.Cin_g = p.Cin_g; a.Hin = p.Hin; a.Win = p.Win;
     a.Cout_tot = p.Cout_tot; a.Cout_g = p.Cout_g; a.Hout = p.Hout; a.Wout = p.Wout;
-    a.sh = 1; a.sw = 1; a.dh = 1; a.dw = 1; a.ph = p.ph; a.pw = p.pw;
+    a.sh = S; a.sw = S; a.dh = 1; a.dw = 1; a.ph = p.ph; a.pw = p.pw;
     a.w_so = p.w_so; a.w_sr = p.w_sr; a.w_gstride = p.w_gstride;
-    a.uh = 1; a.uw = 1; a.Hr = p.Hin; a.Wr = p.Win;
-    const int nb = (p.Hout + 15) / 16;
+    a.uh = p.uh; a.uw = p.uw; a.Hr = p.Hr; a.Wr = p.Wr;
+    // Bands of about 16 input rows.
+#ifndef GCONV_DW_S2_RMAX
+#define GCONV_DW_S2_RMAX 14
+#endif
+    const int rmax = S == 1 ? 16 : GCONV_DW_S2_RMAX;
+    const int nb = (p.Hout + rmax - 1) / rmax;
     a.R = (p.Hout + nb - 1) / nb;
     a.nbands = (p.Hout + a.R - 1) / a.R;
-    a.LR = a.R + 2;
+    a.LR = (a.R - 1) * S + 3;
     a.LW = 64;
     a.plane = a.LR * 64;
     a.div_plane = make_fastdiv((uint32_t)a.plane);
@@ -873,8 +915,9 @@ bool sg_run_dw(const SgProblem& p, hipStream_t st)
     const size_t lds = ((size_t)kDwGroups * a.plane + (size_t)kDwGroups * MQ * 9) * 4;
 #define SG_CASE(mq)                                                             \
     if (MQ == mq) {                                                             \
-        if (p.flip) sg_dw_launch<mq, true>(a, (int)blocks, lds, st);            \
-        else sg_dw_launch<mq, false>(a, (int)blocks, lds, st);                  \
+        if (S == 2) sg_dw_launch<mq, false, 2>(a, (int)blocks, lds, st);        \
+        else if (p.flip) sg_dw_launch<mq, true, 1>(a, (int)blocks, lds, st);    \
+        else sg_dw_launch<mq, false, 1>(a, (int)blocks, lds, st);               \
         return true;                                                            \
     }
     SG_CASE(1) SG_CASE(2) SG_CASE(4) SG_CASE(8)
@@ -886,7 +929,11 @@ bool sg_run(const SgProblem& p, hipStream_t st)
 {
     if (!sg_problem_ok(p)) return false;
 #ifndef GCONV_SG_NO_DW
-    if (p.Cin_g == 1 && sg_row64_ok(p)) return sg_run_dw(p, st);
+#ifdef GCONV_SG_NO_DW_S2
+    if (sg_dw_ok(p) && p.sh == 1) return sg_run_dw(p, st);
+#else
+    if (sg_dw_ok(p) && !(p.flip && p.sh != 1)) return sg_run_dw(p, st);
+#endif
 #endif
 #ifndef GCONV_SG_NO_ROW64
     if (sg_row64_ok(p)) return sg_run_row64(p, st);
@@ -1027,24 +1074,38 @@ bool sgw_plan(const Shape& s, SgWArgs* out, bool* row64 = nullptr)
 
 }  // namespace
 
-// Depthwise gradWeight on the row tile: 3x3, stride and dilation 1, one input
-// and at most 2 output channels per group, rows of at most 62 outputs.
+// Depthwise gradWeight on the row tile: 3x3, dilation 1, stride 1 or 2, one
+// input and at most 2 output channels per group; every x column the outputs
+// read lies in the 64-float LDS row (rows of at most 62 outputs at stride 1,
+// 31 at stride 2).
 bool sg_dw_wgrad_plan(const Shape& s, SgDwWArgs* out, int* mq)
 {
-    if (!(s.kh == 3 && s.kw == 3 && s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1)) return false;
-    if (s.Cg != 1 || s.Kg > 2 || s.N < 1 || s.Wo + 2 > 64 || s.ph < 0 || s.pw < 0 || s.pw > 2) return false;
+    if (!(s.kh == 3 && s.kw == 3 && s.dh == 1 && s.dw == 1)) return false;
+    if (!(s.sh == s.sw && (s.sh == 1 || s.sh == 2))) return false;
+    if (s.Cg != 1 || s.Kg > 2 || s.N < 1 || (s.Wo - 1) * s.sw + 2 > 63 || s.ph < 0 || s.pw < 0 ||
+        s.pw > 2)
+        return false;
     if ((int64_t)kDwwGroups * s.H * s.W * 4 >= (int64_t(1) << 30)) return false;
     if ((int64_t)kDwwGroups * s.Kg * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
     SgDwWArgs a{};
     a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
     a.G = s.G; a.Kg = s.Kg; a.ph = s.ph; a.pw = s.pw;
-    const int nb = (s.Ho + 15) / 16;
+    a.S = s.sh;
+    // Bands of about 16 x rows.
+#ifndef GCONV_DWW_S2_RMAX
+#define GCONV_DWW_S2_RMAX 8
+#endif
+#ifndef GCONV_DWW_WGS
+#define GCONV_DWW_WGS 2048
+#endif
+    const int rmax = a.S == 1 ? 16 : GCONV_DWW_S2_RMAX;
+    const int nb = (s.Ho + rmax - 1) / rmax;
     a.R = (s.Ho + nb - 1) / nb;
     const int ngb = (s.G + kDwwGroups - 1) / kDwwGroups;
-    const int runs = std::max(1, std::min(s.N, 1024 / std::max(1, ngb)));
+    const int runs = std::max(1, std::min(s.N, GCONV_DWW_WGS / std::max(1, ngb)));
     a.run = (s.N + runs - 1) / runs;
     a.nruns = (s.N + a.run - 1) / a.run;
-    a.plane = (a.R + 2) * 64 + 8;
+    a.plane = ((a.R - 1) * a.S + 3) * 64 + 8;
     a.dplane = a.R * 64 + 8;
     if ((int64_t)a.nruns * ngb >= (1 << 30)) return false;
     if (out) *out = a;
@@ -1101,8 +1162,13 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
         const int blocks = ngb * da.nruns;
         const size_t lds = std::max((size_t)kDwwGroups * da.plane + (size_t)kDwwGroups * mq * da.dplane,
                                     (size_t)4 * kDwwGroups * mq * 9) * 4;
-        if (mq == 1) hipLaunchKernelGGL(sg_dw_wgrad_kernel<1>, dim3(blocks), dim3(256), lds, st, da);
-        else hipLaunchKernelGGL(sg_dw_wgrad_kernel<2>, dim3(blocks), dim3(256), lds, st, da);
+        if (da.S == 1) {
+            if (mq == 1) hipLaunchKernelGGL((sg_dw_wgrad_kernel<1, 1>), dim3(blocks), dim3(256), lds, st, da);
+            else hipLaunchKernelGGL((sg_dw_wgrad_kernel<2, 1>), dim3(blocks), dim3(256), lds, st, da);
+        } else {
+            if (mq == 1) hipLaunchKernelGGL((sg_dw_wgrad_kernel<1, 2>), dim3(blocks), dim3(256), lds, st, da);
+            else hipLaunchKernelGGL((sg_dw_wgrad_kernel<2, 2>), dim3(blocks), dim3(256), lds, st, da);
+        }
         const int E = s.G * s.Kg * 9;
         hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 255) / 256), dim3(256), 0, st, ws, dw, da.nruns, s.G,
                            s.Kg, mq);

@@ -374,7 +374,12 @@ ASYM_CASES = [
     (dict(N=3, C=8, K=8, H=17, W=30, kh=3, kw=3, sh=1, sw=1, ph=0, pb=1, pw=2, pr=0, dh=1, dw=1,
           G=8), {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     (dict(N=2, C=8, K=16, H=16, W=18, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=8, **_same(16, 18, 3, 2)),
-     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "direct"}),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # ... at the widest stride-2 row (31 outputs read input columns 0..62 of the LDS row;
+    # gradInput's virtual input is read with pad 2 at the start), multiplier 1, nine groups
+    # (the last block of four holds one)
+    (dict(N=3, C=9, K=9, H=62, W=62, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=9, **_same(62, 62, 3, 2)),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     # LDS-tiled direct kernels (20 in / 3 out per group)
     (dict(N=2, C=20, K=6, H=10, W=11, kh=3, kw=3, sh=1, sw=1, ph=2, pb=0, pw=0, pr=1, dh=1, dw=1,
           G=2), {"fwd": "direct", "bwd_data": "direct", "bwd_filter": "direct"}),
@@ -597,6 +602,15 @@ EDGE_CASES = [
     # ... and 4 in / 2 out channels (gradInput's view) at stride 2, dilation 2
     (dict(N=2, C=4, K=8, H=17, W=19, kh=3, kw=3, sh=2, sw=2, ph=2, pw=2, dh=2, dw=2, G=2),
      {"bwd_data": "smallgroup"}),
+    # depthwise row kernels at stride 2: multiplier 2, pad 2 on the widest row
+    # (31 outputs), 18 output rows in three bands, 37 images over the
+    # gradWeight runs ...
+    (dict(N=37, C=6, K=12, H=35, W=60, kh=3, kw=3, sh=2, sw=2, ph=1, pw=2, dh=1, dw=1, G=6),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # ... and multiplier 1 with pad 1 (gradInput on the depthwise kernel over dy
+    # upsampled by 2: 61-wide rows with pad 1, 17 dy rows)
+    (dict(N=2, C=5, K=5, H=33, W=61, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=5),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     # direct gradWeight with 1024-thread blocks (at least 16K pixels): depthwise
     # 5x5, and 8 per group at stride 2
     (dict(N=4, C=8, K=8, H=64, W=64, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=8),
