@@ -371,6 +371,106 @@ __global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
     }
 }
 
+// Depthwise gradInput at stride 2 (3x3, dilation 1, one input and one output
+// channel per group), split by output phase. With h + ph = 2a + u and
+// w + pw = 2b + v (u, v in {0, 1}), dx[h][w] takes dy rows a (tap row u) and,
+// for u = 0, a - 1 (tap row 2); columns likewise. So the four dx of (a, b)
+//   (0,0): w00 D(a,b) + w02 D(a,b-1) + w20 D(a-1,b) + w22 D(a-1,b-1)
+//   (0,1): w01 D(a,b) + w21 D(a-1,b)
+//   (1,0): w10 D(a,b) + w12 D(a,b-1)
+//   (1,1): w11 D(a,b)
+// where D is dy, 0 outside it. A lane owns dx column w of phase row a and
+// writes its two dx rows (stores stay contiguous across lanes): with
+// (A, B) = (w_i0, w_i2) for v = 0 and (w_i1, 0) for v = 1, tap row i gives
+// A D(., b) + B D(., b-1). A workgroup takes kDwGroups consecutive groups of
+// one band of a; LDS row k of a group holds dy row a_lo - 1 + k with dy
+// column m at position m + 1 (position 0, and rows and columns outside dy,
+// hold 0).
+struct SgDw2Args {
+    const float* dy;
+    const float* wgt;
+    float* dx;
+    int N, G, H, W, Ho, Wo, ph, pw;
+    int a_min, na;              // phase rows a covering dx
+    int RA, nbands;             // values of a per workgroup, bands per plane
+    FastDiv div_W;
+};
+
+__global__ void __launch_bounds__(256) sg_dw_dgrad_s2_kernel(SgDw2Args a)
+{
+    constexpr int GB = kDwGroups;
+    extern __shared__ float lds[];  // [GB][RA + 1][64] dy rows, then [GB][9] filters
+    const int plane = (a.RA + 1) * 64;
+    float* wl = lds + GB * plane;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int band = bid % a.nbands;
+    bid /= a.nbands;
+    const int ngb = (a.G + GB - 1) / GB;
+    const int gb = bid % ngb;
+    const int n = bid / ngb;
+    const int g0 = gb * GB, ng = min(GB, a.G - g0);
+    const int a_lo = a.a_min + band * a.RA;
+    const int ra = min(a.RA, a.a_min + a.na - a_lo);
+
+    const int HWo = a.Ho * a.Wo;
+    const float* dy_n = a.dy + ((size_t)n * a.G + g0) * HWo;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dy_n, (uint32_t)ng * HWo * 4u);
+    const int m = lane - 1;  // dy column of LDS position `lane`
+    const bool colok = (unsigned)m < (unsigned)a.Wo;
+#pragma unroll
+    for (int gi = 0; gi < GB; ++gi)
+        for (int k = wave; k <= ra; k += 4) {
+            const int hd = a_lo - 1 + k;
+            const bool ok = colok && gi < ng && (unsigned)hd < (unsigned)a.Ho;
+            load_lds64(rd, lds + gi * plane + k * 64, ok ? (uint32_t)((gi * a.Ho + hd) * a.Wo + m) * 4u : kOOB);
+        }
+    if (tid < GB * 9) {
+        const int gi = tid / 9;
+        wl[tid] = gi < ng ? a.wgt[(size_t)(g0 + gi) * 9 + tid % 9] : 0.f;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    const size_t HW = (size_t)a.H * a.W;
+    const int npos = ra * a.W;
+    // The (group, 64-position chunk) pairs are dealt to the waves in turn, so
+    // that the four waves get equal shares of the workgroup's chunks.
+    const int nch = (npos + 63) >> 6;
+    for (int c = wave; c < ng * nch; c += 4) {
+        const int gi = c / nch;
+        float wv[9];
+#pragma unroll
+        for (int t = 0; t < 9; ++t) wv[t] = wl[gi * 9 + t];
+        float* dx_g = a.dx + ((size_t)n * a.G + g0 + gi) * HW;
+        {
+            const int pl = (c - gi * nch) * 64 + lane;
+            const int pc = min(pl, npos - 1);
+            const int r = (int)fastdiv((uint32_t)pc, a.div_W);
+            const int w = pc - r * a.W;
+            const int b = (w + a.pw) >> 1;
+            const bool odd = (w + a.pw) & 1;
+            // Tap columns: (A, B) act on dy columns b and b - 1.
+            const float A0 = odd ? wv[1] : wv[0], B0 = odd ? 0.f : wv[2];
+            const float A1 = odd ? wv[4] : wv[3], B1 = odd ? 0.f : wv[5];
+            const float A2 = odd ? wv[7] : wv[6], B2 = odd ? 0.f : wv[8];
+            // Row r + 1 is dy row a = a_lo + r, row r is a - 1; position b + 1
+            // is dy column b, position b is b - 1.
+            const float* L = lds + gi * plane + r * 64 + b;
+            const float d11 = L[64 + 1], d10 = L[64], d01 = L[1], d00 = L[0];
+            const float y0 = fmaf(B2, d00, fmaf(A2, d01, fmaf(B0, d10, A0 * d11)));
+            const float y1 = fmaf(B1, d10, A1 * d11);
+            if (pl < npos) {
+                const int h0 = 2 * (a_lo + r) - a.ph;
+                float* o = dx_g + (size_t)h0 * a.W + w;
+                if ((unsigned)h0 < (unsigned)a.H) __builtin_nontemporal_store(y0, o);
+                if ((unsigned)(h0 + 1) < (unsigned)a.H) __builtin_nontemporal_store(y1, o + a.W);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gradWeight
 // ---------------------------------------------------------------------------
@@ -1120,9 +1220,46 @@ bool smallgroup_fwd_supported(const Shape& s)
     return sg_problem_ok(sg_fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
 }
 
+// Depthwise gradInput at stride 2 by output phase (sg_dw_dgrad_s2_kernel):
+// 3x3, dilation 1, one input and one output channel per group; the phase
+// columns b (and b - 1) fit the 64-float LDS row.
+static bool sg_dw_dgrad_s2_plan(const Shape& s, SgDw2Args* out)
+{
+    if (!(s.kh == 3 && s.kw == 3 && s.sh == 2 && s.sw == 2 && s.dh == 1 && s.dw == 1)) return false;
+    if (s.Cg != 1 || s.Kg != 1 || s.N < 1 || s.ph < 0 || s.pw < 0) return false;
+    SgDw2Args a{};
+    a.N = s.N; a.G = s.G; a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo; a.ph = s.ph; a.pw = s.pw;
+    a.a_min = s.ph / 2;
+    a.na = (s.H - 1 + s.ph) / 2 - a.a_min + 1;
+    const int b_max = (s.W - 1 + s.pw) / 2;
+    if (b_max + 1 > 63 || s.Wo + 1 > 64) return false;
+    // Bands of about 8 phase rows (16 dx rows): more, smaller workgroups
+    // measured faster than bands of 16 (4608 -> 9216 workgroups at 64 x 144
+    // x 28 x 28 dy: 45 -> 40 us).
+    const int nbands = (a.na + 7) / 8;
+    a.RA = (a.na + nbands - 1) / nbands;
+    a.nbands = (a.na + a.RA - 1) / a.RA;
+    if ((int64_t)kDwGroups * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)s.N * ((s.G + kDwGroups - 1) / kDwGroups) * a.nbands >= (1 << 30)) return false;
+    a.div_W = make_fastdiv((uint32_t)s.W);
+    if (out) *out = a;
+    return true;
+}
+
+static bool sg_run_dw_dgrad_s2(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    SgDw2Args a;
+    if (!sg_dw_dgrad_s2_plan(s, &a)) return false;
+    a.dy = dy; a.wgt = w; a.dx = dx;
+    const int blocks = s.N * ((s.G + kDwGroups - 1) / kDwGroups) * a.nbands;
+    const size_t lds = ((size_t)kDwGroups * (a.RA + 1) * 64 + (size_t)kDwGroups * 9) * 4;
+    hipLaunchKernelGGL(sg_dw_dgrad_s2_kernel, dim3(blocks), dim3(256), lds, st, a);
+    return true;
+}
+
 bool smallgroup_bwd_data_supported(const Shape& s)
 {
-    return sg_problem_ok(sg_bwd_data_problem(s, nullptr, nullptr, nullptr));
+    return sg_dw_dgrad_s2_plan(s, nullptr) || sg_problem_ok(sg_bwd_data_problem(s, nullptr, nullptr, nullptr));
 }
 
 bool smallgroup_bwd_filter_supported(const Shape& s) { return sgw_plan(s, nullptr); }
@@ -1148,6 +1285,9 @@ bool smallgroup_fwd(const Shape& s, const float* x, const float* w, const float*
 bool smallgroup_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
                          hipStream_t st)
 {
+#ifndef GCONV_SG_NO_DW_S2_PHASE
+    if (sg_dw_dgrad_s2_plan(s, nullptr)) return sg_run_dw_dgrad_s2(s, dy, w, dx, st);
+#endif
     return sg_run(sg_bwd_data_problem(s, dy, w, dx), st);
 }
 

@@ -611,6 +611,14 @@ EDGE_CASES = [
     # upsampled by 2: 61-wide rows with pad 1, 17 dy rows)
     (dict(N=2, C=5, K=5, H=33, W=61, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=5),
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # depthwise gradInput at stride 2 split by output phase: pad 2 (the first
+    # phase row and column start one dx row and column early), 50 phase rows in
+    # four bands, 50 phase columns, six groups (the second block of four holds two)
+    (dict(N=2, C=6, K=6, H=100, W=100, kh=3, kw=3, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=6),
+     {"bwd_data": "smallgroup"}),
+    # ... odd sizes with pad 0 and 1 (the last phase row and column are half outside dx)
+    (dict(N=3, C=5, K=5, H=19, W=23, kh=3, kw=3, sh=2, sw=2, ph=0, pw=1, dh=1, dw=1, G=5),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     # direct gradWeight with 1024-thread blocks (at least 16K pixels): depthwise
     # 5x5, and 8 per group at stride 2
     (dict(N=4, C=8, K=8, H=64, W=64, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=8),
