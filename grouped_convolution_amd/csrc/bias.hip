@@ -2,7 +2,10 @@
 //   db[k] = sum over n, ho, wo of dy[n, k, ho, wo]
 // (a plain reduction of dy over everything but the channel: "Pointwise
 // Broadcast/Reduce" on the dlprimitives blog, the bias-gradient formula).
-// Two passes, deterministic: split blocks write partial sums laid out
+// Deterministic throughout. Where each channel is small (at most 1 MiB of
+// planes), one 1024-thread workgroup per channel sums it in one pass; the
+// launch and finalize of a second pass cost more than the extra parallelism
+// gains there. Otherwise two passes: split blocks write partial sums laid out
 // [split][channel], then a second kernel adds each channel's splits in a
 // fixed order (consecutive channels read consecutive partials).
 //   plane layout (Ho*Wo > 1): block (s, k) sums images [s*chunk, (s+1)*chunk)
@@ -10,6 +13,7 @@
 //   column layout (Ho*Wo == 1, dy is [N, K], fully-connected mode): block
 //     (kb, s) sums rows [s*chunk, (s+1)*chunk) of 1024 columns (4 per thread).
 #include "device_util.h"
+#include "fastdiv.h"
 #include "gconv_internal.h"
 
 namespace gconv {
@@ -105,7 +109,78 @@ bias_finalize(const float* __restrict__ ws, float* __restrict__ db, int K, int S
     db[k] = sum;
 }
 
+// One pass, one 1024-thread workgroup per channel (shapes where every channel
+// is small enough for one CU): thread t sums elements t, t + 1024, ... of the
+// channel's N planes taken as one sequence (eight independent loads in flight
+// per thread), then the 16 wave sums are added in order. No partials, no
+// second launch.
+constexpr int kB1 = 1024;
+template <bool VEC>
+__global__ void __launch_bounds__(kB1)
+bias_planes_single(const float* __restrict__ dy, float* __restrict__ db, int N, int K, int P, FastDiv div_len)
+{
+    __shared__ float red[16];
+    const int k = blockIdx.x;
+    const int len = VEC ? (P >> 2) : P;    // elements (f4 or float) per plane
+    const int total = N * len;
+    float acc = 0.f;
+    f4 a4 = f4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * kB1) {
+        if constexpr (VEC) {
+            f4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kB1;
+                v[u] = f4{0.f, 0.f, 0.f, 0.f};
+                if (i < total) {
+                    const int n = (int)fastdiv((uint32_t)i, div_len);
+                    v[u] = reinterpret_cast<const f4*>(dy + ((int64_t)n * K + k) * P)[i - n * len];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a4 += v[u];
+        } else {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kB1;
+                v[u] = 0.f;
+                if (i < total) {
+                    const int n = (int)fastdiv((uint32_t)i, div_len);
+                    v[u] = dy[((int64_t)n * K + k) * P + (i - n * len)];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += v[u];
+        }
+    }
+    if constexpr (VEC) acc = (a4.x + a4.y) + (a4.z + a4.w);
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = red[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) t += red[i];
+        db[k] = t;
+    }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// The one-pass form: planes (Ho*Wo > 1), at most 1 MiB per channel, and
+// either enough channels to occupy a quarter of the CUs or little data in all.
+bool bias_single(const Shape& s)
+{
+#ifdef GCONV_BIAS_TWO_PASS
+    return false;
+#else
+    const int64_t P = (int64_t)s.Ho * s.Wo;
+    const int64_t per = (int64_t)s.N * P;  // floats per channel
+    return P > 1 && per * 4 <= (int64_t(1) << 20) && (s.K >= 64 || per * s.K * 4 <= (int64_t(8) << 20));
+#endif
+}
 bool cols_vec(const Shape& s) { return (s.K & 3) == 0; }
 
 // Splits: about 2048 partial blocks for the plane layout (whole images per
@@ -130,13 +205,22 @@ int bias_splits(const Shape& s)
 
 size_t bias_workspace_bytes(const Shape& s)
 {
-    if (s.N == 0) return 0;
+    if (s.N == 0 || bias_single(s)) return 0;
     return (size_t)s.K * (size_t)bias_splits(s) * sizeof(float);
 }
 
 void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStream_t st)
 {
     const int P = s.Ho * s.Wo;
+    if (bias_single(s)) {
+        if ((P & 3) == 0 && aligned16(dy))
+            hipLaunchKernelGGL(bias_planes_single<true>, dim3(s.K), dim3(kB1), 0, st, dy, db, s.N, s.K, P,
+                               make_fastdiv((uint32_t)(P >> 2)));
+        else
+            hipLaunchKernelGGL(bias_planes_single<false>, dim3(s.K), dim3(kB1), 0, st, dy, db, s.N, s.K, P,
+                               make_fastdiv((uint32_t)P));
+        return;
+    }
     const int S = bias_splits(s);
     const int chunk = (s.N + S - 1) / S;
     if (P == 1) {

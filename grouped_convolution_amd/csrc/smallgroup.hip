@@ -822,17 +822,30 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
     }
 }
 
-// dw[g*Kg + o][0][t] = sum over image runs (in order) of ws[run][g][o][t].
+// dw[g*Kg + o][0][t] = sum over image runs of ws[run][g][o][t] in a fixed
+// order. Block = 16 outputs x 16 run groups: thread (e, rg) sums runs rg,
+// rg + 16, ... in order, then the 16 group sums are added in order (a serial
+// loop over all runs per output left each thread waiting on one load at a time).
 __global__ void __launch_bounds__(256) sg_dw_wgrad_reduce(const float* __restrict__ ws, float* __restrict__ dw,
                                                           int nruns, int G, int Kg, int MQ)
 {
-    const int e = blockIdx.x * 256 + threadIdx.x;  // over G * Kg * 9
-    if (e >= G * Kg * 9) return;
-    const int t = e % 9, go = e / 9, g = go / Kg, o = go - (go / Kg) * Kg;
-    const size_t per = (size_t)G * MQ * 9;
-    const size_t idx = ((size_t)g * MQ + o) * 9 + t;
-    float sum = ws[idx];
-    for (int r = 1; r < nruns; ++r) sum += ws[(size_t)r * per + idx];
+    __shared__ float part[16][17];
+    const int el = threadIdx.x & 15, rg = threadIdx.x >> 4;
+    const int e = blockIdx.x * 16 + el;  // over G * Kg * 9
+    const int E = G * Kg * 9;
+    float sum = 0.f;
+    if (e < E) {
+        const int t = e % 9, go = e / 9, g = go / Kg, o = go - g * Kg;
+        const size_t per = (size_t)G * MQ * 9;
+        const size_t idx = ((size_t)g * MQ + o) * 9 + t;
+        for (int r = rg; r < nruns; r += 16) sum += ws[(size_t)r * per + idx];
+    }
+    part[rg][el] = sum;
+    __syncthreads();
+    if (rg != 0 || e >= E) return;
+    sum = part[0][el];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) sum += part[i][el];
     dw[e] = sum;
 }
 
@@ -1310,7 +1323,7 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
             else hipLaunchKernelGGL((sg_dw_wgrad_kernel<2, 2>), dim3(blocks), dim3(256), lds, st, da);
         }
         const int E = s.G * s.Kg * 9;
-        hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 255) / 256), dim3(256), 0, st, ws, dw, da.nruns, s.G,
+        hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, da.nruns, s.G,
                            s.Kg, mq);
         return true;
     }

@@ -418,6 +418,25 @@ def test_asymmetric_padding_cases(case):
         assert np.array_equal(g.cpu().numpy().astype(np.float64), val), d
 
 
+@pytest.mark.parametrize("shape", [
+    (3, 6, 13, 13),     # one pass, odd plane length (scalar loads)
+    (5, 70, 28, 28),    # one pass, 16-byte loads, 70 channels
+    (70, 2, 64, 64),    # split partials: more than 1 MiB per channel
+    (700, 40, 1, 1),    # split partials over the rows of a [N, K] gradient
+])
+def test_bias_reduction_forms(shape):
+    """gradBias in each of its forms (one workgroup per channel, or split
+    partials plus an ordered finalize) against the oracle; integer-valued dy
+    bit for bit."""
+    say("bias %s" % (shape,))
+    dy = draw(("normal", 1.0), shape, 2300 + shape[1])
+    val, mag = oracle.bwd_bias(dy)
+    check("bias %s" % (shape,), G.gconv_bwd_bias(dev(dy)).cpu().numpy(), val, mag)
+    dyi = draw(("int", -3, 3), shape, 2400 + shape[1])
+    vali, _ = oracle.bwd_bias(dyi)
+    assert np.array_equal(G.gconv_bwd_bias(dev(dyi)).cpu().numpy().astype(np.float64), vali)
+
+
 def test_fc_1x1_on_1x1_is_linear():
     """A 1x1 convolution of a 1x1 input (the Linear(128, 32) case of the
     cudnn.torch issue) runs the GEMM path and matches the oracle."""
