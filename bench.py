@@ -30,6 +30,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -94,16 +96,19 @@ def run_gpu(args, wl_name):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(wl_name)
-    x = torch.from_numpy(inp["x"]).to(dev)
+    # make_inputs gives NCHW arrays; channels-last workloads store them transposed.
+    store = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1))) if wl.layout == "nhwc" else (lambda a: a)
+    x = torch.from_numpy(store(inp["x"])).to(dev)
     w = torch.from_numpy(inp["w"]).to(dev)
     b = None if inp["b"] is None else torch.from_numpy(inp["b"]).to(dev)
-    dy = torch.from_numpy(inp["dy"]).to(dev)
-    kw = dict(stride=wl.stride, padding=wl.padding, dilation=wl.dilation, groups=wl.groups)
+    dy = torch.from_numpy(store(inp["dy"])).to(dev)
+    kw = dict(stride=wl.stride, padding=wl.padding, dilation=wl.dilation, groups=wl.groups,
+              layout=wl.layout)
     N, C, H, W = wl.x_shape
     K, Cg, kh, kwid = wl.w_shape
     desc = G.make_desc(N, C, H, W, K, kh, kwid, **kw)
     Ho, Wo = G.gconv_output_dims(desc)
-    y = torch.empty((N, K, Ho, Wo), device=dev)
+    y = torch.empty((N, Ho, Wo, K) if wl.layout == "nhwc" else (N, K, Ho, Wo), device=dev)
     dx = torch.empty_like(x)
     dw = torch.empty_like(w)
     db = torch.empty((K,), device=dev)
@@ -111,7 +116,7 @@ def run_gpu(args, wl_name):
         "fwd": G.Plan.fwd(x, w, b, y, **kw),
         "bwd_data": G.Plan.bwd_data(dy, w, dx, **kw),
         "bwd_filter": G.Plan.bwd_filter(x, dy, dw, **kw),
-        "bwd_bias": G.Plan.bwd_bias(dy, db),
+        "bwd_bias": G.Plan.bwd_bias(dy, db, layout=wl.layout),
     }
     paths = {op: G.PATH_NAMES[G.gconv_select_path(desc, i)] for i, op in enumerate(OPS)}
     for _ in range(args.warmup):
@@ -134,7 +139,7 @@ def run_gpu(args, wl_name):
             cs.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(cs):
                 gplans = [G.Plan.fwd(x, w, b, y, **kw), G.Plan.bwd_data(dy, w, dx, **kw),
-                          G.Plan.bwd_filter(x, dy, dw, **kw), G.Plan.bwd_bias(dy, db)]
+                          G.Plan.bwd_filter(x, dy, dw, **kw), G.Plan.bwd_bias(dy, db, layout=wl.layout)]
                 torch.cuda.synchronize()
                 graph = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(graph, stream=cs):

@@ -25,6 +25,7 @@ STATUS = {0: "GCONV_OK", 1: "GCONV_ERR_NULL", 2: "GCONV_ERR_SHAPE", 3: "GCONV_ER
 OP_FWD, OP_BWD_DATA, OP_BWD_FILTER, OP_BWD_BIAS = 0, 1, 2, 3
 PATH_AUTO, PATH_DIRECT, PATH_SMALLGROUP, PATH_IGEMM, PATH_FC, PATH_POINTWISE = 0, 1, 2, 3, 4, 5
 EPILOGUE_NONE, EPILOGUE_RELU = 0, 1
+LAYOUT_NCHW, LAYOUT_NHWC = 0, 1
 PATH_NAMES = {PATH_AUTO: "auto", PATH_DIRECT: "direct", PATH_SMALLGROUP: "smallgroup",
               PATH_IGEMM: "igemm", PATH_FC: "fc", PATH_POINTWISE: "pointwise"}
 
@@ -44,7 +45,7 @@ class GconvError(RuntimeError):
 class gconv_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "N", "C", "H", "W", "K", "kh", "kw", "stride_h", "stride_w", "pad_h", "pad_w",
-        "dil_h", "dil_w", "groups", "pad_h_extra", "pad_w_extra")]
+        "dil_h", "dil_w", "groups", "pad_h_extra", "pad_w_extra", "layout")]
 
 
 _lib = None
@@ -122,13 +123,38 @@ def same_padding(H, W, kh, kw, stride=1, dilation=1):
     return tuple(out)
 
 
-def make_desc(N, C, H, W, K, kh, kw, stride=1, padding=0, dilation=1, groups=1) -> gconv_desc:
-    """`padding` is an int, a pair (pad_h, pad_w) or a 4-tuple (top, bottom, left, right)."""
+def _layout(v) -> int:
+    """"nchw" / "nhwc" (or LAYOUT_NCHW / LAYOUT_NHWC) -> gconv_layout."""
+    if isinstance(v, str):
+        key = v.lower()
+        if key not in ("nchw", "nhwc"):
+            raise ValueError("layout must be 'nchw' or 'nhwc', got %r" % v)
+        return LAYOUT_NHWC if key == "nhwc" else LAYOUT_NCHW
+    if int(v) not in (LAYOUT_NCHW, LAYOUT_NHWC):
+        raise ValueError("unknown layout %r" % (v,))
+    return int(v)
+
+
+def make_desc(N, C, H, W, K, kh, kw, stride=1, padding=0, dilation=1, groups=1,
+              layout="nchw") -> gconv_desc:
+    """`padding` is an int, a pair (pad_h, pad_w) or a 4-tuple (top, bottom, left, right);
+    `layout` ("nchw" or "nhwc") is that of x, dx, y and dy."""
     sh, sw = _pair(stride, "stride")
     ph, pw, eh, ew = _padding(padding)
     dh, dw = _pair(dilation, "dilation")
     return gconv_desc(int(N), int(C), int(H), int(W), int(K), int(kh), int(kw), sh, sw, ph, pw,
-                      dh, dw, int(groups), eh, ew)
+                      dh, dw, int(groups), eh, ew, _layout(layout))
+
+
+def _act_shape(N, C, H, W, layout):
+    """The 4-D shape of an activation with N images, C channels, H x W pixels."""
+    return (N, H, W, C) if _layout(layout) == LAYOUT_NHWC else (N, C, H, W)
+
+
+def _act_dims(shape, layout):
+    """(N, C, H, W) of an activation tensor shape in `layout`."""
+    N, a, b, c = (int(v) for v in shape)
+    return (N, c, a, b) if _layout(layout) == LAYOUT_NHWC else (N, a, b, c)
 
 
 def gconv_output_dims(desc: gconv_desc):
@@ -176,7 +202,7 @@ def _dev_f32(t, name):
     if t.device.type != "cuda":
         raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
     if not t.is_contiguous():
-        raise ValueError("%s must be contiguous (NCHW row-major)" % name)
+        raise ValueError("%s must be contiguous (row-major in its layout)" % name)
     return t
 
 
@@ -213,14 +239,15 @@ def _out(out, shape, like, name):
 
 
 def gconv_fwd(x, w, bias=None, *, stride=1, padding=0, dilation=1, groups=1, out=None,
-              workspace=None, relu=False):
-    """y = conv(x, w) + bias; x [N,C,H,W], w [K,C/groups,kh,kw], bias [K] or None.
+              workspace=None, relu=False, layout="nchw"):
+    """y = conv(x, w) + bias; x [N,C,H,W] (or [N,H,W,C] with layout="nhwc", giving y
+    [N,Ho,Wo,K]), w [K,C/groups,kh,kw], bias [K] or None.
     With relu=True the kernels store max(y, 0) (gconv_fwd_ex, GCONV_EPILOGUE_RELU)."""
     _dev_f32(x, "x")
     _dev_f32(w, "w")
     if x.dim() != 4 or w.dim() != 4:
-        raise ValueError("x and w must be 4-D (NCHW and [K, C/groups, kh, kw])")
-    N, C, H, W = x.shape
+        raise ValueError("x and w must be 4-D (NCHW or NHWC, and [K, C/groups, kh, kw])")
+    N, C, H, W = _act_dims(x.shape, layout)
     K, Cg, kh, kw = w.shape
     if groups < 1 or C % groups or Cg * groups != C:
         raise ValueError("channels_in C=%d must equal w.shape[1]*groups = %d*%d"
@@ -229,9 +256,9 @@ def gconv_fwd(x, w, bias=None, *, stride=1, padding=0, dilation=1, groups=1, out
         _dev_f32(bias, "bias")
         if tuple(bias.shape) != (K,):
             raise ValueError("bias must have shape [K]=[%d]" % K)
-    desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
+    desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups, layout)
     Ho, Wo = gconv_output_dims(desc)
-    y = _out(out, (N, K, Ho, Wo), x, "out")
+    y = _out(out, _act_shape(N, K, Ho, Wo, layout), x, "out")
     ws, nws = _workspace(desc, OP_FWD, x.device, workspace)
     _check(load().gconv_fwd_ex(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias),
                                EPILOGUE_RELU if relu else EPILOGUE_NONE, _ptr(y), _ptr(ws), nws,
@@ -240,20 +267,22 @@ def gconv_fwd(x, w, bias=None, *, stride=1, padding=0, dilation=1, groups=1, out
 
 
 def gconv_bwd_data(dy, w, x_shape, *, stride=1, padding=0, dilation=1, groups=1, out=None,
-                   workspace=None):
-    """gradInput [N,C,H,W] from dy [N,K,Ho,Wo] and w [K,C/groups,kh,kw]."""
+                   workspace=None, layout="nchw"):
+    """gradInput [N,C,H,W] from dy [N,K,Ho,Wo] and w [K,C/groups,kh,kw] (x_shape, dy and
+    the result in `layout`)."""
     _dev_f32(dy, "dy")
     _dev_f32(w, "w")
-    N, C, H, W = (int(v) for v in x_shape)
+    N, C, H, W = _act_dims(x_shape, layout)
     K, Cg, kh, kw = w.shape
     if groups < 1 or Cg * groups != C:
         raise ValueError("channels_in C=%d must equal w.shape[1]*groups = %d*%d"
                          % (C, Cg, groups))
-    desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
+    desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups, layout)
     Ho, Wo = gconv_output_dims(desc)
-    if tuple(dy.shape) != (N, K, Ho, Wo):
-        raise ValueError("dy has shape %s, expected %s" % (tuple(dy.shape), (N, K, Ho, Wo)))
-    dx = _out(out, (N, C, H, W), dy, "out")
+    if tuple(dy.shape) != _act_shape(N, K, Ho, Wo, layout):
+        raise ValueError("dy has shape %s, expected %s"
+                         % (tuple(dy.shape), _act_shape(N, K, Ho, Wo, layout)))
+    dx = _out(out, _act_shape(N, C, H, W, layout), dy, "out")
     ws, nws = _workspace(desc, OP_BWD_DATA, dy.device, workspace)
     _check(load().gconv_bwd_data(ctypes.byref(desc), _ptr(dy), _ptr(w), _ptr(dx), _ptr(ws), nws,
                                  _stream(dy.device)), "gconv_bwd_data")
@@ -261,19 +290,21 @@ def gconv_bwd_data(dy, w, x_shape, *, stride=1, padding=0, dilation=1, groups=1,
 
 
 def gconv_bwd_filter(x, dy, w_shape, *, stride=1, padding=0, dilation=1, groups=1, out=None,
-                     workspace=None):
-    """gradWeight [K,C/groups,kh,kw] from x [N,C,H,W] and dy [N,K,Ho,Wo] (overwrites)."""
+                     workspace=None, layout="nchw"):
+    """gradWeight [K,C/groups,kh,kw] from x [N,C,H,W] and dy [N,K,Ho,Wo] (x and dy in
+    `layout`; overwrites)."""
     _dev_f32(x, "x")
     _dev_f32(dy, "dy")
-    N, C, H, W = x.shape
+    N, C, H, W = _act_dims(x.shape, layout)
     K, Cg, kh, kw = (int(v) for v in w_shape)
     if groups < 1 or Cg * groups != C:
         raise ValueError("channels_in C=%d must equal w_shape[1]*groups = %d*%d"
                          % (C, Cg, groups))
-    desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
+    desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups, layout)
     Ho, Wo = gconv_output_dims(desc)
-    if tuple(dy.shape) != (N, K, Ho, Wo):
-        raise ValueError("dy has shape %s, expected %s" % (tuple(dy.shape), (N, K, Ho, Wo)))
+    if tuple(dy.shape) != _act_shape(N, K, Ho, Wo, layout):
+        raise ValueError("dy has shape %s, expected %s"
+                         % (tuple(dy.shape), _act_shape(N, K, Ho, Wo, layout)))
     dw = _out(out, (K, Cg, kh, kw), x, "out")
     ws, nws = _workspace(desc, OP_BWD_FILTER, x.device, workspace)
     _check(load().gconv_bwd_filter(ctypes.byref(desc), _ptr(x), _ptr(dy), _ptr(dw), _ptr(ws),
@@ -281,14 +312,14 @@ def gconv_bwd_filter(x, dy, w_shape, *, stride=1, padding=0, dilation=1, groups=
     return dw
 
 
-def gconv_bwd_bias(dy, *, out=None, workspace=None):
-    """gradBias [K] = sum of dy [N,K,Ho,Wo] over (n, ho, wo) (overwrites)."""
+def gconv_bwd_bias(dy, *, out=None, workspace=None, layout="nchw"):
+    """gradBias [K] = sum of dy [N,K,Ho,Wo] (or [N,Ho,Wo,K]) over (n, ho, wo) (overwrites)."""
     _dev_f32(dy, "dy")
     if dy.dim() != 4:
-        raise ValueError("dy must be 4-D [N, K, Ho, Wo]")
-    N, K, Ho, Wo = dy.shape
+        raise ValueError("dy must be 4-D [N, K, Ho, Wo] or [N, Ho, Wo, K]")
+    N, K, Ho, Wo = _act_dims(dy.shape, layout)
     # Only N, K, Ho, Wo matter: describe dy as the output of a 1x1 conv.
-    desc = make_desc(N, K, Ho, Wo, K, 1, 1)
+    desc = make_desc(N, K, Ho, Wo, K, 1, 1, layout=layout)
     db = _out(out, (K,), dy, "out")
     ws, nws = _workspace(desc, OP_BWD_BIAS, dy.device, workspace)
     _check(load().gconv_bwd_bias(ctypes.byref(desc), _ptr(dy), _ptr(db), _ptr(ws), nws,
@@ -322,45 +353,46 @@ class Plan:
 
     @classmethod
     def fwd(cls, x, w, bias, y, *, stride=1, padding=0, dilation=1, groups=1, workspace=None,
-            relu=False):
+            relu=False, layout="nchw"):
         gconv_fwd(x, w, bias, stride=stride, padding=padding, dilation=dilation, groups=groups,
-                  out=y, workspace=workspace, relu=relu)  # validates once (and runs once)
-        N, C, H, W = x.shape
+                  out=y, workspace=workspace, relu=relu, layout=layout)  # validates (and runs) once
+        N, C, H, W = _act_dims(x.shape, layout)
         K, _, kh, kw = w.shape
-        desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
+        desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups, layout)
         ws, nws, st = cls._prep(desc, OP_FWD, x.device, workspace)
         act = EPILOGUE_RELU if relu else EPILOGUE_NONE
         return cls("gconv_fwd_ex", (ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias), act, _ptr(y),
                                     _ptr(ws), nws, st), (desc, x, w, bias, y, ws))
 
     @classmethod
-    def bwd_data(cls, dy, w, dx, *, stride=1, padding=0, dilation=1, groups=1, workspace=None):
+    def bwd_data(cls, dy, w, dx, *, stride=1, padding=0, dilation=1, groups=1, workspace=None,
+                 layout="nchw"):
         gconv_bwd_data(dy, w, dx.shape, stride=stride, padding=padding, dilation=dilation,
-                       groups=groups, out=dx, workspace=workspace)
-        N, C, H, W = dx.shape
+                       groups=groups, out=dx, workspace=workspace, layout=layout)
+        N, C, H, W = _act_dims(dx.shape, layout)
         K, _, kh, kw = w.shape
-        desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
+        desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups, layout)
         ws, nws, st = cls._prep(desc, OP_BWD_DATA, dy.device, workspace)
         return cls("gconv_bwd_data", (ctypes.byref(desc), _ptr(dy), _ptr(w), _ptr(dx), _ptr(ws),
                                       nws, st), (desc, dy, w, dx, ws))
 
     @classmethod
     def bwd_filter(cls, x, dy, dw, *, stride=1, padding=0, dilation=1, groups=1,
-                   workspace=None):
+                   workspace=None, layout="nchw"):
         gconv_bwd_filter(x, dy, dw.shape, stride=stride, padding=padding, dilation=dilation,
-                         groups=groups, out=dw, workspace=workspace)
-        N, C, H, W = x.shape
+                         groups=groups, out=dw, workspace=workspace, layout=layout)
+        N, C, H, W = _act_dims(x.shape, layout)
         K, _, kh, kw = dw.shape
-        desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups)
+        desc = make_desc(N, C, H, W, K, kh, kw, stride, padding, dilation, groups, layout)
         ws, nws, st = cls._prep(desc, OP_BWD_FILTER, x.device, workspace)
         return cls("gconv_bwd_filter", (ctypes.byref(desc), _ptr(x), _ptr(dy), _ptr(dw),
                                         _ptr(ws), nws, st), (desc, x, dy, dw, ws))
 
     @classmethod
-    def bwd_bias(cls, dy, db, *, workspace=None):
-        gconv_bwd_bias(dy, out=db, workspace=workspace)
-        N, K, Ho, Wo = dy.shape
-        desc = make_desc(N, K, Ho, Wo, K, 1, 1)
+    def bwd_bias(cls, dy, db, *, workspace=None, layout="nchw"):
+        gconv_bwd_bias(dy, out=db, workspace=workspace, layout=layout)
+        N, K, Ho, Wo = _act_dims(dy.shape, layout)
+        desc = make_desc(N, K, Ho, Wo, K, 1, 1, layout=layout)
         ws, nws, st = cls._prep(desc, OP_BWD_BIAS, dy.device, workspace)
         return cls("gconv_bwd_bias", (ctypes.byref(desc), _ptr(dy), _ptr(db), _ptr(ws), nws, st),
                    (desc, dy, db, ws))

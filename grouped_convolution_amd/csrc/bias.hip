@@ -11,7 +11,8 @@
 //   plane layout (Ho*Wo > 1): block (s, k) sums images [s*chunk, (s+1)*chunk)
 //     of plane k, with 16-byte loads when the plane length is a multiple of 4;
 //   column layout (Ho*Wo == 1, dy is [N, K], fully-connected mode): block
-//     (kb, s) sums rows [s*chunk, (s+1)*chunk) of 1024 columns (4 per thread).
+//     (kb, s) sums rows [s*chunk, (s+1)*chunk) of 1024 columns (4 per thread);
+//     narrower rows (NHWC gradients) take several rows per wave instead.
 #include "device_util.h"
 #include "fastdiv.h"
 #include "gconv_internal.h"
@@ -83,6 +84,34 @@ bias_cols_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, i
         for (int n = n0; n < n1; ++n) a += dy[(int64_t)n * K + k];
         ws[(int64_t)sidx * K + k] = a;
     }
+}
+
+// Column layout with narrow rows (dy is [rows, K] with K a multiple of 4 and
+// fewer than 1024 columns: NHWC gradients): a block of 256 threads is KT
+// column quads x (256 / KT) row phases, so a wave reads whole consecutive rows
+// (KT = 16 for K = 64: four 256-byte rows per wave instruction). Thread (c, r)
+// adds rows r0 + r, r0 + r + 256/KT, ... of its column quad; the row phases
+// are then added in order through LDS, one partial per column and split.
+__global__ void __launch_bounds__(kB)
+bias_rows_partial(const float* __restrict__ dy, float* __restrict__ ws, int N, int K, int chunk, int KT)
+{
+    __shared__ f4 part[kB];
+    const int sidx = blockIdx.y;
+    const int n0 = sidx * chunk, n1 = min(N, n0 + chunk);
+    const int K4 = K >> 2;
+    const int ct = threadIdx.x % KT, rt = threadIdx.x / KT, RT = kB / KT;
+    const int c4 = blockIdx.x * KT + ct;
+    f4 a = f4{0.f, 0.f, 0.f, 0.f};
+    if (c4 < K4) {
+#pragma unroll 8
+        for (int n = n0 + rt; n < n1; n += RT) a += reinterpret_cast<const f4*>(dy + (int64_t)n * K)[c4];
+    }
+    part[threadIdx.x] = a;
+    __syncthreads();
+    if (rt != 0 || c4 >= K4) return;
+    f4 t = part[ct];
+    for (int r = 1; r < RT; ++r) t += part[r * KT + ct];
+    reinterpret_cast<f4*>(ws + (int64_t)sidx * K)[c4] = t;
 }
 
 // db[k] = sum over s of ws[s*K + k]. Block = 16 channels x 16 split groups:
@@ -183,16 +212,30 @@ bool bias_single(const Shape& s)
 }
 bool cols_vec(const Shape& s) { return (s.K & 3) == 0; }
 
+// Column quads per block of the narrow-row column kernel (a power of two up to
+// 64); 0 when the rows are wide enough for one thread per column quad.
+int rows_kt(const Shape& s)
+{
+    if (!cols_vec(s) || s.K >= 1024) return 0;
+    int kt = 1;
+    while (kt < 64 && kt < s.K / 4) kt *= 2;
+    return kt;
+}
+
 // Splits: about 2048 partial blocks for the plane layout (whole images per
 // block); about 1024 blocks of 1024 columns for the column layout.
 int bias_splits(const Shape& s)
 {
     const int P = s.Ho * s.Wo;
     int S;
-    if (P == 1) {
+    if (P == 1 && rows_kt(s) > 0) {
+        // (512 blocks: 2048 left the finalize adding 128 partials per thread)
+        const int kb = (s.K / 4 + rows_kt(s) - 1) / rows_kt(s);
+        S = (512 + kb - 1) / kb;
+    } else if (P == 1) {
         const int cpb = cols_vec(s) ? 4 * kB : kB;  // columns per block
         const int kb = (s.K + cpb - 1) / cpb;
-        S = (1024 + kb - 1) / kb;
+        S = (512 + kb - 1) / kb;
     } else {
         S = (2048 + s.K - 1) / s.K;
     }
@@ -223,7 +266,11 @@ void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStrea
     }
     const int S = bias_splits(s);
     const int chunk = (s.N + S - 1) / S;
-    if (P == 1) {
+    if (P == 1 && rows_kt(s) > 0 && aligned16(dy) && aligned16(ws)) {
+        const int kt = rows_kt(s);
+        hipLaunchKernelGGL(bias_rows_partial, dim3((s.K / 4 + kt - 1) / kt, S), dim3(kB), 0, st, dy, ws, s.N,
+                           s.K, chunk, kt);
+    } else if (P == 1) {
         // (the split count, hence the workspace size, does not depend on the
         // pointers: only the load width does)
         if (cols_vec(s) && aligned16(dy) && aligned16(ws))

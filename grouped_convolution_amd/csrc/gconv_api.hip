@@ -2,6 +2,7 @@
 // extents, routing between kernel families, workspace sizing and error
 // reporting. Everything here runs on the host; kernels live in the other
 // translation units.
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -59,6 +60,8 @@ int make_shape(const gconv_desc* d, Shape* s)
     if (pad_h_end < 0 || pad_w_end < 0)
         return fail(GCONV_ERR_SHAPE, "end padding pad+pad_extra must be >= 0 (got %lld, %lld)",
                     (long long)pad_h_end, (long long)pad_w_end);
+    if (d->layout != GCONV_LAYOUT_NCHW && d->layout != GCONV_LAYOUT_NHWC)
+        return fail(GCONV_ERR_ARG, "unknown layout %lld", (long long)d->layout);
     if (d->groups < 1) return fail(GCONV_ERR_GROUPS, "groups=%lld must be >= 1",
                                    (long long)d->groups);
     if (d->C % d->groups != 0)
@@ -86,6 +89,7 @@ int make_shape(const gconv_desc* d, Shape* s)
     s->dh = (int)d->dil_h; s->dw = (int)d->dil_w;
     s->G = (int)d->groups; s->Cg = (int)(d->C / d->groups); s->Kg = (int)(d->K / d->groups);
     s->Ho = (int)Ho; s->Wo = (int)Wo;
+    s->nhwc = d->layout == GCONV_LAYOUT_NHWC;
     s->x_elems = d->N * d->C * d->H * d->W;
     s->w_elems = d->K * (d->C / d->groups) * d->kh * d->kw;
     s->y_elems = d->N * d->K * Ho * Wo;
@@ -102,6 +106,64 @@ bool overlap(const void* a, int64_t a_elems, const void* b, int64_t b_elems)
     const char* pa = (const char*)a;
     const char* pb = (const char*)b;
     return pa < pb + b_elems * 4 && pb < pa + a_elems * 4;
+}
+
+// ---- channels-last (NHWC) ------------------------------------------------------
+//
+// An NHWC op runs on an NCHW shape, its "effective" shape:
+//   - gradBias: dy [N*Ho*Wo, K] is the [rows, K] gradient of a 1x1 output;
+//   - 1x1, stride 1, no padding, one group: y [N*H*W, K] = x [N*H*W, C] times
+//     w [K, C] transposed, i.e. fully-connected mode over N*H*W rows (the
+//     cudnn.torch issue: a 1x1 convolution is a Linear layer on the pixels);
+//   - otherwise the NCHW shape itself, with the NHWC activations reordered
+//     into NCHW copies in the workspace ("staged").
+bool nhwc_as_gemm(const Shape& s)
+{
+    return s.kh == 1 && s.kw == 1 && s.sh == 1 && s.sw == 1 && s.ph == 0 && s.pw == 0 && s.ph_end == 0 &&
+           s.pw_end == 0 && s.G == 1 && (int64_t)s.N * s.H * s.W < (int64_t(1) << 30);
+}
+
+Shape flat_rows(const Shape& s, int64_t rows, int C, int K)
+{
+    Shape f = s;
+    f.nhwc = 0;
+    f.N = (int)rows; f.C = C; f.H = 1; f.W = 1; f.K = K;
+    f.kh = 1; f.kw = 1; f.sh = 1; f.sw = 1; f.ph = 0; f.pw = 0; f.ph_end = 0; f.pw_end = 0;
+    f.dh = 1; f.dw = 1;
+    f.G = 1; f.Cg = C; f.Kg = K;
+    f.Ho = 1; f.Wo = 1;
+    f.x_elems = rows * C; f.w_elems = (int64_t)K * C; f.y_elems = rows * K;
+    return f;
+}
+
+Shape effective_shape(const Shape& s, int op, bool* staged)
+{
+    *staged = false;
+    if (!s.nhwc) return s;
+    // (rows beyond 2^30 are refused by the prologue)
+    if (op == GCONV_OP_BWD_BIAS) return flat_rows(s, std::min<int64_t>((int64_t)s.N * s.Ho * s.Wo, 1 << 30), s.K, s.K);
+    if (nhwc_as_gemm(s)) {
+        const Shape f = flat_rows(s, (int64_t)s.N * s.H * s.W, s.C, s.K);
+        if (fc_supported(f)) return f;
+    }
+    Shape e = s;
+    e.nhwc = 0;
+    *staged = true;
+    return e;
+}
+
+constexpr size_t kStageAlign = 256;
+size_t stage_bytes(int64_t elems) { return ((size_t)elems * 4 + kStageAlign - 1) / kStageAlign * kStageAlign; }
+
+// Workspace of a staged op: its two NCHW copies, then the NCHW op's own.
+size_t staging_bytes(const Shape& s, int op)
+{
+    switch (op) {
+        case GCONV_OP_FWD: return stage_bytes(s.x_elems) + stage_bytes(s.y_elems);
+        case GCONV_OP_BWD_DATA: return stage_bytes(s.y_elems) + stage_bytes(s.x_elems);
+        case GCONV_OP_BWD_FILTER: return stage_bytes(s.x_elems) + stage_bytes(s.y_elems);
+        default: return 0;
+    }
 }
 
 // ---- routing ----------------------------------------------------------------
@@ -178,27 +240,111 @@ size_t workspace_for(const Shape& s, int op, int path)
         return smallgroup_bwd_filter_workspace(s);
     if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_POINTWISE && s.N > 0)
         return pointwise_bwd_filter_workspace(s);
+    if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_FC && s.N > 0)
+        return fc_bwd_filter_workspace(s);
     if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_DIRECT && s.N > 0)
         return direct_bwd_filter_workspace(s);
     return 0;
 }
 
-// Common prologue of the four ops: shape, path, workspace checks.
-int prologue(const gconv_desc* d, int op, Shape* s, int* path, void* ws, size_t ws_bytes)
+// Common prologue of the four ops: shape, effective (NCHW) shape, path,
+// workspace checks.
+struct Prep {
+    Shape s;      // the descriptor's shape
+    Shape e;      // the NCHW shape the kernels run (== s for NCHW)
+    int path;
+    bool staged;  // NHWC activations reordered through the workspace
+};
+
+int prologue(const gconv_desc* d, int op, Prep* p, void* ws, size_t ws_bytes)
 {
-    int st = make_shape(d, s);
+    int st = make_shape(d, &p->s);
     if (st != GCONV_OK) return st;
-    *path = choose_path(*s, op);
-    if (!path_supports(*path, *s, op))
+    if (p->s.nhwc && op == GCONV_OP_BWD_BIAS && (int64_t)p->s.N * p->s.Ho * p->s.Wo >= (int64_t(1) << 30))
+        return fail(GCONV_ERR_UNSUPPORTED, "NHWC gradBias over 2^30 or more rows");
+    p->e = effective_shape(p->s, op, &p->staged);
+    p->path = choose_path(p->e, op);
+    if (!path_supports(p->path, p->e, op))
         return fail(GCONV_ERR_UNSUPPORTED, "forced path %d cannot run this descriptor for op %d",
-                    *path, op);
-    const size_t need = workspace_for(*s, op, *path);
+                    p->path, op);
+    const size_t need = workspace_for(p->e, op, p->path) + (p->staged ? staging_bytes(p->s, op) : 0);
     if (ws_bytes < need || (need > 0 && ws == nullptr))
         return fail(GCONV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes,
                     need);
     // Partial sums are read back with 16-byte loads.
     if (need > 0 && ((uintptr_t)ws & 15) != 0)
         return fail(GCONV_ERR_WORKSPACE, "workspace pointer %p is not 16-byte aligned", ws);
+    return GCONV_OK;
+}
+
+// The kernels of one op on an NCHW shape.
+int run_fwd(const Shape& s, int path, const float* x, const float* w, const float* bias, float* y,
+            hipStream_t hs)
+{
+    switch (path) {
+        case GCONV_PATH_DIRECT: direct_fwd(s, x, w, bias, y, hs); return GCONV_OK;
+        case GCONV_PATH_IGEMM:
+            if (!igemm_fwd(s, x, w, bias, y, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            return GCONV_OK;
+        case GCONV_PATH_FC: fc_fwd(s, x, w, bias, y, hs); return GCONV_OK;
+        case GCONV_PATH_POINTWISE: pointwise_fwd(s, x, w, bias, y, hs); return GCONV_OK;
+        case GCONV_PATH_SMALLGROUP:
+            if (!smallgroup_fwd(s, x, w, bias, y, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
+            return GCONV_OK;
+        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    }
+}
+
+int run_bwd_data(const Shape& s, int path, const float* dy, const float* w, float* dx, hipStream_t hs)
+{
+    switch (path) {
+        case GCONV_PATH_DIRECT: direct_bwd_data(s, dy, w, dx, hs); return GCONV_OK;
+        case GCONV_PATH_IGEMM:
+            if (!igemm_bwd_data(s, dy, w, dx, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            return GCONV_OK;
+        case GCONV_PATH_FC: fc_bwd_data(s, dy, w, dx, hs); return GCONV_OK;
+        case GCONV_PATH_POINTWISE: pointwise_bwd_data(s, dy, w, dx, hs); return GCONV_OK;
+        case GCONV_PATH_SMALLGROUP:
+            if (!smallgroup_bwd_data(s, dy, w, dx, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
+            return GCONV_OK;
+        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    }
+}
+
+int run_bwd_filter(const Shape& s, int path, const float* x, const float* dy, float* dw, float* ws,
+                   hipStream_t hs)
+{
+    switch (path) {
+        case GCONV_PATH_DIRECT: direct_bwd_filter(s, x, dy, dw, ws, hs); return GCONV_OK;
+        case GCONV_PATH_IGEMM:
+            if (!igemm_bwd_filter(s, x, dy, dw, ws, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            return GCONV_OK;
+        case GCONV_PATH_FC:
+            if (!fc_bwd_filter(s, x, dy, dw, ws, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "fully-connected gradWeight needs its workspace");
+            return GCONV_OK;
+        case GCONV_PATH_POINTWISE:
+            if (!pointwise_bwd_filter(s, x, dy, dw, ws, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "pointwise gradWeight needs its workspace");
+            return GCONV_OK;
+        case GCONV_PATH_SMALLGROUP:
+            if (!smallgroup_bwd_filter(s, x, dy, dw, ws, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
+            return GCONV_OK;
+        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    }
+}
+
+// NHWC [N][R][Cc] -> NCHW [N][Cc][R] (or back, with R and Cc swapped).
+int reorder(const float* src, float* dst, int64_t N, int64_t R, int64_t Cc, hipStream_t hs)
+{
+    if (!transpose_batched(src, dst, N, R, Cc, hs))
+        return fail(GCONV_ERR_UNSUPPORTED, "layout reordering extent exceeds 2^30");
     return GCONV_OK;
 }
 
@@ -235,7 +381,9 @@ int gconv_workspace_size(const gconv_desc* d, int op, size_t* bytes)
     if (st != GCONV_OK) return st;
     if (!bytes) return fail(GCONV_ERR_NULL, "bytes pointer is NULL");
     if (op < GCONV_OP_FWD || op > GCONV_OP_BWD_BIAS) return fail(GCONV_ERR_ARG, "bad op %d", op);
-    *bytes = workspace_for(s, op, choose_path(s, op));
+    bool staged;
+    const Shape e = effective_shape(s, op, &staged);
+    *bytes = workspace_for(e, op, choose_path(e, op)) + (staged ? staging_bytes(s, op) : 0);
     return GCONV_OK;
 }
 
@@ -246,7 +394,8 @@ int gconv_select_path(const gconv_desc* d, int op, int* path)
     if (st != GCONV_OK) return st;
     if (!path) return fail(GCONV_ERR_NULL, "path pointer is NULL");
     if (op < GCONV_OP_FWD || op > GCONV_OP_BWD_BIAS) return fail(GCONV_ERR_ARG, "bad op %d", op);
-    *path = choose_path(s, op);
+    bool staged;
+    *path = choose_path(effective_shape(s, op, &staged), op);
     return GCONV_OK;
 }
 
@@ -267,13 +416,13 @@ int gconv_fwd(const gconv_desc* d, const float* x, const float* w, const float* 
 int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const float* bias, int act,
                  float* y, void* workspace, size_t workspace_bytes, void* stream)
 {
-    Shape s;
-    int path;
+    Prep p;
     if (act != GCONV_EPILOGUE_NONE && act != GCONV_EPILOGUE_RELU)
         return fail(GCONV_ERR_ARG, "unknown epilogue %d", act);
-    int st = prologue(d, GCONV_OP_FWD, &s, &path, workspace, workspace_bytes);
+    int st = prologue(d, GCONV_OP_FWD, &p, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
-    s.relu = act == GCONV_EPILOGUE_RELU;
+    const Shape& s = p.s;
+    p.e.relu = act == GCONV_EPILOGUE_RELU;
     if (!w || (s.N > 0 && (!x || !y)))
         return fail(GCONV_ERR_NULL, "x, w and y must be non-NULL");
     if (overlap(y, s.y_elems, x, s.x_elems) || overlap(y, s.y_elems, w, s.w_elems) ||
@@ -282,30 +431,26 @@ int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const floa
     hipStream_t hs = (hipStream_t)stream;
     (void)hipGetLastError();
     if (s.N == 0) return epilogue();
-    switch (path) {
-        case GCONV_PATH_DIRECT: direct_fwd(s, x, w, bias, y, hs); break;
-        case GCONV_PATH_IGEMM:
-            if (!igemm_fwd(s, x, w, bias, y, hs))
-                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
-            break;
-        case GCONV_PATH_FC: fc_fwd(s, x, w, bias, y, hs); break;
-        case GCONV_PATH_POINTWISE: pointwise_fwd(s, x, w, bias, y, hs); break;
-        case GCONV_PATH_SMALLGROUP:
-            if (!smallgroup_fwd(s, x, w, bias, y, hs))
-                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
-            break;
-        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    if (!p.staged) {
+        st = run_fwd(p.e, p.path, x, w, bias, y, hs);
+    } else {
+        char* base = (char*)workspace;
+        float* xs = (float*)base;
+        float* ys = (float*)(base + stage_bytes(s.x_elems));
+        st = reorder(x, xs, s.N, (int64_t)s.H * s.W, s.C, hs);
+        if (st == GCONV_OK) st = run_fwd(p.e, p.path, xs, w, bias, ys, hs);
+        if (st == GCONV_OK) st = reorder(ys, y, s.N, s.K, (int64_t)s.Ho * s.Wo, hs);
     }
-    return epilogue();
+    return st != GCONV_OK ? st : epilogue();
 }
 
 int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* dx,
                    void* workspace, size_t workspace_bytes, void* stream)
 {
-    Shape s;
-    int path;
-    int st = prologue(d, GCONV_OP_BWD_DATA, &s, &path, workspace, workspace_bytes);
+    Prep p;
+    int st = prologue(d, GCONV_OP_BWD_DATA, &p, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
+    const Shape& s = p.s;
     if (!w || (s.N > 0 && (!dy || !dx)))
         return fail(GCONV_ERR_NULL, "dy, w and dx must be non-NULL");
     if (overlap(dx, s.x_elems, dy, s.y_elems) || overlap(dx, s.x_elems, w, s.w_elems))
@@ -313,30 +458,26 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
     hipStream_t hs = (hipStream_t)stream;
     (void)hipGetLastError();
     if (s.N == 0) return epilogue();
-    switch (path) {
-        case GCONV_PATH_DIRECT: direct_bwd_data(s, dy, w, dx, hs); break;
-        case GCONV_PATH_IGEMM:
-            if (!igemm_bwd_data(s, dy, w, dx, hs))
-                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
-            break;
-        case GCONV_PATH_FC: fc_bwd_data(s, dy, w, dx, hs); break;
-        case GCONV_PATH_POINTWISE: pointwise_bwd_data(s, dy, w, dx, hs); break;
-        case GCONV_PATH_SMALLGROUP:
-            if (!smallgroup_bwd_data(s, dy, w, dx, hs))
-                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
-            break;
-        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    if (!p.staged) {
+        st = run_bwd_data(p.e, p.path, dy, w, dx, hs);
+    } else {
+        char* base = (char*)workspace;
+        float* dys = (float*)base;
+        float* dxs = (float*)(base + stage_bytes(s.y_elems));
+        st = reorder(dy, dys, s.N, (int64_t)s.Ho * s.Wo, s.K, hs);
+        if (st == GCONV_OK) st = run_bwd_data(p.e, p.path, dys, w, dxs, hs);
+        if (st == GCONV_OK) st = reorder(dxs, dx, s.N, s.C, (int64_t)s.H * s.W, hs);
     }
-    return epilogue();
+    return st != GCONV_OK ? st : epilogue();
 }
 
 int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float* dw,
                      void* workspace, size_t workspace_bytes, void* stream)
 {
-    Shape s;
-    int path;
-    int st = prologue(d, GCONV_OP_BWD_FILTER, &s, &path, workspace, workspace_bytes);
+    Prep p;
+    int st = prologue(d, GCONV_OP_BWD_FILTER, &p, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
+    const Shape& s = p.s;
     if (!dw || (s.N > 0 && (!x || !dy)))
         return fail(GCONV_ERR_NULL, "x, dy and dw must be non-NULL");
     if (overlap(dw, s.w_elems, x, s.x_elems) || overlap(dw, s.w_elems, dy, s.y_elems))
@@ -347,33 +488,27 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
         fill_zero(dw, s.w_elems, hs);  // a sum over no images
         return epilogue();
     }
-    switch (path) {
-        case GCONV_PATH_DIRECT: direct_bwd_filter(s, x, dy, dw, (float*)workspace, hs); break;
-        case GCONV_PATH_IGEMM:
-            if (!igemm_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
-                return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
-            break;
-        case GCONV_PATH_FC: fc_bwd_filter(s, x, dy, dw, hs); break;
-        case GCONV_PATH_POINTWISE:
-            if (!pointwise_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
-                return fail(GCONV_ERR_UNSUPPORTED, "pointwise gradWeight needs its workspace");
-            break;
-        case GCONV_PATH_SMALLGROUP:
-            if (!smallgroup_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
-                return fail(GCONV_ERR_UNSUPPORTED, "no small-group kernel instance for this shape");
-            break;
-        default: return fail(GCONV_ERR_UNSUPPORTED, "no kernel for path %d", path);
+    if (!p.staged) {
+        st = run_bwd_filter(p.e, p.path, x, dy, dw, (float*)workspace, hs);
+    } else {
+        char* base = (char*)workspace;
+        float* xs = (float*)base;
+        float* dys = (float*)(base + stage_bytes(s.x_elems));
+        float* rest = (float*)(base + staging_bytes(s, GCONV_OP_BWD_FILTER));
+        st = reorder(x, xs, s.N, (int64_t)s.H * s.W, s.C, hs);
+        if (st == GCONV_OK) st = reorder(dy, dys, s.N, (int64_t)s.Ho * s.Wo, s.K, hs);
+        if (st == GCONV_OK) st = run_bwd_filter(p.e, p.path, xs, dys, dw, rest, hs);
     }
-    return epilogue();
+    return st != GCONV_OK ? st : epilogue();
 }
 
 int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* workspace,
                    size_t workspace_bytes, void* stream)
 {
-    Shape s;
-    int path;
-    int st = prologue(d, GCONV_OP_BWD_BIAS, &s, &path, workspace, workspace_bytes);
+    Prep p;
+    int st = prologue(d, GCONV_OP_BWD_BIAS, &p, workspace, workspace_bytes);
     if (st != GCONV_OK) return st;
+    const Shape& s = p.s;
     if (!db || (s.N > 0 && !dy)) return fail(GCONV_ERR_NULL, "dy and db must be non-NULL");
     if (overlap(db, s.K, dy, s.y_elems)) return fail(GCONV_ERR_ARG, "db overlaps dy");
     hipStream_t hs = (hipStream_t)stream;
@@ -382,7 +517,8 @@ int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* worksp
         fill_zero(db, s.K, hs);
         return epilogue();
     }
-    bias_reduce(s, dy, db, (float*)workspace, hs);
+    // NHWC: the effective shape reads dy as [N*Ho*Wo, K] rows.
+    bias_reduce(p.e, dy, db, (float*)workspace, hs);
     return epilogue();
 }
 
@@ -403,6 +539,6 @@ const char* gconv_status_string(int status)
 
 const char* gconv_last_error(void) { return g_last_error.c_str(); }
 
-int gconv_version(void) { return 100; }
+int gconv_version(void) { return 110; }
 
 }  // extern "C"

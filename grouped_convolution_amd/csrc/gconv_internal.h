@@ -23,6 +23,7 @@ struct Shape {
     // element counts (64-bit) of x, w, y
     int64_t x_elems, w_elems, y_elems;
     int relu = 0;   // forward only: y = max(conv + bias, 0)
+    int nhwc = 0;   // activations channels-last (gconv_layout NHWC)
 };
 
 // The forward epilogue's activation: max(v, 0), with 0 (not NaN) for NaN.
@@ -87,7 +88,8 @@ bool fc_supported(const Shape& s);
 void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
             hipStream_t st);
 void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
-void fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st);
+bool fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st);
+size_t fc_bwd_filter_workspace(const Shape& s);
 
 // ---- pointwise (1x1, stride 1, no padding): batched fp32-MFMA GEMMs --------------
 bool pointwise_supported(const Shape& s);
@@ -101,6 +103,9 @@ bool pointwise_bwd_filter(const Shape& s, const float* x, const float* dy, float
 // ---- reductions -------------------------------------------------------------
 // db[k] = sum over (n, p < P) of dy[(n*K + k)*P + p], P = Ho*Wo.
 size_t bias_workspace_bytes(const Shape& s);
+// dst[n] = src[n]^T for N row-major [R][Cc] matrices (NHWC <-> NCHW); false if
+// the extents do not fit the kernel's 32-bit indices.
+bool transpose_batched(const float* src, float* dst, int64_t N, int64_t R, int64_t Cc, hipStream_t st);
 void bias_reduce(const Shape& s, const float* dy, float* db, float* ws, hipStream_t st);
 // Fill `count` floats with zero (outputs of empty-batch reductions).
 void fill_zero(float* p, int64_t count, hipStream_t st);

@@ -337,19 +337,67 @@ void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hip
     launch<true, false>(a, st);
 }
 
-// dw[g*Kg + k, d] = sum_n dy[n, g*Kg + k] * x[n, g*D + d]
-void fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, hipStream_t st)
+// Reduction slices of a gradWeight GEMM over R rows with `tiles` output tiles:
+// enough slices for about 512 workgroups, each slice at least 8 stages deep
+// and a multiple of the stage depth (one slice when the tiles alone fill the
+// chip, as in the fully-connected layer of the cudnn.torch issue).
+static void split_rows(int64_t R, int64_t tiles, int* nsplit, int* r_split)
+{
+    int64_t want = std::max<int64_t>(1, (512 + tiles - 1) / tiles);
+    want = std::min<int64_t>(want, std::max<int64_t>(1, R / (8 * BR)));
+    int64_t rs = (R + want - 1) / want;
+    rs = (rs + BR - 1) / BR * BR;
+    *r_split = (int)rs;
+    *nsplit = (int)((R + rs - 1) / rs);
+}
+
+static void fc_split(const Shape& s, int* nsplit, int* r_split)
+{
+    const int64_t D = (int64_t)s.Cg * s.kh * s.kw;
+    split_rows(s.N, (int64_t)((s.Kg + BM - 1) / BM) * ((D + BN - 1) / BN) * s.G, nsplit, r_split);
+}
+
+size_t fc_bwd_filter_workspace(const Shape& s)
+{
+    int nsplit, r_split;
+    fc_split(s, &nsplit, &r_split);
+    return nsplit > 1 ? (size_t)nsplit * (size_t)s.w_elems * 4 : 0;
+}
+
+static void split_reduce(const float* ws, float* dw, int64_t E, int nsplit, hipStream_t st)
+{
+    if ((E & 3) == 0 && ((uintptr_t)dw & 15) == 0) {
+        hipLaunchKernelGGL(gemm_split_reduce<f4>, dim3((unsigned)((E / 4 + 15) / 16)), dim3(256), 0, st,
+                           (const f4*)ws, (f4*)dw, E / 4, nsplit);
+    } else {
+        hipLaunchKernelGGL(gemm_split_reduce<float>, dim3((unsigned)((E + 15) / 16)), dim3(256), 0, st, ws, dw,
+                           E, nsplit);
+    }
+}
+
+// dw[g*Kg + k, d] = sum_n dy[n, g*Kg + k] * x[n, g*D + d]; with few output
+// tiles (many rows: a 1x1 layer over N*H*W channels-last pixels) the rows are
+// split over workgroup slices whose partials are added in slice order.
+bool fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st)
 {
     const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
+    int nsplit, r_split;
+    fc_split(s, &nsplit, &r_split);
+    if (nsplit > 1 && !ws) return false;
     GemmArgs a{};
-    a.A = dy; a.B = x; a.bias = nullptr; a.C = dw;
+    a.A = dy; a.B = x; a.bias = nullptr; a.C = nsplit > 1 ? ws : dw;
     a.M = s.Kg; a.N = D; a.R = s.N; a.Z = s.G;
     plain(a);
     a.a_ld = s.K; a.b_ld = Dt; a.c_ld = D;
     a.a_gs = s.Kg; a.b_gs = D; a.c_gs = (int64_t)s.Kg * D; a.bias_gs = 0;
     a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.K + s.Kg) * 4);
     a.b_bytes = (uint32_t)(((int64_t)(s.N - 1) * Dt + D) * 4);
+    a.nsplit = nsplit;
+    a.r_split = r_split;
+    a.c_split = s.w_elems;
     launch<false, false>(a, st);
+    if (nsplit > 1) split_reduce(ws, dw, s.w_elems, nsplit, st);
+    return true;
 }
 
 // ---- pointwise (1x1, stride 1, no padding) ------------------------------------
@@ -374,18 +422,11 @@ bool pointwise_supported(const Shape& s)
            extent_ok(s.N, (int64_t)s.K * P, (int64_t)s.Kg * P) && extent_ok(s.Kg, s.Cg, s.Cg);
 }
 
-// Reduction slices of the gradWeight GEMM: about 512 workgroups, each slice at
-// least 8 stages deep, a multiple of the stage depth.
+// Reduction slices of the pointwise gradWeight GEMM (over every image's pixels).
 static void pointwise_split(const Shape& s, int* nsplit, int* r_split)
 {
-    const int64_t R = (int64_t)s.N * s.H * s.W;
-    const int64_t tiles = (int64_t)((s.Kg + BM - 1) / BM) * ((s.Cg + BN - 1) / BN) * s.G;
-    int64_t want = std::max<int64_t>(1, (512 + tiles - 1) / tiles);
-    want = std::min<int64_t>(want, std::max<int64_t>(1, R / (8 * BR)));
-    int64_t rs = (R + want - 1) / want;
-    rs = (rs + BR - 1) / BR * BR;
-    *r_split = (int)rs;
-    *nsplit = (int)((R + rs - 1) / rs);
+    split_rows((int64_t)s.N * s.H * s.W, (int64_t)((s.Kg + BM - 1) / BM) * ((s.Cg + BN - 1) / BN) * s.G,
+               nsplit, r_split);
 }
 
 size_t pointwise_bwd_filter_workspace(const Shape& s)
@@ -454,16 +495,7 @@ bool pointwise_bwd_filter(const Shape& s, const float* x, const float* dy, float
     a.r_split = r_split;
     a.c_split = s.w_elems;
     launch<true, true, true>(a, st);
-    if (nsplit > 1) {
-        const int64_t E = s.w_elems;
-        if ((E & 3) == 0 && ((uintptr_t)dw & 15) == 0) {
-            hipLaunchKernelGGL(gemm_split_reduce<f4>, dim3((unsigned)((E / 4 + 15) / 16)), dim3(256), 0, st,
-                               (const f4*)ws, (f4*)dw, E / 4, nsplit);
-        } else {
-            hipLaunchKernelGGL(gemm_split_reduce<float>, dim3((unsigned)((E + 15) / 16)), dim3(256), 0, st,
-                               (const float*)ws, dw, E, nsplit);
-        }
-    }
+    if (nsplit > 1) split_reduce(ws, dw, s.w_elems, nsplit, st);
     return true;
 }
 

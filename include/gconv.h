@@ -22,6 +22,9 @@
  *   bias, db [K]
  *   y, dy  [N, K, Ho, Wo],  Ho = floor((H + pad_h + pad_h_end - dil_h*(kh-1) - 1)/stride_h) + 1
  *                           (likewise Wo), pad_h_end = pad_h + pad_h_extra
+ * or, with layout = GCONV_LAYOUT_NHWC (channels last, the layout the
+ * DLPrimitives Blog measures oneDNN fastest in), x, dx [N, H, W, C] and
+ * y, dy [N, Ho, Wo, K]; w, dw and the bias keep their layouts.
  *
  * Ownership and execution. The caller owns every buffer; the library never
  * allocates device memory. Every op is enqueued on the caller's HIP stream
@@ -57,6 +60,7 @@ extern "C" {
  * (nInputPlane, nOutputPlane, kW, kH, dW, dH, padW, padH, groups), plus
  * batch, input extent and dilation. Valid when N >= 0, C,H,W,K,kh,kw >= 1,
  * stride >= 1, dil >= 1, pad >= 0, pad + pad_extra >= 0, groups >= 1,
+ * layout a gconv_layout,
  * C % groups == 0, K % groups == 0 and Ho, Wo >= 1 ("Support groups in
  * DenseConvDims": the channel counts must agree with the tensors and with the
  * group split).
@@ -78,7 +82,22 @@ typedef struct gconv_desc {
     int64_t dil_h, dil_w;
     int64_t groups;
     int64_t pad_h_extra, pad_w_extra;  /* end padding minus start padding (0: symmetric) */
+    int64_t layout;                    /* gconv_layout of x, dx, y, dy (0: NCHW) */
 } gconv_desc;
+
+/*
+ * Activation layout. NHWC: a 1x1 stride-1 unpadded layer with one group is
+ * one GEMM over the N*H*W rows (the fully-connected path, no reordering);
+ * gradBias sums the [N*Ho*Wo, K] rows of dy directly. Every other NHWC op
+ * reorders its NHWC inputs to NCHW in the workspace, runs the NCHW kernels
+ * there and reorders the NHWC outputs back, so gconv_workspace_size() then
+ * includes those copies (x and y for the forward pass, dy and dx for
+ * gradInput, x and dy for gradWeight).
+ */
+typedef enum gconv_layout {
+    GCONV_LAYOUT_NCHW = 0,
+    GCONV_LAYOUT_NHWC = 1
+} gconv_layout;
 
 typedef enum gconv_status {
     GCONV_OK = 0,

@@ -21,18 +21,24 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
 
 
-def gpu_all_ops(x, w, b, dy, stride, padding, dilation, groups):
-    """Run fwd, bwd_data, bwd_filter, bwd_bias on the GPU; return torch tensors."""
+def gpu_all_ops(x, w, b, dy, stride, padding, dilation, groups, layout="nchw"):
+    """Run fwd, bwd_data, bwd_filter, bwd_bias on the GPU; return torch tensors.
+    x and dy are NCHW arrays; with layout="nhwc" they are stored channels-last
+    for the GPU, and y and dx are returned moved back to NCHW for comparison."""
     import torch
     import grouped_convolution_amd as G
-    xd, wd, dyd = dev(x), dev(w), dev(dy)
+    nhwc = layout == "nhwc"
+    store = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1))) if nhwc else (lambda a: a)
+    xd, wd, dyd = dev(store(x)), dev(w), dev(store(dy))
     bd = None if b is None else dev(b)
-    kw = dict(stride=stride, padding=padding, dilation=dilation, groups=groups)
+    kw = dict(stride=stride, padding=padding, dilation=dilation, groups=groups, layout=layout)
     y = G.gconv_fwd(xd, wd, bd, **kw)
-    dx = G.gconv_bwd_data(dyd, wd, x.shape, **kw)
+    dx = G.gconv_bwd_data(dyd, wd, store(x).shape, **kw)
     dw = G.gconv_bwd_filter(xd, dyd, w.shape, **kw)
-    db = G.gconv_bwd_bias(dyd)
+    db = G.gconv_bwd_bias(dyd, layout=layout)
     torch.cuda.synchronize()
+    if nhwc:
+        y, dx = y.permute(0, 3, 1, 2).contiguous(), dx.permute(0, 3, 1, 2).contiguous()
     return y, dx, dw, db
 
 

@@ -41,9 +41,10 @@ def test_library_exports_every_declared_symbol():
 def test_desc_layout_matches_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct gconv_desc \{(.*?)\} gconv_desc;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     fields = re.findall(r"(\w+)(?=[,;])", re.sub(r"int64_t", "", body))
     assert fields == [f for f, _ in B.gconv_desc._fields_]
-    assert ctypes.sizeof(B.gconv_desc) == 16 * 8
+    assert ctypes.sizeof(B.gconv_desc) == 17 * 8
 
 
 def test_output_dims_match_oracle_random():
@@ -207,3 +208,29 @@ def test_workload_output_shapes():
         assert oracle.output_dims(N, C, H, W, K, kh, kw, wl.stride, wl.padding, wl.dilation,
                                   wl.groups) == tuple(wl.dy_shape[2:]), wl.name
         assert wl.dy_shape[:2] == (N, K), wl.name
+
+
+def test_layout_field():
+    """An unknown layout is refused before anything runs; NHWC needs workspace
+    for its NCHW copies except where it is one GEMM (1x1, stride 1, no padding,
+    one group) or gradBias (column sums of the [N*Ho*Wo, K] rows)."""
+    lib = B.load()
+    desc = B.make_desc(2, 8, 7, 7, 8, 3, 3, groups=2)
+    desc.layout = 2
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.gconv_fwd(ctypes.byref(desc), fake, fake, None, fake, None, 0, None) == 7
+    assert b"layout" in lib.gconv_last_error()
+    with pytest.raises(ValueError):
+        B.make_desc(2, 8, 7, 7, 8, 3, 3, layout="chwn")
+    nchw = B.make_desc(2, 8, 7, 7, 8, 3, 3, groups=2)
+    nhwc = B.make_desc(2, 8, 7, 7, 8, 3, 3, groups=2, layout="nhwc")
+    x_bytes, y_bytes = 2 * 8 * 7 * 7 * 4, 2 * 8 * 5 * 5 * 4
+    for op in (B.OP_FWD, B.OP_BWD_DATA, B.OP_BWD_FILTER):
+        assert B.gconv_workspace_size(nhwc, op) >= B.gconv_workspace_size(nchw, op) + x_bytes + y_bytes
+        assert B.gconv_select_path(nhwc, op) == B.gconv_select_path(nchw, op)
+    gemm = B.make_desc(3, 16, 5, 6, 24, 1, 1, layout="nhwc")
+    for op in (B.OP_FWD, B.OP_BWD_DATA, B.OP_BWD_FILTER):
+        assert B.gconv_select_path(gemm, op) == B.PATH_FC
+        assert B.gconv_workspace_size(gemm, op) == 0
+    # gradBias of NHWC dy: the split partials of the column layout
+    assert B.gconv_workspace_size(nhwc, B.OP_BWD_BIAS) > 0

@@ -1,0 +1,176 @@
+"""GPU parity of the channels-last (NHWC) layout against the CPU oracle.
+
+The oracle computes in NCHW; here the NHWC activations are the same values
+with the channel axis last, so the reference is the oracle's result moved to
+that layout (a numpy transpose of test data, no arithmetic). Bar as for NCHW:
+|gpu - oracle| <= 1e-5 * A_e + 1e-6 per element, exact for integer data.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from cases import conv_kwargs, random_descs, tensors
+from gpu_util import check, dev, say
+from grouped_convolution_amd.workloads import draw
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import grouped_convolution_amd as G  # noqa: E402
+
+OPS = ("fwd", "bwd_data", "bwd_filter", "bwd_bias")
+
+
+def to_nhwc(a):
+    return np.ascontiguousarray(a.transpose(0, 2, 3, 1))
+
+
+@pytest.fixture(autouse=True)
+def _auto_path():
+    G.gconv_set_path_override(G.PATH_AUTO)
+    yield
+    G.gconv_set_path_override(G.PATH_AUTO)
+
+
+def refs(x, w, b, dy, kw):
+    """Oracle (value, A_e) per op, with activations moved to NHWC."""
+    y, ya = oracle.fwd(x, w, b, **kw)
+    dx, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+    return {"fwd": (to_nhwc(y), to_nhwc(ya)), "bwd_data": (to_nhwc(dx), to_nhwc(dxa)),
+            "bwd_filter": oracle.bwd_filter(x, dy, w.shape, **kw), "bwd_bias": oracle.bwd_bias(dy)}
+
+
+def gpu_nhwc(x, w, b, dy, kw):
+    """The four ops on NHWC copies of x and dy (NCHW numpy inputs)."""
+    xd, wd, dyd = dev(to_nhwc(x)), dev(w), dev(to_nhwc(dy))
+    bd = None if b is None else dev(b)
+    out = {}
+    for op, fn in (("fwd", lambda: G.gconv_fwd(xd, wd, bd, layout="nhwc", **kw)),
+                   ("bwd_data", lambda: G.gconv_bwd_data(dyd, wd, to_nhwc(x).shape, layout="nhwc", **kw)),
+                   ("bwd_filter", lambda: G.gconv_bwd_filter(xd, dyd, w.shape, layout="nhwc", **kw)),
+                   ("bwd_bias", lambda: G.gconv_bwd_bias(dyd, layout="nhwc"))):
+        try:
+            out[op] = fn()
+        except G.GconvError as e:
+            if "GCONV_ERR_UNSUPPORTED" not in str(e):
+                raise
+            out[op] = None
+    torch.cuda.synchronize()
+    return out
+
+
+def compare(tag, got, ref):
+    done = []
+    for op in OPS:
+        if got[op] is None:
+            continue
+        val, mag = ref[op]
+        assert tuple(got[op].shape) == val.shape, (tag, op, tuple(got[op].shape), val.shape)
+        check("%s %s" % (tag, op), got[op].cpu().numpy(), val, mag)
+        done.append(op)
+    return done
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_nhwc_random_descriptors_every_family(seed):
+    """Random descriptors (strides, pads, dilation, groups) in NHWC on the
+    dispatcher's choice and on each forced family."""
+    for d in random_descs(3100 + seed, 12, max_hw=12, max_k=5, max_cg=6, max_kg=6, max_g=4):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 3200 + seed)
+        y_ref, _ = oracle.fwd(x, w, b, **kw)
+        dy = draw(("normal", 1.0), y_ref.shape, 3300 + seed)
+        ref = refs(x, w, b, dy, kw)
+        covered = set()
+        for path in (G.PATH_AUTO, G.PATH_DIRECT, G.PATH_SMALLGROUP, G.PATH_IGEMM):
+            say("nhwc desc %s path %s" % (d, G.PATH_NAMES[path]))
+            G.gconv_set_path_override(path)
+            try:
+                covered |= set(compare("nhwc %s %s" % (G.PATH_NAMES[path], d), gpu_nhwc(x, w, b, dy, kw), ref))
+            finally:
+                G.gconv_set_path_override(G.PATH_AUTO)
+        assert covered == set(OPS)
+
+
+NHWC_CASES = [
+    # dense 3x3 (MFMA implicit GEMM between the reorderings), several 64-wide tiles
+    # of pixels and channels with ragged tails
+    (dict(N=3, C=70, K=66, H=13, W=11, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1),
+     {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "igemm", "bwd_bias": "direct"}),
+    # ResNeXt-style 4 per group and depthwise stride 2 (small-group family)
+    (dict(N=2, C=32, K=32, H=14, W=15, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    (dict(N=2, C=12, K=12, H=17, W=16, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=12),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # 1x1, one group: one GEMM over the N*H*W pixel rows (fully-connected path)
+    (dict(N=3, C=40, K=72, H=9, W=10, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+     {"fwd": "fc", "bwd_data": "fc", "bwd_filter": "fc"}),
+    # 1x1 with two groups: reordered around the pointwise GEMMs
+    (dict(N=2, C=32, K=48, H=7, W=9, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=2),
+     {"fwd": "pointwise", "bwd_data": "pointwise", "bwd_filter": "pointwise"}),
+    # kernel == input (fully-connected mode) in NHWC
+    (dict(N=5, C=8, K=20, H=4, W=3, kh=4, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+     {"fwd": "fc", "bwd_data": "fc", "bwd_filter": "fc"}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(NHWC_CASES)))
+def test_nhwc_cases(case):
+    """NHWC on the dispatcher's own family (asserted): normal data to the
+    tolerance, integer data bit for bit."""
+    d, paths = NHWC_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout="nhwc", **kw)
+    for op, name in paths.items():
+        chosen = G.gconv_select_path(desc, getattr(G, "OP_" + op.upper()))
+        assert G.PATH_NAMES[chosen] == name, (d, op, G.PATH_NAMES[chosen])
+    say("nhwc case %s" % d)
+    x, w, b = tensors(d, 3400 + case)
+    y_ref, _ = oracle.fwd(x, w, b, **kw)
+    dy = draw(("normal", 1.0), y_ref.shape, 3410 + case)
+    assert compare("nhwc %s" % d, gpu_nhwc(x, w, b, dy, kw), refs(x, w, b, dy, kw)) == list(OPS)
+    xi, wi, bi = tensors(d, 3500 + case, dist=("int", -3, 3))
+    dyi = draw(("int", -3, 3), y_ref.shape, 3510 + case)
+    got = gpu_nhwc(xi, wi, bi, dyi, kw)
+    ref = refs(xi, wi, bi, dyi, kw)
+    for op in OPS:
+        assert np.array_equal(got[op].cpu().numpy().astype(np.float64), ref[op][0]), (d, op)
+
+
+def test_nhwc_workspace_guard_bands():
+    """The staged ops write only their outputs and their workspace: guard
+    floats around every output and around the workspace stay untouched."""
+    d = dict(N=2, C=24, K=40, H=9, W=8, kh=3, kw=3, sh=2, sw=1, ph=1, pw=0, dh=1, dw=2, G=2)
+    kw = conv_kwargs(d)
+    x, w, b = tensors(d, 3600)
+    y_ref, _ = oracle.fwd(x, w, b, **kw)
+    dy = draw(("normal", 1.0), y_ref.shape, 3610)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout="nhwc", **kw)
+    sentinel = 12345.0
+    for op, name in ((G.OP_FWD, "fwd"), (G.OP_BWD_DATA, "bwd_data"), (G.OP_BWD_FILTER, "bwd_filter")):
+        nws = G.gconv_workspace_size(desc, op)
+        assert nws > 0
+        pad = 64
+        buf = torch.full((pad + nws // 4 + pad,), sentinel, device="cuda")
+        ws = buf[pad:pad + nws // 4]
+        ref = refs(x, w, b, dy, kw)[name]
+        shape = ref[0].shape
+        obuf = torch.full((pad + int(np.prod(shape)) + pad,), sentinel, device="cuda")
+        out = obuf[pad:pad + int(np.prod(shape))].view(*shape)
+        xd, wd, dyd = dev(to_nhwc(x)), dev(w), dev(to_nhwc(dy))
+        if name == "fwd":
+            G.gconv_fwd(xd, wd, dev(b), layout="nhwc", out=out, workspace=ws, **kw)
+        elif name == "bwd_data":
+            G.gconv_bwd_data(dyd, wd, to_nhwc(x).shape, layout="nhwc", out=out, workspace=ws, **kw)
+        else:
+            G.gconv_bwd_filter(xd, dyd, w.shape, layout="nhwc", out=out, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        check("guarded nhwc %s" % name, out.cpu().numpy(), ref[0], ref[1])
+        for t in (buf, obuf):
+            h = t.cpu().numpy()
+            assert np.all(h[:pad] == sentinel) and np.all(h[-pad:] == sentinel), name

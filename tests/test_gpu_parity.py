@@ -422,7 +422,10 @@ def test_asymmetric_padding_cases(case):
     (3, 6, 13, 13),     # one pass, odd plane length (scalar loads)
     (5, 70, 28, 28),    # one pass, 16-byte loads, 70 channels
     (70, 2, 64, 64),    # split partials: more than 1 MiB per channel
-    (700, 40, 1, 1),    # split partials over the rows of a [N, K] gradient
+    (700, 40, 1, 1),    # split partials over the rows of a [N, K] gradient (several rows per wave)
+    (5000, 64, 1, 1),   # ... 64 columns: four rows per wave instruction
+    (300, 1000, 1, 1),  # ... 250 column quads over four column blocks
+    (40, 4100, 1, 1),   # ... wide rows: one thread per column quad
 ])
 def test_bias_reduction_forms(shape):
     """gradBias in each of its forms (one workgroup per channel, or split
@@ -474,7 +477,8 @@ def test_ragged_shapes_span_several_tiles():
 # ----------------------------------------------------------------- the five workloads
 
 REDUCED_BATCH = {"tiny_grouped": 2, "dense3x3": 2, "alexnet_conv2": 2, "resnext_32x4d": 3,
-                 "fc_mode": 24, "resnext_1x1": 2, "mobilenet_dw": 2, "mobilenet_dw_s2_same": 2}
+                 "fc_mode": 24, "resnext_1x1": 2, "mobilenet_dw": 2, "mobilenet_dw_s2_same": 2,
+                 "dense3x3_nhwc": 2, "resnext_1x1_nhwc": 2}
 
 
 def wl_kwargs(wl):
@@ -489,7 +493,7 @@ def test_workload_reduced_batch_full_tensors(name):
     kw = wl_kwargs(wl)
     say("workload %s reduced batch %d" % (name, REDUCED_BATCH[name]))
     ref = oracle_all(inp["x"], inp["w"], inp["b"], inp["dy"], kw)
-    gpu = gpu_all_ops(inp["x"], inp["w"], inp["b"], inp["dy"], **kw)
+    gpu = gpu_all_ops(inp["x"], inp["w"], inp["b"], inp["dy"], layout=wl.layout, **kw)
     compare_full(name, gpu, ref)
 
 
@@ -502,7 +506,7 @@ def test_workload_full_size_sampled(name):
     kw = wl_kwargs(wl)
     x, w, b, dy = inp["x"], inp["w"], inp["b"], inp["dy"]
     say("workload %s full size" % name)
-    y, dx, dw, db = gpu_all_ops(x, w, b, dy, **kw)
+    y, dx, dw, db = gpu_all_ops(x, w, b, dy, layout=wl.layout, **kw)
     assert tuple(y.shape) == wl.dy_shape and tuple(dx.shape) == wl.x_shape
     assert tuple(dw.shape) == wl.w_shape and tuple(db.shape) == (wl.w_shape[0],)
     n = 384
@@ -531,7 +535,7 @@ def test_workload_integer_probes_exact(name):
     b = draw(("int", -3, 3), (wl.w_shape[0],), 13)
     dy = draw(("int", -3, 3), wl.dy_shape, 14)
     say("integer probes %s" % name)
-    y, dx, dw, db = gpu_all_ops(x, w, b, dy, **kw)
+    y, dx, dw, db = gpu_all_ops(x, w, b, dy, layout=wl.layout, **kw)
     iy = sample_indices(y.numel(), 256, 4)
     ix = sample_indices(dx.numel(), 256, 5)
     iw = sample_indices(dw.numel(), 96, 6)
@@ -638,6 +642,10 @@ EDGE_CASES = [
     # ... odd sizes with pad 0 and 1 (the last phase row and column are half outside dx)
     (dict(N=3, C=5, K=5, H=19, W=23, kh=3, kw=3, sh=2, sw=2, ph=0, pw=1, dh=1, dw=1, G=5),
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # fully-connected gradWeight with few output tiles and many rows: the rows
+    # split over workgroup slices, partials added in slice order
+    (dict(N=5000, C=8, K=16, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+     {"fwd": "fc", "bwd_data": "fc", "bwd_filter": "fc"}),
     # direct gradWeight with 1024-thread blocks (at least 16K pixels): depthwise
     # 5x5, and 8 per group at stride 2
     (dict(N=4, C=8, K=8, H=64, W=64, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=8),
