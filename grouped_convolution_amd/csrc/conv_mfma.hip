@@ -29,6 +29,7 @@
 
 #include "device_util.h"
 #include "fastdiv.h"
+#include "gconv.h"
 #include "gconv_internal.h"
 
 namespace gconv {
@@ -274,6 +275,7 @@ struct ConvFlatArgs {
     // column w/uw of the stored Hr x Wr planes; 1, 1 otherwise.
     int uh, uw, Hr, Wr;
     int relu;                   // forward epilogue: max(v, 0)
+    int out_nhwc;               // store the output channels-last, [N][Hout*Wout][Cout_tot]
     FastDiv div_P, div_Wout, div_plane, div_LW;
 };
 
@@ -469,7 +471,16 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
                 v.z = relu_if(v.z, 1);
                 v.w = relu_if(v.w, 1);
             }
-            if (vec4) {
+            if (a.out_nhwc) {
+                // Channels-last output: for each pixel the 16 lanes of a lane
+                // group write 16 consecutive channels (64 bytes).
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int qq = qb + u;
+                    if (qq < q1) a.out[(size_t)qq * a.Cout_tot + ch_off] = vv[u];
+                }
+            } else if (vec4) {
                 // P % 4 == 0 and q0 % 16 == 0: the four pixels share an image.
                 if (qb < q1) {
                     const int n = (int)fastdiv((uint32_t)qb, a.div_P);
@@ -552,6 +563,7 @@ struct Problem {
     bool flip;
     int uh = 1, uw = 1, Hr = 0, Wr = 0;  // input upsampling (flat kernel only), stored plane size
     int relu = 0;                        // forward epilogue
+    int out_nhwc = 0;                    // channels-last output (flat kernel only)
 };
 
 int choose_cc(const Problem& p) { return (p.kh * p.kw >= 16) ? 4 : 8; }
@@ -789,6 +801,7 @@ bool run_flat(const Problem& p, hipStream_t st)
     a.halo = (p.kh - 1) * p.dh + 1;
     a.uh = p.uh; a.uw = p.uw; a.Hr = p.Hr; a.Wr = p.Wr;
     a.relu = p.relu;
+    a.out_nhwc = p.out_nhwc;
     a.div_P = make_fastdiv((uint32_t)a.P);
     a.div_Wout = make_fastdiv((uint32_t)p.Wout);
     a.div_plane = make_fastdiv((uint32_t)fp.plane);
@@ -835,6 +848,33 @@ bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, 
     if (use_flat(p)) return run_flat(p, st);
     if (p.uh != 1 || p.uw != 1) return false;
     return run_problem(p, st);
+}
+
+// The flat kernel stores its output channels-last: the NCHW-input ops of the
+// NHWC layout write y or dx in place, with no reordering after them. False
+// (nothing launched) where the flat kernel does not take the shape.
+bool igemm_nhwc_out_supported(const Shape& s, int op)
+{
+    if (op == GCONV_OP_FWD) return use_flat(fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
+    if (op == GCONV_OP_BWD_DATA) return use_flat(bwd_data_problem(s, nullptr, nullptr, nullptr));
+    return false;
+}
+
+bool igemm_fwd_nhwc_out(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                        hipStream_t st)
+{
+    Problem p = fwd_problem(s, x, w, bias, y);
+    if (!use_flat(p)) return false;
+    p.out_nhwc = 1;
+    return run_flat(p, st);
+}
+
+bool igemm_bwd_data_nhwc_out(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    Problem p = bwd_data_problem(s, dy, w, dx);
+    if (!use_flat(p)) return false;
+    p.out_nhwc = 1;
+    return run_flat(p, st);
 }
 
 }  // namespace gconv

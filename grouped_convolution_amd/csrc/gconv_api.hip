@@ -438,8 +438,14 @@ int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const floa
         float* xs = (float*)base;
         float* ys = (float*)(base + stage_bytes(s.x_elems));
         st = reorder(x, xs, s.N, (int64_t)s.H * s.W, s.C, hs);
-        if (st == GCONV_OK) st = run_fwd(p.e, p.path, xs, w, bias, ys, hs);
-        if (st == GCONV_OK) st = reorder(ys, y, s.N, s.K, (int64_t)s.Ho * s.Wo, hs);
+        // The flat MFMA kernel stores y channels-last itself.
+        if (st == GCONV_OK && p.path == GCONV_PATH_IGEMM && igemm_nhwc_out_supported(p.e, GCONV_OP_FWD)) {
+            if (!igemm_fwd_nhwc_out(p.e, xs, w, bias, y, hs))
+                st = fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+        } else {
+            if (st == GCONV_OK) st = run_fwd(p.e, p.path, xs, w, bias, ys, hs);
+            if (st == GCONV_OK) st = reorder(ys, y, s.N, s.K, (int64_t)s.Ho * s.Wo, hs);
+        }
     }
     return st != GCONV_OK ? st : epilogue();
 }
@@ -465,8 +471,13 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
         float* dys = (float*)base;
         float* dxs = (float*)(base + stage_bytes(s.y_elems));
         st = reorder(dy, dys, s.N, (int64_t)s.Ho * s.Wo, s.K, hs);
-        if (st == GCONV_OK) st = run_bwd_data(p.e, p.path, dys, w, dxs, hs);
-        if (st == GCONV_OK) st = reorder(dxs, dx, s.N, s.C, (int64_t)s.H * s.W, hs);
+        if (st == GCONV_OK && p.path == GCONV_PATH_IGEMM && igemm_nhwc_out_supported(p.e, GCONV_OP_BWD_DATA)) {
+            if (!igemm_bwd_data_nhwc_out(p.e, dys, w, dx, hs))
+                st = fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+        } else {
+            if (st == GCONV_OK) st = run_bwd_data(p.e, p.path, dys, w, dxs, hs);
+            if (st == GCONV_OK) st = reorder(dxs, dx, s.N, s.C, (int64_t)s.H * s.W, hs);
+        }
     }
     return st != GCONV_OK ? st : epilogue();
 }

@@ -63,6 +63,11 @@ bool igemm_bwd_data_supported(const Shape& s);
 bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
                hipStream_t st);
 bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+// The same ops writing y or dx channels-last (NHWC) where the flat kernel runs.
+bool igemm_nhwc_out_supported(const Shape& s, int op);
+bool igemm_fwd_nhwc_out(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+                        hipStream_t st);
+bool igemm_bwd_data_nhwc_out(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
 
 // ---- fp32-MFMA gradWeight (split pixel reduction + deterministic reduce) -----
 bool igemm_bwd_filter_supported(const Shape& s);

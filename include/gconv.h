@@ -90,9 +90,10 @@ typedef struct gconv_desc {
  * one GEMM over the N*H*W rows (the fully-connected path, no reordering);
  * gradBias sums the [N*Ho*Wo, K] rows of dy directly. Every other NHWC op
  * reorders its NHWC inputs to NCHW in the workspace, runs the NCHW kernels
- * there and reorders the NHWC outputs back, so gconv_workspace_size() then
- * includes those copies (x and y for the forward pass, dy and dx for
- * gradInput, x and dy for gradWeight).
+ * there and reorders the NHWC outputs back (the MFMA implicit-GEMM forward
+ * and gradInput store y and dx channels-last themselves), so
+ * gconv_workspace_size() then includes those copies (x and y for the forward
+ * pass, dy and dx for gradInput, x and dy for gradWeight).
  */
 typedef enum gconv_layout {
     GCONV_LAYOUT_NCHW = 0,
