@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from cases import conv_kwargs, random_descs, tensors
+from cases import asym_descs, conv_kwargs, random_descs, tensors
 from gpu_util import check, dev, say
 from grouped_convolution_amd.workloads import draw
 
@@ -95,6 +95,22 @@ def test_nhwc_random_descriptors_every_family(seed):
             finally:
                 G.gconv_set_path_override(G.PATH_AUTO)
         assert covered == set(OPS)
+
+
+def test_nhwc_asymmetric_padding():
+    """End padding that differs from the start padding, in NHWC, on the
+    dispatcher's choice, with ReLU fused into the forward pass."""
+    for d in asym_descs(3700, 10, max_hw=12, max_k=5, max_cg=6, max_kg=6, max_g=4):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 3710)
+        y_ref, ya = oracle.fwd(x, w, b, relu=True, **kw)
+        dy = draw(("normal", 1.0), y_ref.shape, 3720)
+        say("nhwc asym %s" % d)
+        ref = refs(x, w, b, dy, kw)
+        ref["fwd"] = (to_nhwc(y_ref), to_nhwc(ya))
+        got = gpu_nhwc(x, w, b, dy, kw)
+        got["fwd"] = G.gconv_fwd(dev(to_nhwc(x)), dev(w), dev(b), layout="nhwc", relu=True, **kw)
+        assert compare("nhwc asym %s" % d, got, ref) == list(OPS)
 
 
 NHWC_CASES = [
