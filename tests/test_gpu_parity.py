@@ -714,22 +714,25 @@ def test_deterministic_bitwise():
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("name", ["tiny_grouped", "resnext_32x4d", "dense3x3"])
+@pytest.mark.parametrize("name", ["tiny_grouped", "resnext_32x4d", "dense3x3", "dense3x3_nhwc"])
 def test_hip_graph_replay(name):
     """The four ops of a step captured in one HIP graph (prepared plans, no
     allocation or memset inside) and replayed several times, with eager work
     and synchronisations in between: every replay equals the eager results
-    bit for bit."""
+    bit for bit. The channels-last workload captures its reorderings through
+    the workspace as well."""
     wl = WORKLOADS[name]
     inp = make_inputs(name, batch=REDUCED_BATCH[name])
-    kw = wl_kwargs(wl)
-    x, w, dy = dev(inp["x"]), dev(inp["w"]), dev(inp["dy"])
+    kw = dict(wl_kwargs(wl), layout=wl.layout)
+    store = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1))) if wl.layout == "nhwc" else (lambda a: a)
+    x, w, dy = dev(store(inp["x"])), dev(inp["w"]), dev(store(inp["dy"]))
     b = None if inp["b"] is None else dev(inp["b"])
-    y = torch.empty((x.shape[0],) + tuple(wl.dy_shape[1:]), device="cuda")
+    N, K, Ho, Wo = (x.shape[0],) + tuple(wl.dy_shape[1:])
+    y = torch.empty((N, Ho, Wo, K) if wl.layout == "nhwc" else (N, K, Ho, Wo), device="cuda")
     dx, dw = torch.empty_like(x), torch.empty_like(w)
     db = torch.empty(w.shape[0], device="cuda")
     plans = [G.Plan.fwd(x, w, b, y, **kw), G.Plan.bwd_data(dy, w, dx, **kw),
-             G.Plan.bwd_filter(x, dy, dw, **kw), G.Plan.bwd_bias(dy, db)]
+             G.Plan.bwd_filter(x, dy, dw, **kw), G.Plan.bwd_bias(dy, db, layout=wl.layout)]
     torch.cuda.synchronize()
     eager = [t.clone() for t in (y, dx, dw, db)]
     say("hip graph %s" % name)
@@ -738,7 +741,7 @@ def test_hip_graph_replay(name):
     with torch.cuda.stream(s):
         # plans run on the stream they were built on: rebuild them on the capture stream
         plans = [G.Plan.fwd(x, w, b, y, **kw), G.Plan.bwd_data(dy, w, dx, **kw),
-                 G.Plan.bwd_filter(x, dy, dw, **kw), G.Plan.bwd_bias(dy, db)]
+                 G.Plan.bwd_filter(x, dy, dw, **kw), G.Plan.bwd_bias(dy, db, layout=wl.layout)]
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=s):
