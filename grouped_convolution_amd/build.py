@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgconv.so")
 
-SOURCES = ["gconv_api.hip", "direct.hip", "direct_tile.hip", "bias.hip", "conv_mfma.hip", "wgrad_mfma.hip", "gemm_fc.hip", "smallgroup.hip", "layout.hip"]
+SOURCES = ["gconv_api.hip", "direct.hip", "direct_tile.hip", "bias.hip", "conv_mfma.hip", "wgrad_mfma.hip", "gemm_fc.hip", "smallgroup.hip", "layout.hip", "depthwise_nhwc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,286 @@
+// depthwise_nhwc.hip -- depthwise convolution (one input and one output
+// channel per group) on channels-last activations, forward and gradInput.
+// In NHWC the channels of a pixel are contiguous, so a thread owns four
+// consecutive channels of one output pixel and every tap is one 16-byte load
+// that the wave's lanes read as one contiguous run of pixels x channels; the
+// neighbouring pixels' overlapping windows are served from the caches. No
+// reordering, no LDS: each output is a KS*KS-tap FMA chain per channel.
+//   forward   y[n,ho,wo,c] = b[c] + sum_{i,j} w[c,i,j] * x[n, ho*sh - ph + i*dh, wo*sw - pw + j*dw, c]
+//   gradInput dx[n,h,w,c]  = sum_{i,j} w[c,i,j] * dy[n, (h + ph - i*dh)/sh, (w + pw - j*dw)/sw, c]
+//             over the taps whose quotients are exact and inside dy (the
+//             adjoint of the forward correlation).
+// The depthwise layers of the mobilenet family the DLPrimitives Blog
+// validates are the target shapes; TensorFlow stores them channels-last.
+#include <algorithm>
+
+#include "device_util.h"
+#include "fastdiv.h"
+#include "gconv_internal.h"
+
+namespace gconv {
+namespace {
+
+struct DwNhwcArgs {
+    const float* in;     // x (forward) or dy (gradInput), NHWC
+    const float* wgt;    // [C][KS][KS]
+    const float* bias;   // forward only, may be null
+    float* out;          // y or dx, NHWC
+    int N, C, Hin, Win, Hout, Wout;   // extents of `in` and `out`
+    int sh, sw, dh, dw, ph, pw;       // of the forward convolution
+    int relu;
+    int CQ;                           // channel groups per pixel (C / 4 or C)
+    int total;                        // N * Hout * Wout * CQ (< 2^31)
+    FastDiv div_cq, div_wout, div_img;
+};
+
+template <int KS, bool BWD, bool VEC>
+__global__ void __launch_bounds__(256) dw_nhwc_kernel(DwNhwcArgs a)
+{
+    constexpr int T = KS * KS;
+    constexpr int V = VEC ? 4 : 1;  // channels per thread
+    const int tid = blockIdx.x * 256 + threadIdx.x;
+    if (tid >= a.total) return;
+    // (n, oh, ow, cq) from the flat index.
+    const int pix = (int)fastdiv((uint32_t)tid, a.div_cq);
+    const int cq = tid - pix * a.CQ;
+    const int per_img = a.Hout * a.Wout;
+    const int n = (int)fastdiv((uint32_t)pix, a.div_img);
+    const int p = pix - n * per_img;
+    const int oh = (int)fastdiv((uint32_t)p, a.div_wout);
+    const int ow = p - oh * a.Wout;
+    const int c = cq * V;
+
+    float wv[T][V];
+    if constexpr (VEC && T % 4 == 1) {
+        // The 4*T weights of channels c..c+3 are contiguous and 16-byte aligned.
+        float wf[4 * T];
+        const f4* w4 = reinterpret_cast<const f4*>(a.wgt + (size_t)c * T);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+            const f4 v = w4[u];
+            wf[4 * u] = v.x; wf[4 * u + 1] = v.y; wf[4 * u + 2] = v.z; wf[4 * u + 3] = v.w;
+        }
+#pragma unroll
+        for (int q = 0; q < V; ++q)
+#pragma unroll
+            for (int t = 0; t < T; ++t) wv[t][q] = wf[q * T + t];
+    } else {
+#pragma unroll
+        for (int q = 0; q < V; ++q)
+#pragma unroll
+            for (int t = 0; t < T; ++t) wv[t][q] = a.wgt[(size_t)(c + q) * T + t];
+    }
+    float acc[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) acc[q] = (!BWD && a.bias) ? a.bias[c + q] : 0.f;
+
+    const float* img = a.in + (size_t)n * a.Hin * a.Win * a.C + c;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        int h;
+        bool hok;
+        if (!BWD) {
+            h = oh * a.sh - a.ph + i * a.dh;
+            hok = (unsigned)h < (unsigned)a.Hin;
+        } else {
+            const int hh = oh + a.ph - i * a.dh;
+            h = hh >= 0 ? hh / a.sh : -1;
+            hok = hh >= 0 && h * a.sh == hh && h < a.Hin;
+        }
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            int w;
+            bool wok;
+            if (!BWD) {
+                w = ow * a.sw - a.pw + j * a.dw;
+                wok = (unsigned)w < (unsigned)a.Win;
+            } else {
+                const int ww = ow + a.pw - j * a.dw;
+                w = ww >= 0 ? ww / a.sw : -1;
+                wok = ww >= 0 && w * a.sw == ww && w < a.Win;
+            }
+            if (hok && wok) {
+                const float* src = img + ((size_t)h * a.Win + w) * a.C;
+                if constexpr (VEC) {
+                    const f4 v = *reinterpret_cast<const f4*>(src);
+                    acc[0] = fmaf(wv[i * KS + j][0], v.x, acc[0]);
+                    acc[1] = fmaf(wv[i * KS + j][1], v.y, acc[1]);
+                    acc[2] = fmaf(wv[i * KS + j][2], v.z, acc[2]);
+                    acc[3] = fmaf(wv[i * KS + j][3], v.w, acc[3]);
+                } else {
+                    acc[0] = fmaf(wv[i * KS + j][0], src[0], acc[0]);
+                }
+            }
+        }
+    }
+    float* dst = a.out + ((size_t)n * per_img + p) * a.C + c;
+    if constexpr (VEC) {
+        f4 o;
+        o.x = relu_if(acc[0], a.relu);
+        o.y = relu_if(acc[1], a.relu);
+        o.z = relu_if(acc[2], a.relu);
+        o.w = relu_if(acc[3], a.relu);
+        __builtin_nontemporal_store(o, reinterpret_cast<f4*>(dst));
+    } else {
+        __builtin_nontemporal_store(relu_if(acc[0], a.relu), dst);
+    }
+}
+
+// Unit stride and dilation, four channels per thread: a thread computes PX
+// consecutive outputs of one row, loading each row's PX + KS - 1 input
+// columns once (a sliding window in registers) and its 4*KS*KS weights once.
+// gradInput at unit stride is the forward correlation of dy with the
+// tap-reversed filter (FLIP) and padding KS - 1 - p.
+template <int KS, int PX, bool FLIP>
+__global__ void __launch_bounds__(256) dw_nhwc_row_kernel(DwNhwcArgs a)
+{
+    constexpr int T = KS * KS, NC = PX + KS - 1;
+    const int tid = blockIdx.x * 256 + threadIdx.x;
+    if (tid >= a.total) return;
+    const int pix = (int)fastdiv((uint32_t)tid, a.div_cq);   // (n, oh, ow block)
+    const int cq = tid - pix * a.CQ;
+    const int nb = (a.Wout + PX - 1) / PX;
+    const int per_img = a.Hout * nb;
+    const int n = (int)fastdiv((uint32_t)pix, a.div_img);
+    const int p = pix - n * per_img;
+    const int oh = (int)fastdiv((uint32_t)p, a.div_wout);      // div_wout holds nb here
+    const int ow0 = (p - oh * nb) * PX;
+    const int c = cq * 4;
+
+    float wf[4 * T];
+    const f4* w4 = reinterpret_cast<const f4*>(a.wgt + (size_t)c * T);
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        const f4 v = w4[u];
+        wf[4 * u] = v.x; wf[4 * u + 1] = v.y; wf[4 * u + 2] = v.z; wf[4 * u + 3] = v.w;
+    }
+    // Weight of channel q at tap (i, j), tap-reversed for gradInput.
+    auto wt = [&](int q, int i, int j) { return FLIP ? wf[q * T + (KS - 1 - i) * KS + (KS - 1 - j)] : wf[q * T + i * KS + j]; };
+
+    f4 acc[PX];
+#pragma unroll
+    for (int u = 0; u < PX; ++u) {
+        acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+        if (a.bias) {
+            acc[u].x = a.bias[c]; acc[u].y = a.bias[c + 1]; acc[u].z = a.bias[c + 2]; acc[u].w = a.bias[c + 3];
+        }
+    }
+    const float* img = a.in + (size_t)n * a.Hin * a.Win * a.C + c;
+    const int wb = ow0 - a.pw;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        const int h = oh - a.ph + i;
+        if ((unsigned)h >= (unsigned)a.Hin) continue;
+        f4 col[NC];
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int w = wb + u;
+            col[u] = (unsigned)w < (unsigned)a.Win ? *reinterpret_cast<const f4*>(img + ((size_t)h * a.Win + w) * a.C)
+                                                    : f4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < PX; ++u)
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                acc[u].x = fmaf(wt(0, i, j), col[u + j].x, acc[u].x);
+                acc[u].y = fmaf(wt(1, i, j), col[u + j].y, acc[u].y);
+                acc[u].z = fmaf(wt(2, i, j), col[u + j].z, acc[u].z);
+                acc[u].w = fmaf(wt(3, i, j), col[u + j].w, acc[u].w);
+            }
+    }
+    float* dst = a.out + (((size_t)n * a.Hout + oh) * a.Wout + ow0) * a.C + c;
+#pragma unroll
+    for (int u = 0; u < PX; ++u) {
+        if (ow0 + u >= a.Wout) break;
+        f4 o = acc[u];
+        o.x = relu_if(o.x, a.relu); o.y = relu_if(o.y, a.relu); o.z = relu_if(o.z, a.relu); o.w = relu_if(o.w, a.relu);
+        __builtin_nontemporal_store(o, reinterpret_cast<f4*>(dst + (size_t)u * a.C));
+    }
+}
+
+constexpr int kRowPx = 4;
+
+template <int KS, bool FLIP>
+void launch_row(DwNhwcArgs a, hipStream_t st)
+{
+    const int nb = (a.Wout + kRowPx - 1) / kRowPx;
+    a.total = (int)((int64_t)a.N * a.Hout * nb * a.CQ);
+    a.div_img = make_fastdiv((uint32_t)(a.Hout * nb));
+    a.div_wout = make_fastdiv((uint32_t)nb);
+    const unsigned blocks = (unsigned)((a.total + 255) / 256);
+    hipLaunchKernelGGL((dw_nhwc_row_kernel<KS, kRowPx, FLIP>), dim3(blocks), dim3(256), 0, st, a);
+}
+
+template <int KS, bool BWD>
+void launch(const DwNhwcArgs& a, bool vec, hipStream_t st)
+{
+    const unsigned blocks = (unsigned)((a.total + 255) / 256);
+    if (vec) hipLaunchKernelGGL((dw_nhwc_kernel<KS, BWD, true>), dim3(blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dw_nhwc_kernel<KS, BWD, false>), dim3(blocks), dim3(256), 0, st, a);
+}
+
+}  // namespace
+
+// Depthwise (multiplier 1), square 3x3 or 5x5 filters, any stride, padding and dilation.
+bool dw_nhwc_supported(const Shape& s)
+{
+    if (!(s.Cg == 1 && s.Kg == 1 && s.kh == s.kw && (s.kh == 3 || s.kh == 5) && s.N >= 1)) return false;
+    // Flat thread indices (pixels x channels of either tensor) stay below 2^31.
+    const int64_t px = (int64_t)s.N * std::max((int64_t)s.H * s.W, (int64_t)s.Ho * s.Wo);
+    return px * s.C < (int64_t(1) << 31);
+}
+
+static DwNhwcArgs dw_args(const Shape& s, bool bwd, bool vec)
+{
+    DwNhwcArgs a{};
+    a.N = s.N; a.C = s.C;
+    a.Hin = bwd ? s.Ho : s.H; a.Win = bwd ? s.Wo : s.W;
+    a.Hout = bwd ? s.H : s.Ho; a.Wout = bwd ? s.W : s.Wo;
+    a.sh = s.sh; a.sw = s.sw; a.dh = s.dh; a.dw = s.dw; a.ph = s.ph; a.pw = s.pw;
+    a.CQ = vec ? s.C / 4 : s.C;
+    a.total = (int)((int64_t)s.N * a.Hout * a.Wout * a.CQ);
+    a.div_cq = make_fastdiv((uint32_t)a.CQ);
+    a.div_img = make_fastdiv((uint32_t)(a.Hout * a.Wout));
+    a.div_wout = make_fastdiv((uint32_t)a.Wout);
+    return a;
+}
+
+static bool vec_ok(const Shape& s, const void* p0, const void* p1)
+{
+    return (s.C & 3) == 0 && ((uintptr_t)p0 & 15) == 0 && ((uintptr_t)p1 & 15) == 0;
+}
+
+static bool unit(const Shape& s) { return s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1; }
+
+void dw_nhwc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y, hipStream_t st)
+{
+    const bool vec = vec_ok(s, x, y) && ((uintptr_t)w & 15) == 0;
+    DwNhwcArgs a = dw_args(s, false, vec);
+    a.in = x; a.wgt = w; a.bias = bias; a.out = y; a.relu = s.relu;
+    if (vec && unit(s)) {
+        if (s.kh == 3) launch_row<3, false>(a, st);
+        else launch_row<5, false>(a, st);
+        return;
+    }
+    if (s.kh == 3) launch<3, false>(a, vec, st);
+    else launch<5, false>(a, vec, st);
+}
+
+void dw_nhwc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    const bool vec = vec_ok(s, dy, dx) && ((uintptr_t)w & 15) == 0;
+    DwNhwcArgs a = dw_args(s, true, vec);
+    a.in = dy; a.wgt = w; a.bias = nullptr; a.out = dx; a.relu = 0;
+    if (vec && unit(s)) {
+        // The forward correlation of dy with the reversed taps and padding k - 1 - p.
+        a.ph = s.kh - 1 - s.ph;
+        a.pw = s.kw - 1 - s.pw;
+        if (s.kh == 3) launch_row<3, true>(a, st);
+        else launch_row<5, true>(a, st);
+        return;
+    }
+    if (s.kh == 3) launch<3, true>(a, vec, st);
+    else launch<5, true>(a, vec, st);
+}
+
+}  // namespace gconv

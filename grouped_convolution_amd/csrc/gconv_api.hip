@@ -136,15 +136,35 @@ Shape flat_rows(const Shape& s, int64_t rows, int C, int K)
     return f;
 }
 
-Shape effective_shape(const Shape& s, int op, bool* staged)
+int choose_path(const Shape& s, int op);
+
+// NHWC depthwise forward / gradInput on the native kernel: where the NCHW
+// dispatcher would pick the small-group family for the same shape.
+bool dw_nhwc_native(const Shape& s, int op)
+{
+    Shape e = s;
+    e.nhwc = 0;
+    return dw_nhwc_supported(s) && choose_path(e, op) == GCONV_PATH_SMALLGROUP;
+}
+
+Shape effective_shape(const Shape& s, int op, bool* staged, bool* native_dw = nullptr)
 {
     *staged = false;
+    if (native_dw) *native_dw = false;
     if (!s.nhwc) return s;
     // (rows beyond 2^30 are refused by the prologue)
     if (op == GCONV_OP_BWD_BIAS) return flat_rows(s, std::min<int64_t>((int64_t)s.N * s.Ho * s.Wo, 1 << 30), s.K, s.K);
     if (nhwc_as_gemm(s)) {
         const Shape f = flat_rows(s, (int64_t)s.N * s.H * s.W, s.C, s.K);
         if (fc_supported(f)) return f;
+    }
+    // Depthwise forward and gradInput read NHWC natively (the small-group
+    // family's choice; a forced family stages as below).
+    if ((op == GCONV_OP_FWD || op == GCONV_OP_BWD_DATA) && dw_nhwc_native(s, op)) {
+        Shape e = s;
+        e.nhwc = 0;
+        if (native_dw) *native_dw = true;
+        return e;
     }
     Shape e = s;
     e.nhwc = 0;
@@ -254,6 +274,7 @@ struct Prep {
     Shape e;      // the NCHW shape the kernels run (== s for NCHW)
     int path;
     bool staged;  // NHWC activations reordered through the workspace
+    bool native;  // NHWC depthwise forward / gradInput on its own kernel
 };
 
 int prologue(const gconv_desc* d, int op, Prep* p, void* ws, size_t ws_bytes)
@@ -262,7 +283,7 @@ int prologue(const gconv_desc* d, int op, Prep* p, void* ws, size_t ws_bytes)
     if (st != GCONV_OK) return st;
     if (p->s.nhwc && op == GCONV_OP_BWD_BIAS && (int64_t)p->s.N * p->s.Ho * p->s.Wo >= (int64_t(1) << 30))
         return fail(GCONV_ERR_UNSUPPORTED, "NHWC gradBias over 2^30 or more rows");
-    p->e = effective_shape(p->s, op, &p->staged);
+    p->e = effective_shape(p->s, op, &p->staged, &p->native);
     p->path = choose_path(p->e, op);
     if (!path_supports(p->path, p->e, op))
         return fail(GCONV_ERR_UNSUPPORTED, "forced path %d cannot run this descriptor for op %d",
@@ -431,7 +452,11 @@ int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const floa
     hipStream_t hs = (hipStream_t)stream;
     (void)hipGetLastError();
     if (s.N == 0) return epilogue();
-    if (!p.staged) {
+    if (p.native) {
+        Shape sr = s;
+        sr.relu = p.e.relu;
+        dw_nhwc_fwd(sr, x, w, bias, y, hs);
+    } else if (!p.staged) {
         st = run_fwd(p.e, p.path, x, w, bias, y, hs);
     } else {
         char* base = (char*)workspace;
@@ -464,7 +489,9 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
     hipStream_t hs = (hipStream_t)stream;
     (void)hipGetLastError();
     if (s.N == 0) return epilogue();
-    if (!p.staged) {
+    if (p.native) {
+        dw_nhwc_bwd_data(s, dy, w, dx, hs);
+    } else if (!p.staged) {
         st = run_bwd_data(p.e, p.path, dy, w, dx, hs);
     } else {
         char* base = (char*)workspace;

@@ -35,8 +35,8 @@ measure or motivate:
                  padding, which puts the one padding row and column at the
                  end only (DLPrimitives Blog, "TensorFlow"): padding given as
                  (top, bottom, left, right) = (0, 1, 0, 1).
-  dense3x3_nhwc, resnext_1x1_nhwc
-                 dense3x3 and resnext_1x1 with x, dx, y and dy stored
+  dense3x3_nhwc, resnext_1x1_nhwc, mobilenet_dw_nhwc
+                 dense3x3, resnext_1x1 and mobilenet_dw with x, dx, y and dy stored
                  channels-last, the layout the DLPrimitives Blog measures
                  oneDNN fastest in ("Attempt to integrate with OneDNN");
                  make_inputs returns the same NCHW arrays for them and the
@@ -98,16 +98,20 @@ WORKLOADS = {
     "mobilenet_dw_s2_same": Workload(
         "mobilenet_dw_s2_same", 8, (64, 144, 56, 56), (144, 1, 3, 3), (64, 144, 28, 28), 144, 2,
         (0, 1, 0, 1), 1, ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 9.0))), None),
-    # The same tensors as dense3x3 and resnext_1x1 (same seeds), stored channels-last.
+    # The same tensors as dense3x3, resnext_1x1 and mobilenet_dw (same seeds), stored channels-last.
     "dense3x3_nhwc": Workload(
         "dense3x3_nhwc", 2, (32, 64, 56, 56), (64, 64, 3, 3), (32, 64, 56, 56), 1, 1, 1, 1,
         ("normal", 1.0), ("normal", float(np.sqrt(2.0 / 576.0))), ("normal", 0.01), layout="nhwc"),
+    "mobilenet_dw_nhwc": Workload(
+        "mobilenet_dw_nhwc", 7, (64, 144, 56, 56), (144, 1, 3, 3), (64, 144, 56, 56), 144, 1, 1, 1,
+        ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 9.0))), None, layout="nhwc"),
     "resnext_1x1_nhwc": Workload(
         "resnext_1x1_nhwc", 6, (64, 256, 56, 56), (128, 256, 1, 1), (64, 128, 56, 56), 1, 1, 0, 1,
         ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 256.0))), None, layout="nhwc"),
 }
 WORKLOAD_ORDER = ["tiny_grouped", "dense3x3", "alexnet_conv2", "resnext_32x4d", "fc_mode", "resnext_1x1",
-                  "mobilenet_dw", "mobilenet_dw_s2_same", "dense3x3_nhwc", "resnext_1x1_nhwc"]
+                  "mobilenet_dw", "mobilenet_dw_s2_same", "dense3x3_nhwc", "resnext_1x1_nhwc",
+                  "mobilenet_dw_nhwc"]
 
 
 def draw(dist, shape, seed) -> np.ndarray:

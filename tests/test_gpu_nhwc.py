@@ -123,6 +123,25 @@ NHWC_CASES = [
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     (dict(N=2, C=12, K=12, H=17, W=16, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=12),
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # depthwise forward and gradInput on the native NHWC kernel (no reordering):
+    # 10 channels (one per thread, no 16-byte loads), 3x3 ...
+    (dict(N=2, C=10, K=10, H=13, W=11, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=10),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    # ... four channels per thread at unit stride: each thread slides a window along four
+    # outputs of a row (13 columns: the last block holds one), 3x3 and 5x5 ...
+    (dict(N=2, C=12, K=12, H=9, W=13, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=12),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
+    (dict(N=3, C=8, K=8, H=11, W=10, kh=5, kw=5, sh=1, sw=1, ph=2, pw=0, dh=1, dw=1, G=8),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup"}),
+    # ... 16 channels (four per thread) 5x5 at stride 2 (gradInput keeps only the exact quotients) ...
+    (dict(N=2, C=16, K=16, H=17, W=16, kh=5, kw=5, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=16),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "direct"}),
+    # ... dilation 2 ...
+    (dict(N=1, C=8, K=8, H=15, W=14, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=2, dw=2, G=8),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup"}),
+    # ... and one more zero row and column at the end than at the start, at stride 2
+    (dict(N=2, C=24, K=24, H=16, W=15, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=24, ph=0, pb=1, pw=0, pr=1),
+     {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     # 1x1, one group: one GEMM over the N*H*W pixel rows (fully-connected path)
     (dict(N=3, C=40, K=72, H=9, W=10, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
      {"fwd": "fc", "bwd_data": "fc", "bwd_filter": "fc"}),
@@ -145,6 +164,9 @@ def test_nhwc_cases(case):
     for op, name in paths.items():
         chosen = G.gconv_select_path(desc, getattr(G, "OP_" + op.upper()))
         assert G.PATH_NAMES[chosen] == name, (d, op, G.PATH_NAMES[chosen])
+    if d["G"] == d["C"] == d["K"] and d["kh"] in (3, 5):
+        # the native depthwise kernel: no reordering, no workspace
+        assert G.gconv_workspace_size(desc, G.OP_FWD) == 0 and G.gconv_workspace_size(desc, G.OP_BWD_DATA) == 0
     say("nhwc case %s" % d)
     x, w, b = tensors(d, 3400 + case)
     y_ref, _ = oracle.fwd(x, w, b, **kw)

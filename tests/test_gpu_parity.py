@@ -478,7 +478,7 @@ def test_ragged_shapes_span_several_tiles():
 
 REDUCED_BATCH = {"tiny_grouped": 2, "dense3x3": 2, "alexnet_conv2": 2, "resnext_32x4d": 3,
                  "fc_mode": 24, "resnext_1x1": 2, "mobilenet_dw": 2, "mobilenet_dw_s2_same": 2,
-                 "dense3x3_nhwc": 2, "resnext_1x1_nhwc": 2}
+                 "dense3x3_nhwc": 2, "resnext_1x1_nhwc": 2, "mobilenet_dw_nhwc": 2}
 
 
 def wl_kwargs(wl):
