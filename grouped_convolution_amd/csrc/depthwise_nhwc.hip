@@ -250,6 +250,155 @@ static bool vec_ok(const Shape& s, const void* p0, const void* p1)
     return (s.C & 3) == 0 && ((uintptr_t)p0 & 15) == 0 && ((uintptr_t)p1 & 15) == 0;
 }
 
+// gradWeight: dw[c,i,j] = sum_{n,oh,ow} dy[n,oh,ow,c] * x[n, oh*sh - ph + i*dh, ow*sw - pw + j*dw, c].
+// A block takes a slice of the N*Ho*Wo output pixels for every channel:
+// thread t owns channels 4*(t % CQ) .. +3 and pixel lane t / CQ of the NP =
+// 256 / CQ lanes (consecutive threads read consecutive channels of one pixel,
+// then the next pixel: each load instruction covers whole pixels). A thread
+// keeps 4*KS*KS sums; the pixel lanes are added in order through LDS and the
+// block writes its partial [C][KS*KS] (or dw itself when there is one slice);
+// dw_nhwc_wgrad_reduce adds the slices in order.
+struct DwWgradArgs {
+    const float* x;
+    const float* dy;
+    float* out;                 // dw, or the workspace [nslice][C*KS*KS]
+    int N, C, H, W, Ho, Wo, sh, sw, dh, dw, ph, pw;
+    int CQ, NP;                 // channel quads, pixel lanes per block
+    int slice, total;           // pixels per slice, N*Ho*Wo
+    FastDiv div_cq, div_hw, div_wo;
+};
+
+template <int KS>
+__global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
+{
+    constexpr int T = KS * KS;
+    extern __shared__ float red[];  // [NP][CQ][4*T]
+    const int t = threadIdx.x;
+    const int lp = (int)fastdiv((uint32_t)t, a.div_cq);
+    const int cq = t - lp * a.CQ;
+    const bool active = lp < a.NP;
+    const int c = cq * 4;
+    const int p0 = blockIdx.x * a.slice, p1 = min(a.total, p0 + a.slice);
+    float acc[4 * T];
+#pragma unroll
+    for (int e = 0; e < 4 * T; ++e) acc[e] = 0.f;
+    if (active) {
+        for (int p = p0 + lp; p < p1; p += a.NP) {
+            const int n = (int)fastdiv((uint32_t)p, a.div_hw);
+            const int q = p - n * a.Ho * a.Wo;
+            const int oh = (int)fastdiv((uint32_t)q, a.div_wo);
+            const int ow = q - oh * a.Wo;
+            const f4 d = *reinterpret_cast<const f4*>(a.dy + (size_t)p * a.C + c);
+            const float* img = a.x + (size_t)n * a.H * a.W * a.C + c;
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+                const int h = oh * a.sh - a.ph + i * a.dh;
+                if ((unsigned)h >= (unsigned)a.H) continue;
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    const int w = ow * a.sw - a.pw + j * a.dw;
+                    if ((unsigned)w >= (unsigned)a.W) continue;
+                    const f4 v = *reinterpret_cast<const f4*>(img + ((size_t)h * a.W + w) * a.C);
+                    const int tt = i * KS + j;
+                    acc[tt] = fmaf(d.x, v.x, acc[tt]);
+                    acc[T + tt] = fmaf(d.y, v.y, acc[T + tt]);
+                    acc[2 * T + tt] = fmaf(d.z, v.z, acc[2 * T + tt]);
+                    acc[3 * T + tt] = fmaf(d.w, v.w, acc[3 * T + tt]);
+                }
+            }
+        }
+        float* r = red + ((size_t)lp * a.CQ + cq) * (4 * T);
+#pragma unroll
+        for (int e = 0; e < 4 * T; ++e) r[e] = acc[e];
+    }
+    __syncthreads();
+    // Thread e < C*T adds the NP lanes' sums of output e = c*T + tap in order.
+    float* out = a.out + (size_t)blockIdx.x * a.C * T;
+    for (int e = t; e < a.C * T; e += 256) {
+        const int ch = e / T, tap = e - (e / T) * T;
+        const int off = (ch >> 2) * (4 * T) + (ch & 3) * T + tap;
+        float sum = red[off];
+        for (int l = 1; l < a.NP; ++l) sum += red[(size_t)l * a.CQ * (4 * T) + off];
+        out[e] = sum;
+    }
+}
+
+// dw[e] = sum over slices (in order) of ws[slice][e]: 16 outputs x 16 slice
+// groups per block, the group sums added in order.
+__global__ void __launch_bounds__(256) dw_nhwc_wgrad_reduce(const float* __restrict__ ws, float* __restrict__ dw,
+                                                            int E, int nslice)
+{
+    __shared__ float part[16][17];
+    const int el = threadIdx.x & 15, sg = threadIdx.x >> 4;
+    const int e = blockIdx.x * 16 + el;
+    float sum = 0.f;
+    if (e < E)
+        for (int k = sg; k < nslice; k += 16) sum += ws[(size_t)k * E + e];
+    part[sg][el] = sum;
+    __syncthreads();
+    if (sg != 0 || e >= E) return;
+    sum = part[0][el];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) sum += part[i][el];
+    dw[e] = sum;
+}
+
+static bool dw_wgrad_plan(const Shape& s, DwWgradArgs* out, int* nslice)
+{
+    if (!dw_nhwc_supported(s) || (s.C & 3) != 0) return false;
+    DwWgradArgs a{};
+    a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo;
+    a.sh = s.sh; a.sw = s.sw; a.dh = s.dh; a.dw = s.dw; a.ph = s.ph; a.pw = s.pw;
+    a.CQ = s.C / 4;
+    if (a.CQ > 256) return false;
+    a.NP = 256 / a.CQ;
+    const int T = s.kh * s.kw;
+    if ((size_t)a.NP * a.CQ * 4 * T * 4 > 64 * 1024) return false;
+    a.total = s.N * s.Ho * s.Wo;
+    // About 1024 slices, each giving every pixel lane at least four pixels.
+    int64_t want = std::min<int64_t>(1024, std::max<int64_t>(1, a.total / (4 * a.NP)));
+    a.slice = (int)((a.total + want - 1) / want);
+    *nslice = (a.total + a.slice - 1) / a.slice;
+    a.div_cq = make_fastdiv((uint32_t)a.CQ);
+    a.div_hw = make_fastdiv((uint32_t)(s.Ho * s.Wo));
+    a.div_wo = make_fastdiv((uint32_t)s.Wo);
+    if (out) *out = a;
+    return true;
+}
+
+bool dw_nhwc_wgrad_supported(const Shape& s)
+{
+    int ns;
+    return dw_wgrad_plan(s, nullptr, &ns);
+}
+
+size_t dw_nhwc_wgrad_workspace(const Shape& s)
+{
+    DwWgradArgs a;
+    int ns;
+    if (!dw_wgrad_plan(s, &a, &ns) || ns <= 1) return 0;
+    return (size_t)ns * s.C * s.kh * s.kw * sizeof(float);
+}
+
+bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st)
+{
+    DwWgradArgs a;
+    int ns;
+    if (!dw_wgrad_plan(s, &a, &ns)) return false;
+    if (((uintptr_t)x & 15) || ((uintptr_t)dy & 15)) return false;
+    if (ns > 1 && !ws) return false;
+    a.x = x; a.dy = dy; a.out = ns > 1 ? ws : dw;
+    const int T = s.kh * s.kw;
+    const size_t lds = (size_t)a.NP * a.CQ * 4 * T * sizeof(float);
+    if (s.kh == 3) hipLaunchKernelGGL(dw_nhwc_wgrad_kernel<3>, dim3(ns), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL(dw_nhwc_wgrad_kernel<5>, dim3(ns), dim3(256), lds, st, a);
+    if (ns > 1) {
+        const int E = s.C * T;
+        hipLaunchKernelGGL(dw_nhwc_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, E, ns);
+    }
+    return true;
+}
+
 static bool unit(const Shape& s) { return s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1; }
 
 void dw_nhwc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y, hipStream_t st)

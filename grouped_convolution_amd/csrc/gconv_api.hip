@@ -138,12 +138,15 @@ Shape flat_rows(const Shape& s, int64_t rows, int C, int K)
 
 int choose_path(const Shape& s, int op);
 
-// NHWC depthwise forward / gradInput on the native kernel: where the NCHW
-// dispatcher would pick the small-group family for the same shape.
+// NHWC depthwise on its own kernels: forward and gradInput where the NCHW
+// dispatcher would pick the small-group family for the same shape, gradWeight
+// whenever no family is forced (16-byte channel groups).
 bool dw_nhwc_native(const Shape& s, int op)
 {
     Shape e = s;
     e.nhwc = 0;
+    if (op == GCONV_OP_BWD_FILTER)
+        return g_path_override.load() == GCONV_PATH_AUTO && dw_nhwc_wgrad_supported(s);
     return dw_nhwc_supported(s) && choose_path(e, op) == GCONV_PATH_SMALLGROUP;
 }
 
@@ -160,7 +163,7 @@ Shape effective_shape(const Shape& s, int op, bool* staged, bool* native_dw = nu
     }
     // Depthwise forward and gradInput read NHWC natively (the small-group
     // family's choice; a forced family stages as below).
-    if ((op == GCONV_OP_FWD || op == GCONV_OP_BWD_DATA) && dw_nhwc_native(s, op)) {
+    if (op != GCONV_OP_BWD_BIAS && dw_nhwc_native(s, op)) {
         Shape e = s;
         e.nhwc = 0;
         if (native_dw) *native_dw = true;
@@ -277,6 +280,13 @@ struct Prep {
     bool native;  // NHWC depthwise forward / gradInput on its own kernel
 };
 
+// Workspace of an op on its effective shape.
+size_t op_workspace(const Shape& s, const Shape& e, int op, int path, bool staged, bool native)
+{
+    if (native) return op == GCONV_OP_BWD_FILTER ? dw_nhwc_wgrad_workspace(s) : 0;
+    return workspace_for(e, op, path) + (staged ? staging_bytes(s, op) : 0);
+}
+
 int prologue(const gconv_desc* d, int op, Prep* p, void* ws, size_t ws_bytes)
 {
     int st = make_shape(d, &p->s);
@@ -288,7 +298,7 @@ int prologue(const gconv_desc* d, int op, Prep* p, void* ws, size_t ws_bytes)
     if (!path_supports(p->path, p->e, op))
         return fail(GCONV_ERR_UNSUPPORTED, "forced path %d cannot run this descriptor for op %d",
                     p->path, op);
-    const size_t need = workspace_for(p->e, op, p->path) + (p->staged ? staging_bytes(p->s, op) : 0);
+    const size_t need = op_workspace(p->s, p->e, op, p->path, p->staged, p->native);
     if (ws_bytes < need || (need > 0 && ws == nullptr))
         return fail(GCONV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes,
                     need);
@@ -402,9 +412,9 @@ int gconv_workspace_size(const gconv_desc* d, int op, size_t* bytes)
     if (st != GCONV_OK) return st;
     if (!bytes) return fail(GCONV_ERR_NULL, "bytes pointer is NULL");
     if (op < GCONV_OP_FWD || op > GCONV_OP_BWD_BIAS) return fail(GCONV_ERR_ARG, "bad op %d", op);
-    bool staged;
-    const Shape e = effective_shape(s, op, &staged);
-    *bytes = workspace_for(e, op, choose_path(e, op)) + (staged ? staging_bytes(s, op) : 0);
+    bool staged, native;
+    const Shape e = effective_shape(s, op, &staged, &native);
+    *bytes = op_workspace(s, e, op, choose_path(e, op), staged, native);
     return GCONV_OK;
 }
 
@@ -526,7 +536,10 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
         fill_zero(dw, s.w_elems, hs);  // a sum over no images
         return epilogue();
     }
-    if (!p.staged) {
+    if (p.native) {
+        if (!dw_nhwc_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
+            st = fail(GCONV_ERR_ARG, "channels-last depthwise gradWeight needs 16-byte aligned x and dy");
+    } else if (!p.staged) {
         st = run_bwd_filter(p.e, p.path, x, dy, dw, (float*)workspace, hs);
     } else {
         char* base = (char*)workspace;

@@ -112,6 +112,9 @@ size_t bias_workspace_bytes(const Shape& s);
 bool dw_nhwc_supported(const Shape& s);
 void dw_nhwc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y, hipStream_t st);
 void dw_nhwc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+bool dw_nhwc_wgrad_supported(const Shape& s);
+size_t dw_nhwc_wgrad_workspace(const Shape& s);
+bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st);
 // dst[n] = src[n]^T for N row-major [R][Cc] matrices (NHWC <-> NCHW); false if
 // the extents do not fit the kernel's 32-bit indices.
 bool transpose_batched(const float* src, float* dst, int64_t N, int64_t R, int64_t Cc, hipStream_t st);

@@ -88,7 +88,10 @@ typedef struct gconv_desc {
 /*
  * Activation layout. NHWC: a 1x1 stride-1 unpadded layer with one group is
  * one GEMM over the N*H*W rows (the fully-connected path, no reordering);
- * gradBias sums the [N*Ho*Wo, K] rows of dy directly. Every other NHWC op
+ * gradBias sums the [N*Ho*Wo, K] rows of dy directly; depthwise layers (one
+ * channel per group, 3x3 or 5x5) run on channels-last kernels of their own
+ * (gradWeight there, when C % 4 == 0 and no family is forced, needs x and dy
+ * 16-byte aligned and returns GCONV_ERR_ARG otherwise). Every other NHWC op
  * reorders its NHWC inputs to NCHW in the workspace, runs the NCHW kernels
  * there and reorders the NHWC outputs back (the MFMA implicit-GEMM forward
  * and gradInput store y and dx channels-last themselves), so
