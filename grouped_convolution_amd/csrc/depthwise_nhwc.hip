@@ -20,6 +20,8 @@
 namespace gconv {
 namespace {
 
+constexpr int kRowPx = 4;  // outputs of a row per thread in the unit-stride kernels
+
 struct DwNhwcArgs {
     const float* in;     // x (forward) or dy (gradInput), NHWC
     const float* wgt;    // [C][KS][KS]
@@ -198,8 +200,6 @@ __global__ void __launch_bounds__(256) dw_nhwc_row_kernel(DwNhwcArgs a)
     }
 }
 
-constexpr int kRowPx = 4;
-
 template <int KS, bool FLIP>
 void launch_row(DwNhwcArgs a, hipStream_t st)
 {
@@ -264,11 +264,12 @@ struct DwWgradArgs {
     float* out;                 // dw, or the workspace [nslice][C*KS*KS]
     int N, C, H, W, Ho, Wo, sh, sw, dh, dw, ph, pw;
     int CQ, NP;                 // channel quads, pixel lanes per block
-    int slice, total;           // pixels per slice, N*Ho*Wo
+    int slice, total;           // units per slice, units (pixels, or runs of kRowPx pixels of a row)
+    int nb;                     // runs per output row (unit stride: ceil(Wo / kRowPx))
     FastDiv div_cq, div_hw, div_wo;
 };
 
-template <int KS>
+template <int KS, bool RUN>
 __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
 {
     constexpr int T = KS * KS;
@@ -282,7 +283,46 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
     float acc[4 * T];
 #pragma unroll
     for (int e = 0; e < 4 * T; ++e) acc[e] = 0.f;
-    if (active) {
+    if (active && RUN) {
+        // Unit stride and dilation: unit p is a run of kRowPx outputs of one
+        // row; each input row's kRowPx + KS - 1 columns are loaded once.
+        constexpr int NC = kRowPx + KS - 1;
+        for (int p = p0 + lp; p < p1; p += a.NP) {
+            const int n = (int)fastdiv((uint32_t)p, a.div_hw);   // div_hw: Ho * nb
+            const int q = p - n * a.Ho * a.nb;
+            const int oh = (int)fastdiv((uint32_t)q, a.div_wo);  // div_wo: nb
+            const int ow0 = (q - oh * a.nb) * kRowPx;
+            f4 d[kRowPx];
+#pragma unroll
+            for (int u = 0; u < kRowPx; ++u)
+                d[u] = ow0 + u < a.Wo ? *reinterpret_cast<const f4*>(a.dy + (((size_t)n * a.Ho + oh) * a.Wo + ow0 + u) * a.C + c)
+                                      : f4{0.f, 0.f, 0.f, 0.f};
+            const float* img = a.x + (size_t)n * a.H * a.W * a.C + c;
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+                const int h = oh - a.ph + i;
+                if ((unsigned)h >= (unsigned)a.H) continue;
+                f4 col[NC];
+#pragma unroll
+                for (int v = 0; v < NC; ++v) {
+                    const int w = ow0 - a.pw + v;
+                    col[v] = (unsigned)w < (unsigned)a.W ? *reinterpret_cast<const f4*>(img + ((size_t)h * a.W + w) * a.C)
+                                                         : f4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    const int tt = i * KS + j;
+#pragma unroll
+                    for (int u = 0; u < kRowPx; ++u) {
+                        acc[tt] = fmaf(d[u].x, col[u + j].x, acc[tt]);
+                        acc[T + tt] = fmaf(d[u].y, col[u + j].y, acc[T + tt]);
+                        acc[2 * T + tt] = fmaf(d[u].z, col[u + j].z, acc[2 * T + tt]);
+                        acc[3 * T + tt] = fmaf(d[u].w, col[u + j].w, acc[3 * T + tt]);
+                    }
+                }
+            }
+        }
+    } else if (active) {
         for (int p = p0 + lp; p < p1; p += a.NP) {
             const int n = (int)fastdiv((uint32_t)p, a.div_hw);
             const int q = p - n * a.Ho * a.Wo;
@@ -307,6 +347,8 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
                 }
             }
         }
+    }
+    if (active) {
         float* r = red + ((size_t)lp * a.CQ + cq) * (4 * T);
 #pragma unroll
         for (int e = 0; e < 4 * T; ++e) r[e] = acc[e];
@@ -354,14 +396,16 @@ static bool dw_wgrad_plan(const Shape& s, DwWgradArgs* out, int* nslice)
     a.NP = 256 / a.CQ;
     const int T = s.kh * s.kw;
     if ((size_t)a.NP * a.CQ * 4 * T * 4 > 64 * 1024) return false;
-    a.total = s.N * s.Ho * s.Wo;
-    // About 1024 slices, each giving every pixel lane at least four pixels.
-    int64_t want = std::min<int64_t>(1024, std::max<int64_t>(1, a.total / (4 * a.NP)));
+    const bool run = s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1;
+    a.nb = run ? (s.Wo + kRowPx - 1) / kRowPx : s.Wo;
+    a.total = s.N * s.Ho * a.nb;
+    // About 1024 slices, each giving every pixel lane at least a few units.
+    int64_t want = std::min<int64_t>(1024, std::max<int64_t>(1, a.total / ((run ? 1 : 4) * a.NP)));
     a.slice = (int)((a.total + want - 1) / want);
     *nslice = (a.total + a.slice - 1) / a.slice;
     a.div_cq = make_fastdiv((uint32_t)a.CQ);
-    a.div_hw = make_fastdiv((uint32_t)(s.Ho * s.Wo));
-    a.div_wo = make_fastdiv((uint32_t)s.Wo);
+    a.div_hw = make_fastdiv((uint32_t)(s.Ho * a.nb));
+    a.div_wo = make_fastdiv((uint32_t)a.nb);
     if (out) *out = a;
     return true;
 }
@@ -390,8 +434,14 @@ bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* 
     a.x = x; a.dy = dy; a.out = ns > 1 ? ws : dw;
     const int T = s.kh * s.kw;
     const size_t lds = (size_t)a.NP * a.CQ * 4 * T * sizeof(float);
-    if (s.kh == 3) hipLaunchKernelGGL(dw_nhwc_wgrad_kernel<3>, dim3(ns), dim3(256), lds, st, a);
-    else hipLaunchKernelGGL(dw_nhwc_wgrad_kernel<5>, dim3(ns), dim3(256), lds, st, a);
+    const bool run = s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1;
+    if (s.kh == 3) {
+        if (run) hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<3, true>), dim3(ns), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<3, false>), dim3(ns), dim3(256), lds, st, a);
+    } else {
+        if (run) hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<5, true>), dim3(ns), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<5, false>), dim3(ns), dim3(256), lds, st, a);
+    }
     if (ns > 1) {
         const int E = s.C * T;
         hipLaunchKernelGGL(dw_nhwc_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, E, ns);
