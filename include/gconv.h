@@ -189,7 +189,7 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
 /*
  * gradBias: db[k] = sum_{n,ho,wo} dy[n,k,ho,wo] (DLPrimitives Blog,
  * "Pointwise Broadcast Reduce": the sum of dy over dims 0, 2 and 3).
- * Only N, K, Ho and Wo of the descriptor matter. Overwrites db.
+ * Only N, K, Ho, Wo and the layout of the descriptor matter. Overwrites db.
  */
 int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* workspace,
                    size_t workspace_bytes, void* stream);
