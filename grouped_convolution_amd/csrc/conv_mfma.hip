@@ -279,7 +279,11 @@ struct ConvFlatArgs {
     FastDiv div_P, div_Wout, div_plane, div_LW;
 };
 
-template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, int MINW>
+// INH: the input is channels-last ([N][Hr][Wr][Cin_tot]); the LDS tile then
+// holds each pixel's 4 chunk channels together ([row][col][4]), filled by
+// 16-byte DMA (one pixel per lane), and a fragment's 16 pixels x 4 channels
+// read 64 consecutive floats.
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, int MINW, bool INH = false>
 __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlatArgs a)
 {
     constexpr int T = KH * KW;
@@ -324,9 +328,9 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
     uint32_t xoff[NSX];
 #pragma unroll
     for (int k = 0; k < NSX; ++k) {
-        const int e = (wave + NW * k) * 64 + lane;
-        const int c = (int)fastdiv((uint32_t)e, a.div_plane);
-        const int rem = e - c * a.plane;
+        const int e = (wave + NW * k) * 64 + lane;  // INH: the pixel slot of the tile
+        const int c = INH ? 0 : (int)fastdiv((uint32_t)e, a.div_plane);
+        const int rem = INH ? e : e - c * a.plane;
         const int v = (int)fastdiv((uint32_t)rem, a.div_LW);
         const int col = rem - v * a.LW;
         const bool second = v >= rows0;
@@ -340,7 +344,10 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             wr = w / a.uw;
             ok = ok && hr * a.uh == h && wr * a.uw == w;
         }
-        xoff[k] = ok ? (uint32_t)(((second ? a.Cin_tot : 0) + c) * HWin + hr * a.Wr + wr) * 4u : kOOB;
+        if constexpr (INH)
+            xoff[k] = ok ? (uint32_t)(((second ? HWin : 0) + hr * a.Wr + wr) * a.Cin_tot) * 4u : kOOB;
+        else
+            xoff[k] = ok ? (uint32_t)(((second ? a.Cin_tot : 0) + c) * HWin + hr * a.Wr + wr) * 4u : kOOB;
     }
 
     // LDS address (floats, buffer-relative) of each pixel fragment at tap 0,
@@ -355,7 +362,7 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
         const int ho = (int)fastdiv((uint32_t)p, a.div_Wout);
         const int wo = p - ho * a.Wout;
         const int v = (n == n0) ? (ho - ho0) * a.sh : rows0 + ho * a.sh;
-        la[f] = q * a.plane + v * a.LW + wo * a.sw;
+        la[f] = INH ? (v * a.LW + wo * a.sw) * 4 + q : q * a.plane + v * a.LW + wo * a.sw;
     }
 
     // Filter operands: lane (l16, q) holds W[o = l16 of fragment m][r = c0 + q][tap].
@@ -382,9 +389,23 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
         }
     };
 
-    const float* in_n0 = a.in + ((size_t)n0 * a.Cin_tot + (size_t)g * a.Cin_g) * HWin;
+    const float* in_n0 = INH ? a.in + (size_t)n0 * HWin * a.Cin_tot + (size_t)g * a.Cin_g
+                             : a.in + ((size_t)n0 * a.Cin_tot + (size_t)g * a.Cin_g) * HWin;
     const uint32_t second_recs = rows1 > 0 ? (uint32_t)a.Cin_tot * HWin : 0u;
+    auto issue_x_nhwc = [&](int c0, int buf) {
+        // Chunks are whole (Cin_g % 4 == 0): 16 bytes per pixel, all inside the group.
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(
+            in_n0 + c0, (second_recs + (uint32_t)a.Cin_tot * HWin - (uint32_t)(g * a.Cin_g + c0)) * 4u);
+        float* dst = lds + buf * a.bufsz + wave * 256;
+#pragma unroll
+        for (int k = 0; k < NSX; ++k)
+            if (k < a.nseg) load_lds256(rx, dst + k * (NW * 256), xoff[k]);
+    };
     auto issue_x = [&](int c0, int buf) {
+        if constexpr (INH) {
+            issue_x_nhwc(c0, buf);
+            return;
+        }
         const __amdgpu_buffer_rsrc_t rx =
             make_rsrc(in_n0 + (size_t)c0 * HWin, (second_recs + (uint32_t)(a.Cin_g - c0) * HWin) * 4u);
         // Channels past the group end: the second image's fall outside the
@@ -432,7 +453,7 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             const int cur = t & 1, nxt = cur ^ 1;
             if (t + 1 < T) {
                 const int i = (t + 1) / KW, j = (t + 1) % KW;
-                const int toff = i * a.dh * a.LW + j * a.dw;
+                const int toff = (i * a.dh * a.LW + j * a.dw) * (INH ? 4 : 1);
 #pragma unroll
                 for (int f = 0; f < MP; ++f) av[nxt][f] = xb[la[f] + toff];
             }
@@ -564,6 +585,7 @@ struct Problem {
     int uh = 1, uw = 1, Hr = 0, Wr = 0;  // input upsampling (flat kernel only), stored plane size
     int relu = 0;                        // forward epilogue
     int out_nhwc = 0;                    // channels-last output (flat kernel only)
+    int in_nhwc = 0;                     // channels-last input (flat kernel only; Cin_g % 4 == 0)
 };
 
 int choose_cc(const Problem& p) { return (p.kh * p.kw >= 16) ? 4 : 8; }
@@ -732,8 +754,11 @@ bool flat_plan(const Problem& p, FlatPlan& fp)
         LW = (int64_t)(p.Wout - 1) * p.sw + (p.kw - 1) * p.dw + 1;
         plane = LR * LW;
         plane = ((plane + 47) / 64) * 64 + 16;  // == 16 (mod 64): the 4 lane groups hit distinct banks
-        nseg = (4 * plane + 64 * NWi - 1) / (64 * NWi);
-        if (nseg <= fi.NSX) {
+        // channels-last input: one 16-byte DMA lane per pixel of the LR x LW tile
+        nseg = p.in_nhwc ? (LR * LW + 64 * NWi - 1) / (64 * NWi) : (4 * plane + 64 * NWi - 1) / (64 * NWi);
+        // (16 bytes a lane in the channels-last form, so its double buffer must
+        // also fit the CU's 160 KiB of LDS)
+        if (nseg <= fi.NSX && (!p.in_nhwc || 2 * nseg * 64 * NWi * 16 <= 160 * 1024)) {
             inst = &fi;
             break;
         }
@@ -747,11 +772,14 @@ bool flat_plan(const Problem& p, FlatPlan& fp)
     fp.LW = (int)LW;
     fp.plane = (int)plane;
     fp.nseg = (int)nseg;
-    fp.bufsz = (int)(nseg * 64 * NW);
+    fp.bufsz = (int)(nseg * 64 * NW * (p.in_nhwc ? 4 : 1));
     fp.lds_bytes = (size_t)2 * fp.bufsz * 4;
     // Buffer resources: two images' worth of one group's planes, and one
     // group's weights, addressed in bytes below 2^31.
     if ((int64_t)(p.Cin_tot + p.Cin_g) * p.Hr * p.Wr * 4 >= (int64_t(1) << 31)) return false;
+    if (p.in_nhwc && ((p.Cin_g & 3) != 0 || (p.Cin_tot & 3) != 0 ||
+                      (int64_t)2 * p.Hr * p.Wr * p.Cin_tot * 4 >= (int64_t(1) << 31)))
+        return false;
     if ((int64_t)p.w_gstride * 4 >= (int64_t(1) << 31)) return false;
     const int BO = inst->WO * inst->MO * 16;
     const int64_t blocks = ((NP + BPX - 1) / BPX) * p.G * ((p.Cout_g + BO - 1) / BO);
@@ -760,21 +788,21 @@ bool flat_plan(const Problem& p, FlatPlan& fp)
     return true;
 }
 
-template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP>
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, bool INH>
 void launch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     constexpr int MINW = (KH * KW <= 9) ? 4 : 2;
-    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW>;
+    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW, INH>;
     hipLaunchKernelGGL(kern, dim3(fp.blocks), dim3(64 * WO * WPX), fp.lds_bytes, st, a);
 }
 
-template <bool FLIP>
+template <bool FLIP, bool INH>
 bool dispatch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     const FlatInst& i = fp.inst;
 #define GCONV_FLAT_CASE(t, k, mo, wo, wpx, mp, nsx)                                     \
     if (i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
-        launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP>(a, fp, st);                       \
+        launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP, INH>(a, fp, st);                  \
         return true;                                                                   \
     }
     GCONV_FLAT_INSTS(GCONV_FLAT_CASE)
@@ -806,7 +834,8 @@ bool run_flat(const Problem& p, hipStream_t st)
     a.div_Wout = make_fastdiv((uint32_t)p.Wout);
     a.div_plane = make_fastdiv((uint32_t)fp.plane);
     a.div_LW = make_fastdiv((uint32_t)fp.LW);
-    return p.flip ? dispatch_flat<true>(a, fp, st) : dispatch_flat<false>(a, fp, st);
+    if (p.in_nhwc) return p.flip ? dispatch_flat<true, true>(a, fp, st) : dispatch_flat<false, true>(a, fp, st);
+    return p.flip ? dispatch_flat<true, false>(a, fp, st) : dispatch_flat<false, false>(a, fp, st);
 }
 
 bool use_flat(const Problem& p)
@@ -875,6 +904,35 @@ bool igemm_bwd_data_nhwc_out(const Shape& s, const float* dy, const float* w, fl
     if (!use_flat(p)) return false;
     p.out_nhwc = 1;
     return run_flat(p, st);
+}
+
+// Channels-last in and out: the flat kernel's loader reads NHWC pixels with
+// 16-byte DMA (4 channels per pixel) where the group's channels come in whole
+// quads; no reordering at all.
+static Problem nhwc_io(Problem p)
+{
+    p.in_nhwc = 1;
+    p.out_nhwc = 1;
+    return p;
+}
+
+bool igemm_nhwc_io_supported(const Shape& s, int op)
+{
+    if (op == GCONV_OP_FWD) return use_flat(nhwc_io(fwd_problem(s, nullptr, nullptr, nullptr, nullptr)));
+    if (op == GCONV_OP_BWD_DATA) return use_flat(nhwc_io(bwd_data_problem(s, nullptr, nullptr, nullptr)));
+    return false;
+}
+
+bool igemm_fwd_nhwc_io(const Shape& s, const float* x, const float* w, const float* bias, float* y, hipStream_t st)
+{
+    const Problem p = nhwc_io(fwd_problem(s, x, w, bias, y));
+    return use_flat(p) && run_flat(p, st);
+}
+
+bool igemm_bwd_data_nhwc_io(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    const Problem p = nhwc_io(bwd_data_problem(s, dy, w, dx));
+    return use_flat(p) && run_flat(p, st);
 }
 
 }  // namespace gconv

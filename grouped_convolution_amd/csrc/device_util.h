@@ -42,6 +42,13 @@ __device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
 }
 
+// The 64 lanes load 16 bytes each into 256 consecutive LDS floats at `dst`
+// (lane i to dst + 4i; wave-uniform `dst`); out-of-range offsets write 0.
+__device__ __forceinline__ void load_lds256(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, byte_off, 0, 0, 0);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs of the MI355X (block b
 // runs on XCD b % 8). Renumber so that each XCD gets a contiguous range of
 // logical tiles: neighbouring tiles then share that XCD's L2.

@@ -472,6 +472,13 @@ int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const floa
         char* base = (char*)workspace;
         float* xs = (float*)base;
         float* ys = (float*)(base + stage_bytes(s.x_elems));
+        const bool a16 = ((uintptr_t)x & 15) == 0;
+        if (p.path == GCONV_PATH_IGEMM && a16 && igemm_nhwc_io_supported(p.e, GCONV_OP_FWD)) {
+            // The flat MFMA kernel reads x and stores y channels-last itself.
+            if (!igemm_fwd_nhwc_io(p.e, x, w, bias, y, hs))
+                st = fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            return st != GCONV_OK ? st : epilogue();
+        }
         st = reorder(x, xs, s.N, (int64_t)s.H * s.W, s.C, hs);
         // The flat MFMA kernel stores y channels-last itself.
         if (st == GCONV_OK && p.path == GCONV_PATH_IGEMM && igemm_nhwc_out_supported(p.e, GCONV_OP_FWD)) {
@@ -507,6 +514,13 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
         char* base = (char*)workspace;
         float* dys = (float*)base;
         float* dxs = (float*)(base + stage_bytes(s.y_elems));
+        const bool a16 = ((uintptr_t)dy & 15) == 0;
+        if (p.path == GCONV_PATH_IGEMM && a16 && igemm_nhwc_io_supported(p.e, GCONV_OP_BWD_DATA)) {
+            // The flat MFMA kernel reads dy and stores dx channels-last itself.
+            if (!igemm_bwd_data_nhwc_io(p.e, dy, w, dx, hs))
+                st = fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
+            return st != GCONV_OK ? st : epilogue();
+        }
         st = reorder(dy, dys, s.N, (int64_t)s.Ho * s.Wo, s.K, hs);
         if (st == GCONV_OK && p.path == GCONV_PATH_IGEMM && igemm_nhwc_out_supported(p.e, GCONV_OP_BWD_DATA)) {
             if (!igemm_bwd_data_nhwc_out(p.e, dys, w, dx, hs))

@@ -68,6 +68,10 @@ bool igemm_nhwc_out_supported(const Shape& s, int op);
 bool igemm_fwd_nhwc_out(const Shape& s, const float* x, const float* w, const float* bias, float* y,
                         hipStream_t st);
 bool igemm_bwd_data_nhwc_out(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+// ... and reading x or dy channels-last too (no reordering).
+bool igemm_nhwc_io_supported(const Shape& s, int op);
+bool igemm_fwd_nhwc_io(const Shape& s, const float* x, const float* w, const float* bias, float* y, hipStream_t st);
+bool igemm_bwd_data_nhwc_io(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
 
 // ---- fp32-MFMA gradWeight (split pixel reduction + deterministic reduce) -----
 bool igemm_bwd_filter_supported(const Shape& s);

@@ -118,6 +118,14 @@ NHWC_CASES = [
     # of pixels and channels with ragged tails
     (dict(N=3, C=70, K=66, H=13, W=11, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1),
      {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "igemm", "bwd_bias": "direct"}),
+    # channel counts in whole quads: the flat MFMA kernel reads the NHWC input itself
+    # (16-byte DMA per pixel) and stores NHWC; two groups at stride 2 (gradInput reads
+    # dy as if upsampled) ...
+    (dict(N=2, C=64, K=96, H=15, W=17, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=2),
+     {"fwd": "igemm", "bwd_data": "igemm"}),
+    # ... and 5x5 with tiles spanning two images
+    (dict(N=3, C=16, K=32, H=9, W=11, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=1),
+     {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "igemm"}),
     # ResNeXt-style 4 per group and depthwise stride 2 (small-group family)
     (dict(N=2, C=32, K=32, H=14, W=15, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8),
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
