@@ -384,10 +384,12 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             const uint32_t base =
                 (r < a.Cin_g && wbase[m] >= 0) ? (uint32_t)(wbase[m] + r * a.w_sr) * 4u : kOOB;
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                b[m][t] = load_f32(rw, base + (uint32_t)(FLIP ? T - 1 - t : t) * 4u);
+            for (int t = 0; t < T; ++t) b[m][t] = load_f32(rw, base + (uint32_t)t * 4u);
         }
     };
+    // Taps in memory order (so the loads merge into 16-byte ones); the flipped
+    // filter of gradInput picks them in reverse at the MFMA.
+    constexpr auto tap = [](int t) { return FLIP ? T - 1 - t : t; };
 
     const float* in_n0 = INH ? a.in + (size_t)n0 * HWin * a.Cin_tot + (size_t)g * a.Cin_g
                              : a.in + ((size_t)n0 * a.Cin_tot + (size_t)g * a.Cin_g) * HWin;
@@ -461,8 +463,8 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             for (int f = 0; f < MP; ++f)
 #pragma unroll
                 for (int m = 0; m < MO; ++m)
-                    acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cur][f], bc[m][t], acc[f][m],
-                                                                     0, 0, 0);
+                    acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cur][f], bc[m][tap(t)],
+                                                                     acc[f][m], 0, 0, 0);
             if (t + 1 < T) __builtin_amdgcn_sched_group_barrier(0x100, MP, 0);  // LDS reads first
             __builtin_amdgcn_sched_group_barrier(0x008, MP * MO, 0);          // then the MFMAs
             __builtin_amdgcn_sched_barrier(0);
