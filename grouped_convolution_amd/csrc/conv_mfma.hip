@@ -412,15 +412,19 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             make_rsrc(in_n0 + (size_t)c0 * HWin, (second_recs + (uint32_t)(a.Cin_g - c0) * HWin) * 4u);
         // Channels past the group end: the second image's fall outside the
         // resource; the first image's would alias the next group, so mask them.
+        // (A uniform branch: whole chunks issue their DMA with no per-lane select.)
         const int lim = min(CC, a.Cin_g - c0) * a.plane;
         float* dst = lds + buf * a.bufsz + wave * 64;
+        if (lim >= CC * a.plane) {
 #pragma unroll
-        for (int k = 0; k < NSX; ++k) {
-            if (k < a.nseg) {
-                uint32_t off = xoff[k];
-                if (lim < CC * a.plane) off = ((wave + NW * k) * 64 + lane < lim) ? off : kOOB;
-                load_lds64(rx, dst + k * (NW * 64), off);
-            }
+            for (int k = 0; k < NSX; ++k)
+                if (k < a.nseg) load_lds64(rx, dst + k * (NW * 64), xoff[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NSX; ++k)
+                if (k < a.nseg)
+                    load_lds64(rx, dst + k * (NW * 64),
+                               ((wave + NW * k) * 64 + lane < lim) ? xoff[k] : kOOB);
         }
     };
 
