@@ -450,6 +450,45 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             issue_x((ch + 1) * CC, (ch + 1) & 1);
             load_b((ch + 1) * CC, bn);
         }
+        if (MO == 1 && a.dw == 1) {
+            // Unit column dilation: a row's taps sit at compile-time offsets
+            // from one address per fragment, so the LDS reads take immediate
+            // offsets and only each filter row's start is added. (Instances
+            // with two output fragments per wave keep the general form: the
+            // extra registers cost them more than the adds.)
+            constexpr int CS = INH ? 4 : 1;
+            const int rstep = a.dh * a.LW * CS;
+            const int boff = (ch & 1) * a.bufsz;
+            int ra[MP];
+#pragma unroll
+            for (int f = 0; f < MP; ++f) ra[f] = la[f] + boff;
+            float av[2][MP];
+#pragma unroll
+            for (int f = 0; f < MP; ++f) av[0][f] = lds[ra[f]];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int cur = t & 1, nxt = cur ^ 1;
+                if (t + 1 < T) {
+                    const int j = (t + 1) % KW;
+                    if (j == 0) {
+#pragma unroll
+                        for (int f = 0; f < MP; ++f) ra[f] += rstep;
+                    }
+#pragma unroll
+                    for (int f = 0; f < MP; ++f) av[nxt][f] = lds[ra[f] + j * CS];
+                }
+#pragma unroll
+                for (int f = 0; f < MP; ++f)
+#pragma unroll
+                    for (int m = 0; m < MO; ++m)
+                        acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cur][f], bc[m][tap(t)],
+                                                                         acc[f][m], 0, 0, 0);
+                if (t + 1 < T) __builtin_amdgcn_sched_group_barrier(0x100, MP, 0);  // LDS reads first
+                __builtin_amdgcn_sched_group_barrier(0x008, MP * MO, 0);          // then the MFMAs
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            continue;
+        }
         const float* xb = lds + (ch & 1) * a.bufsz;
         float av[2][MP];
 #pragma unroll
