@@ -178,10 +178,20 @@ __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
         auto fetch = [&](int slot, int rr, int ss) {
             const float* xr = xl + rr * a.sh * a.LW + ss * 4 * a.sw;
             const float* dr = dl + rr * a.WoP + ss * 4;
+            if (a.dw == 1) {
+                // Unit column dilation: a filter row's taps at immediate offsets.
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int i = t / KW, j = t % KW;
-                av[slot][t] = xr[i * a.dh * a.LW + j * a.dw];
+                for (int i = 0; i < KH; ++i) {
+                    const float* xri = xr + i * a.dh * a.LW;
+#pragma unroll
+                    for (int j = 0; j < KW; ++j) av[slot][i * KW + j] = xri[j];
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int i = t / KW, j = t % KW;
+                    av[slot][t] = xr[i * a.dh * a.LW + j * a.dw];
+                }
             }
 #pragma unroll
             for (int m = 0; m < WK; ++m) bv[slot][m] = dr[m * 16 * a.DS];
