@@ -33,8 +33,12 @@ inline bool is_fc_mode(const Shape& s)
 {
     // Kernel covers the whole (unpadded) input: the conv is one dense layer
     // on the flattened image ("SpatialConvolution running in fully-connected
-    // mode is very slow, even with R4", the View + Linear replacement).
-    return s.kh == s.H && s.kw == s.W && s.ph == 0 && s.pw == 0 && s.Ho == 1 && s.Wo == 1;
+    // mode is very slow, even with R4", the View + Linear replacement). Only
+    // undilated taps read every input pixel once: a dilated kernel the size of
+    // the input reaches past it, into the end padding, and is not a Linear
+    // layer (dilation is moot on an axis with a single tap).
+    return s.kh == s.H && s.kw == s.W && s.ph == 0 && s.pw == 0 && (s.dh == 1 || s.kh == 1) &&
+           (s.dw == 1 || s.kw == 1) && s.Ho == 1 && s.Wo == 1;
 }
 
 // ---- general direct kernels (any valid descriptor) -------------------------

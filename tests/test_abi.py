@@ -234,3 +234,31 @@ def test_layout_field():
         assert B.gconv_workspace_size(gemm, op) == 0
     # gradBias of NHWC dy: the split partials of the column layout
     assert B.gconv_workspace_size(nhwc, B.OP_BWD_BIAS) > 0
+
+
+def test_dilated_kernel_never_routes_to_fc():
+    """Kernel == input is a Linear layer only with undilated taps ("SpatialConvolution
+    running in fully-connected mode is very slow, even with R4", the View + Linear
+    replacement): a dilated kernel as large as the input reads the end padding, so no
+    descriptor with dilation above 1 on an axis whose kernel spans more than one tap
+    is routed to the fully-connected GEMM."""
+    # the case that once went to FC: 2x2 kernel, dilation 2, one row and column of end padding
+    desc = B.make_desc(3, 4, 2, 2, 5, 2, 2, 1, (0, 1, 0, 1), 2, 1)
+    assert B.gconv_output_dims(desc) == (1, 1)
+    for op in (B.OP_FWD, B.OP_BWD_DATA, B.OP_BWD_FILTER):
+        assert B.gconv_select_path(desc, op) != B.PATH_FC
+    for H in range(1, 7):
+        for W in range(1, 7):
+            for dh in (1, 2, 3):
+                for dw in (1, 2, 3):
+                    for pb in range(0, 2 * max(dh, dw) * 3):
+                        for pr in (0, pb):
+                            try:
+                                desc = B.make_desc(2, 4, H, W, 4, H, W, 1, (0, pb, 0, pr), (dh, dw), 1)
+                                B.gconv_output_dims(desc)
+                            except B.GconvError:
+                                continue
+                            for op in (B.OP_FWD, B.OP_BWD_DATA, B.OP_BWD_FILTER):
+                                fc = B.gconv_select_path(desc, op) == B.PATH_FC
+                                if (dh > 1 and H > 1) or (dw > 1 and W > 1):
+                                    assert not fc, (H, W, dh, dw, pb, pr, op)

@@ -393,6 +393,10 @@ ASYM_CASES = [
     # kernel == input with end padding below the stride: still one output, FC mode
     (dict(N=5, C=8, K=6, H=3, W=3, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1,
           G=1), {"fwd": "fc", "bwd_data": "fc", "bwd_filter": "fc"}),
+    # a dilated kernel the size of the input with end padding: one output, but its taps past
+    # (0, 0) fall in the padding, so it is not a Linear layer and leaves the FC path
+    (dict(N=3, C=4, K=5, H=2, W=2, kh=2, kw=2, sh=1, sw=1, ph=0, pb=1, pw=0, pr=1, dh=2, dw=2,
+          G=1), {"fwd": "direct", "bwd_data": "direct", "bwd_filter": "direct"}),
 ]
 
 
