@@ -46,6 +46,13 @@ MUTANTS = [
      "x[((n * d->C + c) * d->H + h) * d->W + w];", 1),
     ("bwd_filter_pad_sign", "const int64_t h = ho * d->stride_h - d->pad_h + i * d->dil_h;",
      "const int64_t h = ho * d->stride_h + d->pad_h + i * d->dil_h;", 1),
+    # the per-element magnitude A_e of each op (the scale of every tolerance bound)
+    ("fwd_abs_bias_dropped", "a += fabs(bias[k]);", "a += 0.0;", 0),
+    ("bwd_data_abs_scaled", "a += fabs(p);", "a += 4.0 * fabs(p);", 1),
+    ("bwd_filter_abs_scaled", "a += fabs(p);", "a += 4.0 * fabs(p);", 2),
+    ("bwd_filter_abs_signed", "a += fabs(p);", "a += p;", 2),
+    ("bwd_bias_abs_scaled", "a += fabs(v);", "a += 4.0 * fabs(v);", 0),
+    ("bwd_bias_abs_signed", "a += fabs(v);", "a += v;", 0),
     ("bwd_bias_drops_column", "const double v = dy[((n * d->K + k) * Ho + ho) * Wo + wo];",
      "const double v = wo ? dy[((n * d->K + k) * Ho + ho) * Wo + wo] : 0.0;", 0),
     ("extent_ceil", "return num / s + 1;", "return (num + s - 1) / s + 1;", 0),
@@ -89,6 +96,7 @@ def _battery():
     run("adjoint", pins.test_adjoint_identities)
     run("bias", pins.test_bias_closed_forms)
     run("abs_sum", pins.test_abs_sum_is_sum_of_abs_products)
+    run("abs_sums_vs_torch", lambda: pins.test_abs_sums_match_torch(0))
     run("closed_forms", closed_forms)
     run("asym_explicit_pad", lambda: pins.test_asymmetric_padding_equals_explicit_zero_pad(0))
     return failed

@@ -382,6 +382,53 @@ def test_abs_sum_is_sum_of_abs_products():
     np.testing.assert_allclose(ya2, ya, rtol=1e-14)
 
 
+def torch_abs_sums(x, w, b, dy, d):
+    """Per-element sums of |product| from torch CPU float64, independently of the
+    oracle: each op's terms with every factor replaced by its absolute value.
+    The forward map is linear in x and in w, so
+      fwd:        conv2d(|x|, |w|) + |b|
+      bwd_data:   d<conv2d(x, |w|), |dy|>/dx   (= sum of |w|*|dy| over the taps that read x)
+      bwd_filter: d<conv2d(|x|, w), |dy|>/dw   (= sum of |dy|*|x| over the pixels)
+      bwd_bias:   |dy| summed over images and pixels.
+    The padding is applied to the input explicitly (F.pad), so the end pads may
+    differ from the start pads."""
+    pad = (d["pw"], d.get("pr", d["pw"]), d["ph"], d.get("pb", d["ph"]))
+    conv = dict(stride=(d["sh"], d["sw"]), dilation=(d["dh"], d["dw"]), groups=d["G"])
+    f64 = lambda a: torch.tensor(np.abs(a), dtype=torch.float64)
+    xa, wa, dya = f64(x), f64(w), f64(dy)
+    ya = F.conv2d(F.pad(xa, pad), wa, None if b is None else f64(b), **conv)
+    xv = torch.zeros_like(xa, requires_grad=True)
+    (dxa,) = torch.autograd.grad((F.conv2d(F.pad(xv, pad), wa, **conv) * dya).sum(), [xv])
+    wv = torch.zeros_like(wa, requires_grad=True)
+    (dwa,) = torch.autograd.grad((F.conv2d(F.pad(xa, pad), wv, **conv) * dya).sum(), [wv])
+    return ya.numpy(), dxa.numpy(), dwa.numpy(), dya.sum(dim=(0, 2, 3)).numpy()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_abs_sums_match_torch(seed):
+    """A_e, the scale of every tolerance bound, is pinned for all four ops: the
+    oracle's per-element sums of |product| (forward with |bias|, as the bias add
+    rounds too) equal torch float64 on absolute values, on random descriptors
+    with symmetric and asymmetric padding, strides and dilations, and the bias
+    sum of |dy| ("Pointwise Broadcast Reduce", DLPrimitives Blog: gradBias sums
+    dy over images and pixels)."""
+    descs = random_descs(60 + seed, 10) + asym_descs(70 + seed, 6)
+    for t, d in enumerate(descs):
+        kw = conv_kwargs(d)
+        x, w, b = tensors(d, 8000 + 10 * seed + t)
+        pad = (d["pw"], d.get("pr", d["pw"]), d["ph"], d.get("pb", d["ph"]))
+        y_shape = F.conv2d(F.pad(torch.tensor(x, dtype=torch.float64), pad),
+                           torch.tensor(w, dtype=torch.float64), stride=kw["stride"],
+                           dilation=kw["dilation"], groups=d["G"]).shape
+        dy = draw(("normal", 1.0), tuple(y_shape), 8500 + 10 * seed + t)
+        ya_t, dxa_t, dwa_t, dba_t = torch_abs_sums(x, w, b, dy, d)
+        (_, ya), (_, dxa), (_, dwa), (_, dba) = run_oracle_all(x, w, b, dy, kw)
+        for name, got, want in (("fwd", ya, ya_t), ("bwd_data", dxa, dxa_t),
+                                ("bwd_filter", dwa, dwa_t), ("bwd_bias", dba, dba_t)):
+            assert got.shape == want.shape, (name, d)
+            assert np.allclose(got, want, rtol=1e-12, atol=1e-14), (name, d)
+
+
 def test_empty_batch():
     """N = 0 is a valid descriptor: empty y and gradInput, zero gradWeight and
     gradBias (sums over no terms), as torch's float64 conv gives."""
