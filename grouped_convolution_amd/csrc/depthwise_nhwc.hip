@@ -269,7 +269,17 @@ struct DwWgradArgs {
     FastDiv div_cq, div_hw, div_wo;
 };
 
-template <int KS, bool RUN>
+// Four consecutive channels of one pixel: one 16-byte load when the tensors
+// are 16-byte aligned, four 4-byte loads otherwise (e.g. a view that starts
+// one float into its allocation).
+template <bool V4>
+__device__ inline f4 ld_quad(const float* p)
+{
+    if constexpr (V4) return *reinterpret_cast<const f4*>(p);
+    else return f4{p[0], p[1], p[2], p[3]};
+}
+
+template <int KS, bool RUN, bool V4 = true>
 __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
 {
     constexpr int T = KS * KS;
@@ -328,7 +338,7 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
             const int q = p - n * a.Ho * a.Wo;
             const int oh = (int)fastdiv((uint32_t)q, a.div_wo);
             const int ow = q - oh * a.Wo;
-            const f4 d = *reinterpret_cast<const f4*>(a.dy + (size_t)p * a.C + c);
+            const f4 d = ld_quad<V4>(a.dy + (size_t)p * a.C + c);
             const float* img = a.x + (size_t)n * a.H * a.W * a.C + c;
 #pragma unroll
             for (int i = 0; i < KS; ++i) {
@@ -338,7 +348,7 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
                 for (int j = 0; j < KS; ++j) {
                     const int w = ow * a.sw - a.pw + j * a.dw;
                     if ((unsigned)w >= (unsigned)a.W) continue;
-                    const f4 v = *reinterpret_cast<const f4*>(img + ((size_t)h * a.W + w) * a.C);
+                    const f4 v = ld_quad<V4>(img + ((size_t)h * a.W + w) * a.C);
                     const int tt = i * KS + j;
                     acc[tt] = fmaf(d.x, v.x, acc[tt]);
                     acc[T + tt] = fmaf(d.y, v.y, acc[T + tt]);
@@ -429,13 +439,27 @@ bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* 
     DwWgradArgs a;
     int ns;
     if (!dw_wgrad_plan(s, &a, &ns)) return false;
-    if (((uintptr_t)x & 15) || ((uintptr_t)dy & 15)) return false;
     if (ns > 1 && !ws) return false;
     a.x = x; a.dy = dy; a.out = ns > 1 ? ws : dw;
     const int T = s.kh * s.kw;
     const size_t lds = (size_t)a.NP * a.CQ * 4 * T * sizeof(float);
     const bool run = s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1;
-    if (s.kh == 3) {
+    if (((uintptr_t)x & 15) || ((uintptr_t)dy & 15)) {
+        // Tensors that are not 16-byte aligned: the one-pixel units with
+        // 4-byte loads (the run units hold windows of 16-byte loads). The plan
+        // (slices, units per slice) is the same, so is the workspace.
+        if (run) {
+            a.nb = s.Wo;
+            a.total = s.N * s.Ho * s.Wo;
+            a.slice = (int)(((int64_t)a.total + ns - 1) / ns);
+            ns = (a.total + a.slice - 1) / a.slice;
+            a.div_hw = make_fastdiv((uint32_t)(s.Ho * s.Wo));
+            a.div_wo = make_fastdiv((uint32_t)s.Wo);
+            a.out = ns > 1 ? ws : dw;
+        }
+        if (s.kh == 3) hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<3, false, false>), dim3(ns), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<5, false, false>), dim3(ns), dim3(256), lds, st, a);
+    } else if (s.kh == 3) {
         if (run) hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<3, true>), dim3(ns), dim3(256), lds, st, a);
         else hipLaunchKernelGGL((dw_nhwc_wgrad_kernel<3, false>), dim3(ns), dim3(256), lds, st, a);
     } else {

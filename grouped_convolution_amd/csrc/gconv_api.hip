@@ -552,7 +552,7 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
     }
     if (p.native) {
         if (!dw_nhwc_bwd_filter(s, x, dy, dw, (float*)workspace, hs))
-            st = fail(GCONV_ERR_ARG, "channels-last depthwise gradWeight needs 16-byte aligned x and dy");
+            st = fail(GCONV_ERR_UNSUPPORTED, "no channels-last depthwise gradWeight plan for this shape");
     } else if (!p.staged) {
         st = run_bwd_filter(p.e, p.path, x, dy, dw, (float*)workspace, hs);
     } else {

@@ -90,8 +90,8 @@ typedef struct gconv_desc {
  * one GEMM over the N*H*W rows (the fully-connected path, no reordering);
  * gradBias sums the [N*Ho*Wo, K] rows of dy directly; depthwise layers (one
  * channel per group, 3x3 or 5x5) run on channels-last kernels of their own
- * (gradWeight there, when C % 4 == 0 and no family is forced, needs x and dy
- * 16-byte aligned and returns GCONV_ERR_ARG otherwise). Every other NHWC op
+ * (gradWeight there when C % 4 == 0 and no family is forced; x and dy that
+ * are not 16-byte aligned take 4-byte loads). Every other NHWC op
  * reorders its NHWC inputs to NCHW in the workspace, runs the NCHW kernels
  * there and reorders the NHWC outputs back (the MFMA implicit-GEMM forward
  * and gradInput store y and dx channels-last themselves), so
@@ -132,14 +132,26 @@ typedef enum gconv_path {
                                   (image, group), gradWeight split over images */
 } gconv_path;
 
-/* Output extent of the descriptor (the floor rule above). */
+/*
+ * Output extent of the descriptor: the floor rule above, which fits every
+ * shape the pages print ("Support groups in DenseConvDims": a 3x3 kernel
+ * takes the 28x28 grouped benchmark input to 26x26; "SpatialConvolution
+ * running in fully-connected mode is very slow, even with R4": a 6x6 kernel
+ * on a 6x6 input gives the 1x1 output MatConvNet's gradient shape shows).
+ * Writes *Ho and *Wo and returns GCONV_OK, or returns the descriptor's error
+ * status (GCONV_ERR_SHAPE when the dilated kernel exceeds the padded input)
+ * and writes nothing. Host only; launches nothing.
+ */
 int gconv_output_dims(const gconv_desc* d, int64_t* Ho, int64_t* Wo);
 
 /*
- * Bytes of device workspace `op` needs for this descriptor (0 when none).
- * Pass at least this much to the op, 16-byte aligned (GCONV_ERR_WORKSPACE
- * otherwise); the workspace may be NULL when 0. The contents need no
- * initialisation and are scratch after the call.
+ * Bytes of device workspace `op` (a gconv_op) needs for this descriptor (0
+ * when none), written to *bytes. Pass at least this much to the op, 16-byte
+ * aligned (GCONV_ERR_WORKSPACE otherwise); the workspace may be NULL when 0.
+ * The contents need no initialisation and are scratch after the call. The
+ * size comes back through *bytes so that an invalid descriptor or op can
+ * return its status (GCONV_ERR_SHAPE, GCONV_ERR_GROUPS, GCONV_ERR_ARG) rather
+ * than a size a caller might allocate. Host only.
  */
 int gconv_workspace_size(const gconv_desc* d, int op, size_t* bytes);
 
@@ -210,7 +222,13 @@ int gconv_set_path_override(int path);
 
 const char* gconv_status_string(int status);
 
-/* Detail of the calling thread's last failed call ("" if none). */
+/*
+ * Readable detail of the calling thread's last failed call, "" after a call
+ * that succeeded ("Support groups in DenseConvDims" adds a channel check so
+ * that a bad group split gets a clear message: here, e.g., "input channels
+ * C=10 not divisible by groups=3"). The string is owned by the library and
+ * stays valid until the thread's next call into it.
+ */
 const char* gconv_last_error(void);
 
 /* Library version: major*10000 + minor*100 + patch. */

@@ -220,3 +220,37 @@ def test_nhwc_workspace_guard_bands():
         for t in (buf, obuf):
             h = t.cpu().numpy()
             assert np.all(h[:pad] == sentinel) and np.all(h[-pad:] == sentinel), name
+
+
+@pytest.mark.parametrize("stride", [1, 2])
+def test_nhwc_depthwise_wgrad_misaligned(stride):
+    """Channels-last depthwise gradWeight on x and dy that start one float into
+    their allocations (not 16-byte aligned): the native kernel takes 4-byte
+    loads and agrees with the oracle, with normal data to the tolerance and
+    integer data bit for bit; the workspace is the aligned call's."""
+    d = dict(N=3, C=12, K=12, H=11, W=13, kh=3, kw=3, sh=stride, sw=stride, ph=1, pw=1, dh=1, dw=1, G=12)
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], 3, 3, layout="nhwc", **kw)
+    nws = G.gconv_workspace_size(desc, G.OP_BWD_FILTER)
+    for dist, seed in ((("normal", 1.0), 3700), (("int", -3, 3), 3800)):
+        x, w, _ = tensors(d, seed + stride, dist=dist, bias=False)
+        y_ref, _ = oracle.fwd(x, w, None, **kw)
+        dy = draw(dist, y_ref.shape, seed + 10 + stride)
+        say("misaligned nhwc depthwise gradWeight stride %d %s" % (stride, dist[0]))
+
+        def offset_view(a):
+            flat = torch.zeros(a.size + 1, device="cuda")
+            v = flat[1:].view(*a.shape)
+            v.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+            assert v.data_ptr() % 16 != 0
+            return v
+
+        xd, dyd = offset_view(to_nhwc(x)), offset_view(to_nhwc(dy))
+        ws = torch.empty(max(nws // 4, 1), device="cuda")
+        dw = G.gconv_bwd_filter(xd, dyd, w.shape, layout="nhwc", workspace=ws, **kw)
+        torch.cuda.synchronize()
+        val, mag = oracle.bwd_filter(x, dy, w.shape, **kw)
+        if dist[0] == "int":
+            assert np.array_equal(dw.cpu().numpy().astype(np.float64), val)
+        else:
+            check("misaligned dw", dw.cpu().numpy(), val, mag)

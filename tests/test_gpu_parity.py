@@ -822,3 +822,49 @@ def test_binding_rejects_bad_tensors():
         G.gconv_fwd(x, w, groups=3)
     with pytest.raises(ValueError):
         G.gconv_bwd_data(torch.zeros((2, 4, 4, 4), device="cuda"), w, x.shape, groups=2)
+
+
+def test_c_abi_symbols_directly():
+    """The four ops called through their own C symbols (gconv_fwd itself, not the
+    binding's gconv_fwd_ex), with plain device pointers, a caller-owned workspace
+    and torch's current stream, on a grouped descriptor whose gradWeight and
+    gradBias use the workspace; every result against the oracle."""
+    import ctypes
+    from grouped_convolution_amd import binding as B
+    lib = B.load()
+    d = dict(N=3, C=32, K=48, H=13, W=11, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2)
+    kw = conv_kwargs(d)
+    x, w, b = tensors(d, 3900)
+    y_ref, _ = oracle.fwd(x, w, b, **kw)
+    dy = draw(("normal", 1.0), y_ref.shape, 3903)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
+    ho, wo = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.gconv_output_dims(ctypes.byref(desc), ctypes.byref(ho), ctypes.byref(wo)) == 0
+    assert (ho.value, wo.value) == y_ref.shape[2:]
+    xd, wd, bd, dyd = dev(x), dev(w), dev(b), dev(dy)
+    y = torch.empty(y_ref.shape, device="cuda")
+    dx = torch.empty(x.shape, device="cuda")
+    dw = torch.empty(w.shape, device="cuda")
+    db = torch.empty((d["K"],), device="cuda")
+    sizes = []
+    for op in range(4):
+        n = ctypes.c_size_t()
+        assert lib.gconv_workspace_size(ctypes.byref(desc), op, ctypes.byref(n)) == 0
+        sizes.append(n.value)
+    ws = torch.empty(max(max(sizes) // 4, 1), device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    D = ctypes.byref(desc)
+    say("raw C-ABI calls %s, workspaces %s" % (d, sizes))
+    assert lib.gconv_fwd(D, P(xd), P(wd), P(bd), P(y), P(ws), ctypes.c_size_t(sizes[0]), st) == 0
+    assert lib.gconv_bwd_data(D, P(dyd), P(wd), P(dx), P(ws), ctypes.c_size_t(sizes[1]), st) == 0
+    assert lib.gconv_bwd_filter(D, P(xd), P(dyd), P(dw), P(ws), ctypes.c_size_t(sizes[2]), st) == 0
+    assert lib.gconv_bwd_bias(D, P(dyd), P(db), P(ws), ctypes.c_size_t(sizes[3]), st) == 0
+    assert lib.gconv_last_error() == b""
+    torch.cuda.synchronize()
+    compare_full("raw C ABI", (y, dx, dw, db), oracle_all(x, w, b, dy, kw))
+    # gconv_fwd without a bias pointer
+    assert lib.gconv_fwd(D, P(xd), P(wd), None, P(y), P(ws), ctypes.c_size_t(sizes[0]), st) == 0
+    torch.cuda.synchronize()
+    val, mag = oracle.fwd(x, w, None, **kw)
+    check("raw gconv_fwd no bias", y.cpu().numpy(), val, mag)
