@@ -265,6 +265,8 @@ size_t workspace_for(const Shape& s, int op, int path)
         return pointwise_bwd_filter_workspace(s);
     if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_FC && s.N > 0)
         return fc_bwd_filter_workspace(s);
+    if ((op == GCONV_OP_FWD || op == GCONV_OP_BWD_DATA) && path == GCONV_PATH_FC && s.N > 0)
+        return fc_data_workspace(s, op);
     if (op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_DIRECT && s.N > 0)
         return direct_bwd_filter_workspace(s);
     return 0;
@@ -310,7 +312,7 @@ int prologue(const gconv_desc* d, int op, Prep* p, void* ws, size_t ws_bytes)
 
 // The kernels of one op on an NCHW shape.
 int run_fwd(const Shape& s, int path, const float* x, const float* w, const float* bias, float* y,
-            hipStream_t hs)
+            float* ws, hipStream_t hs)
 {
     switch (path) {
         case GCONV_PATH_DIRECT: direct_fwd(s, x, w, bias, y, hs); return GCONV_OK;
@@ -318,7 +320,10 @@ int run_fwd(const Shape& s, int path, const float* x, const float* w, const floa
             if (!igemm_fwd(s, x, w, bias, y, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             return GCONV_OK;
-        case GCONV_PATH_FC: fc_fwd(s, x, w, bias, y, hs); return GCONV_OK;
+        case GCONV_PATH_FC:
+            if (!fc_fwd(s, x, w, bias, y, ws, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "fully-connected forward needs its workspace");
+            return GCONV_OK;
         case GCONV_PATH_POINTWISE: pointwise_fwd(s, x, w, bias, y, hs); return GCONV_OK;
         case GCONV_PATH_SMALLGROUP:
             if (!smallgroup_fwd(s, x, w, bias, y, hs))
@@ -328,7 +333,8 @@ int run_fwd(const Shape& s, int path, const float* x, const float* w, const floa
     }
 }
 
-int run_bwd_data(const Shape& s, int path, const float* dy, const float* w, float* dx, hipStream_t hs)
+int run_bwd_data(const Shape& s, int path, const float* dy, const float* w, float* dx, float* ws,
+                 hipStream_t hs)
 {
     switch (path) {
         case GCONV_PATH_DIRECT: direct_bwd_data(s, dy, w, dx, hs); return GCONV_OK;
@@ -336,7 +342,10 @@ int run_bwd_data(const Shape& s, int path, const float* dy, const float* w, floa
             if (!igemm_bwd_data(s, dy, w, dx, hs))
                 return fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
             return GCONV_OK;
-        case GCONV_PATH_FC: fc_bwd_data(s, dy, w, dx, hs); return GCONV_OK;
+        case GCONV_PATH_FC:
+            if (!fc_bwd_data(s, dy, w, dx, ws, hs))
+                return fail(GCONV_ERR_UNSUPPORTED, "fully-connected gradInput needs its workspace");
+            return GCONV_OK;
         case GCONV_PATH_POINTWISE: pointwise_bwd_data(s, dy, w, dx, hs); return GCONV_OK;
         case GCONV_PATH_SMALLGROUP:
             if (!smallgroup_bwd_data(s, dy, w, dx, hs))
@@ -467,11 +476,12 @@ int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const floa
         sr.relu = p.e.relu;
         dw_nhwc_fwd(sr, x, w, bias, y, hs);
     } else if (!p.staged) {
-        st = run_fwd(p.e, p.path, x, w, bias, y, hs);
+        st = run_fwd(p.e, p.path, x, w, bias, y, (float*)workspace, hs);
     } else {
         char* base = (char*)workspace;
         float* xs = (float*)base;
         float* ys = (float*)(base + stage_bytes(s.x_elems));
+        float* rest = (float*)(base + staging_bytes(s, GCONV_OP_FWD));
         const bool a16 = ((uintptr_t)x & 15) == 0;
         if (p.path == GCONV_PATH_IGEMM && a16 && igemm_nhwc_io_supported(p.e, GCONV_OP_FWD)) {
             // The flat MFMA kernel reads x and stores y channels-last itself.
@@ -485,7 +495,7 @@ int gconv_fwd_ex(const gconv_desc* d, const float* x, const float* w, const floa
             if (!igemm_fwd_nhwc_out(p.e, xs, w, bias, y, hs))
                 st = fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
         } else {
-            if (st == GCONV_OK) st = run_fwd(p.e, p.path, xs, w, bias, ys, hs);
+            if (st == GCONV_OK) st = run_fwd(p.e, p.path, xs, w, bias, ys, rest, hs);
             if (st == GCONV_OK) st = reorder(ys, y, s.N, s.K, (int64_t)s.Ho * s.Wo, hs);
         }
     }
@@ -509,11 +519,12 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
     if (p.native) {
         dw_nhwc_bwd_data(s, dy, w, dx, hs);
     } else if (!p.staged) {
-        st = run_bwd_data(p.e, p.path, dy, w, dx, hs);
+        st = run_bwd_data(p.e, p.path, dy, w, dx, (float*)workspace, hs);
     } else {
         char* base = (char*)workspace;
         float* dys = (float*)base;
         float* dxs = (float*)(base + stage_bytes(s.y_elems));
+        float* rest = (float*)(base + staging_bytes(s, GCONV_OP_BWD_DATA));
         const bool a16 = ((uintptr_t)dy & 15) == 0;
         if (p.path == GCONV_PATH_IGEMM && a16 && igemm_nhwc_io_supported(p.e, GCONV_OP_BWD_DATA)) {
             // The flat MFMA kernel reads dy and stores dx channels-last itself.
@@ -526,7 +537,7 @@ int gconv_bwd_data(const gconv_desc* d, const float* dy, const float* w, float* 
             if (!igemm_bwd_data_nhwc_out(p.e, dys, w, dx, hs))
                 st = fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
         } else {
-            if (st == GCONV_OK) st = run_bwd_data(p.e, p.path, dys, w, dxs, hs);
+            if (st == GCONV_OK) st = run_bwd_data(p.e, p.path, dys, w, dxs, rest, hs);
             if (st == GCONV_OK) st = reorder(dxs, dx, s.N, s.C, (int64_t)s.H * s.W, hs);
         }
     }

@@ -98,9 +98,12 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
 
 // ---- fully-connected mode (kernel == input): fp32-MFMA GEMMs ----------------
 bool fc_supported(const Shape& s);
-void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+// Forward and gradInput split their reduction when the output tiles alone
+// would leave part of the chip idle; the partials need fc_data_workspace().
+size_t fc_data_workspace(const Shape& s, int op);
+bool fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y, float* ws,
             hipStream_t st);
-void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);
+bool fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, float* ws, hipStream_t st);
 bool fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st);
 size_t fc_bwd_filter_workspace(const Shape& s);
 

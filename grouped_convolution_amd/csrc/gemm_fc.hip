@@ -25,6 +25,7 @@
 
 #include "device_util.h"
 #include "fastdiv.h"
+#include "gconv.h"
 #include "gconv_internal.h"
 
 namespace gconv {
@@ -253,6 +254,37 @@ __global__ void __launch_bounds__(256) gemm_split_reduce(const V* __restrict__ w
     }
 }
 
+// Sum of a few split partials with the forward pass's epilogue:
+// out[e] = act(bias[e % bias_n] + sum_s ws[s*E + e]), slices added in order
+// (bias may be NULL; V = f4 needs E and bias_n multiples of 4). One thread
+// per element (or float4): each partial is read once, coalesced.
+template <typename V>
+__global__ void __launch_bounds__(256) gemm_split_epilogue(const V* __restrict__ ws, V* __restrict__ out,
+                                                           int64_t E, int nsplit, const float* __restrict__ bias,
+                                                           int bias_n, int relu)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    V sum = ws[e];
+    for (int sl = 1; sl < nsplit; ++sl) sum += ws[(int64_t)sl * E + e];
+    if constexpr (sizeof(V) == sizeof(f4)) {
+        if (bias) {
+            const int c = (int)((e * 4) % bias_n);
+            sum += *(const f4*)(bias + c);
+        }
+        if (relu) {
+            sum.x = relu_if(sum.x, 1);
+            sum.y = relu_if(sum.y, 1);
+            sum.z = relu_if(sum.z, 1);
+            sum.w = relu_if(sum.w, 1);
+        }
+    } else {
+        if (bias) sum += bias[e % bias_n];
+        sum = relu_if(sum, relu);
+    }
+    out[e] = sum;
+}
+
 // Defaults that make the batch entries plain groups with one reduction slice.
 void plain(GemmArgs& a)
 {
@@ -305,36 +337,124 @@ bool fc_supported(const Shape& s)
            D < (1 << 30) && s.w_elems < (int64_t(1) << 28);
 }
 
-// y[n, g*Kg + k] = sum_d x[n, g*D + d] * w[g*Kg + k, d] + b
-void fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
+// Reduction slices for a GEMM whose output tiles alone spread unevenly over
+// the chip. With T tiles and n slices each CU works through about
+// ceil(T*n / CUs) units of 1/n of a tile, so a split pays when it evens out
+// the last round (fully-connected mode's forward: 13 x 32 = 416 tiles of
+// 128 x 128 on 256 CUs leave 96 CUs with one tile and 160 with two; three
+// slices make 1248 units, 4.875 per CU). It costs a pass that reads the n
+// partials of the E outputs and writes the result (the partials themselves
+// are written while the matrix cores are busy).
+// Each slice keeps at least 8 stages. The constants are MI355X's: 256 CUs,
+// about 0.48 TFLOP/s per CU on one 128 x 128 tile stream, about 4.5 TB/s for
+// the partials pass.
+static int balance_splits(int64_t tiles, int64_t R, int64_t E, int max_split)
+{
+    constexpr int64_t kCUs = 256;
+    constexpr double kTileRate = 0.48e12, kPassBw = 4.5e12, kLaunch = 4e-6;
+    const double t_tile = 2.0 * BM * BN * (double)R / kTileRate;
+    int best = 1;
+    double best_t = 0.0;
+    for (int n = 1; n <= max_split; ++n) {
+        if (n > 1 && R / n < 8 * BR) break;
+        const double rounds = (double)((tiles * n + kCUs - 1) / kCUs);
+        double t = rounds / n * t_tile;
+        if (n > 1) t += (double)(n + 1) * (double)E * 4.0 / kPassBw + kLaunch;  // the partials pass
+        if (n == 1 || t < 0.98 * best_t) {
+            best = n;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
+static void fc_data_split(const Shape& s, int op, int* nsplit, int* r_split)
+{
+    const int64_t D = (int64_t)s.Cg * s.kh * s.kw;
+    int64_t M = s.N, N, R, E;
+    if (op == GCONV_OP_FWD) { N = s.Kg; R = D; E = (int64_t)s.N * s.K; }
+    else { N = D; R = s.Kg; E = (int64_t)s.N * s.C * s.H * s.W; }
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN) * s.G;
+    const int n = balance_splits(tiles, R, E, 6);
+    int64_t rs = (R + n - 1) / n;
+    rs = (rs + BR - 1) / BR * BR;
+    *r_split = (int)rs;
+    *nsplit = (int)((R + rs - 1) / rs);
+}
+
+size_t fc_data_workspace(const Shape& s, int op)
+{
+    int nsplit, r_split;
+    fc_data_split(s, op, &nsplit, &r_split);
+    if (nsplit <= 1) return 0;
+    const int64_t E = op == GCONV_OP_FWD ? (int64_t)s.N * s.K : (int64_t)s.N * s.C * s.H * s.W;
+    return (size_t)nsplit * (size_t)E * 4;
+}
+
+static void split_epilogue(const float* ws, float* out, int64_t E, int nsplit, const float* bias,
+                           int bias_n, int relu, hipStream_t st)
+{
+    const bool v4 = (E & 3) == 0 && ((uintptr_t)out & 15) == 0 &&
+                    (!bias || ((bias_n & 3) == 0 && ((uintptr_t)bias & 15) == 0));
+    if (v4) {
+        const int64_t E4 = E / 4;
+        hipLaunchKernelGGL(gemm_split_epilogue<f4>, dim3((unsigned)((E4 + 255) / 256)), dim3(256), 0, st,
+                           (const f4*)ws, (f4*)out, E4, nsplit, bias, bias_n, relu);
+    } else {
+        hipLaunchKernelGGL(gemm_split_epilogue<float>, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, st,
+                           ws, out, E, nsplit, bias, bias_n, relu);
+    }
+}
+
+// y[n, g*Kg + k] = sum_d x[n, g*D + d] * w[g*Kg + k, d] + b. When the tiles
+// spread unevenly the reduction is split into slices whose partials go to the
+// workspace, and one pass adds them in slice order with the bias and the
+// activation.
+bool fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y, float* ws,
             hipStream_t st)
 {
     const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
+    int nsplit, r_split;
+    fc_data_split(s, GCONV_OP_FWD, &nsplit, &r_split);
+    if (nsplit > 1 && !ws) return false;
     GemmArgs a{};
-    a.A = x; a.B = w; a.bias = bias; a.C = y;
+    a.A = x; a.B = w; a.bias = nsplit > 1 ? nullptr : bias; a.C = nsplit > 1 ? ws : y;
     a.M = s.N; a.N = s.Kg; a.R = D; a.Z = s.G;
     plain(a);
     a.a_ld = Dt; a.b_ld = D; a.c_ld = s.K;
     a.a_gs = D; a.b_gs = (int64_t)s.Kg * D; a.c_gs = s.Kg; a.bias_gs = s.Kg;
-    a.relu = s.relu;
+    a.relu = nsplit > 1 ? 0 : s.relu;
     a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * Dt + D) * 4);
     a.b_bytes = (uint32_t)((int64_t)s.Kg * D * 4);
+    a.nsplit = nsplit;
+    a.r_split = r_split;
+    a.c_split = (int64_t)s.N * s.K;
     launch<true, true>(a, st);
+    if (nsplit > 1) split_epilogue(ws, y, (int64_t)s.N * s.K, nsplit, bias, s.K, s.relu, st);
+    return true;
 }
 
-// dx[n, g*D + d] = sum_k dy[n, g*Kg + k] * w[g*Kg + k, d]
-void fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+// dx[n, g*D + d] = sum_k dy[n, g*Kg + k] * w[g*Kg + k, d] (split like the forward pass)
+bool fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, float* ws, hipStream_t st)
 {
     const int D = s.Cg * s.kh * s.kw, Dt = s.C * s.H * s.W;
+    int nsplit, r_split;
+    fc_data_split(s, GCONV_OP_BWD_DATA, &nsplit, &r_split);
+    if (nsplit > 1 && !ws) return false;
     GemmArgs a{};
-    a.A = dy; a.B = w; a.bias = nullptr; a.C = dx;
+    a.A = dy; a.B = w; a.bias = nullptr; a.C = nsplit > 1 ? ws : dx;
     a.M = s.N; a.N = D; a.R = s.Kg; a.Z = s.G;
     plain(a);
     a.a_ld = s.K; a.b_ld = D; a.c_ld = Dt;
     a.a_gs = s.Kg; a.b_gs = (int64_t)s.Kg * D; a.c_gs = D; a.bias_gs = 0;
     a.a_bytes = (uint32_t)(((int64_t)(s.N - 1) * s.K + s.Kg) * 4);
     a.b_bytes = (uint32_t)((int64_t)s.Kg * D * 4);
+    a.nsplit = nsplit;
+    a.r_split = r_split;
+    a.c_split = (int64_t)s.N * Dt;
     launch<true, false>(a, st);
+    if (nsplit > 1) split_epilogue(ws, dx, (int64_t)s.N * Dt, nsplit, nullptr, 1, 0, st);
+    return true;
 }
 
 // Reduction slices of a gradWeight GEMM over R rows with `tiles` output tiles:
