@@ -42,6 +42,14 @@ __device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, 0, 0, 0);
 }
 
+// As load_lds64 with a wave-uniform byte offset `soff` added to every lane's
+// `byte_off` (an SGPR operand: advancing a stream of loads by a uniform step
+// costs no vector instruction). Lanes given kOOB still read 0.
+__device__ __forceinline__ void load_lds64s(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, byte_off, (int)soff, 0, 0);
+}
+
 // The 64 lanes load 16 bytes each into 256 consecutive LDS floats at `dst`
 // (lane i to dst + 4i; wave-uniform `dst`); out-of-range offsets write 0.
 __device__ __forceinline__ void load_lds256(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)

@@ -107,6 +107,43 @@ __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, float* dst
     }
 }
 
+// Per-lane byte offsets of the 16 load instructions of a stage at reduction
+// index r0 (the same lanes and LDS slots as load_stage); rows past `rows` get
+// kOOB. A later stage at r0 + t*BR adds the uniform t*BR*4 (RCONTIG) or
+// t*BR*ld*4 bytes as the instruction's scalar offset, so a stage that lies
+// wholly inside the reduction needs no per-lane arithmetic.
+template <bool RCONTIG>
+__device__ __forceinline__ void stage_offsets(uint32_t (&off)[16], int row0, int rows, int r0, int ld, int wave,
+                                              int lane)
+{
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int i = wave + 4 * k;
+        if constexpr (RCONTIG) {
+            const int row = 2 * i + (lane >> 5);
+            const int chunk = ((lane & 31) >> 2) ^ (row & 7);
+            const int r = 4 * chunk + (lane & 3);
+            off[k] = row0 + row < rows ? (uint32_t)((row0 + row) * ld + r0 + r) * 4u : kOOB;
+        } else {
+            const int r = i >> 1, h = i & 1;
+            const int row = h * 64 + lane;
+            off[k] = row0 + row < rows ? (uint32_t)((r0 + r) * ld + row0 + row) * 4u : kOOB;
+        }
+    }
+}
+
+template <bool RCONTIG>
+__device__ __forceinline__ void load_stage_fast(__amdgpu_buffer_rsrc_t rs, float* dst, const uint32_t (&off)[16],
+                                                uint32_t soff, int wave)
+{
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int i = wave + 4 * k;
+        if constexpr (RCONTIG) load_lds64s(rs, dst + i * 64, off[k], soff);
+        else load_lds64s(rs, dst + (i >> 1) * SROW + (i & 1) * 64, off[k], soff);
+    }
+}
+
 // Operand values of one 16-deep reduction group (4 MFMA steps) for fragment
 // rows row0..row0+15 of an LDS stage: v[s] feeds MFMA step s.
 template <bool RCONTIG>
@@ -154,9 +191,26 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
+    // Stages wholly inside the reduction (all but a ragged last one) load
+    // through precomputed lane offsets; the image-split reduction, whose
+    // offsets jump at image boundaries, and a ragged stage take the masked
+    // per-element path.
+    const int full = RIMG ? 0 : (r_end - r_begin) / BR;
+    uint32_t offa[16], offb[16];
+    if constexpr (!RIMG) {
+        stage_offsets<A_RC>(offa, m0, a.M, r_begin, a.a_ld, wave, lane);
+        stage_offsets<B_RC>(offb, n0, a.N, r_begin, a.b_ld, wave, lane);
+    }
+    const uint32_t step_a = A_RC ? BR * 4u : (uint32_t)(BR * a.a_ld) * 4u;
+    const uint32_t step_b = B_RC ? BR * 4u : (uint32_t)(BR * a.b_ld) * 4u;
     auto issue = [&](int stage, int b) {
         float* ta = lds + b * (TA + TB);
         float* tb = ta + TA;
+        if (!RIMG && stage < full) {
+            load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)stage * step_a, wave);
+            load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)stage * step_b, wave);
+            return;
+        }
         load_stage<A_RC, RIMG>(ra, ta, m0, a.M, r_begin + stage * BR, r_end, a.a_ld, wave, lane, &a, a.a_is);
         load_stage<B_RC, RIMG>(rb, tb, n0, a.N, r_begin + stage * BR, r_end, a.b_ld, wave, lane, &a, a.b_is);
     };
