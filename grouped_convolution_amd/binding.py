@@ -31,8 +31,8 @@ PATH_NAMES = {PATH_AUTO: "auto", PATH_DIRECT: "direct", PATH_SMALLGROUP: "smallg
 
 # Every symbol include/gconv.h declares.
 EXPORTS = ("gconv_output_dims", "gconv_workspace_size", "gconv_fwd", "gconv_fwd_ex", "gconv_bwd_data",
-           "gconv_bwd_filter", "gconv_bwd_bias", "gconv_select_path", "gconv_set_path_override",
-           "gconv_status_string", "gconv_last_error", "gconv_version")
+           "gconv_bwd_filter", "gconv_bwd_filter_static", "gconv_bwd_bias", "gconv_select_path",
+           "gconv_set_path_override", "gconv_status_string", "gconv_last_error", "gconv_version")
 
 
 class GconvError(RuntimeError):
@@ -70,6 +70,7 @@ def load(path: str = LIB_PATH):
         "gconv_fwd_ex": [D, P, P, P, I, P, P, S, P],
         "gconv_bwd_data": [D, P, P, P, P, S, P],
         "gconv_bwd_filter": [D, P, P, P, P, S, P],
+        "gconv_bwd_filter_static": [D, P, P, P, P],
         "gconv_bwd_bias": [D, P, P, P, S, P],
         "gconv_select_path": [D, I, ctypes.POINTER(ctypes.c_int)],
         "gconv_set_path_override": [I],

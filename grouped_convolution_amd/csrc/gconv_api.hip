@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "gconv.h"
@@ -388,6 +389,54 @@ int reorder(const float* src, float* dst, int64_t N, int64_t R, int64_t Cc, hipS
     return GCONV_OK;
 }
 
+// ---- the allocation-free gradWeight (gconv_bwd_filter_static) -----------------
+//
+// Device memory for what gconv_bwd_filter keeps in the caller's workspace
+// (split partials, channels-last copies). Every device the library runs on
+// holds its own copy of this array until the process ends. On the host the
+// array's name is only a stand-in: kernels get the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+}  // namespace
+}  // namespace gconv
+
+static __device__ __align__(256) float scratch[gconv::kScratchBytes / sizeof(float)];
+
+namespace gconv {
+namespace {
+
+// Device address of `scratch` on the device `stream` runs on, which must be
+// the current device.
+int scratch_address(hipStream_t stream, void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GCONV_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GCONV_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices - 1);
+    if (stream) {
+        int sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return fail(GCONV_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(GCONV_ERR_ARG, "the stream belongs to device %d but device %d is current", sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GCONV_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return GCONV_OK;
+}
+
 int epilogue()
 {
     const hipError_t e = hipGetLastError();
@@ -576,6 +625,20 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
         if (st == GCONV_OK) st = run_bwd_filter(p.e, p.path, xs, dys, dw, rest, hs);
     }
     return st != GCONV_OK ? st : epilogue();
+}
+
+int gconv_bwd_filter_static(const gconv_desc* d, const float* x, const float* dy, float* dw, void* stream)
+{
+    size_t need = 0;
+    int st = gconv_workspace_size(d, GCONV_OP_BWD_FILTER, &need);
+    if (st != GCONV_OK) return st;
+    if (need > kScratchBytes)
+        return fail(GCONV_ERR_WORKSPACE, "this gradWeight needs %zu bytes of scratch; the static scratch holds %zu",
+                    need, kScratchBytes);
+    void* ws = nullptr;
+    st = scratch_address((hipStream_t)stream, &ws);
+    if (st != GCONV_OK) return st;
+    return gconv_bwd_filter(d, x, dy, dw, ws, kScratchBytes, stream);
 }
 
 int gconv_bwd_bias(const gconv_desc* d, const float* dy, float* db, void* workspace,

@@ -199,6 +199,23 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gradWeight without a workspace argument and without allocating, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, results
+ * and errors as gconv_bwd_filter, whose kernels it runs; what that call keeps
+ * in the workspace (split partials, channels-last copies) goes to a static
+ * device array of 64 MiB instead, one per device, held until the process
+ * ends. A descriptor that needs more (gconv_workspace_size) returns
+ * GCONV_ERR_WORKSPACE before anything is enqueued. The stream must belong to
+ * the current device (GCONV_ERR_ARG otherwise); the array's device address is
+ * looked up on the first call on each device. Nothing in the array needs to
+ * start at zero: every call writes what it reads. All calls on one device
+ * share the array, so calls that overlap on one device (concurrent streams,
+ * or threads) race and give wrong results; serialise them.
+ */
+int gconv_bwd_filter_static(const gconv_desc* d, const float* x, const float* dy, float* dw, void* stream);
+
+/*
  * gradBias: db[k] = sum_{n,ho,wo} dy[n,k,ho,wo] (DLPrimitives Blog,
  * "Pointwise Broadcast Reduce": the sum of dy over dims 0, 2 and 3).
  * Only N, K, Ho, Wo and the layout of the descriptor matter. Overwrites db.
