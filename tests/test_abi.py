@@ -134,10 +134,11 @@ def test_null_and_workspace_errors():
     assert lib.gconv_fwd(None, fake, fake, None, fake, None, 0, None) == 1
     assert lib.gconv_fwd(ctypes.byref(desc), None, fake, None, fake, None, 0, None) == 1
     assert lib.gconv_bwd_data(ctypes.byref(desc), fake, None, fake, None, 0, None) == 1
-    # gradBias of small planes runs in one pass without a workspace; a 1x1
-    # output (dy is [N, K]) takes split partials in the workspace.
+    # gradBias of a few small planes runs on one workgroup per channel without
+    # a workspace; a 1x1 output over many images (dy is [N, K]) splits its rows
+    # over workgroups, with partials and arrival counters in the workspace.
     assert B.gconv_workspace_size(desc, B.OP_BWD_BIAS) == 0
-    desc = B.make_desc(2, 8, 3, 3, 8, 3, 3, groups=2)
+    desc = B.make_desc(64, 8, 3, 3, 8, 3, 3, groups=2)
     n = B.gconv_workspace_size(desc, B.OP_BWD_BIAS)
     assert n > 0
     assert lib.gconv_bwd_bias(ctypes.byref(desc), fake, fake, None, 0, None) == 4

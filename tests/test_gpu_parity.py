@@ -444,6 +444,40 @@ def test_bias_reduction_forms(shape):
     assert np.array_equal(G.gconv_bwd_bias(dev(dyi)).cpu().numpy().astype(np.float64), vali)
 
 
+@pytest.mark.parametrize("shape,layout", [
+    ((32, 64, 56, 56), "nchw"),     # planes split over 8 workgroups per channel
+    ((40, 6, 25, 25), "nchw"),      # planes of 625 floats (scalar loads), 3 slices per channel
+    ((1600, 4096, 1, 1), "nchw"),   # [N, K] rows, 4 column blocks x 124 row slices
+    ((3000, 1002, 1, 1), "nchw"),   # [N, K] rows, K not a multiple of 4 (one column per thread)
+    ((8, 64, 28, 28), "nhwc"),      # NHWC: [N*Ho*Wo, 64] narrow rows
+])
+def test_bias_split_slices(shape, layout):
+    """gradBias whose reduction groups are split over workgroups, with the
+    slices' partials in the workspace and added in order by a second kernel.
+    Whatever the workspace holds beforehand (random bits), and on a second call
+    with the same workspace, the result matches the oracle, and integer data
+    bit for bit."""
+    N, K, Ho, Wo = shape
+    nhwc = layout == "nhwc"
+    desc = G.make_desc(N, K, Ho, Wo, K, 1, 1, layout=layout)
+    nws = G.gconv_workspace_size(desc, G.OP_BWD_BIAS)
+    assert nws > 0, shape
+    gen = torch.Generator(device="cuda").manual_seed(shape[1])
+    ws = torch.randint(-2**31, 2**31 - 1, (nws // 4,), dtype=torch.int32, device="cuda",
+                       generator=gen).view(torch.float32)
+    for dist, seed in ((("normal", 1.0), 2500), (("int", -3, 3), 2600)):
+        dy = draw(dist, shape, seed + K)
+        val, mag = oracle.bwd_bias(dy)
+        dyd = dev(np.ascontiguousarray(dy.transpose(0, 2, 3, 1)) if nhwc else dy)
+        for call in range(2):
+            say("bias slices %s %s %s call %d" % (shape, layout, dist[0], call))
+            got = G.gconv_bwd_bias(dyd, workspace=ws, layout=layout).cpu().numpy()
+            if dist[0] == "int":
+                assert np.array_equal(got.astype(np.float64), val), (shape, call)
+            else:
+                check("bias %s call %d" % (shape, call), got, val, mag)
+
+
 def test_fc_1x1_on_1x1_is_linear():
     """A 1x1 convolution of a 1x1 input (the Linear(128, 32) case of the
     cudnn.torch issue) runs the GEMM path and matches the oracle."""
@@ -718,7 +752,7 @@ def test_deterministic_bitwise():
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("name", ["tiny_grouped", "resnext_32x4d", "dense3x3", "dense3x3_nhwc"])
+@pytest.mark.parametrize("name", ["tiny_grouped", "resnext_32x4d", "dense3x3", "dense3x3_nhwc", "fc_mode"])
 def test_hip_graph_replay(name):
     """The four ops of a step captured in one HIP graph (prepared plans, no
     allocation or memset inside) and replayed several times, with eager work
