@@ -268,10 +268,12 @@ def run_gpu(args, wl_name, evict, copy_gbs, headline=False):
         tm = st["median"] * 1e-3
         f = 0.0 if op == "bwd_bias" else flop
         ai = f / nbytes[op]
-        if op == "bwd_bias" or paths[op] in ("direct", "smallgroup"):
-            bound = "hbm" if ai < RIDGE else "alu"
+        # Below the ridge the op is bound by HBM whatever unit computes it;
+        # above it, by the matrix cores (MFMA families) or the vector ALUs.
+        if ai < RIDGE:
+            bound = "hbm"
         else:
-            bound = "mfma"
+            bound = "alu" if paths[op] == "direct" else "mfma"
         peak = {"hbm": PEAK_HBM, "alu": PEAK_VALU_F32, "mfma": PEAK_MFMA_F32}[bound]
         achieved = nbytes[op] / tm if bound == "hbm" else f / tm
         rec = {"ms": st["median"], "ms_min": st["min"], "ms_p90": st["p90"], "ms_mean": st["mean"],

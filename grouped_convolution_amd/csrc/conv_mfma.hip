@@ -277,13 +277,20 @@ struct ConvFlatArgs {
     int relu;                   // forward epilogue: max(v, 0)
     int out_nhwc;               // store the output channels-last, [N][Hout*Wout][Cout_tot]
     FastDiv div_P, div_Wout, div_plane, div_LW;
+    // Phase of a strided gradInput (PH instances): tap t = (i, j) of the
+    // KH x KW sub-filter is tap (t_i0 + i*t_si, t_j0 + j*t_sj) of the stored
+    // filter, whose rows hold t_kw taps; output pixel (ho, wo) is pixel
+    // (ho*o_sh + o_h0, wo*o_sw + o_w0) of the stored o_H x o_W planes.
+    int t_kw, t_i0, t_j0, t_si, t_sj;
+    int o_sh, o_sw, o_h0, o_w0, o_H, o_W;
 };
 
 // INH: the input is channels-last ([N][Hr][Wr][Cin_tot]); the LDS tile then
 // holds each pixel's 4 chunk channels together ([row][col][4]), filled by
 // 16-byte DMA (one pixel per lane), and a fragment's 16 pixels x 4 channels
 // read 64 consecutive floats.
-template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, int MINW, bool INH = false>
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, int MINW, bool INH = false,
+          bool PH = false>
 __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlatArgs a)
 {
     constexpr int T = KH * KW;
@@ -384,7 +391,14 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             const uint32_t base =
                 (r < a.Cin_g && wbase[m] >= 0) ? (uint32_t)(wbase[m] + r * a.w_sr) * 4u : kOOB;
 #pragma unroll
-            for (int t = 0; t < T; ++t) b[m][t] = load_f32(rw, base + (uint32_t)t * 4u);
+            for (int t = 0; t < T; ++t) {
+                if constexpr (PH) {
+                    const int tm = (a.t_i0 + (t / KW) * a.t_si) * a.t_kw + a.t_j0 + (t % KW) * a.t_sj;
+                    b[m][t] = load_f32(rw, base + (uint32_t)tm * 4u);
+                } else {
+                    b[m][t] = load_f32(rw, base + (uint32_t)t * 4u);
+                }
+            }
         }
     };
     // Taps in memory order (so the loads merge into 16-byte ones); the flipped
@@ -537,7 +551,25 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
                 v.z = relu_if(v.z, 1);
                 v.w = relu_if(v.w, 1);
             }
-            if (a.out_nhwc) {
+            if constexpr (PH) {
+                // A phase of a strided gradInput: output pixel (ho, wo) is
+                // pixel (ho*o_sh + o_h0, wo*o_sw + o_w0) of the stored planes.
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+                const size_t Preal = (size_t)a.o_H * a.o_W;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int qq = qb + u;
+                    if (qq < q1) {
+                        const int n = (int)fastdiv((uint32_t)qq, a.div_P);
+                        const int p = qq - n * a.P;
+                        const int ho = (int)fastdiv((uint32_t)p, a.div_Wout);
+                        const int wo = p - ho * a.Wout;
+                        const size_t pr = (size_t)(ho * a.o_sh + a.o_h0) * a.o_W + (size_t)(wo * a.o_sw + a.o_w0);
+                        if (a.out_nhwc) a.out[((size_t)n * Preal + pr) * a.Cout_tot + ch_off] = vv[u];
+                        else a.out[((size_t)n * a.Cout_tot + ch_off) * Preal + pr] = vv[u];
+                    }
+                }
+            } else if (a.out_nhwc) {
                 // Channels-last output: for each pixel the 16 lanes of a lane
                 // group write 16 consecutive channels (64 bytes).
                 const float vv[4] = {v.x, v.y, v.z, v.w};
@@ -631,6 +663,11 @@ struct Problem {
     int relu = 0;                        // forward epilogue
     int out_nhwc = 0;                    // channels-last output (flat kernel only)
     int in_nhwc = 0;                     // channels-last input (flat kernel only; Cin_g % 4 == 0)
+    // One phase of a strided gradInput (flat kernel only): the sub-filter's
+    // taps within the stored filter and the output pixels within dx.
+    bool phase = false;
+    int t_kw = 0, t_i0 = 0, t_j0 = 0, t_si = 1, t_sj = 1;
+    int o_sh = 1, o_sw = 1, o_h0 = 0, o_w0 = 0, o_H = 0, o_W = 0;
 };
 
 int choose_cc(const Problem& p) { return (p.kh * p.kw >= 16) ? 4 : 8; }
@@ -748,6 +785,8 @@ Problem bwd_data_problem(const Shape& s, const float* dy, const float* w, float*
 
 struct FlatInst {
     int T, MO, WO, WPX, MP, NSX;
+    int KH, KW;
+    bool PH;  // a phase of a strided gradInput (sub-filter taps, strided output)
 };
 #ifndef GCONV_FLAT_MP3
 #define GCONV_FLAT_MP3 5
@@ -768,9 +807,19 @@ struct FlatInst {
     X(25, 5, 1, 4, 1, 4, 8) X(25, 5, 2, 4, 1, 4, 8) X(25, 5, 1, 3, 1, 4, 8)                \
     X(25, 5, 1, 2, 2, 4, 8) X(25, 5, 1, 1, 4, 4, 12)                                       \
     X(9, 3, 2, 4, 1, 4, 16) X(9, 3, 1, 1, 4, 4, 24) X(25, 5, 1, 3, 1, 4, 12)
-#define GCONV_FLAT_ENTRY(t, k, mo, wo, wpx, mp, nsx) {t, mo, wo, wpx, mp, nsx},
-constexpr FlatInst kFlatInsts[] = {GCONV_FLAT_INSTS(GCONV_FLAT_ENTRY)};
+// Phase instances of a strided gradInput (always flipped): the sub-filters of
+// a 3x3 filter at stride 2 (2x2, 2x1, 1x2, 1x1), and of other filters up to
+// twice the stride, over the same wave layouts.
+#define GCONV_PHASE_SHAPES(X, mo, wo, wpx, mp, nsx) \
+    X(2, 2, mo, wo, wpx, mp, nsx) X(2, 1, mo, wo, wpx, mp, nsx) X(1, 2, mo, wo, wpx, mp, nsx) X(1, 1, mo, wo, wpx, mp, nsx)
+#define GCONV_PHASE_INSTS(X)                                                     \
+    GCONV_PHASE_SHAPES(X, 1, 1, 4, 4, 12) GCONV_PHASE_SHAPES(X, 1, 2, 2, 4, 8)    \
+    GCONV_PHASE_SHAPES(X, 1, 4, 1, 5, 8) GCONV_PHASE_SHAPES(X, 2, 4, 1, 4, 12)
+#define GCONV_FLAT_ENTRY(t, k, mo, wo, wpx, mp, nsx) {t, mo, wo, wpx, mp, nsx, k, k, false},
+#define GCONV_PHASE_ENTRY(kh, kw, mo, wo, wpx, mp, nsx) {kh * kw, mo, wo, wpx, mp, nsx, kh, kw, true},
+constexpr FlatInst kFlatInsts[] = {GCONV_FLAT_INSTS(GCONV_FLAT_ENTRY) GCONV_PHASE_INSTS(GCONV_PHASE_ENTRY)};
 #undef GCONV_FLAT_ENTRY
+#undef GCONV_PHASE_ENTRY
 
 struct FlatPlan {
     FlatInst inst;
@@ -781,15 +830,19 @@ struct FlatPlan {
 
 bool flat_plan(const Problem& p, FlatPlan& fp)
 {
-    const int T = p.kh * p.kw;
-    if (!((p.kh == 3 && p.kw == 3) || (p.kh == 5 && p.kw == 5))) return false;
+    if (p.phase) {
+        if (!(p.kh >= 1 && p.kh <= 2 && p.kw >= 1 && p.kw <= 2 && p.flip)) return false;
+    } else if (!((p.kh == 3 && p.kw == 3) || (p.kh == 5 && p.kw == 5))) {
+        return false;
+    }
     const int nfrag = (p.Cout_g + 15) / 16;
     const int mo = nfrag > 4 ? 2 : 1;
-    const int wo = nfrag > 4 ? 4 : nfrag;  // waves across output channels
+    // waves across output channels (phase instances: 1, 2 or 4)
+    const int wo = nfrag > 4 ? 4 : (p.phase && nfrag == 3) ? 4 : nfrag;
     const FlatInst* inst = nullptr;
     int64_t plane = 0, nseg = 0, LW = 0, P = (int64_t)p.Hout * p.Wout;
     for (const FlatInst& fi : kFlatInsts) {
-        if (!(fi.T == T && fi.MO == mo && fi.WO == wo)) continue;
+        if (!(fi.KH == p.kh && fi.KW == p.kw && fi.PH == p.phase && fi.MO == mo && fi.WO == wo)) continue;
         const int NWi = fi.WO * fi.WPX;
         const int BPXi = fi.WPX * fi.MP * 16;
         if (P < BPXi) continue;  // a tile must span at most two images
@@ -833,12 +886,27 @@ bool flat_plan(const Problem& p, FlatPlan& fp)
     return true;
 }
 
-template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, bool INH>
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, bool INH, bool PH = false>
 void launch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     constexpr int MINW = (KH * KW <= 9) ? 4 : 2;
-    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW, INH>;
+    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW, INH, PH>;
     hipLaunchKernelGGL(kern, dim3(fp.blocks), dim3(64 * WO * WPX), fp.lds_bytes, st, a);
+}
+
+template <bool INH>
+bool dispatch_phase(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
+{
+    const FlatInst& i = fp.inst;
+#define GCONV_PHASE_CASE(kh, kw, mo, wo, wpx, mp, nsx)                                          \
+    if (i.PH && i.KH == kh && i.KW == kw && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && \
+        i.NSX == nsx) {                                                                         \
+        launch_flat<kh, kw, mp, mo, wo, wpx, nsx, true, INH, true>(a, fp, st);                  \
+        return true;                                                                           \
+    }
+    GCONV_PHASE_INSTS(GCONV_PHASE_CASE)
+#undef GCONV_PHASE_CASE
+    return false;
 }
 
 template <bool FLIP, bool INH>
@@ -846,7 +914,7 @@ bool dispatch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     const FlatInst& i = fp.inst;
 #define GCONV_FLAT_CASE(t, k, mo, wo, wpx, mp, nsx)                                     \
-    if (i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
+    if (!i.PH && i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
         launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP, INH>(a, fp, st);                  \
         return true;                                                                   \
     }
@@ -879,6 +947,9 @@ bool run_flat(const Problem& p, hipStream_t st)
     a.div_Wout = make_fastdiv((uint32_t)p.Wout);
     a.div_plane = make_fastdiv((uint32_t)fp.plane);
     a.div_LW = make_fastdiv((uint32_t)fp.LW);
+    a.t_kw = p.t_kw; a.t_i0 = p.t_i0; a.t_j0 = p.t_j0; a.t_si = p.t_si; a.t_sj = p.t_sj;
+    a.o_sh = p.o_sh; a.o_sw = p.o_sw; a.o_h0 = p.o_h0; a.o_w0 = p.o_w0; a.o_H = p.o_H; a.o_W = p.o_W;
+    if (p.phase) return p.in_nhwc ? dispatch_phase<true>(a, fp, st) : dispatch_phase<false>(a, fp, st);
     if (p.in_nhwc) return p.flip ? dispatch_flat<true, true>(a, fp, st) : dispatch_flat<false, true>(a, fp, st);
     return p.flip ? dispatch_flat<true, false>(a, fp, st) : dispatch_flat<false, false>(a, fp, st);
 }
@@ -894,6 +965,94 @@ bool use_flat(const Problem& p)
 #endif
 }
 
+// ---- strided gradInput by phases ------------------------------------------------
+//
+// dx[h][w] sums w[k][c][i][j] * dy[k][(h + ph - i)/sh][(w + pw - j)/sw] over the
+// taps whose quotients are exact. With h + ph = sh*a + u (0 <= u < sh) only
+// the taps i = u + sh*i' qualify, and they read dy row a - i'; likewise for
+// columns. So the dx pixels of phase (u, v) are a unit-stride correlation of
+// the stored dy with the sub-filter w[u + sh*i'][v + sw*j'] (reversed, padding
+// Ti - 1 rows above the phase's first row a_min), written to every sh-th row
+// and sw-th column of dx. The sh*sw phases together do the strided layer's
+// real work, where the virtually upsampled dy costs sh*sw times that in
+// products with zeros.
+struct PhaseSet {
+    int n = 0;
+    Problem ph[16];
+};
+
+// The phases of a strided gradInput the flat kernel can run (3x3 and other
+// filters up to twice the stride, unit dilation); false if any cannot.
+bool phase_problems(const Shape& s, const float* dy, const float* w, float* dx, PhaseSet* set)
+{
+    if (!(s.sh > 1 || s.sw > 1) || s.dh != 1 || s.dw != 1) return false;
+    if (s.kh < s.sh || s.kw < s.sw || s.kh > 2 * s.sh || s.kw > 2 * s.sw || s.sh * s.sw > 16) return false;
+    const int T = s.kh * s.kw;
+    set->n = 0;
+    for (int u = 0; u < s.sh; ++u)
+        for (int v = 0; v < s.sw; ++v) {
+            const int Ti = (s.kh - u + s.sh - 1) / s.sh, Tj = (s.kw - v + s.sw - 1) / s.sw;
+            const int xu = s.ph - u, xv = s.pw - v;
+            const int a_min = xu <= 0 ? 0 : (xu + s.sh - 1) / s.sh;
+            const int b_min = xv <= 0 ? 0 : (xv + s.sw - 1) / s.sw;
+            const int ru = s.H - 1 + s.ph - u, rv = s.W - 1 + s.pw - v;
+            if (ru < 0 || rv < 0) continue;             // no dx pixel in this phase
+            const int Ha = ru / s.sh - a_min + 1, Wb = rv / s.sw - b_min + 1;
+            if (Ha <= 0 || Wb <= 0) continue;
+            Problem p;
+            p.in = dy; p.wgt = w; p.bias = nullptr; p.out = dx;
+            p.N = s.N; p.G = s.G;
+            p.Cin_tot = s.K; p.Cin_g = s.Kg; p.Hin = s.Ho; p.Win = s.Wo;
+            p.Hr = s.Ho; p.Wr = s.Wo;
+            p.Cout_tot = s.C; p.Cout_g = s.Cg; p.Hout = Ha; p.Wout = Wb;
+            p.kh = Ti; p.kw = Tj; p.sh = 1; p.sw = 1; p.dh = 1; p.dw = 1;
+            p.ph = Ti - 1 - a_min; p.pw = Tj - 1 - b_min;
+            p.w_so = T; p.w_sr = s.Cg * T; p.w_gstride = s.Kg * s.Cg * T;
+            p.flip = true;
+            p.phase = true;
+            p.t_kw = s.kw; p.t_i0 = u; p.t_j0 = v; p.t_si = s.sh; p.t_sj = s.sw;
+            p.o_sh = s.sh; p.o_sw = s.sw;
+            p.o_h0 = s.sh * a_min + u - s.ph; p.o_w0 = s.sw * b_min + v - s.pw;
+            p.o_H = s.H; p.o_W = s.W;
+            if (!use_flat(p)) return false;
+            set->ph[set->n++] = p;
+        }
+    return set->n > 0;
+}
+
+bool run_phases(PhaseSet& set, bool in_nhwc, bool out_nhwc, hipStream_t st)
+{
+    for (int i = 0; i < set.n; ++i) {
+        set.ph[i].in_nhwc = in_nhwc;
+        set.ph[i].out_nhwc = out_nhwc;
+        if (!run_flat(set.ph[i], st)) return false;
+    }
+    return true;
+}
+
+bool phases_ok(const Shape& s, bool in_nhwc)
+{
+#ifdef GCONV_NO_PHASES
+    (void)s; (void)in_nhwc;
+    return false;
+#else
+    // Each phase is its own launch over a quarter (at stride 2) of the output
+    // pixels: where that leaves fewer workgroups than CUs, the single launch
+    // over the virtually upsampled dy is faster (a 512 -> 256-channel 28 x 28
+    // layer: 341 against 450 us), so phases are taken only when every phase
+    // launch fills the chip (a 64-channel 112 x 112 layer: 3010 -> 177 us; 128
+    // channels at 56 x 56: 295 -> 205 us).
+    PhaseSet set;
+    if (!phase_problems(s, nullptr, nullptr, nullptr, &set)) return false;
+    for (int i = 0; i < set.n; ++i) {
+        set.ph[i].in_nhwc = in_nhwc;
+        FlatPlan fp;
+        if (!flat_plan(set.ph[i], fp) || fp.blocks < 256) return false;
+    }
+    return true;
+#endif
+}
+
 }  // namespace
 
 bool igemm_fwd_supported(const Shape& s)
@@ -904,6 +1063,7 @@ bool igemm_fwd_supported(const Shape& s)
 
 bool igemm_bwd_data_supported(const Shape& s)
 {
+    if (phases_ok(s, false)) return true;
     const Problem p = bwd_data_problem(s, nullptr, nullptr, nullptr);
     if (p.uh != 1 || p.uw != 1) return use_flat(p);  // only the flat kernel upsamples
     return use_flat(p) || problem_supported(p);
@@ -918,6 +1078,8 @@ bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias
 
 bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
+    PhaseSet set;
+    if (phases_ok(s, false) && phase_problems(s, dy, w, dx, &set)) return run_phases(set, false, false, st);
     const Problem p = bwd_data_problem(s, dy, w, dx);
     if (use_flat(p)) return run_flat(p, st);
     if (p.uh != 1 || p.uw != 1) return false;
@@ -930,7 +1092,8 @@ bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, 
 bool igemm_nhwc_out_supported(const Shape& s, int op)
 {
     if (op == GCONV_OP_FWD) return use_flat(fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
-    if (op == GCONV_OP_BWD_DATA) return use_flat(bwd_data_problem(s, nullptr, nullptr, nullptr));
+    if (op == GCONV_OP_BWD_DATA)
+        return phases_ok(s, false) || use_flat(bwd_data_problem(s, nullptr, nullptr, nullptr));
     return false;
 }
 
@@ -945,6 +1108,8 @@ bool igemm_fwd_nhwc_out(const Shape& s, const float* x, const float* w, const fl
 
 bool igemm_bwd_data_nhwc_out(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
+    PhaseSet set;
+    if (phases_ok(s, false) && phase_problems(s, dy, w, dx, &set)) return run_phases(set, false, true, st);
     Problem p = bwd_data_problem(s, dy, w, dx);
     if (!use_flat(p)) return false;
     p.out_nhwc = 1;
@@ -964,7 +1129,8 @@ static Problem nhwc_io(Problem p)
 bool igemm_nhwc_io_supported(const Shape& s, int op)
 {
     if (op == GCONV_OP_FWD) return use_flat(nhwc_io(fwd_problem(s, nullptr, nullptr, nullptr, nullptr)));
-    if (op == GCONV_OP_BWD_DATA) return use_flat(nhwc_io(bwd_data_problem(s, nullptr, nullptr, nullptr)));
+    if (op == GCONV_OP_BWD_DATA)
+        return phases_ok(s, true) || use_flat(nhwc_io(bwd_data_problem(s, nullptr, nullptr, nullptr)));
     return false;
 }
 
@@ -976,6 +1142,8 @@ bool igemm_fwd_nhwc_io(const Shape& s, const float* x, const float* w, const flo
 
 bool igemm_bwd_data_nhwc_io(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
+    PhaseSet set;
+    if (phases_ok(s, true) && phase_problems(s, dy, w, dx, &set)) return run_phases(set, true, true, st);
     const Problem p = nhwc_io(bwd_data_problem(s, dy, w, dx));
     return use_flat(p) && run_flat(p, st);
 }

@@ -35,6 +35,11 @@ measure or motivate:
                  padding, which puts the one padding row and column at the
                  end only (DLPrimitives Blog, "TensorFlow"): padding given as
                  (top, bottom, left, right) = (0, 1, 0, 1).
+  resnext_32x4d_s2
+                 the stride-2 grouped 3x3 that opens a later stage of
+                 resnext50_32x4d (DLPrimitives Blog validates the network):
+                 256 channels in 32 groups of 8, 56x56 -> 28x28, pad 1, no
+                 bias (the strided-path "next" row).
   dense3x3_nhwc, resnext_1x1_nhwc, mobilenet_dw_nhwc
                  dense3x3, resnext_1x1 and mobilenet_dw with x, dx, y and dy stored
                  channels-last, the layout the DLPrimitives Blog measures
@@ -98,6 +103,9 @@ WORKLOADS = {
     "mobilenet_dw_s2_same": Workload(
         "mobilenet_dw_s2_same", 8, (64, 144, 56, 56), (144, 1, 3, 3), (64, 144, 28, 28), 144, 2,
         (0, 1, 0, 1), 1, ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 9.0))), None),
+    "resnext_32x4d_s2": Workload(
+        "resnext_32x4d_s2", 9, (64, 256, 56, 56), (256, 8, 3, 3), (64, 256, 28, 28), 32, 2, 1, 1,
+        ("normal", 1.0), ("normal", float(np.sqrt(2.0 / 72.0))), None),
     # The same tensors as dense3x3, resnext_1x1 and mobilenet_dw (same seeds), stored channels-last.
     "dense3x3_nhwc": Workload(
         "dense3x3_nhwc", 2, (32, 64, 56, 56), (64, 64, 3, 3), (32, 64, 56, 56), 1, 1, 1, 1,
@@ -110,8 +118,8 @@ WORKLOADS = {
         ("relu_normal", 1.0), ("normal", float(np.sqrt(2.0 / 256.0))), None, layout="nhwc"),
 }
 WORKLOAD_ORDER = ["tiny_grouped", "dense3x3", "alexnet_conv2", "resnext_32x4d", "fc_mode", "resnext_1x1",
-                  "mobilenet_dw", "mobilenet_dw_s2_same", "dense3x3_nhwc", "resnext_1x1_nhwc",
-                  "mobilenet_dw_nhwc"]
+                  "mobilenet_dw", "mobilenet_dw_s2_same", "resnext_32x4d_s2", "dense3x3_nhwc",
+                  "resnext_1x1_nhwc", "mobilenet_dw_nhwc"]
 
 
 def draw(dist, shape, seed) -> np.ndarray:

@@ -400,6 +400,97 @@ ASYM_CASES = [
 ]
 
 
+# Strided gradInput on the MFMA path. By phases, every (row, column) phase of
+# dx is a unit-stride correlation of the stored dy with a sub-filter of the taps
+# that reach it (3x3 at stride 2: 2x2, 2x1, 1x2 and 1x1).
+PHASE_CASES = [
+    dict(N=2, C=64, K=64, H=40, W=36, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),    # 8 per group
+    dict(N=2, C=32, K=48, H=35, W=41, kh=3, kw=3, sh=2, sw=2, ph=1, pw=0, dh=1, dw=1, G=1),    # odd sizes
+    dict(N=3, C=128, K=64, H=34, W=34, kh=3, kw=3, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=2),   # 64 dx channels
+    dict(N=1, C=256, K=32, H=36, W=38, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),   # 256 dx channels
+    dict(N=2, C=32, K=32, H=48, W=47, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=2),    # stride 3: 9 1x1 phases
+    dict(N=2, C=48, K=32, H=40, W=40, kh=4, kw=4, sh=2, sw=2, ph=1, pw=2, dh=1, dw=1, G=1),    # 4x4: four 2x2 phases
+    dict(N=2, C=32, K=32, H=40, W=36, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=2),    # 2x2: four 1x1 phases
+    dict(N=2, C=64, K=64, H=40, W=40, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1, G=8),  # "same"
+]
+
+
+# Shapes whose every phase launch has at least 256 workgroups, so the library
+# takes the phases (8 input channels per group: 256 output pixels per workgroup,
+# 8 groups; 32: 128 pixels, one group):
+PHASE_LARGE = [
+    dict(N=8, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 4 x 32x32 x 8 / 256
+    dict(N=9, C=64, K=64, H=65, W=63, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # ragged phases
+    dict(N=8, C=32, K=48, H=128, W=128, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),  # 8 x 64x64 / 128
+    dict(N=8, C=64, K=64, H=96, W=96, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=8),   # 9 1x1 phases
+    dict(N=8, C=64, K=64, H=64, W=64, kh=4, kw=4, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 2x2 sub-filters
+    dict(N=8, C=128, K=128, H=64, W=64, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=8),  # 1x1 sub-filters
+    dict(N=8, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1, G=8),  # "same"
+]
+
+
+@pytest.mark.parametrize("case", range(len(PHASE_LARGE)))
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+def test_strided_gradinput_phases_sampled(case, layout):
+    """Strided gradInput by phases at sizes where the library takes them, against
+    the oracle on 4000 sampled outputs: normal data to the tolerance, integer
+    data bit for bit."""
+    d = PHASE_LARGE[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout=layout, **kw)
+    assert G.PATH_NAMES[G.gconv_select_path(desc, G.OP_BWD_DATA)] == "igemm", d
+    nhwc = layout == "nhwc"
+    to = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1))) if nhwc else (lambda a: a)
+    Ho, Wo = G.gconv_output_dims(desc)
+    ws = G.gconv_workspace_size(desc, G.OP_BWD_DATA)
+    for dist, seed in ((("normal", 1.0), 2900), (("int", -3, 3), 2950)):
+        w = draw(dist, (d["K"], d["C"] // d["G"], d["kh"], d["kw"]), seed + case)
+        dy = draw(dist, (d["N"], d["K"], Ho, Wo), seed + 20 + case)
+        say("phases sampled %s %s %s" % (layout, d, dist[0]))
+        got = G.gconv_bwd_data(dev(to(dy)), dev(w), to(np.empty((d["N"], d["C"], d["H"], d["W"]), np.float32)).shape,
+                               layout=layout, workspace=torch.empty(max(ws // 4, 1), device="cuda"), **kw)
+        if nhwc:
+            got = got.permute(0, 3, 1, 2).contiguous()
+        idx = sample_indices(d["N"] * d["C"] * d["H"] * d["W"], 4000, seed + case)
+        g = gather(got, idx)
+        val, mag = oracle.bwd_data(dy, w, (d["N"], d["C"], d["H"], d["W"]), idx=idx, **kw)
+        if dist[0] == "int":
+            assert np.array_equal(g.astype(np.float64), val), d
+        else:
+            check("phases sampled %s" % d, g, val, mag)
+
+
+@pytest.mark.parametrize("case", range(len(PHASE_CASES)))
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+def test_strided_gradinput_phases(case, layout):
+    """Strided gradInput against the oracle at sizes where the phases' launches
+    would be small (the MFMA path then reads dy virtually upsampled; filters it
+    has no upsampled form for go to the direct kernels): normal data to the
+    tolerance, integer data bit for bit."""
+    d = PHASE_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout=layout, **kw)
+    nhwc = layout == "nhwc"
+    to = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1))) if nhwc else (lambda a: a)
+    for dist, seed in ((("normal", 1.0), 2700), (("int", -3, 3), 2800)):
+        x, w, _ = tensors(d, seed + case, dist=dist, bias=False)
+        Ho, Wo = G.gconv_output_dims(desc)
+        dy = draw(dist, (d["N"], d["K"], Ho, Wo), seed + 50 + case)
+        say("phases %s %s %s" % (layout, d, dist[0]))
+        ws = G.gconv_workspace_size(desc, G.OP_BWD_DATA)
+        got = G.gconv_bwd_data(dev(to(dy)), dev(w), to(x).shape, layout=layout,
+                               workspace=torch.empty(max(ws // 4, 1), device="cuda"), **kw)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        if nhwc:
+            got = got.transpose(0, 3, 1, 2)
+        val, mag = oracle.bwd_data(dy, w, x.shape, **kw)
+        if dist[0] == "int":
+            assert np.array_equal(got.astype(np.float64), val), d
+        else:
+            check("phases %s" % d, got, val, mag)
+
+
 @pytest.mark.parametrize("case", range(len(ASYM_CASES)))
 def test_asymmetric_padding_cases(case):
     """Asymmetric padding on the dispatcher's own choice of family (asserted):
@@ -516,7 +607,7 @@ def test_ragged_shapes_span_several_tiles():
 
 REDUCED_BATCH = {"tiny_grouped": 2, "dense3x3": 2, "alexnet_conv2": 2, "resnext_32x4d": 3,
                  "fc_mode": 24, "resnext_1x1": 2, "mobilenet_dw": 2, "mobilenet_dw_s2_same": 2,
-                 "dense3x3_nhwc": 2, "resnext_1x1_nhwc": 2, "mobilenet_dw_nhwc": 2}
+                 "resnext_32x4d_s2": 2, "dense3x3_nhwc": 2, "resnext_1x1_nhwc": 2, "mobilenet_dw_nhwc": 2}
 
 
 def wl_kwargs(wl):
