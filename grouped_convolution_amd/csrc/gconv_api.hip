@@ -287,7 +287,12 @@ struct Prep {
 size_t op_workspace(const Shape& s, const Shape& e, int op, int path, bool staged, bool native)
 {
     if (native) return op == GCONV_OP_BWD_FILTER ? dw_nhwc_wgrad_workspace(s) : 0;
-    return workspace_for(e, op, path) + (staged ? staging_bytes(s, op) : 0);
+    size_t ws = workspace_for(e, op, path);
+    // The MFMA gradWeight reads channels-last tensors in place where they are
+    // aligned (its partials only); the size covers the reordering route too.
+    if (staged && op == GCONV_OP_BWD_FILTER && path == GCONV_PATH_IGEMM && igemm_bwd_filter_nhwc_supported(e))
+        ws = std::max(ws, igemm_bwd_filter_nhwc_workspace(e));
+    return ws + (staged ? staging_bytes(s, op) : 0);
 }
 
 int prologue(const gconv_desc* d, int op, Prep* p, void* ws, size_t ws_bytes)
@@ -615,6 +620,11 @@ int gconv_bwd_filter(const gconv_desc* d, const float* x, const float* dy, float
             st = fail(GCONV_ERR_UNSUPPORTED, "no channels-last depthwise gradWeight plan for this shape");
     } else if (!p.staged) {
         st = run_bwd_filter(p.e, p.path, x, dy, dw, (float*)workspace, hs);
+    } else if (p.path == GCONV_PATH_IGEMM && ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 15) == 0 &&
+               igemm_bwd_filter_nhwc_supported(p.e)) {
+        // The MFMA gradWeight reads x and dy channels-last itself.
+        if (!igemm_bwd_filter_nhwc(p.e, x, dy, dw, (float*)workspace, hs))
+            st = fail(GCONV_ERR_UNSUPPORTED, "no MFMA kernel instance for this shape");
     } else {
         char* base = (char*)workspace;
         float* xs = (float*)base;

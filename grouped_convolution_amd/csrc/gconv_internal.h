@@ -82,6 +82,12 @@ bool igemm_bwd_filter_supported(const Shape& s);
 size_t igemm_bwd_filter_workspace(const Shape& s);
 bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                       hipStream_t st);
+// The same with channels-last x [N][H][W][C] and dy [N][Ho][Wo][K] read in
+// place (s: the layer's NCHW shape; whole channel quads per group, 16-byte
+// aligned tensors, else false and nothing launched).
+bool igemm_bwd_filter_nhwc_supported(const Shape& s);
+size_t igemm_bwd_filter_nhwc_workspace(const Shape& s);
+bool igemm_bwd_filter_nhwc(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st);
 
 // ---- few channels per group: v_mfma_f32_4x4x1 kernels (HBM-bound shapes) ------
 bool smallgroup_fwd_supported(const Shape& s);

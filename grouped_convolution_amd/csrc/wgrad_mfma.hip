@@ -50,7 +50,207 @@ struct WgradArgs {
     FastDiv div_LW, div_WoP, div_cpi;
 };
 
+// Channels-last tiles (INH): x is [N][H][W][C] and dy [N][Ho][Wo][K]. The LDS
+// tile of x holds one plane per quad of 4 channels, [pixel][4] (XS floats
+// apart, == 8 mod 32), and likewise dy (DS apart); one 16-byte DMA lane brings
+// a pixel's quad, so a 64-lane instruction fills 64 pixels of one quad plane
+// (nsx, nsd: such segments per quad plane). A half-wave's operand reads (16
+// channels as 4 quads x 4, at 2 pixels) then fall in 32 distinct banks.
+
 template <int KH, int KW, int WC, int WK, int R, int NH>
+__device__ __forceinline__ void wgrad_nhwc_body(const WgradArgs& a, int kt, int ct, int g, int s, int ch_begin,
+                                                int ch_end, int wave, int lane)
+{
+    constexpr int T = KH * KW;
+    constexpr int CT = 16 * WC;
+    constexpr int KT = 16 * WK * (4 / WC);
+    constexpr int NW = 4 * NH;
+    constexpr int CQ = CT / 4, KQ = KT / 4;  // channel quads of the two tiles
+    extern __shared__ float lds[];
+    const int buf_floats = CQ * a.XS + KQ * a.DS;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int wq = wave & 3, h = wave >> 2;
+    const int wc = wq % WC, wk = wq / WC;
+    const int c0 = ct * CT, k0 = kt * KT;
+    const int cq_ok = min(CQ, (a.Cg - c0) / 4), kq_ok = min(KQ, (a.Kg - k0) / 4);  // quads inside the group
+
+    // Per-lane pixel parts of the loads: segment sg covers tile pixels
+    // 64*sg .. 64*sg + 63 (x: row-major LR x LW; dy: R x WoP).
+    int xrow[kMaxSegX], xpix[kMaxSegX];
+    bool xok[kMaxSegX];
+#pragma unroll
+    for (int sg = 0; sg < kMaxSegX; ++sg) {
+        const int e = sg * 64 + lane;
+        const int r = (int)fastdiv((uint32_t)e, a.div_LW);
+        const int w = e - r * a.LW - a.pw;
+        xrow[sg] = r;
+        xpix[sg] = r * a.W + w;
+        xok[sg] = sg < a.nsx && e < a.LR * a.LW && (unsigned)w < (unsigned)a.W;
+    }
+    int drow[kMaxSegD], dpix[kMaxSegD];
+    bool dok[kMaxSegD];
+#pragma unroll
+    for (int sg = 0; sg < kMaxSegD; ++sg) {
+        const int e = sg * 64 + lane;
+        const int r = (int)fastdiv((uint32_t)e, a.div_WoP);
+        const int col = e - r * a.WoP;
+        drow[sg] = r;
+        dpix[sg] = r * a.Wo + col;
+        dok[sg] = sg < a.nsd && e < R * a.WoP && col < a.Wo;
+    }
+    const uint32_t ximg = (uint32_t)a.H * a.W * a.C * 4u, dimg = (uint32_t)a.Ho * a.Wo * a.K * 4u;
+
+    // Chunk ch into buffer b: instruction i of the x tile is quad i % CQ,
+    // segment i / CQ; this wave takes i = wave, wave + NW, ... (likewise dy).
+    auto issue = [&](int ch, int b) {
+        float* xs = lds + b * buf_floats;
+        float* ds = xs + CQ * a.XS;
+        const int n = (int)fastdiv((uint32_t)ch, a.div_cpi);
+        const int ho0 = (ch - n * a.chunks_per_image) * R;
+        const float* xg = a.x + (size_t)n * a.H * a.W * a.C + (size_t)g * a.Cg + c0;
+        const float* dyg = a.dy + (size_t)n * a.Ho * a.Wo * a.K + (size_t)g * a.Kg + k0;
+        // (the resources end at the image's last pixel: quads of a pixel past
+        // the group's channels are masked below, never read)
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, ximg - (uint32_t)(g * a.Cg + c0) * 4u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, dimg - (uint32_t)(g * a.Kg + k0) * 4u);
+        const int hb = ho0 * a.sh - a.ph;
+        const int row_lo = -hb, row_hi = a.H - hb;
+        const int drow_hi = a.Ho - ho0;
+        const int xbase = hb * a.W;  // pixels
+        const int dbase = ho0 * a.Wo;
+        for (int i = wave; i < CQ * a.nsx; i += NW) {
+            const int cq = i % CQ, sg = i / CQ;
+            uint32_t off = kOOB;
+#pragma unroll
+            for (int u = 0; u < kMaxSegX; ++u)
+                if (u == sg) {
+                    const bool ok = cq < cq_ok && xok[u] && xrow[u] >= row_lo && xrow[u] < row_hi;
+                    off = ok ? (uint32_t)((xbase + xpix[u]) * a.C + 4 * cq) * 4u : kOOB;
+                }
+            load_lds256(rx, xs + cq * a.XS + sg * 256, off);
+        }
+        for (int i = wave; i < KQ * a.nsd; i += NW) {
+            const int kq = i % KQ, sg = i / KQ;
+            uint32_t off = kOOB;
+#pragma unroll
+            for (int u = 0; u < kMaxSegD; ++u)
+                if (u == sg) {
+                    const bool ok = kq < kq_ok && dok[u] && drow[u] < drow_hi;
+                    off = ok ? (uint32_t)((dbase + dpix[u]) * a.K + 4 * kq) * 4u : kOOB;
+                }
+            load_lds256(rd, ds + kq * a.DS + sg * 256, off);
+        }
+    };
+
+    f4 acc[T][WK];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int m = 0; m < WK; ++m) acc[t][m] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = a.WoP / 4;
+    // Lane (l16, q): A = x of channel wc*16 + l16 (quad plane, component) at
+    // the step's pixel q; B = dy of output channel wk*16*WK + m*16 + l16.
+    const int xlane = (wc * 4 + (l16 >> 2)) * a.XS + (l16 & 3) + q * a.sw * 4;
+    const int dlane = ((wk * 16 * WK + l16) >> 2) * a.DS + (l16 & 3) + q * 4;
+    if (ch_begin < ch_end) issue(ch_begin, 0);
+    for (int ch = ch_begin; ch < ch_end; ++ch) {
+        const int b = (ch - ch_begin) & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (ch + 1 < ch_end) issue(ch + 1, b ^ 1);
+        const float* xs = lds + b * buf_floats;
+        const float* ds = xs + CQ * a.XS;
+        const int n = (int)fastdiv((uint32_t)ch, a.div_cpi);
+        const int ho0 = (ch - n * a.chunks_per_image) * R;
+        const int total = min(R, a.Ho - ho0) * nsteps;
+        const float* xl = xs + xlane;
+        const float* dl = ds + dlane;
+        float av[2][T], bv[2][WK];
+        auto fetch = [&](int slot, int rr, int ss) {
+            const float* xr = xl + (rr * a.sh * a.LW + ss * 4 * a.sw) * 4;
+            const float* dr = dl + (rr * a.WoP + ss * 4) * 4;
+#pragma unroll
+            for (int i = 0; i < KH; ++i) {
+                const float* xri = xr + i * a.dh * a.LW * 4;
+#pragma unroll
+                for (int j = 0; j < KW; ++j) av[slot][i * KW + j] = xri[j * a.dw * 4];
+            }
+#pragma unroll
+            for (int m = 0; m < WK; ++m) bv[slot][m] = dr[m * 4 * a.DS];
+        };
+        auto mfmas = [&](int slot) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int m = 0; m < WK; ++m)
+                    acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[slot][t], bv[slot][m],
+                                                                     acc[t][m], 0, 0, 0);
+        };
+        const int u0 = h * total / NH, u1 = (h + 1) * total / NH;
+        if (u0 < u1) {
+            int fr = u0 / nsteps, fs = u0 - (u0 / nsteps) * nsteps;
+            auto advance = [&]() {
+                if (++fs == nsteps) {
+                    fs = 0;
+                    ++fr;
+                }
+            };
+            const int last_r = (u1 - 1) / nsteps, last_s = (u1 - 1) - last_r * nsteps;
+            constexpr int NRD = T + WK, NMF = T * WK;
+            fetch(0, fr, fs);
+            int u = u0;
+            for (; u + 1 < u1; u += 2) {
+                advance();
+                fetch(1, fr, fs);
+                mfmas(0);
+                __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                advance();
+                const bool more = u + 2 < u1;
+                fetch(0, more ? fr : last_r, more ? fs : last_s);
+                mfmas(1);
+                __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (u < u1) mfmas(0);
+        }
+        __syncthreads();
+    }
+
+    if constexpr (NH == 2) {
+        float* xch = lds + (size_t)wq * (T * WK * 256) + lane;
+        if (h == 1) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int m = 0; m < WK; ++m)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) xch[(t * WK + m) * 256 + v * 64] = acc[t][m][v];
+        }
+        __syncthreads();
+        if (h == 1) return;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int m = 0; m < WK; ++m)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][m][v] += xch[(t * WK + m) * 256 + v * 64];
+    }
+    const int tile = (g * a.n_ctiles + ct) * a.n_ktiles + kt;
+    const int n_tiles = a.G * a.n_ctiles * a.n_ktiles;
+    float* out = a.ws + (((size_t)s * n_tiles + tile) * 4 + wq) * (size_t)(T * WK * 256);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int m = 0; m < WK; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out[(t * WK + m) * 256 + v * 64 + lane] = acc[t][m][v];
+}
+
+template <int KH, int KW, int WC, int WK, int R, int NH, bool INH = false>
 __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
 {
     constexpr int T = KH * KW;
@@ -81,6 +281,10 @@ __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
     const int ch_begin = s * a.chunks_per_split;
     const int ch_end = min(a.chunks_total, ch_begin + a.chunks_per_split);
 
+    if constexpr (INH) {
+        wgrad_nhwc_body<KH, KW, WC, WK, R, NH>(a, kt, ct, g, s, ch_begin, ch_end, wave, lane);
+        return;
+    }
     // Per-lane parts of the tile loads, fixed for the whole kernel: for the
     // segment sg of a plane, this lane's (row, column) inside the tile.
     int xrow[kMaxSegX], xoff[kMaxSegX];
@@ -344,10 +548,12 @@ struct Plan {
     int per_split;
 };
 
-Plan make_plan(const Shape& s)
+Plan make_plan(const Shape& s, bool nhwc = false)
 {
     Plan p{};
     p.ok = false;
+    // Channels-last tiles move whole quads of a group's channels.
+    if (nhwc && ((s.Cg & 3) != 0 || (s.Kg & 3) != 0)) return p;
     const bool k3 = s.kh == 3 && s.kw == 3, k5 = s.kh == 5 && s.kw == 5;
     if (!k3 && !k5) return p;
     if (s.N < 1) return p;
@@ -387,9 +593,16 @@ Plan make_plan(const Shape& s)
         const int xspan = a.LR * a.LW + 4 * s.sw;
         a.nsx = (xspan + 63) / 64;
         a.nsd = (R * a.WoP + 63) / 64;
-        a.XS = plane_stride(a.nsx);
-        a.DS = plane_stride(a.nsd);
-        p.lds_bytes = 2 * ((size_t)CT * a.XS + (size_t)KT * a.DS) * 4;
+        if (nhwc) {
+            // quad planes of 64-pixel segments, 8 floats (mod 32) apart
+            a.XS = a.nsx * 256 + 8;
+            a.DS = a.nsd * 256 + 8;
+            p.lds_bytes = 2 * ((size_t)(CT / 4) * a.XS + (size_t)(KT / 4) * a.DS) * 4;
+        } else {
+            a.XS = plane_stride(a.nsx);
+            a.DS = plane_stride(a.nsd);
+            p.lds_bytes = 2 * ((size_t)CT * a.XS + (size_t)KT * a.DS) * 4;
+        }
         // The second wave set's sums pass through LDS at the end.
         if (cfg.NH == 2) p.lds_bytes = std::max(p.lds_bytes, (size_t)4 * T * cfg.WK * 256 * 4);
         if (a.nsx <= kMaxSegX && a.nsd <= kMaxSegD && p.lds_bytes <= (size_t)lds_cap) break;
@@ -408,6 +621,10 @@ Plan make_plan(const Shape& s)
     // channels a tile may reach past the end of its group.
     if ((int64_t)(s.Cg + CT) * s.H * s.W * 4 >= (int64_t(1) << 30)) return p;
     if ((int64_t)(s.Kg + KT) * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return p;
+    // channels-last: one image's pixels, all channels, from one resource
+    if (nhwc && ((int64_t)s.H * s.W * s.C * 4 >= (int64_t(1) << 30) ||
+                 (int64_t)s.Ho * s.Wo * s.K * 4 >= (int64_t(1) << 30)))
+        return p;
     const int n_tiles = s.G * a.n_ctiles * a.n_ktiles;
     // Blocks per CU that fit in LDS, and about that many blocks per CU in total.
     const int per_cu = std::max(1, (int)((160 * 1024) / p.lds_bytes));
@@ -429,10 +646,10 @@ Plan make_plan(const Shape& s)
     return p;
 }
 
-template <int KH, int KW, int WC, int WK, int R, int NH>
+template <int KH, int KW, int WC, int WK, int R, int NH, bool INH = false>
 void launch_main(const Plan& p, hipStream_t st)
 {
-    auto kern = wgrad_mfma_kernel<KH, KW, WC, WK, R, NH>;
+    auto kern = wgrad_mfma_kernel<KH, KW, WC, WK, R, NH, INH>;
     // Allow dynamic LDS up to the CU's 160 KiB (once per kernel instance).
     static const bool attr_set = hipFuncSetAttribute((const void*)kern,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -441,14 +658,14 @@ void launch_main(const Plan& p, hipStream_t st)
     hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(256 * NH), p.lds_bytes, st, p.a);
 }
 
-template <int KH, int KW, int WC, int WK, int NH>
+template <int KH, int KW, int WC, int WK, int NH, bool INH = false>
 bool launch_r(const Plan& p, hipStream_t st)
 {
     switch (p.cfg.R) {
-        case 1: launch_main<KH, KW, WC, WK, 1, NH>(p, st); return true;
-        case 2: launch_main<KH, KW, WC, WK, 2, NH>(p, st); return true;
-        case 3: launch_main<KH, KW, WC, WK, 3, NH>(p, st); return true;
-        case 4: launch_main<KH, KW, WC, WK, 4, NH>(p, st); return true;
+        case 1: launch_main<KH, KW, WC, WK, 1, NH, INH>(p, st); return true;
+        case 2: launch_main<KH, KW, WC, WK, 2, NH, INH>(p, st); return true;
+        case 3: launch_main<KH, KW, WC, WK, 3, NH, INH>(p, st); return true;
+        case 4: launch_main<KH, KW, WC, WK, 4, NH, INH>(p, st); return true;
         default: return false;
     }
 }
@@ -471,34 +688,56 @@ size_t igemm_bwd_filter_workspace(const Shape& s)
     return p.ok ? p.ws_floats * sizeof(float) : 0;
 }
 
-bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+template <bool INH>
+static bool run_wgrad(Plan& p, const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                       hipStream_t st)
 {
-    Plan p = make_plan(s);
-    if (!p.ok) return false;
     p.a.x = x;
     p.a.dy = dy;
     p.a.ws = ws;
     const Config c = p.cfg;
     if (s.kh == 3 && c.WC == 2 && c.WK == 2) {
-        if (!launch_r<3, 3, 2, 2, 2>(p, st)) return false;
+        if (!launch_r<3, 3, 2, 2, 2, INH>(p, st)) return false;
         launch_reduce<9, 2, 2>(p, s, ws, dw, st);
     } else if (s.kh == 3 && c.WC == 2 && c.WK == 1) {
-        if (!launch_r<3, 3, 2, 1, 2>(p, st)) return false;
+        if (!launch_r<3, 3, 2, 1, 2, INH>(p, st)) return false;
         launch_reduce<9, 2, 1>(p, s, ws, dw, st);
     } else if (s.kh == 3 && c.WC == 1 && c.WK == 1) {
-        if (!launch_r<3, 3, 1, 1, 1>(p, st)) return false;
+        if (!launch_r<3, 3, 1, 1, 1, INH>(p, st)) return false;
         launch_reduce<9, 1, 1>(p, s, ws, dw, st);
     } else if (s.kh == 5 && c.WC == 1 && c.WK == 2) {
-        if (!launch_r<5, 5, 1, 2, 1>(p, st)) return false;
+        if (!launch_r<5, 5, 1, 2, 1, INH>(p, st)) return false;
         launch_reduce<25, 1, 2>(p, s, ws, dw, st);
     } else if (s.kh == 5 && c.WC == 1 && c.WK == 1) {
-        if (!launch_r<5, 5, 1, 1, 1>(p, st)) return false;
+        if (!launch_r<5, 5, 1, 1, 1, INH>(p, st)) return false;
         launch_reduce<25, 1, 1>(p, s, ws, dw, st);
     } else {
         return false;
     }
     return true;
+}
+
+bool igemm_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
+                      hipStream_t st)
+{
+    Plan p = make_plan(s);
+    return p.ok && run_wgrad<false>(p, s, x, dy, dw, ws, st);
+}
+
+// Channels-last x and dy read in place (s is the NCHW shape of the layer).
+bool igemm_bwd_filter_nhwc_supported(const Shape& s) { return make_plan(s, true).ok; }
+
+size_t igemm_bwd_filter_nhwc_workspace(const Shape& s)
+{
+    const Plan p = make_plan(s, true);
+    return p.ok ? p.ws_floats * sizeof(float) : 0;
+}
+
+bool igemm_bwd_filter_nhwc(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st)
+{
+    if (((uintptr_t)x & 15) || ((uintptr_t)dy & 15)) return false;
+    Plan p = make_plan(s, true);
+    return p.ok && run_wgrad<true>(p, s, x, dy, dw, ws, st);
 }
 
 }  // namespace gconv

@@ -254,3 +254,49 @@ def test_nhwc_depthwise_wgrad_misaligned(stride):
             assert np.array_equal(dw.cpu().numpy().astype(np.float64), val)
         else:
             check("misaligned dw", dw.cpu().numpy(), val, mag)
+
+
+NHWC_WGRAD_CASES = [
+    dict(N=3, C=64, K=64, H=20, W=22, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1),    # 32 x 64 tiles, 8 waves
+    dict(N=2, C=32, K=48, H=17, W=31, kh=3, kw=3, sh=1, sw=1, ph=0, pw=1, dh=1, dw=1, G=2),    # 16 x 24 per group
+    dict(N=2, C=32, K=32, H=19, W=21, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),    # stride 2
+    dict(N=2, C=16, K=32, H=18, W=18, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=2, dw=2, G=1),    # dilation 2
+    dict(N=2, C=48, K=128, H=13, W=15, kh=5, kw=5, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=1),   # 5x5
+    dict(N=2, C=32, K=32, H=15, W=63, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1),    # wide rows
+    dict(N=2, C=64, K=64, H=16, W=16, kh=3, kw=3, sh=1, sw=1, ph=0, pb=1, pw=1, pr=2, dh=1, dw=1, G=2),  # asym pads
+]
+
+
+@pytest.mark.parametrize("case", range(len(NHWC_WGRAD_CASES)))
+def test_nhwc_mfma_gradweight(case):
+    """gradWeight of channels-last x and dy on the MFMA path, read in place (quad
+    planes filled by 16-byte DMA): normal data to the tolerance, integer data bit
+    for bit; and the same call on tensors one float off 16-byte alignment (the
+    reordering route) gives the same bits."""
+    d = NHWC_WGRAD_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout="nhwc", **kw)
+    assert G.PATH_NAMES[G.gconv_select_path(desc, G.OP_BWD_FILTER)] == "igemm", d
+    Ho, Wo = G.gconv_output_dims(desc)
+    wshape = (d["K"], d["C"] // d["G"], d["kh"], d["kw"])
+    for dist, seed in ((("normal", 1.0), 3950), (("int", -3, 3), 3970)):
+        x = draw(dist, (d["N"], d["C"], d["H"], d["W"]), seed + case)
+        dy = draw(dist, (d["N"], d["K"], Ho, Wo), seed + 10 + case)
+        say("nhwc mfma gradWeight %s %s" % (d, dist[0]))
+        got = G.gconv_bwd_filter(dev(to_nhwc(x)), dev(to_nhwc(dy)), wshape, layout="nhwc", **kw)
+
+        def offset_view(a):
+            flat = torch.zeros(a.size + 1, device="cuda")
+            v = flat[1:].view(*a.shape)
+            v.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+            return v
+
+        staged = G.gconv_bwd_filter(offset_view(to_nhwc(x)), offset_view(to_nhwc(dy)), wshape, layout="nhwc", **kw)
+        torch.cuda.synchronize()
+        val, mag = oracle.bwd_filter(x, dy, wshape, **kw)
+        g = got.cpu().numpy()
+        if dist[0] == "int":
+            assert np.array_equal(g.astype(np.float64), val), d
+        else:
+            check("nhwc mfma dw %s" % d, g, val, mag)
+        check("nhwc staged dw %s" % d, staged.cpu().numpy(), val, mag)
