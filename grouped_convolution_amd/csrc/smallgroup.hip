@@ -597,9 +597,14 @@ __global__ void __launch_bounds__(256) sg_wgrad_kernel(SgWArgs a)
 // pixels of a half-wave hit distinct banks). Each wave walks whole output
 // rows in 16-pixel steps (MFMA block b = pixel b of the step; columns past the
 // image width hold dy = 0), so a step costs one dy read, nine x reads at
-// immediate offsets and nine MFMAs.
+// immediate offsets and nine MFMAs. At most 128 registers a lane (74 in
+// practice, no spills), so that the 1024 workgroups of a ResNeXt 32x4d layer
+// (four per CU) are resident at once: at 148 registers three fitted, and the
+// fourth workgroup of each CU ran alone in a second round (61.3 -> 59.8 us).
+// (Double-buffered bands, two workgroups per CU at 62 KB of LDS each,
+// measured 67.9 us: four resident workgroups hide each other's copies better.)
 template <int NSTEP>
-__global__ void __launch_bounds__(256) sg_wgrad_row64_kernel(SgWArgs a)
+__global__ void __launch_bounds__(256, 4) sg_wgrad_row64_kernel(SgWArgs a)
 {
     constexpr int T = 9;
     extern __shared__ float lds[];  // [4][plane] x rows, [4][dplane] dy rows; later [4][T*16] sums
