@@ -283,6 +283,10 @@ struct ConvFlatArgs {
     // (ho*o_sh + o_h0, wo*o_sw + o_w0) of the stored o_H x o_W planes.
     int t_kw, t_i0, t_j0, t_si, t_sj;
     int o_sh, o_sw, o_h0, o_w0, o_H, o_W;
+    // Packed groups (pk_o > 0): a "group" of the launch is several real
+    // groups side by side, pk_o output and pk_r reduction channels each, with
+    // a block-diagonal filter (w_gs floats per real group; zero across groups).
+    int pk_o, pk_r, w_gs;
 };
 
 // INH: the input is channels-last ([N][Hr][Wr][Cin_tot]); the LDS tile then
@@ -377,19 +381,25 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
     const float* w_g = a.wgt + (size_t)g * a.w_gstride;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_g, (uint32_t)a.w_gstride * 4u);
     int wbase[MO];  // -1: output channel past the group end
+    int osub[MO];   // packed groups: the real group of the output channel
 #pragma unroll
     for (int m = 0; m < MO; ++m) {
         const int o = o0 + (wo_i * MO + m) * 16 + l16;
-        wbase[m] = o < a.Cout_g ? o * a.w_so : -1;
+        osub[m] = a.pk_o ? o / a.pk_o : 0;
+        wbase[m] = o >= a.Cout_g ? -1 : a.pk_o ? osub[m] * a.w_gs + (o - osub[m] * a.pk_o) * a.w_so : o * a.w_so;
     }
     auto load_b = [&](int c0, float (&b)[MO][T]) {
         const int r = c0 + q;
+        // packed groups: filter values across real groups are 0
+        const int rsub = a.pk_o ? r / a.pk_r : 0;
+        const int rr = r - rsub * a.pk_r;
 #pragma unroll
         for (int m = 0; m < MO; ++m) {
             // One select per fragment; the tap offsets then ride on the
             // instruction's immediate offset (out-of-range stays out of range).
-            const uint32_t base =
-                (r < a.Cin_g && wbase[m] >= 0) ? (uint32_t)(wbase[m] + r * a.w_sr) * 4u : kOOB;
+            const uint32_t base = (r < a.Cin_g && wbase[m] >= 0 && rsub == osub[m])
+                                      ? (uint32_t)(wbase[m] + rr * a.w_sr) * 4u
+                                      : kOOB;
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 if constexpr (PH) {
@@ -668,7 +678,31 @@ struct Problem {
     bool phase = false;
     int t_kw = 0, t_i0 = 0, t_j0 = 0, t_si = 1, t_sj = 1;
     int o_sh = 1, o_sw = 1, o_h0 = 0, o_w0 = 0, o_H = 0, o_W = 0;
+    int pk_o = 0, pk_r = 0, w_gs = 0;    // packed groups (flat kernel only)
 };
+
+// Groups with fewer than 16 output channels leave most of each 16-wide MFMA
+// fragment idle, and a workgroup then reuses its input tile (whose per-lane
+// DMA offsets cost it a fixed prologue) for only Cin_g / 4 chunks. Packing P
+// consecutive groups into one launch group with a block-diagonal filter fills
+// the fragment (the products across groups are with zero weights: the same
+// MFMA count per output as the idle lanes had) and gives each workgroup P
+// times the chunks. Channels of consecutive groups are contiguous, so the
+// packed group is a plain group of P*Cin_g inputs and P*Cout_g outputs.
+Problem pack_groups(Problem p)
+{
+    int P = 1;
+    while (p.Cout_g * P * 2 <= 16 && p.G % (P * 2) == 0) P *= 2;
+    if (P == 1) return p;
+    p.pk_o = p.Cout_g;
+    p.pk_r = p.Cin_g;
+    p.w_gs = p.w_gstride;
+    p.G /= P;
+    p.Cout_g *= P;
+    p.Cin_g *= P;
+    p.w_gstride *= P;
+    return p;
+}
 
 int choose_cc(const Problem& p) { return (p.kh * p.kw >= 16) ? 4 : 8; }
 
@@ -828,8 +862,9 @@ struct FlatPlan {
     int blocks;
 };
 
-bool flat_plan(const Problem& p, FlatPlan& fp)
+bool flat_plan(const Problem& p_in, FlatPlan& fp)
 {
+    const Problem p = pack_groups(p_in);
     if (p.phase) {
         if (!(p.kh >= 1 && p.kh <= 2 && p.kw >= 1 && p.kw <= 2 && p.flip)) return false;
     } else if (!((p.kh == 3 && p.kw == 3) || (p.kh == 5 && p.kw == 5))) {
@@ -923,10 +958,11 @@ bool dispatch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
     return false;
 }
 
-bool run_flat(const Problem& p, hipStream_t st)
+bool run_flat(const Problem& p_in, hipStream_t st)
 {
     FlatPlan fp;
-    if (!flat_plan(p, fp)) return false;
+    if (!flat_plan(p_in, fp)) return false;
+    const Problem p = pack_groups(p_in);
     ConvFlatArgs a;
     a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
     a.N = p.N; a.G = p.G;
@@ -947,6 +983,7 @@ bool run_flat(const Problem& p, hipStream_t st)
     a.div_Wout = make_fastdiv((uint32_t)p.Wout);
     a.div_plane = make_fastdiv((uint32_t)fp.plane);
     a.div_LW = make_fastdiv((uint32_t)fp.LW);
+    a.pk_o = p.pk_o; a.pk_r = p.pk_r; a.w_gs = p.w_gs;
     a.t_kw = p.t_kw; a.t_i0 = p.t_i0; a.t_j0 = p.t_j0; a.t_si = p.t_si; a.t_sj = p.t_sj;
     a.o_sh = p.o_sh; a.o_sw = p.o_sw; a.o_h0 = p.o_h0; a.o_w0 = p.o_w0; a.o_H = p.o_H; a.o_W = p.o_W;
     if (p.phase) return p.in_nhwc ? dispatch_phase<true>(a, fp, st) : dispatch_phase<false>(a, fp, st);

@@ -416,16 +416,16 @@ PHASE_CASES = [
 
 
 # Shapes whose every phase launch has at least 256 workgroups, so the library
-# takes the phases (8 input channels per group: 256 output pixels per workgroup,
-# 8 groups; 32: 128 pixels, one group):
+# takes the phases (8 dx channels per group: two groups packed per workgroup,
+# 256 output pixels each, 4 packed groups; 32: 128 pixels, one group):
 PHASE_LARGE = [
-    dict(N=8, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 4 x 32x32 x 8 / 256
-    dict(N=9, C=64, K=64, H=65, W=63, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # ragged phases
+    dict(N=16, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 16x32x32/256 x 4
+    dict(N=18, C=64, K=64, H=65, W=63, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # ragged phases
     dict(N=8, C=32, K=48, H=128, W=128, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),  # 8 x 64x64 / 128
-    dict(N=8, C=64, K=64, H=96, W=96, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=8),   # 9 1x1 phases
-    dict(N=8, C=64, K=64, H=64, W=64, kh=4, kw=4, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 2x2 sub-filters
+    dict(N=16, C=64, K=64, H=96, W=96, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=8),   # 9 1x1 phases
+    dict(N=16, C=64, K=64, H=64, W=64, kh=4, kw=4, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 2x2 sub-filters
     dict(N=8, C=128, K=128, H=64, W=64, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=8),  # 1x1 sub-filters
-    dict(N=8, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1, G=8),  # "same"
+    dict(N=16, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1, G=8),  # "same"
 ]
 
 
