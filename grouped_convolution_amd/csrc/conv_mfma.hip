@@ -277,24 +277,35 @@ struct ConvFlatArgs {
     int relu;                   // forward epilogue: max(v, 0)
     int out_nhwc;               // store the output channels-last, [N][Hout*Wout][Cout_tot]
     FastDiv div_P, div_Wout, div_plane, div_LW;
-    // Phase of a strided gradInput (PH instances): tap t = (i, j) of the
-    // KH x KW sub-filter is tap (t_i0 + i*t_si, t_j0 + j*t_sj) of the stored
-    // filter, whose rows hold t_kw taps; output pixel (ho, wo) is pixel
-    // (ho*o_sh + o_h0, wo*o_sw + o_w0) of the stored o_H x o_W planes.
-    int t_kw, t_i0, t_j0, t_si, t_sj;
-    int o_sh, o_sw, o_h0, o_w0, o_H, o_W;
     // Packed groups (pk_o > 0): a "group" of the launch is several real
     // groups side by side, pk_o output and pk_r reduction channels each, with
     // a block-diagonal filter (w_gs floats per real group; zero across groups).
     int pk_o, pk_r, w_gs;
+    // Sub-pixel form of a strided gradInput (SP instances): the launch's
+    // output channel o = (c*o_sh + du)*o_sw + dv at pixel (a, b) is dx channel
+    // c of the group (sp_cg per group) at (a*o_sh + du, b*o_sw + dv) of the
+    // o_H x o_W planes. With the padding written p = sp_bh*o_sh + sp_rh, that
+    // row's stored taps are i = u + o_sh*i' with u = (du + p) mod o_sh, and
+    // tap i reads dy row a + (du + p) div o_sh - i'; super-tap ti reads dy
+    // row a + sp_mh + ti (sp_mh the least such offset). Columns alike. The
+    // stored filter has sp_kh x sp_kw taps.
+    int o_sh, o_sw, o_H, o_W;
+    int sp_cg, sp_bh, sp_rh, sp_bw, sp_rw, sp_mh, sp_mw, sp_kh, sp_kw;
+    int sp_vec;                 // 2x2 sub-pixels, Hout*Wout and Wout multiples of 4, o_W == 2*Wout, NCHW
 };
+
+// Lane l and lane l ^ 1 exchange a value (DPP quad permutation 1, 0, 3, 2).
+__device__ __forceinline__ float swap_pair(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
 
 // INH: the input is channels-last ([N][Hr][Wr][Cin_tot]); the LDS tile then
 // holds each pixel's 4 chunk channels together ([row][col][4]), filled by
 // 16-byte DMA (one pixel per lane), and a fragment's 16 pixels x 4 channels
 // read 64 consecutive floats.
 template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, int MINW, bool INH = false,
-          bool PH = false>
+          bool SP = false>
 __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlatArgs a)
 {
     constexpr int T = KH * KW;
@@ -382,14 +393,42 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_g, (uint32_t)a.w_gstride * 4u);
     int wbase[MO];  // -1: output channel past the group end
     int osub[MO];   // packed groups: the real group of the output channel
+    int soff[SP ? MO : 1][SP ? T : 1];  // sub-pixel form: stored tap of each super-tap, -1 none
 #pragma unroll
     for (int m = 0; m < MO; ++m) {
         const int o = o0 + (wo_i * MO + m) * 16 + l16;
         osub[m] = a.pk_o ? o / a.pk_o : 0;
         wbase[m] = o >= a.Cout_g ? -1 : a.pk_o ? osub[m] * a.w_gs + (o - osub[m] * a.pk_o) * a.w_so : o * a.w_so;
+        if constexpr (SP) {
+            const int c = o / (a.o_sh * a.o_sw), rem = o - c * (a.o_sh * a.o_sw);
+            const int du = rem / a.o_sw, dv = rem - du * a.o_sw;
+            wbase[m] = o >= a.Cout_g ? -1 : c * a.w_so;
+            const bool ch = du + a.sp_rh >= a.o_sh, cw = dv + a.sp_rw >= a.o_sw;
+            const int Ah = a.sp_bh + ch - a.sp_mh, uh = du + a.sp_rh - (ch ? a.o_sh : 0);
+            const int Aw = a.sp_bw + cw - a.sp_mw, uw = dv + a.sp_rw - (cw ? a.o_sw : 0);
+#pragma unroll
+            for (int ti = 0; ti < KH; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < KW; ++tj) {
+                    const int i = uh + a.o_sh * (Ah - ti), j = uw + a.o_sw * (Aw - tj);
+                    soff[m][ti * KW + tj] =
+                        (Ah - ti >= 0 && i < a.sp_kh && Aw - tj >= 0 && j < a.sp_kw) ? i * a.sp_kw + j : -1;
+                }
+        }
     }
     auto load_b = [&](int c0, float (&b)[MO][T]) {
         const int r = c0 + q;
+        if constexpr (SP) {
+#pragma unroll
+            for (int m = 0; m < MO; ++m) {
+                const uint32_t base =
+                    (r < a.Cin_g && wbase[m] >= 0) ? (uint32_t)(wbase[m] + r * a.w_sr) * 4u : kOOB;
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    b[m][t] = load_f32(rw, soff[m][t] >= 0 ? base + (uint32_t)soff[m][t] * 4u : kOOB);
+            }
+            return;
+        }
         // packed groups: filter values across real groups are 0
         const int rsub = a.pk_o ? r / a.pk_r : 0;
         const int rr = r - rsub * a.pk_r;
@@ -401,14 +440,7 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
                                       ? (uint32_t)(wbase[m] + rr * a.w_sr) * 4u
                                       : kOOB;
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                if constexpr (PH) {
-                    const int tm = (a.t_i0 + (t / KW) * a.t_si) * a.t_kw + a.t_j0 + (t % KW) * a.t_sj;
-                    b[m][t] = load_f32(rw, base + (uint32_t)tm * 4u);
-                } else {
-                    b[m][t] = load_f32(rw, base + (uint32_t)t * 4u);
-                }
-            }
+            for (int t = 0; t < T; ++t) b[m][t] = load_f32(rw, base + (uint32_t)t * 4u);
         }
     };
     // Taps in memory order (so the loads merge into 16-byte ones); the flipped
@@ -561,22 +593,47 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
                 v.z = relu_if(v.z, 1);
                 v.w = relu_if(v.w, 1);
             }
-            if constexpr (PH) {
-                // A phase of a strided gradInput: output pixel (ho, wo) is
-                // pixel (ho*o_sh + o_h0, wo*o_sw + o_w0) of the stored planes.
-                const float vv[4] = {v.x, v.y, v.z, v.w};
-                const size_t Preal = (size_t)a.o_H * a.o_W;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int qq = qb + u;
-                    if (qq < q1) {
-                        const int n = (int)fastdiv((uint32_t)qq, a.div_P);
-                        const int p = qq - n * a.P;
+            if constexpr (SP) {
+                // Sub-pixel form: channel o is sub-pixel (du, dv) of dx channel c.
+                const int ss = a.o_sh * a.o_sw;
+                const int c = o / ss, rem = o - c * ss;
+                const int du = rem / a.o_sw, dv = rem - du * a.o_sw;
+                const size_t chd = (size_t)g * a.sp_cg + c;
+                if (a.sp_vec) {
+                    // dv = l16 & 1: the pair of lanes holds dx columns 2b..2b+7
+                    // of one row; after the exchange the even lane has 2b..2b+3
+                    // and the odd one 2b+4..2b+7, one 16-byte store each.
+                    const float s0 = dv ? v.x : v.z, s1 = dv ? v.y : v.w;
+                    const float r0 = swap_pair(s0), r1 = swap_pair(s1);
+                    const f4 vs = dv ? f4{r0, v.z, r1, v.w} : f4{v.x, r0, v.y, r1};
+                    if (qb < q1) {
+                        const int n = (int)fastdiv((uint32_t)qb, a.div_P);
+                        const int p = qb - n * a.P;
                         const int ho = (int)fastdiv((uint32_t)p, a.div_Wout);
                         const int wo = p - ho * a.Wout;
-                        const size_t pr = (size_t)(ho * a.o_sh + a.o_h0) * a.o_W + (size_t)(wo * a.o_sw + a.o_w0);
-                        if (a.out_nhwc) a.out[((size_t)n * Preal + pr) * a.Cout_tot + ch_off] = vv[u];
-                        else a.out[((size_t)n * a.Cout_tot + ch_off) * Preal + pr] = vv[u];
+                        const int h = 2 * ho + du;
+                        if (h < a.o_H)
+                            *(f4*)(a.out + (((size_t)n * a.Cout_tot + chd) * a.o_H + h) * a.o_W + 2 * wo +
+                                   4 * dv) = vs;
+                    }
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
+                    const size_t Preal = (size_t)a.o_H * a.o_W;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int qq = qb + u;
+                        if (qq < q1) {
+                            const int n = (int)fastdiv((uint32_t)qq, a.div_P);
+                            const int p = qq - n * a.P;
+                            const int ho = (int)fastdiv((uint32_t)p, a.div_Wout);
+                            const int wo = p - ho * a.Wout;
+                            const int h = ho * a.o_sh + du, w = wo * a.o_sw + dv;
+                            if (h < a.o_H && w < a.o_W) {
+                                const size_t pr = (size_t)h * a.o_W + w;
+                                if (a.out_nhwc) a.out[((size_t)n * Preal + pr) * a.Cout_tot + chd] = vv[u];
+                                else a.out[((size_t)n * a.Cout_tot + chd) * Preal + pr] = vv[u];
+                            }
+                        }
                     }
                 }
             } else if (a.out_nhwc) {
@@ -673,12 +730,13 @@ struct Problem {
     int relu = 0;                        // forward epilogue
     int out_nhwc = 0;                    // channels-last output (flat kernel only)
     int in_nhwc = 0;                     // channels-last input (flat kernel only; Cin_g % 4 == 0)
-    // One phase of a strided gradInput (flat kernel only): the sub-filter's
-    // taps within the stored filter and the output pixels within dx.
-    bool phase = false;
-    int t_kw = 0, t_i0 = 0, t_j0 = 0, t_si = 1, t_sj = 1;
-    int o_sh = 1, o_sw = 1, o_h0 = 0, o_w0 = 0, o_H = 0, o_W = 0;
     int pk_o = 0, pk_r = 0, w_gs = 0;    // packed groups (flat kernel only)
+    // Sub-pixel form of a strided gradInput (flat kernel only): dx's stride,
+    // extent and the mapping of super-taps to stored taps (the kernel
+    // arguments of the same names).
+    bool sp = false;
+    int o_sh = 1, o_sw = 1, o_H = 0, o_W = 0;
+    int sp_cg = 0, sp_bh = 0, sp_rh = 0, sp_bw = 0, sp_rw = 0, sp_mh = 0, sp_mw = 0, sp_kh = 0, sp_kw = 0;
 };
 
 // Groups with fewer than 16 output channels leave most of each 16-wide MFMA
@@ -691,6 +749,7 @@ struct Problem {
 // packed group is a plain group of P*Cin_g inputs and P*Cout_g outputs.
 Problem pack_groups(Problem p)
 {
+    if (p.sp) return p;  // its output channels are already sub-pixels of a group's channels
     int P = 1;
     while (p.Cout_g * P * 2 <= 16 && p.G % (P * 2) == 0) P *= 2;
     if (P == 1) return p;
@@ -820,7 +879,7 @@ Problem bwd_data_problem(const Shape& s, const float* dy, const float* w, float*
 struct FlatInst {
     int T, MO, WO, WPX, MP, NSX;
     int KH, KW;
-    bool PH;  // a phase of a strided gradInput (sub-filter taps, strided output)
+    bool SP;  // the sub-pixel form of a strided gradInput (super-taps, depth-to-space output)
 };
 #ifndef GCONV_FLAT_MP3
 #define GCONV_FLAT_MP3 5
@@ -841,19 +900,19 @@ struct FlatInst {
     X(25, 5, 1, 4, 1, 4, 8) X(25, 5, 2, 4, 1, 4, 8) X(25, 5, 1, 3, 1, 4, 8)                \
     X(25, 5, 1, 2, 2, 4, 8) X(25, 5, 1, 1, 4, 4, 12)                                       \
     X(9, 3, 2, 4, 1, 4, 16) X(9, 3, 1, 1, 4, 4, 24) X(25, 5, 1, 3, 1, 4, 12)
-// Phase instances of a strided gradInput (always flipped): the sub-filters of
-// a 3x3 filter at stride 2 (2x2, 2x1, 1x2, 1x1), and of other filters up to
-// twice the stride, over the same wave layouts.
-#define GCONV_PHASE_SHAPES(X, mo, wo, wpx, mp, nsx) \
-    X(2, 2, mo, wo, wpx, mp, nsx) X(2, 1, mo, wo, wpx, mp, nsx) X(1, 2, mo, wo, wpx, mp, nsx) X(1, 1, mo, wo, wpx, mp, nsx)
-#define GCONV_PHASE_INSTS(X)                                                     \
-    GCONV_PHASE_SHAPES(X, 1, 1, 4, 4, 12) GCONV_PHASE_SHAPES(X, 1, 2, 2, 4, 8)    \
-    GCONV_PHASE_SHAPES(X, 1, 4, 1, 5, 8) GCONV_PHASE_SHAPES(X, 2, 4, 1, 4, 12)
+// Sub-pixel instances (never flipped): super-filters of 1x1 (2x2 filters at
+// stride 2), 2x2 (3x3 at stride 2 or 3) and 3x3 (4x4 and 5x5 at stride 2),
+// over the same wave layouts.
+#define GCONV_SP_SHAPES(X, mo, wo, wpx, mp, nsx) \
+    X(1, mo, wo, wpx, mp, nsx) X(2, mo, wo, wpx, mp, nsx) X(3, mo, wo, wpx, mp, nsx)
+#define GCONV_SP_INSTS(X)                                                     \
+    GCONV_SP_SHAPES(X, 1, 1, 4, 4, 12) GCONV_SP_SHAPES(X, 1, 2, 2, 4, 8)       \
+    GCONV_SP_SHAPES(X, 1, 4, 1, 5, 8) GCONV_SP_SHAPES(X, 2, 4, 1, 4, 12)
 #define GCONV_FLAT_ENTRY(t, k, mo, wo, wpx, mp, nsx) {t, mo, wo, wpx, mp, nsx, k, k, false},
-#define GCONV_PHASE_ENTRY(kh, kw, mo, wo, wpx, mp, nsx) {kh * kw, mo, wo, wpx, mp, nsx, kh, kw, true},
-constexpr FlatInst kFlatInsts[] = {GCONV_FLAT_INSTS(GCONV_FLAT_ENTRY) GCONV_PHASE_INSTS(GCONV_PHASE_ENTRY)};
+#define GCONV_SP_ENTRY(k, mo, wo, wpx, mp, nsx) {k * k, mo, wo, wpx, mp, nsx, k, k, true},
+constexpr FlatInst kFlatInsts[] = {GCONV_FLAT_INSTS(GCONV_FLAT_ENTRY) GCONV_SP_INSTS(GCONV_SP_ENTRY)};
 #undef GCONV_FLAT_ENTRY
-#undef GCONV_PHASE_ENTRY
+#undef GCONV_SP_ENTRY
 
 struct FlatPlan {
     FlatInst inst;
@@ -865,19 +924,20 @@ struct FlatPlan {
 bool flat_plan(const Problem& p_in, FlatPlan& fp)
 {
     const Problem p = pack_groups(p_in);
-    if (p.phase) {
-        if (!(p.kh >= 1 && p.kh <= 2 && p.kw >= 1 && p.kw <= 2 && p.flip)) return false;
+    if (p.sp) {
+        if (!(p.kh == p.kw && p.kh >= 1 && p.kh <= 3 && !p.flip)) return false;
     } else if (!((p.kh == 3 && p.kw == 3) || (p.kh == 5 && p.kw == 5))) {
         return false;
     }
     const int nfrag = (p.Cout_g + 15) / 16;
     const int mo = nfrag > 4 ? 2 : 1;
-    // waves across output channels (phase instances: 1, 2 or 4)
-    const int wo = nfrag > 4 ? 4 : (p.phase && nfrag == 3) ? 4 : nfrag;
+    // waves across output channels (sub-pixel instances: 1, 2 or 4)
+    const int wo = nfrag > 4 ? 4 : (p.sp && nfrag == 3) ? 4 : nfrag;
     const FlatInst* inst = nullptr;
     int64_t plane = 0, nseg = 0, LW = 0, P = (int64_t)p.Hout * p.Wout;
     for (const FlatInst& fi : kFlatInsts) {
-        if (!(fi.KH == p.kh && fi.KW == p.kw && fi.PH == p.phase && fi.MO == mo && fi.WO == wo)) continue;
+        if (!(fi.KH == p.kh && fi.KW == p.kw && fi.SP == p.sp && fi.MO == mo && fi.WO == wo))
+            continue;
         const int NWi = fi.WO * fi.WPX;
         const int BPXi = fi.WPX * fi.MP * 16;
         if (P < BPXi) continue;  // a tile must span at most two images
@@ -921,26 +981,25 @@ bool flat_plan(const Problem& p_in, FlatPlan& fp)
     return true;
 }
 
-template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, bool INH, bool PH = false>
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, bool INH, bool SP = false>
 void launch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     constexpr int MINW = (KH * KW <= 9) ? 4 : 2;
-    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW, INH, PH>;
+    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW, INH, SP>;
     hipLaunchKernelGGL(kern, dim3(fp.blocks), dim3(64 * WO * WPX), fp.lds_bytes, st, a);
 }
 
 template <bool INH>
-bool dispatch_phase(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
+bool dispatch_sp(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     const FlatInst& i = fp.inst;
-#define GCONV_PHASE_CASE(kh, kw, mo, wo, wpx, mp, nsx)                                          \
-    if (i.PH && i.KH == kh && i.KW == kw && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && \
-        i.NSX == nsx) {                                                                         \
-        launch_flat<kh, kw, mp, mo, wo, wpx, nsx, true, INH, true>(a, fp, st);                  \
-        return true;                                                                           \
+#define GCONV_SP_CASE(k, mo, wo, wpx, mp, nsx)                                                     \
+    if (i.SP && i.KH == k && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
+        launch_flat<k, k, mp, mo, wo, wpx, nsx, false, INH, true>(a, fp, st);              \
+        return true;                                                                             \
     }
-    GCONV_PHASE_INSTS(GCONV_PHASE_CASE)
-#undef GCONV_PHASE_CASE
+    GCONV_SP_INSTS(GCONV_SP_CASE)
+#undef GCONV_SP_CASE
     return false;
 }
 
@@ -949,7 +1008,7 @@ bool dispatch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     const FlatInst& i = fp.inst;
 #define GCONV_FLAT_CASE(t, k, mo, wo, wpx, mp, nsx)                                     \
-    if (!i.PH && i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
+    if (!i.SP && i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
         launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP, INH>(a, fp, st);                  \
         return true;                                                                   \
     }
@@ -984,9 +1043,12 @@ bool run_flat(const Problem& p_in, hipStream_t st)
     a.div_plane = make_fastdiv((uint32_t)fp.plane);
     a.div_LW = make_fastdiv((uint32_t)fp.LW);
     a.pk_o = p.pk_o; a.pk_r = p.pk_r; a.w_gs = p.w_gs;
-    a.t_kw = p.t_kw; a.t_i0 = p.t_i0; a.t_j0 = p.t_j0; a.t_si = p.t_si; a.t_sj = p.t_sj;
-    a.o_sh = p.o_sh; a.o_sw = p.o_sw; a.o_h0 = p.o_h0; a.o_w0 = p.o_w0; a.o_H = p.o_H; a.o_W = p.o_W;
-    if (p.phase) return p.in_nhwc ? dispatch_phase<true>(a, fp, st) : dispatch_phase<false>(a, fp, st);
+    a.o_sh = p.o_sh; a.o_sw = p.o_sw; a.o_H = p.o_H; a.o_W = p.o_W;
+    a.sp_cg = p.sp_cg; a.sp_bh = p.sp_bh; a.sp_rh = p.sp_rh; a.sp_bw = p.sp_bw; a.sp_rw = p.sp_rw;
+    a.sp_mh = p.sp_mh; a.sp_mw = p.sp_mw; a.sp_kh = p.sp_kh; a.sp_kw = p.sp_kw;
+    a.sp_vec = p.sp && p.o_sh == 2 && p.o_sw == 2 && !p.out_nhwc && a.P % 4 == 0 && p.Wout % 4 == 0 &&
+               p.o_W == 2 * p.Wout && ((uintptr_t)p.out & 15) == 0;
+    if (p.sp) return p.in_nhwc ? dispatch_sp<true>(a, fp, st) : dispatch_sp<false>(a, fp, st);
     if (p.in_nhwc) return p.flip ? dispatch_flat<true, true>(a, fp, st) : dispatch_flat<false, true>(a, fp, st);
     return p.flip ? dispatch_flat<true, false>(a, fp, st) : dispatch_flat<false, false>(a, fp, st);
 }
@@ -1002,92 +1064,95 @@ bool use_flat(const Problem& p)
 #endif
 }
 
-// ---- strided gradInput by phases ------------------------------------------------
+// ---- strided gradInput in sub-pixel form -----------------------------------------
 //
-// dx[h][w] sums w[k][c][i][j] * dy[k][(h + ph - i)/sh][(w + pw - j)/sw] over the
-// taps whose quotients are exact. With h + ph = sh*a + u (0 <= u < sh) only
-// the taps i = u + sh*i' qualify, and they read dy row a - i'; likewise for
-// columns. So the dx pixels of phase (u, v) are a unit-stride correlation of
-// the stored dy with the sub-filter w[u + sh*i'][v + sw*j'] (reversed, padding
-// Ti - 1 rows above the phase's first row a_min), written to every sh-th row
-// and sw-th column of dx. The sh*sw phases together do the strided layer's
-// real work, where the virtually upsampled dy costs sh*sw times that in
-// products with zeros.
-struct PhaseSet {
-    int n = 0;
-    Problem ph[16];
-};
+// dx[h][w] sums w[k][c][i][j] * dy[k][(h + ph - i)/sh][(w + pw - j)/sw] over
+// the taps whose quotients are exact. With h + ph = sh*A + u (0 <= u < sh, the
+// row's phase) only the taps i = u + sh*i' qualify, and tap i reads dy row
+// A - i'; columns alike. Group the dx pixels into blocks of sh x sw, block
+// (a, b) holding pixels (a*sh + du, b*sw + dv): the pixel at du has
+// A = a + (du + ph) div sh, so every pixel of the block reads dy rows a + d
+// for offsets d within a small spread E. The block is thus a unit-stride
+// correlation of the stored dy with an E x E super-filter and Cg*sh*sw output
+// channels, one per (channel, sub-pixel), whose super-taps that match no
+// stored tap are zero. One launch covers every phase over a shared dy tile and
+// stores whole dx rows. The zero taps cost MFMA work (16 super-taps for the 9
+// real ones of a 3x3 filter at stride 2); against one launch per phase (exact
+// taps, but every other dx column written per launch, which doubles the HBM
+// writes, and four launches with a quarter of the pixels each) it was faster
+// on every layer measured: 254 -> 102 us for 256 channels in groups of 8 at
+// 56 x 56, 204 -> 152 us for 128 dense channels, 347 -> 185 us for 512 -> 256
+// channels at 28 x 28.
 
-// The phases of a strided gradInput the flat kernel can run (3x3 and other
-// filters up to twice the stride, unit dilation); false if any cannot.
-bool phase_problems(const Shape& s, const float* dy, const float* w, float* dx, PhaseSet* set)
+// Least dy offset and spread of a dimension's super-taps: the sub-pixel at
+// du has phase u = (du + p) mod s, whose taps i = u + s*i' (i < k) read dy at
+// offset (du + p) div s - i'.
+void sp_extent(int k, int st, int pad, int* dmin, int* ext)
 {
-    if (!(s.sh > 1 || s.sw > 1) || s.dh != 1 || s.dw != 1) return false;
-    if (s.kh < s.sh || s.kw < s.sw || s.kh > 2 * s.sh || s.kw > 2 * s.sw || s.sh * s.sw > 16) return false;
-    const int T = s.kh * s.kw;
-    set->n = 0;
-    for (int u = 0; u < s.sh; ++u)
-        for (int v = 0; v < s.sw; ++v) {
-            const int Ti = (s.kh - u + s.sh - 1) / s.sh, Tj = (s.kw - v + s.sw - 1) / s.sw;
-            const int xu = s.ph - u, xv = s.pw - v;
-            const int a_min = xu <= 0 ? 0 : (xu + s.sh - 1) / s.sh;
-            const int b_min = xv <= 0 ? 0 : (xv + s.sw - 1) / s.sw;
-            const int ru = s.H - 1 + s.ph - u, rv = s.W - 1 + s.pw - v;
-            if (ru < 0 || rv < 0) continue;             // no dx pixel in this phase
-            const int Ha = ru / s.sh - a_min + 1, Wb = rv / s.sw - b_min + 1;
-            if (Ha <= 0 || Wb <= 0) continue;
-            Problem p;
-            p.in = dy; p.wgt = w; p.bias = nullptr; p.out = dx;
-            p.N = s.N; p.G = s.G;
-            p.Cin_tot = s.K; p.Cin_g = s.Kg; p.Hin = s.Ho; p.Win = s.Wo;
-            p.Hr = s.Ho; p.Wr = s.Wo;
-            p.Cout_tot = s.C; p.Cout_g = s.Cg; p.Hout = Ha; p.Wout = Wb;
-            p.kh = Ti; p.kw = Tj; p.sh = 1; p.sw = 1; p.dh = 1; p.dw = 1;
-            p.ph = Ti - 1 - a_min; p.pw = Tj - 1 - b_min;
-            p.w_so = T; p.w_sr = s.Cg * T; p.w_gstride = s.Kg * s.Cg * T;
-            p.flip = true;
-            p.phase = true;
-            p.t_kw = s.kw; p.t_i0 = u; p.t_j0 = v; p.t_si = s.sh; p.t_sj = s.sw;
-            p.o_sh = s.sh; p.o_sw = s.sw;
-            p.o_h0 = s.sh * a_min + u - s.ph; p.o_w0 = s.sw * b_min + v - s.pw;
-            p.o_H = s.H; p.o_W = s.W;
-            if (!use_flat(p)) return false;
-            set->ph[set->n++] = p;
-        }
-    return set->n > 0;
+    const int b = pad / st, r = pad % st;
+    int lo = 1 << 30, hi = -(1 << 30);
+    for (int du = 0; du < st; ++du) {
+        const bool c = du + r >= st;
+        const int A = b + c, u = du + r - (c ? st : 0);
+        if (u >= k) continue;  // no tap: the sub-pixel's dx values are 0
+        const int Ti = (k - u + st - 1) / st;
+        lo = std::min(lo, A - (Ti - 1));
+        hi = std::max(hi, A);
+    }
+    *dmin = lo;
+    *ext = hi - lo + 1;
 }
 
-bool run_phases(PhaseSet& set, bool in_nhwc, bool out_nhwc, hipStream_t st)
+bool sp_problem(const Shape& s, const float* dy, const float* w, float* dx, Problem* out)
 {
-    for (int i = 0; i < set.n; ++i) {
-        set.ph[i].in_nhwc = in_nhwc;
-        set.ph[i].out_nhwc = out_nhwc;
-        if (!run_flat(set.ph[i], st)) return false;
-    }
+    if (!(s.sh > 1 || s.sw > 1) || s.dh != 1 || s.dw != 1 || s.ph < 0 || s.pw < 0) return false;
+    int mh, eh, mw, ew;
+    sp_extent(s.kh, s.sh, s.ph, &mh, &eh);
+    sp_extent(s.kw, s.sw, s.pw, &mw, &ew);
+    const int E = std::max(eh, ew);  // the shorter dimension's extra taps match no stored tap
+    if (E > 3 || s.sh * s.sw > 16) return false;
+    const int T = s.kh * s.kw;
+    Problem p;
+    p.in = dy; p.wgt = w; p.bias = nullptr; p.out = dx;
+    p.N = s.N; p.G = s.G;
+    p.Cin_tot = s.K; p.Cin_g = s.Kg; p.Hin = s.Ho; p.Win = s.Wo; p.Hr = s.Ho; p.Wr = s.Wo;
+    p.Cout_tot = s.C; p.Cout_g = s.Cg * s.sh * s.sw;
+    p.Hout = (s.H + s.sh - 1) / s.sh; p.Wout = (s.W + s.sw - 1) / s.sw;
+    p.kh = E; p.kw = E; p.sh = 1; p.sw = 1; p.dh = 1; p.dw = 1;
+    p.ph = -mh; p.pw = -mw;
+    p.w_so = T; p.w_sr = s.Cg * T; p.w_gstride = s.Kg * s.Cg * T;
+    p.flip = false;
+    p.sp = true;
+    p.sp_cg = s.Cg;
+    p.sp_bh = s.ph / s.sh; p.sp_rh = s.ph % s.sh; p.sp_bw = s.pw / s.sw; p.sp_rw = s.pw % s.sw;
+    p.sp_mh = mh; p.sp_mw = mw; p.sp_kh = s.kh; p.sp_kw = s.kw;
+    p.o_sh = s.sh; p.o_sw = s.sw; p.o_H = s.H; p.o_W = s.W;
+    if (!use_flat(p)) return false;
+    *out = p;
     return true;
 }
 
-bool phases_ok(const Shape& s, bool in_nhwc)
+bool sp_ok(const Shape& s, bool in_nhwc)
 {
-#ifdef GCONV_NO_PHASES
+#ifdef GCONV_NO_SUBPIXEL
     (void)s; (void)in_nhwc;
     return false;
 #else
-    // Each phase is its own launch over a quarter (at stride 2) of the output
-    // pixels: where that leaves fewer workgroups than CUs, the single launch
-    // over the virtually upsampled dy is faster (a 512 -> 256-channel 28 x 28
-    // layer: 341 against 450 us), so phases are taken only when every phase
-    // launch fills the chip (a 64-channel 112 x 112 layer: 3010 -> 177 us; 128
-    // channels at 56 x 56: 295 -> 205 us).
-    PhaseSet set;
-    if (!phase_problems(s, nullptr, nullptr, nullptr, &set)) return false;
-    for (int i = 0; i < set.n; ++i) {
-        set.ph[i].in_nhwc = in_nhwc;
-        FlatPlan fp;
-        if (!flat_plan(set.ph[i], fp) || fp.blocks < 256) return false;
-    }
-    return true;
+    Problem p;
+    if (!sp_problem(s, nullptr, nullptr, nullptr, &p)) return false;
+    p.in_nhwc = in_nhwc;
+    return use_flat(p);
 #endif
+}
+
+bool run_sp(const Shape& s, const float* dy, const float* w, float* dx, bool in_nhwc, bool out_nhwc,
+            hipStream_t st)
+{
+    Problem p;
+    if (!sp_problem(s, dy, w, dx, &p)) return false;
+    p.in_nhwc = in_nhwc;
+    p.out_nhwc = out_nhwc;
+    return run_flat(p, st);
 }
 
 }  // namespace
@@ -1100,7 +1165,7 @@ bool igemm_fwd_supported(const Shape& s)
 
 bool igemm_bwd_data_supported(const Shape& s)
 {
-    if (phases_ok(s, false)) return true;
+    if (sp_ok(s, false)) return true;
     const Problem p = bwd_data_problem(s, nullptr, nullptr, nullptr);
     if (p.uh != 1 || p.uw != 1) return use_flat(p);  // only the flat kernel upsamples
     return use_flat(p) || problem_supported(p);
@@ -1115,8 +1180,7 @@ bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias
 
 bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
-    PhaseSet set;
-    if (phases_ok(s, false) && phase_problems(s, dy, w, dx, &set)) return run_phases(set, false, false, st);
+    if (sp_ok(s, false)) return run_sp(s, dy, w, dx, false, false, st);
     const Problem p = bwd_data_problem(s, dy, w, dx);
     if (use_flat(p)) return run_flat(p, st);
     if (p.uh != 1 || p.uw != 1) return false;
@@ -1130,7 +1194,7 @@ bool igemm_nhwc_out_supported(const Shape& s, int op)
 {
     if (op == GCONV_OP_FWD) return use_flat(fwd_problem(s, nullptr, nullptr, nullptr, nullptr));
     if (op == GCONV_OP_BWD_DATA)
-        return phases_ok(s, false) || use_flat(bwd_data_problem(s, nullptr, nullptr, nullptr));
+        return sp_ok(s, false) || use_flat(bwd_data_problem(s, nullptr, nullptr, nullptr));
     return false;
 }
 
@@ -1145,8 +1209,7 @@ bool igemm_fwd_nhwc_out(const Shape& s, const float* x, const float* w, const fl
 
 bool igemm_bwd_data_nhwc_out(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
-    PhaseSet set;
-    if (phases_ok(s, false) && phase_problems(s, dy, w, dx, &set)) return run_phases(set, false, true, st);
+    if (sp_ok(s, false)) return run_sp(s, dy, w, dx, false, true, st);
     Problem p = bwd_data_problem(s, dy, w, dx);
     if (!use_flat(p)) return false;
     p.out_nhwc = 1;
@@ -1167,7 +1230,7 @@ bool igemm_nhwc_io_supported(const Shape& s, int op)
 {
     if (op == GCONV_OP_FWD) return use_flat(nhwc_io(fwd_problem(s, nullptr, nullptr, nullptr, nullptr)));
     if (op == GCONV_OP_BWD_DATA)
-        return phases_ok(s, true) || use_flat(nhwc_io(bwd_data_problem(s, nullptr, nullptr, nullptr)));
+        return sp_ok(s, true) || use_flat(nhwc_io(bwd_data_problem(s, nullptr, nullptr, nullptr)));
     return false;
 }
 
@@ -1179,8 +1242,7 @@ bool igemm_fwd_nhwc_io(const Shape& s, const float* x, const float* w, const flo
 
 bool igemm_bwd_data_nhwc_io(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
-    PhaseSet set;
-    if (phases_ok(s, true) && phase_problems(s, dy, w, dx, &set)) return run_phases(set, true, true, st);
+    if (sp_ok(s, true)) return run_sp(s, dy, w, dx, true, true, st);
     const Problem p = nhwc_io(bwd_data_problem(s, dy, w, dx));
     return use_flat(p) && run_flat(p, st);
 }

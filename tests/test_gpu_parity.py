@@ -400,42 +400,49 @@ ASYM_CASES = [
 ]
 
 
-# Strided gradInput on the MFMA path. By phases, every (row, column) phase of
-# dx is a unit-stride correlation of the stored dy with a sub-filter of the taps
-# that reach it (3x3 at stride 2: 2x2, 2x1, 1x2 and 1x1).
-PHASE_CASES = [
-    dict(N=2, C=64, K=64, H=40, W=36, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),    # 8 per group
+# Strided gradInput on the MFMA path, in sub-pixel form: the dx pixels in
+# blocks of sh x sw, each block a unit-stride correlation of the stored dy
+# with an E x E super-filter (its taps that match no stored tap zero) and
+# Cg*sh*sw output channels, one per (channel, sub-pixel). Cases span E = 1, 2
+# and 3, 1 to 9 sub-pixels, the 16-byte stores (2x2 sub-pixels, dx width a
+# multiple of 8) and the per-element ones, and 1 to 16 output fragments.
+SUBPIXEL_CASES = [
+    dict(N=2, C=64, K=64, H=40, W=40, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),    # 8 per group, 16-byte stores
     dict(N=2, C=32, K=48, H=35, W=41, kh=3, kw=3, sh=2, sw=2, ph=1, pw=0, dh=1, dw=1, G=1),    # odd sizes
-    dict(N=3, C=128, K=64, H=34, W=34, kh=3, kw=3, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=2),   # 64 dx channels
-    dict(N=1, C=256, K=32, H=36, W=38, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),   # 256 dx channels
-    dict(N=2, C=32, K=32, H=48, W=47, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=2),    # stride 3: 9 1x1 phases
-    dict(N=2, C=48, K=32, H=40, W=40, kh=4, kw=4, sh=2, sw=2, ph=1, pw=2, dh=1, dw=1, G=1),    # 4x4: four 2x2 phases
-    dict(N=2, C=32, K=32, H=40, W=36, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=2),    # 2x2: four 1x1 phases
+    dict(N=3, C=128, K=64, H=34, W=34, kh=3, kw=3, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=2),   # pad 0: offsets -1, 0
+    dict(N=1, C=256, K=32, H=36, W=38, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),   # 1024 super-channels
+    dict(N=2, C=32, K=32, H=48, W=47, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=2),    # stride 3: 9 sub-pixels
+    dict(N=2, C=48, K=32, H=40, W=40, kh=4, kw=4, sh=2, sw=2, ph=1, pw=2, dh=1, dw=1, G=1),    # 4x4: E = 3
+    dict(N=2, C=32, K=32, H=40, W=36, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=2),    # 2x2: E = 1
     dict(N=2, C=64, K=64, H=40, W=40, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1, G=8),  # "same"
+    dict(N=2, C=48, K=48, H=33, W=32, kh=5, kw=5, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=2),    # 5x5: E = 3
+    dict(N=2, C=24, K=32, H=30, W=29, kh=3, kw=3, sh=2, sw=1, ph=1, pw=1, dh=1, dw=1, G=2),    # strides (2, 1)
+    dict(N=2, C=48, K=64, H=32, W=32, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=4),    # 3 output fragments
+    dict(N=2, C=32, K=32, H=20, W=24, kh=3, kw=3, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=4),    # pad 2: offsets 0, 1
+    dict(N=2, C=16, K=64, H=20, W=20, kh=1, kw=1, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=1),    # 1x1: zero sub-pixels
 ]
 
 
-# Shapes whose every phase launch has at least 256 workgroups, so the library
-# takes the phases (8 dx channels per group: two groups packed per workgroup,
-# 256 output pixels each, 4 packed groups; 32: 128 pixels, one group):
-PHASE_LARGE = [
-    dict(N=16, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 16x32x32/256 x 4
-    dict(N=18, C=64, K=64, H=65, W=63, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # ragged phases
-    dict(N=8, C=32, K=48, H=128, W=128, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),  # 8 x 64x64 / 128
-    dict(N=16, C=64, K=64, H=96, W=96, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=8),   # 9 1x1 phases
-    dict(N=16, C=64, K=64, H=64, W=64, kh=4, kw=4, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # 2x2 sub-filters
-    dict(N=8, C=128, K=128, H=64, W=64, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=8),  # 1x1 sub-filters
+# Larger shapes (many workgroups, images spanning tiles), checked on sampled outputs.
+SUBPIXEL_LARGE = [
+    dict(N=16, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),
+    dict(N=18, C=64, K=64, H=65, W=63, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # ragged blocks
+    dict(N=8, C=32, K=48, H=128, W=128, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),
+    dict(N=16, C=64, K=64, H=96, W=96, kh=3, kw=3, sh=3, sw=3, ph=1, pw=1, dh=1, dw=1, G=8),   # 9 sub-pixels
+    dict(N=16, C=64, K=64, H=64, W=64, kh=4, kw=4, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),   # E = 3
+    dict(N=8, C=128, K=128, H=64, W=64, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=8),  # E = 1
     dict(N=16, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1, G=8),  # "same"
+    dict(N=8, C=256, K=256, H=56, W=56, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),  # 16 fragments
 ]
 
 
-@pytest.mark.parametrize("case", range(len(PHASE_LARGE)))
+@pytest.mark.parametrize("case", range(len(SUBPIXEL_LARGE)))
 @pytest.mark.parametrize("layout", ["nchw", "nhwc"])
-def test_strided_gradinput_phases_sampled(case, layout):
-    """Strided gradInput by phases at sizes where the library takes them, against
+def test_strided_gradinput_subpixel_sampled(case, layout):
+    """Strided gradInput in sub-pixel form at sizes of many workgroups, against
     the oracle on 4000 sampled outputs: normal data to the tolerance, integer
     data bit for bit."""
-    d = PHASE_LARGE[case]
+    d = SUBPIXEL_LARGE[case]
     kw = conv_kwargs(d)
     desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout=layout, **kw)
     assert G.PATH_NAMES[G.gconv_select_path(desc, G.OP_BWD_DATA)] == "igemm", d
@@ -446,7 +453,7 @@ def test_strided_gradinput_phases_sampled(case, layout):
     for dist, seed in ((("normal", 1.0), 2900), (("int", -3, 3), 2950)):
         w = draw(dist, (d["K"], d["C"] // d["G"], d["kh"], d["kw"]), seed + case)
         dy = draw(dist, (d["N"], d["K"], Ho, Wo), seed + 20 + case)
-        say("phases sampled %s %s %s" % (layout, d, dist[0]))
+        say("subpixel sampled %s %s %s" % (layout, d, dist[0]))
         got = G.gconv_bwd_data(dev(to(dy)), dev(w), to(np.empty((d["N"], d["C"], d["H"], d["W"]), np.float32)).shape,
                                layout=layout, workspace=torch.empty(max(ws // 4, 1), device="cuda"), **kw)
         if nhwc:
@@ -457,26 +464,26 @@ def test_strided_gradinput_phases_sampled(case, layout):
         if dist[0] == "int":
             assert np.array_equal(g.astype(np.float64), val), d
         else:
-            check("phases sampled %s" % d, g, val, mag)
+            check("subpixel sampled %s" % d, g, val, mag)
 
 
-@pytest.mark.parametrize("case", range(len(PHASE_CASES)))
+@pytest.mark.parametrize("case", range(len(SUBPIXEL_CASES)))
 @pytest.mark.parametrize("layout", ["nchw", "nhwc"])
-def test_strided_gradinput_phases(case, layout):
-    """Strided gradInput against the oracle at sizes where the phases' launches
-    would be small (the MFMA path then reads dy virtually upsampled; filters it
-    has no upsampled form for go to the direct kernels): normal data to the
-    tolerance, integer data bit for bit."""
-    d = PHASE_CASES[case]
+def test_strided_gradinput_subpixel(case, layout):
+    """Strided gradInput in sub-pixel form (the family asserted) against the
+    oracle on every output: normal data to the tolerance, integer data bit for
+    bit."""
+    d = SUBPIXEL_CASES[case]
     kw = conv_kwargs(d)
     desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout=layout, **kw)
+    assert G.PATH_NAMES[G.gconv_select_path(desc, G.OP_BWD_DATA)] == "igemm", d
     nhwc = layout == "nhwc"
     to = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1))) if nhwc else (lambda a: a)
     for dist, seed in ((("normal", 1.0), 2700), (("int", -3, 3), 2800)):
         x, w, _ = tensors(d, seed + case, dist=dist, bias=False)
         Ho, Wo = G.gconv_output_dims(desc)
         dy = draw(dist, (d["N"], d["K"], Ho, Wo), seed + 50 + case)
-        say("phases %s %s %s" % (layout, d, dist[0]))
+        say("subpixel %s %s %s" % (layout, d, dist[0]))
         ws = G.gconv_workspace_size(desc, G.OP_BWD_DATA)
         got = G.gconv_bwd_data(dev(to(dy)), dev(w), to(x).shape, layout=layout,
                                workspace=torch.empty(max(ws // 4, 1), device="cuda"), **kw)
@@ -488,7 +495,7 @@ def test_strided_gradinput_phases(case, layout):
         if dist[0] == "int":
             assert np.array_equal(got.astype(np.float64), val), d
         else:
-            check("phases %s" % d, got, val, mag)
+            check("subpixel %s" % d, got, val, mag)
 
 
 @pytest.mark.parametrize("case", range(len(ASYM_CASES)))
