@@ -1163,6 +1163,8 @@ bool igemm_fwd_supported(const Shape& s)
     return use_flat(p) || problem_supported(p);
 }
 
+bool igemm_bwd_data_subpixel_ok(const Shape& s) { return sp_ok(s, false); }
+
 bool igemm_bwd_data_supported(const Shape& s)
 {
     if (sp_ok(s, false)) return true;

@@ -59,11 +59,13 @@ bool direct_tile_bwd_filter(const Shape& s, const float* x, const float* dy, flo
                             hipStream_t st);
 size_t direct_tile_bwd_filter_workspace(const Shape& s);
 
-// ---- fp32-MFMA implicit GEMM (forward; gradInput at stride 1) ---------------
+// ---- fp32-MFMA implicit GEMM (forward; gradInput, strided in sub-pixel form) ---
 // *_supported() tell whether the family covers a shape; the launchers return
 // false if no kernel instance matches (the dispatcher checks support first).
 bool igemm_fwd_supported(const Shape& s);
 bool igemm_bwd_data_supported(const Shape& s);
+// Strided gradInput in the MFMA path's sub-pixel form (NCHW dy).
+bool igemm_bwd_data_subpixel_ok(const Shape& s);
 bool igemm_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
                hipStream_t st);
 bool igemm_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st);

@@ -266,6 +266,15 @@ __global__ void __launch_bounds__(256) sg_conv_row64_kernel(SgArgs a)
     }
 }
 
+// Waits until at most N vector memory instructions of this wave are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Depthwise form (one input channel per group, up to 8 outputs): a workgroup
 // takes kDwGroups consecutive groups of one band, so that the tiles stay large
 // although each group has a single input plane, and every output is a plain
@@ -695,6 +704,148 @@ __global__ void __launch_bounds__(256, 4) sg_wgrad_row64_kernel(SgWArgs a)
     }
     __syncthreads();
     // Partial of this (image run, group): [chunk][g][k][c][t].
+    float* out = a.ws + ((size_t)chunk * a.G + g) * (16 * T);
+    for (int e = tid; e < 16 * T; e += 256) {
+        const int t = e % T, kc = e / T;  // kc = k*4 + c
+        out[e] = ((red[(0 * T + t) * 16 + kc] + red[(1 * T + t) * 16 + kc]) +
+                  red[(2 * T + t) * 16 + kc]) +
+                 red[(3 * T + t) * 16 + kc];
+    }
+}
+
+// Streaming form of the gradWeight kernel above (same shapes): a workgroup
+// owns one group, its four waves stream units (one band of one image each)
+// independently, each through rings in its own LDS slice: RX = PF + 3 input
+// rows and RD = PF + 1 dy rows, 4 channels of 72 floats each (== 8 mod 32, so
+// the 4 channels x 8 pixels of a half-wave read distinct banks). Stream step
+// j loads input row j and dy row j - 2, which output row j - 2 needs last; it
+// is issued when output row j - RX is done, so PF steps stay in flight behind
+// the row being summed and no barrier ties the waves together until the
+// final cross-wave sum. Every step issues the same 8 DMA rows (past the band:
+// out-of-range zeros into freed slots), so the wait for a step counts exactly
+// the PF steps after it.
+struct SgWStreamArgs {
+    const float* x;
+    const float* dy;
+    float* ws;
+    int N, C, H, W, K, Ho, Wo, G, Cg, Kg;
+    int ph, pw;
+    int R, nbands;              // output rows per band, bands per image
+    int upw, nchunks;           // units (image, band) per wave, workgroups per group
+};
+
+template <int NSTEP, int PF>
+__global__ void __launch_bounds__(256) sg_wgrad_stream_kernel(SgWStreamArgs a)
+{
+    constexpr int T = 9, RX = PF + 3, RD = PF + 1;
+    constexpr int CS = 72;                   // channel stride of a slot
+    constexpr int SLOT = 4 * CS;
+    constexpr int WLDS = (RX + RD) * SLOT;
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c4 = lane & 3, blk = lane >> 2;  // this lane's channel (c and k), MFMA block
+    float* xring = lds + wave * WLDS;
+    float* dring = xring + RX * SLOT;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int g = bid % a.G;
+    const int chunk = bid / a.G;
+    const int units = a.N * a.nbands;
+
+    // Columns 64..71 of the input slots are never loaded: zero them once
+    // (lanes past the image width read up to column 65, times dy = 0).
+    for (int e = lane; e < RX * 4 * 8; e += 64) xring[(e >> 3) * CS + 64 + (e & 7)] = 0.f;
+
+    const int wcol = lane - a.pw;
+    const bool colok = (unsigned)wcol < (unsigned)a.W;
+    f4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k = 0; k < a.upw; ++k) {
+        const int u = (chunk * a.upw + k) * 4 + wave;
+        if (u >= units) break;
+        const int n = u / a.nbands, band = u - n * a.nbands;
+        const int r0 = band * a.R;
+        const int rows = min(a.R, a.Ho - r0);
+        const int hfirst = r0 - a.ph;
+        const float* xg = a.x + ((size_t)n * a.C + (size_t)g * a.Cg) * a.H * a.W;
+        const float* dyg = a.dy + ((size_t)n * a.K + (size_t)g * a.Kg) * a.Ho * a.Wo;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, (uint32_t)a.Cg * a.H * a.W * 4u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, (uint32_t)a.Kg * a.Ho * a.Wo * 4u);
+        // Step j: input row j of the band into slot sx, dy row j - 2 into slot sd.
+        auto issue_step = [&](int j, int sx, int sd, bool with_dy) {
+            const int h = hfirst + j;
+            const bool okx = colok && j < rows + 2 && (unsigned)h < (unsigned)a.H;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                load_lds64(rx, xring + sx * SLOT + c * CS,
+                           (okx && c < a.Cg) ? (uint32_t)((c * a.H + h) * a.W + wcol) * 4u : kOOB);
+            if (with_dy) {
+                const int d = j - 2;
+                const bool okd = lane < a.Wo && d < rows;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    load_lds64(rd, dring + sd * SLOT + kk * CS,
+                               (okd && kk < a.Kg) ? (uint32_t)((kk * a.Ho + r0 + d) * a.Wo + lane) * 4u : kOOB);
+            }
+        };
+        // Steps 0 and 1 carry no dy row; steps 2 .. RX-1 carry dy rows 0 .. PF.
+        issue_step(0, 0, 0, false);
+        issue_step(1, 1, 0, false);
+#pragma unroll
+        for (int j = 2; j < RX; ++j) issue_step(j, j, j - 2, true);
+
+        int sx0 = 0, sd0 = 0;  // slots of input row i and dy row i
+        for (int i = 0; i < rows; ++i) {
+            wait_vmcnt<PF * 8>();  // step i + 2 landed: PF steps of 8 DMA rows follow it
+            const int sx1 = sx0 + 1 == RX ? 0 : sx0 + 1;
+            const int sx2 = sx1 + 1 == RX ? 0 : sx1 + 1;
+            const float* dl = dring + sd0 * SLOT + c4 * CS + blk;
+            const float* x0 = xring + sx0 * SLOT + c4 * CS + blk;
+            const float* x1 = xring + sx1 * SLOT + c4 * CS + blk;
+            const float* x2 = xring + sx2 * SLOT + c4 * CS + blk;
+#pragma unroll
+            for (int st = 0; st < NSTEP; ++st) {
+                const float dv = dl[st * 16];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const float* xr = t < 3 ? x0 : t < 6 ? x1 : x2;
+                    acc[t] = mfma4(dv, xr[st * 16 + t % 3], acc[t]);
+                }
+            }
+            // Input row i and dy row i are no longer read: step i + RX reuses their slots.
+            issue_step(i + RX, sx0, sd0, true);
+            sx0 = sx1;
+            sd0 = sd0 + 1 == RD ? 0 : sd0 + 1;
+        }
+    }
+
+    // acc[t][v] of lane l = sum over its block's pixels of dy[k = v] * x[c = l%4].
+    // Sum the 16 blocks (lanes with equal l%4), in a fixed butterfly order.
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sum = acc[t][v];
+            sum += __shfl_xor(sum, 4, 64);
+            sum += __shfl_xor(sum, 8, 64);
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            acc[t][v] = sum;
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero rows landed before LDS is reused
+    __syncthreads();
+    float* red = lds;  // [wave][t][k(4)][c(4)]
+    if (lane < 4) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[(wave * T + t) * 16 + v * 4 + lane] = acc[t][v];
+    }
+    __syncthreads();
+    // Partial of this (unit run, group): [chunk][g][k][c][t].
     float* out = a.ws + ((size_t)chunk * a.G + g) * (16 * T);
     for (int e = tid; e < 16 * T; e += 256) {
         const int t = e % T, kc = e / T;  // kc = k*4 + c
@@ -1190,6 +1341,43 @@ bool sgw_plan(const Shape& s, SgWArgs* out, bool* row64 = nullptr)
     return true;
 }
 
+// The streaming gradWeight kernel: same shapes as the row-per-DMA one. Bands
+// per image such that about 4096 waves have a unit each (four workgroups of
+// 28 KiB per CU, one round), bands of at least 8 rows; a wave takes several
+// units where there are more than 8192. One step of prefetch: on ResNeXt
+// 32x4d (64 images of 56 x 56) deeper rings cost resident workgroups and time
+// (49.9 us at one step, 51.4 at two, 56.1 at three; the banded kernel 60.1).
+#ifndef GCONV_SG_WSTREAM_PF
+#define GCONV_SG_WSTREAM_PF 1
+#endif
+constexpr int kSgwStreamPF = GCONV_SG_WSTREAM_PF;
+
+bool sgw_stream_plan(const Shape& s, SgWStreamArgs* out)
+{
+#ifdef GCONV_SG_NO_STREAM
+    (void)s; (void)out;
+    return false;
+#else
+    if (!(sgw_row64_ok(s) && s.Cg <= 4 && s.Kg <= 4 && s.N >= 1)) return false;
+    if ((int64_t)(s.Cg + 4) * s.H * s.W * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)(s.Kg + 4) * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
+    SgWStreamArgs a{};
+    a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
+    a.G = s.G; a.Cg = s.Cg; a.Kg = s.Kg; a.ph = s.ph; a.pw = s.pw;
+    const int64_t planes = (int64_t)s.N * s.G;
+    const int64_t want = (4096 + planes - 1) / planes;
+    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, s.Ho / 8)));
+    a.R = (s.Ho + nb - 1) / nb;
+    a.nbands = (s.Ho + a.R - 1) / a.R;
+    const int64_t units = (int64_t)s.N * a.nbands;  // per group
+    a.upw = (int)std::max<int64_t>(1, (units * s.G + 8191) / 8192);
+    a.nchunks = (int)((units + 4 * a.upw - 1) / (4 * a.upw));
+    if ((int64_t)a.nchunks * s.G >= (1 << 30)) return false;
+    if (out) *out = a;
+    return true;
+#endif
+}
+
 }  // namespace
 
 // Depthwise gradWeight on the row tile: 3x3, dilation 1, stride 1 or 2, one
@@ -1287,6 +1475,8 @@ size_t smallgroup_bwd_filter_workspace(const Shape& s)
     SgDwWArgs da;
     int mq;
     if (sg_dw_wgrad_plan(s, &da, &mq)) return (size_t)da.nruns * s.G * mq * 9 * sizeof(float);
+    SgWStreamArgs sa;
+    if (sgw_stream_plan(s, &sa)) return (size_t)sa.nchunks * s.G * 16 * 9 * sizeof(float);
     SgWArgs a;
     bool row64 = false;
     if (!sgw_plan(s, &a, &row64)) return 0;
@@ -1330,6 +1520,22 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
         const int E = s.G * s.Kg * 9;
         hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, da.nruns, s.G,
                            s.Kg, mq);
+        return true;
+    }
+    SgWStreamArgs sa;
+    if (sgw_stream_plan(s, &sa)) {
+        sa.x = x; sa.dy = dy; sa.ws = ws;
+        constexpr int PF = kSgwStreamPF;
+        const size_t lds = (size_t)4 * ((PF + 3) + (PF + 1)) * 4 * 72 * 4;
+        const int nstep = (s.Wo + 15) / 16;
+        const int blocks = sa.nchunks * s.G;
+        if (nstep == 1) hipLaunchKernelGGL((sg_wgrad_stream_kernel<1, PF>), dim3(blocks), dim3(256), lds, st, sa);
+        else if (nstep == 2) hipLaunchKernelGGL((sg_wgrad_stream_kernel<2, PF>), dim3(blocks), dim3(256), lds, st, sa);
+        else if (nstep == 3) hipLaunchKernelGGL((sg_wgrad_stream_kernel<3, PF>), dim3(blocks), dim3(256), lds, st, sa);
+        else hipLaunchKernelGGL((sg_wgrad_stream_kernel<4, PF>), dim3(blocks), dim3(256), lds, st, sa);
+        const int total = s.G * 16 * 9;
+        hipLaunchKernelGGL(sg_wgrad_reduce, dim3((total + 15) / 16), dim3(256), 0, st, ws, dw,
+                           sa.nchunks, s.G, s.Kg, s.Cg, 9);
         return true;
     }
     SgWArgs a;

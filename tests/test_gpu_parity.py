@@ -420,6 +420,8 @@ SUBPIXEL_CASES = [
     dict(N=2, C=48, K=64, H=32, W=32, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=4),    # 3 output fragments
     dict(N=2, C=32, K=32, H=20, W=24, kh=3, kw=3, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=4),    # pad 2: offsets 0, 1
     dict(N=2, C=16, K=64, H=20, W=20, kh=1, kw=1, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=1),    # 1x1: zero sub-pixels
+    dict(N=2, C=32, K=32, H=40, W=40, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),    # 4 per group
+    dict(N=2, C=24, K=16, H=21, W=26, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=4),    # 6 dx, 4 dy per group
 ]
 
 
@@ -433,6 +435,7 @@ SUBPIXEL_LARGE = [
     dict(N=8, C=128, K=128, H=64, W=64, kh=2, kw=2, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=8),  # E = 1
     dict(N=16, C=64, K=64, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=0, pb=1, pw=0, pr=1, dh=1, dw=1, G=8),  # "same"
     dict(N=8, C=256, K=256, H=56, W=56, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=1),  # 16 fragments
+    dict(N=16, C=128, K=128, H=64, W=64, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=32),  # 4 per group
 ]
 
 
