@@ -713,17 +713,21 @@ __global__ void __launch_bounds__(256, 4) sg_wgrad_row64_kernel(SgWArgs a)
     }
 }
 
-// Streaming form of the gradWeight kernel above (same shapes): a workgroup
-// owns one group, its four waves stream units (one band of one image each)
-// independently, each through rings in its own LDS slice: RX = PF + 3 input
-// rows and RD = PF + 1 dy rows, 4 channels of 72 floats each (== 8 mod 32, so
-// the 4 channels x 8 pixels of a half-wave read distinct banks). Stream step
-// j loads input row j and dy row j - 2, which output row j - 2 needs last; it
-// is issued when output row j - RX is done, so PF steps stay in flight behind
-// the row being summed and no barrier ties the waves together until the
-// final cross-wave sum. Every step issues the same 8 DMA rows (past the band:
-// out-of-range zeros into freed slots), so the wait for a step counts exactly
-// the PF steps after it.
+// Streaming form of the gradWeight kernel above, for 3x3 filters at stride 1
+// or 2 with up to 8 input and 8 output channels per group (CQ and KQ quads of
+// 4: each (k quad, c quad) pair is a 4x4 block of the 4x4x1 MFMA, kept in its
+// own accumulators). A workgroup owns one group; its four waves stream units
+// (one band of one image each) independently, each through rings in its own
+// LDS slice: input rows and dy rows, 72 floats per channel (== 8 mod 32, so
+// the 4 channels x 8 pixels of a half-wave read distinct banks at stride 1).
+// Stream step j loads input rows S*j .. S*j + S - 1 and dy row j - D, D the
+// steps until an output row's three input rows are all in (2 at stride 1, 1
+// at stride 2). Step i + D + PF + 1 is issued when output row i is done, into
+// the slots that row no longer needs, so PF steps stay in flight behind the
+// row being summed and no barrier ties the waves together until the final
+// cross-wave sum. Every step past the first D issues the same DMA rows (past
+// the band: out-of-range zeros into freed slots), so the wait for a step
+// counts exactly the PF steps after it.
 struct SgWStreamArgs {
     const float* x;
     const float* dy;
@@ -734,19 +738,24 @@ struct SgWStreamArgs {
     int upw, nchunks;           // units (image, band) per wave, workgroups per group
 };
 
-template <int NSTEP, int PF>
-__global__ void __launch_bounds__(256) sg_wgrad_stream_kernel(SgWStreamArgs a)
+// (8 x 8 channels: 144 accumulators a lane; at most 256 registers keep two
+// workgroups per CU.)
+template <int NSTEP, int PF, int S, int CQ, int KQ>
+__global__ void __launch_bounds__(256, (CQ * KQ > 1 ? 2 : 1)) sg_wgrad_stream_kernel(SgWStreamArgs a)
 {
-    constexpr int T = 9, RX = PF + 3, RD = PF + 1;
-    constexpr int CS = 72;                   // channel stride of a slot
-    constexpr int SLOT = 4 * CS;
-    constexpr int WLDS = (RX + RD) * SLOT;
+    constexpr int T = 9;
+    constexpr int D = S == 1 ? 2 : 1;
+    constexpr int RX = S * (D + 1 + PF), RD = PF + 1;  // input-row and dy-row slots
+    constexpr int CS = 72;                              // channel stride of a slot
+    constexpr int XSLOT = 4 * CQ * CS, DSLOT = 4 * KQ * CS;
+    constexpr int WLDS = RX * XSLOT + RD * DSLOT;
+    constexpr int NDMA = S * 4 * CQ + 4 * KQ;          // DMA rows per step
     extern __shared__ float lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c4 = lane & 3, blk = lane >> 2;  // this lane's channel (c and k), MFMA block
+    const int c4 = lane & 3, blk = lane >> 2;  // this lane's channel in a quad (c and k), MFMA block
     float* xring = lds + wave * WLDS;
-    float* dring = xring + RX * SLOT;
+    float* dring = xring + RX * XSLOT;
 
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int g = bid % a.G;
@@ -754,14 +763,18 @@ __global__ void __launch_bounds__(256) sg_wgrad_stream_kernel(SgWStreamArgs a)
     const int units = a.N * a.nbands;
 
     // Columns 64..71 of the input slots are never loaded: zero them once
-    // (lanes past the image width read up to column 65, times dy = 0).
-    for (int e = lane; e < RX * 4 * 8; e += 64) xring[(e >> 3) * CS + 64 + (e & 7)] = 0.f;
+    // (lanes past the output width read up to column 64 + S - 1, times dy = 0).
+    for (int e = lane; e < RX * 4 * CQ * 8; e += 64) xring[(e >> 3) * CS + 64 + (e & 7)] = 0.f;
 
     const int wcol = lane - a.pw;
     const bool colok = (unsigned)wcol < (unsigned)a.W;
-    f4 acc[T];
+    f4 acc[KQ][CQ][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+        for (int cq = 0; cq < CQ; ++cq)
+#pragma unroll
+            for (int t = 0; t < T; ++t) acc[kq][cq][t] = f4{0.f, 0.f, 0.f, 0.f};
 
     for (int k = 0; k < a.upw; ++k) {
         const int u = (chunk * a.upw + k) * 4 + wave;
@@ -769,90 +782,108 @@ __global__ void __launch_bounds__(256) sg_wgrad_stream_kernel(SgWStreamArgs a)
         const int n = u / a.nbands, band = u - n * a.nbands;
         const int r0 = band * a.R;
         const int rows = min(a.R, a.Ho - r0);
-        const int hfirst = r0 - a.ph;
+        const int nin = S * (rows - 1) + 3;   // input rows of the band
+        const int hfirst = S * r0 - a.ph;
         const float* xg = a.x + ((size_t)n * a.C + (size_t)g * a.Cg) * a.H * a.W;
         const float* dyg = a.dy + ((size_t)n * a.K + (size_t)g * a.Kg) * a.Ho * a.Wo;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, (uint32_t)a.Cg * a.H * a.W * 4u);
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, (uint32_t)a.Kg * a.Ho * a.Wo * 4u);
-        // Step j: input row j of the band into slot sx, dy row j - 2 into slot sd.
+        // Step j: input rows S*j .. into slots sx, sx + 1 (S = 2: sx is even,
+        // RX too, so no wrap), dy row j - D into slot sd. One lane offset per
+        // row; the channel's plane offset rides in the scalar offset, and
+        // channels past the group fall outside the resource (read 0).
+        const uint32_t xplane = (uint32_t)a.H * a.W * 4u, dplane = (uint32_t)a.Ho * a.Wo * 4u;
         auto issue_step = [&](int j, int sx, int sd, bool with_dy) {
-            const int h = hfirst + j;
-            const bool okx = colok && j < rows + 2 && (unsigned)h < (unsigned)a.H;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                load_lds64(rx, xring + sx * SLOT + c * CS,
-                           (okx && c < a.Cg) ? (uint32_t)((c * a.H + h) * a.W + wcol) * 4u : kOOB);
+            for (int r = 0; r < S; ++r) {
+                const int jj = S * j + r, h = hfirst + jj;
+                const bool okx = colok && jj < nin && (unsigned)h < (unsigned)a.H;
+                const uint32_t off = okx ? (uint32_t)(h * a.W + wcol) * 4u : kOOB;
+#pragma unroll
+                for (int c = 0; c < 4 * CQ; ++c) load_lds64s(rx, xring + (sx + r) * XSLOT + c * CS, off, c * xplane);
+            }
             if (with_dy) {
-                const int d = j - 2;
-                const bool okd = lane < a.Wo && d < rows;
+                const int d = j - D;
+                const uint32_t off = (lane < a.Wo && d < rows) ? (uint32_t)((r0 + d) * a.Wo + lane) * 4u : kOOB;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    load_lds64(rd, dring + sd * SLOT + kk * CS,
-                               (okd && kk < a.Kg) ? (uint32_t)((kk * a.Ho + r0 + d) * a.Wo + lane) * 4u : kOOB);
+                for (int kk = 0; kk < 4 * KQ; ++kk) load_lds64s(rd, dring + sd * DSLOT + kk * CS, off, kk * dplane);
             }
         };
-        // Steps 0 and 1 carry no dy row; steps 2 .. RX-1 carry dy rows 0 .. PF.
-        issue_step(0, 0, 0, false);
-        issue_step(1, 1, 0, false);
+        // Steps 0 .. D - 1 carry no dy row; steps D .. D + PF carry dy rows 0 .. PF.
 #pragma unroll
-        for (int j = 2; j < RX; ++j) issue_step(j, j, j - 2, true);
+        for (int j = 0; j < D; ++j) issue_step(j, S * j, 0, false);
+#pragma unroll
+        for (int j = D; j <= D + PF; ++j) issue_step(j, S * j, j - D, true);
 
-        int sx0 = 0, sd0 = 0;  // slots of input row i and dy row i
+        int sx0 = 0, sd0 = 0;  // slots of input row S*i and dy row i
         for (int i = 0; i < rows; ++i) {
-            wait_vmcnt<PF * 8>();  // step i + 2 landed: PF steps of 8 DMA rows follow it
-            const int sx1 = sx0 + 1 == RX ? 0 : sx0 + 1;
-            const int sx2 = sx1 + 1 == RX ? 0 : sx1 + 1;
-            const float* dl = dring + sd0 * SLOT + c4 * CS + blk;
-            const float* x0 = xring + sx0 * SLOT + c4 * CS + blk;
-            const float* x1 = xring + sx1 * SLOT + c4 * CS + blk;
-            const float* x2 = xring + sx2 * SLOT + c4 * CS + blk;
+            wait_vmcnt<PF * NDMA>();  // step i + D landed: PF steps follow it
+            int sx[3];
+#pragma unroll
+            for (int ti = 0; ti < 3; ++ti) sx[ti] = sx0 + ti >= RX ? sx0 + ti - RX : sx0 + ti;
 #pragma unroll
             for (int st = 0; st < NSTEP; ++st) {
-                const float dv = dl[st * 16];
+                float dv[KQ];
+#pragma unroll
+                for (int kq = 0; kq < KQ; ++kq) dv[kq] = dring[sd0 * DSLOT + (kq * 4 + c4) * CS + st * 16 + blk];
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    const float* xr = t < 3 ? x0 : t < 6 ? x1 : x2;
-                    acc[t] = mfma4(dv, xr[st * 16 + t % 3], acc[t]);
+                    float xv[CQ];
+#pragma unroll
+                    for (int cq = 0; cq < CQ; ++cq)
+                        xv[cq] = xring[sx[t / 3] * XSLOT + (cq * 4 + c4) * CS + S * (st * 16 + blk) + t % 3];
+#pragma unroll
+                    for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+                        for (int cq = 0; cq < CQ; ++cq) acc[kq][cq][t] = mfma4(dv[kq], xv[cq], acc[kq][cq][t]);
                 }
             }
-            // Input row i and dy row i are no longer read: step i + RX reuses their slots.
-            issue_step(i + RX, sx0, sd0, true);
-            sx0 = sx1;
+            // Input rows S*i .. S*i + S - 1 and dy row i are no longer read:
+            // step i + D + PF + 1 reuses their slots.
+            issue_step(i + D + PF + 1, sx0, sd0, true);
+            sx0 = sx0 + S >= RX ? sx0 + S - RX : sx0 + S;
             sd0 = sd0 + 1 == RD ? 0 : sd0 + 1;
         }
     }
 
-    // acc[t][v] of lane l = sum over its block's pixels of dy[k = v] * x[c = l%4].
-    // Sum the 16 blocks (lanes with equal l%4), in a fixed butterfly order.
+    // acc[kq][cq][t][v] of lane l = sum over its block's pixels of
+    // dy[k = 4 kq + v] * x[c = 4 cq + l%4]. Sum the 16 blocks (lanes with
+    // equal l%4), in a fixed butterfly order.
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float sum = acc[t][v];
-            sum += __shfl_xor(sum, 4, 64);
-            sum += __shfl_xor(sum, 8, 64);
-            sum += __shfl_xor(sum, 16, 64);
-            sum += __shfl_xor(sum, 32, 64);
-            acc[t][v] = sum;
-        }
+        for (int cq = 0; cq < CQ; ++cq)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float sum = acc[kq][cq][t][v];
+                    sum += __shfl_xor(sum, 4, 64);
+                    sum += __shfl_xor(sum, 8, 64);
+                    sum += __shfl_xor(sum, 16, 64);
+                    sum += __shfl_xor(sum, 32, 64);
+                    acc[kq][cq][t][v] = sum;
+                }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero rows landed before LDS is reused
     __syncthreads();
-    float* red = lds;  // [wave][t][k(4)][c(4)]
+    constexpr int KC = 16 * KQ * CQ;  // (k, c) pairs of the partial
+    float* red = lds;                 // [wave][k][c][t]
     if (lane < 4) {
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) red[(wave * T + t) * 16 + v * 4 + lane] = acc[t][v];
+            for (int cq = 0; cq < CQ; ++cq)
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        red[(wave * KC + (kq * 4 + v) * (4 * CQ) + cq * 4 + lane) * T + t] = acc[kq][cq][t][v];
     }
     __syncthreads();
     // Partial of this (unit run, group): [chunk][g][k][c][t].
-    float* out = a.ws + ((size_t)chunk * a.G + g) * (16 * T);
-    for (int e = tid; e < 16 * T; e += 256) {
-        const int t = e % T, kc = e / T;  // kc = k*4 + c
-        out[e] = ((red[(0 * T + t) * 16 + kc] + red[(1 * T + t) * 16 + kc]) +
-                  red[(2 * T + t) * 16 + kc]) +
-                 red[(3 * T + t) * 16 + kc];
-    }
+    float* out = a.ws + ((size_t)chunk * a.G + g) * (KC * T);
+    for (int e = tid; e < KC * T; e += 256)
+        out[e] = ((red[e] + red[KC * T + e]) + red[2 * KC * T + e]) + red[3 * KC * T + e];
 }
 
 // dw[g*Kg + k, c, t] = sum over the (image, band) partial sets. Block = 16
@@ -1007,12 +1038,12 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_reduce(const float* __restric
 
 __global__ void __launch_bounds__(256) sg_wgrad_reduce(const float* __restrict__ ws,
                                                        float* __restrict__ dw, int nsets, int G,
-                                                       int Kg, int Cg, int T)
+                                                       int Kg, int Cg, int T, int K4, int C4)
 {
     __shared__ float part[16][17];
     const int el = threadIdx.x & 15, sg = threadIdx.x >> 4;
-    const int e = blockIdx.x * 16 + el;  // over G * 16 * T
-    const int per_set = G * 16 * T;
+    const int e = blockIdx.x * 16 + el;  // over G * K4 * C4 * T (partials of K4 x C4 channel pairs)
+    const int per_set = G * K4 * C4 * T;
     float sum = 0.f;
     if (e < per_set)
         for (int s = sg; s < nsets; s += 16) sum += ws[(size_t)s * per_set + e];
@@ -1022,8 +1053,8 @@ __global__ void __launch_bounds__(256) sg_wgrad_reduce(const float* __restrict__
     sum = part[0][el];
 #pragma unroll
     for (int i = 1; i < 16; ++i) sum += part[i][el];
-    const int t = e % T, kc = (e / T) % 16, g = e / (16 * T);
-    const int k = kc >> 2, c = kc & 3;
+    const int t = e % T, kc = (e / T) % (K4 * C4), g = e / (K4 * C4 * T);
+    const int k = kc / C4, c = kc - k * C4;
     if (k >= Kg || c >= Cg) return;
     dw[(((size_t)g * Kg + k) * Cg + c) * T + t] = sum;
 }
@@ -1341,41 +1372,90 @@ bool sgw_plan(const Shape& s, SgWArgs* out, bool* row64 = nullptr)
     return true;
 }
 
-// The streaming gradWeight kernel: same shapes as the row-per-DMA one. Bands
-// per image such that about 4096 waves have a unit each (four workgroups of
-// 28 KiB per CU, one round), bands of at least 8 rows; a wave takes several
-// units where there are more than 8192. One step of prefetch: on ResNeXt
-// 32x4d (64 images of 56 x 56) deeper rings cost resident workgroups and time
+// The streaming gradWeight kernel: 3x3, unit dilation, stride 1 or 2, up to 8
+// input and 8 output channels per group, every input column the outputs read
+// inside a 64-float row (rows of at most 62 outputs at stride 1, 31 at
+// stride 2). Bands per image such that the waves of one round of resident
+// workgroups have a unit each (ResNeXt 32x4d, 64 images of 56 x 56: 1024
+// workgroups of 28 KiB, four per CU), bands of at least 8 rows; a wave takes
+// several units where there are more than two rounds' worth. One step of
+// prefetch: on ResNeXt 32x4d deeper rings cost resident workgroups and time
 // (49.9 us at one step, 51.4 at two, 56.1 at three; the banded kernel 60.1).
 #ifndef GCONV_SG_WSTREAM_PF
 #define GCONV_SG_WSTREAM_PF 1
 #endif
 constexpr int kSgwStreamPF = GCONV_SG_WSTREAM_PF;
 
-bool sgw_stream_plan(const Shape& s, SgWStreamArgs* out)
+struct SgwStreamShape {
+    int S, CQ, KQ, nstep;
+    size_t lds;   // bytes per workgroup
+};
+
+bool sgw_stream_plan(const Shape& s, SgWStreamArgs* out, SgwStreamShape* shp = nullptr)
 {
 #ifdef GCONV_SG_NO_STREAM
-    (void)s; (void)out;
+    (void)s; (void)out; (void)shp;
     return false;
 #else
-    if (!(sgw_row64_ok(s) && s.Cg <= 4 && s.Kg <= 4 && s.N >= 1)) return false;
-    if ((int64_t)(s.Cg + 4) * s.H * s.W * 4 >= (int64_t(1) << 30)) return false;
-    if ((int64_t)(s.Kg + 4) * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
+    if (!(s.kh == 3 && s.kw == 3 && s.dh == 1 && s.dw == 1 && s.sh == s.sw && (s.sh == 1 || s.sh == 2))) return false;
+    if (!(s.Cg <= 8 && s.Kg <= 8 && s.N >= 1 && s.ph >= 0 && s.pw >= 0)) return false;
+    const int S = s.sh;
+    if (S == 1 ? s.Wo + 2 > 64 : 2 * s.Wo > 63) return false;
+    if ((int64_t)(s.Cg + 8) * s.H * s.W * 4 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)(s.Kg + 8) * s.Ho * s.Wo * 4 >= (int64_t(1) << 30)) return false;
+    SgwStreamShape sh;
+    sh.S = S;
+    sh.CQ = s.Cg <= 4 ? 1 : 2;
+    sh.KQ = s.Kg <= 4 ? 1 : 2;
+    sh.nstep = (s.Wo + 15) / 16;
+    constexpr int PF = kSgwStreamPF, CS = 72;
+    const int D = S == 1 ? 2 : 1;
+    const int RX = S * (D + 1 + PF), RD = PF + 1;
+    sh.lds = (size_t)4 * (RX * 4 * sh.CQ + RD * 4 * sh.KQ) * CS * 4;
+    const int per_cu = (int)std::min<size_t>(8, (160 * 1024) / sh.lds);
+    const int64_t waves = (int64_t)256 * per_cu * 4;
     SgWStreamArgs a{};
     a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
     a.G = s.G; a.Cg = s.Cg; a.Kg = s.Kg; a.ph = s.ph; a.pw = s.pw;
     const int64_t planes = (int64_t)s.N * s.G;
-    const int64_t want = (4096 + planes - 1) / planes;
-    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, s.Ho / 8)));
+    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(waves / planes, std::max(1, s.Ho / 8)));
     a.R = (s.Ho + nb - 1) / nb;
     a.nbands = (s.Ho + a.R - 1) / a.R;
     const int64_t units = (int64_t)s.N * a.nbands;  // per group
-    a.upw = (int)std::max<int64_t>(1, (units * s.G + 8191) / 8192);
+    a.upw = (int)std::max<int64_t>(1, (units * s.G + 2 * waves - 1) / (2 * waves));
     a.nchunks = (int)((units + 4 * a.upw - 1) / (4 * a.upw));
     if ((int64_t)a.nchunks * s.G >= (1 << 30)) return false;
     if (out) *out = a;
+    if (shp) *shp = sh;
     return true;
 #endif
+}
+
+template <int S, int CQ, int KQ>
+void sgw_stream_launch(const SgWStreamArgs& a, const SgwStreamShape& sh, int blocks, hipStream_t st)
+{
+    constexpr int PF = kSgwStreamPF;
+    switch (sh.nstep) {
+        case 1: hipLaunchKernelGGL((sg_wgrad_stream_kernel<1, PF, S, CQ, KQ>), dim3(blocks), dim3(256), sh.lds, st, a); break;
+        case 2: hipLaunchKernelGGL((sg_wgrad_stream_kernel<2, PF, S, CQ, KQ>), dim3(blocks), dim3(256), sh.lds, st, a); break;
+        case 3:
+            if constexpr (S == 1)
+                hipLaunchKernelGGL((sg_wgrad_stream_kernel<3, PF, S, CQ, KQ>), dim3(blocks), dim3(256), sh.lds, st, a);
+            break;
+        default:
+            if constexpr (S == 1)
+                hipLaunchKernelGGL((sg_wgrad_stream_kernel<4, PF, S, CQ, KQ>), dim3(blocks), dim3(256), sh.lds, st, a);
+            break;
+    }
+}
+
+void sgw_stream_dispatch(const SgWStreamArgs& a, const SgwStreamShape& sh, int blocks, hipStream_t st)
+{
+#define SGW_CASE(s_, cq, kq) \
+    if (sh.S == s_ && sh.CQ == cq && sh.KQ == kq) return sgw_stream_launch<s_, cq, kq>(a, sh, blocks, st);
+    SGW_CASE(1, 1, 1) SGW_CASE(1, 1, 2) SGW_CASE(1, 2, 1) SGW_CASE(1, 2, 2)
+    SGW_CASE(2, 1, 1) SGW_CASE(2, 1, 2) SGW_CASE(2, 2, 1) SGW_CASE(2, 2, 2)
+#undef SGW_CASE
 }
 
 }  // namespace
@@ -1468,7 +1548,7 @@ bool smallgroup_bwd_data_supported(const Shape& s)
     return sg_dw_dgrad_s2_plan(s, nullptr) || sg_problem_ok(sg_bwd_data_problem(s, nullptr, nullptr, nullptr));
 }
 
-bool smallgroup_bwd_filter_supported(const Shape& s) { return sgw_plan(s, nullptr); }
+bool smallgroup_bwd_filter_supported(const Shape& s) { return sgw_stream_plan(s, nullptr) || sgw_plan(s, nullptr); }
 
 size_t smallgroup_bwd_filter_workspace(const Shape& s)
 {
@@ -1476,7 +1556,8 @@ size_t smallgroup_bwd_filter_workspace(const Shape& s)
     int mq;
     if (sg_dw_wgrad_plan(s, &da, &mq)) return (size_t)da.nruns * s.G * mq * 9 * sizeof(float);
     SgWStreamArgs sa;
-    if (sgw_stream_plan(s, &sa)) return (size_t)sa.nchunks * s.G * 16 * 9 * sizeof(float);
+    SgwStreamShape sh;
+    if (sgw_stream_plan(s, &sa, &sh)) return (size_t)sa.nchunks * s.G * 16 * sh.CQ * sh.KQ * 9 * sizeof(float);
     SgWArgs a;
     bool row64 = false;
     if (!sgw_plan(s, &a, &row64)) return 0;
@@ -1523,19 +1604,13 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
         return true;
     }
     SgWStreamArgs sa;
-    if (sgw_stream_plan(s, &sa)) {
+    SgwStreamShape sh;
+    if (sgw_stream_plan(s, &sa, &sh)) {
         sa.x = x; sa.dy = dy; sa.ws = ws;
-        constexpr int PF = kSgwStreamPF;
-        const size_t lds = (size_t)4 * ((PF + 3) + (PF + 1)) * 4 * 72 * 4;
-        const int nstep = (s.Wo + 15) / 16;
-        const int blocks = sa.nchunks * s.G;
-        if (nstep == 1) hipLaunchKernelGGL((sg_wgrad_stream_kernel<1, PF>), dim3(blocks), dim3(256), lds, st, sa);
-        else if (nstep == 2) hipLaunchKernelGGL((sg_wgrad_stream_kernel<2, PF>), dim3(blocks), dim3(256), lds, st, sa);
-        else if (nstep == 3) hipLaunchKernelGGL((sg_wgrad_stream_kernel<3, PF>), dim3(blocks), dim3(256), lds, st, sa);
-        else hipLaunchKernelGGL((sg_wgrad_stream_kernel<4, PF>), dim3(blocks), dim3(256), lds, st, sa);
-        const int total = s.G * 16 * 9;
+        sgw_stream_dispatch(sa, sh, sa.nchunks * s.G, st);
+        const int total = s.G * 16 * sh.CQ * sh.KQ * 9;
         hipLaunchKernelGGL(sg_wgrad_reduce, dim3((total + 15) / 16), dim3(256), 0, st, ws, dw,
-                           sa.nchunks, s.G, s.Kg, s.Cg, 9);
+                           sa.nchunks, s.G, s.Kg, s.Cg, 9, 4 * sh.KQ, 4 * sh.CQ);
         return true;
     }
     SgWArgs a;
@@ -1556,7 +1631,7 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
         else hipLaunchKernelGGL(sg_wgrad_row64_kernel<4>, dim3(rblocks), dim3(256), lds, st, a);
         const int total = s.G * 16 * T;
         hipLaunchKernelGGL(sg_wgrad_reduce, dim3((total + 15) / 16), dim3(256), 0, st, ws, dw,
-                           a.nruns, s.G, s.Kg, s.Cg, T);
+                           a.nruns, s.G, s.Kg, s.Cg, T, 4, 4);
         return true;
     } else {
         const size_t lds =
@@ -1565,7 +1640,7 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
     }
     const int total = s.G * 16 * T;
     hipLaunchKernelGGL(sg_wgrad_reduce, dim3((total + 15) / 16), dim3(256), 0, st, ws, dw,
-                       s.N * a.nbands, s.G, s.Kg, s.Cg, T);
+                       s.N * a.nbands, s.G, s.Kg, s.Cg, T, 4, 4);
     return true;
 }
 

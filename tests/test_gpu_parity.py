@@ -710,9 +710,10 @@ EDGE_CASES = [
     (dict(N=37, C=128, K=128, H=13, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=32),
      {"fwd": "smallgroup", "bwd_data": "smallgroup", "bwd_filter": "smallgroup"}),
     # ... the widest tile with pad 2 (60 + 2 columns), 3 in / 7 out channels
-    # per group (two output quads, the second partial)
+    # per group (two output quads, the second partial; gradWeight streams one
+    # input and two output quads)
     (dict(N=3, C=2 * 3, K=2 * 7, H=9, W=60, kh=3, kw=3, sh=1, sw=1, ph=1, pw=2, dh=1, dw=1, G=2),
-     {"fwd": "smallgroup", "bwd_data": "direct", "bwd_filter": "direct"}),
+     {"fwd": "smallgroup", "bwd_data": "direct", "bwd_filter": "smallgroup"}),
     # ... gradInput with 3 in / 6 out channels per group
     (dict(N=2, C=2 * 6, K=2 * 3, H=7, W=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2),
      {"bwd_data": "smallgroup"}),
@@ -725,10 +726,30 @@ EDGE_CASES = [
     # ... and two input channels per group at stride 2, unequal padding
     (dict(N=3, C=4, K=6, H=15, W=11, kh=5, kw=5, sh=2, sw=2, ph=1, pw=2, dh=1, dw=1, G=2),
      {"fwd": "smallgroup", "bwd_data": "direct", "bwd_filter": "direct"}),
-    # 8 in / 8 out channels per group (ResNeXt's second stage): one 16-wide MFMA
-    # fragment half used on forward and gradInput; gradWeight stays direct
+    # 8 in / 8 out channels per group (ResNeXt's second stage): two groups per
+    # 16-wide MFMA fragment on forward and gradInput; gradWeight streams 2 x 2
+    # channel quads on the 4x4 MFMA blocks
     (dict(N=2, C=64, K=64, H=20, W=20, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8),
-     {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "direct"}),
+     {"fwd": "igemm", "bwd_data": "igemm", "bwd_filter": "smallgroup"}),
+    # streaming small-group gradWeight at stride 2: 8 x 8 channels per group
+    # (ResNeXt's strided 3x3), 15 outputs a row ...
+    (dict(N=3, C=32, K=32, H=28, W=30, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=4),
+     {"bwd_filter": "smallgroup"}),
+    # ... the widest strided row (31 outputs over 61 + 1 columns), odd height
+    (dict(N=5, C=16, K=16, H=23, W=61, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=4),
+     {"bwd_filter": "smallgroup"}),
+    # ... 8 in / 4 out channels, no padding
+    (dict(N=2, C=16, K=8, H=20, W=24, kh=3, kw=3, sh=2, sw=2, ph=0, pw=0, dh=1, dw=1, G=2),
+     {"bwd_filter": "smallgroup"}),
+    # ... at stride 1: 5 in / 3 out channels, pad 2
+    (dict(N=2, C=10, K=6, H=17, W=33, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=2),
+     {"bwd_filter": "smallgroup"}),
+    # ... two units a wave (more units than two rounds of resident waves): 4 x 4
+    # channels over 400 images, and 8 x 8 over 600
+    (dict(N=400, C=128, K=128, H=8, W=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=32),
+     {"bwd_filter": "smallgroup"}),
+    (dict(N=600, C=64, K=64, H=8, W=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8),
+     {"bwd_filter": "smallgroup"}),
     # strided gradInput on the direct kernel (taps filtered once per element,
     # channels of the group innermost): 6 channels per group, stride 2; 2 per
     # group, strides 3 and 2 with dilation
