@@ -907,7 +907,7 @@ struct FlatInst {
     X(1, mo, wo, wpx, mp, nsx) X(2, mo, wo, wpx, mp, nsx) X(3, mo, wo, wpx, mp, nsx)
 #define GCONV_SP_INSTS(X)                                                     \
     GCONV_SP_SHAPES(X, 1, 1, 4, 4, 12) GCONV_SP_SHAPES(X, 1, 2, 2, 4, 8)       \
-    GCONV_SP_SHAPES(X, 1, 4, 1, 5, 8) GCONV_SP_SHAPES(X, 2, 4, 1, 4, 12)
+    GCONV_SP_SHAPES(X, 1, 4, 1, 5, 8) GCONV_SP_SHAPES(X, 2, 4, 1, 4, 12) GCONV_SP_SHAPES(X, 2, 1, 4, 4, 12)
 #define GCONV_FLAT_ENTRY(t, k, mo, wo, wpx, mp, nsx) {t, mo, wo, wpx, mp, nsx, k, k, false},
 #define GCONV_SP_ENTRY(k, mo, wo, wpx, mp, nsx) {k * k, mo, wo, wpx, mp, nsx, k, k, true},
 constexpr FlatInst kFlatInsts[] = {GCONV_FLAT_INSTS(GCONV_FLAT_ENTRY) GCONV_SP_INSTS(GCONV_SP_ENTRY)};
@@ -930,12 +930,19 @@ bool flat_plan(const Problem& p_in, FlatPlan& fp)
         return false;
     }
     const int nfrag = (p.Cout_g + 15) / 16;
-    const int mo = nfrag > 4 ? 2 : 1;
+    const int mo0 = nfrag > 4 ? 2 : 1;
     // waves across output channels (sub-pixel instances: 1, 2 or 4)
-    const int wo = nfrag > 4 ? 4 : (p.sp && nfrag == 3) ? 4 : nfrag;
+    const int wo0 = nfrag > 4 ? 4 : (p.sp && nfrag == 3) ? 4 : nfrag;
+    // Sub-pixel form with two fragments (8 channels per group at stride 2):
+    // one wave takes both over 256 pixels where the images hold that many,
+    // so each workgroup's set-up (DMA offsets, tap map, store addresses)
+    // serves twice the MFMAs; else the two-wave layout.
+    const bool wide = p.sp && nfrag == 2;
     const FlatInst* inst = nullptr;
     int64_t plane = 0, nseg = 0, LW = 0, P = (int64_t)p.Hout * p.Wout;
+    for (int pass = wide ? 0 : 1; pass < 2 && !inst; ++pass)
     for (const FlatInst& fi : kFlatInsts) {
+        const int mo = pass == 0 ? 2 : mo0, wo = pass == 0 ? 1 : wo0;
         if (!(fi.KH == p.kh && fi.KW == p.kw && fi.SP == p.sp && fi.MO == mo && fi.WO == wo))
             continue;
         const int NWi = fi.WO * fi.WPX;
@@ -946,7 +953,11 @@ bool flat_plan(const Problem& p_in, FlatPlan& fp)
         const int LR = std::max((R - 1) * p.sh + halo, (R - 2) * p.sh + 2 * halo);
         LW = (int64_t)(p.Wout - 1) * p.sw + (p.kw - 1) * p.dw + 1;
         plane = LR * LW;
-        plane = ((plane + 47) / 64) * 64 + 16;  // == 16 (mod 64): the 4 lane groups hit distinct banks
+        // == 16 (mod 64): the 4 lane groups hit distinct banks. At column
+        // stride 2 a fragment's 16 pixels read every other float (16 even
+        // banks), so an odd plane puts the other channel lane of each
+        // half-wave on the odd banks.
+        plane = p.sw == 2 && !p.in_nhwc ? ((plane + 63) / 64) * 64 + 1 : ((plane + 47) / 64) * 64 + 16;
         // channels-last input: one 16-byte DMA lane per pixel of the LR x LW tile
         nseg = p.in_nhwc ? (LR * LW + 64 * NWi - 1) / (64 * NWi) : (4 * plane + 64 * NWi - 1) / (64 * NWi);
         // (16 bytes a lane in the channels-last form, so its double buffer must

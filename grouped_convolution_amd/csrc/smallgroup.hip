@@ -848,7 +848,12 @@ __global__ void __launch_bounds__(256, (CQ * KQ > 1 ? 2 : 1)) sg_wgrad_stream_ke
 
     // acc[kq][cq][t][v] of lane l = sum over its block's pixels of
     // dy[k = 4 kq + v] * x[c = 4 cq + l%4]. Sum the 16 blocks (lanes with
-    // equal l%4), in a fixed butterfly order.
+    // equal l%4), in a fixed butterfly order, each sum going straight to this
+    // wave's own LDS slice (its rings are idle once the tail's zero rows have
+    // landed), so the accumulators die one by one.
+    constexpr int KC = 16 * KQ * CQ;  // (k, c) pairs of the partial
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    float* red = xring;               // [k][c][t] of this wave
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
@@ -862,28 +867,13 @@ __global__ void __launch_bounds__(256, (CQ * KQ > 1 ? 2 : 1)) sg_wgrad_stream_ke
                     sum += __shfl_xor(sum, 8, 64);
                     sum += __shfl_xor(sum, 16, 64);
                     sum += __shfl_xor(sum, 32, 64);
-                    acc[kq][cq][t][v] = sum;
+                    if (lane < 4) red[((kq * 4 + v) * (4 * CQ) + cq * 4 + lane) * T + t] = sum;
                 }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero rows landed before LDS is reused
     __syncthreads();
-    constexpr int KC = 16 * KQ * CQ;  // (k, c) pairs of the partial
-    float* red = lds;                 // [wave][k][c][t]
-    if (lane < 4) {
-#pragma unroll
-        for (int kq = 0; kq < KQ; ++kq)
-#pragma unroll
-            for (int cq = 0; cq < CQ; ++cq)
-#pragma unroll
-                for (int t = 0; t < T; ++t)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        red[(wave * KC + (kq * 4 + v) * (4 * CQ) + cq * 4 + lane) * T + t] = acc[kq][cq][t][v];
-    }
-    __syncthreads();
-    // Partial of this (unit run, group): [chunk][g][k][c][t].
+    // Partial of this (unit run, group): [chunk][g][k][c][t], the waves added in order.
     float* out = a.ws + ((size_t)chunk * a.G + g) * (KC * T);
     for (int e = tid; e < KC * T; e += 256)
-        out[e] = ((red[e] + red[KC * T + e]) + red[2 * KC * T + e]) + red[3 * KC * T + e];
+        out[e] = ((lds[e] + lds[WLDS + e]) + lds[2 * WLDS + e]) + lds[3 * WLDS + e];
 }
 
 // dw[g*Kg + k, c, t] = sum over the (image, band) partial sets. Block = 16
