@@ -304,8 +304,11 @@ __device__ __forceinline__ float swap_pair(float v)
 // holds each pixel's 4 chunk channels together ([row][col][4]), filled by
 // 16-byte DMA (one pixel per lane), and a fragment's 16 pixels x 4 channels
 // read 64 consecutive floats.
+// PK: packed groups (pk_o > 0; instances with one fragment and one wave
+// across the output channels only), so the filter addressing of unpacked
+// launches carries none of it.
 template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, int MINW, bool INH = false,
-          bool SP = false>
+          bool SP = false, bool PK = false>
 __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlatArgs a)
 {
     constexpr int T = KH * KW;
@@ -392,13 +395,17 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
     const float* w_g = a.wgt + (size_t)g * a.w_gstride;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_g, (uint32_t)a.w_gstride * 4u);
     int wbase[MO];  // -1: output channel past the group end
-    int osub[MO];   // packed groups: the real group of the output channel
+    int osub[PK ? MO : 1];  // packed groups: the real group of the output channel
     int soff[SP ? MO : 1][SP ? T : 1];  // sub-pixel form: stored tap of each super-tap, -1 none
 #pragma unroll
     for (int m = 0; m < MO; ++m) {
         const int o = o0 + (wo_i * MO + m) * 16 + l16;
-        osub[m] = a.pk_o ? o / a.pk_o : 0;
-        wbase[m] = o >= a.Cout_g ? -1 : a.pk_o ? osub[m] * a.w_gs + (o - osub[m] * a.pk_o) * a.w_so : o * a.w_so;
+        if constexpr (PK) {
+            osub[m] = o / a.pk_o;
+            wbase[m] = o >= a.Cout_g ? -1 : osub[m] * a.w_gs + (o - osub[m] * a.pk_o) * a.w_so;
+        } else {
+            wbase[m] = o >= a.Cout_g ? -1 : o * a.w_so;
+        }
         if constexpr (SP) {
             const int c = o / (a.o_sh * a.o_sw), rem = o - c * (a.o_sh * a.o_sw);
             const int du = rem / a.o_sw, dv = rem - du * a.o_sw;
@@ -429,16 +436,19 @@ __global__ void __launch_bounds__(64 * WO * WPX, MINW) conv_flat_kernel(ConvFlat
             }
             return;
         }
-        // packed groups: filter values across real groups are 0
-        const int rsub = a.pk_o ? r / a.pk_r : 0;
-        const int rr = r - rsub * a.pk_r;
 #pragma unroll
         for (int m = 0; m < MO; ++m) {
             // One select per fragment; the tap offsets then ride on the
             // instruction's immediate offset (out-of-range stays out of range).
-            const uint32_t base = (r < a.Cin_g && wbase[m] >= 0 && rsub == osub[m])
-                                      ? (uint32_t)(wbase[m] + rr * a.w_sr) * 4u
-                                      : kOOB;
+            uint32_t base;
+            if constexpr (PK) {
+                // packed groups: filter values across real groups are 0
+                const int rsub = r / a.pk_r, rr = r - rsub * a.pk_r;
+                base = (r < a.Cin_g && wbase[m] >= 0 && rsub == osub[m]) ? (uint32_t)(wbase[m] + rr * a.w_sr) * 4u
+                                                                          : kOOB;
+            } else {
+                base = (r < a.Cin_g && wbase[m] >= 0) ? (uint32_t)(wbase[m] + r * a.w_sr) * 4u : kOOB;
+            }
 #pragma unroll
             for (int t = 0; t < T; ++t) b[m][t] = load_f32(rw, base + (uint32_t)t * 4u);
         }
@@ -992,11 +1002,12 @@ bool flat_plan(const Problem& p_in, FlatPlan& fp)
     return true;
 }
 
-template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, bool INH, bool SP = false>
+template <int KH, int KW, int MP, int MO, int WO, int WPX, int NSX, bool FLIP, bool INH, bool SP = false,
+          bool PK = false>
 void launch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
 {
     constexpr int MINW = (KH * KW <= 9) ? 4 : 2;
-    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW, INH, SP>;
+    auto kern = conv_flat_kernel<KH, KW, MP, MO, WO, WPX, NSX, FLIP, MINW, INH, SP, PK>;
     hipLaunchKernelGGL(kern, dim3(fp.blocks), dim3(64 * WO * WPX), fp.lds_bytes, st, a);
 }
 
@@ -1020,8 +1031,15 @@ bool dispatch_flat(const ConvFlatArgs& a, const FlatPlan& fp, hipStream_t st)
     const FlatInst& i = fp.inst;
 #define GCONV_FLAT_CASE(t, k, mo, wo, wpx, mp, nsx)                                     \
     if (!i.SP && i.T == t && i.MO == mo && i.WO == wo && i.WPX == wpx && i.MP == mp && i.NSX == nsx) { \
-        launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP, INH>(a, fp, st);                  \
-        return true;                                                                   \
+        if (!a.pk_o) {                                                                 \
+            launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP, INH>(a, fp, st);              \
+            return true;                                                               \
+        }                                                                              \
+        if constexpr (mo == 1 && wo == 1) {                                            \
+            launch_flat<k, k, mp, mo, wo, wpx, nsx, FLIP, INH, false, true>(a, fp, st); \
+            return true;                                                               \
+        }                                                                              \
+        return false;                                                                  \
     }
     GCONV_FLAT_INSTS(GCONV_FLAT_CASE)
 #undef GCONV_FLAT_CASE
