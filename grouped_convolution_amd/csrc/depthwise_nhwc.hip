@@ -289,7 +289,8 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
     const int cq = t - lp * a.CQ;
     const bool active = lp < a.NP;
     const int c = cq * 4;
-    const int p0 = blockIdx.x * a.slice, p1 = min(a.total, p0 + a.slice);
+    const int sl = blockIdx.x;
+    const int p0 = sl * a.slice, p1 = min(a.total, p0 + a.slice);
     float acc[4 * T];
 #pragma unroll
     for (int e = 0; e < 4 * T; ++e) acc[e] = 0.f;
@@ -365,7 +366,7 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
     }
     __syncthreads();
     // Thread e < C*T adds the NP lanes' sums of output e = c*T + tap in order.
-    float* out = a.out + (size_t)blockIdx.x * a.C * T;
+    float* out = a.out + (size_t)sl * a.C * T;
     for (int e = t; e < a.C * T; e += 256) {
         const int ch = e / T, tap = e - (e / T) * T;
         const int off = (ch >> 2) * (4 * T) + (ch & 3) * T + tap;
@@ -375,23 +376,32 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
     }
 }
 
-// dw[e] = sum over slices (in order) of ws[slice][e]: 16 outputs x 16 slice
-// groups per block, the group sums added in order.
-__global__ void __launch_bounds__(256) dw_nhwc_wgrad_reduce(const float* __restrict__ ws, float* __restrict__ dw,
-                                                            int E, int nslice)
+// dw[e] = sum over slices (in order) of ws[slice][e]: 16 outputs x 64 slice
+// groups per 1024-thread block; thread (e, sg) adds slices sg, sg + 64, ... in
+// order (16 loads in flight), then the 64 group sums are added in order.
+__global__ void __launch_bounds__(1024) dw_nhwc_wgrad_reduce(const float* __restrict__ ws, float* __restrict__ dw,
+                                                             int E, int nslice)
 {
-    __shared__ float part[16][17];
+    __shared__ float part[64][17];
     const int el = threadIdx.x & 15, sg = threadIdx.x >> 4;
     const int e = blockIdx.x * 16 + el;
     float sum = 0.f;
-    if (e < E)
-        for (int k = sg; k < nslice; k += 16) sum += ws[(size_t)k * E + e];
+    if (e < E) {
+        int k = sg;
+        for (; k + 15 * 64 < nslice; k += 16 * 64) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = ws[(size_t)(k + u * 64) * E + e];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) sum += v[u];
+        }
+        for (; k < nslice; k += 64) sum += ws[(size_t)k * E + e];
+    }
     part[sg][el] = sum;
     __syncthreads();
     if (sg != 0 || e >= E) return;
     sum = part[0][el];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) sum += part[i][el];
+    for (int i = 1; i < 64; ++i) sum += part[i][el];
     dw[e] = sum;
 }
 
@@ -468,7 +478,7 @@ bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* 
     }
     if (ns > 1) {
         const int E = s.C * T;
-        hipLaunchKernelGGL(dw_nhwc_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, E, ns);
+        hipLaunchKernelGGL(dw_nhwc_wgrad_reduce, dim3((E + 15) / 16), dim3(1024), 0, st, ws, dw, E, ns);
     }
     return true;
 }
