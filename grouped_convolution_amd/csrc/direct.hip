@@ -139,6 +139,138 @@ direct_bwd_filter_kernel(Shape s, const float* __restrict__ x, const float* __re
     }
 }
 
+// Small problems (a few hundred KB: the whole layer fits the caches many
+// times over) are bound by the latency of their longest dependent chain, not
+// by bandwidth; the kernels below trade every staging step for parallelism.
+//
+// Forward: eight lanes per output (consecutive lanes), lane q taking input
+// channels q, q + 8, ..., three channels' taps loaded at once (the data is cold:
+// each dependent round of loads costs an HBM latency); the eight partial sums
+// are combined by a fixed butterfly, so the result does not depend on
+// scheduling.
+template <int KS>
+__global__ void __launch_bounds__(kBlock) direct_small_fwd_kernel(Shape s, const float* __restrict__ x,
+                                                                  const float* __restrict__ w,
+                                                                  const float* __restrict__ bias,
+                                                                  float* __restrict__ y)
+{
+    const int64_t gt = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t e = gt >> 3;
+    const int q = (int)(gt & 7);
+    const bool live = e < s.y_elems;
+    float acc = 0.f;
+    int k = 0;
+    if (live) {
+        const int wo = (int)(e % s.Wo);
+        int64_t t = e / s.Wo;
+        const int ho = (int)(t % s.Ho);
+        t /= s.Ho;
+        k = (int)(t % s.K);
+        const int64_t n = t / s.K;
+        const int g = k / s.Kg;
+        const int64_t HW = (int64_t)s.H * s.W;
+        const float* xg = x + (n * s.C + (int64_t)g * s.Cg) * HW;
+        const float* wk = w + (int64_t)k * s.Cg * KS * KS;
+        for (int c0 = q; c0 < s.Cg; c0 += 24) {
+            float xv[3][KS * KS], wv[3][KS * KS];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int c = c0 + 8 * u;
+                const bool cok = c < s.Cg;
+                const float* xc = xg + c * HW;
+                const float* wc = wk + c * KS * KS;
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    const int h = ho * s.sh - s.ph + i * s.dh;
+                    const bool hok = cok && (unsigned)h < (unsigned)s.H;
+#pragma unroll
+                    for (int j = 0; j < KS; ++j) {
+                        const int ww = wo * s.sw - s.pw + j * s.dw;
+                        const bool ok = hok && (unsigned)ww < (unsigned)s.W;
+                        xv[u][i * KS + j] = ok ? xc[(int64_t)h * s.W + ww] : 0.f;
+                        wv[u][i * KS + j] = ok ? wc[i * KS + j] : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 3; ++u)
+#pragma unroll
+                for (int t = 0; t < KS * KS; ++t) acc = fmaf(wv[u][t], xv[u][t], acc);
+        }
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    if (live && q == 0) {
+        if (bias) acc += bias[k];
+        y[e] = relu_if(acc, s.relu);
+    }
+}
+
+// gradWeight: one 1024-thread block per (output channel k, input channel c)
+// pair, all KS*KS taps in registers; threads stride over the N*Ho*Wo pixels
+// (about one each at the target sizes), then each tap's sum goes through a
+// fixed-order tree (wave butterfly, the 16 waves in index order).
+constexpr int kSmallWgradBlock = 1024;
+template <int KS>
+__global__ void __launch_bounds__(kSmallWgradBlock) direct_small_wgrad_kernel(Shape s, const float* __restrict__ x,
+                                                                               const float* __restrict__ dy,
+                                                                               float* __restrict__ dw)
+{
+    constexpr int T = KS * KS, NWV = kSmallWgradBlock / 64;
+    __shared__ float part[NWV][T];
+    const int kc = blockIdx.x;                 // k * Cg + c
+    const int k = kc / s.Cg, c = kc - k * s.Cg;
+    const int g = k / s.Kg;
+    const int P = s.Ho * s.Wo;
+    const int64_t HW = (int64_t)s.H * s.W;
+    const int total = s.N * P;
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.f;
+    // Two pixels a pass, their loads issued together.
+    for (int pix0 = threadIdx.x; pix0 < total; pix0 += 2 * kSmallWgradBlock) {
+        float d[2], xv[2][T];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pix = pix0 + u * kSmallWgradBlock;
+            const bool pok = pix < total;
+            const int n = pok ? pix / P : 0, p = pix - n * P;
+            const int ho = p / s.Wo, wo = p - ho * s.Wo;
+            d[u] = pok ? dy[((int64_t)n * s.K + k) * P + p] : 0.f;
+            const float* xc = x + ((int64_t)n * s.C + (int64_t)g * s.Cg + c) * HW;
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+                const int h = ho * s.sh - s.ph + i * s.dh;
+                const bool hok = pok && (unsigned)h < (unsigned)s.H;
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    const int ww = wo * s.sw - s.pw + j * s.dw;
+                    xv[u][i * KS + j] = (hok && (unsigned)ww < (unsigned)s.W) ? xc[(int64_t)h * s.W + ww] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < T; ++t) acc[t] = fmaf(d[u], xv[u][t], acc[t]);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        float v = acc[t];
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) part[wave][t] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < T) {
+        const int t = threadIdx.x;
+        float sum = part[0][t];
+        for (int wv = 1; wv < NWV; ++wv) sum += part[wv][t];
+        dw[(int64_t)kc * T + t] = sum;
+    }
+}
+
 __global__ void __launch_bounds__(kBlock) fill_zero_kernel(float* p, int64_t count)
 {
     for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < count;
@@ -154,10 +286,30 @@ unsigned grid_for(int64_t total)
 
 }  // namespace
 
+// Small enough that latency, not bandwidth or arithmetic, sets the time: a
+// few tens of thousands of outputs (the NNlib benchmark's grouped layer:
+// 2 x 15 x 26 x 26), square 3x3 or 5x5 filters.
+static bool small_fwd(const Shape& s)
+{
+    return s.kh == s.kw && (s.kh == 3 || s.kh == 5) && s.y_elems <= (1 << 16) && s.Cg >= 4;
+}
+static bool small_bwd_data(const Shape& s) { return s.x_elems <= (1 << 18) && s.Kg * s.kh * s.kw <= 64; }
+static bool small_wgrad(const Shape& s)
+{
+    return s.kh == s.kw && (s.kh == 3 || s.kh == 5) && (int64_t)s.N * s.Ho * s.Wo <= 4096 &&
+           (int64_t)s.K * s.Cg >= 128 && (int64_t)s.K * s.Cg < (1 << 30);
+}
+
 void direct_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y,
                 hipStream_t st)
 {
     if (s.y_elems == 0) return;
+    if (small_fwd(s)) {
+        const unsigned blocks = (unsigned)((s.y_elems * 8 + kBlock - 1) / kBlock);
+        if (s.kh == 3) hipLaunchKernelGGL((direct_small_fwd_kernel<3>), dim3(blocks), dim3(kBlock), 0, st, s, x, w, bias, y);
+        else hipLaunchKernelGGL((direct_small_fwd_kernel<5>), dim3(blocks), dim3(kBlock), 0, st, s, x, w, bias, y);
+        return;
+    }
     if (direct_tile_fwd(s, x, w, bias, y, st)) return;
     hipLaunchKernelGGL(direct_fwd_kernel, dim3(grid_for(s.y_elems)), dim3(kBlock), 0, st, s, x,
                        w, bias, y);
@@ -166,16 +318,29 @@ void direct_fwd(const Shape& s, const float* x, const float* w, const float* bia
 void direct_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
     if (s.x_elems == 0) return;
-    if (direct_tile_bwd_data(s, dy, w, dx, st)) return;
+    if (!small_bwd_data(s) && direct_tile_bwd_data(s, dy, w, dx, st)) return;
     hipLaunchKernelGGL(direct_bwd_data_kernel, dim3(grid_for(s.x_elems)), dim3(kBlock), 0, st, s,
                        dy, w, dx);
 }
 
-size_t direct_bwd_filter_workspace(const Shape& s) { return direct_tile_bwd_filter_workspace(s); }
+size_t direct_bwd_filter_workspace(const Shape& s)
+{
+    return small_wgrad(s) ? 0 : direct_tile_bwd_filter_workspace(s);
+}
 
 void direct_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws,
                        hipStream_t st)
 {
+    if (small_wgrad(s)) {
+        if (s.N == 0) {
+            fill_zero(dw, s.w_elems, st);
+            return;
+        }
+        const unsigned blocks = (unsigned)((int64_t)s.K * s.Cg);
+        if (s.kh == 3) hipLaunchKernelGGL((direct_small_wgrad_kernel<3>), dim3(blocks), dim3(kSmallWgradBlock), 0, st, s, x, dy, dw);
+        else hipLaunchKernelGGL((direct_small_wgrad_kernel<5>), dim3(blocks), dim3(kSmallWgradBlock), 0, st, s, x, dy, dw);
+        return;
+    }
     if (direct_tile_bwd_filter(s, x, dy, dw, ws, st)) return;
     const int64_t blocks = s.w_elems < (1 << 20) ? s.w_elems : (1 << 20);
     hipLaunchKernelGGL(direct_bwd_filter_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, s,
