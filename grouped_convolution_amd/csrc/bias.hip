@@ -44,12 +44,13 @@ struct BiasArgs {
 // Plane layout: workgroup (s, k) sums values [s*chunk, (s+1)*chunk) of
 // channel k's N planes, then the four wave sums are added in order. A thread
 // keeps U loads in flight: 8 of 16 bytes, or 32 of 4 bytes when the planes
-// are not whole float4s (either way 32 KB per workgroup, which is what keeps
-// a CU's share of the HBM bandwidth busy).
+// are not whole float4s (either way 32 KB per 256-thread workgroup, which is
+// what keeps a CU's share of the HBM bandwidth busy); the one-pass form's
+// 1024 threads keep 16 each (256 KB: one CU streams a whole channel).
 template <bool VEC, int NT>
 __global__ void __launch_bounds__(NT) bias_planes(BiasArgs a)
 {
-    constexpr int U = VEC ? 8 : 32;
+    constexpr int U = VEC ? (NT == 1024 ? 16 : 8) : 32;  // 16 a thread for the one-pass form
     constexpr int NW = NT / 64;
     __shared__ float red[NW];
     const int s = blockIdx.x, k = blockIdx.y;
@@ -248,7 +249,20 @@ Plan make_plan(const Shape& s, bool ptr_aligned)
         // channels: 22.6 against 24.2 us).
         const int64_t floats = (int64_t)s.N * P;
         int64_t S0 = std::max<int64_t>(1, std::min<int64_t>((kTargetBlocks + s.K - 1) / s.K, floats / 8192));
-        if (S0 <= 2) S0 = 1;
+        // One 1024-thread workgroup per channel (no second launch) where
+        // that is faster by a model fitted on the box: a lone CU streams about
+        // 36 GB/s, a split reduction about 5.5 TB/s plus a finalize launch of
+        // about 4 us. 144 channels of 56 x 56 (or 28 x 28) take the single
+        // pass (26.7 -> 24.5 us, 11.4 -> 9.7 us); 64 and 128 channels keep the
+        // split (10.7 against 12.8 us, 22.4 against 23.7 us).
+        if (S0 > 2) {
+            const double bytes = (double)floats * 4.0;
+            const double single = bytes / 36e9 * (double)((s.K + 255) / 256) + 1.5e-6;
+            const double split = bytes * s.K / 5.5e12 + 4.7e-6;
+            if (single < split) S0 = 1;
+        } else {
+            S0 = 1;
+        }
         p.chunk = (int)((p.total + S0 - 1) / S0);
         p.S = (p.total + p.chunk - 1) / p.chunk;
         return p;

@@ -547,7 +547,7 @@ def test_bias_reduction_forms(shape):
 
 @pytest.mark.parametrize("shape,layout", [
     ((32, 64, 56, 56), "nchw"),     # planes split over 8 workgroups per channel
-    ((40, 6, 25, 25), "nchw"),      # planes of 625 floats (scalar loads), 3 slices per channel
+    ((160, 6, 25, 25), "nchw"),     # planes of 625 floats (scalar loads), 12 slices per channel
     ((1600, 4096, 1, 1), "nchw"),   # [N, K] rows, 4 column blocks x 124 row slices
     ((3000, 1002, 1, 1), "nchw"),   # [N, K] rows, K not a multiple of 4 (one column per thread)
     ((8, 64, 28, 28), "nhwc"),      # NHWC: [N*Ho*Wo, 64] narrow rows
