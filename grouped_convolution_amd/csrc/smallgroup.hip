@@ -876,6 +876,119 @@ __global__ void __launch_bounds__(256, (CQ * KQ > 1 ? 2 : 1)) sg_wgrad_stream_ke
         out[e] = ((lds[e] + lds[WLDS + e]) + lds[2 * WLDS + e]) + lds[3 * WLDS + e];
 }
 
+// Depthwise form of the streaming gradWeight (one input and MQ <= 2 output
+// channels per group, 3x3, stride 1 or 2): the same per-wave rings and exact
+// waits, with the 9 x MQ sums of a lane (lane = output column) on the vector
+// ALUs, since 4x4 MFMA blocks would be a sixteenth used with one channel. A
+// workgroup owns one group; its waves stream units (one band of one image)
+// independently through rings of 72-float rows: input rows and the group's
+// MQ dy rows. At stride 2 lanes past the output width read the last output's
+// x (their dy is 0).
+template <int S, int MQ, int PF>
+__global__ void __launch_bounds__(256) sg_dw_wgrad_stream_kernel(SgWStreamArgs a)
+{
+    constexpr int T = 9;
+    constexpr int D = S == 1 ? 2 : 1;
+    constexpr int RX = S * (D + 1 + PF), RD = PF + 1;  // input-row and dy-row slots
+    constexpr int CS = 72;
+    constexpr int WLDS = RX * CS + RD * MQ * CS;
+    constexpr int NDMA = S + MQ;                        // DMA rows per step
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float* xring = lds + wave * WLDS;
+    float* dring = xring + RX * CS;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int g = bid % a.G;
+    const int chunk = bid / a.G;
+    const int units = a.N * a.nbands;
+
+    // Columns 64..71 of the input slots are never loaded (stride-1 lanes past
+    // the output width read up to column 65, times dy = 0).
+    for (int e = lane; e < RX * 8; e += 64) xring[(e >> 3) * CS + 64 + (e & 7)] = 0.f;
+
+    const int wcol = lane - a.pw;
+    const bool colok = (unsigned)wcol < (unsigned)a.W;
+    const int xcol = S == 1 ? lane : min(lane, a.Wo - 1) * S;
+    const uint32_t dplane = (uint32_t)a.Ho * a.Wo * 4u;
+    float acc[MQ][T];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[m][t] = 0.f;
+
+    for (int k = 0; k < a.upw; ++k) {
+        const int u = (chunk * a.upw + k) * 4 + wave;
+        if (u >= units) break;
+        const int n = u / a.nbands, band = u - n * a.nbands;
+        const int r0 = band * a.R;
+        const int rows = min(a.R, a.Ho - r0);
+        const int nin = S * (rows - 1) + 3;
+        const int hfirst = S * r0 - a.ph;
+        const float* xg = a.x + ((size_t)n * a.C + g) * a.H * a.W;
+        const float* dyg = a.dy + ((size_t)n * a.K + (size_t)g * a.Kg) * a.Ho * a.Wo;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xg, (uint32_t)a.H * a.W * 4u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dyg, (uint32_t)a.Kg * a.Ho * a.Wo * 4u);
+        auto issue_step = [&](int j, int sx, int sd, bool with_dy) {
+#pragma unroll
+            for (int r = 0; r < S; ++r) {
+                const int jj = S * j + r, h = hfirst + jj;
+                const bool okx = colok && jj < nin && (unsigned)h < (unsigned)a.H;
+                load_lds64(rx, xring + (sx + r) * CS, okx ? (uint32_t)(h * a.W + wcol) * 4u : kOOB);
+            }
+            if (with_dy) {
+                const int d = j - D;
+                const uint32_t off = (lane < a.Wo && d < rows) ? (uint32_t)((r0 + d) * a.Wo + lane) * 4u : kOOB;
+#pragma unroll
+                for (int m = 0; m < MQ; ++m) load_lds64s(rd, dring + (sd * MQ + m) * CS, off, m * dplane);
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < D; ++j) issue_step(j, S * j, 0, false);
+#pragma unroll
+        for (int j = D; j <= D + PF; ++j) issue_step(j, S * j, j - D, true);
+
+        int sx0 = 0, sd0 = 0;
+        for (int i = 0; i < rows; ++i) {
+            wait_vmcnt<PF * NDMA>();
+            float dv[MQ];
+#pragma unroll
+            for (int m = 0; m < MQ; ++m) dv[m] = dring[(sd0 * MQ + m) * CS + lane];
+#pragma unroll
+            for (int ti = 0; ti < 3; ++ti) {
+                const int sv = sx0 + ti >= RX ? sx0 + ti - RX : sx0 + ti;
+                const float* xr = xring + sv * CS + xcol;
+#pragma unroll
+                for (int tj = 0; tj < 3; ++tj) {
+                    const float xv = xr[tj];
+#pragma unroll
+                    for (int m = 0; m < MQ; ++m) acc[m][ti * 3 + tj] = fmaf(dv[m], xv, acc[m][ti * 3 + tj]);
+                }
+            }
+            issue_step(i + D + PF + 1, sx0, sd0, true);
+            sx0 = sx0 + S >= RX ? sx0 + S - RX : sx0 + S;
+            sd0 = sd0 + 1 == RD ? 0 : sd0 + 1;
+        }
+    }
+
+    // Sum the 64 lanes (a fixed butterfly) into this wave's own slice, then
+    // the four waves in order.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float v = acc[m][t];
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+            if (lane == 0) xring[m * T + t] = v;
+        }
+    __syncthreads();
+    if (tid < MQ * T)
+        a.ws[((size_t)chunk * a.G + g) * (MQ * T) + tid] =
+            ((lds[tid] + lds[WLDS + tid]) + lds[2 * WLDS + tid]) + lds[3 * WLDS + tid];
+}
+
 // dw[g*Kg + k, c, t] = sum over the (image, band) partial sets. Block = 16
 // outputs x 16 set groups: thread (e, sg) sums sets sg, sg+16, ... in order,
 // then the 16 group sums are added in order.
@@ -1489,6 +1602,48 @@ bool sg_dw_wgrad_plan(const Shape& s, SgDwWArgs* out, int* mq)
     return true;
 }
 
+// The streaming depthwise gradWeight: the shapes of sg_dw_wgrad_plan. Units
+// (one image's rows, or bands of at least 8 rows where images are few) such
+// that at most one round of resident waves (32 a CU) has them, a wave taking
+// several units where there are more. Three steps of prefetch: mobilenet_dw
+// 64.8 -> 63.1 us against the banded kernel, its stride-2 "same" layer 49.7
+// -> 45.9 us; six steps measured the same, twelve slower (66.4, 62.1).
+#ifndef GCONV_SG_DW_STREAM_PF
+#define GCONV_SG_DW_STREAM_PF 3
+#endif
+constexpr int kSgDwStreamPF = GCONV_SG_DW_STREAM_PF;
+
+bool sg_dw_stream_plan(const Shape& s, SgWStreamArgs* out, int* mq, size_t* lds)
+{
+#ifdef GCONV_SG_NO_DW_STREAM
+    (void)s; (void)out; (void)mq; (void)lds;
+    return false;
+#else
+    if (!sg_dw_wgrad_plan(s, nullptr, nullptr)) return false;
+    const int S = s.sh, MQ = s.Kg <= 1 ? 1 : 2;
+    constexpr int PF = kSgDwStreamPF, CS = 72;
+    const int D = S == 1 ? 2 : 1;
+    const size_t wg_lds = (size_t)4 * (S * (D + 1 + PF) + (PF + 1) * MQ) * CS * 4;
+    const int per_cu = (int)std::min<size_t>(8, (160 * 1024) / wg_lds);
+    const int64_t waves = (int64_t)256 * per_cu * 4;
+    SgWStreamArgs a{};
+    a.N = s.N; a.C = s.C; a.H = s.H; a.W = s.W; a.K = s.K; a.Ho = s.Ho; a.Wo = s.Wo;
+    a.G = s.G; a.Cg = s.Cg; a.Kg = s.Kg; a.ph = s.ph; a.pw = s.pw;
+    const int64_t planes = (int64_t)s.N * s.G;
+    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(waves / planes, std::max(1, s.Ho / 8)));
+    a.R = (s.Ho + nb - 1) / nb;
+    a.nbands = (s.Ho + a.R - 1) / a.R;
+    const int64_t units = (int64_t)s.N * a.nbands;  // per group
+    a.upw = (int)std::max<int64_t>(1, (units * s.G + waves - 1) / waves);
+    a.nchunks = (int)((units + 4 * a.upw - 1) / (4 * a.upw));
+    if ((int64_t)a.nchunks * s.G >= (1 << 30)) return false;
+    if (out) *out = a;
+    if (mq) *mq = MQ;
+    if (lds) *lds = wg_lds;
+    return true;
+#endif
+}
+
 bool smallgroup_dw_wgrad_ok(const Shape& s) { return sg_dw_wgrad_plan(s, nullptr, nullptr); }
 
 bool smallgroup_fwd_supported(const Shape& s)
@@ -1544,6 +1699,9 @@ size_t smallgroup_bwd_filter_workspace(const Shape& s)
 {
     SgDwWArgs da;
     int mq;
+    SgWStreamArgs dsa;
+    size_t dlds;
+    if (sg_dw_stream_plan(s, &dsa, &mq, &dlds)) return (size_t)dsa.nchunks * s.G * mq * 9 * sizeof(float);
     if (sg_dw_wgrad_plan(s, &da, &mq)) return (size_t)da.nruns * s.G * mq * 9 * sizeof(float);
     SgWStreamArgs sa;
     SgwStreamShape sh;
@@ -1575,6 +1733,26 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
 {
     SgDwWArgs da;
     int mq;
+    {
+        SgWStreamArgs dsa;
+        size_t dlds;
+        if (sg_dw_stream_plan(s, &dsa, &mq, &dlds)) {
+            dsa.x = x; dsa.dy = dy; dsa.ws = ws;
+            constexpr int PF = kSgDwStreamPF;
+            const dim3 grid(dsa.nchunks * s.G);
+            if (s.sh == 1) {
+                if (mq == 1) hipLaunchKernelGGL((sg_dw_wgrad_stream_kernel<1, 1, PF>), grid, dim3(256), dlds, st, dsa);
+                else hipLaunchKernelGGL((sg_dw_wgrad_stream_kernel<1, 2, PF>), grid, dim3(256), dlds, st, dsa);
+            } else {
+                if (mq == 1) hipLaunchKernelGGL((sg_dw_wgrad_stream_kernel<2, 1, PF>), grid, dim3(256), dlds, st, dsa);
+                else hipLaunchKernelGGL((sg_dw_wgrad_stream_kernel<2, 2, PF>), grid, dim3(256), dlds, st, dsa);
+            }
+            const int E = s.G * s.Kg * 9;
+            hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, dsa.nchunks, s.G,
+                               s.Kg, mq);
+            return true;
+        }
+    }
     if (sg_dw_wgrad_plan(s, &da, &mq)) {
         da.x = x; da.dy = dy; da.ws = ws;
         const int ngb = (s.G + kDwwGroups - 1) / kDwwGroups;
