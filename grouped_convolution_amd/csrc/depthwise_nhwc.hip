@@ -200,6 +200,164 @@ __global__ void __launch_bounds__(256) dw_nhwc_row_kernel(DwNhwcArgs a)
     }
 }
 
+// Unit stride and dilation, four channels per lane, walking down the rows: a
+// wave owns 64 consecutive (channel quad, run of PX outputs) units of one
+// output row and a band of R output rows, and streams the band's input rows
+// once each. Input row h adds its tap row i to output row h + ph - i, whose
+// sums sit in a ring of KS accumulator rows in registers; an output row is
+// stored as soon as its last input row is in, and the next input row's window
+// is loaded before this row's FMAs. The cached row kernel below fetches every
+// input row once for each output row that reads it, from whichever XCD runs
+// that row; here a band fetches it once (its halo rows twice).
+struct DwWalkArgs {
+    const float* in;     // x (forward) or dy (gradInput), NHWC
+    const float* wgt;    // [C][KS][KS]
+    const float* bias;   // forward only, may be null
+    float* out;          // y or dx, NHWC
+    int Hin, Win, Hout, Wout, C, ph, pw, relu;
+    int CQ, units, strips, R, nbands, waves;
+    FastDiv div_cq;
+};
+
+template <int KS, int PX, int PF, bool FLIP>
+__global__ void __launch_bounds__(256) dw_nhwc_walk_kernel(DwWalkArgs a)
+{
+    constexpr int T = KS * KS, NC = PX + KS - 1;
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (gw >= a.waves) return;
+    const int strip = gw % a.strips;
+    const int nbd = gw / a.strips;
+    const int band = nbd % a.nbands;
+    const int n = nbd / a.nbands;
+    const int ul = strip * 64 + lane;
+    const bool live = ul < a.units;
+    const int u = live ? ul : a.units - 1;
+    const int blk = (int)fastdiv((uint32_t)u, a.div_cq);
+    const int c = (u - blk * a.CQ) * 4;
+    const int ow0 = blk * PX;
+
+    float wf[4 * T];
+    const f4* w4 = reinterpret_cast<const f4*>(a.wgt + (size_t)c * T);
+#pragma unroll
+    for (int e = 0; e < T; ++e) {
+        const f4 v = w4[e];
+        wf[4 * e] = v.x; wf[4 * e + 1] = v.y; wf[4 * e + 2] = v.z; wf[4 * e + 3] = v.w;
+    }
+    // Weight of channel q at tap (i, j), tap-reversed for gradInput.
+    auto wt = [&](int q, int i, int j) { return FLIP ? wf[q * T + (KS - 1 - i) * KS + (KS - 1 - j)] : wf[q * T + i * KS + j]; };
+    f4 b4 = f4{0.f, 0.f, 0.f, 0.f};
+    if (a.bias) b4 = f4{a.bias[c], a.bias[c + 1], a.bias[c + 2], a.bias[c + 3]};
+
+    const int r0 = band * a.R;
+    const int rows = min(a.R, a.Hout - r0);
+    const int ns = rows + KS - 1;          // input rows the band reads
+    const int hb = r0 - a.ph;              // input row of step 0
+    const float* img = a.in + (size_t)n * a.Hin * a.Win * a.C + c;
+    float* dst = a.out + ((size_t)n * a.Hout + r0) * a.Wout * a.C + (size_t)ow0 * a.C + c;
+    const size_t orow = (size_t)a.Wout * a.C;
+    const int wb = ow0 - a.pw;
+
+    auto load = [&](int t, f4 (&win)[NC]) {
+        const int h = hb + t;
+        const bool hok = (unsigned)h < (unsigned)a.Hin;
+        const float* src = img + (size_t)(hok ? h : 0) * a.Win * a.C;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const int w = wb + k;
+            win[k] = hok && (unsigned)w < (unsigned)a.Win ? *reinterpret_cast<const f4*>(src + (size_t)w * a.C)
+                                                           : f4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    f4 acc[KS][PX];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int p = 0; p < PX; ++p) acc[s][p] = b4;
+    // PF input rows in flight ahead of the one being summed.
+    constexpr int NB = PF + 1;
+    constexpr int UN = KS % NB == 0 ? KS : (NB % KS == 0 ? NB : KS * NB);
+    f4 win[NB][NC];
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+        if (k < ns) load(k, win[k]);
+    // Step t reads input row hb + t; its tap row i goes to output row t - i,
+    // held in ring slot (t - i) mod KS. After step t, row t - (KS - 1) is
+    // complete. Steps are unrolled UN at a time so that the ring slot and the
+    // window buffer of every step are static.
+    for (int m = 0; m < ns; m += UN) {
+#pragma unroll
+        for (int s = 0; s < UN; ++s) {
+            const int t = m + s;
+            if (t < ns) {
+                if (t + PF < ns) load(t + PF, win[(s + PF) % NB]);
+                f4(&cur)[NC] = win[s % NB];
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    f4(&o)[PX] = acc[(s % KS - i + KS) % KS];
+#pragma unroll
+                    for (int p = 0; p < PX; ++p)
+#pragma unroll
+                        for (int j = 0; j < KS; ++j) {
+                            o[p].x = fmaf(wt(0, i, j), cur[p + j].x, o[p].x);
+                            o[p].y = fmaf(wt(1, i, j), cur[p + j].y, o[p].y);
+                            o[p].z = fmaf(wt(2, i, j), cur[p + j].z, o[p].z);
+                            o[p].w = fmaf(wt(3, i, j), cur[p + j].w, o[p].w);
+                        }
+                }
+                const int q = t - (KS - 1);
+                f4(&done)[PX] = acc[(s % KS + 1) % KS];
+                if (q >= 0 && live) {
+#pragma unroll
+                    for (int p = 0; p < PX; ++p) {
+                        if (ow0 + p >= a.Wout) break;
+                        f4 v = done[p];
+                        v.x = relu_if(v.x, a.relu); v.y = relu_if(v.y, a.relu);
+                        v.z = relu_if(v.z, a.relu); v.w = relu_if(v.w, a.relu);
+                        *reinterpret_cast<f4*>(dst + (size_t)q * orow + (size_t)p * a.C) = v;
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < PX; ++p) done[p] = b4;
+            }
+        }
+    }
+}
+
+#ifndef GCONV_DW_WALK_PX
+#define GCONV_DW_WALK_PX 4
+#endif
+#ifndef GCONV_DW_WALK_WAVES
+#define GCONV_DW_WALK_WAVES 2048
+#endif
+#ifndef GCONV_DW_WALK_PF
+#define GCONV_DW_WALK_PF 1
+#endif
+
+template <int KS, bool FLIP>
+void launch_walk(const DwNhwcArgs& s, hipStream_t st)
+{
+    constexpr int PX = GCONV_DW_WALK_PX;
+    DwWalkArgs a{};
+    a.in = s.in; a.wgt = s.wgt; a.bias = s.bias; a.out = s.out;
+    a.Hin = s.Hin; a.Win = s.Win; a.Hout = s.Hout; a.Wout = s.Wout; a.C = s.C;
+    a.ph = s.ph; a.pw = s.pw; a.relu = s.relu;
+    a.CQ = s.CQ;
+    a.div_cq = make_fastdiv((uint32_t)a.CQ);
+    a.units = a.CQ * ((a.Wout + PX - 1) / PX);
+    a.strips = (a.units + 63) / 64;
+    // Bands: about GCONV_DW_WALK_WAVES waves in all (two a SIMD), so that every
+    // wave is resident at once and the halo rows stay a small fraction.
+    const int64_t per_band = (int64_t)s.N * a.strips;
+    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(a.Hout, (GCONV_DW_WALK_WAVES + per_band / 2) / per_band));
+    a.R = (a.Hout + nb - 1) / nb;
+    a.nbands = (a.Hout + a.R - 1) / a.R;
+    a.waves = (int)(per_band * a.nbands);
+    const unsigned blocks = (unsigned)((a.waves + 3) / 4);
+    hipLaunchKernelGGL((dw_nhwc_walk_kernel<KS, PX, GCONV_DW_WALK_PF, FLIP>), dim3(blocks), dim3(256), 0, st, a);
+}
+
 template <int KS, bool FLIP>
 void launch_row(DwNhwcArgs a, hipStream_t st)
 {
@@ -484,6 +642,9 @@ bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* 
 }
 
 static bool unit(const Shape& s) { return s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1; }
+// 3x3 walks down the rows; 5x5 (a ring of five accumulator rows and a
+// seven-column window) would leave one wave a SIMD, and keeps the row kernel.
+static bool walk_ok(const Shape& s) { return s.kh == 3; }
 
 void dw_nhwc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y, hipStream_t st)
 {
@@ -491,6 +652,12 @@ void dw_nhwc_fwd(const Shape& s, const float* x, const float* w, const float* bi
     DwNhwcArgs a = dw_args(s, false, vec);
     a.in = x; a.wgt = w; a.bias = bias; a.out = y; a.relu = s.relu;
     if (vec && unit(s)) {
+#ifndef GCONV_DW_NHWC_NO_WALK
+        if (walk_ok(s)) {
+            launch_walk<3, false>(a, st);
+            return;
+        }
+#endif
         if (s.kh == 3) launch_row<3, false>(a, st);
         else launch_row<5, false>(a, st);
         return;
@@ -508,6 +675,12 @@ void dw_nhwc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx
         // The forward correlation of dy with the reversed taps and padding k - 1 - p.
         a.ph = s.kh - 1 - s.ph;
         a.pw = s.kw - 1 - s.pw;
+#ifndef GCONV_DW_NHWC_NO_WALK
+        if (walk_ok(s)) {
+            launch_walk<3, true>(a, st);
+            return;
+        }
+#endif
         if (s.kh == 3) launch_row<3, true>(a, st);
         else launch_row<5, true>(a, st);
         return;

@@ -371,9 +371,10 @@ __global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
                     float acc = 0.f;
 #pragma unroll
                     for (int t = 0; t < T; ++t) acc = fmaf(wv[o][t], xv[t], acc);
-                    // Streaming stores: the output is not read again here.
+                    // Write-back stores: non-temporal ones (which skip the
+                    // L2's merging of partial lines) measured slower here.
                     if (o < a.Cout_g)
-                        __builtin_nontemporal_store(relu_if(acc + bv[o], a.relu), out_g + (size_t)o * P + pl);
+                        out_g[(size_t)o * P + pl] = relu_if(acc + bv[o], a.relu);
                 }
             }
         }

@@ -188,6 +188,52 @@ def test_nhwc_cases(case):
         assert np.array_equal(got[op].cpu().numpy().astype(np.float64), ref[op][0]), (d, op)
 
 
+# Depthwise 3x3 at unit stride, four channels a lane, on the row-walking kernel:
+# a wave owns 64 (channel quad, four-column run) units of a row and walks a band
+# of rows. The band height follows from the problem size (about 2048 waves in
+# all), so these shapes are large enough for bands of several rows, a ragged
+# last band and a ragged last strip of units.
+WALK_CASES = [
+    # 62 quads x 14 runs = 868 units (14 strips, the last 36 lanes); bands of 3
+    # rows, the last of 1; bias and ReLU
+    (dict(N=8, C=248, K=248, H=40, W=54, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=248), True),
+    # no padding: 70 columns (the last run of 2), 288 units in 5 strips, bands of 2 rows
+    (dict(N=16, C=64, K=64, H=30, W=72, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=64), False),
+    # two zero rows at the end and none at the start, two zero columns at the
+    # start and none at the end; bands of 3 rows
+    (dict(N=32, C=128, K=128, H=33, W=40, kh=3, kw=3, sh=1, sw=1, dh=1, dw=1, G=128,
+          ph=0, pb=2, pw=2, pr=0), True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WALK_CASES)))
+def test_nhwc_depthwise_walk(case):
+    """Channels-last depthwise forward (bias, optional ReLU) and gradInput on
+    the row-walking kernel against the oracle; integer data bit for bit."""
+    d, relu = WALK_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout="nhwc", **kw)
+    for op in ("fwd", "bwd_data"):
+        assert G.PATH_NAMES[G.gconv_select_path(desc, getattr(G, "OP_" + op.upper()))] == "smallgroup"
+        assert G.gconv_workspace_size(desc, getattr(G, "OP_" + op.upper())) == 0
+    for dist, seed in ((("normal", 1.0), 3800), (("int", -3, 3), 3850)):
+        say("nhwc depthwise walk %s relu %s %s" % (d, relu, dist[0]))
+        x, w, b = tensors(d, seed + 10 * case, dist=dist)
+        y_ref, ya = oracle.fwd(x, w, b, relu=relu, **kw)
+        dy = draw(dist, y_ref.shape, seed + 10 * case + 5)
+        dx_ref, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+        y = G.gconv_fwd(dev(to_nhwc(x)), dev(w), dev(b), layout="nhwc", relu=relu, **kw)
+        dx = G.gconv_bwd_data(dev(to_nhwc(dy)), dev(w), to_nhwc(x).shape, layout="nhwc", **kw)
+        torch.cuda.synchronize()
+        for tag, got, val, mag in (("fwd", y, to_nhwc(y_ref), to_nhwc(ya)), ("bwd_data", dx, to_nhwc(dx_ref), to_nhwc(dxa))):
+            g = got.cpu().numpy()
+            assert g.shape == val.shape, (d, tag)
+            if dist[0] == "int":
+                assert np.array_equal(g.astype(np.float64), val), (d, tag)
+            else:
+                check("walk %s %s" % (tag, d), g, val, mag)
+
+
 def test_nhwc_workspace_guard_bands():
     """The staged ops write only their outputs and their workspace: guard
     floats around every output and around the workspace stay untouched."""
