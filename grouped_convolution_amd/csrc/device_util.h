@@ -35,6 +35,12 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byt
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
+// 32-bit raw buffer store of a float; out-of-range offsets are dropped.
+__device__ __forceinline__ void store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
+}
+
 // The 64 lanes load one dword each into 64 consecutive LDS floats at `dst`
 // (wave-uniform); out-of-range offsets write 0.
 __device__ __forceinline__ void load_lds64(__amdgpu_buffer_rsrc_t r, float* dst, uint32_t byte_off)

@@ -23,6 +23,8 @@
 //   in a fixed order. One workgroup per (image, group) writes a partial to the
 //   workspace and a second kernel sums the images in order.
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "fastdiv.h"
 #include "device_util.h"
@@ -379,6 +381,119 @@ __global__ void __launch_bounds__(256) sg_dw_row64_kernel(SgArgs a)
             }
         }
     }
+}
+
+// Depthwise 3x3 with multiplier 1 at unit stride and dilation, walking down
+// the rows: a wave owns 64 / lpw planes side by side (lane = output column of
+// plane lane / lpw; lpw = 32 or 16 where rows have at most 30 or 14 outputs)
+// and a band of output rows, and streams the band's input rows once each, PF
+// rows ahead.
+// Input row t of the band adds its tap row i to output row t - i, whose sum
+// sits in a ring of three accumulators; output row t - 2 is stored after step
+// t. gradInput is the forward of dy with the reversed taps (FLIP). Loads and
+// stores are buffer operations whose out-of-range offsets (rows outside the
+// image or past the band, columns outside the row, idle lanes) read 0 or are
+// dropped, so a band's steps are one straight run of code (the band height is
+// a compile-time constant) and the compiler's waits count exactly the rows in
+// flight.
+struct SgDwWalkArgs {
+    const float* in;     // x or dy, planes of Hin x Win
+    const float* wgt;    // [C][3][3]
+    const float* bias;   // forward only, may be null
+    float* out;          // planes of Hout x Wout
+    int C, Hin, Win, Hout, Wout, ph, pw, relu;
+    int planes;          // N * C
+    int lpw_log2;        // lanes per plane: 64, 32 or 16
+    int nbands, waves;   // bands of RB output rows per plane
+};
+
+// f(integral_constant<int, I>) for each I of the sequence, in order (a loop
+// unrolled with the index usable as a constant expression).
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <bool FLIP, int PF, int RB>
+__global__ void __launch_bounds__(256) sg_dw_walk_kernel(SgDwWalkArgs a)
+{
+    constexpr int T = 9;
+    constexpr int NS = RB + 2;                   // input rows a band reads
+    constexpr int NB = PF + 1;                   // input-row buffers
+    // A lane's column offset past its planes (reads 0, stores dropped), and a
+    // row offset past everything; their sum stays below 2^32.
+    constexpr uint32_t kColOOB = 0x40000000u, kRowOOB = 0x80000000u;
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (gw >= a.waves) return;
+    const int band = gw % a.nbands;
+    const int pg = gw / a.nbands;
+    const int ppw = 64 >> a.lpw_log2;
+    const int p0 = pg * ppw;
+    const int np = min(ppw, a.planes - p0);
+    const int slot = lane >> a.lpw_log2;
+    const int wo = lane - (slot << a.lpw_log2);
+    const bool live = slot < np && wo < a.Wout;
+    const int c = (p0 + min(slot, np - 1)) % a.C;
+
+    float wv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) wv[t] = a.wgt[(size_t)c * T + (FLIP ? T - 1 - t : t)];
+    const float b0 = a.bias ? a.bias[c] : 0.f;
+
+    const uint32_t HWi = (uint32_t)a.Hin * a.Win, HWo = (uint32_t)a.Hout * a.Wout;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.in + (size_t)p0 * HWi, (uint32_t)np * HWi * 4u);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.out + (size_t)p0 * HWo, (uint32_t)np * HWo * 4u);
+    const int r0 = band * RB;
+    const int rows = min(RB, a.Hout - r0);
+    const int hb = r0 - a.ph;
+    // Lane wo loads input column wo - pw (tap column 0 of its output); tap
+    // columns 1 and 2 are the values of lanes wo + 1 and wo + 2, moved down
+    // the wave by DPP (lanes past a plane's last output feed only idle ones).
+    const int cc = wo - a.pw;
+    const uint32_t xcol = slot < np && (unsigned)cc < (unsigned)a.Win ? (uint32_t)(slot * HWi + cc) * 4u : kColOOB;
+    const uint32_t ycol = live ? (uint32_t)(slot * HWo + r0 * a.Wout + wo) * 4u : kColOOB;
+
+    // Rows outside the image and past the (last, shorter) band read 0.
+    auto load = [&](int t) {
+        const int h = hb + t;
+        const uint32_t hs = t < rows + 2 && (unsigned)h < (unsigned)a.Hin ? (uint32_t)h * a.Win * 4u : kRowOOB;
+        return load_f32(rx, xcol + hs);
+    };
+    auto down1 = [](float v) {  // lane L takes lane L + 1's value
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
+    };
+
+    float acc[3] = {b0, b0, b0};
+    float win[NB];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) win[k] = load(k);
+    // Step t: issue row t + PF, add row t's taps, store output row t - 2. The
+    // band is unrolled whole (straight-line code: the compiler's waits count
+    // exactly the PF rows in flight).
+    unroll_seq(
+        [&](auto sc) {
+            constexpr int t = decltype(sc)::value;
+            if constexpr (t + PF < NS) win[(t + PF) % NB] = load(t + PF);
+            float v[3];
+            v[0] = win[t % NB];
+            v[1] = down1(v[0]);
+            v[2] = down1(v[1]);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                float& o = acc[(t - i + 3) % 3];
+#pragma unroll
+                for (int j = 0; j < 3; ++j) o = fmaf(wv[i * 3 + j], v[j], o);
+            }
+            // Slot (t + 1) mod 3 is complete (output t - 2), or before step 2
+            // holds only the taps of rows above the band's first output.
+            float& done = acc[(t + 1) % 3];
+            if constexpr (t >= 2)
+                store_f32(ry, ycol + (t - 2 < rows ? (uint32_t)(t - 2) * a.Wout * 4u : kRowOOB), relu_if(done, a.relu));
+            done = b0;
+        },
+        std::make_integer_sequence<int, NS>{});
 }
 
 // Depthwise gradInput at stride 2 (3x3, dilation 1, one input and one output
@@ -1266,6 +1381,51 @@ bool sg_run_row64(const SgProblem& p, hipStream_t st)
     return false;
 }
 
+// The walking depthwise kernel: 3x3, multiplier 1, unit dilation and stride
+// (forward, or gradInput as the forward of dy), rows of at most 62 outputs
+// (a lane per output and two lanes past the last).
+bool sg_dw_walk_ok(const SgProblem& p)
+{
+#ifdef GCONV_SG_NO_DW_WALK
+    (void)p;
+    return false;
+#else
+    if (!(p.kh == 3 && p.kw == 3 && p.dh == 1 && p.dw == 1 && p.Cin_g == 1 && p.Cout_g == 1)) return false;
+    if (!(p.uh == 1 && p.uw == 1 && p.sh == 1 && p.sw == 1)) return false;
+    if (p.Wout + 2 > 64 || p.N < 1 || (int64_t)p.N * p.G >= (1 << 30)) return false;
+    // Two planes' bytes stay below 2^30 (the buffer offsets of the kernel).
+    return (int64_t)p.Hin * p.Win * 8 < (int64_t(1) << 30) && (int64_t)p.Hout * p.Wout * 8 < (int64_t(1) << 30);
+#endif
+}
+
+#ifndef GCONV_DW_WALK_PF
+#define GCONV_DW_WALK_PF 8
+#endif
+#ifndef GCONV_DW_WALK_RB
+#define GCONV_DW_WALK_RB 14
+#endif
+// Output rows per band (a band is one straight run of code).
+constexpr int kDwWalkRows = GCONV_DW_WALK_RB;
+
+bool sg_run_dw_walk(const SgProblem& p, hipStream_t st)
+{
+    SgDwWalkArgs a{};
+    a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.C = p.G; a.Hin = p.Hin; a.Win = p.Win; a.Hout = p.Hout; a.Wout = p.Wout;
+    a.ph = p.ph; a.pw = p.pw; a.relu = p.relu;
+    a.planes = p.N * p.G;
+    a.lpw_log2 = p.Wout + 2 <= 16 ? 4 : p.Wout + 2 <= 32 ? 5 : 6;
+    const int64_t groups = ((int64_t)a.planes + (64 >> a.lpw_log2) - 1) >> (6 - a.lpw_log2);
+    a.nbands = (p.Hout + kDwWalkRows - 1) / kDwWalkRows;
+    const int64_t waves = groups * a.nbands;
+    if (waves >= (int64_t(1) << 30)) return false;
+    a.waves = (int)waves;
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    if (p.flip) hipLaunchKernelGGL((sg_dw_walk_kernel<true, GCONV_DW_WALK_PF, kDwWalkRows>), dim3(blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((sg_dw_walk_kernel<false, GCONV_DW_WALK_PF, kDwWalkRows>), dim3(blocks), dim3(256), 0, st, a);
+    return true;
+}
+
 template <int MQ, bool FLIP, int S>
 void sg_dw_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
 {
@@ -1332,6 +1492,7 @@ bool sg_run_dw(const SgProblem& p, hipStream_t st)
 bool sg_run(const SgProblem& p, hipStream_t st)
 {
     if (!sg_problem_ok(p)) return false;
+    if (sg_dw_walk_ok(p)) return sg_run_dw_walk(p, st);
 #ifndef GCONV_SG_NO_DW
 #ifdef GCONV_SG_NO_DW_S2
     if (sg_dw_ok(p) && p.sh == 1) return sg_run_dw(p, st);

@@ -501,6 +501,54 @@ def test_strided_gradinput_subpixel(case, layout):
             check("subpixel %s" % d, got, val, mag)
 
 
+# Depthwise 3x3 at unit stride (forward and gradInput) on the row-walking
+# kernel: lanes = output columns of one, two or four planes (rows of up to 62,
+# 30 or 14 outputs), bands of 14 output rows streamed one input row at a time.
+DW_WALK_CASES = [
+    # 62 outputs a row (the widest: lanes 62 and 63 only feed tap columns), three
+    # bands (14, 14, 2 rows), 3 planes (one a wave), bias and ReLU
+    (dict(N=1, C=3, K=3, H=30, W=62, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=3), True),
+    # two planes a wave (30 outputs), an odd plane count (the last wave half
+    # idle), no padding: 28 x 28 outputs in two bands
+    (dict(N=3, C=5, K=5, H=30, W=30, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=5), False),
+    # four planes a wave (14 outputs), 7 planes (the second wave's last slot
+    # idle), two bands
+    (dict(N=1, C=7, K=7, H=20, W=14, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=7), True),
+    # padding 2: 18 x 14 outputs, four planes a wave
+    (dict(N=2, C=4, K=4, H=16, W=12, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=4), False),
+    # asymmetric padding: one row on top, none below, none left, two right
+    (dict(N=2, C=6, K=6, H=29, W=20, kh=3, kw=3, sh=1, sw=1, dh=1, dw=1, G=6, ph=1, pb=0, pw=0, pr=2), False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DW_WALK_CASES)))
+def test_depthwise_walk(case):
+    """Depthwise forward (bias, optional ReLU) and gradInput at unit stride on
+    the row-walking kernel against the oracle on every output; integer data
+    bit for bit."""
+    d, relu = DW_WALK_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
+    for op in (G.OP_FWD, G.OP_BWD_DATA):
+        assert G.PATH_NAMES[G.gconv_select_path(desc, op)] == "smallgroup", d
+    for dist, seed in ((("normal", 1.0), 2900), (("int", -3, 3), 2950)):
+        say("depthwise walk %s relu %s %s" % (d, relu, dist[0]))
+        x, w, b = tensors(d, seed + 10 * case, dist=dist)
+        y_ref, ya = oracle.fwd(x, w, b, relu=relu, **kw)
+        dy = draw(dist, y_ref.shape, seed + 10 * case + 5)
+        dx_ref, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+        y = G.gconv_fwd(dev(x), dev(w), dev(b), relu=relu, **kw)
+        dx = G.gconv_bwd_data(dev(dy), dev(w), x.shape, **kw)
+        torch.cuda.synchronize()
+        for tag, got, val, mag in (("fwd", y, y_ref, ya), ("bwd_data", dx, dx_ref, dxa)):
+            g = got.cpu().numpy()
+            assert g.shape == val.shape, (d, tag)
+            if dist[0] == "int":
+                assert np.array_equal(g.astype(np.float64), val), (d, tag)
+            else:
+                check("dw walk %s %s" % (tag, d), g, val, mag)
+
+
 @pytest.mark.parametrize("case", range(len(ASYM_CASES)))
 def test_asymmetric_padding_cases(case):
     """Asymmetric padding on the dispatcher's own choice of family (asserted):
