@@ -277,6 +277,11 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Waits until this wave's LDS reads have returned their data. A buffer load
+// into LDS writes by another path than the wave's LDS instructions, so a slot
+// that was just read is only free for a new DMA after this.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Depthwise form (one input channel per group, up to 8 outputs): a workgroup
 // takes kDwGroups consecutive groups of one band, so that the tiles stay large
 // although each group has a single input plane, and every output is a plain
@@ -492,6 +497,189 @@ __global__ void __launch_bounds__(256) sg_dw_walk_kernel(SgDwWalkArgs a)
             if constexpr (t >= 2)
                 store_f32(ry, ycol + (t - 2 < rows ? (uint32_t)(t - 2) * a.Wout * 4u : kRowOOB), relu_if(done, a.relu));
             done = b0;
+        },
+        std::make_integer_sequence<int, NS>{});
+}
+
+// The walk at a forward stride of 2 (3x3, multiplier 1, unit dilation): lane
+// L of a plane loads input column L - pw of each input row, and output wo sits
+// on lane 2 wo with its tap columns on lanes 2 wo, 2 wo + 1, 2 wo + 2 (DPP
+// moves them down). A band of RB output rows reads 2 RB + 1 input rows; input
+// row t adds tap row i to output (t - i) / 2 where that divides, so an even
+// step starts one output (tap row 0) and ends the one before (tap row 2).
+template <int PF, int RB>
+__global__ void __launch_bounds__(256) sg_dw_walk_s2_kernel(SgDwWalkArgs a)
+{
+    constexpr int T = 9;
+    constexpr int NS = 2 * RB + 1;
+    constexpr int NB = PF + 1;
+    constexpr uint32_t kColOOB = 0x40000000u, kRowOOB = 0x80000000u;
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (gw >= a.waves) return;
+    const int band = gw % a.nbands;
+    const int pg = gw / a.nbands;
+    const int ppw = 64 >> a.lpw_log2;
+    const int p0 = pg * ppw;
+    const int np = min(ppw, a.planes - p0);
+    const int slot = lane >> a.lpw_log2;
+    const int L = lane - (slot << a.lpw_log2);
+    const int wo = L >> 1;
+    const bool live = slot < np && (L & 1) == 0 && wo < a.Wout;
+    const int c = (p0 + min(slot, np - 1)) % a.C;
+
+    float wv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) wv[t] = a.wgt[(size_t)c * T + t];
+    const float b0 = a.bias ? a.bias[c] : 0.f;
+
+    const uint32_t HWi = (uint32_t)a.Hin * a.Win, HWo = (uint32_t)a.Hout * a.Wout;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.in + (size_t)p0 * HWi, (uint32_t)np * HWi * 4u);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.out + (size_t)p0 * HWo, (uint32_t)np * HWo * 4u);
+    const int r0 = band * RB;
+    const int rows = min(RB, a.Hout - r0);
+    const int nin = 2 * rows + 1;
+    const int hb = 2 * r0 - a.ph;
+    const int cc = L - a.pw;
+    const uint32_t xcol = slot < np && (unsigned)cc < (unsigned)a.Win ? (uint32_t)(slot * HWi + cc) * 4u : kColOOB;
+    const uint32_t ycol = live ? (uint32_t)(slot * HWo + r0 * a.Wout + wo) * 4u : kColOOB;
+
+    auto load = [&](int t) {
+        const int h = hb + t;
+        const uint32_t hs = t < nin && (unsigned)h < (unsigned)a.Hin ? (uint32_t)h * a.Win * 4u : kRowOOB;
+        return load_f32(rx, xcol + hs);
+    };
+    auto down1 = [](float v) {  // lane L takes lane L + 1's value
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
+    };
+
+    float acc[2] = {b0, b0};
+    float win[NB];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) win[k] = load(k);
+    unroll_seq(
+        [&](auto sc) {
+            constexpr int t = decltype(sc)::value;
+            if constexpr (t + PF < NS) win[(t + PF) % NB] = load(t + PF);
+            float v[3];
+            v[0] = win[t % NB];
+            v[1] = down1(v[0]);
+            v[2] = down1(v[1]);
+            if constexpr (t % 2 == 0) {
+                float& o0 = acc[(t / 2) % 2];       // output t / 2, tap row 0
+                float& o2 = acc[(t / 2 + 1) % 2];   // output t / 2 - 1, tap row 2
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    o0 = fmaf(wv[j], v[j], o0);
+                    o2 = fmaf(wv[6 + j], v[j], o2);
+                }
+                if constexpr (t >= 2)
+                    store_f32(ry, ycol + (t / 2 - 1 < rows ? (uint32_t)(t / 2 - 1) * a.Wout * 4u : kRowOOB),
+                              relu_if(o2, a.relu));
+                o2 = b0;
+            } else {
+                float& o1 = acc[(t / 2) % 2];       // output (t - 1) / 2, tap row 1
+#pragma unroll
+                for (int j = 0; j < 3; ++j) o1 = fmaf(wv[3 + j], v[j], o1);
+            }
+        },
+        std::make_integer_sequence<int, NS>{});
+}
+
+// Depthwise gradInput at stride 2 (3x3, multiplier 1, unit dilation) walking
+// down dy: lane L of a plane is dx column w = L - 2 and loads dy column
+// b = floor((w + pw) / 2) of each dy row; dy column b - 1 is lane L - 2's
+// value (DPP moves it up). Tap columns: w + pw even takes j = 0 on column b
+// and j = 2 on b - 1, odd takes j = 1 on column b, so with (A_i, B_i) =
+// (w_i0, w_i2) or (w_i1, 0), tap row i of dy row r gives
+// X_i = A_i d(b) + B_i d(b - 1), and dy row r completes dx rows 2r - ph
+// (X_0 plus X_2 of row r - 1) and 2r - ph + 1 (X_1); its X_2 carries to the
+// next step. A band of RB dy-row steps starts from the carry of the row
+// before it.
+struct SgDwWalkDArgs {
+    const float* dy;     // planes of Ho x Wo
+    const float* wgt;    // [C][3][3]
+    float* dx;           // planes of H x W
+    int C, H, W, Ho, Wo, ph, pw;
+    int planes, lpw_log2;
+    int r_lo;            // first dy-row step (dx rows 2 r_lo - ph, + 1)
+    int nsteps;          // dy-row steps over all bands
+    int nbands, waves;
+};
+
+template <int PF, int RB>
+__global__ void __launch_bounds__(256) sg_dw_walk_dgrad_s2_kernel(SgDwWalkDArgs a)
+{
+    constexpr int NS = RB + 1;                  // the carry row, then RB steps
+    constexpr int NB = PF + 1;
+    constexpr uint32_t kColOOB = 0x40000000u, kRowOOB = 0x80000000u;
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (gw >= a.waves) return;
+    const int band = gw % a.nbands;
+    const int pg = gw / a.nbands;
+    const int ppw = 64 >> a.lpw_log2;
+    const int p0 = pg * ppw;
+    const int np = min(ppw, a.planes - p0);
+    const int slot = lane >> a.lpw_log2;
+    const int w = lane - (slot << a.lpw_log2) - 2;
+    const bool live = slot < np && w >= 0 && w < a.W;
+    const int c = (p0 + min(slot, np - 1)) % a.C;
+    const int par = (w + a.pw) & 1;
+    const int bcol = (w + a.pw) >> 1;           // arithmetic shift: floor
+
+    float A[3], B[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const float* wr = a.wgt + (size_t)c * 9 + i * 3;
+        A[i] = par ? wr[1] : wr[0];
+        B[i] = par ? 0.f : wr[2];
+    }
+
+    const uint32_t HWi = (uint32_t)a.Ho * a.Wo, HWo = (uint32_t)a.H * a.W;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dy + (size_t)p0 * HWi, (uint32_t)np * HWi * 4u);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.dx + (size_t)p0 * HWo, (uint32_t)np * HWo * 4u);
+    const int s0 = band * RB;                   // first step of the band
+    const int nst = min(RB, a.nsteps - s0);
+    const int rb = a.r_lo + s0;                 // its first dy row
+    const uint32_t dcol = slot < np && bcol >= 0 && bcol < a.Wo ? (uint32_t)(slot * HWi + bcol) * 4u : kColOOB;
+    const uint32_t xcol = live ? (uint32_t)(slot * HWo + w) * 4u : kColOOB;
+
+    // Step k reads dy row rb - 1 + k (k = 0: the carry row).
+    auto load = [&](int k) {
+        const int r = rb - 1 + k;
+        const uint32_t rs = k <= nst && (unsigned)r < (unsigned)a.Ho ? (uint32_t)r * a.Wo * 4u : kRowOOB;
+        return load_f32(rd, dcol + rs);
+    };
+    auto up2 = [](float v) {  // lane L takes lane L - 2's value
+        const int x = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x138, 0xF, 0xF, false);
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x138, 0xF, 0xF, false));
+    };
+    auto row_store = [&](int h, float v) {
+        const uint32_t hs = (unsigned)h < (unsigned)a.H ? (uint32_t)h * a.W * 4u : kRowOOB;
+        store_f32(rx, xcol + hs, v);
+    };
+
+    float carry = 0.f;
+    float win[NB];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) win[k] = load(k);
+    unroll_seq(
+        [&](auto sc) {
+            constexpr int k = decltype(sc)::value;
+            if constexpr (k + PF < NS) win[(k + PF) % NB] = load(k + PF);
+            const float d0 = win[k % NB];
+            const float d1 = up2(d0);
+            const float x2 = fmaf(B[2], d1, A[2] * d0);
+            if constexpr (k > 0) {
+                const int r = rb - 1 + k;
+                const bool in_band = k <= nst;
+                const float x0 = fmaf(B[0], d1, fmaf(A[0], d0, carry));
+                const float x1 = fmaf(B[1], d1, A[1] * d0);
+                row_store(in_band ? 2 * r - a.ph : -1, x0);
+                row_store(in_band ? 2 * r - a.ph + 1 : -1, x1);
+            }
+            carry = x2;
         },
         std::make_integer_sequence<int, NS>{});
 }
@@ -955,7 +1143,11 @@ __global__ void __launch_bounds__(256, (CQ * KQ > 1 ? 2 : 1)) sg_wgrad_stream_ke
                 }
             }
             // Input rows S*i .. S*i + S - 1 and dy row i are no longer read:
-            // step i + D + PF + 1 reuses their slots.
+            // step i + D + PF + 1 reuses their slots. Their LDS reads must
+            // have returned first: a DMA whose rows are out of range writes
+            // its zeros without a memory access, soon enough to land ahead of
+            // a read still queued at the LDS.
+            lds_reads_done();
             issue_step(i + D + PF + 1, sx0, sd0, true);
             sx0 = sx0 + S >= RX ? sx0 + S - RX : sx0 + S;
             sd0 = sd0 + 1 == RD ? 0 : sd0 + 1;
@@ -1082,6 +1274,7 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_stream_kernel(SgWStreamArgs a
                     for (int m = 0; m < MQ; ++m) acc[m][ti * 3 + tj] = fmaf(dv[m], xv, acc[m][ti * 3 + tj]);
                 }
             }
+            lds_reads_done();  // (the slots' reads returned before the DMA reuses them)
             issue_step(i + D + PF + 1, sx0, sd0, true);
             sx0 = sx0 + S >= RX ? sx0 + S - RX : sx0 + S;
             sd0 = sd0 + 1 == RD ? 0 : sd0 + 1;
@@ -1426,6 +1619,47 @@ bool sg_run_dw_walk(const SgProblem& p, hipStream_t st)
     return true;
 }
 
+#ifndef GCONV_DW_WALK2_RB
+#define GCONV_DW_WALK2_RB 7
+#endif
+#ifndef GCONV_DW_WALK2_PF
+#define GCONV_DW_WALK2_PF 8
+#endif
+constexpr int kDwWalk2Rows = GCONV_DW_WALK2_RB;  // output rows per band, stride 2
+
+// The stride-2 forward walk: 3x3, multiplier 1, unit dilation, 2 Wout + 1
+// lanes a plane within the wave.
+bool sg_dw_walk_s2_ok(const SgProblem& p)
+{
+#ifdef GCONV_SG_NO_DW_WALK2
+    (void)p;
+    return false;
+#else
+    if (!(p.kh == 3 && p.kw == 3 && p.dh == 1 && p.dw == 1 && p.Cin_g == 1 && p.Cout_g == 1)) return false;
+    if (!(p.uh == 1 && p.uw == 1 && p.sh == 2 && p.sw == 2 && !p.flip)) return false;
+    if (2 * p.Wout + 1 > 64 || p.N < 1 || (int64_t)p.N * p.G >= (1 << 30)) return false;
+    return (int64_t)p.Hin * p.Win * 8 < (int64_t(1) << 30) && (int64_t)p.Hout * p.Wout * 8 < (int64_t(1) << 30);
+#endif
+}
+
+bool sg_run_dw_walk_s2(const SgProblem& p, hipStream_t st)
+{
+    SgDwWalkArgs a{};
+    a.in = p.in; a.wgt = p.wgt; a.bias = p.bias; a.out = p.out;
+    a.C = p.G; a.Hin = p.Hin; a.Win = p.Win; a.Hout = p.Hout; a.Wout = p.Wout;
+    a.ph = p.ph; a.pw = p.pw; a.relu = p.relu;
+    a.planes = p.N * p.G;
+    a.lpw_log2 = 2 * p.Wout + 1 <= 16 ? 4 : 2 * p.Wout + 1 <= 32 ? 5 : 6;
+    const int64_t groups = ((int64_t)a.planes + (64 >> a.lpw_log2) - 1) >> (6 - a.lpw_log2);
+    a.nbands = (p.Hout + kDwWalk2Rows - 1) / kDwWalk2Rows;
+    const int64_t waves = groups * a.nbands;
+    if (waves >= (int64_t(1) << 30)) return false;
+    a.waves = (int)waves;
+    hipLaunchKernelGGL((sg_dw_walk_s2_kernel<GCONV_DW_WALK2_PF, kDwWalk2Rows>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, st, a);
+    return true;
+}
+
 template <int MQ, bool FLIP, int S>
 void sg_dw_launch(const SgArgs& a, int blocks, size_t lds, hipStream_t st)
 {
@@ -1493,6 +1727,7 @@ bool sg_run(const SgProblem& p, hipStream_t st)
 {
     if (!sg_problem_ok(p)) return false;
     if (sg_dw_walk_ok(p)) return sg_run_dw_walk(p, st);
+    if (sg_dw_walk_s2_ok(p)) return sg_run_dw_walk_s2(p, st);
 #ifndef GCONV_SG_NO_DW
 #ifdef GCONV_SG_NO_DW_S2
     if (sg_dw_ok(p) && p.sh == 1) return sg_run_dw(p, st);
@@ -1839,6 +2074,54 @@ static bool sg_dw_dgrad_s2_plan(const Shape& s, SgDw2Args* out)
     return true;
 }
 
+#ifndef GCONV_DW_WALKD_RB
+#define GCONV_DW_WALKD_RB 14
+#endif
+#ifndef GCONV_DW_WALKD_PF
+#define GCONV_DW_WALKD_PF 12
+#endif
+constexpr int kDwWalkDRows = GCONV_DW_WALKD_RB;  // dy-row steps per band
+
+// The stride-2 gradInput walk: 3x3, multiplier 1, unit dilation, W + 2 lanes
+// a plane within the wave.
+static bool sg_dw_walk_dgrad_s2_plan(const Shape& s, SgDwWalkDArgs* out)
+{
+#ifdef GCONV_SG_NO_DW_WALKD
+    (void)s; (void)out;
+    return false;
+#else
+    if (!(s.kh == 3 && s.kw == 3 && s.sh == 2 && s.sw == 2 && s.dh == 1 && s.dw == 1)) return false;
+    if (s.Cg != 1 || s.Kg != 1 || s.N < 1 || s.ph < 0 || s.pw < 0 || s.W + 2 > 64) return false;
+    if ((int64_t)s.N * s.G >= (1 << 30)) return false;
+    if ((int64_t)s.H * s.W * 8 >= (int64_t(1) << 30) || (int64_t)s.Ho * s.Wo * 8 >= (int64_t(1) << 30)) return false;
+    SgDwWalkDArgs a{};
+    a.C = s.G; a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo; a.ph = s.ph; a.pw = s.pw;
+    a.planes = s.N * s.G;
+    a.lpw_log2 = s.W + 2 <= 16 ? 4 : s.W + 2 <= 32 ? 5 : 6;
+    // dy-row steps r_lo .. r_hi: dx rows 2r - ph and 2r - ph + 1 cover 0 .. H - 1.
+    a.r_lo = s.ph / 2;
+    const int r_hi = (s.H - 1 + s.ph) / 2;
+    a.nsteps = r_hi - a.r_lo + 1;
+    a.nbands = (a.nsteps + kDwWalkDRows - 1) / kDwWalkDRows;
+    const int64_t groups = ((int64_t)a.planes + (64 >> a.lpw_log2) - 1) >> (6 - a.lpw_log2);
+    const int64_t waves = groups * a.nbands;
+    if (waves >= (int64_t(1) << 30)) return false;
+    a.waves = (int)waves;
+    if (out) *out = a;
+    return true;
+#endif
+}
+
+static bool sg_run_dw_walk_dgrad_s2(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
+{
+    SgDwWalkDArgs a;
+    if (!sg_dw_walk_dgrad_s2_plan(s, &a)) return false;
+    a.dy = dy; a.wgt = w; a.dx = dx;
+    hipLaunchKernelGGL((sg_dw_walk_dgrad_s2_kernel<GCONV_DW_WALKD_PF, kDwWalkDRows>),
+                       dim3((unsigned)((a.waves + 3) / 4)), dim3(256), 0, st, a);
+    return true;
+}
+
 static bool sg_run_dw_dgrad_s2(const Shape& s, const float* dy, const float* w, float* dx, hipStream_t st)
 {
     SgDw2Args a;
@@ -1852,7 +2135,8 @@ static bool sg_run_dw_dgrad_s2(const Shape& s, const float* dy, const float* w, 
 
 bool smallgroup_bwd_data_supported(const Shape& s)
 {
-    return sg_dw_dgrad_s2_plan(s, nullptr) || sg_problem_ok(sg_bwd_data_problem(s, nullptr, nullptr, nullptr));
+    return sg_dw_walk_dgrad_s2_plan(s, nullptr) || sg_dw_dgrad_s2_plan(s, nullptr) ||
+           sg_problem_ok(sg_bwd_data_problem(s, nullptr, nullptr, nullptr));
 }
 
 bool smallgroup_bwd_filter_supported(const Shape& s) { return sgw_stream_plan(s, nullptr) || sgw_plan(s, nullptr); }
@@ -1884,6 +2168,7 @@ bool smallgroup_fwd(const Shape& s, const float* x, const float* w, const float*
 bool smallgroup_bwd_data(const Shape& s, const float* dy, const float* w, float* dx,
                          hipStream_t st)
 {
+    if (sg_dw_walk_dgrad_s2_plan(s, nullptr)) return sg_run_dw_walk_dgrad_s2(s, dy, w, dx, st);
 #ifndef GCONV_SG_NO_DW_S2_PHASE
     if (sg_dw_dgrad_s2_plan(s, nullptr)) return sg_run_dw_dgrad_s2(s, dy, w, dx, st);
 #endif

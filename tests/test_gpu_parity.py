@@ -521,11 +521,31 @@ DW_WALK_CASES = [
 ]
 
 
+# ... and at stride 2: the forward puts output wo on lane 2 wo of its plane
+# (planes of up to 31, 15 or 7 outputs a row: one, two or four a wave), the
+# gradInput walks dy rows with dx column w on lane w + 2 (rows of up to 62, 30
+# or 14 dx columns); bands of 7 output rows or 7 dy-row steps.
+DW_WALK_CASES += [
+    # 56 -> 28 "same" (no start padding, one zero row and column at the end):
+    # four bands, one plane a wave
+    (dict(N=2, C=3, K=3, H=56, W=56, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=3, ph=0, pb=1, pw=0, pr=1), True),
+    # padding 1, odd sizes: 30 x 29 -> 15 x 15, two planes a wave (forward), two
+    # dx planes a wave (gradInput, 29 columns), five planes
+    (dict(N=1, C=5, K=5, H=30, W=29, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=5), False),
+    # padding 2 on 13 x 14: 8 x 8 outputs (forward: two planes a wave), four dx
+    # planes a wave
+    (dict(N=3, C=2, K=2, H=13, W=14, kh=3, kw=3, sh=2, sw=2, ph=2, pw=2, dh=1, dw=1, G=2), True),
+    # 7-column outputs (four forward planes a wave); two zero rows on top and
+    # none below, one zero column each side
+    (dict(N=2, C=9, K=9, H=33, W=13, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=9, ph=2, pb=0, pw=1, pr=1), False),
+]
+
+
 @pytest.mark.parametrize("case", range(len(DW_WALK_CASES)))
 def test_depthwise_walk(case):
-    """Depthwise forward (bias, optional ReLU) and gradInput at unit stride on
-    the row-walking kernel against the oracle on every output; integer data
-    bit for bit."""
+    """Depthwise forward (bias, optional ReLU) and gradInput at stride 1 and 2
+    on the row-walking kernels against the oracle on every output; integer
+    data bit for bit."""
     d, relu = DW_WALK_CASES[case]
     kw = conv_kwargs(d)
     desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
