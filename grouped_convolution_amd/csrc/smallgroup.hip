@@ -1421,6 +1421,110 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_kernel(SgDwWArgs a)
     }
 }
 
+// Depthwise gradWeight (3x3, multiplier 1, unit dilation, stride S = 1 or 2)
+// walking down the rows: a wave owns 64 / lpw planes side by side and a band
+// of RB output rows. Lane L of a plane loads input column L - pw of each input
+// row (tap columns 1 and 2 are lanes L + 1 and L + 2, moved down by DPP) and
+// dy column L / S of the output rows (lanes that hold no output read 0). Input
+// row t pairs tap row i with output row (t - i) / S where that divides; each
+// lane keeps the 9 tap sums of its column, and at the band's end the lanes of
+// a plane are added by a fixed butterfly into the band's partial [n, band][c][9]
+// (sg_dw_wgrad_reduce adds the partials in order).
+struct SgDwWalkWArgs {
+    const float* x;      // planes of H x W
+    const float* dy;     // planes of Ho x Wo
+    float* ws;           // [N * nbands][C][9]
+    int C, H, W, Ho, Wo, ph, pw;
+    int planes, lpw_log2, nbands, waves;
+};
+
+template <int S, int PF, int RB>
+__global__ void __launch_bounds__(256) sg_dw_wgrad_walk_kernel(SgDwWalkWArgs a)
+{
+    constexpr int NS = S * (RB - 1) + 3;        // input rows a band reads
+    constexpr int NB = PF + 1;                  // input-row buffers
+    constexpr int PFD = (PF + S - 1) / S;       // dy rows loaded ahead
+    constexpr int NBD = PFD + 3;                // dy rows held: in flight, and the three being paired
+    constexpr uint32_t kColOOB = 0x40000000u, kRowOOB = 0x80000000u;
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (gw >= a.waves) return;
+    const int band = gw % a.nbands;
+    const int pg = gw / a.nbands;
+    const int ppw = 64 >> a.lpw_log2;
+    const int p0 = pg * ppw;
+    const int np = min(ppw, a.planes - p0);
+    const int slot = lane >> a.lpw_log2;
+    const int L = lane - (slot << a.lpw_log2);
+    const int wo = S == 1 ? L : L >> 1;
+    const bool has_dy = slot < np && (S == 1 || (L & 1) == 0) && wo < a.Wo;
+
+    const uint32_t HWi = (uint32_t)a.H * a.W, HWo = (uint32_t)a.Ho * a.Wo;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)p0 * HWi, (uint32_t)np * HWi * 4u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dy + (size_t)p0 * HWo, (uint32_t)np * HWo * 4u);
+    const int r0 = band * RB;
+    const int rows = min(RB, a.Ho - r0);
+    const int nin = S * (rows - 1) + 3;
+    const int hb = S * r0 - a.ph;
+    const int cc = L - a.pw;
+    const uint32_t xcol = slot < np && (unsigned)cc < (unsigned)a.W ? (uint32_t)(slot * HWi + cc) * 4u : kColOOB;
+    const uint32_t dcol = has_dy ? (uint32_t)(slot * HWo + r0 * a.Wo + wo) * 4u : kColOOB;
+
+    auto loadx = [&](int t) {
+        const int h = hb + t;
+        const uint32_t hs = t < nin && (unsigned)h < (unsigned)a.H ? (uint32_t)h * a.W * 4u : kRowOOB;
+        return load_f32(rx, xcol + hs);
+    };
+    auto loadd = [&](int q) { return load_f32(rd, dcol + (q < rows ? (uint32_t)q * a.Wo * 4u : kRowOOB)); };
+    auto down1 = [](float v) {  // lane L takes lane L + 1's value
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x130, 0xF, 0xF, false));
+    };
+
+    float acc[9];
+#pragma unroll
+    for (int e = 0; e < 9; ++e) acc[e] = 0.f;
+    float xw[NB], dw[NBD];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) xw[k] = loadx(k);
+#pragma unroll
+    for (int q = 0; q < PFD && q < RB; ++q) dw[q] = loadd(q);
+    unroll_seq(
+        [&](auto sc) {
+            constexpr int t = decltype(sc)::value;
+            if constexpr (t + PF < NS) xw[(t + PF) % NB] = loadx(t + PF);
+            // dy row q + PFD is loaded at the first step that pairs with row q.
+            if constexpr (t % S == 0 && t / S + PFD < RB) dw[(t / S + PFD) % NBD] = loadd(t / S + PFD);
+            float v[3];
+            v[0] = xw[t % NB];
+            v[1] = down1(v[0]);
+            v[2] = down1(v[1]);
+            unroll_seq(
+                [&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr ((t - i) % S == 0 && t >= i && (t - i) / S < RB) {
+                        const float d = dw[((t - i) / S) % NBD];
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) acc[i * 3 + j] = fmaf(d, v[j], acc[i * 3 + j]);
+                    }
+                },
+                std::make_integer_sequence<int, 3>{});
+        },
+        std::make_integer_sequence<int, NS>{});
+
+    // The lanes of each plane, by a fixed butterfly (xor offsets below lpw stay
+    // within the plane), then lane 0 of the plane writes the band's partial.
+    const int lpw = 1 << a.lpw_log2;
+#pragma unroll
+    for (int e = 0; e < 9; ++e)
+        for (int off = lpw >> 1; off > 0; off >>= 1) acc[e] += __shfl_xor(acc[e], off, 64);
+    if (L == 0 && slot < np) {
+        const int p = p0 + slot, n = p / a.C, c = p - n * a.C;
+        float* out = a.ws + (((size_t)n * a.nbands + band) * a.C + c) * 9;
+#pragma unroll
+        for (int e = 0; e < 9; ++e) out[e] = acc[e];
+    }
+}
+
 // dw[g*Kg + o][0][t] = sum over image runs of ws[run][g][o][t] in a fixed
 // order. Block = 16 outputs x 16 run groups: thread (e, rg) sums runs rg,
 // rg + 16, ... in order, then the 16 group sums are added in order (a serial
@@ -2041,6 +2145,45 @@ bool sg_dw_stream_plan(const Shape& s, SgWStreamArgs* out, int* mq, size_t* lds)
 #endif
 }
 
+#ifndef GCONV_DWW_WALK_PF
+#define GCONV_DWW_WALK_PF 12
+#endif
+#ifndef GCONV_DWW_WALK_RB1
+#define GCONV_DWW_WALK_RB1 28
+#endif
+#ifndef GCONV_DWW_WALK_RB2
+#define GCONV_DWW_WALK_RB2 14
+#endif
+
+// The walking depthwise gradWeight: 3x3, multiplier 1, unit dilation, stride
+// 1 or 2, a plane's lanes within the wave (S = 1: Wo + 2 of them, S = 2:
+// 2 Wo + 1).
+bool sg_dw_wgrad_walk_plan(const Shape& s, SgDwWalkWArgs* out)
+{
+#ifdef GCONV_SG_NO_DWW_WALK
+    (void)s; (void)out;
+    return false;
+#else
+    if (!(s.kh == 3 && s.kw == 3 && s.dh == 1 && s.dw == 1 && s.sh == s.sw && (s.sh == 1 || s.sh == 2))) return false;
+    if (s.Cg != 1 || s.Kg != 1 || s.N < 1 || s.ph < 0 || s.pw < 0) return false;
+    const int lanes = s.sh == 1 ? s.Wo + 2 : 2 * s.Wo + 1;
+    if (lanes > 64 || (int64_t)s.N * s.G >= (1 << 30)) return false;
+    if ((int64_t)s.H * s.W * 8 >= (int64_t(1) << 30) || (int64_t)s.Ho * s.Wo * 8 >= (int64_t(1) << 30)) return false;
+    SgDwWalkWArgs a{};
+    a.C = s.G; a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo; a.ph = s.ph; a.pw = s.pw;
+    a.planes = s.N * s.G;
+    a.lpw_log2 = lanes <= 16 ? 4 : lanes <= 32 ? 5 : 6;
+    const int RB = s.sh == 1 ? GCONV_DWW_WALK_RB1 : GCONV_DWW_WALK_RB2;
+    a.nbands = (s.Ho + RB - 1) / RB;
+    const int64_t groups = ((int64_t)a.planes + (64 >> a.lpw_log2) - 1) >> (6 - a.lpw_log2);
+    const int64_t waves = groups * a.nbands;
+    if (waves >= (int64_t(1) << 30) || (int64_t)s.N * a.nbands * s.G * 9 >= (int64_t(1) << 31)) return false;
+    a.waves = (int)waves;
+    if (out) *out = a;
+    return true;
+#endif
+}
+
 bool smallgroup_dw_wgrad_ok(const Shape& s) { return sg_dw_wgrad_plan(s, nullptr, nullptr); }
 
 bool smallgroup_fwd_supported(const Shape& s)
@@ -2145,6 +2288,8 @@ size_t smallgroup_bwd_filter_workspace(const Shape& s)
 {
     SgDwWArgs da;
     int mq;
+    SgDwWalkWArgs wa;
+    if (sg_dw_wgrad_walk_plan(s, &wa)) return (size_t)s.N * wa.nbands * s.G * 9 * sizeof(float);
     SgWStreamArgs dsa;
     size_t dlds;
     if (sg_dw_stream_plan(s, &dsa, &mq, &dlds)) return (size_t)dsa.nchunks * s.G * mq * 9 * sizeof(float);
@@ -2180,6 +2325,21 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
 {
     SgDwWArgs da;
     int mq;
+    {
+        SgDwWalkWArgs wa;
+        if (sg_dw_wgrad_walk_plan(s, &wa)) {
+            wa.x = x; wa.dy = dy; wa.ws = ws;
+            const dim3 grid((unsigned)((wa.waves + 3) / 4));
+            if (s.sh == 1)
+                hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<1, GCONV_DWW_WALK_PF, GCONV_DWW_WALK_RB1>), grid, dim3(256), 0, st, wa);
+            else
+                hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<2, GCONV_DWW_WALK_PF, GCONV_DWW_WALK_RB2>), grid, dim3(256), 0, st, wa);
+            const int E = s.G * 9;
+            hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, s.N * wa.nbands,
+                               s.G, 1, 1);
+            return true;
+        }
+    }
     {
         SgWStreamArgs dsa;
         size_t dlds;

@@ -516,6 +516,8 @@ DW_WALK_CASES = [
     (dict(N=1, C=7, K=7, H=20, W=14, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=7), True),
     # padding 2: 18 x 14 outputs, four planes a wave
     (dict(N=2, C=4, K=4, H=16, W=12, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=4), False),
+    # 60 rows of 10: three gradWeight bands (28, 28, 4), four planes a wave, 6 planes
+    (dict(N=1, C=6, K=6, H=60, W=10, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=6), False),
     # asymmetric padding: one row on top, none below, none left, two right
     (dict(N=2, C=6, K=6, H=29, W=20, kh=3, kw=3, sh=1, sw=1, dh=1, dw=1, G=6, ph=1, pb=0, pw=0, pr=2), False),
 ]
@@ -543,13 +545,13 @@ DW_WALK_CASES += [
 
 @pytest.mark.parametrize("case", range(len(DW_WALK_CASES)))
 def test_depthwise_walk(case):
-    """Depthwise forward (bias, optional ReLU) and gradInput at stride 1 and 2
-    on the row-walking kernels against the oracle on every output; integer
-    data bit for bit."""
+    """Depthwise forward (bias, optional ReLU), gradInput and gradWeight at
+    stride 1 and 2 on the row-walking kernels against the oracle on every
+    output; integer data bit for bit."""
     d, relu = DW_WALK_CASES[case]
     kw = conv_kwargs(d)
     desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
-    for op in (G.OP_FWD, G.OP_BWD_DATA):
+    for op in (G.OP_FWD, G.OP_BWD_DATA, G.OP_BWD_FILTER):
         assert G.PATH_NAMES[G.gconv_select_path(desc, op)] == "smallgroup", d
     for dist, seed in ((("normal", 1.0), 2900), (("int", -3, 3), 2950)):
         say("depthwise walk %s relu %s %s" % (d, relu, dist[0]))
@@ -557,10 +559,13 @@ def test_depthwise_walk(case):
         y_ref, ya = oracle.fwd(x, w, b, relu=relu, **kw)
         dy = draw(dist, y_ref.shape, seed + 10 * case + 5)
         dx_ref, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+        dw_ref, dwa = oracle.bwd_filter(x, dy, w.shape, **kw)
         y = G.gconv_fwd(dev(x), dev(w), dev(b), relu=relu, **kw)
         dx = G.gconv_bwd_data(dev(dy), dev(w), x.shape, **kw)
+        dwg = G.gconv_bwd_filter(dev(x), dev(dy), w.shape, **kw)
         torch.cuda.synchronize()
-        for tag, got, val, mag in (("fwd", y, y_ref, ya), ("bwd_data", dx, dx_ref, dxa)):
+        for tag, got, val, mag in (("fwd", y, y_ref, ya), ("bwd_data", dx, dx_ref, dxa),
+                                   ("bwd_filter", dwg, dw_ref, dwa)):
             g = got.cpu().numpy()
             assert g.shape == val.shape, (d, tag)
             if dist[0] == "int":
