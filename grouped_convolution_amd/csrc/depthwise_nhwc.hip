@@ -12,6 +12,8 @@
 // The depthwise layers of the mobilenet family the DLPrimitives Blog
 // validates are the target shapes; TensorFlow stores them channels-last.
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "device_util.h"
 #include "fastdiv.h"
@@ -21,6 +23,15 @@ namespace gconv {
 namespace {
 
 constexpr int kRowPx = 4;  // outputs of a row per thread in the unit-stride kernels
+
+// f(integral_constant<int, I>) for each I of the sequence, in order (a loop
+// unrolled with the index usable as a constant expression).
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
 
 struct DwNhwcArgs {
     const float* in;     // x (forward) or dy (gradInput), NHWC
@@ -537,8 +548,136 @@ __global__ void __launch_bounds__(256) dw_nhwc_wgrad_kernel(DwWgradArgs a)
 // dw[e] = sum over slices (in order) of ws[slice][e]: 16 outputs x 64 slice
 // groups per 1024-thread block; thread (e, sg) adds slices sg, sg + 64, ... in
 // order (16 loads in flight), then the 64 group sums are added in order.
+// gradWeight at unit stride and dilation, 3x3, walking down the rows: a wave
+// owns 64 consecutive (group of V channels, run of PX outputs) units of one
+// image and a band of RB output rows. Each input row's (PX + 2)-column window
+// and each dy row's PX columns are buffer loads of V floats (out-of-range
+// offsets read 0), PF input rows ahead; input row t pairs its tap row i with
+// dy row t - i, held in a ring of registers. A lane keeps the 9 taps x V
+// channels of its unit and writes them as the partial [tap][channel] of
+// (image, band, run of columns); dw_nhwc_wgrad_reduce adds the partials in
+// order. The band is one straight run of code, so the compiler's waits count
+// exactly the rows in flight.
+struct DwWalkWArgs {
+    const float* x;
+    const float* dy;
+    float* ws;           // [N * nbands * nb][9][C]
+    int H, W, Ho, Wo, C, ph, pw;
+    int CV, nb, units, strips, nbands, waves;
+    FastDiv div_cv;
+};
+
+template <int V> struct VecOf;
+template <> struct VecOf<1> { using T = float; };
+template <> struct VecOf<2> { using T = float __attribute__((ext_vector_type(2))); };
+template <> struct VecOf<4> { using T = f4; };
+
+template <int V>
+__device__ __forceinline__ typename VecOf<V>::T load_vec(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    if constexpr (V == 4) return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    else if constexpr (V == 2)
+        return __builtin_bit_cast(typename VecOf<2>::T, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+    else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+template <int V, int PX, int PF, int RB>
+__global__ void __launch_bounds__(256) dw_nhwc_wgrad_walk_kernel(DwWalkWArgs a)
+{
+    using vt = typename VecOf<V>::T;
+    constexpr int NC = PX + 2, NS = RB + 2, NB = PF + 1;
+    constexpr int PFD = PF, NBD = PFD + 3;
+    constexpr uint32_t kColOOB = 0x40000000u, kRowOOB = 0x80000000u;
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (gw >= a.waves) return;
+    const int strip = gw % a.strips;
+    const int nbd = gw / a.strips;
+    const int band = nbd % a.nbands;
+    const int n = nbd / a.nbands;
+    const int ul = strip * 64 + lane;
+    const bool live = ul < a.units;
+    const int u = live ? ul : a.units - 1;
+    const int blk = (int)fastdiv((uint32_t)u, a.div_cv);
+    const int c = (u - blk * a.CV) * V;
+    const int ow0 = blk * PX;
+
+    const uint32_t rowx = (uint32_t)a.W * a.C * 4u, rowd = (uint32_t)a.Wo * a.C * 4u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (size_t)n * a.H * a.W * a.C, (uint32_t)a.H * rowx);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dy + (size_t)n * a.Ho * a.Wo * a.C, (uint32_t)a.Ho * rowd);
+    const int r0 = band * RB;
+    const int rows = min(RB, a.Ho - r0);
+    const int hb = r0 - a.ph;
+    uint32_t xo[NC], dof[PX];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        const int w = ow0 - a.pw + k;
+        xo[k] = live && (unsigned)w < (unsigned)a.W ? (uint32_t)(w * a.C + c) * 4u : kColOOB;
+    }
+#pragma unroll
+    for (int p = 0; p < PX; ++p)
+        dof[p] = live && ow0 + p < a.Wo ? (uint32_t)((r0 * a.Wo + ow0 + p) * a.C + c) * 4u : kColOOB;
+
+    auto loadx = [&](int t, vt (&v)[NC]) {
+        const int h = hb + t;
+        const uint32_t hs = t < rows + 2 && (unsigned)h < (unsigned)a.H ? (uint32_t)h * rowx : kRowOOB;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) v[k] = load_vec<V>(rx, xo[k] + hs);
+    };
+    auto loadd = [&](int q, vt (&v)[PX]) {
+        const uint32_t qs = q < rows ? (uint32_t)q * rowd : kRowOOB;
+#pragma unroll
+        for (int p = 0; p < PX; ++p) v[p] = load_vec<V>(rd, dof[p] + qs);
+    };
+
+    vt acc[9];
+#pragma unroll
+    for (int e = 0; e < 9; ++e) acc[e] = vt{};
+    vt xw[NB][NC], dw[NBD][PX];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) loadx(k, xw[k]);
+#pragma unroll
+    for (int q = 0; q < PFD && q < RB; ++q) loadd(q, dw[q]);
+    unroll_seq(
+        [&](auto sc) {
+            constexpr int t = decltype(sc)::value;
+            // Steps stay in order: hoisting later rows' loads (the code
+            // generator would issue all of them first) holds them all in
+            // registers ...
+            asm volatile("" ::: "memory");
+            if constexpr (t + PF < NS) loadx(t + PF, xw[(t + PF) % NB]);
+            if constexpr (t + PFD < RB) loadd(t + PFD, dw[(t + PFD) % NBD]);
+            unroll_seq(
+                [&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (t >= i && t - i < RB) {
+#pragma unroll
+                        for (int p = 0; p < PX; ++p)
+#pragma unroll
+                            for (int j = 0; j < 3; ++j)
+                                acc[i * 3 + j] = __builtin_elementwise_fma(dw[(t - i) % NBD][p], xw[t % NB][p + j],
+                                                                           acc[i * 3 + j]);
+                    }
+                },
+                std::make_integer_sequence<int, 3>{});
+            // ... and this step's sums are formed before the next step's
+            // loads (else all FMAs sink below all loads).
+            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+                         "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]));
+        },
+        std::make_integer_sequence<int, NS>{});
+
+    if (!live) return;
+    // Partial [slice][tap][channel]: consecutive lanes write consecutive channels.
+    float* out = a.ws + (((size_t)n * a.nbands + band) * a.nb + blk) * ((size_t)a.C * 9) + c;
+#pragma unroll
+    for (int e = 0; e < 9; ++e) *reinterpret_cast<vt*>(out + (size_t)e * a.C) = acc[e];
+}
+
+// TM: the partials are [slice][tap][channel] (the walk's); dw is [channel][tap].
+template <bool TM = false>
 __global__ void __launch_bounds__(1024) dw_nhwc_wgrad_reduce(const float* __restrict__ ws, float* __restrict__ dw,
-                                                             int E, int nslice)
+                                                             int E, int nslice, int C = 0)
 {
     __shared__ float part[64][17];
     const int el = threadIdx.x & 15, sg = threadIdx.x >> 4;
@@ -560,7 +699,8 @@ __global__ void __launch_bounds__(1024) dw_nhwc_wgrad_reduce(const float* __rest
     if (sg != 0 || e >= E) return;
     sum = part[0][el];
     for (int i = 1; i < 64; ++i) sum += part[i][el];
-    dw[e] = sum;
+    if constexpr (TM) dw[(e % C) * 9 + e / C] = sum;
+    else dw[e] = sum;
 }
 
 static bool dw_wgrad_plan(const Shape& s, DwWgradArgs* out, int* nslice)
@@ -594,12 +734,58 @@ bool dw_nhwc_wgrad_supported(const Shape& s)
     return dw_wgrad_plan(s, nullptr, &ns);
 }
 
+#ifndef GCONV_DWN_WALKW_V
+#define GCONV_DWN_WALKW_V 1
+#endif
+#ifndef GCONV_DWN_WALKW_PX
+#define GCONV_DWN_WALKW_PX 8
+#endif
+#ifndef GCONV_DWN_WALKW_PF
+#define GCONV_DWN_WALKW_PF 4
+#endif
+#ifndef GCONV_DWN_WALKW_RB
+#define GCONV_DWN_WALKW_RB 28
+#endif
+
+// The walking gradWeight: 3x3 at unit stride and dilation, channel quads.
+static bool dw_walkw_plan(const Shape& s, DwWalkWArgs* out)
+{
+#ifdef GCONV_DWN_NO_WALKW
+    (void)s; (void)out;
+    return false;
+#else
+    constexpr int V = GCONV_DWN_WALKW_V, PX = GCONV_DWN_WALKW_PX, RB = GCONV_DWN_WALKW_RB;
+    if (!(s.kh == 3 && s.kw == 3 && s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1)) return false;
+    if (!dw_nhwc_supported(s) || (s.C & 3) != 0) return false;
+    if ((int64_t)s.H * s.W * s.C * 4 >= (int64_t(1) << 30) || (int64_t)s.Ho * s.Wo * s.C * 4 >= (int64_t(1) << 30))
+        return false;
+    DwWalkWArgs a{};
+    a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo; a.C = s.C; a.ph = s.ph; a.pw = s.pw;
+    a.CV = s.C / V;
+    a.nb = (s.Wo + PX - 1) / PX;
+    a.units = a.CV * a.nb;
+    a.strips = (a.units + 63) / 64;
+    a.nbands = (s.Ho + RB - 1) / RB;
+    const int64_t waves = (int64_t)s.N * a.nbands * a.strips;
+    const int64_t slices = (int64_t)s.N * a.nbands * a.nb;
+    if (waves >= (int64_t(1) << 30) || slices * s.C * 9 >= (int64_t(1) << 31)) return false;
+    a.waves = (int)waves;
+    a.div_cv = make_fastdiv((uint32_t)a.CV);
+    if (out) *out = a;
+    return true;
+#endif
+}
+
 size_t dw_nhwc_wgrad_workspace(const Shape& s)
 {
     DwWgradArgs a;
     int ns;
-    if (!dw_wgrad_plan(s, &a, &ns) || ns <= 1) return 0;
-    return (size_t)ns * s.C * s.kh * s.kw * sizeof(float);
+    if (!dw_wgrad_plan(s, &a, &ns)) return 0;
+    size_t bytes = ns > 1 ? (size_t)ns * s.C * s.kh * s.kw * sizeof(float) : 0;
+    DwWalkWArgs wa;
+    // (the walk needs 16-byte aligned tensors; the workspace covers both routes)
+    if (dw_walkw_plan(s, &wa)) bytes = std::max(bytes, (size_t)s.N * wa.nbands * wa.nb * s.C * 9 * sizeof(float));
+    return bytes;
 }
 
 bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, float* ws, hipStream_t st)
@@ -607,6 +793,17 @@ bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* 
     DwWgradArgs a;
     int ns;
     if (!dw_wgrad_plan(s, &a, &ns)) return false;
+    DwWalkWArgs wa;
+    if (ws && dw_walkw_plan(s, &wa) && ((uintptr_t)x & 15) == 0 && ((uintptr_t)dy & 15) == 0) {
+        wa.x = x; wa.dy = dy; wa.ws = ws;
+        hipLaunchKernelGGL((dw_nhwc_wgrad_walk_kernel<GCONV_DWN_WALKW_V, GCONV_DWN_WALKW_PX, GCONV_DWN_WALKW_PF,
+                                                      GCONV_DWN_WALKW_RB>),
+                           dim3((unsigned)((wa.waves + 3) / 4)), dim3(256), 0, st, wa);
+        const int E = s.C * 9;
+        hipLaunchKernelGGL(dw_nhwc_wgrad_reduce<true>, dim3((E + 15) / 16), dim3(1024), 0, st, ws, dw, E,
+                           s.N * wa.nbands * wa.nb, s.C);
+        return true;
+    }
     if (ns > 1 && !ws) return false;
     a.x = x; a.dy = dy; a.out = ns > 1 ? ws : dw;
     const int T = s.kh * s.kw;
@@ -636,7 +833,7 @@ bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* 
     }
     if (ns > 1) {
         const int E = s.C * T;
-        hipLaunchKernelGGL(dw_nhwc_wgrad_reduce, dim3((E + 15) / 16), dim3(1024), 0, st, ws, dw, E, ns);
+        hipLaunchKernelGGL(dw_nhwc_wgrad_reduce<false>, dim3((E + 15) / 16), dim3(1024), 0, st, ws, dw, E, ns);
     }
     return true;
 }

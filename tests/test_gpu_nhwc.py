@@ -208,8 +208,9 @@ WALK_CASES = [
 
 @pytest.mark.parametrize("case", range(len(WALK_CASES)))
 def test_nhwc_depthwise_walk(case):
-    """Channels-last depthwise forward (bias, optional ReLU) and gradInput on
-    the row-walking kernel against the oracle; integer data bit for bit."""
+    """Channels-last depthwise forward (bias, optional ReLU), gradInput and
+    gradWeight on the row-walking kernels against the oracle; integer data bit
+    for bit."""
     d, relu = WALK_CASES[case]
     kw = conv_kwargs(d)
     desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout="nhwc", **kw)
@@ -222,10 +223,13 @@ def test_nhwc_depthwise_walk(case):
         y_ref, ya = oracle.fwd(x, w, b, relu=relu, **kw)
         dy = draw(dist, y_ref.shape, seed + 10 * case + 5)
         dx_ref, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+        dw_ref, dwa = oracle.bwd_filter(x, dy, w.shape, **kw)
         y = G.gconv_fwd(dev(to_nhwc(x)), dev(w), dev(b), layout="nhwc", relu=relu, **kw)
         dx = G.gconv_bwd_data(dev(to_nhwc(dy)), dev(w), to_nhwc(x).shape, layout="nhwc", **kw)
+        dwg = G.gconv_bwd_filter(dev(to_nhwc(x)), dev(to_nhwc(dy)), w.shape, layout="nhwc", **kw)
         torch.cuda.synchronize()
-        for tag, got, val, mag in (("fwd", y, to_nhwc(y_ref), to_nhwc(ya)), ("bwd_data", dx, to_nhwc(dx_ref), to_nhwc(dxa))):
+        for tag, got, val, mag in (("fwd", y, to_nhwc(y_ref), to_nhwc(ya)), ("bwd_data", dx, to_nhwc(dx_ref), to_nhwc(dxa)),
+                                   ("bwd_filter", dwg, dw_ref, dwa)):
             g = got.cpu().numpy()
             assert g.shape == val.shape, (d, tag)
             if dist[0] == "int":
