@@ -211,29 +211,54 @@ __global__ void __launch_bounds__(256) dw_nhwc_row_kernel(DwNhwcArgs a)
     }
 }
 
-// Unit stride and dilation, four channels per lane, walking down the rows: a
-// wave owns 64 consecutive (channel quad, run of PX outputs) units of one
-// output row and a band of R output rows, and streams the band's input rows
-// once each. Input row h adds its tap row i to output row h + ph - i, whose
-// sums sit in a ring of KS accumulator rows in registers; an output row is
-// stored as soon as its last input row is in, and the next input row's window
-// is loaded before this row's FMAs. The cached row kernel below fetches every
-// input row once for each output row that reads it, from whichever XCD runs
-// that row; here a band fetches it once (its halo rows twice).
+// Unit stride and dilation, 3x3, walking down the rows: a wave owns 64
+// consecutive (group of V channels, run of PX outputs) units of one output
+// row and a band of RB output rows, and streams the band's input rows once
+// each, PF rows ahead. Input row h adds its tap row i to output row
+// h + ph - i, whose sums sit in a ring of three accumulator rows in registers;
+// an output row is stored as soon as its last input row is in. Loads and
+// stores are buffer operations whose out-of-range offsets read 0 or are
+// dropped, so a band is one straight run of code (two compiler fences a step
+// keep its loads and sums in step order) and the compiler's waits count
+// exactly the rows in flight. The cached row kernel below fetches every input
+// row once for each output row that reads it, from whichever XCD runs that
+// row; here a band fetches it once (its halo rows twice).
 struct DwWalkArgs {
     const float* in;     // x (forward) or dy (gradInput), NHWC
-    const float* wgt;    // [C][KS][KS]
+    const float* wgt;    // [C][3][3]
     const float* bias;   // forward only, may be null
     float* out;          // y or dx, NHWC
     int Hin, Win, Hout, Wout, C, ph, pw, relu;
-    int CQ, units, strips, R, nbands, waves;
-    FastDiv div_cq;
+    int CV, units, strips, nbands, waves;
+    FastDiv div_cv;
 };
 
-template <int KS, int PX, int PF, bool FLIP>
+template <int V> struct VecOf;
+template <> struct VecOf<1> { using T = float; };
+template <> struct VecOf<4> { using T = f4; };
+
+template <int V>
+__device__ __forceinline__ typename VecOf<V>::T load_vec(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    if constexpr (V == 4) return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+template <int V>
+__device__ __forceinline__ void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, typename VecOf<V>::T v)
+{
+    if constexpr (V == 4)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r,
+                                               byte_off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
+}
+
+template <int V, int PX, int PF, int RB, bool FLIP>
 __global__ void __launch_bounds__(256) dw_nhwc_walk_kernel(DwWalkArgs a)
 {
-    constexpr int T = KS * KS, NC = PX + KS - 1;
+    using vt = typename VecOf<V>::T;
+    constexpr int T = 9, NC = PX + 2, NS = RB + 2, NB = PF + 1;
+    constexpr uint32_t kColOOB = 0x40000000u, kRowOOB = 0x80000000u;
     const int lane = threadIdx.x & 63;
     const int gw = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     if (gw >= a.waves) return;
@@ -244,129 +269,122 @@ __global__ void __launch_bounds__(256) dw_nhwc_walk_kernel(DwWalkArgs a)
     const int ul = strip * 64 + lane;
     const bool live = ul < a.units;
     const int u = live ? ul : a.units - 1;
-    const int blk = (int)fastdiv((uint32_t)u, a.div_cq);
-    const int c = (u - blk * a.CQ) * 4;
+    const int blk = (int)fastdiv((uint32_t)u, a.div_cv);
+    const int c = (u - blk * a.CV) * V;
     const int ow0 = blk * PX;
 
-    float wf[4 * T];
-    const f4* w4 = reinterpret_cast<const f4*>(a.wgt + (size_t)c * T);
+    // Weights of the lane's V channels, tap-reversed for gradInput, and bias.
+    vt wv[T];
 #pragma unroll
-    for (int e = 0; e < T; ++e) {
-        const f4 v = w4[e];
-        wf[4 * e] = v.x; wf[4 * e + 1] = v.y; wf[4 * e + 2] = v.z; wf[4 * e + 3] = v.w;
-    }
-    // Weight of channel q at tap (i, j), tap-reversed for gradInput.
-    auto wt = [&](int q, int i, int j) { return FLIP ? wf[q * T + (KS - 1 - i) * KS + (KS - 1 - j)] : wf[q * T + i * KS + j]; };
-    f4 b4 = f4{0.f, 0.f, 0.f, 0.f};
-    if (a.bias) b4 = f4{a.bias[c], a.bias[c + 1], a.bias[c + 2], a.bias[c + 3]};
-
-    const int r0 = band * a.R;
-    const int rows = min(a.R, a.Hout - r0);
-    const int ns = rows + KS - 1;          // input rows the band reads
-    const int hb = r0 - a.ph;              // input row of step 0
-    const float* img = a.in + (size_t)n * a.Hin * a.Win * a.C + c;
-    float* dst = a.out + ((size_t)n * a.Hout + r0) * a.Wout * a.C + (size_t)ow0 * a.C + c;
-    const size_t orow = (size_t)a.Wout * a.C;
-    const int wb = ow0 - a.pw;
-
-    auto load = [&](int t, f4 (&win)[NC]) {
-        const int h = hb + t;
-        const bool hok = (unsigned)h < (unsigned)a.Hin;
-        const float* src = img + (size_t)(hok ? h : 0) * a.Win * a.C;
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-            const int w = wb + k;
-            win[k] = hok && (unsigned)w < (unsigned)a.Win ? *reinterpret_cast<const f4*>(src + (size_t)w * a.C)
-                                                           : f4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < T; ++t) {
+        const int tt = FLIP ? T - 1 - t : t;
+        if constexpr (V == 4) {
+            wv[t] = f4{a.wgt[(size_t)c * T + tt], a.wgt[(size_t)(c + 1) * T + tt], a.wgt[(size_t)(c + 2) * T + tt],
+                       a.wgt[(size_t)(c + 3) * T + tt]};
+        } else {
+            wv[t] = a.wgt[(size_t)c * T + tt];
         }
+    }
+    vt b0 = vt{};
+    if (a.bias) {
+        if constexpr (V == 4) b0 = f4{a.bias[c], a.bias[c + 1], a.bias[c + 2], a.bias[c + 3]};
+        else b0 = a.bias[c];
+    }
+
+    const uint32_t rowi = (uint32_t)a.Win * a.C * 4u, rowo = (uint32_t)a.Wout * a.C * 4u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.in + (size_t)n * a.Hin * a.Win * a.C, (uint32_t)a.Hin * rowi);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.out + (size_t)n * a.Hout * a.Wout * a.C, (uint32_t)a.Hout * rowo);
+    const int r0 = band * RB;
+    const int rows = min(RB, a.Hout - r0);
+    const int hb = r0 - a.ph;
+    uint32_t xo[NC], yo[PX];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        const int w = ow0 - a.pw + k;
+        xo[k] = (unsigned)w < (unsigned)a.Win ? (uint32_t)(w * a.C + c) * 4u : kColOOB;
+    }
+#pragma unroll
+    for (int p = 0; p < PX; ++p)
+        yo[p] = live && ow0 + p < a.Wout ? (uint32_t)((r0 * a.Wout + ow0 + p) * a.C + c) * 4u : kColOOB;
+
+    auto load = [&](int t, vt (&v)[NC]) {
+        const int h = hb + t;
+        const uint32_t hs = t < rows + 2 && (unsigned)h < (unsigned)a.Hin ? (uint32_t)h * rowi : kRowOOB;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) v[k] = load_vec<V>(rx, xo[k] + hs);
     };
 
-    f4 acc[KS][PX];
+    vt acc[3][PX];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int k = 0; k < 3; ++k)
 #pragma unroll
-        for (int p = 0; p < PX; ++p) acc[s][p] = b4;
-    // PF input rows in flight ahead of the one being summed.
-    constexpr int NB = PF + 1;
-    constexpr int UN = KS % NB == 0 ? KS : (NB % KS == 0 ? NB : KS * NB);
-    f4 win[NB][NC];
+        for (int p = 0; p < PX; ++p) acc[k][p] = b0;
+    vt win[NB][NC];
 #pragma unroll
-    for (int k = 0; k < PF; ++k)
-        if (k < ns) load(k, win[k]);
-    // Step t reads input row hb + t; its tap row i goes to output row t - i,
-    // held in ring slot (t - i) mod KS. After step t, row t - (KS - 1) is
-    // complete. Steps are unrolled UN at a time so that the ring slot and the
-    // window buffer of every step are static.
-    for (int m = 0; m < ns; m += UN) {
+    for (int k = 0; k < PF; ++k) load(k, win[k]);
+    unroll_seq(
+        [&](auto sc) {
+            constexpr int t = decltype(sc)::value;
+            asm volatile("" ::: "memory");  // this step's loads stay after the previous step
+            if constexpr (t + PF < NS) load(t + PF, win[(t + PF) % NB]);
 #pragma unroll
-        for (int s = 0; s < UN; ++s) {
-            const int t = m + s;
-            if (t < ns) {
-                if (t + PF < ns) load(t + PF, win[(s + PF) % NB]);
-                f4(&cur)[NC] = win[s % NB];
+            for (int i = 0; i < 3; ++i)
 #pragma unroll
-                for (int i = 0; i < KS; ++i) {
-                    f4(&o)[PX] = acc[(s % KS - i + KS) % KS];
+                for (int p = 0; p < PX; ++p)
 #pragma unroll
-                    for (int p = 0; p < PX; ++p)
+                    for (int j = 0; j < 3; ++j)
+                        acc[(t - i + 3) % 3][p] =
+                            __builtin_elementwise_fma(wv[i * 3 + j], win[t % NB][p + j], acc[(t - i + 3) % 3][p]);
+            // Slot (t + 1) mod 3 is complete (output t - 2), or before step 2
+            // holds only taps of rows above the band's first output.
+            vt(&done)[PX] = acc[(t + 1) % 3];
+            if constexpr (t >= 2) {
+                const uint32_t rs = t - 2 < rows ? (uint32_t)(t - 2) * rowo : kRowOOB;
 #pragma unroll
-                        for (int j = 0; j < KS; ++j) {
-                            o[p].x = fmaf(wt(0, i, j), cur[p + j].x, o[p].x);
-                            o[p].y = fmaf(wt(1, i, j), cur[p + j].y, o[p].y);
-                            o[p].z = fmaf(wt(2, i, j), cur[p + j].z, o[p].z);
-                            o[p].w = fmaf(wt(3, i, j), cur[p + j].w, o[p].w);
-                        }
+                for (int p = 0; p < PX; ++p) {
+                    vt v = done[p];
+                    if (a.relu) v = __builtin_elementwise_max(v, vt{});
+                    store_vec<V>(ry, yo[p] + rs, v);
                 }
-                const int q = t - (KS - 1);
-                f4(&done)[PX] = acc[(s % KS + 1) % KS];
-                if (q >= 0 && live) {
-#pragma unroll
-                    for (int p = 0; p < PX; ++p) {
-                        if (ow0 + p >= a.Wout) break;
-                        f4 v = done[p];
-                        v.x = relu_if(v.x, a.relu); v.y = relu_if(v.y, a.relu);
-                        v.z = relu_if(v.z, a.relu); v.w = relu_if(v.w, a.relu);
-                        *reinterpret_cast<f4*>(dst + (size_t)q * orow + (size_t)p * a.C) = v;
-                    }
-                }
-#pragma unroll
-                for (int p = 0; p < PX; ++p) done[p] = b4;
             }
-        }
-    }
+#pragma unroll
+            for (int p = 0; p < PX; ++p) {
+                done[p] = b0;
+                asm volatile("" : "+v"(acc[0][p]), "+v"(acc[1][p]), "+v"(acc[2][p]));  // sums formed in this step
+            }
+        },
+        std::make_integer_sequence<int, NS>{});
 }
 
+#ifndef GCONV_DW_WALK_V
+#define GCONV_DW_WALK_V 4
+#endif
 #ifndef GCONV_DW_WALK_PX
 #define GCONV_DW_WALK_PX 4
 #endif
-#ifndef GCONV_DW_WALK_WAVES
-#define GCONV_DW_WALK_WAVES 2048
-#endif
 #ifndef GCONV_DW_WALK_PF
-#define GCONV_DW_WALK_PF 1
+#define GCONV_DW_WALK_PF 2
+#endif
+#ifndef GCONV_DW_WALK_RB
+#define GCONV_DW_WALK_RB 14
 #endif
 
-template <int KS, bool FLIP>
+template <bool FLIP>
 void launch_walk(const DwNhwcArgs& s, hipStream_t st)
 {
-    constexpr int PX = GCONV_DW_WALK_PX;
+    constexpr int V = GCONV_DW_WALK_V, PX = GCONV_DW_WALK_PX, RB = GCONV_DW_WALK_RB;
     DwWalkArgs a{};
     a.in = s.in; a.wgt = s.wgt; a.bias = s.bias; a.out = s.out;
     a.Hin = s.Hin; a.Win = s.Win; a.Hout = s.Hout; a.Wout = s.Wout; a.C = s.C;
     a.ph = s.ph; a.pw = s.pw; a.relu = s.relu;
-    a.CQ = s.CQ;
-    a.div_cq = make_fastdiv((uint32_t)a.CQ);
-    a.units = a.CQ * ((a.Wout + PX - 1) / PX);
+    a.CV = s.C / V;
+    a.div_cv = make_fastdiv((uint32_t)a.CV);
+    a.units = a.CV * ((a.Wout + PX - 1) / PX);
     a.strips = (a.units + 63) / 64;
-    // Bands: about GCONV_DW_WALK_WAVES waves in all (two a SIMD), so that every
-    // wave is resident at once and the halo rows stay a small fraction.
-    const int64_t per_band = (int64_t)s.N * a.strips;
-    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(a.Hout, (GCONV_DW_WALK_WAVES + per_band / 2) / per_band));
-    a.R = (a.Hout + nb - 1) / nb;
-    a.nbands = (a.Hout + a.R - 1) / a.R;
-    a.waves = (int)(per_band * a.nbands);
+    a.nbands = (a.Hout + RB - 1) / RB;
+    a.waves = (int)((int64_t)s.N * a.strips * a.nbands);
     const unsigned blocks = (unsigned)((a.waves + 3) / 4);
-    hipLaunchKernelGGL((dw_nhwc_walk_kernel<KS, PX, GCONV_DW_WALK_PF, FLIP>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dw_nhwc_walk_kernel<V, PX, GCONV_DW_WALK_PF, RB, FLIP>), dim3(blocks), dim3(256), 0, st, a);
 }
 
 template <int KS, bool FLIP>
@@ -566,20 +584,6 @@ struct DwWalkWArgs {
     int CV, nb, units, strips, nbands, waves;
     FastDiv div_cv;
 };
-
-template <int V> struct VecOf;
-template <> struct VecOf<1> { using T = float; };
-template <> struct VecOf<2> { using T = float __attribute__((ext_vector_type(2))); };
-template <> struct VecOf<4> { using T = f4; };
-
-template <int V>
-__device__ __forceinline__ typename VecOf<V>::T load_vec(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
-{
-    if constexpr (V == 4) return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-    else if constexpr (V == 2)
-        return __builtin_bit_cast(typename VecOf<2>::T, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
-    else return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
-}
 
 template <int V, int PX, int PF, int RB>
 __global__ void __launch_bounds__(256) dw_nhwc_wgrad_walk_kernel(DwWalkWArgs a)
@@ -841,7 +845,13 @@ bool dw_nhwc_bwd_filter(const Shape& s, const float* x, const float* dy, float* 
 static bool unit(const Shape& s) { return s.sh == 1 && s.sw == 1 && s.dh == 1 && s.dw == 1; }
 // 3x3 walks down the rows; 5x5 (a ring of five accumulator rows and a
 // seven-column window) would leave one wave a SIMD, and keeps the row kernel.
-static bool walk_ok(const Shape& s) { return s.kh == 3; }
+// The walk's buffer offsets cover one image of either tensor below 2^30 bytes.
+static bool walk_ok(const Shape& s)
+{
+    return s.kh == 3 && (int64_t)s.H * s.W * s.C * 4 < (int64_t(1) << 30) &&
+           (int64_t)s.Ho * s.Wo * s.C * 4 < (int64_t(1) << 30) &&
+           (int64_t)s.N * std::max(s.H, s.Ho) * ((std::max(s.W, s.Wo) + 3) / 4 * s.C / 4 + 64) < (int64_t(1) << 30);
+}
 
 void dw_nhwc_fwd(const Shape& s, const float* x, const float* w, const float* bias, float* y, hipStream_t st)
 {
@@ -851,7 +861,7 @@ void dw_nhwc_fwd(const Shape& s, const float* x, const float* w, const float* bi
     if (vec && unit(s)) {
 #ifndef GCONV_DW_NHWC_NO_WALK
         if (walk_ok(s)) {
-            launch_walk<3, false>(a, st);
+            launch_walk<false>(a, st);
             return;
         }
 #endif
@@ -874,7 +884,7 @@ void dw_nhwc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx
         a.pw = s.kw - 1 - s.pw;
 #ifndef GCONV_DW_NHWC_NO_WALK
         if (walk_ok(s)) {
-            launch_walk<3, true>(a, st);
+            launch_walk<true>(a, st);
             return;
         }
 #endif
