@@ -200,6 +200,12 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
     if constexpr (!RIMG) {
         stage_offsets<A_RC>(offa, m0, a.M, r_begin, a.a_ld, wave, lane);
         stage_offsets<B_RC>(offb, n0, a.N, r_begin, a.b_ld, wave, lane);
+    } else {
+        // The image-split reduction: lane parts at reduction index 0; a stage
+        // inside one image adds the image's and the position's offset as the
+        // scalar offset.
+        stage_offsets<A_RC>(offa, m0, a.M, 0, a.a_ld, wave, lane);
+        stage_offsets<B_RC>(offb, n0, a.N, 0, a.b_ld, wave, lane);
     }
     const uint32_t step_a = A_RC ? BR * 4u : (uint32_t)(BR * a.a_ld) * 4u;
     const uint32_t step_b = B_RC ? BR * 4u : (uint32_t)(BR * a.b_ld) * 4u;
@@ -210,6 +216,16 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
             load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)stage * step_a, wave);
             load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)stage * step_b, wave);
             return;
+        }
+        if constexpr (RIMG) {
+            const int r0 = __builtin_amdgcn_readfirstlane(r_begin + stage * BR);
+            const int img = (int)fastdiv((uint32_t)r0, a.div_rimg);
+            const int p0 = r0 - img * a.r_img;
+            if (r0 + BR <= r_end && p0 + BR <= a.r_img) {
+                load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)(img * a.a_is + p0) * 4u, wave);
+                load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)(img * a.b_is + p0) * 4u, wave);
+                return;
+            }
         }
         load_stage<A_RC, RIMG>(ra, ta, m0, a.M, r_begin + stage * BR, r_end, a.a_ld, wave, lane, &a, a.a_is);
         load_stage<B_RC, RIMG>(rb, tb, n0, a.N, r_begin + stage * BR, r_end, a.b_ld, wave, lane, &a, a.b_is);
