@@ -1690,8 +1690,8 @@ bool sg_dw_walk_ok(const SgProblem& p)
     if (!(p.kh == 3 && p.kw == 3 && p.dh == 1 && p.dw == 1 && p.Cin_g == 1 && p.Cout_g == 1)) return false;
     if (!(p.uh == 1 && p.uw == 1 && p.sh == 1 && p.sw == 1)) return false;
     if (p.Wout + 2 > 64 || p.N < 1 || (int64_t)p.N * p.G >= (1 << 30)) return false;
-    // Two planes' bytes stay below 2^30 (the buffer offsets of the kernel).
-    return (int64_t)p.Hin * p.Win * 8 < (int64_t(1) << 30) && (int64_t)p.Hout * p.Wout * 8 < (int64_t(1) << 30);
+    // A wave's (up to four) planes stay below 2^30 bytes (the buffer offsets of the kernel).
+    return (int64_t)p.Hin * p.Win * 16 < (int64_t(1) << 30) && (int64_t)p.Hout * p.Wout * 16 < (int64_t(1) << 30);
 #endif
 }
 
@@ -1742,7 +1742,7 @@ bool sg_dw_walk_s2_ok(const SgProblem& p)
     if (!(p.kh == 3 && p.kw == 3 && p.dh == 1 && p.dw == 1 && p.Cin_g == 1 && p.Cout_g == 1)) return false;
     if (!(p.uh == 1 && p.uw == 1 && p.sh == 2 && p.sw == 2 && !p.flip)) return false;
     if (2 * p.Wout + 1 > 64 || p.N < 1 || (int64_t)p.N * p.G >= (1 << 30)) return false;
-    return (int64_t)p.Hin * p.Win * 8 < (int64_t(1) << 30) && (int64_t)p.Hout * p.Wout * 8 < (int64_t(1) << 30);
+    return (int64_t)p.Hin * p.Win * 16 < (int64_t(1) << 30) && (int64_t)p.Hout * p.Wout * 16 < (int64_t(1) << 30);
 #endif
 }
 
@@ -2168,7 +2168,7 @@ bool sg_dw_wgrad_walk_plan(const Shape& s, SgDwWalkWArgs* out)
     if (s.Cg != 1 || s.Kg != 1 || s.N < 1 || s.ph < 0 || s.pw < 0) return false;
     const int lanes = s.sh == 1 ? s.Wo + 2 : 2 * s.Wo + 1;
     if (lanes > 64 || (int64_t)s.N * s.G >= (1 << 30)) return false;
-    if ((int64_t)s.H * s.W * 8 >= (int64_t(1) << 30) || (int64_t)s.Ho * s.Wo * 8 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)s.H * s.W * 16 >= (int64_t(1) << 30) || (int64_t)s.Ho * s.Wo * 16 >= (int64_t(1) << 30)) return false;
     SgDwWalkWArgs a{};
     a.C = s.G; a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo; a.ph = s.ph; a.pw = s.pw;
     a.planes = s.N * s.G;
@@ -2236,7 +2236,7 @@ static bool sg_dw_walk_dgrad_s2_plan(const Shape& s, SgDwWalkDArgs* out)
     if (!(s.kh == 3 && s.kw == 3 && s.sh == 2 && s.sw == 2 && s.dh == 1 && s.dw == 1)) return false;
     if (s.Cg != 1 || s.Kg != 1 || s.N < 1 || s.ph < 0 || s.pw < 0 || s.W + 2 > 64) return false;
     if ((int64_t)s.N * s.G >= (1 << 30)) return false;
-    if ((int64_t)s.H * s.W * 8 >= (int64_t(1) << 30) || (int64_t)s.Ho * s.Wo * 8 >= (int64_t(1) << 30)) return false;
+    if ((int64_t)s.H * s.W * 16 >= (int64_t(1) << 30) || (int64_t)s.Ho * s.Wo * 16 >= (int64_t(1) << 30)) return false;
     SgDwWalkDArgs a{};
     a.C = s.G; a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo; a.ph = s.ph; a.pw = s.pw;
     a.planes = s.N * s.G;
