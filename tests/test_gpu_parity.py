@@ -540,6 +540,11 @@ DW_WALK_CASES += [
     # 7-column outputs (four forward planes a wave); two zero rows on top and
     # none below, one zero column each side
     (dict(N=2, C=9, K=9, H=33, W=13, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=9, ph=2, pb=0, pw=1, pr=1), False),
+    # the widest rows of the stride-2 walks: 31 outputs on lanes 0 .. 62 (forward and
+    # gradWeight), 62 dx columns on lanes 2 .. 63 (gradInput)
+    (dict(N=1, C=3, K=3, H=12, W=62, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=3, ph=0, pb=1, pw=0, pr=1), True),
+    # 30 outputs a row at unit stride: two planes a wave, each its 32 lanes exactly
+    (dict(N=1, C=3, K=3, H=9, W=30, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=3), True),
 ]
 
 
