@@ -1436,6 +1436,7 @@ struct SgDwWalkWArgs {
     float* ws;           // [N * nbands][C][9]
     int C, H, W, Ho, Wo, ph, pw;
     int planes, lpw_log2, nbands, waves;
+    int rb;              // dy rows per band (the kernel's RB)
 };
 
 template <int S, int PF, int RB>
@@ -1491,6 +1492,10 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_walk_kernel(SgDwWalkWArgs a)
     unroll_seq(
         [&](auto sc) {
             constexpr int t = decltype(sc)::value;
+            // Steps stay in order: hoisting later rows' loads (the code
+            // generator would issue most of them first) holds them all in
+            // registers and cuts the waves a SIMD keeps ...
+            asm volatile("" ::: "memory");
             if constexpr (t + PF < NS) xw[(t + PF) % NB] = loadx(t + PF);
             // dy row q + PFD is loaded at the first step that pairs with row q.
             if constexpr (t % S == 0 && t / S + PFD < RB) dw[(t / S + PFD) % NBD] = loadd(t / S + PFD);
@@ -1508,6 +1513,10 @@ __global__ void __launch_bounds__(256) sg_dw_wgrad_walk_kernel(SgDwWalkWArgs a)
                     }
                 },
                 std::make_integer_sequence<int, 3>{});
+            // ... and this step's sums are formed before the next step's
+            // loads (else the FMAs sink below them).
+            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]),
+                         "+v"(acc[6]), "+v"(acc[7]), "+v"(acc[8]));
         },
         std::make_integer_sequence<int, NS>{});
 
@@ -2148,11 +2157,20 @@ bool sg_dw_stream_plan(const Shape& s, SgWStreamArgs* out, int* mq, size_t* lds)
 #ifndef GCONV_DWW_WALK_PF
 #define GCONV_DWW_WALK_PF 12
 #endif
+// dy rows per band: a long band where the planes are tall enough to fill it
+// most of the way (fewer halo rows and partials), else a short one (its
+// unrolled steps past the last row would still be issued).
 #ifndef GCONV_DWW_WALK_RB1
-#define GCONV_DWW_WALK_RB1 28
+#define GCONV_DWW_WALK_RB1 56
+#endif
+#ifndef GCONV_DWW_WALK_RB1S
+#define GCONV_DWW_WALK_RB1S 28
 #endif
 #ifndef GCONV_DWW_WALK_RB2
-#define GCONV_DWW_WALK_RB2 14
+#define GCONV_DWW_WALK_RB2 28
+#endif
+#ifndef GCONV_DWW_WALK_RB2S
+#define GCONV_DWW_WALK_RB2S 14
 #endif
 
 // The walking depthwise gradWeight: 3x3, multiplier 1, unit dilation, stride
@@ -2173,7 +2191,9 @@ bool sg_dw_wgrad_walk_plan(const Shape& s, SgDwWalkWArgs* out)
     a.C = s.G; a.H = s.H; a.W = s.W; a.Ho = s.Ho; a.Wo = s.Wo; a.ph = s.ph; a.pw = s.pw;
     a.planes = s.N * s.G;
     a.lpw_log2 = lanes <= 16 ? 4 : lanes <= 32 ? 5 : 6;
-    const int RB = s.sh == 1 ? GCONV_DWW_WALK_RB1 : GCONV_DWW_WALK_RB2;
+    const int RB = s.sh == 1 ? (s.Ho > GCONV_DWW_WALK_RB1S ? GCONV_DWW_WALK_RB1 : GCONV_DWW_WALK_RB1S)
+                             : (s.Ho > GCONV_DWW_WALK_RB2S ? GCONV_DWW_WALK_RB2 : GCONV_DWW_WALK_RB2S);
+    a.rb = RB;
     a.nbands = (s.Ho + RB - 1) / RB;
     const int64_t groups = ((int64_t)a.planes + (64 >> a.lpw_log2) - 1) >> (6 - a.lpw_log2);
     const int64_t waves = groups * a.nbands;
@@ -2330,10 +2350,18 @@ bool smallgroup_bwd_filter(const Shape& s, const float* x, const float* dy, floa
         if (sg_dw_wgrad_walk_plan(s, &wa)) {
             wa.x = x; wa.dy = dy; wa.ws = ws;
             const dim3 grid((unsigned)((wa.waves + 3) / 4));
-            if (s.sh == 1)
-                hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<1, GCONV_DWW_WALK_PF, GCONV_DWW_WALK_RB1>), grid, dim3(256), 0, st, wa);
-            else
-                hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<2, GCONV_DWW_WALK_PF, GCONV_DWW_WALK_RB2>), grid, dim3(256), 0, st, wa);
+            constexpr int PF = GCONV_DWW_WALK_PF;
+            if (s.sh == 1) {
+                if (wa.rb == GCONV_DWW_WALK_RB1)
+                    hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<1, PF, GCONV_DWW_WALK_RB1>), grid, dim3(256), 0, st, wa);
+                else
+                    hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<1, PF, GCONV_DWW_WALK_RB1S>), grid, dim3(256), 0, st, wa);
+            } else {
+                if (wa.rb == GCONV_DWW_WALK_RB2)
+                    hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<2, PF, GCONV_DWW_WALK_RB2>), grid, dim3(256), 0, st, wa);
+                else
+                    hipLaunchKernelGGL((sg_dw_wgrad_walk_kernel<2, PF, GCONV_DWW_WALK_RB2S>), grid, dim3(256), 0, st, wa);
+            }
             const int E = s.G * 9;
             hipLaunchKernelGGL(sg_dw_wgrad_reduce, dim3((E + 15) / 16), dim3(256), 0, st, ws, dw, s.N * wa.nbands,
                                s.G, 1, 1);

@@ -516,7 +516,7 @@ DW_WALK_CASES = [
     (dict(N=1, C=7, K=7, H=20, W=14, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=7), True),
     # padding 2: 18 x 14 outputs, four planes a wave
     (dict(N=2, C=4, K=4, H=16, W=12, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=4), False),
-    # 60 rows of 10: three gradWeight bands (28, 28, 4), four planes a wave, 6 planes
+    # 60 rows of 10: two gradWeight bands (56, 4), four planes a wave, 6 planes
     (dict(N=1, C=6, K=6, H=60, W=10, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=6), False),
     # asymmetric padding: one row on top, none below, none left, two right
     (dict(N=2, C=6, K=6, H=29, W=20, kh=3, kw=3, sh=1, sw=1, dh=1, dw=1, G=6, ph=1, pb=0, pw=0, pr=2), False),
@@ -545,7 +545,63 @@ DW_WALK_CASES += [
     (dict(N=1, C=3, K=3, H=12, W=62, kh=3, kw=3, sh=2, sw=2, dh=1, dw=1, G=3, ph=0, pb=1, pw=0, pr=1), True),
     # 30 outputs a row at unit stride: two planes a wave, each its 32 lanes exactly
     (dict(N=1, C=3, K=3, H=9, W=30, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=3), True),
+    # 120 x 20 -> 60 x 10 at stride 2: three gradWeight bands (28, 28, 4), two
+    # planes a wave
+    (dict(N=1, C=4, K=4, H=120, W=20, kh=3, kw=3, sh=2, sw=2, ph=1, pw=1, dh=1, dw=1, G=4), False),
 ]
+
+
+# Groups of two to four input and up to four output channels, 3x3 at unit
+# stride (forward, and gradInput as the forward of dy with reversed taps), on
+# the banded row kernel (one 64-float LDS row per input row, bands of up to
+# 16 output rows).
+SG_ROW_CASES = [
+    # 4 in / 4 out, 62 outputs a row (the widest tile row: 64 floats), 30 rows
+    # in two bands of 15, bias and ReLU
+    (dict(N=2, C=16, K=16, H=30, W=62, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=4), True),
+    # 3 in / 2 out, no padding: 15 x 19 outputs in one band
+    (dict(N=1, C=12, K=8, H=17, W=21, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=4), False),
+    # 2 in / 4 out with padding 2: 11 x 42 outputs
+    (dict(N=3, C=6, K=12, H=9, W=40, kh=3, kw=3, sh=1, sw=1, ph=2, pw=2, dh=1, dw=1, G=3), True),
+    # 1 in / 4 out (channel multiplier 4): the forward takes the depthwise
+    # kernel, gradInput (4 in / 1 out) the row kernel
+    (dict(N=1, C=5, K=20, H=28, W=28, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=5), False),
+    # asymmetric padding: one row on top, none below, none left, two right
+    (dict(N=2, C=8, K=8, H=29, W=20, kh=3, kw=3, sh=1, sw=1, dh=1, dw=1, G=2, ph=1, pb=0, pw=0, pr=2), False),
+    # 4 in / 3 out at 56 x 56: four bands of 14
+    (dict(N=2, C=8, K=6, H=56, W=56, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2), True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SG_ROW_CASES)))
+def test_smallgroup_rows(case):
+    """Small groups at unit stride on the banded row kernel: forward (bias,
+    optional ReLU) and gradInput against the oracle on every output, gradWeight
+    alongside; integer data bit for bit."""
+    d, relu = SG_ROW_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
+    for op in (G.OP_FWD, G.OP_BWD_DATA):
+        assert G.PATH_NAMES[G.gconv_select_path(desc, op)] == "smallgroup", d
+    for dist, seed in ((("normal", 1.0), 3100), (("int", -3, 3), 3150)):
+        say("small-group rows %s relu %s %s" % (d, relu, dist[0]))
+        x, w, b = tensors(d, seed + 10 * case, dist=dist)
+        y_ref, ya = oracle.fwd(x, w, b, relu=relu, **kw)
+        dy = draw(dist, y_ref.shape, seed + 10 * case + 5)
+        dx_ref, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+        dw_ref, dwa = oracle.bwd_filter(x, dy, w.shape, **kw)
+        y = G.gconv_fwd(dev(x), dev(w), dev(b), relu=relu, **kw)
+        dx = G.gconv_bwd_data(dev(dy), dev(w), x.shape, **kw)
+        dwg = G.gconv_bwd_filter(dev(x), dev(dy), w.shape, **kw)
+        torch.cuda.synchronize()
+        for tag, got, val, mag in (("fwd", y, y_ref, ya), ("bwd_data", dx, dx_ref, dxa),
+                                   ("bwd_filter", dwg, dw_ref, dwa)):
+            g = got.cpu().numpy()
+            assert g.shape == val.shape, (d, tag)
+            if dist[0] == "int":
+                assert np.array_equal(g.astype(np.float64), val), (d, tag)
+            else:
+                check("sg rows %s %s" % (tag, d), g, val, mag)
 
 
 @pytest.mark.parametrize("case", range(len(DW_WALK_CASES)))
