@@ -15,7 +15,7 @@
 //
 // Block = 4 waves arranged WC (input-channel fragments) x 4/WC, each wave
 // 16 input channels x 16*WK output channels x all taps (for the wide 9-tap
-// tile, two such sets of 4 waves split each chunk's pixels and add their sums
+// tile, four such sets of 4 waves split each chunk's pixels and add their sums
 // at the end, in a fixed order). The pixel reduction
 // is split: the N*Ho output rows are cut into chunks of R rows of one image,
 // and each block reduces a contiguous run of chunks for one (group, input tile,
@@ -56,6 +56,43 @@ struct WgradArgs {
 // a pixel's quad, so a 64-lane instruction fills 64 pixels of one quad plane
 // (nsx, nsd: such segments per quad plane). A half-wave's operand reads (16
 // channels as 4 quads x 4, at 2 pixels) then fall in 32 distinct banks.
+
+// The NH wave sets of a block hold sums over disjoint pixels of the same
+// tile. They are added down a fixed tree through LDS (the tile buffers are
+// free after the chunk loop's last barrier): set h + half hands its sums to
+// set h, for half = NH/2, NH/4, .., 1, so set 0 ends with
+// ((s0 + s2) + (s1 + s3)) for four sets. Every wave takes part in the
+// barriers; returns whether this wave holds the block's total (set 0).
+template <int T, int WK, int NH>
+__device__ __forceinline__ bool sum_wave_sets(f4 (&acc)[T][WK], float* lds, int wq, int h, int lane)
+{
+    static_assert(NH == 1 || NH == 2 || NH == 4, "wave sets: 1, 2 or 4");
+    constexpr int SLOT = T * WK * 256;  // floats of one wave's sums
+#pragma unroll
+    for (int half = NH / 2; half >= 1; half /= 2) {
+        if (h >= half && h < 2 * half) {
+            float* xch = lds + (size_t)((h - half) * 4 + wq) * SLOT + lane;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int m = 0; m < WK; ++m)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) xch[(t * WK + m) * 256 + v * 64] = acc[t][m][v];
+        }
+        __syncthreads();
+        if (h < half) {
+            const float* xch = lds + (size_t)(h * 4 + wq) * SLOT + lane;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int m = 0; m < WK; ++m)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[t][m][v] += xch[(t * WK + m) * 256 + v * 64];
+        }
+        if (half > 1) __syncthreads();  // the next round's writers reuse the slots
+    }
+    return h == 0;
+}
 
 template <int KH, int KW, int WC, int WK, int R, int NH>
 __device__ __forceinline__ void wgrad_nhwc_body(const WgradArgs& a, int kt, int ct, int g, int s, int ch_begin,
@@ -220,25 +257,7 @@ __device__ __forceinline__ void wgrad_nhwc_body(const WgradArgs& a, int kt, int 
         __syncthreads();
     }
 
-    if constexpr (NH == 2) {
-        float* xch = lds + (size_t)wq * (T * WK * 256) + lane;
-        if (h == 1) {
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int m = 0; m < WK; ++m)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) xch[(t * WK + m) * 256 + v * 64] = acc[t][m][v];
-        }
-        __syncthreads();
-        if (h == 1) return;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int m = 0; m < WK; ++m)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][m][v] += xch[(t * WK + m) * 256 + v * 64];
-    }
+    if (!sum_wave_sets<T, WK, NH>(acc, lds, wq, h, lane)) return;
     const int tile = (g * a.n_ctiles + ct) * a.n_ktiles + kt;
     const int n_tiles = a.G * a.n_ctiles * a.n_ktiles;
     float* out = a.ws + (((size_t)s * n_tiles + tile) * 4 + wq) * (size_t)(T * WK * 256);
@@ -263,9 +282,9 @@ __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l16 = lane & 15, q = lane >> 4;
-    // Waves wq = wave % 4 own the output sub-tiles; with NH = 2 a second set
-    // of four (h = 1) shares them and takes the second half of every chunk's
-    // pixels, so two waves per SIMD hide each other's stalls.
+    // Waves wq = wave % 4 own the output sub-tiles; with NH > 1 further sets
+    // of four (h = 1 .. NH - 1) share them, each taking its slice of every
+    // chunk's pixels, so NH waves per SIMD hide each other's stalls.
     const int wq = wave & 3, h = wave >> 2;
     const int wc = wq % WC, wk = wq / WC;
 
@@ -446,27 +465,7 @@ __global__ void __launch_bounds__(256 * NH) wgrad_mfma_kernel(WgradArgs a)
         __syncthreads();  // every wave is done with buffer b before it is refilled
     }
 
-    if constexpr (NH == 2) {
-        // The second wave set hands its sums to the first through LDS (the
-        // tile buffers are free after the last barrier of the chunk loop).
-        float* xch = lds + (size_t)wq * (T * WK * 256) + lane;
-        if (h == 1) {
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int m = 0; m < WK; ++m)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) xch[(t * WK + m) * 256 + v * 64] = acc[t][m][v];
-        }
-        __syncthreads();
-        if (h == 1) return;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int m = 0; m < WK; ++m)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][m][v] += xch[(t * WK + m) * 256 + v * 64];
-    }
+    if (!sum_wave_sets<T, WK, NH>(acc, lds, wq, h, lane)) return;
 
     // Partial tile in accumulator order: [split][tile][wave][t][m][v][lane].
     const int tile = (g * a.n_ctiles + ct) * a.n_ktiles + kt;
@@ -566,6 +565,11 @@ Plan make_plan(const Shape& s, bool nhwc = false)
 #ifndef GCONV_WGRAD_WIDE
 #define GCONV_WGRAD_WIDE 0
 #endif
+// Wave sets of the wide 9-tap tile: four (16 waves, four a SIMD) measured
+// 87.6-88.8 against 90.0-90.3 us on dense3x3's gradWeight with two.
+#ifndef GCONV_WGRAD_NH
+#define GCONV_WGRAD_NH 4
+#endif
     // 9-tap tiles with >= 32 input and output channels per group: two wave
     // sets per block (8 waves) on a 32 x 32 tile whose LDS stays under 80 KiB,
     // so two blocks share a CU and one block's barriers and loads overlap the
@@ -574,7 +578,7 @@ Plan make_plan(const Shape& s, bool nhwc = false)
     if (GCONV_WGRAD_WIDE >= 1 && T <= 9 && s.Cg >= 32 && s.Kg >= 32) {
         cfg = {2, 1, 0, 2};
         if (GCONV_WGRAD_WIDE == 1) lds_cap = 80 * 1024;
-    } else if (T <= 9 && s.Cg >= 32 && s.Kg >= 64) cfg = {2, 2, 0, 2};
+    } else if (T <= 9 && s.Cg >= 32 && s.Kg >= 64) cfg = {2, 2, 0, GCONV_WGRAD_NH};
     else if (T > 9 && s.Kg >= 128) cfg = {1, 2, 0, 1};
     else cfg = {1, 1, 0, 1};
     const int CT = 16 * cfg.WC, KT = 16 * cfg.WK * (4 / cfg.WC);
@@ -604,7 +608,8 @@ Plan make_plan(const Shape& s, bool nhwc = false)
             p.lds_bytes = 2 * ((size_t)CT * a.XS + (size_t)KT * a.DS) * 4;
         }
         // The second wave set's sums pass through LDS at the end.
-        if (cfg.NH == 2) p.lds_bytes = std::max(p.lds_bytes, (size_t)4 * T * cfg.WK * 256 * 4);
+        // The wave sets' sums pass through LDS at the end: NH / 2 sets at once.
+        if (cfg.NH > 1) p.lds_bytes = std::max(p.lds_bytes, (size_t)(cfg.NH / 2) * 4 * T * cfg.WK * 256 * 4);
         if (a.nsx <= kMaxSegX && a.nsd <= kMaxSegD && p.lds_bytes <= (size_t)lds_cap) break;
     }
     cfg.R = R;
@@ -697,7 +702,7 @@ static bool run_wgrad(Plan& p, const Shape& s, const float* x, const float* dy, 
     p.a.ws = ws;
     const Config c = p.cfg;
     if (s.kh == 3 && c.WC == 2 && c.WK == 2) {
-        if (!launch_r<3, 3, 2, 2, 2, INH>(p, st)) return false;
+        if (!launch_r<3, 3, 2, 2, GCONV_WGRAD_NH, INH>(p, st)) return false;
         launch_reduce<9, 2, 2>(p, s, ws, dw, st);
     } else if (s.kh == 3 && c.WC == 2 && c.WK == 1) {
         if (!launch_r<3, 3, 2, 1, 2, INH>(p, st)) return false;
