@@ -959,8 +959,14 @@ bool flat_plan(const Problem& p_in, FlatPlan& fp)
         const int BPXi = fi.WPX * fi.MP * 16;
         if (P < BPXi) continue;  // a tile must span at most two images
         const int halo = (p.kh - 1) * p.dh + 1;
-        const int R = (int)std::min<int64_t>(p.Hout, (BPXi - 1) / p.Wout + 2);  // output rows per tile
-        const int LR = std::max((R - 1) * p.sh + halo, (R - 2) * p.sh + 2 * halo);
+        // Output rows a tile's BPXi consecutive pixels touch: at most `span`
+        // in all, at most Hout of them in one image. A tile that crosses into
+        // the next image stages both images' rows, each part with its own
+        // halo, and its parts together may hold more rows than one image has.
+        const int64_t span = (BPXi - 1) / p.Wout + 2;
+        const int R1 = (int)std::min<int64_t>(p.Hout, span);      // within one image
+        const int R2 = (int)std::min<int64_t>(2 * (int64_t)p.Hout, span);  // across two
+        const int LR = std::max((R1 - 1) * p.sh + halo, (R2 - 2) * p.sh + 2 * halo);
         LW = (int64_t)(p.Wout - 1) * p.sw + (p.kw - 1) * p.dw + 1;
         plane = LR * LW;
         // == 16 (mod 64): the 4 lane groups hit distinct banks. At column

@@ -973,6 +973,55 @@ def test_kernel_edge_cases(case):
     compare_full("edge %s" % d, gpu_all_ops(x, w, b, dy, **kw), oracle_all(x, w, b, dy, kw))
 
 
+# The flattened-pixel MFMA kernel takes tiles of consecutive pixels over the
+# N x Ho x Wo output, so a tile may end one image and start the next; its LDS
+# tile then holds both parts, each with its own halo rows. On short images
+# (few output rows against the tile's pixel span) the two parts together hold
+# more rows than one image has. These layers put such a tile on each kernel
+# layout (256- and 128-pixel tiles, packed and unpacked groups, stride 2 with
+# dilation, the upsampled gradInput).
+SPAN_CASES = [
+    dict(N=2, C=7, K=35, H=7, W=52, kh=3, kw=3, sh=1, sw=1, ph=0, pw=1, dh=1, dw=1, G=7),
+    dict(N=3, C=64, K=32, H=29, W=41, kh=3, kw=3, sh=2, sw=2, ph=1, pw=0, dh=2, dw=2, G=8),
+    dict(N=3, C=32, K=8, H=6, W=43, kh=3, kw=3, sh=1, sw=2, ph=1, pw=1, dh=1, dw=1, G=8),
+    dict(N=2, C=8, K=64, H=7, W=50, kh=3, kw=3, sh=1, sw=1, ph=0, pw=2, dh=1, dw=1, G=8),
+    dict(N=2, C=21, K=93, H=13, W=24, kh=3, kw=3, sh=2, sw=1, ph=1, pw=0, dh=2, dw=1, G=3),
+    # the same kind of span with the dispatcher choosing the MFMA path itself
+    dict(N=3, C=32, K=64, H=5, W=52, kh=3, kw=3, sh=1, sw=1, ph=0, pw=1, dh=1, dw=1, G=2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPAN_CASES)))
+def test_flat_tiles_spanning_short_images(case):
+    """Tiles that cross from one short image into the next, on the MFMA path
+    (forced, and the dispatcher's choice), NCHW and channels-last, every
+    element against the oracle."""
+    from test_gpu_nhwc import gpu_nhwc, refs
+    d = SPAN_CASES[case]
+    kw = conv_kwargs(d)
+    x, w, b = tensors(d, 3400 + case)
+    y_ref, _ = oracle.fwd(x, w, b, **kw)
+    dy = draw(("normal", 1.0), y_ref.shape, 3410 + case)
+    ref = oracle_all(x, w, b, dy, kw)
+    say("span case %s" % d)
+    # (a layout whose staged rows no longer fit the kernel's registers is
+    # declined, GCONV_ERR_UNSUPPORTED, rather than run)
+    done = compare_full("igemm %s" % d, run_path(G.PATH_IGEMM, x, w, b, dy, kw), ref)
+    assert "fwd" in done or "bwd_data" in done, (d, done)
+    compare_full("auto %s" % d, run_path(G.PATH_AUTO, x, w, b, dy, kw), ref)
+    rn = refs(x, w, b, dy, kw)
+    for path in (G.PATH_IGEMM, G.PATH_AUTO):
+        G.gconv_set_path_override(path)
+        try:
+            got = gpu_nhwc(x, w, b, dy, kw)
+        finally:
+            G.gconv_set_path_override(G.PATH_AUTO)
+        for op in OPS:
+            if got[op] is not None:
+                val, mag = rn[op]
+                check("nhwc %s %s %s" % (G.PATH_NAMES[path], op, d), got[op].cpu().numpy(), val, mag)
+
+
 def test_fc_all_ones_bit_exact():
     """The all-ones fully-connected problem of the cudnn.torch issue: every
     element of all four results equals its integer closed form."""
