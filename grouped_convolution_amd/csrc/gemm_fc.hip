@@ -418,21 +418,24 @@ bool fc_supported(const Shape& s)
            D < (1 << 30) && s.w_elems < (int64_t(1) << 28);
 }
 
-// Reduction slices for a GEMM whose output tiles alone spread unevenly over
-// the chip. With T tiles and n slices each CU works through about
-// ceil(T*n / CUs) units of 1/n of a tile, so a split pays when it evens out
-// the last round (fully-connected mode's forward: 13 x 32 = 416 tiles of
-// 128 x 128 on 256 CUs leave 96 CUs with one tile and 160 with two; three
-// slices make 1248 units, 4.875 per CU). It costs a pass that reads the n
-// partials of the E outputs and writes the result (the partials themselves
-// are written while the matrix cores are busy).
-// Each slice keeps at least 8 stages. The constants are MI355X's: 256 CUs,
-// about 0.48 TFLOP/s per CU on one 128 x 128 tile stream, about 4.5 TB/s for
-// the partials pass.
+// Reduction slices for a GEMM whose output tiles alone leave CUs idle. With
+// T tiles and n slices each CU works through about ceil(T*n / CUs) units of
+// 1/n of a tile, so a split pays when it fills CUs that would otherwise wait
+// out the last round. It costs a pass that reads the n partials of the E
+// outputs and writes the result (the partials themselves are written while
+// the matrix cores are busy). Each slice keeps at least 8 stages. The
+// constants are MI355X's: 256 CUs, about 0.48 TFLOP/s per CU on one 128 x 128
+// tile stream, about 4.5 TB/s for the partials pass.
+// Grids of at least one tile per CU are not split: two blocks share a CU and
+// the blocks do not run in lockstep rounds, so the uneven last round costs
+// less than this count says, and the partials pass more. Fully-connected
+// mode measured so: gradInput's 936 tiles ran 955 us whole against 1001-1034
+// in two to four slices, the forward's 416 tiles 1081-1111 against 1095-1120.
 static int balance_splits(int64_t tiles, int64_t R, int64_t E, int max_split)
 {
     constexpr int64_t kCUs = 256;
     constexpr double kTileRate = 0.48e12, kPassBw = 4.5e12, kLaunch = 4e-6;
+    if (tiles >= kCUs) return 1;
     const double t_tile = 2.0 * BM * BN * (double)R / kTileRate;
     int best = 1;
     double best_t = 0.0;
