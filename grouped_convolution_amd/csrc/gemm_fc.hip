@@ -177,7 +177,10 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
     // a few A and B panels serve many tiles from L2 (fully-connected mode:
     // gradWeight's reads 1.9 -> 0.7 GB, forward 2.5% faster; the results are
     // those of the row-major order, tile for tile).
-    constexpr int GM = 8;
+#ifndef GCONV_GEMM_GROUP_M
+#define GCONV_GEMM_GROUP_M 8
+#endif
+    constexpr int GM = GCONV_GEMM_GROUP_M;
     const int mn = a.m_tiles * a.n_tiles;
     const int L = bid % mn;
     bid /= mn;
