@@ -62,6 +62,11 @@ struct GemmArgs {
     int nsplit, r_split;
     int64_t c_split;
     int m_tiles, n_tiles;
+    // Balanced form (SK kernels): sk_nb blocks share the sk_total = tiles *
+    // sk_spt (tile, stage) iterations; split tiles' parts go to sk_ws.
+    int sk_nb, sk_spt;
+    int64_t sk_total;
+    float* sk_ws;
 };
 
 // Load one 32-deep stage of an operand into LDS.
@@ -159,122 +164,33 @@ __device__ __forceinline__ f4 frag(const float* t, int row, int kg, int q)
     }
 }
 
-template <bool A_RC, bool B_RC, bool RIMG>
-__global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
-{
-    static_assert(!RIMG || (A_RC && B_RC), "the image-split reduction needs contiguous reductions");
-    constexpr int TA = A_RC ? TILE_R : TILE_N;
-    constexpr int TB = B_RC ? TILE_R : TILE_N;
-    extern __shared__ float lds[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, q = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;  // wave's 64x64 quadrant
-
-    int bid = xcd_remap(blockIdx.x, gridDim.x);
-    // Tiles in groups of 8 row panels: consecutive blocks (which an XCD runs
-    // together) walk an 8-tall strip of the tile grid, so the stage slices of
-    // a few A and B panels serve many tiles from L2 (fully-connected mode:
-    // gradWeight's reads 1.9 -> 0.7 GB, forward 2.5% faster; the results are
-    // those of the row-major order, tile for tile).
+// Tile (mt, nt) of linear index L of the m_tiles x n_tiles grid. Tiles go in
+// groups of 8 row panels: consecutive blocks (which an XCD runs together)
+// walk an 8-tall strip of the tile grid, so the stage slices of a few A and B
+// panels serve many tiles from L2 (fully-connected mode: gradWeight's reads
+// 1.9 -> 0.7 GB, forward 2.5% faster; the results are those of the row-major
+// order, tile for tile).
 #ifndef GCONV_GEMM_GROUP_M
 #define GCONV_GEMM_GROUP_M 8
 #endif
+__device__ __forceinline__ void tile_of(const GemmArgs& a, int L, int& mt, int& nt)
+{
     constexpr int GM = GCONV_GEMM_GROUP_M;
-    const int mn = a.m_tiles * a.n_tiles;
-    const int L = bid % mn;
-    bid /= mn;
     const int grp = L / (GM * a.n_tiles);
     const int first_m = grp * GM;
     const int gm = min(a.m_tiles - first_m, GM);
     const int in_grp = L - grp * GM * a.n_tiles;
-    const int mt = first_m + in_grp % gm;
-    const int nt = in_grp / gm;
-    const int z = bid % a.Z;
-    const int ks = bid / a.Z;
+    mt = first_m + in_grp % gm;
+    nt = in_grp / gm;
+}
+
+// Stores a finished 128 x 128 tile: lane (l16, q) of wave (wm, wn) holds
+// C[m0 + wm*64 + i*16 + l16][n0 + wn*64 + j*16 + 4q .. +3] in acc[i][j], plus
+// the bias (per column, or per row) and the activation.
+__device__ __forceinline__ void store_tile(const GemmArgs& a, int mt, int nt, int z, int ks, const f4 (&acc)[4][4],
+                                           int wm, int wn, int l16, int q)
+{
     const int m0 = mt * BM, n0 = nt * BN;
-    const int r_begin = ks * a.r_split;
-    const int r_end = min(a.R, r_begin + a.r_split);
-
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A + (z % a.a_mod) * a.a_gs, a.a_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B + (z % a.b_mod) * a.b_gs, a.b_bytes);
-
-    f4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-
-    // Stages wholly inside the reduction (all but a ragged last one) load
-    // through precomputed lane offsets; the image-split reduction, whose
-    // offsets jump at image boundaries, and a ragged stage take the masked
-    // per-element path.
-    const int full = RIMG ? 0 : (r_end - r_begin) / BR;
-    uint32_t offa[16], offb[16];
-    if constexpr (!RIMG) {
-        stage_offsets<A_RC>(offa, m0, a.M, r_begin, a.a_ld, wave, lane);
-        stage_offsets<B_RC>(offb, n0, a.N, r_begin, a.b_ld, wave, lane);
-    } else {
-        // The image-split reduction: lane parts at reduction index 0; a stage
-        // inside one image adds the image's and the position's offset as the
-        // scalar offset.
-        stage_offsets<A_RC>(offa, m0, a.M, 0, a.a_ld, wave, lane);
-        stage_offsets<B_RC>(offb, n0, a.N, 0, a.b_ld, wave, lane);
-    }
-    const uint32_t step_a = A_RC ? BR * 4u : (uint32_t)(BR * a.a_ld) * 4u;
-    const uint32_t step_b = B_RC ? BR * 4u : (uint32_t)(BR * a.b_ld) * 4u;
-    auto issue = [&](int stage, int b) {
-        float* ta = lds + b * (TA + TB);
-        float* tb = ta + TA;
-        if (!RIMG && stage < full) {
-            load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)stage * step_a, wave);
-            load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)stage * step_b, wave);
-            return;
-        }
-        if constexpr (RIMG) {
-            const int r0 = __builtin_amdgcn_readfirstlane(r_begin + stage * BR);
-            const int img = (int)fastdiv((uint32_t)r0, a.div_rimg);
-            const int p0 = r0 - img * a.r_img;
-            if (r0 + BR <= r_end && p0 + BR <= a.r_img) {
-                load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)(img * a.a_is + p0) * 4u, wave);
-                load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)(img * a.b_is + p0) * 4u, wave);
-                return;
-            }
-        }
-        load_stage<A_RC, RIMG>(ra, ta, m0, a.M, r_begin + stage * BR, r_end, a.a_ld, wave, lane, &a, a.a_is);
-        load_stage<B_RC, RIMG>(rb, tb, n0, a.N, r_begin + stage * BR, r_end, a.b_ld, wave, lane, &a, a.b_is);
-    };
-
-    const int nst = (r_end - r_begin + BR - 1) / BR;
-    issue(0, 0);
-    for (int st = 0; st < nst; ++st) {
-        const int b = st & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (st + 1 < nst) issue(st + 1, b ^ 1);
-        const float* ta = lds + b * (TA + TB);
-        const float* tb = ta + TA;
-#pragma unroll
-        for (int kg = 0; kg < BR / 16; ++kg) {
-            f4 av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[i] = frag<A_RC>(ta, wm * 64 + i * 16 + l16, kg, q);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = frag<B_RC>(tb, wn * 64 + j * 16 + l16, kg, q);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        // A role <- B operand, B role <- A operand: lane l then
-                        // holds C[m = l%16][n = 4*(l/16) + v].
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[j][s], av[i][s],
-                                                                         acc[i][j], 0, 0, 0);
-        }
-        __syncthreads();
-    }
-
     float* Cg = a.C + (z % a.c_mod) * a.c_gs + ks * a.c_split;
     const float* bias = a.bias ? a.bias + (z % a.bias_mod) * a.bias_gs : nullptr;
     const bool vec = (a.N & 3) == 0 && (a.c_ld & 3) == 0 && ((uintptr_t)Cg & 15) == 0;
@@ -311,6 +227,195 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
             }
         }
     }
+}
+
+// Balanced form: the grid is sk_nb blocks and block b takes iterations
+// [b*T/nb, (b+1)*T/nb) of the sequence of (tile, stage) pairs, T = tiles *
+// spt, tile-major (tile t = L + z * mn in the tile order above). A tile a
+// block holds whole is stored at once; the first and the last tile of a
+// block may be parts, whose sums go to the block's two workspace slots
+// (16 float4 a thread, [slot][k][thread], so each store is one coalesced
+// row), and gemm_sk_fixup adds a split tile's parts in block order. Every
+// block thus does the same number of MFMAs whatever the tile count.
+__device__ __forceinline__ int64_t sk_it0(const GemmArgs& a, int b)
+{
+    return (int64_t)b * a.sk_total / a.sk_nb;
+}
+
+// Block holding iteration x: the largest b with sk_it0(b) <= x.
+__device__ __forceinline__ int sk_block_of(const GemmArgs& a, int64_t x)
+{
+    return (int)(((x + 1) * a.sk_nb - 1) / a.sk_total);
+}
+
+template <bool A_RC, bool B_RC, bool RIMG, bool SK>
+__global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
+{
+    static_assert(!RIMG || (A_RC && B_RC), "the image-split reduction needs contiguous reductions");
+    static_assert(!(RIMG && SK), "the balanced form takes plain reductions");
+    constexpr int TA = A_RC ? TILE_R : TILE_N;
+    constexpr int TB = B_RC ? TILE_R : TILE_N;
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, q = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;  // wave's 64x64 quadrant
+    const int mn = a.m_tiles * a.n_tiles;
+
+    // Stages [s_begin, s_end) of tile (mt, nt) of batch entry z, reduction
+    // slice ks, into acc (zeroed first).
+    auto run_tile = [&](int mt, int nt, int z, int ks, int s_begin, int s_end, f4 (&acc)[4][4]) {
+        const int m0 = mt * BM, n0 = nt * BN;
+        const int r_begin = ks * a.r_split;
+        const int r_end = min(a.R, r_begin + a.r_split);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A + (z % a.a_mod) * a.a_gs, a.a_bytes);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B + (z % a.b_mod) * a.b_gs, a.b_bytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+        // Stages wholly inside the reduction (all but a ragged last one) load
+        // through precomputed lane offsets; the image-split reduction, whose
+        // offsets jump at image boundaries, and a ragged stage take the masked
+        // per-element path.
+        const int full = RIMG ? 0 : (r_end - r_begin) / BR;
+        uint32_t offa[16], offb[16];
+        if constexpr (!RIMG) {
+            stage_offsets<A_RC>(offa, m0, a.M, r_begin, a.a_ld, wave, lane);
+            stage_offsets<B_RC>(offb, n0, a.N, r_begin, a.b_ld, wave, lane);
+        } else {
+            // The image-split reduction: lane parts at reduction index 0; a
+            // stage inside one image adds the image's and the position's
+            // offset as the scalar offset.
+            stage_offsets<A_RC>(offa, m0, a.M, 0, a.a_ld, wave, lane);
+            stage_offsets<B_RC>(offb, n0, a.N, 0, a.b_ld, wave, lane);
+        }
+        const uint32_t step_a = A_RC ? BR * 4u : (uint32_t)(BR * a.a_ld) * 4u;
+        const uint32_t step_b = B_RC ? BR * 4u : (uint32_t)(BR * a.b_ld) * 4u;
+        auto issue = [&](int stage, int b) {
+            float* ta = lds + b * (TA + TB);
+            float* tb = ta + TA;
+            if (!RIMG && stage < full) {
+                load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)stage * step_a, wave);
+                load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)stage * step_b, wave);
+                return;
+            }
+            if constexpr (RIMG) {
+                const int r0 = __builtin_amdgcn_readfirstlane(r_begin + stage * BR);
+                const int img = (int)fastdiv((uint32_t)r0, a.div_rimg);
+                const int p0 = r0 - img * a.r_img;
+                if (r0 + BR <= r_end && p0 + BR <= a.r_img) {
+                    load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)(img * a.a_is + p0) * 4u, wave);
+                    load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)(img * a.b_is + p0) * 4u, wave);
+                    return;
+                }
+            }
+            load_stage<A_RC, RIMG>(ra, ta, m0, a.M, r_begin + stage * BR, r_end, a.a_ld, wave, lane, &a, a.a_is);
+            load_stage<B_RC, RIMG>(rb, tb, n0, a.N, r_begin + stage * BR, r_end, a.b_ld, wave, lane, &a, a.b_is);
+        };
+
+        const int nst = (r_end - r_begin + BR - 1) / BR;
+        const int s1 = s_end < 0 ? nst : s_end;
+        issue(s_begin, 0);
+        for (int st = s_begin; st < s1; ++st) {
+            const int b = (st - s_begin) & 1;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (st + 1 < s1) issue(st + 1, b ^ 1);
+            const float* ta = lds + b * (TA + TB);
+            const float* tb = ta + TA;
+#pragma unroll
+            for (int kg = 0; kg < BR / 16; ++kg) {
+                f4 av[4], bv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) av[i] = frag<A_RC>(ta, wm * 64 + i * 16 + l16, kg, q);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bv[j] = frag<B_RC>(tb, wn * 64 + j * 16 + l16, kg, q);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            // A role <- B operand, B role <- A operand: lane l
+                            // then holds C[m = l%16][n = 4*(l/16) + v].
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[j][s], av[i][s],
+                                                                             acc[i][j], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+    };
+
+    f4 acc[4][4];
+    if constexpr (!SK) {
+        int bid = xcd_remap(blockIdx.x, gridDim.x);
+        const int L = bid % mn;
+        bid /= mn;
+        const int z = bid % a.Z;
+        const int ks = bid / a.Z;
+        int mt, nt;
+        tile_of(a, L, mt, nt);
+        run_tile(mt, nt, z, ks, 0, -1, acc);
+        store_tile(a, mt, nt, z, ks, acc, wm, wn, l16, q);
+    } else {
+        const int b = xcd_remap(blockIdx.x, gridDim.x);
+        const int spt = a.sk_spt;
+        const int64_t it1 = sk_it0(a, b + 1);
+        int64_t it = sk_it0(a, b);
+        const int t_first = (int)(it / spt);
+        while (it < it1) {
+            const int t = (int)(it / spt);
+            const int s0 = (int)(it - (int64_t)t * spt);
+            const int s1 = (int)min((int64_t)spt, it1 - (int64_t)t * spt);
+            const int L = t % mn, z = t / mn;
+            int mt, nt;
+            tile_of(a, L, mt, nt);
+            run_tile(mt, nt, z, 0, s0, s1, acc);
+            if (s0 == 0 && s1 == spt) {
+                store_tile(a, mt, nt, z, 0, acc, wm, wn, l16, q);
+            } else {
+                f4* slot = reinterpret_cast<f4*>(a.sk_ws) + (size_t)(2 * b + (t == t_first ? 0 : 1)) * (16 * 256);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) slot[(i * 4 + j) * 256 + tid] = acc[i][j];
+            }
+            it = (int64_t)t * spt + s1;
+        }
+    }
+}
+
+// The split tiles of the balanced form: tile t's parts, held by blocks
+// b_lo .. b_hi, are added in block order (each block's slot 0 holds its
+// first tile, slot 1 its last) and stored with the bias and activation. A
+// tile one block held whole was stored by that block.
+__global__ void __launch_bounds__(256) gemm_sk_fixup(GemmArgs a)
+{
+    const int t = blockIdx.x;
+    const int spt = a.sk_spt;
+    const int b_lo = sk_block_of(a, (int64_t)t * spt), b_hi = sk_block_of(a, (int64_t)(t + 1) * spt - 1);
+    if (b_lo == b_hi) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+    f4 acc[4][4];
+    const f4* ws = reinterpret_cast<const f4*>(a.sk_ws);
+    for (int b = b_lo; b <= b_hi; ++b) {
+        const int first = (int)(sk_it0(a, b) / spt);
+        const f4* slot = ws + (size_t)(2 * b + (t == first ? 0 : 1)) * (16 * 256);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f4 v = slot[(i * 4 + j) * 256 + tid];
+                acc[i][j] = b == b_lo ? v : acc[i][j] + v;
+            }
+    }
+    const int mn = a.m_tiles * a.n_tiles;
+    int mt, nt;
+    tile_of(a, t % mn, mt, nt);
+    store_tile(a, mt, nt, t / mn, 0, acc, wm, wn, l16, q);
 }
 
 // Sum of the split partials: out[e] = sum_s ws[s*E + e]. A workgroup owns 16
@@ -383,16 +488,58 @@ void plain(GemmArgs& a)
     a.c_split = 0;
 }
 
+// Blocks of the balanced form: two a CU.
+constexpr int kSkBlocks = 512;
+
+#ifndef GCONV_GEMM_NO_SK
+constexpr bool kSkOn = true;
+#else
+constexpr bool kSkOn = false;
+#endif
+
+// Whether a one-slice GEMM over `tiles` output tiles takes the balanced form:
+// from a tile per CU (fewer tiles split their reduction instead) to fewer
+// than one tile per block slot, where one round of whole tiles leaves CUs
+// with a single block, which does not keep a CU's matrix cores busy
+// (fully-connected mode's forward, 416 tiles: 1.036 -> 0.953 ms). With more
+// tiles the dispatcher's handing of tiles to free slots balances better than
+// a fixed split of the sequence (its gradInput, 936 tiles: 0.959 ms whole,
+// 1.089 balanced; gradWeight, 2304 tiles: 0.962 against 1.045).
+bool use_sk(int64_t tiles) { return kSkOn && tiles >= 256 && tiles < kSkBlocks; }
+
+// Workspace of the balanced form: two 128 x 128 slots a block.
+size_t sk_workspace() { return (size_t)2 * kSkBlocks * BM * BN * sizeof(float); }
+
+// One launch of the GEMM: one block per (tile, batch entry, reduction slice),
+// or, with sk_ws, the balanced form (kSkBlocks blocks over the tile-stage
+// sequence, one slice) and its fix-up pass over the split tiles.
 template <bool A_RC, bool B_RC, bool RIMG = false>
-void launch(GemmArgs& a, hipStream_t st)
+void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
 {
     constexpr int TA = A_RC ? TILE_R : TILE_N;
     constexpr int TB = B_RC ? TILE_R : TILE_N;
     const size_t lds = 2 * (size_t)(TA + TB) * 4;
     a.m_tiles = (a.M + BM - 1) / BM;
     a.n_tiles = (a.N + BN - 1) / BN;
-    const int blocks = a.m_tiles * a.n_tiles * a.Z * a.nsplit;
-    auto kern = gemm_fc_kernel<A_RC, B_RC, RIMG>;
+    const int tiles = a.m_tiles * a.n_tiles * a.Z;
+    if constexpr (!RIMG) {
+        if (sk_ws) {
+            a.sk_nb = kSkBlocks;
+            a.sk_spt = (a.R + BR - 1) / BR;
+            a.sk_total = (int64_t)tiles * a.sk_spt;
+            a.sk_ws = sk_ws;
+            auto kern = gemm_fc_kernel<A_RC, B_RC, false, true>;
+            static const bool attr = hipFuncSetAttribute((const void*)kern,
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         160 * 1024) == hipSuccess;
+            (void)attr;
+            hipLaunchKernelGGL(kern, dim3(kSkBlocks), dim3(256), lds, st, a);
+            hipLaunchKernelGGL(gemm_sk_fixup, dim3(tiles), dim3(256), 0, st, a);
+            return;
+        }
+    }
+    const int blocks = tiles * a.nsplit;
+    auto kern = gemm_fc_kernel<A_RC, B_RC, RIMG, false>;
     static const bool attr = hipFuncSetAttribute((const void*)kern,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  160 * 1024) == hipSuccess;
@@ -469,11 +616,19 @@ static void fc_data_split(const Shape& s, int op, int* nsplit, int* r_split)
     *nsplit = (int)((R + rs - 1) / rs);
 }
 
+// Output tiles of the FC forward (gradInput) GEMM over all groups.
+static int64_t fc_data_tiles(const Shape& s, int op)
+{
+    const int64_t D = (int64_t)s.Cg * s.kh * s.kw;
+    const int64_t N = op == GCONV_OP_FWD ? s.Kg : D;
+    return ((s.N + BM - 1) / BM) * ((N + BN - 1) / BN) * s.G;
+}
+
 size_t fc_data_workspace(const Shape& s, int op)
 {
     int nsplit, r_split;
     fc_data_split(s, op, &nsplit, &r_split);
-    if (nsplit <= 1) return 0;
+    if (nsplit <= 1) return use_sk(fc_data_tiles(s, op)) ? sk_workspace() : 0;
     const int64_t E = op == GCONV_OP_FWD ? (int64_t)s.N * s.K : (int64_t)s.N * s.C * s.H * s.W;
     return (size_t)nsplit * (size_t)E * 4;
 }
@@ -516,7 +671,9 @@ bool fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, f
     a.nsplit = nsplit;
     a.r_split = r_split;
     a.c_split = (int64_t)s.N * s.K;
-    launch<true, true>(a, st);
+    const bool sk = nsplit == 1 && use_sk(fc_data_tiles(s, GCONV_OP_FWD));
+    if (sk && !ws) return false;
+    launch<true, true>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_epilogue(ws, y, (int64_t)s.N * s.K, nsplit, bias, s.K, s.relu, st);
     return true;
 }
@@ -539,7 +696,9 @@ bool fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, flo
     a.nsplit = nsplit;
     a.r_split = r_split;
     a.c_split = (int64_t)s.N * Dt;
-    launch<true, false>(a, st);
+    const bool sk = nsplit == 1 && use_sk(fc_data_tiles(s, GCONV_OP_BWD_DATA));
+    if (sk && !ws) return false;
+    launch<true, false>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_epilogue(ws, dx, (int64_t)s.N * Dt, nsplit, nullptr, 1, 0, st);
     return true;
 }
@@ -564,11 +723,19 @@ static void fc_split(const Shape& s, int* nsplit, int* r_split)
     split_rows(s.N, (int64_t)((s.Kg + BM - 1) / BM) * ((D + BN - 1) / BN) * s.G, nsplit, r_split);
 }
 
+// Output tiles of the FC gradWeight GEMM over all groups.
+static int64_t fc_filter_tiles(const Shape& s)
+{
+    const int64_t D = (int64_t)s.Cg * s.kh * s.kw;
+    return (int64_t)((s.Kg + BM - 1) / BM) * ((D + BN - 1) / BN) * s.G;
+}
+
 size_t fc_bwd_filter_workspace(const Shape& s)
 {
     int nsplit, r_split;
     fc_split(s, &nsplit, &r_split);
-    return nsplit > 1 ? (size_t)nsplit * (size_t)s.w_elems * 4 : 0;
+    if (nsplit <= 1) return use_sk(fc_filter_tiles(s)) ? sk_workspace() : 0;
+    return (size_t)nsplit * (size_t)s.w_elems * 4;
 }
 
 static void split_reduce(const float* ws, float* dw, int64_t E, int nsplit, hipStream_t st)
@@ -602,7 +769,9 @@ bool fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, f
     a.nsplit = nsplit;
     a.r_split = r_split;
     a.c_split = s.w_elems;
-    launch<false, false>(a, st);
+    const bool sk = nsplit == 1 && use_sk(fc_filter_tiles(s));
+    if (sk && !ws) return false;
+    launch<false, false>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_reduce(ws, dw, s.w_elems, nsplit, st);
     return true;
 }

@@ -1022,6 +1022,51 @@ def test_flat_tiles_spanning_short_images(case):
                 check("nhwc %s %s %s" % (G.PATH_NAMES[path], op, d), got[op].cpu().numpy(), val, mag)
 
 
+# Fully-connected layers whose GEMMs have at least a tile per CU take the
+# balanced form: 512 blocks share the (tile, stage) sequence evenly, a tile
+# held by two or three blocks is summed from their parts in block order.
+# These put each FC GEMM on it in turn (ragged tiles, groups, ReLU).
+SK_CASES = [
+    # forward: 6 x 47 = 282 tiles of 2 stages
+    (dict(N=700, C=4, K=6000, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), True),
+    # gradInput: 6 x 43 = 258 tiles (64 output channels: 2 stages)
+    (dict(N=650, C=600, K=64, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), False),
+    # gradWeight: 16 x 18 = 288 tiles of 10 stages (300 images)
+    (dict(N=300, C=256, K=2048, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), False),
+    # four groups: forward 5 x 14 x 4 = 280 tiles
+    (dict(N=520, C=256, K=6800, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=4), True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SK_CASES)))
+def test_fc_balanced_form(case):
+    """FC GEMMs on the balanced form: every element against the oracle,
+    integer data bit for bit."""
+    d, relu = SK_CASES[case]
+    kw = conv_kwargs(d)
+    desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], **kw)
+    assert G.PATH_NAMES[G.gconv_select_path(desc, G.OP_FWD)] == "fc", d
+    for dist, seed in ((("normal", 1.0), 3500), (("int", -3, 3), 3550)):
+        say("fc balanced %s relu %s %s" % (d, relu, dist[0]))
+        x, w, b = tensors(d, seed + 10 * case, dist=dist)
+        y_ref, ya = oracle.fwd(x, w, b, relu=relu, **kw)
+        dy = draw(dist, y_ref.shape, seed + 10 * case + 5)
+        dx_ref, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+        dw_ref, dwa = oracle.bwd_filter(x, dy, w.shape, **kw)
+        y = G.gconv_fwd(dev(x), dev(w), dev(b), relu=relu, **kw)
+        dx = G.gconv_bwd_data(dev(dy), dev(w), x.shape, **kw)
+        dwg = G.gconv_bwd_filter(dev(x), dev(dy), w.shape, **kw)
+        torch.cuda.synchronize()
+        for tag, got, val, mag in (("fwd", y, y_ref, ya), ("bwd_data", dx, dx_ref, dxa),
+                                   ("bwd_filter", dwg, dw_ref, dwa)):
+            g = got.cpu().numpy()
+            assert g.shape == val.shape, (d, tag)
+            if dist[0] == "int":
+                assert np.array_equal(g.astype(np.float64), val), (d, tag)
+            else:
+                check("fc balanced %s %s" % (tag, d), g, val, mag)
+
+
 def test_fc_all_ones_bit_exact():
     """The all-ones fully-connected problem of the cudnn.torch issue: every
     element of all four results equals its integer closed form."""
