@@ -1067,6 +1067,54 @@ def test_fc_balanced_form(case):
                 check("fc balanced %s %s" % (tag, d), g, val, mag)
 
 
+# GEMMs of more tiles than the chip holds blocks at once, with short
+# reductions: the pointwise forward and gradInput, the channels-last 1x1 GEMM
+# and FC forward and gradWeight (ragged stages and tiles, groups, ReLU, tile
+# counts that 512 does not divide).
+MANY_TILE_CASES = [
+    # pointwise: forward 2 x 29 x 16 = 928 tiles of 5 stages, gradInput 928 of 7
+    (dict(N=16, C=136, K=200, H=60, W=60, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), True, "nchw"),
+    # two groups: 41 x 16 = 656 tiles of 3 stages each way
+    (dict(N=8, C=144, K=192, H=72, W=72, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=2), True, "nchw"),
+    # channels-last 1x1: one GEMM of 113 x 2 x 4 = 904 tiles (forward)
+    (dict(N=16, C=136, K=200, H=60, W=60, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), False, "nhwc"),
+    # FC gradWeight: 16 x 36 = 576 tiles over 100 images (4 stages, ragged)
+    (dict(N=100, C=512, K=2048, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), False, "nchw"),
+    # FC forward: 16 x 47 = 752 tiles of 2 stages
+    (dict(N=2000, C=4, K=6000, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), True, "nchw"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MANY_TILE_CASES)))
+def test_gemm_many_short_tiles(case):
+    """Every element of the forward, gradInput and gradWeight against the
+    oracle, integer data bit for bit."""
+    d, relu, layout = MANY_TILE_CASES[case]
+    kw = conv_kwargs(d)
+    nhwc = layout == "nhwc"
+    store = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 3, 1))) if nhwc else (lambda a: a)
+    back = (lambda t: t.permute(0, 3, 1, 2).contiguous()) if nhwc else (lambda t: t)
+    for dist, seed in ((("normal", 1.0), 3700), (("int", -3, 3), 3750)):
+        say("gemm many tiles %s relu %s %s %s" % (d, relu, layout, dist[0]))
+        x, w, b = tensors(d, seed + 10 * case, dist=dist)
+        y_ref, ya = oracle.fwd(x, w, b, relu=relu, **kw)
+        dy = draw(dist, y_ref.shape, seed + 10 * case + 5)
+        dx_ref, dxa = oracle.bwd_data(dy, w, x.shape, **kw)
+        dw_ref, dwa = oracle.bwd_filter(x, dy, w.shape, **kw)
+        y = back(G.gconv_fwd(dev(store(x)), dev(w), dev(b), relu=relu, layout=layout, **kw))
+        dx = back(G.gconv_bwd_data(dev(store(dy)), dev(w), store(x).shape, layout=layout, **kw))
+        dwg = G.gconv_bwd_filter(dev(store(x)), dev(store(dy)), w.shape, layout=layout, **kw)
+        torch.cuda.synchronize()
+        for tag, got, val, mag in (("fwd", y, y_ref, ya), ("bwd_data", dx, dx_ref, dxa),
+                                   ("bwd_filter", dwg, dw_ref, dwa)):
+            g = got.cpu().numpy()
+            assert g.shape == val.shape, (d, tag)
+            if dist[0] == "int":
+                assert np.array_equal(g.astype(np.float64), val), (d, tag)
+            else:
+                check("gemm many tiles %s %s" % (tag, d), g, val, mag)
+
+
 def test_fc_all_ones_bit_exact():
     """The all-ones fully-connected problem of the cudnn.torch issue: every
     element of all four results equals its integer closed form."""
