@@ -18,7 +18,8 @@
 // reads 4 consecutive reduction values with one 128-bit LDS read; the MFMA
 // steps consume them in a permuted order (any bijection of the reduction index
 // applied to both operands leaves the sum unchanged). An operand whose row
-// index is contiguous is kept as [32][row + 4]. The MFMA's A/B roles are
+// index is contiguous is kept as [32][row + 4], or as [8][row][4] with four
+// consecutive reduction values of a row side by side. The MFMA's A/B roles are
 // swapped so that each lane ends up holding 4 consecutive output columns,
 // stored as one 16-byte write.
 #include <algorithm>
@@ -32,9 +33,21 @@ namespace gconv {
 namespace {
 
 constexpr int BM = 128, BN = 128, BR = 32;
-constexpr int SROW = BM + 4;          // row stride of a [32][row] tile (== 4 mod 8)
-constexpr int TILE_R = BM * BR;       // floats of a swizzled [row][32] tile
-constexpr int TILE_N = BR * SROW;     // floats of a [32][row + 4] tile
+// Operand layouts of a stage in LDS:
+//   LR: reduction index contiguous in memory; [row][32], the 16-byte chunks
+//       of a row XOR-swizzled by the row;
+//   LN: row index contiguous; [32][row + 4];
+//   LI: row index contiguous; [32/4][row][4], four consecutive reduction
+//       values of a row side by side (one 128-bit LDS read a fragment, where
+//       LN takes four 32-bit reads, but each load instruction then gathers
+//       four 64-byte runs of global memory instead of one 256-byte run).
+constexpr int LR = 0, LN = 1, LI = 2;
+constexpr int SROW = BM + 4;          // row stride of an LN tile (== 4 mod 8)
+template <int L>
+constexpr int tile_floats()
+{
+    return L == LR ? BM * BR : L == LN ? BR * SROW : BR * BM;
+}
 
 // C[M x N] = A[M x R] * B[R x N] for Z batch entries. Entry z uses block
 // z % a_mod of A (a_gs floats apart), z % b_mod of B, z % c_mod of C and
@@ -70,15 +83,17 @@ struct GemmArgs {
 };
 
 // Load one 32-deep stage of an operand into LDS.
-//   RCONTIG: element (row, r) at P[row*ld + r]; LDS [row][32], chunk c of row
-//            `row` stored at chunk position c ^ (row & 7).
-//   else:    element (row, r) at P[r*ld + row]; LDS [r][SROW].
-template <bool RCONTIG, bool RIMG = false>
+//   LR: element (row, r) at P[row*ld + r]; LDS [row][32], chunk c of row
+//       `row` stored at chunk position c ^ (row & 7).
+//   LN: element (row, r) at P[r*ld + row]; LDS [r][SROW].
+//   LI: element (row, r) at P[r*ld + row]; LDS [r/4][row][r%4]: each
+//       instruction fills 16 rows x 4 reduction values.
+template <int LAY, bool RIMG = false>
 __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, float* dst, int row0, int rows,
                                            int r0, int R, int ld, int wave, int lane,
                                            const GemmArgs* ga = nullptr, int64_t img_stride = 0)
 {
-    if constexpr (RCONTIG) {
+    if constexpr (LAY == LR) {
         // 64 instructions of 64 floats = 2 rows of 32 each.
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -98,7 +113,7 @@ __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, float* dst
             }
             load_lds64(rs, dst + i * 64, ok ? off : kOOB);
         }
-    } else {
+    } else if constexpr (LAY == LN) {
         // 32 rows of 128 floats = 2 instructions per row.
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -109,58 +124,74 @@ __device__ __forceinline__ void load_stage(__amdgpu_buffer_rsrc_t rs, float* dst
             load_lds64(rs, dst + r * SROW + h * 64,
                        ok ? (uint32_t)((r0 + r) * ld + row0 + row) * 4u : kOOB);
         }
+    } else {
+        // 8 groups of 4 reduction values x 128 rows = 8 instructions a group.
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = wave + 4 * k;
+            const int r = 4 * (i >> 3) + (lane & 3);
+            const int row = (i & 7) * 16 + (lane >> 2);
+            const bool ok = r0 + r < R && row0 + row < rows;
+            load_lds64(rs, dst + i * 64, ok ? (uint32_t)((r0 + r) * ld + row0 + row) * 4u : kOOB);
+        }
     }
 }
 
 // Per-lane byte offsets of the 16 load instructions of a stage at reduction
 // index r0 (the same lanes and LDS slots as load_stage); rows past `rows` get
-// kOOB. A later stage at r0 + t*BR adds the uniform t*BR*4 (RCONTIG) or
+// kOOB. A later stage at r0 + t*BR adds the uniform t*BR*4 (LR) or
 // t*BR*ld*4 bytes as the instruction's scalar offset, so a stage that lies
 // wholly inside the reduction needs no per-lane arithmetic.
-template <bool RCONTIG>
+template <int LAY>
 __device__ __forceinline__ void stage_offsets(uint32_t (&off)[16], int row0, int rows, int r0, int ld, int wave,
                                               int lane)
 {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int i = wave + 4 * k;
-        if constexpr (RCONTIG) {
+        if constexpr (LAY == LR) {
             const int row = 2 * i + (lane >> 5);
             const int chunk = ((lane & 31) >> 2) ^ (row & 7);
             const int r = 4 * chunk + (lane & 3);
             off[k] = row0 + row < rows ? (uint32_t)((row0 + row) * ld + r0 + r) * 4u : kOOB;
-        } else {
+        } else if constexpr (LAY == LN) {
             const int r = i >> 1, h = i & 1;
             const int row = h * 64 + lane;
+            off[k] = row0 + row < rows ? (uint32_t)((r0 + r) * ld + row0 + row) * 4u : kOOB;
+        } else {
+            const int r = 4 * (i >> 3) + (lane & 3);
+            const int row = (i & 7) * 16 + (lane >> 2);
             off[k] = row0 + row < rows ? (uint32_t)((r0 + r) * ld + row0 + row) * 4u : kOOB;
         }
     }
 }
 
-template <bool RCONTIG>
+template <int LAY>
 __device__ __forceinline__ void load_stage_fast(__amdgpu_buffer_rsrc_t rs, float* dst, const uint32_t (&off)[16],
                                                 uint32_t soff, int wave)
 {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int i = wave + 4 * k;
-        if constexpr (RCONTIG) load_lds64s(rs, dst + i * 64, off[k], soff);
-        else load_lds64s(rs, dst + (i >> 1) * SROW + (i & 1) * 64, off[k], soff);
+        if constexpr (LAY == LN) load_lds64s(rs, dst + (i >> 1) * SROW + (i & 1) * 64, off[k], soff);
+        else load_lds64s(rs, dst + i * 64, off[k], soff);
     }
 }
 
 // Operand values of one 16-deep reduction group (4 MFMA steps) for fragment
 // rows row0..row0+15 of an LDS stage: v[s] feeds MFMA step s.
-template <bool RCONTIG>
+template <int LAY>
 __device__ __forceinline__ f4 frag(const float* t, int row, int kg, int q)
 {
-    if constexpr (RCONTIG) {
+    if constexpr (LAY == LR) {
         const int chunk = (kg * 4 + q) ^ (row & 7);
         return *(const f4*)(t + row * BR + chunk * 4);
-    } else {
+    } else if constexpr (LAY == LN) {
         const int r = kg * 16 + q * 4;
         return f4{t[(r + 0) * SROW + row], t[(r + 1) * SROW + row], t[(r + 2) * SROW + row],
                   t[(r + 3) * SROW + row]};
+    } else {
+        return *(const f4*)(t + ((kg * 4 + q) * BM + row) * 4);
     }
 }
 
@@ -248,13 +279,13 @@ __device__ __forceinline__ int sk_block_of(const GemmArgs& a, int64_t x)
     return (int)(((x + 1) * a.sk_nb - 1) / a.sk_total);
 }
 
-template <bool A_RC, bool B_RC, bool RIMG, bool SK>
+template <int A_L, int B_L, bool RIMG, bool SK>
 __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
 {
-    static_assert(!RIMG || (A_RC && B_RC), "the image-split reduction needs contiguous reductions");
+    static_assert(!RIMG || (A_L == LR && B_L == LR), "the image-split reduction needs contiguous reductions");
     static_assert(!(RIMG && SK), "the balanced form takes plain reductions");
-    constexpr int TA = A_RC ? TILE_R : TILE_N;
-    constexpr int TB = B_RC ? TILE_R : TILE_N;
+    constexpr int TA = tile_floats<A_L>();
+    constexpr int TB = tile_floats<B_L>();
     extern __shared__ float lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,23 +313,23 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
         const int full = RIMG ? 0 : (r_end - r_begin) / BR;
         uint32_t offa[16], offb[16];
         if constexpr (!RIMG) {
-            stage_offsets<A_RC>(offa, m0, a.M, r_begin, a.a_ld, wave, lane);
-            stage_offsets<B_RC>(offb, n0, a.N, r_begin, a.b_ld, wave, lane);
+            stage_offsets<A_L>(offa, m0, a.M, r_begin, a.a_ld, wave, lane);
+            stage_offsets<B_L>(offb, n0, a.N, r_begin, a.b_ld, wave, lane);
         } else {
             // The image-split reduction: lane parts at reduction index 0; a
             // stage inside one image adds the image's and the position's
             // offset as the scalar offset.
-            stage_offsets<A_RC>(offa, m0, a.M, 0, a.a_ld, wave, lane);
-            stage_offsets<B_RC>(offb, n0, a.N, 0, a.b_ld, wave, lane);
+            stage_offsets<A_L>(offa, m0, a.M, 0, a.a_ld, wave, lane);
+            stage_offsets<B_L>(offb, n0, a.N, 0, a.b_ld, wave, lane);
         }
-        const uint32_t step_a = A_RC ? BR * 4u : (uint32_t)(BR * a.a_ld) * 4u;
-        const uint32_t step_b = B_RC ? BR * 4u : (uint32_t)(BR * a.b_ld) * 4u;
+        const uint32_t step_a = A_L == LR ? BR * 4u : (uint32_t)(BR * a.a_ld) * 4u;
+        const uint32_t step_b = B_L == LR ? BR * 4u : (uint32_t)(BR * a.b_ld) * 4u;
         auto issue = [&](int stage, int b) {
             float* ta = lds + b * (TA + TB);
             float* tb = ta + TA;
             if (!RIMG && stage < full) {
-                load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)stage * step_a, wave);
-                load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)stage * step_b, wave);
+                load_stage_fast<A_L>(ra, ta, offa, (uint32_t)stage * step_a, wave);
+                load_stage_fast<B_L>(rb, tb, offb, (uint32_t)stage * step_b, wave);
                 return;
             }
             if constexpr (RIMG) {
@@ -306,13 +337,13 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
                 const int img = (int)fastdiv((uint32_t)r0, a.div_rimg);
                 const int p0 = r0 - img * a.r_img;
                 if (r0 + BR <= r_end && p0 + BR <= a.r_img) {
-                    load_stage_fast<A_RC>(ra, ta, offa, (uint32_t)(img * a.a_is + p0) * 4u, wave);
-                    load_stage_fast<B_RC>(rb, tb, offb, (uint32_t)(img * a.b_is + p0) * 4u, wave);
+                    load_stage_fast<A_L>(ra, ta, offa, (uint32_t)(img * a.a_is + p0) * 4u, wave);
+                    load_stage_fast<B_L>(rb, tb, offb, (uint32_t)(img * a.b_is + p0) * 4u, wave);
                     return;
                 }
             }
-            load_stage<A_RC, RIMG>(ra, ta, m0, a.M, r_begin + stage * BR, r_end, a.a_ld, wave, lane, &a, a.a_is);
-            load_stage<B_RC, RIMG>(rb, tb, n0, a.N, r_begin + stage * BR, r_end, a.b_ld, wave, lane, &a, a.b_is);
+            load_stage<A_L, RIMG>(ra, ta, m0, a.M, r_begin + stage * BR, r_end, a.a_ld, wave, lane, &a, a.a_is);
+            load_stage<B_L, RIMG>(rb, tb, n0, a.N, r_begin + stage * BR, r_end, a.b_ld, wave, lane, &a, a.b_is);
         };
 
         const int nst = (r_end - r_begin + BR - 1) / BR;
@@ -329,9 +360,9 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
             for (int kg = 0; kg < BR / 16; ++kg) {
                 f4 av[4], bv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) av[i] = frag<A_RC>(ta, wm * 64 + i * 16 + l16, kg, q);
+                for (int i = 0; i < 4; ++i) av[i] = frag<A_L>(ta, wm * 64 + i * 16 + l16, kg, q);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bv[j] = frag<B_RC>(tb, wn * 64 + j * 16 + l16, kg, q);
+                for (int j = 0; j < 4; ++j) bv[j] = frag<B_L>(tb, wn * 64 + j * 16 + l16, kg, q);
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -513,11 +544,11 @@ size_t sk_workspace() { return (size_t)2 * kSkBlocks * BM * BN * sizeof(float); 
 // One launch of the GEMM: one block per (tile, batch entry, reduction slice),
 // or, with sk_ws, the balanced form (kSkBlocks blocks over the tile-stage
 // sequence, one slice) and its fix-up pass over the split tiles.
-template <bool A_RC, bool B_RC, bool RIMG = false>
+template <int A_L, int B_L, bool RIMG = false>
 void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
 {
-    constexpr int TA = A_RC ? TILE_R : TILE_N;
-    constexpr int TB = B_RC ? TILE_R : TILE_N;
+    constexpr int TA = tile_floats<A_L>();
+    constexpr int TB = tile_floats<B_L>();
     const size_t lds = 2 * (size_t)(TA + TB) * 4;
     a.m_tiles = (a.M + BM - 1) / BM;
     a.n_tiles = (a.N + BN - 1) / BN;
@@ -528,7 +559,7 @@ void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
             a.sk_spt = (a.R + BR - 1) / BR;
             a.sk_total = (int64_t)tiles * a.sk_spt;
             a.sk_ws = sk_ws;
-            auto kern = gemm_fc_kernel<A_RC, B_RC, false, true>;
+            auto kern = gemm_fc_kernel<A_L, B_L, false, true>;
             static const bool attr = hipFuncSetAttribute((const void*)kern,
                                                          hipFuncAttributeMaxDynamicSharedMemorySize,
                                                          160 * 1024) == hipSuccess;
@@ -539,7 +570,7 @@ void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
         }
     }
     const int blocks = tiles * a.nsplit;
-    auto kern = gemm_fc_kernel<A_RC, B_RC, RIMG, false>;
+    auto kern = gemm_fc_kernel<A_L, B_L, RIMG, false>;
     static const bool attr = hipFuncSetAttribute((const void*)kern,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  160 * 1024) == hipSuccess;
@@ -556,6 +587,22 @@ bool extent_ok(int64_t rows, int64_t ld, int64_t used_last)
 }
 
 }  // namespace
+
+// LDS layouts of the row-contiguous FC operands: gradInput's filter (B) and
+// gradWeight's dy (A) as LI, gradWeight's x (B) as LN. Measured on fully-
+// connected mode, four alternating runs each: gradInput 1032 -> 1017 us and
+// gradWeight 980 -> 963 against LN throughout; LI on both gradWeight operands
+// ran 975, and LI on the pointwise operands (short reductions, whose stage
+// fetches weigh more) was slower.
+#ifndef GCONV_FCD_B_LAY
+#define GCONV_FCD_B_LAY LI
+#endif
+#ifndef GCONV_FCW_A_LAY
+#define GCONV_FCW_A_LAY LI
+#endif
+#ifndef GCONV_FCW_B_LAY
+#define GCONV_FCW_B_LAY LN
+#endif
 
 bool fc_supported(const Shape& s)
 {
@@ -673,7 +720,7 @@ bool fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, f
     a.c_split = (int64_t)s.N * s.K;
     const bool sk = nsplit == 1 && use_sk(fc_data_tiles(s, GCONV_OP_FWD));
     if (sk && !ws) return false;
-    launch<true, true>(a, st, sk ? ws : nullptr);
+    launch<LR, LR>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_epilogue(ws, y, (int64_t)s.N * s.K, nsplit, bias, s.K, s.relu, st);
     return true;
 }
@@ -698,7 +745,7 @@ bool fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, flo
     a.c_split = (int64_t)s.N * Dt;
     const bool sk = nsplit == 1 && use_sk(fc_data_tiles(s, GCONV_OP_BWD_DATA));
     if (sk && !ws) return false;
-    launch<true, false>(a, st, sk ? ws : nullptr);
+    launch<LR, GCONV_FCD_B_LAY>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_epilogue(ws, dx, (int64_t)s.N * Dt, nsplit, nullptr, 1, 0, st);
     return true;
 }
@@ -771,7 +818,7 @@ bool fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, f
     a.c_split = s.w_elems;
     const bool sk = nsplit == 1 && use_sk(fc_filter_tiles(s));
     if (sk && !ws) return false;
-    launch<false, false>(a, st, sk ? ws : nullptr);
+    launch<GCONV_FCW_A_LAY, GCONV_FCW_B_LAY>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_reduce(ws, dw, s.w_elems, nsplit, st);
     return true;
 }
@@ -828,7 +875,7 @@ void pointwise_fwd(const Shape& s, const float* x, const float* w, const float* 
     a.relu = s.relu;
     a.a_bytes = (uint32_t)((int64_t)s.Kg * s.Cg * 4);
     a.b_bytes = (uint32_t)((int64_t)s.Cg * P * 4);
-    launch<true, false>(a, st);
+    launch<LR, LN>(a, st);
 }
 
 // dx[n, g*Cg + c, p] = sum_k w[g*Kg + k, c] * dy[n, g*Kg + k, p]
@@ -844,7 +891,7 @@ void pointwise_bwd_data(const Shape& s, const float* dy, const float* w, float* 
     a.a_gs = (int64_t)s.Kg * s.Cg; a.b_gs = (int64_t)s.Kg * P; a.c_gs = (int64_t)s.Cg * P;
     a.a_bytes = (uint32_t)((int64_t)s.Kg * s.Cg * 4);
     a.b_bytes = (uint32_t)((int64_t)s.Kg * P * 4);
-    launch<false, false>(a, st);
+    launch<LN, LN>(a, st);
 }
 
 // dw[g*Kg + k, c] = sum_{n, p} dy[n, g*Kg + k, p] * x[n, g*Cg + c, p]
@@ -870,7 +917,7 @@ bool pointwise_bwd_filter(const Shape& s, const float* x, const float* dy, float
     a.nsplit = nsplit;
     a.r_split = r_split;
     a.c_split = s.w_elems;
-    launch<true, true, true>(a, st);
+    launch<LR, LR, true>(a, st);
     if (nsplit > 1) split_reduce(ws, dw, s.w_elems, nsplit, st);
     return true;
 }
