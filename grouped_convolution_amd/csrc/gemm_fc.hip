@@ -588,21 +588,17 @@ bool extent_ok(int64_t rows, int64_t ld, int64_t used_last)
 
 }  // namespace
 
-// LDS layouts of the row-contiguous FC operands: gradInput's filter (B) and
-// gradWeight's dy (A) as LI, gradWeight's x (B) as LN. Measured on fully-
-// connected mode, four alternating runs each: gradInput 1032 -> 1017 us and
-// gradWeight 980 -> 963 against LN throughout; LI on both gradWeight operands
-// ran 975, and LI on the pointwise operands (short reductions, whose stage
-// fetches weigh more) was slower.
-#ifndef GCONV_FCD_B_LAY
-#define GCONV_FCD_B_LAY LI
-#endif
-#ifndef GCONV_FCW_A_LAY
-#define GCONV_FCW_A_LAY LI
-#endif
-#ifndef GCONV_FCW_B_LAY
-#define GCONV_FCW_B_LAY LN
-#endif
+// LDS layout of the row-contiguous FC operands (gradInput's filter, gradWeight's
+// dy; gradWeight's x stays LN): LI where a block's reduction runs at least
+// kLiMinStages stages, LN below. LI saves LDS reads but makes each stage's
+// fetch gather four 64-byte runs, which a short reduction cannot hide.
+// Measured: fully-connected mode (gradInput 128 stages, gradWeight 50),
+// four alternating runs each, gradInput 1032 -> 1017 us and gradWeight 980
+// -> 963 against LN (LI on both gradWeight operands: 975); the channels-last
+// 1x1 layer's gradInput (4 stages) 165 -> 175 us with LI, its gradWeight
+// (256 slices of 25 stages) 132 -> 122.
+constexpr int kLiMinStages = 16;
+bool use_li(int r_split) { return (r_split + BR - 1) / BR >= kLiMinStages; }
 
 bool fc_supported(const Shape& s)
 {
@@ -745,7 +741,8 @@ bool fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, flo
     a.c_split = (int64_t)s.N * Dt;
     const bool sk = nsplit == 1 && use_sk(fc_data_tiles(s, GCONV_OP_BWD_DATA));
     if (sk && !ws) return false;
-    launch<LR, GCONV_FCD_B_LAY>(a, st, sk ? ws : nullptr);
+    if (use_li(r_split)) launch<LR, LI>(a, st, sk ? ws : nullptr);
+    else launch<LR, LN>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_epilogue(ws, dx, (int64_t)s.N * Dt, nsplit, nullptr, 1, 0, st);
     return true;
 }
@@ -818,7 +815,8 @@ bool fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, f
     a.c_split = s.w_elems;
     const bool sk = nsplit == 1 && use_sk(fc_filter_tiles(s));
     if (sk && !ws) return false;
-    launch<GCONV_FCW_A_LAY, GCONV_FCW_B_LAY>(a, st, sk ? ws : nullptr);
+    if (use_li(r_split)) launch<LI, LN>(a, st, sk ? ws : nullptr);
+    else launch<LN, LN>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_reduce(ws, dw, s.w_elems, nsplit, st);
     return true;
 }

@@ -1115,6 +1115,35 @@ def test_gemm_many_short_tiles(case):
                 check("gemm many tiles %s %s" % (tag, d), g, val, mag)
 
 
+# FC GEMMs whose blocks run long reductions stage the row-contiguous operand
+# (gradInput's filter, gradWeight's dy) as [8][row][4]: gradInput 9 x 32 = 288
+# tiles of 64 stages (balanced form), gradWeight 16 x 32 = 512 whole tiles of
+# 35 stages (1100 images, the last stage ragged). Too large for the full
+# oracle in seconds, so sampled elements are computed one by one.
+LONG_FC = dict(N=1100, C=256, K=2048, H=4, W=4, kh=4, kw=4, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1)
+
+
+def test_fc_long_reductions_sampled():
+    d = LONG_FC
+    kw = conv_kwargs(d)
+    for dist, seed in ((("normal", 1.0), 3800), (("int", -3, 3), 3850)):
+        say("fc long reductions %s" % dist[0])
+        x, w, b = tensors(d, seed, dist=dist)
+        dy = draw(dist, (d["N"], d["K"], 1, 1), seed + 5)
+        y, dx, dwg, _ = gpu_all_ops(x, w, b, dy, **kw)
+        iy = sample_indices(y.numel(), 256, seed + 1)
+        ix = sample_indices(dx.numel(), 256, seed + 2)
+        iw = sample_indices(dwg.numel(), 256, seed + 3)
+        for tag, got, (val, mag) in (
+                ("fwd", gather(y, iy), oracle.fwd(x, w, b, idx=iy, **kw)),
+                ("bwd_data", gather(dx, ix), oracle.bwd_data(dy, w, x.shape, idx=ix, **kw)),
+                ("bwd_filter", gather(dwg, iw), oracle.bwd_filter(x, dy, w.shape, idx=iw, **kw))):
+            if dist[0] == "int":
+                assert np.array_equal(got.astype(np.float64), val), tag
+            else:
+                check("fc long %s" % tag, got, val, mag)
+
+
 def test_fc_all_ones_bit_exact():
     """The all-ones fully-connected problem of the cudnn.torch issue: every
     element of all four results equals its integer closed form."""
