@@ -1116,18 +1116,24 @@ def test_gemm_many_short_tiles(case):
 
 
 # FC GEMMs whose blocks run long reductions stage the row-contiguous operand
-# (gradInput's filter, gradWeight's dy) as [8][row][4]: gradInput 9 x 32 = 288
-# tiles of 64 stages (balanced form), gradWeight 16 x 32 = 512 whole tiles of
-# 35 stages (1100 images, the last stage ragged). Too large for the full
+# (gradInput's filter, gradWeight's dy) as [8][row][4]. Too large for the full
 # oracle in seconds, so sampled elements are computed one by one.
-LONG_FC = dict(N=1100, C=256, K=2048, H=4, W=4, kh=4, kw=4, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1)
+LONG_FC = [
+    # gradInput 9 x 32 = 288 tiles of 64 stages (balanced form), gradWeight
+    # 16 x 32 = 512 whole tiles of 35 stages (1100 images, the last stage ragged)
+    dict(N=1100, C=256, K=2048, H=4, W=4, kh=4, kw=4, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+    # gradInput over 1500 output planes (47 stages, the last ragged, balanced
+    # form); gradWeight 12 x 32 = 384 tiles in two slices of 18 stages
+    dict(N=1100, C=256, K=1500, H=4, W=4, kh=4, kw=4, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+]
 
 
-def test_fc_long_reductions_sampled():
-    d = LONG_FC
+@pytest.mark.parametrize("case", range(len(LONG_FC)))
+def test_fc_long_reductions_sampled(case):
+    d = LONG_FC[case]
     kw = conv_kwargs(d)
-    for dist, seed in ((("normal", 1.0), 3800), (("int", -3, 3), 3850)):
-        say("fc long reductions %s" % dist[0])
+    for dist, seed in ((("normal", 1.0), 3800 + 10 * case), (("int", -3, 3), 3850 + 10 * case)):
+        say("fc long reductions %s %s" % (d, dist[0]))
         x, w, b = tensors(d, seed, dist=dist)
         dy = draw(dist, (d["N"], d["K"], 1, 1), seed + 5)
         y, dx, dwg, _ = gpu_all_ops(x, w, b, dy, **kw)
