@@ -262,12 +262,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, int mt, int nt, in
 
 // Balanced form: the grid is sk_nb blocks and block b takes iterations
 // [b*T/nb, (b+1)*T/nb) of the sequence of (tile, stage) pairs, T = tiles *
-// spt, tile-major (tile t = L + z * mn in the tile order above). A tile a
-// block holds whole is stored at once; the first and the last tile of a
-// block may be parts, whose sums go to the block's two workspace slots
-// (16 float4 a thread, [slot][k][thread], so each store is one coalesced
-// row), and gemm_sk_fixup adds a split tile's parts in block order. Every
-// block thus does the same number of MFMAs whatever the tile count.
+// spt, tile-major (tile t = L + z * mn in the tile order above). With
+// fewer tiles than blocks a block's range is at most spt long, so it covers
+// parts of at most two tiles (or one whole tile); their sums go to the
+// block's two workspace slots (16 float4 a thread, [slot][k][thread], so each
+// store is one coalesced row), and gemm_sk_fixup adds each tile's parts in
+// block order. Every block thus does the same number of MFMAs whatever the
+// tile count.
 __device__ __forceinline__ int64_t sk_it0(const GemmArgs& a, int b)
 {
     return (int64_t)b * a.sk_total / a.sk_nb;
@@ -390,43 +391,39 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
         run_tile(mt, nt, z, ks, 0, -1, acc);
         store_tile(a, mt, nt, z, ks, acc, wm, wn, l16, q);
     } else {
+        // The block's range: the end of tile t0 (all of it, or all of its
+        // range) and perhaps the start of t0 + 1, to slots 0 and 1.
         const int b = xcd_remap(blockIdx.x, gridDim.x);
         const int spt = a.sk_spt;
-        const int64_t it1 = sk_it0(a, b + 1);
-        int64_t it = sk_it0(a, b);
-        const int t_first = (int)(it / spt);
-        while (it < it1) {
-            const int t = (int)(it / spt);
-            const int s0 = (int)(it - (int64_t)t * spt);
-            const int s1 = (int)min((int64_t)spt, it1 - (int64_t)t * spt);
+        const int64_t it0 = sk_it0(a, b), it1 = sk_it0(a, b + 1);
+        const int t0 = (int)(it0 / spt);
+        const int s0 = (int)(it0 - (int64_t)t0 * spt);
+        const int64_t end0 = min((int64_t)(t0 + 1) * spt, it1);
+        auto part = [&](int t, int sb, int se, int slot_i) {
             const int L = t % mn, z = t / mn;
             int mt, nt;
             tile_of(a, L, mt, nt);
-            run_tile(mt, nt, z, 0, s0, s1, acc);
-            if (s0 == 0 && s1 == spt) {
-                store_tile(a, mt, nt, z, 0, acc, wm, wn, l16, q);
-            } else {
-                f4* slot = reinterpret_cast<f4*>(a.sk_ws) + (size_t)(2 * b + (t == t_first ? 0 : 1)) * (16 * 256);
+            run_tile(mt, nt, z, 0, sb, se, acc);
+            f4* slot = reinterpret_cast<f4*>(a.sk_ws) + (size_t)(2 * b + slot_i) * (16 * 256);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) slot[(i * 4 + j) * 256 + tid] = acc[i][j];
-            }
-            it = (int64_t)t * spt + s1;
-        }
+                for (int j = 0; j < 4; ++j) slot[(i * 4 + j) * 256 + tid] = acc[i][j];
+        };
+        if (it0 < it1) part(t0, s0, (int)(end0 - (int64_t)t0 * spt), 0);
+        if (end0 < it1) part(t0 + 1, 0, (int)(it1 - (int64_t)(t0 + 1) * spt), 1);
     }
 }
 
-// The split tiles of the balanced form: tile t's parts, held by blocks
-// b_lo .. b_hi, are added in block order (each block's slot 0 holds its
-// first tile, slot 1 its last) and stored with the bias and activation. A
-// tile one block held whole was stored by that block.
+// Every tile of the balanced form: tile t's parts, held by blocks b_lo ..
+// b_hi (one block for a tile held whole), are added in block order (each
+// block's slot 0 holds its first tile, slot 1 its second) and stored with the
+// bias and activation.
 __global__ void __launch_bounds__(256) gemm_sk_fixup(GemmArgs a)
 {
     const int t = blockIdx.x;
     const int spt = a.sk_spt;
     const int b_lo = sk_block_of(a, (int64_t)t * spt), b_hi = sk_block_of(a, (int64_t)(t + 1) * spt - 1);
-    if (b_lo == b_hi) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
@@ -536,6 +533,8 @@ constexpr bool kSkOn = false;
 // tiles the dispatcher's handing of tiles to free slots balances better than
 // a fixed split of the sequence (its gradInput, 936 tiles: 0.959 ms whole,
 // 1.089 balanced; gradWeight, 2304 tiles: 0.962 against 1.045).
+// (The form itself needs fewer tiles than blocks: a block then covers parts
+// of at most two tiles.)
 bool use_sk(int64_t tiles) { return kSkOn && tiles >= 256 && tiles < kSkBlocks; }
 
 // Workspace of the balanced form: two 128 x 128 slots a block.
@@ -554,7 +553,7 @@ void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
     a.n_tiles = (a.N + BN - 1) / BN;
     const int tiles = a.m_tiles * a.n_tiles * a.Z;
     if constexpr (!RIMG) {
-        if (sk_ws) {
+        if (sk_ws && tiles < kSkBlocks) {
             a.sk_nb = kSkBlocks;
             a.sk_spt = (a.R + BR - 1) / BR;
             a.sk_total = (int64_t)tiles * a.sk_spt;
