@@ -77,7 +77,9 @@ struct GemmArgs {
     int m_tiles, n_tiles;
     // Balanced form (SK kernels): sk_nb blocks share the sk_total = tiles *
     // sk_spt (tile, stage) iterations; split tiles' parts go to sk_ws.
-    int sk_nb, sk_spt;
+    // A launch that first ran whole tiles in full rounds gives the balanced
+    // form only the tiles from sk_t0 on (tile t of the form is tile sk_t0 + t).
+    int sk_nb, sk_spt, sk_t0;
     int64_t sk_total;
     float* sk_ws;
 };
@@ -260,11 +262,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, int mt, int nt, in
     }
 }
 
-// Balanced form: the grid is sk_nb blocks and block b takes iterations
-// [b*T/nb, (b+1)*T/nb) of the sequence of (tile, stage) pairs, T = tiles *
-// spt, tile-major (tile t = L + z * mn in the tile order above). With
-// fewer tiles than blocks a block's range is at most spt long, so it covers
-// parts of at most two tiles (or one whole tile); their sums go to the
+// Balanced form: the grid is sk_nb = min(512, T) blocks and block b takes
+// iterations [b*T/nb, (b+1)*T/nb) of the sequence of (tile, stage) pairs,
+// T = tiles * spt, tile-major (tile t = L + z * mn in the tile order above),
+// so no block's range is empty. With at most as many tiles as blocks a
+// block's range is at most spt long, so it covers parts of at most two
+// tiles (or one whole tile); their sums go to the
 // block's two workspace slots (16 float4 a thread, [slot][k][thread], so each
 // store is one coalesced row), and gemm_sk_fixup adds each tile's parts in
 // block order. Every block thus does the same number of MFMAs whatever the
@@ -400,7 +403,7 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
         const int s0 = (int)(it0 - (int64_t)t0 * spt);
         const int64_t end0 = min((int64_t)(t0 + 1) * spt, it1);
         auto part = [&](int t, int sb, int se, int slot_i) {
-            const int L = t % mn, z = t / mn;
+            const int L = (t + a.sk_t0) % mn, z = (t + a.sk_t0) / mn;
             int mt, nt;
             tile_of(a, L, mt, nt);
             run_tile(mt, nt, z, 0, sb, se, acc);
@@ -442,8 +445,8 @@ __global__ void __launch_bounds__(256) gemm_sk_fixup(GemmArgs a)
     }
     const int mn = a.m_tiles * a.n_tiles;
     int mt, nt;
-    tile_of(a, t % mn, mt, nt);
-    store_tile(a, mt, nt, t / mn, 0, acc, wm, wn, l16, q);
+    tile_of(a, (t + a.sk_t0) % mn, mt, nt);
+    store_tile(a, mt, nt, (t + a.sk_t0) / mn, 0, acc, wm, wn, l16, q);
 }
 
 // Sum of the split partials: out[e] = sum_s ws[s*E + e]. A workgroup owns 16
@@ -537,11 +540,32 @@ constexpr bool kSkOn = false;
 // of at most two tiles.)
 bool use_sk(int64_t tiles) { return kSkOn && tiles >= 256 && tiles < kSkBlocks; }
 
+// Whether a larger one-slice GEMM over an R-long reduction runs its whole
+// rounds of kSkBlocks tiles as plain blocks and hands a last round of at
+// most half that many tiles, which would leave CUs with a single block, to
+// the balanced form. Only long reductions gain: fully-connected mode's
+// gradWeight (2304 tiles of 50 stages, a last round of 256) 995 -> 962 us
+// in four alternating runs, 949 -> 891 in two more; the channels-last 1x1
+// layer's forward (1568 tiles of 8 stages) went
+// 150 -> 161 us and its gradInput (3136 of 4) 167 -> 182, where the two more
+// launches cost more than the short last round.
+#ifndef GCONV_GEMM_SK_TAIL
+#define GCONV_GEMM_SK_TAIL 1
+#endif
+constexpr int kSkTailMinStages = 32;
+bool use_sk_tail(int64_t tiles, int R)
+{
+    const int64_t r = tiles % kSkBlocks;
+    return kSkOn && GCONV_GEMM_SK_TAIL && tiles > kSkBlocks && r > 0 && r <= kSkBlocks / 2 &&
+           (R + BR - 1) / BR >= kSkTailMinStages;
+}
+bool use_sk_any(int64_t tiles, int R) { return use_sk(tiles) || use_sk_tail(tiles, R); }
+
 // Workspace of the balanced form: two 128 x 128 slots a block.
 size_t sk_workspace() { return (size_t)2 * kSkBlocks * BM * BN * sizeof(float); }
 
 // One launch of the GEMM: one block per (tile, batch entry, reduction slice),
-// or, with sk_ws, the balanced form (kSkBlocks blocks over the tile-stage
+// or, with sk_ws, the balanced form (up to kSkBlocks blocks over the tile-stage
 // sequence, one slice) and its fix-up pass over the split tiles.
 template <int A_L, int B_L, bool RIMG = false>
 void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
@@ -553,18 +577,32 @@ void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
     a.n_tiles = (a.N + BN - 1) / BN;
     const int tiles = a.m_tiles * a.n_tiles * a.Z;
     if constexpr (!RIMG) {
-        if (sk_ws && tiles < kSkBlocks) {
-            a.sk_nb = kSkBlocks;
+        if (sk_ws && (tiles < kSkBlocks || use_sk_tail(tiles, a.R))) {
+            // whole rounds first (none below kSkBlocks tiles)
+            const int dp = tiles / kSkBlocks * kSkBlocks;
+            if (dp > 0) {
+                auto kdp = gemm_fc_kernel<A_L, B_L, false, false>;
+                static const bool attr_dp = hipFuncSetAttribute((const void*)kdp,
+                                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                                160 * 1024) == hipSuccess;
+                (void)attr_dp;
+                hipLaunchKernelGGL(kdp, dim3(dp), dim3(256), lds, st, a);
+            }
             a.sk_spt = (a.R + BR - 1) / BR;
-            a.sk_total = (int64_t)tiles * a.sk_spt;
+            a.sk_t0 = dp;
+            a.sk_total = (int64_t)(tiles - dp) * a.sk_spt;
+            // no block without iterations: every block in a tile's range then
+            // holds a part of it (a few tiles of few stages have fewer
+            // (tile, stage) pairs than kSkBlocks)
+            a.sk_nb = (int)std::min<int64_t>(kSkBlocks, a.sk_total);
             a.sk_ws = sk_ws;
             auto kern = gemm_fc_kernel<A_L, B_L, false, true>;
             static const bool attr = hipFuncSetAttribute((const void*)kern,
                                                          hipFuncAttributeMaxDynamicSharedMemorySize,
                                                          160 * 1024) == hipSuccess;
             (void)attr;
-            hipLaunchKernelGGL(kern, dim3(kSkBlocks), dim3(256), lds, st, a);
-            hipLaunchKernelGGL(gemm_sk_fixup, dim3(tiles), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(kern, dim3(a.sk_nb), dim3(256), lds, st, a);
+            hipLaunchKernelGGL(gemm_sk_fixup, dim3(tiles - dp), dim3(256), 0, st, a);
             return;
         }
     }
@@ -659,6 +697,11 @@ static void fc_data_split(const Shape& s, int op, int* nsplit, int* r_split)
 }
 
 // Output tiles of the FC forward (gradInput) GEMM over all groups.
+// Reduction length of the forward (C*kh*kw a group) and gradInput (K a group) GEMMs.
+static int fc_data_reduction(const Shape& s, int op)
+{
+    return op == GCONV_OP_FWD ? s.Cg * s.kh * s.kw : s.Kg;
+}
 static int64_t fc_data_tiles(const Shape& s, int op)
 {
     const int64_t D = (int64_t)s.Cg * s.kh * s.kw;
@@ -670,7 +713,7 @@ size_t fc_data_workspace(const Shape& s, int op)
 {
     int nsplit, r_split;
     fc_data_split(s, op, &nsplit, &r_split);
-    if (nsplit <= 1) return use_sk(fc_data_tiles(s, op)) ? sk_workspace() : 0;
+    if (nsplit <= 1) return use_sk_any(fc_data_tiles(s, op), fc_data_reduction(s, op)) ? sk_workspace() : 0;
     const int64_t E = op == GCONV_OP_FWD ? (int64_t)s.N * s.K : (int64_t)s.N * s.C * s.H * s.W;
     return (size_t)nsplit * (size_t)E * 4;
 }
@@ -713,7 +756,7 @@ bool fc_fwd(const Shape& s, const float* x, const float* w, const float* bias, f
     a.nsplit = nsplit;
     a.r_split = r_split;
     a.c_split = (int64_t)s.N * s.K;
-    const bool sk = nsplit == 1 && use_sk(fc_data_tiles(s, GCONV_OP_FWD));
+    const bool sk = nsplit == 1 && use_sk_any(fc_data_tiles(s, GCONV_OP_FWD), fc_data_reduction(s, GCONV_OP_FWD));
     if (sk && !ws) return false;
     launch<LR, LR>(a, st, sk ? ws : nullptr);
     if (nsplit > 1) split_epilogue(ws, y, (int64_t)s.N * s.K, nsplit, bias, s.K, s.relu, st);
@@ -738,7 +781,7 @@ bool fc_bwd_data(const Shape& s, const float* dy, const float* w, float* dx, flo
     a.nsplit = nsplit;
     a.r_split = r_split;
     a.c_split = (int64_t)s.N * Dt;
-    const bool sk = nsplit == 1 && use_sk(fc_data_tiles(s, GCONV_OP_BWD_DATA));
+    const bool sk = nsplit == 1 && use_sk_any(fc_data_tiles(s, GCONV_OP_BWD_DATA), fc_data_reduction(s, GCONV_OP_BWD_DATA));
     if (sk && !ws) return false;
     if (use_li(r_split)) launch<LR, LI>(a, st, sk ? ws : nullptr);
     else launch<LR, LN>(a, st, sk ? ws : nullptr);
@@ -777,7 +820,7 @@ size_t fc_bwd_filter_workspace(const Shape& s)
 {
     int nsplit, r_split;
     fc_split(s, &nsplit, &r_split);
-    if (nsplit <= 1) return use_sk(fc_filter_tiles(s)) ? sk_workspace() : 0;
+    if (nsplit <= 1) return use_sk_any(fc_filter_tiles(s), s.N) ? sk_workspace() : 0;
     return (size_t)nsplit * (size_t)s.w_elems * 4;
 }
 
@@ -812,7 +855,7 @@ bool fc_bwd_filter(const Shape& s, const float* x, const float* dy, float* dw, f
     a.nsplit = nsplit;
     a.r_split = r_split;
     a.c_split = s.w_elems;
-    const bool sk = nsplit == 1 && use_sk(fc_filter_tiles(s));
+    const bool sk = nsplit == 1 && use_sk_any(fc_filter_tiles(s), s.N);
     if (sk && !ws) return false;
     if (use_li(r_split)) launch<LI, LN>(a, st, sk ? ws : nullptr);
     else launch<LN, LN>(a, st, sk ? ws : nullptr);

@@ -1125,6 +1125,12 @@ LONG_FC = [
     # gradInput over 1500 output planes (47 stages, the last ragged, balanced
     # form); gradWeight 12 x 32 = 384 tiles in two slices of 18 stages
     dict(N=1100, C=256, K=1500, H=4, W=4, kh=4, kw=4, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+    # whole rounds, then a balanced tail: forward 9 x 61 = 549 tiles of 32 stages (512 whole,
+    # 37 balanced); gradWeight 61 x 8 = 488 tiles in two slices of 18 stages
+    dict(N=1100, C=64, K=7800, H=4, W=4, kh=4, kw=4, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
+    # a tail of fewer (tile, stage) pairs than blocks: gradWeight 11 x 47 = 517 tiles, 5 balanced
+    # tiles of 35 stages (the last ragged) over 175 blocks
+    dict(N=1100, C=376, K=1408, H=4, W=4, kh=4, kw=4, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1),
 ]
 
 
