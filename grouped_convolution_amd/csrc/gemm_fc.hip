@@ -553,10 +553,13 @@ bool use_sk(int64_t tiles) { return kSkOn && tiles >= 256 && tiles < kSkBlocks; 
 #define GCONV_GEMM_SK_TAIL 1
 #endif
 constexpr int kSkTailMinStages = 32;
+#ifndef GCONV_GEMM_SK_TAIL_MAX
+#define GCONV_GEMM_SK_TAIL_MAX (kSkBlocks / 2)
+#endif
 bool use_sk_tail(int64_t tiles, int R)
 {
     const int64_t r = tiles % kSkBlocks;
-    return kSkOn && GCONV_GEMM_SK_TAIL && tiles > kSkBlocks && r > 0 && r <= kSkBlocks / 2 &&
+    return kSkOn && GCONV_GEMM_SK_TAIL && tiles > kSkBlocks && r > 0 && r <= GCONV_GEMM_SK_TAIL_MAX &&
            (R + BR - 1) / BR >= kSkTailMinStages;
 }
 bool use_sk_any(int64_t tiles, int R) { return use_sk(tiles) || use_sk_tail(tiles, R); }
