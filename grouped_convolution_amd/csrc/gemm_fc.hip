@@ -219,9 +219,11 @@ __device__ __forceinline__ void tile_of(const GemmArgs& a, int L, int& mt, int& 
 
 // Stores a finished 128 x 128 tile: lane (l16, q) of wave (wm, wn) holds
 // C[m0 + wm*64 + i*16 + l16][n0 + wn*64 + j*16 + 4q .. +3] in acc[i][j], plus
-// the bias (per column, or per row) and the activation.
-__device__ __forceinline__ void store_tile(const GemmArgs& a, int mt, int nt, int z, int ks, const f4 (&acc)[4][4],
-                                           int wm, int wn, int l16, int q)
+// the bias (per column, or per row) and the activation. NI < 4: only the
+// fragment rows i0 .. i0 + NI - 1, held in acc[i - i0][j].
+template <int NI = 4>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, int mt, int nt, int z, int ks, const f4 (&acc)[NI][4],
+                                           int wm, int wn, int l16, int q, int i0 = 0)
 {
     const int m0 = mt * BM, n0 = nt * BN;
     float* Cg = a.C + (z % a.c_mod) * a.c_gs + ks * a.c_split;
@@ -238,10 +240,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, int mt, int nt, in
             bv.w = n + 3 < a.N ? bias[n + 3] : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wm * 64 + i * 16 + l16;
+        for (int ii = 0; ii < NI; ++ii) {
+            const int m = m0 + wm * 64 + (i0 + ii) * 16 + l16;
             if (m >= a.M) continue;
-            f4 v = acc[i][j] + bv;
+            f4 v = acc[ii][j] + bv;
             if (bias && a.bias_rows) v += bias[m];
             if (a.relu) {
                 v.x = relu_if(v.x, 1);
@@ -421,7 +423,8 @@ __global__ void __launch_bounds__(256, 2) gemm_fc_kernel(GemmArgs a)
 // Every tile of the balanced form: tile t's parts, held by blocks b_lo ..
 // b_hi (one block for a tile held whole), are added in block order (each
 // block's slot 0 holds its first tile, slot 1 its second) and stored with the
-// bias and activation.
+// bias and activation. Four blocks a tile, one a row of fragments
+// (blockIdx.y), so that enough waves keep the part reads in flight.
 __global__ void __launch_bounds__(256) gemm_sk_fixup(GemmArgs a)
 {
     const int t = blockIdx.x;
@@ -430,23 +433,22 @@ __global__ void __launch_bounds__(256) gemm_sk_fixup(GemmArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
-    f4 acc[4][4];
+    const int i = blockIdx.y;
+    f4 acc[1][4];
     const f4* ws = reinterpret_cast<const f4*>(a.sk_ws);
     for (int b = b_lo; b <= b_hi; ++b) {
         const int first = (int)(sk_it0(a, b) / spt);
         const f4* slot = ws + (size_t)(2 * b + (t == first ? 0 : 1)) * (16 * 256);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f4 v = slot[(i * 4 + j) * 256 + tid];
-                acc[i][j] = b == b_lo ? v : acc[i][j] + v;
-            }
+        for (int j = 0; j < 4; ++j) {
+            const f4 v = slot[(i * 4 + j) * 256 + tid];
+            acc[0][j] = b == b_lo ? v : acc[0][j] + v;
+        }
     }
     const int mn = a.m_tiles * a.n_tiles;
     int mt, nt;
     tile_of(a, (t + a.sk_t0) % mn, mt, nt);
-    store_tile(a, mt, nt, (t + a.sk_t0) / mn, 0, acc, wm, wn, l16, q);
+    store_tile<1>(a, mt, nt, (t + a.sk_t0) / mn, 0, acc, wm, wn, l16, q, i);
 }
 
 // Sum of the split partials: out[e] = sum_s ws[s*E + e]. A workgroup owns 16
@@ -605,7 +607,7 @@ void launch(GemmArgs& a, hipStream_t st, float* sk_ws = nullptr)
                                                          160 * 1024) == hipSuccess;
             (void)attr;
             hipLaunchKernelGGL(kern, dim3(a.sk_nb), dim3(256), lds, st, a);
-            hipLaunchKernelGGL(gemm_sk_fixup, dim3(tiles - dp), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(gemm_sk_fixup, dim3(tiles - dp, 4), dim3(256), 0, st, a);
             return;
         }
     }
