@@ -33,6 +33,9 @@ CASES = [
     (dict(N=6, C=32, K=32, H=30, W=26, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=8), "smallgroup", "nchw"),
     (dict(N=4, C=64, K=48, H=20, W=20, kh=1, kw=1, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), "pointwise", "nchw"),
     (dict(N=3, C=32, K=32, H=15, W=17, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=1), "igemm", "nhwc"),
+    # fully-connected gradWeight in the balanced form (16 x 18 = 288 tiles over 300 images, then
+    # 150): its split tiles' parts go through the array, the second call over fewer stages
+    (dict(N=300, C=256, K=2048, H=3, W=3, kh=3, kw=3, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1, G=1), "fc", "nchw"),
 ]
 
 
@@ -62,7 +65,8 @@ def test_static_matches_workspace_entry_point(case):
     d, family, layout = CASES[case]
     desc = G.make_desc(d["N"], d["C"], d["H"], d["W"], d["K"], d["kh"], d["kw"], layout=layout, **conv_kwargs(d))
     assert G.PATH_NAMES[G.gconv_select_path(desc, G.OP_BWD_FILTER)] == family
-    small = dict(d, N=max(1, d["N"] // 2), H=d["H"] - 3)
+    # a smaller second call (fully-connected mode keeps its kernel == input)
+    small = dict(d, N=max(1, d["N"] // 2)) if family == "fc" else dict(d, N=max(1, d["N"] // 2), H=d["H"] - 3)
     for i, dd in enumerate((d, small)):
         say("no-alloc gradWeight %s %s call %d" % (layout, dd, i))
         got, want, nws = _run(lib, dd, layout, 4100 + 10 * case + i)
